@@ -1,0 +1,334 @@
+"""fp64 CPU oracle of the HSTU layer -- TEST INFRASTRUCTURE, NOT PRODUCT CODE.
+
+Only the test suite, the package entry's smoke check and the benchmark's CPU
+baseline leg may import this module.  The HIP library never calls it and
+shares no code with it; both only consume the seeded inputs made by `synth`.
+
+Pages cited (their text, not line numbers):
+  [GR]     NVIDIA generative-recommenders summary (quantumzeitgeist.com),
+           section "HSTU Architecture: Efficient Attention for User History".
+  [DLRMv4] "DLRMv4 Brings Sequence-Based Recommendation Training to MLPerf"
+           (xfinit.ro), sections "Model Architecture", "HSTU Hyperparameters",
+           "Computation Cost Analysis" (Tables 6 and 7).
+
+What is computed (every array is float64; integer work is exact):
+
+1. Projection ([DLRMv4] "Model Architecture", first bullet; width from
+   Table 7's UVQK row): Z = X W1 (+ b1), Zh = SiLU(Z) when proj_silu, split
+   column-wise into U | V | Q | K blocks of widths H*d_v, H*d_v, H*d_qk,
+   H*d_qk; inside a block head h owns columns h*d .. h*d+d-1.
+2. Pointwise attention ([GR]: SiLU weighting instead of softmax plus a
+   relative bias; [DLRMv4] "Model Architecture", second bullet: the bias
+   comes from positional and temporal distance; Table 7 note: only the lower
+   triangle is evaluated; "Model Architecture": candidates appended and
+   compared with the history in one pass).  Per sequence of n tokens of which
+   the last c are candidates (n_h = n - c), for each head:
+       s_ij = q_i . k_j + rab_pos[h, bp(i,j)] + rab_time[h, bt(i,j)]
+       a_ij = SiLU(s_ij) / N   if allowed(i, j), else 0
+       O_i  = sum_j a_ij v_j
+   allowed(i, j): history row i sees history j <= i; a candidate row sees all
+   history and itself only.  p(i) = min(i, n_h); bp = min(p(i) - p(j), P-1);
+   dt = min(max(ts_i - ts_j, 0), 2^31 - 1); bt = min(floor(log2(dt + 1)), Tb-1).
+   N = norm_len (norm_mode 0) or the sequence's own n (norm_mode 1).
+3. Gated output ([GR]: elementwise gating before the output projection;
+   [DLRMv4] third bullet): LayerNorm over the H*d_v vector of each token
+   (biased variance, eps; optional gamma/beta), G = LN(O) * U.
+4. Y = G W2 (+ b2) (+ X when residual).  Layers stack Y -> next X.
+5. Backward: the chain rule of 1-4 written out by hand (no autograd).
+
+Readings where the pages are silent (each is a flag here):
+  proj_silu=True, residual=True, no 1/sqrt(d) on q.k, LayerNorm eps=1e-6 with
+  no affine by default, clamp-style position buckets, integer log2 time
+  buckets, dt = t_query - t_key clamped at 0, per-head bias tables.
+
+Parity status: every function below is pinned by tests in tests/ (brute-force
+loops on tiny inputs, closed forms, invariants, finite differences, the
+page's Table 7 FLOP totals for the cost model).  The numeric choices listed
+as readings above cannot be pinned by any value the pages print; they are
+pinned only to their own definitions.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+
+INT31_MAX = (1 << 31) - 1
+
+
+# ----------------------------------------------------------------------------
+# Elementwise pieces
+# ----------------------------------------------------------------------------
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """Logistic function via the exact identity 1/(1+e^-x) = (1 + tanh(x/2)) / 2."""
+    return 0.5 * (1.0 + np.tanh(0.5 * x))
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU(x) = x * sigmoid(x) ([GR]: the weighting that replaces softmax)."""
+    return x * sigmoid(x)
+
+
+def silu_grad(x: np.ndarray) -> np.ndarray:
+    """d/dx SiLU(x) = sigmoid(x) * (1 + x * (1 - sigmoid(x)))."""
+    s = sigmoid(x)
+    return s * (1.0 + x * (1.0 - s))
+
+
+# ----------------------------------------------------------------------------
+# Relative-bias buckets ([DLRMv4] "Model Architecture": positional and temporal distance)
+# ----------------------------------------------------------------------------
+
+def time_bucket(dt: np.ndarray, n_buckets: int = 128) -> np.ndarray:
+    """floor(log2(dt + 1)) with dt clamped to [0, 2^31-1], capped at n_buckets-1.
+
+    Computed exactly: frexp of an integer below 2^53 returns its bit length.
+    """
+    dt = np.clip(np.asarray(dt, dtype=np.int64), 0, INT31_MAX)
+    _, e = np.frexp((dt + 1).astype(np.float64))
+    return np.minimum(e.astype(np.int64) - 1, n_buckets - 1)
+
+
+def pos_bucket(dp: np.ndarray, n_buckets: int = 128) -> np.ndarray:
+    """Clamp of the (non-negative) position distance to n_buckets-1."""
+    return np.minimum(np.maximum(np.asarray(dp, dtype=np.int64), 0), n_buckets - 1)
+
+
+def positions(n: int, c: int) -> np.ndarray:
+    """p(i) = min(i, n_h): candidates all sit at the position after the history."""
+    return np.minimum(np.arange(n, dtype=np.int64), n - c)
+
+
+def allowed_mask(n: int, c: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Boolean [len(rows), n]: causal for history rows, history+self for candidates."""
+    n_h = n - c
+    i = np.arange(n) if rows is None else np.asarray(rows)
+    j = np.arange(n)
+    hist_row = (i < n_h)[:, None]
+    causal = j[None, :] <= i[:, None]
+    cand = (j[None, :] < n_h) | (j[None, :] == i[:, None])
+    return np.where(hist_row, causal, cand)
+
+
+def bias_buckets(ts: np.ndarray, c: int, rows: np.ndarray, n_pos: int, n_time: int):
+    """(bp, bt) integer arrays [len(rows), n] for one sequence."""
+    n = ts.shape[0]
+    p = positions(n, c)
+    bp = pos_bucket(p[rows][:, None] - p[None, :], n_pos)
+    bt = time_bucket(ts[rows][:, None] - ts[None, :], n_time)
+    return bp, bt
+
+
+# ----------------------------------------------------------------------------
+# Attention
+# ----------------------------------------------------------------------------
+
+def _norm(n: int, norm_mode: int, norm_len: int) -> float:
+    return float(norm_len) if norm_mode == 0 else float(n)
+
+
+def _seq_iter(seq_offsets, num_candidates):
+    B = len(seq_offsets) - 1
+    for b in range(B):
+        o0, o1 = int(seq_offsets[b]), int(seq_offsets[b + 1])
+        c = 0 if num_candidates is None else int(num_candidates[b])
+        yield b, o0, o1, c
+
+
+def _rab(tab: np.ndarray, H: int) -> np.ndarray:
+    tab = np.asarray(tab, dtype=np.float64)
+    return np.broadcast_to(tab, (H, tab.shape[-1])) if tab.ndim == 1 else tab
+
+
+def attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time,
+             num_candidates=None, norm_mode=0, norm_len=1, row_block=1024,
+             return_rows=None):
+    """O[T, H, d_v] of the pointwise attention (step 2 above).
+
+    q, k: [T, H, d_qk]; v: [T, H, d_v]; rab_pos/rab_time: [H, P] or [P].
+    return_rows: optional per-sequence list of local query rows to compute
+    (others stay zero) -- used for sampled checks at full size.
+    """
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    T, H, _ = q.shape
+    dv = v.shape[2]
+    rp, rt = _rab(rab_pos, H), _rab(rab_time, H)
+    O = np.zeros((T, H, dv))
+    for b, o0, o1, c in _seq_iter(seq_offsets, num_candidates):
+        n = o1 - o0
+        if n == 0:
+            continue
+        N = _norm(n, norm_mode, norm_len)
+        ts = np.asarray(timestamps[o0:o1], np.int64)
+        all_rows = np.arange(n) if return_rows is None else np.asarray(return_rows[b], np.int64)
+        for r0 in range(0, len(all_rows), row_block):
+            rows = all_rows[r0:r0 + row_block]
+            M = allowed_mask(n, c, rows)
+            bp, bt = bias_buckets(ts, c, rows, rp.shape[1], rt.shape[1])
+            for h in range(H):
+                s = q[o0 + rows, h, :] @ k[o0:o1, h, :].T + rp[h][bp] + rt[h][bt]
+                a = np.where(M, silu(s), 0.0) / N
+                O[o0 + rows, h, :] = a @ v[o0:o1, h, :]
+    return O
+
+
+def attn_bwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, d_out,
+             num_candidates=None, norm_mode=0, norm_len=1, row_block=1024):
+    """(dq, dk, dv, d_rab_pos[H,P], d_rab_time[H,Tb]) for attn_fwd's output gradient."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    dO = np.asarray(d_out, np.float64)
+    T, H, _ = q.shape
+    rp, rt = _rab(rab_pos, H), _rab(rab_time, H)
+    P, Tb = rp.shape[1], rt.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    drp, drt = np.zeros((H, P)), np.zeros((H, Tb))
+    for b, o0, o1, c in _seq_iter(seq_offsets, num_candidates):
+        n = o1 - o0
+        if n == 0:
+            continue
+        N = _norm(n, norm_mode, norm_len)
+        ts = np.asarray(timestamps[o0:o1], np.int64)
+        for r0 in range(0, n, row_block):
+            rows = np.arange(r0, min(n, r0 + row_block))
+            M = allowed_mask(n, c, rows)
+            bp, bt = bias_buckets(ts, c, rows, P, Tb)
+            for h in range(H):
+                s = q[o0 + rows, h, :] @ k[o0:o1, h, :].T + rp[h][bp] + rt[h][bt]
+                a = np.where(M, silu(s), 0.0) / N                 # A = SiLU(S) M / N
+                dv[o0:o1, h, :] += a.T @ dO[o0 + rows, h, :]      # dV = A^T dO
+                da = dO[o0 + rows, h, :] @ v[o0:o1, h, :].T       # dA = dO V^T
+                ds = np.where(M, da * silu_grad(s), 0.0) / N      # dS = dA SiLU'(S) M / N
+                dq[o0 + rows, h, :] += ds @ k[o0:o1, h, :]        # dQ = dS K
+                dk[o0:o1, h, :] += ds.T @ q[o0 + rows, h, :]      # dK = dS^T Q
+                drp[h] += np.bincount(bp.ravel(), weights=ds.ravel(), minlength=P)
+                drt[h] += np.bincount(bt.ravel(), weights=ds.ravel(), minlength=Tb)
+    return dq, dk, dv, drp, drt
+
+
+# ----------------------------------------------------------------------------
+# LayerNorm + gating (step 3)
+# ----------------------------------------------------------------------------
+
+def layernorm_fwd(x, eps=1e-6, gamma=None, beta=None):
+    """Returns (y, mu, rstd, xhat); normalises over the last axis with biased variance."""
+    x = np.asarray(x, np.float64)
+    mu = x.mean(axis=-1)
+    var = ((x - mu[..., None]) ** 2).mean(axis=-1)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = (x - mu[..., None]) * rstd[..., None]
+    y = xhat
+    if gamma is not None:
+        y = y * np.asarray(gamma, np.float64)
+    if beta is not None:
+        y = y + np.asarray(beta, np.float64)
+    return y, mu, rstd, xhat
+
+
+def layernorm_bwd(dy, xhat, rstd, gamma=None):
+    """(dx, dgamma, dbeta) of layernorm_fwd."""
+    dy = np.asarray(dy, np.float64)
+    dgamma = (dy * xhat).sum(axis=0)
+    dbeta = dy.sum(axis=0)
+    dxh = dy * np.asarray(gamma, np.float64) if gamma is not None else dy
+    m1 = dxh.mean(axis=-1, keepdims=True)
+    m2 = (dxh * xhat).mean(axis=-1, keepdims=True)
+    dx = rstd[..., None] * (dxh - m1 - xhat * m2)
+    return dx, dgamma, dbeta
+
+
+# ----------------------------------------------------------------------------
+# Whole layer
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class LayerFlags:
+    H: int
+    d_qk: int
+    d_v: int
+    norm_mode: int = 0
+    norm_len: int = 1
+    proj_silu: bool = True
+    residual: bool = True
+    eps: float = 1e-6
+
+
+def split_uvqk(Zh: np.ndarray, f: LayerFlags):
+    T = Zh.shape[0]
+    a, bq = f.H * f.d_v, f.H * f.d_qk
+    U = Zh[:, 0:a]
+    V = Zh[:, a:2 * a].reshape(T, f.H, f.d_v)
+    Q = Zh[:, 2 * a:2 * a + bq].reshape(T, f.H, f.d_qk)
+    K = Zh[:, 2 * a + bq:2 * a + 2 * bq].reshape(T, f.H, f.d_qk)
+    return U, V, Q, K
+
+
+def layer_fwd(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
+              f: LayerFlags, b1=None, b2=None, gamma=None, beta=None):
+    """Y and the saved intermediates of one HSTU layer (steps 1-4)."""
+    X = np.asarray(X, np.float64)
+    Z = X @ np.asarray(W1, np.float64)
+    if b1 is not None:
+        Z = Z + np.asarray(b1, np.float64)
+    Zh = silu(Z) if f.proj_silu else Z
+    U, V, Q, K = split_uvqk(Zh, f)
+    O = attn_fwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
+                 f.norm_mode, f.norm_len)
+    T = X.shape[0]
+    O2 = O.reshape(T, f.H * f.d_v)
+    Yn, mu, rstd, xhat = layernorm_fwd(O2, f.eps, gamma, beta)
+    G = Yn * U
+    Y = G @ np.asarray(W2, np.float64)
+    if b2 is not None:
+        Y = Y + np.asarray(b2, np.float64)
+    if f.residual:
+        Y = Y + X
+    saved = dict(Z=Z, Zh=Zh, O=O2, mu=mu, rstd=rstd, xhat=xhat, Yn=Yn, G=G)
+    return Y, saved
+
+
+def layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
+              f: LayerFlags, saved: Dict, b1=None, b2=None, gamma=None, beta=None):
+    """All gradients of one layer, by the chain rule written out (step 5)."""
+    dY = np.asarray(dY, np.float64)
+    X = np.asarray(X, np.float64)
+    W1 = np.asarray(W1, np.float64); W2 = np.asarray(W2, np.float64)
+    T = X.shape[0]
+    U, V, Q, K = split_uvqk(saved["Zh"], f)
+    # Y = G W2 + b2 (+ X)
+    dG = dY @ W2.T
+    dW2 = saved["G"].T @ dY
+    db2 = dY.sum(axis=0)
+    # G = Yn * U
+    dU = dG * saved["Yn"]
+    dYn = dG * U
+    # Yn = LN(O)
+    dO2, dgamma, dbeta = layernorm_bwd(dYn, saved["xhat"], saved["rstd"], gamma)
+    dO = dO2.reshape(T, f.H, f.d_v)
+    dQ, dK, dV, drp, drt = attn_bwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, dO,
+                                    num_candidates, f.norm_mode, f.norm_len)
+    dZh = np.concatenate([dU, dV.reshape(T, -1), dQ.reshape(T, -1), dK.reshape(T, -1)], axis=1)
+    dZ = dZh * silu_grad(saved["Z"]) if f.proj_silu else dZh
+    dW1 = X.T @ dZ
+    db1 = dZ.sum(axis=0)
+    dX = dZ @ W1.T
+    if f.residual:
+        dX = dX + dY
+    return dict(dX=dX, dW1=dW1, dW2=dW2, db1=db1, db2=db2, dgamma=dgamma, dbeta=dbeta,
+                drab_pos=drp, drab_time=drt, dZ=dZ, dO=dO2, dG=dG)
+
+
+def stack_fwd(X, layers: List, seq_offsets, timestamps, num_candidates, f: LayerFlags):
+    """Layers stacked: the output of layer l is the input of layer l+1.
+
+    `layers` holds objects with W1, W2, rab_pos, rab_time attributes.
+    Returns the list of per-layer outputs.
+    """
+    outs = []
+    x = np.asarray(X, np.float64)
+    for w in layers:
+        x, _ = layer_fwd(x, w.W1, w.W2, w.rab_pos, w.rab_time, seq_offsets, timestamps,
+                         num_candidates, f)
+        outs.append(x)
+    return outs

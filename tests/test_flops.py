@@ -1,0 +1,46 @@
+"""The cost model against the DLRMv4 page's Table 7 totals."""
+import os
+
+import numpy as np
+
+from hstu_sequential_transduction_amd import flops
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "table7_flops.txt")
+
+
+def _golden():
+    out = {}
+    with open(GOLD) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                out[k] = float(v)
+    return out
+
+
+def test_table7_printed_values():
+    want = _golden()
+    got = flops.table7(B=1024, L=3, h=4, d_qk=128, d_v=128, D=512, S=4096, outproj_width_mult=3)
+    for k, v in want.items():
+        assert round(got[k] / 1e12, 2) == v, (k, got[k])
+
+
+def test_table7_built_width_differs():
+    got = flops.table7(B=1024, L=3, h=4, d_qk=128, d_v=128, D=512, S=4096, outproj_width_mult=1)
+    assert round(got["outproj"] / 1e12, 2) == 19.79
+
+
+def test_jagged_counter_reduces_to_table7():
+    # one layer, every sequence full length: the jagged counter equals the table's rows / (B*L)
+    B, S = 4, 4096
+    per = flops.layer_flops([S] * B, None, D=512, H=4, d_qk=128, d_v=128, backward=True)
+    t7 = flops.table7(B=B, L=1, h=4, d_qk=128, d_v=128, D=512, S=S, outproj_width_mult=1)
+    np.testing.assert_allclose(per["uvqk"], t7["uvqk"])
+    np.testing.assert_allclose(per["outproj"], t7["outproj"])
+    np.testing.assert_allclose(per["attn"], t7["attn"])
+
+
+def test_candidate_pairs():
+    # 4 history + 2 candidates: 4^2/2 history pairs, 2*4 candidate-history pairs, 2 self pairs
+    assert flops.attn_pairs([6], [2]) == 8 + 8 + 2
