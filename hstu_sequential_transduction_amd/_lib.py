@@ -1,0 +1,126 @@
+"""ctypes declarations of libhstu.so's C ABI (include/hstu.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation anywhere in this package.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhstu.so")
+
+HSTU_OK = 0
+STATUS_NAMES = {0: "HSTU_OK", -1: "HSTU_ERR_INVALID_ARG", -2: "HSTU_ERR_UNSUPPORTED",
+                -3: "HSTU_ERR_WORKSPACE", -4: "HSTU_ERR_HIP", -5: "HSTU_ERR_VALIDATION"}
+HSTU_F32, HSTU_BF16 = 0, 1
+
+EXPORTED = [
+    "hstu_status_string", "hstu_version",
+    "hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size",
+    "hstu_attn_fwd", "hstu_attn_bwd",
+    "hstu_layer_fwd_workspace_size", "hstu_layer_bwd_workspace_size",
+    "hstu_layer_fwd", "hstu_layer_bwd",
+    "hstu_bias_buckets", "hstu_schedule_capacity", "hstu_schedule",
+    "hstu_schedule_workspace_size", "hstu_validate_inputs",
+]
+
+
+class AttnDesc(C.Structure):
+    _fields_ = [("B", C.c_int32), ("T", C.c_int64), ("H", C.c_int32), ("d_qk", C.c_int32),
+                ("d_v", C.c_int32), ("n_pos_buckets", C.c_int32),
+                ("n_time_buckets", C.c_int32), ("norm_mode", C.c_int32),
+                ("norm_len", C.c_int32), ("dtype", C.c_int32),
+                ("rab_head_stride", C.c_int64)]
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("attn", AttnDesc), ("D", C.c_int32), ("proj_silu", C.c_int32),
+                ("residual", C.c_int32), ("ln_eps", C.c_float)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [("W1", C.c_void_p), ("W2", C.c_void_p), ("b1", C.c_void_p), ("b2", C.c_void_p),
+                ("ln_gamma", C.c_void_p), ("ln_beta", C.c_void_p), ("rab_pos", C.c_void_p),
+                ("rab_time", C.c_void_p)]
+
+
+class LayerSaved(C.Structure):
+    _fields_ = [("Z", C.c_void_p), ("Zh", C.c_void_p), ("O", C.c_void_p), ("G", C.c_void_p),
+                ("mu", C.c_void_p), ("rstd", C.c_void_p)]
+
+
+class LayerGrads(C.Structure):
+    _fields_ = [("dW1", C.c_void_p), ("dW2", C.c_void_p), ("db1", C.c_void_p),
+                ("db2", C.c_void_p), ("dgamma", C.c_void_p), ("dbeta", C.c_void_p),
+                ("drab_pos", C.c_void_p), ("drab_time", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded library (raises if libhstu.so is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()' or "
+            "python hstu_sequential_transduction_amd/build.py)")
+    L = C.CDLL(LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    P = C.POINTER
+    L.hstu_status_string.restype = C.c_char_p
+    L.hstu_status_string.argtypes = [C.c_int]
+    L.hstu_version.restype = C.c_char_p
+    L.hstu_version.argtypes = []
+    for f in ("hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size"):
+        getattr(L, f).restype = sz
+        getattr(L, f).argtypes = [P(AttnDesc)]
+    L.hstu_layer_fwd_workspace_size.restype = sz
+    L.hstu_layer_fwd_workspace_size.argtypes = [P(LayerDesc), C.c_int]
+    L.hstu_layer_bwd_workspace_size.restype = sz
+    L.hstu_layer_bwd_workspace_size.argtypes = [P(LayerDesc)]
+    L.hstu_attn_fwd.restype = C.c_int
+    L.hstu_attn_fwd.argtypes = [P(AttnDesc), vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i64,
+                                vp, sz, vp]
+    L.hstu_attn_bwd.restype = C.c_int
+    L.hstu_attn_bwd.argtypes = [P(AttnDesc), vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i64,
+                                vp, vp, vp, vp, vp, vp, sz, vp]
+    L.hstu_layer_fwd.restype = C.c_int
+    L.hstu_layer_fwd.argtypes = [P(LayerDesc), vp, P(LayerWeights), vp, vp, vp, vp,
+                                 P(LayerSaved), vp, sz, vp]
+    L.hstu_layer_bwd.restype = C.c_int
+    L.hstu_layer_bwd.argtypes = [P(LayerDesc), vp, P(LayerWeights), vp, vp, vp, P(LayerSaved),
+                                 vp, vp, P(LayerGrads), vp, sz, vp]
+    L.hstu_bias_buckets.restype = C.c_int
+    L.hstu_bias_buckets.argtypes = [P(AttnDesc), vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+    L.hstu_schedule_capacity.restype = i64
+    L.hstu_schedule_capacity.argtypes = [i64, i32, i32]
+    L.hstu_schedule_workspace_size.restype = sz
+    L.hstu_schedule_workspace_size.argtypes = [i32, i64, i32]
+    L.hstu_schedule.restype = C.c_int
+    L.hstu_schedule.argtypes = [i32, i64, vp, i32, i32, vp, vp, vp, sz, vp]
+    L.hstu_validate_inputs.restype = C.c_int
+    L.hstu_validate_inputs.argtypes = [i32, i64, vp, vp, vp, vp]
+    _lib = L
+    return L
+
+
+class HstuError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        name = STATUS_NAMES.get(status, str(status))
+        try:
+            msg = lib().hstu_status_string(status).decode()
+        except Exception:  # pragma: no cover
+            msg = ""
+        super().__init__(f"{fn} failed: {name} ({msg})")
+        self.status = status
+
+
+def check(fn: str, status: int) -> None:
+    if status != HSTU_OK:
+        raise HstuError(fn, status)

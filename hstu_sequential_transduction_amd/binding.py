@@ -1,0 +1,268 @@
+"""Thin torch-facing binding of libhstu.so: argument marshalling only.
+
+Each function takes device tensors, allocates outputs and the workspace with
+torch (device memory only), and calls the C entry point of the same name on
+torch's current HIP stream.  No computation happens here.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import AttnDesc, LayerDesc, LayerGrads, LayerSaved, LayerWeights, check
+
+_DT = {torch.float32: _lib.HSTU_F32, torch.bfloat16: _lib.HSTU_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dev(t: Optional[torch.Tensor], name: str) -> None:
+    if t is not None and not t.is_cuda:
+        raise ValueError(f"{name} must be a device (cuda/hip) tensor")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+@dataclasses.dataclass
+class AttnConfig:
+    H: int
+    d_qk: int
+    d_v: int
+    norm_len: int = 1
+    norm_mode: int = 0
+    n_pos_buckets: int = 128
+    n_time_buckets: int = 128
+
+
+def attn_desc(cfg: AttnConfig, B: int, T: int, dtype: torch.dtype, rab_stride: int) -> AttnDesc:
+    return AttnDesc(B, T, cfg.H, cfg.d_qk, cfg.d_v, cfg.n_pos_buckets, cfg.n_time_buckets,
+                    cfg.norm_mode, cfg.norm_len, _DT[dtype], rab_stride)
+
+
+def _rab_stride(rab_pos: torch.Tensor, rab_time: torch.Tensor) -> int:
+    if rab_pos.dim() == 1:
+        if rab_time.dim() != 1:
+            raise ValueError("rab_pos and rab_time must both be shared or both per head")
+        return 0
+    if rab_pos.stride(0) != rab_time.stride(0) or rab_pos.stride(1) != 1 or rab_time.stride(1) != 1:
+        raise ValueError("per-head rab tables must share one contiguous head stride")
+    return rab_pos.stride(0)
+
+
+def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, cfg: AttnConfig,
+                  num_candidates=None, out=None, stream=None):
+    """O [T, H*d_v] of the pointwise attention (see include/hstu.h)."""
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("seq_offsets", seq_offsets),
+                   ("timestamps", timestamps), ("rab_pos", rab_pos), ("rab_time", rab_time),
+                   ("num_candidates", num_candidates)):
+        _dev(t_, n_)
+    T = q.shape[0]
+    B = seq_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, cfg.H * cfg.d_v), dtype=q.dtype, device=q.device)
+    d = attn_desc(cfg, B, T, q.dtype, _rab_stride(rab_pos, rab_time))
+    L = _lib.lib()
+    ws = _ws(L.hstu_attn_fwd_workspace_size(C.byref(d)), q.device)
+    st = L.hstu_attn_fwd(C.byref(d), _ptr(q), _ptr(k), q.stride(0), _ptr(v), v.stride(0),
+                         _ptr(seq_offsets), _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time),
+                         _ptr(num_candidates), _ptr(out), out.stride(0), _ptr(ws), ws.numel(),
+                         _stream(stream))
+    check("hstu_attn_fwd", st)
+    return out
+
+
+def hstu_attn_bwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, d_out, cfg: AttnConfig,
+                  num_candidates=None, stream=None):
+    """(dq, dk, dv, d_rab_pos, d_rab_time) for the output gradient d_out."""
+    T = q.shape[0]
+    B = seq_offsets.shape[0] - 1
+    dev = q.device
+    dq = torch.empty((T, cfg.H * cfg.d_qk), dtype=q.dtype, device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty((T, cfg.H * cfg.d_v), dtype=q.dtype, device=dev)
+    drp = torch.empty_like(rab_pos, dtype=torch.float32)
+    drt = torch.empty_like(rab_time, dtype=torch.float32)
+    d = attn_desc(cfg, B, T, q.dtype, _rab_stride(rab_pos, rab_time))
+    L = _lib.lib()
+    ws = _ws(L.hstu_attn_bwd_workspace_size(C.byref(d)), dev)
+    st = L.hstu_attn_bwd(C.byref(d), _ptr(q), _ptr(k), q.stride(0), _ptr(v), v.stride(0),
+                         _ptr(seq_offsets), _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time),
+                         _ptr(num_candidates), _ptr(d_out), d_out.stride(0), _ptr(dq), _ptr(dk),
+                         _ptr(dv), _ptr(drp), _ptr(drt), _ptr(ws), ws.numel(), _stream(stream))
+    check("hstu_attn_bwd", st)
+    return dq, dk, dv, drp, drt
+
+
+@dataclasses.dataclass
+class LayerConfig:
+    D: int
+    attn: AttnConfig
+    proj_silu: bool = True
+    residual: bool = True
+    ln_eps: float = 1e-6
+
+    @property
+    def f1(self) -> int:
+        return self.attn.H * (2 * self.attn.d_v + 2 * self.attn.d_qk)
+
+
+def layer_desc(cfg: LayerConfig, B: int, T: int, dtype, rab_stride: int) -> LayerDesc:
+    return LayerDesc(attn_desc(cfg.attn, B, T, dtype, rab_stride), cfg.D, int(cfg.proj_silu),
+                     int(cfg.residual), cfg.ln_eps)
+
+
+def _weights(W1, W2, rab_pos, rab_time, b1=None, b2=None, gamma=None, beta=None):
+    return LayerWeights(_ptr(W1), _ptr(W2), _ptr(b1), _ptr(b2), _ptr(gamma), _ptr(beta),
+                        _ptr(rab_pos), _ptr(rab_time))
+
+
+class Saved:
+    """Forward intermediates of a training step (device tensors)."""
+
+    def __init__(self, T: int, cfg: LayerConfig, dtype, device):
+        W = cfg.attn.H * cfg.attn.d_v
+        self.Z = torch.empty((T, cfg.f1), dtype=dtype, device=device)
+        self.Zh = torch.empty((T, cfg.f1), dtype=dtype, device=device)
+        self.O = torch.empty((T, W), dtype=torch.float32, device=device)
+        self.G = torch.empty((T, W), dtype=dtype, device=device)
+        self.mu = torch.empty((T,), dtype=torch.float32, device=device)
+        self.rstd = torch.empty((T,), dtype=torch.float32, device=device)
+
+    def c(self) -> LayerSaved:
+        return LayerSaved(_ptr(self.Z), _ptr(self.Zh), _ptr(self.O), _ptr(self.G),
+                          _ptr(self.mu), _ptr(self.rstd))
+
+
+class LayerWorkspace:
+    """Reusable workspace for repeated layer calls of one shape."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = _ws(nbytes, device)
+        return self.buf
+
+
+def hstu_layer_fwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: LayerConfig,
+                   num_candidates=None, b1=None, b2=None, gamma=None, beta=None,
+                   saved: Optional[Saved] = None, y=None, workspace: Optional[LayerWorkspace] = None,
+                   stream=None):
+    """Y = HSTU layer(x); fills `saved` when given (training)."""
+    T = x.shape[0]
+    B = seq_offsets.shape[0] - 1
+    if y is None:
+        y = torch.empty_like(x)
+    d = layer_desc(cfg, B, T, x.dtype, _rab_stride(rab_pos, rab_time))
+    L = _lib.lib()
+    nb = L.hstu_layer_fwd_workspace_size(C.byref(d), 1 if saved is not None else 0)
+    ws = workspace.get(nb, x.device) if workspace is not None else _ws(nb, x.device)
+    w = _weights(W1, W2, rab_pos, rab_time, b1, b2, gamma, beta)
+    sv = saved.c() if saved is not None else None
+    st = L.hstu_layer_fwd(C.byref(d), _ptr(x), C.byref(w), _ptr(seq_offsets), _ptr(timestamps),
+                          _ptr(num_candidates), _ptr(y), C.byref(sv) if sv is not None else None,
+                          _ptr(ws), ws.numel(), _stream(stream))
+    check("hstu_layer_fwd", st)
+    return y
+
+
+@dataclasses.dataclass
+class Grads:
+    dW1: torch.Tensor
+    dW2: torch.Tensor
+    drab_pos: torch.Tensor
+    drab_time: torch.Tensor
+    db1: Optional[torch.Tensor] = None
+    db2: Optional[torch.Tensor] = None
+    dgamma: Optional[torch.Tensor] = None
+    dbeta: Optional[torch.Tensor] = None
+
+
+def hstu_layer_bwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: LayerConfig,
+                   saved: Saved, dy, num_candidates=None, b1=None, b2=None, gamma=None,
+                   beta=None, dx=None, grads: Optional[Grads] = None,
+                   workspace: Optional[LayerWorkspace] = None, stream=None):
+    """(dx, Grads) of the layer for the output gradient dy."""
+    T = x.shape[0]
+    B = seq_offsets.shape[0] - 1
+    dev = x.device
+    if dx is None:
+        dx = torch.empty_like(x)
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        grads = Grads(torch.empty(W1.shape, **f32), torch.empty(W2.shape, **f32),
+                      torch.empty(rab_pos.shape, **f32), torch.empty(rab_time.shape, **f32),
+                      None if b1 is None else torch.empty(b1.shape, **f32),
+                      None if b2 is None else torch.empty(b2.shape, **f32),
+                      None if gamma is None else torch.empty(gamma.shape, **f32),
+                      None if beta is None else torch.empty(beta.shape, **f32))
+    d = layer_desc(cfg, B, T, x.dtype, _rab_stride(rab_pos, rab_time))
+    L = _lib.lib()
+    nb = L.hstu_layer_bwd_workspace_size(C.byref(d))
+    ws = workspace.get(nb, dev) if workspace is not None else _ws(nb, dev)
+    w = _weights(W1, W2, rab_pos, rab_time, b1, b2, gamma, beta)
+    g = LayerGrads(_ptr(grads.dW1), _ptr(grads.dW2), _ptr(grads.db1), _ptr(grads.db2),
+                   _ptr(grads.dgamma), _ptr(grads.dbeta), _ptr(grads.drab_pos),
+                   _ptr(grads.drab_time))
+    sv = saved.c()
+    st = L.hstu_layer_bwd(C.byref(d), _ptr(x), C.byref(w), _ptr(seq_offsets), _ptr(timestamps),
+                          _ptr(num_candidates), C.byref(sv), _ptr(dy), _ptr(dx), C.byref(g),
+                          _ptr(ws), ws.numel(), _stream(stream))
+    check("hstu_layer_bwd", st)
+    return dx, grads
+
+
+def hstu_bias_buckets(seq_offsets, timestamps, pair_seq, pair_i, pair_j, cfg: AttnConfig,
+                      num_candidates=None, stream=None):
+    """(bp, bt) int32 device tensors for the listed (sequence, query row, key row) pairs."""
+    T = timestamps.shape[0]
+    B = seq_offsets.shape[0] - 1
+    n = pair_seq.shape[0]
+    dev = timestamps.device
+    bp = torch.empty((n,), dtype=torch.int32, device=dev)
+    bt = torch.empty((n,), dtype=torch.int32, device=dev)
+    d = attn_desc(cfg, B, T, torch.bfloat16, 0)
+    L = _lib.lib()
+    ws = _ws(L.hstu_attn_fwd_workspace_size(C.byref(d)), dev)
+    st = L.hstu_bias_buckets(C.byref(d), _ptr(seq_offsets), _ptr(timestamps),
+                             _ptr(num_candidates), _ptr(pair_seq), _ptr(pair_i), _ptr(pair_j), n,
+                             _ptr(bp), _ptr(bt), _ptr(ws), ws.numel(), _stream(stream))
+    check("hstu_bias_buckets", st)
+    return bp, bt
+
+
+def hstu_schedule(seq_offsets, T: int, block_rows: int, reverse: bool = False, stream=None):
+    """(items [n, 2] int32, n) of the device-built jagged work list."""
+    B = seq_offsets.shape[0] - 1
+    dev = seq_offsets.device
+    L = _lib.lib()
+    cap = L.hstu_schedule_capacity(T, B, block_rows)
+    items = torch.full((cap, 2), -1, dtype=torch.int32, device=dev)
+    n = torch.zeros((1,), dtype=torch.int32, device=dev)
+    ws = _ws(L.hstu_schedule_workspace_size(B, T, block_rows), dev)
+    st = L.hstu_schedule(B, T, _ptr(seq_offsets), block_rows, int(reverse), _ptr(items), _ptr(n),
+                         _ptr(ws), ws.numel(), _stream(stream))
+    check("hstu_schedule", st)
+    return items, n
+
+
+def hstu_validate_inputs(seq_offsets, T: int, num_candidates=None, stream=None) -> int:
+    """Status code of the synchronous device-contract check (0 = ok)."""
+    B = seq_offsets.shape[0] - 1
+    flag = torch.zeros((1,), dtype=torch.int32, device=seq_offsets.device)
+    return _lib.lib().hstu_validate_inputs(B, T, _ptr(seq_offsets), _ptr(num_candidates),
+                                           _ptr(flag), _stream(stream))

@@ -1,0 +1,586 @@
+// C ABI of the HSTU layer library: argument checks, workspace carving and the
+// launch sequence of each entry point.  Every step of the computation runs in
+// the HIP kernels of this directory; this file only orders them on the
+// caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+using namespace hstu;
+
+namespace {
+
+#define HSTU_TRY(expr)                                  \
+  do {                                                  \
+    hipError_t e_ = (expr);                             \
+    if (e_ != hipSuccess) return HSTU_ERR_HIP;          \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+size_t esize(int dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
+
+hstu_status check_attn_desc(const hstu_attn_desc* d) {
+  if (!d) return HSTU_ERR_INVALID_ARG;
+  if (d->B < 0 || d->T < 0 || d->T >= (int64_t(1) << 31)) return HSTU_ERR_INVALID_ARG;
+  if (d->H < 1 || d->H > 64) return HSTU_ERR_UNSUPPORTED;
+  auto okd = [](int x) { return x == 32 || x == 64 || x == 128; };
+  if (!okd(d->d_qk) || !okd(d->d_v)) return HSTU_ERR_UNSUPPORTED;
+  if (d->n_pos_buckets < 1 || d->n_pos_buckets > 1024) return HSTU_ERR_UNSUPPORTED;
+  if (d->n_time_buckets < 1 || d->n_time_buckets > 1024) return HSTU_ERR_UNSUPPORTED;
+  if (d->norm_mode != 0 && d->norm_mode != 1) return HSTU_ERR_INVALID_ARG;
+  if (d->norm_mode == 0 && d->norm_len <= 0) return HSTU_ERR_INVALID_ARG;
+  if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+  if (d->rab_head_stride < 0) return HSTU_ERR_INVALID_ARG;
+  if (d->rab_head_stride != 0 &&
+      d->rab_head_stride < std::max(d->n_pos_buckets, d->n_time_buckets))
+    return HSTU_ERR_INVALID_ARG;
+  return HSTU_OK;
+}
+
+// bf16 operands are read 16 bytes at a time.
+bool stride_ok(int dtype, const void* p, int64_t ld, int64_t min_ld) {
+  if (ld < min_ld) return false;
+  if (dtype == HSTU_BF16) return aligned16(p) && (ld % 8) == 0;
+  return (reinterpret_cast<uintptr_t>(p) & 3) == 0;
+}
+
+int fwd_bm(int dtype) { return dtype == HSTU_BF16 ? ATTN_FWD_BM_BF16 : ATTN_FWD_BM_F32; }
+
+struct FwdWs {
+  TimeMeta tm;
+  Sched sc;
+};
+FwdWs carve_fwd(Carver& c, const hstu_attn_desc* d) {
+  FwdWs w;
+  w.tm = carve_time(c, d->T, d->B);
+  w.sc = carve_sched(c, d->T, d->B, fwd_bm(d->dtype));
+  return w;
+}
+
+struct BwdWs {
+  TimeMeta tm;
+  Sched kv, q;
+};
+BwdWs carve_bwd(Carver& c, const hstu_attn_desc* d) {
+  BwdWs w;
+  w.tm = carve_time(c, d->T, d->B);
+  w.kv = carve_sched(c, d->T, d->B, ATTN_BWD_BN);
+  w.q = carve_sched(c, d->T, d->B, ATTN_BWD_BM);
+  return w;
+}
+
+AttnArgs base_args(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                   const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                   const float* rp, const float* rt, const int32_t* nc, const TimeMeta& tm) {
+  AttnArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ld_qk = ld_qk;
+  a.ld_v = ld_v;
+  a.seq_offsets = offs;
+  a.num_cand = nc;
+  a.ts = ts;
+  a.rel_t = tm.rel_t;
+  a.seq_flags = tm.seq_flags;
+  a.rab_pos = rp;
+  a.rab_time = rt;
+  a.rab_stride = d->rab_head_stride;
+  a.H = d->H;
+  a.nP = d->n_pos_buckets;
+  a.nT = d->n_time_buckets;
+  a.norm_mode = d->norm_mode;
+  a.norm_len = d->norm_len;
+  return a;
+}
+
+int64_t rab_floats(const hstu_attn_desc* d) {
+  const int64_t per = std::max(d->n_pos_buckets, d->n_time_buckets);
+  return d->rab_head_stride == 0 ? per : d->rab_head_stride * (d->H - 1) + per;
+}
+
+// ---- attention forward/backward bodies (shared with the layer) -------------
+
+hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                          const float* rp, const float* rt, const int32_t* nc, void* out,
+                          int64_t ld_out, bool out_f32, void* ws, hipStream_t st) {
+  Carver c(ws);
+  FwdWs w = carve_fwd(c, d);
+  AttnArgs a = base_args(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, w.tm);
+  a.out = out;
+  a.ld_out = ld_out;
+  a.out_f32 = out_f32;
+  a.items = w.sc.items;
+  a.counters = w.sc.counters;
+  HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st));
+  HSTU_TRY(launch_sched(w.sc, d->B, offs, 0, st));
+  HSTU_TRY(launch_attn_fwd(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st));
+  return HSTU_OK;
+}
+
+hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                          const float* rp, const float* rt, const int32_t* nc, const void* dout,
+                          int64_t ld_dout, void* dq, void* dk, void* dv, float* drp, float* drt,
+                          const void* zpre, int64_t ld_z, int64_t zq, int64_t zk, int64_t zv,
+                          void* ws, hipStream_t st) {
+  Carver c(ws);
+  BwdWs w = carve_bwd(c, d);
+  AttnArgs a = base_args(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, w.tm);
+  a.dout = dout;
+  a.ld_dout = ld_dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.drab_pos = drp;
+  a.drab_time = drt;
+  a.zpre = zpre;
+  a.ld_z = ld_z;
+  a.zq_col = zq;
+  a.zk_col = zk;
+  a.zv_col = zv;
+  HSTU_TRY(launch_zero_f32(drp, rab_floats(d), st));
+  HSTU_TRY(launch_zero_f32(drt, rab_floats(d), st));
+  HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st));
+  HSTU_TRY(launch_sched(w.kv, d->B, offs, 1, st));
+  HSTU_TRY(launch_sched(w.q, d->B, offs, 0, st));
+  AttnArgs akv = a;
+  akv.items = w.kv.items;
+  akv.counters = w.kv.counters;
+  HSTU_TRY(launch_attn_bwd_dkdv(akv, d->d_qk, d->d_v, w.kv.cap, st));
+  AttnArgs aq = a;
+  aq.items = w.q.items;
+  aq.counters = w.q.counters;
+  HSTU_TRY(launch_attn_bwd_dq(aq, d->d_qk, d->d_v, w.q.cap, st));
+  return HSTU_OK;
+}
+
+// ---- layer workspace layout --------------------------------------------------
+
+int64_t f1_width(const hstu_layer_desc* L) {
+  return (int64_t)L->attn.H * (2 * L->attn.d_v + 2 * L->attn.d_qk);
+}
+
+struct LayerFwdWs {
+  void* Zh = nullptr;
+  void* O = nullptr;
+  void* G = nullptr;
+  void* attn = nullptr;
+};
+LayerFwdWs carve_layer_fwd(Carver& c, const hstu_layer_desc* L, int training) {
+  LayerFwdWs w;
+  const hstu_attn_desc* d = &L->attn;
+  const size_t es = esize(d->dtype);
+  const int64_t T = std::max<int64_t>(d->T, 1);
+  if (!training) {
+    w.Zh = c.take<char>(T * f1_width(L) * es);
+    w.O = c.take<float>(T * (int64_t)d->H * d->d_v);  // O stays fp32 up to the LayerNorm
+    w.G = c.take<char>(T * (int64_t)d->H * d->d_v * es);
+  }
+  w.attn = c.take<char>(0);
+  carve_fwd(c, d);
+  return w;
+}
+
+int splitk_for(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int64_t s = (512 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, K / 512));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 32));
+}
+
+struct LayerBwdWs {
+  void* dG = nullptr;
+  void* dO = nullptr;
+  void* dZ = nullptr;
+  float* part1 = nullptr;   // split-K partials of dW1
+  float* part2 = nullptr;   // split-K partials of dW2
+  float* colws = nullptr;   // column-sum scratch
+  float* lnpg = nullptr;    // LayerNorm partial dgamma
+  float* lnpb = nullptr;
+  void* attn = nullptr;
+  int s1 = 1, s2 = 1;
+  int64_t ln_blocks = 1;
+};
+LayerBwdWs carve_layer_bwd(Carver& c, const hstu_layer_desc* L) {
+  LayerBwdWs w;
+  const hstu_attn_desc* d = &L->attn;
+  const size_t es = esize(d->dtype);
+  const int64_t T = std::max<int64_t>(d->T, 1);
+  const int64_t W = (int64_t)d->H * d->d_v, F1 = f1_width(L), D = L->D;
+  w.dG = c.take<char>(T * W * es);
+  w.dO = c.take<char>(T * W * es);
+  w.dZ = c.take<char>(T * F1 * es);
+  w.s1 = splitk_for(D, F1, d->T);
+  w.s2 = splitk_for(W, D, d->T);
+  w.part1 = c.take<float>((int64_t)w.s1 * D * F1);
+  w.part2 = c.take<float>((int64_t)w.s2 * W * D);
+  w.colws = c.take<float>(64 * std::max<int64_t>(F1, std::max<int64_t>(D, W)));
+  w.ln_blocks = ln_bwd_part_blocks(d->T);
+  w.lnpg = c.take<float>(w.ln_blocks * W);
+  w.lnpb = c.take<float>(w.ln_blocks * W);
+  w.attn = c.take<char>(0);
+  carve_bwd(c, d);
+  return w;
+}
+
+hstu_status check_layer(const hstu_layer_desc* L) {
+  if (!L) return HSTU_ERR_INVALID_ARG;
+  hstu_status s = check_attn_desc(&L->attn);
+  if (s != HSTU_OK) return s;
+  if (L->D < 8 || L->D % 8 != 0) return HSTU_ERR_UNSUPPORTED;
+  if ((int64_t)L->attn.H * L->attn.d_v > 1024) return HSTU_ERR_UNSUPPORTED;
+  if (!(L->ln_eps >= 0.0f)) return HSTU_ERR_INVALID_ARG;
+  return HSTU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hstu_status_string(hstu_status s) {
+  switch (s) {
+    case HSTU_OK: return "ok";
+    case HSTU_ERR_INVALID_ARG: return "invalid argument";
+    case HSTU_ERR_UNSUPPORTED: return "unsupported configuration";
+    case HSTU_ERR_WORKSPACE: return "workspace too small";
+    case HSTU_ERR_HIP: return "HIP launch error";
+    case HSTU_ERR_VALIDATION: return "device-side input contract violated";
+  }
+  return "unknown status";
+}
+
+const char* hstu_version(void) { return "hstu-mi355x 0.1 (gfx950)"; }
+
+size_t hstu_attn_fwd_workspace_size(const hstu_attn_desc* d) {
+  if (check_attn_desc(d) != HSTU_OK) return 0;
+  Carver c(nullptr);
+  carve_fwd(c, d);
+  return c.off + 256;
+}
+
+size_t hstu_attn_bwd_workspace_size(const hstu_attn_desc* d) {
+  if (check_attn_desc(d) != HSTU_OK) return 0;
+  Carver c(nullptr);
+  carve_bwd(c, d);
+  return c.off + 256;
+}
+
+hstu_status hstu_attn_fwd(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                          const float* rp, const float* rt, const int32_t* nc, void* out,
+                          int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
+  hstu_status s = check_attn_desc(d);
+  if (s != HSTU_OK) return s;
+  if (d->T > 0 && (!q || !k || !v || !out || !ts)) return HSTU_ERR_INVALID_ARG;
+  if (!offs || !rp || !rt || !ws) return HSTU_ERR_INVALID_ARG;
+  const int64_t hq = (int64_t)d->H * d->d_qk, hv = (int64_t)d->H * d->d_v;
+  if (d->T > 0 && (!stride_ok(d->dtype, q, ld_qk, hq) || !stride_ok(d->dtype, k, ld_qk, hq) ||
+                   !stride_ok(d->dtype, v, ld_v, hv) || ld_out < hv))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_attn_fwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
+  return attn_fwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, false, ws,
+                       (hipStream_t)stream);
+}
+
+hstu_status hstu_attn_bwd(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                          const float* rp, const float* rt, const int32_t* nc, const void* dout,
+                          int64_t ld_dout, void* dq, void* dk, void* dv, float* drp, float* drt,
+                          void* ws, size_t ws_bytes, void* stream) {
+  hstu_status s = check_attn_desc(d);
+  if (s != HSTU_OK) return s;
+  if (d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+  if (d->T > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv || !ts))
+    return HSTU_ERR_INVALID_ARG;
+  if (!offs || !rp || !rt || !drp || !drt || !ws) return HSTU_ERR_INVALID_ARG;
+  const int64_t hq = (int64_t)d->H * d->d_qk, hv = (int64_t)d->H * d->d_v;
+  if (d->T > 0 && (!stride_ok(d->dtype, q, ld_qk, hq) || !stride_ok(d->dtype, k, ld_qk, hq) ||
+                   !stride_ok(d->dtype, v, ld_v, hv) || !stride_ok(d->dtype, dout, ld_dout, hv)))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_attn_bwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
+  return attn_bwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, dout, ld_dout, dq, dk, dv,
+                       drp, drt, nullptr, 0, 0, 0, 0, ws, (hipStream_t)stream);
+}
+
+size_t hstu_layer_fwd_workspace_size(const hstu_layer_desc* L, int training) {
+  if (check_layer(L) != HSTU_OK) return 0;
+  Carver c(nullptr);
+  carve_layer_fwd(c, L, training);
+  return c.off + 256;
+}
+
+size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* L) {
+  if (check_layer(L) != HSTU_OK) return 0;
+  Carver c(nullptr);
+  carve_layer_bwd(c, L);
+  return c.off + 256;
+}
+
+hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
+                           const int32_t* offs, const int64_t* ts, const int32_t* nc, void* y,
+                           const hstu_layer_saved* saved, void* ws, size_t ws_bytes,
+                           void* stream) {
+  hstu_status s = check_layer(L);
+  if (s != HSTU_OK) return s;
+  const hstu_attn_desc* d = &L->attn;
+  if (!w || !w->W1 || !w->W2 || !w->rab_pos || !w->rab_time || !offs || !ws)
+    return HSTU_ERR_INVALID_ARG;
+  if (d->T > 0 && (!x || !y || !ts)) return HSTU_ERR_INVALID_ARG;
+  if (x == y && d->T > 0) return HSTU_ERR_INVALID_ARG;
+  if (saved && (!saved->Z || !saved->Zh || !saved->O || !saved->G || !saved->mu || !saved->rstd))
+    return HSTU_ERR_INVALID_ARG;
+  if (d->dtype == HSTU_BF16) {
+    if (!aligned16(x) || !aligned16(y) || !aligned16(w->W1) || !aligned16(w->W2))
+      return HSTU_ERR_INVALID_ARG;
+    if (saved && (!aligned16(saved->Z) || !aligned16(saved->Zh) || !aligned16(saved->G)))
+      return HSTU_ERR_INVALID_ARG;
+  }
+  if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_layer_fwd_workspace_size(L, saved != nullptr)) return HSTU_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+
+  Carver c(ws);
+  LayerFwdWs lw = carve_layer_fwd(c, L, saved != nullptr);
+  const int64_t T = d->T, D = L->D, F1 = f1_width(L);
+  const int64_t W = (int64_t)d->H * d->d_v, HQ = (int64_t)d->H * d->d_qk;
+  void* Zh = saved ? saved->Zh : lw.Zh;
+  void* O = saved ? saved->O : lw.O;
+  void* G = saved ? saved->G : lw.G;
+  const size_t es = esize(d->dtype);
+  char* zh = static_cast<char*>(Zh);
+
+  // 1. Z = X W1 (+ b1); Zh = SiLU(Z)
+  GemmArgs g1;
+  g1.M = T;
+  g1.N = F1;
+  g1.K = D;
+  g1.A = x;
+  g1.lda = D;
+  g1.a_kcont = true;
+  g1.B = w->W1;
+  g1.ldb = F1;
+  g1.b_kcont = false;
+  g1.C = Zh;
+  g1.ldc = F1;
+  g1.bias = w->b1;
+  if (L->proj_silu) {
+    g1.epi = EPI_SILU;
+    g1.C2 = saved ? saved->Z : nullptr;
+  } else {
+    g1.epi = EPI_RESID;  // bias only
+    g1.R = nullptr;
+  }
+  HSTU_TRY(launch_gemm(g1, d->dtype, st));
+  if (!L->proj_silu && saved) {
+    // without the nonlinearity Z and Zh coincide
+    GemmArgs gz = g1;
+    gz.C = saved->Z;
+    HSTU_TRY(launch_gemm(gz, d->dtype, st));
+  }
+  // 2. attention on the V, Q, K column blocks
+  s = attn_fwd_impl(d, zh + 2 * W * es, zh + (2 * W + HQ) * es, F1, zh + W * es, F1, offs, ts,
+                    w->rab_pos, w->rab_time, nc, O, W, /*out_f32=*/true, lw.attn, st);
+  if (s != HSTU_OK) return s;
+  // 3. G = LN(O) * U
+  LnArgs la;
+  la.o_f32 = true;
+  la.T = T;
+  la.W = (int)W;
+  la.O = O;
+  la.ld_o = W;
+  la.U = Zh;
+  la.ld_u = F1;
+  la.gamma = w->ln_gamma;
+  la.beta = w->ln_beta;
+  la.eps = L->ln_eps;
+  la.G = G;
+  la.ld_g = W;
+  la.mu = saved ? saved->mu : nullptr;
+  la.rstd = saved ? saved->rstd : nullptr;
+  HSTU_TRY(launch_ln_gate_fwd(la, d->dtype, st));
+  // 4. Y = G W2 (+ b2) (+ X)
+  GemmArgs g2;
+  g2.M = T;
+  g2.N = D;
+  g2.K = W;
+  g2.A = G;
+  g2.lda = W;
+  g2.a_kcont = true;
+  g2.B = w->W2;
+  g2.ldb = D;
+  g2.b_kcont = false;
+  g2.C = y;
+  g2.ldc = D;
+  g2.epi = EPI_RESID;
+  g2.bias = w->b2;
+  g2.R = L->residual ? x : nullptr;
+  g2.ldr = D;
+  HSTU_TRY(launch_gemm(g2, d->dtype, st));
+  return HSTU_OK;
+}
+
+hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
+                           const int32_t* offs, const int64_t* ts, const int32_t* nc,
+                           const hstu_layer_saved* saved, const void* dy, void* dx,
+                           const hstu_layer_grads* g, void* ws, size_t ws_bytes, void* stream) {
+  hstu_status s = check_layer(L);
+  if (s != HSTU_OK) return s;
+  const hstu_attn_desc* d = &L->attn;
+  if (d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+  if (!w || !w->W1 || !w->W2 || !w->rab_pos || !w->rab_time || !offs || !ws || !g || !saved)
+    return HSTU_ERR_INVALID_ARG;
+  if (!saved->Z || !saved->Zh || !saved->O || !saved->G || !saved->mu || !saved->rstd)
+    return HSTU_ERR_INVALID_ARG;
+  if (!g->dW1 || !g->dW2 || !g->drab_pos || !g->drab_time) return HSTU_ERR_INVALID_ARG;
+  if ((w->b1 && !g->db1) || (w->b2 && !g->db2) || (w->ln_gamma && !g->dgamma) ||
+      (w->ln_beta && !g->dbeta))
+    return HSTU_ERR_INVALID_ARG;
+  if (d->T > 0 && (!x || !dy || !dx || !ts)) return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(w->W1) ||
+      !aligned16(w->W2) || !aligned16(saved->Z) || !aligned16(saved->Zh) ||
+      !aligned16(saved->O) || !aligned16(saved->G) || !aligned16(ws))
+    return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_layer_bwd_workspace_size(L)) return HSTU_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+
+  Carver c(ws);
+  LayerBwdWs bw = carve_layer_bwd(c, L);
+  const int64_t T = d->T, D = L->D, F1 = f1_width(L);
+  const int64_t W = (int64_t)d->H * d->d_v, HQ = (int64_t)d->H * d->d_qk;
+  const size_t es = esize(d->dtype);
+  char* dz = static_cast<char*>(bw.dZ);
+  const char* zh = static_cast<const char*>(saved->Zh);
+  const void* zpre = L->proj_silu ? saved->Z : nullptr;
+
+  // 1. dG = dY W2^T
+  GemmArgs a1;
+  a1.M = T; a1.N = W; a1.K = D;
+  a1.A = dy; a1.lda = D; a1.a_kcont = true;
+  a1.B = w->W2; a1.ldb = D; a1.b_kcont = true;
+  a1.C = bw.dG; a1.ldc = W;
+  a1.epi = EPI_STORE;
+  HSTU_TRY(launch_gemm(a1, d->dtype, st));
+  // 2. dW2 = G^T dY (split over T)
+  GemmArgs a2;
+  a2.M = W; a2.N = D; a2.K = T;
+  a2.A = saved->G; a2.lda = W; a2.a_kcont = false;
+  a2.B = dy; a2.ldb = D; a2.b_kcont = false;
+  a2.epi = EPI_PARTIAL; a2.split_k = bw.s2; a2.partial = bw.part2;
+  HSTU_TRY(launch_gemm(a2, d->dtype, st));
+  HSTU_TRY(launch_splitk_reduce(bw.part2, bw.s2, W, D, g->dW2, D, st));
+  if (w->b2) HSTU_TRY(launch_colsum(dy, T, D, D, d->dtype, g->db2, bw.colws, st));
+  // 3. LayerNorm + gate backward: dU (into dZ's U block, times SiLU'(Z)), dO
+  LnArgs la;
+  la.o_f32 = true;
+  la.T = T; la.W = (int)W;
+  la.O = saved->O; la.ld_o = W;
+  la.U = saved->Zh; la.ld_u = F1;
+  la.gamma = w->ln_gamma; la.beta = w->ln_beta; la.eps = L->ln_eps;
+  la.mu = saved->mu; la.rstd = saved->rstd;
+  la.dG = bw.dG; la.ld_dg = W;
+  la.dU = dz; la.ld_du = F1;
+  la.zu = zpre; la.ld_zu = F1;
+  la.dO = bw.dO; la.ld_do = W;
+  la.dgamma_part = w->ln_gamma ? bw.lnpg : nullptr;
+  la.dbeta_part = w->ln_beta ? bw.lnpb : nullptr;
+  la.n_part_blocks = bw.ln_blocks;
+  HSTU_TRY(launch_ln_gate_bwd(la, d->dtype, st));
+  if (w->ln_gamma)
+    HSTU_TRY(launch_colsum(bw.lnpg, bw.ln_blocks, W, W, HSTU_F32, g->dgamma, bw.colws, st));
+  if (w->ln_beta)
+    HSTU_TRY(launch_colsum(bw.lnpb, bw.ln_blocks, W, W, HSTU_F32, g->dbeta, bw.colws, st));
+  // 4. attention backward into dZ's V, Q, K blocks (times SiLU'(Z))
+  s = attn_bwd_impl(d, zh + 2 * W * es, zh + (2 * W + HQ) * es, F1, zh + W * es, F1, offs, ts,
+                    w->rab_pos, w->rab_time, nc, bw.dO, W, dz + 2 * W * es,
+                    dz + (2 * W + HQ) * es, dz + W * es, g->drab_pos, g->drab_time, zpre, F1,
+                    2 * W, 2 * W + HQ, W, bw.attn, st);
+  if (s != HSTU_OK) return s;
+  // 5. dW1 = X^T dZ (split over T), db1
+  GemmArgs a3;
+  a3.M = D; a3.N = F1; a3.K = T;
+  a3.A = x; a3.lda = D; a3.a_kcont = false;
+  a3.B = dz; a3.ldb = F1; a3.b_kcont = false;
+  a3.epi = EPI_PARTIAL; a3.split_k = bw.s1; a3.partial = bw.part1;
+  HSTU_TRY(launch_gemm(a3, d->dtype, st));
+  HSTU_TRY(launch_splitk_reduce(bw.part1, bw.s1, D, F1, g->dW1, F1, st));
+  if (w->b1) HSTU_TRY(launch_colsum(dz, T, F1, F1, d->dtype, g->db1, bw.colws, st));
+  // 6. dX = dZ W1^T (+ dY)
+  GemmArgs a4;
+  a4.M = T; a4.N = D; a4.K = F1;
+  a4.A = dz; a4.lda = F1; a4.a_kcont = true;
+  a4.B = w->W1; a4.ldb = F1; a4.b_kcont = true;
+  a4.C = dx; a4.ldc = D;
+  a4.epi = EPI_RESID;
+  a4.R = L->residual ? dy : nullptr; a4.ldr = D;
+  HSTU_TRY(launch_gemm(a4, d->dtype, st));
+  return HSTU_OK;
+}
+
+size_t hstu_schedule_workspace_size(int32_t B, int64_t T, int32_t block_rows) {
+  if (B < 0 || T < 0 || block_rows < 1) return 0;
+  Carver c(nullptr);
+  carve_sched(c, T, B, block_rows);
+  return c.off + 256;
+}
+
+int64_t hstu_schedule_capacity(int64_t T, int32_t B, int32_t block_rows) {
+  if (B < 0 || T < 0 || block_rows < 1) return 0;
+  return sched_capacity(T, B, block_rows);
+}
+
+hstu_status hstu_schedule(int32_t B, int64_t T, const int32_t* offs, int32_t block_rows,
+                          int32_t reverse, int32_t* items, int32_t* n_items, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (B < 0 || T < 0 || T >= (int64_t(1) << 31) || block_rows < 1 || !offs || !items ||
+      !n_items || !ws)
+    return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_schedule_workspace_size(B, T, block_rows)) return HSTU_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(ws);
+  Sched sc = carve_sched(c, T, B, block_rows);
+  HSTU_TRY(launch_sched(sc, B, offs, reverse, st));
+  HSTU_TRY(hipMemcpyAsync(items, sc.items, sizeof(int32_t) * 2 * sc.cap,
+                          hipMemcpyDeviceToDevice, st));
+  HSTU_TRY(hipMemcpyAsync(n_items, sc.counters, sizeof(int32_t), hipMemcpyDeviceToDevice, st));
+  return HSTU_OK;
+}
+
+hstu_status hstu_bias_buckets(const hstu_attn_desc* d, const int32_t* offs, const int64_t* ts,
+                              const int32_t* nc, const int32_t* ps, const int32_t* pi,
+                              const int32_t* pj, int64_t n_pairs, int32_t* bp, int32_t* bt,
+                              void* ws, size_t ws_bytes, void* stream) {
+  hstu_status s = check_attn_desc(d);
+  if (s != HSTU_OK) return s;
+  if (!offs || !ws || n_pairs < 0) return HSTU_ERR_INVALID_ARG;
+  if (n_pairs > 0 && (!ts || !ps || !pi || !pj || !bp || !bt)) return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_attn_fwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(ws);
+  FwdWs w = carve_fwd(c, d);
+  AttnArgs a = base_args(d, nullptr, nullptr, 0, nullptr, 0, offs, ts, nullptr, nullptr, nc, w.tm);
+  HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st));
+  HSTU_TRY(launch_bias_buckets(a, ps, pi, pj, n_pairs, bp, bt, st));
+  return HSTU_OK;
+}
+
+hstu_status hstu_validate_inputs(int32_t B, int64_t T, const int32_t* offs, const int32_t* nc,
+                                 int32_t* flag_ws, void* stream) {
+  if (B < 0 || T < 0 || !offs || !flag_ws) return HSTU_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  HSTU_TRY(launch_zero_i32(flag_ws, 1, st));
+  HSTU_TRY(launch_validate(B, offs, nc, T, flag_ws, st));
+  int32_t h = 0;
+  HSTU_TRY(hipMemcpyAsync(&h, flag_ws, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+  HSTU_TRY(hipStreamSynchronize(st));
+  return h ? HSTU_ERR_VALIDATION : HSTU_OK;
+}
+
+}  // extern "C"

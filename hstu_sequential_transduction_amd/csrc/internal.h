@@ -1,0 +1,177 @@
+// Host-side declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hstu.h"
+
+namespace hstu {
+
+// Bump allocator over the caller's workspace.  With base == nullptr it only
+// measures, so the *_workspace_size functions and the entry points share one
+// carving routine.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+// Jagged work list of (sequence, row block) items.
+struct Sched {
+  int32_t* items = nullptr;     // [2*cap]
+  int32_t* counters = nullptr;  // [0] items, [1] max blocks per sequence
+  int32_t* hist = nullptr;      // [cap+2] sequences per block count
+  int32_t* cnt = nullptr;       // [cap+2] sequences with more than m blocks
+  int32_t* levelstart = nullptr;// [cap+2]
+  int32_t* tie = nullptr;       // [cap+2]
+  int64_t cap = 0;
+  int block_rows = 0;
+};
+
+inline int64_t sched_capacity(int64_t T, int64_t B, int block_rows) {
+  return (T + B * (int64_t)(block_rows - 1)) / block_rows + 1;
+}
+Sched carve_sched(Carver& c, int64_t T, int64_t B, int block_rows);
+hipError_t launch_sched(const Sched& s, int B, const int32_t* seq_offsets, int reverse,
+                        hipStream_t st);
+
+// Per-token relative timestamps and per-sequence flags.
+struct TimeMeta {
+  int32_t* rel_t = nullptr;      // [T] t - min_t of the sequence (valid when not wide)
+  int32_t* seq_flags = nullptr;  // [B] bit0: span >= 2^31 ("wide"), bit1: non-decreasing
+};
+TimeMeta carve_time(Carver& c, int64_t T, int64_t B);
+hipError_t launch_time_prepass(const TimeMeta& tm, int B, const int32_t* seq_offsets,
+                               const int64_t* ts, hipStream_t st);
+
+struct AttnArgs {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t ld_qk = 0, ld_v = 0;
+  void* out = nullptr;
+  int64_t ld_out = 0;
+  bool out_f32 = false;   // bf16 kernels: store O in fp32 (the layer keeps O in fp32 for the LayerNorm)
+  const int32_t* seq_offsets = nullptr;
+  const int32_t* num_cand = nullptr;
+  const int64_t* ts = nullptr;
+  const int32_t* rel_t = nullptr;
+  const int32_t* seq_flags = nullptr;
+  const int32_t* items = nullptr;
+  const int32_t* counters = nullptr;
+  const float* rab_pos = nullptr;
+  const float* rab_time = nullptr;
+  int64_t rab_stride = 0;
+  int H = 0, nP = 0, nT = 0, norm_mode = 0, norm_len = 1;
+  // backward
+  const void* dout = nullptr;
+  int64_t ld_dout = 0;
+  void* dq = nullptr;
+  void* dk = nullptr;
+  void* dv = nullptr;
+  float* drab_pos = nullptr;
+  float* drab_time = nullptr;
+  // Optional pre-activation Z: gradients are multiplied by SiLU'(Z) before
+  // they are stored (the layer backward's dZ = dZh * SiLU'(Z)).
+  const void* zpre = nullptr;
+  int64_t ld_z = 0;
+  int64_t zq_col = 0, zk_col = 0, zv_col = 0;
+};
+
+// Row-block sizes of the kernels (rows of Q per forward work item, keys per
+// backward key-block work item).
+constexpr int ATTN_FWD_BM_BF16 = 128;
+constexpr int ATTN_FWD_BM_F32 = 64;
+constexpr int ATTN_BWD_BN = 128;   // keys per dK/dV work item
+constexpr int ATTN_BWD_BM = 128;   // queries per dQ work item
+
+hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, int d_qk, int d_v,
+                           int64_t max_items, hipStream_t st);
+hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, int d_qk, int d_v, int64_t max_items,
+                                hipStream_t st);
+hipError_t launch_attn_bwd_dq(const AttnArgs& a, int d_qk, int d_v, int64_t max_items,
+                              hipStream_t st);
+hipError_t launch_bias_buckets(const AttnArgs& a, const int32_t* pair_seq,
+                               const int32_t* pair_i, const int32_t* pair_j, int64_t n,
+                               int32_t* bp, int32_t* bt, hipStream_t st);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st);
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t st);
+
+// GEMM: C[M,N] = sum_k A(m,k) B(k,n), epilogue below.
+//  a_kcont: A(m,k) at A[m*lda + k] (else A[k*lda + m]);
+//  b_kcont: B(k,n) at B[n*ldb + k] (else B[k*ldb + n]).
+enum GemmEpi {
+  EPI_STORE = 0,    // C = acc
+  EPI_SILU = 1,     // Z = acc + bias; C2 = Z (optional); C = SiLU(Z)  (bf16)
+  EPI_RESID = 2,    // C = acc + bias + R
+  EPI_PARTIAL = 3,  // fp32 partial sums of a split-K slice -> ws[z][M][N]
+};
+struct GemmArgs {
+  int64_t M = 0, N = 0, K = 0;
+  const void* A = nullptr;
+  int64_t lda = 0;
+  bool a_kcont = true;
+  const void* B = nullptr;
+  int64_t ldb = 0;
+  bool b_kcont = true;
+  void* C = nullptr;
+  int64_t ldc = 0;
+  bool c_f32 = false;     // output fp32 (else dtype of inputs)
+  void* C2 = nullptr;     // EPI_SILU: pre-activation output (may be null)
+  const float* bias = nullptr;  // [N] or null
+  const void* R = nullptr;      // EPI_RESID residual, same dtype as C, row stride ldr
+  int64_t ldr = 0;
+  int epi = EPI_STORE;
+  int split_k = 1;
+  float* partial = nullptr;     // EPI_PARTIAL workspace [split_k][M][N]
+};
+hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st);
+// Split-K reduction: out[m*ldo + n] = sum_z partial[z][m][n]  (fp32)
+hipError_t launch_splitk_reduce(const float* partial, int split, int64_t M, int64_t N,
+                                float* out, int64_t ldo, hipStream_t st);
+// Column sums over rows of a [rows, cols] matrix (dtype) -> fp32 out[cols].
+hipError_t launch_colsum(const void* x, int64_t rows, int64_t cols, int64_t ld, int dtype,
+                         float* out, float* ws, hipStream_t st);
+
+// LayerNorm + gating.
+struct LnArgs {
+  bool o_f32 = false;        // O (and its saved copy) is fp32 regardless of the layer dtype
+  int64_t T = 0;
+  int W = 0;                 // H*d_v
+  const void* O = nullptr;   // [T, W] stride ld_o
+  int64_t ld_o = 0;
+  const void* U = nullptr;   // [T, W] stride ld_u
+  int64_t ld_u = 0;
+  const float* gamma = nullptr;
+  const float* beta = nullptr;
+  float eps = 1e-6f;
+  void* G = nullptr;         // [T, W] stride ld_g
+  int64_t ld_g = 0;
+  float* mu = nullptr;       // [T] or null
+  float* rstd = nullptr;     // [T] or null
+  // backward
+  const void* dG = nullptr;  int64_t ld_dg = 0;
+  void* dU = nullptr;        int64_t ld_du = 0;   // written as dU * SiLU'(Zu) if zu != null
+  const void* zu = nullptr;  int64_t ld_zu = 0;
+  void* dO = nullptr;        int64_t ld_do = 0;
+  float* dgamma_part = nullptr;  // [blocks][W] partial column sums (or null)
+  float* dbeta_part = nullptr;
+  int64_t n_part_blocks = 0;
+};
+hipError_t launch_ln_gate_fwd(const LnArgs& a, int dtype, hipStream_t st);
+hipError_t launch_ln_gate_bwd(const LnArgs& a, int dtype, hipStream_t st);
+int64_t ln_bwd_part_blocks(int64_t T);
+
+hipError_t launch_validate(int B, const int32_t* seq_offsets, const int32_t* num_cand,
+                           int64_t T, int32_t* flag, hipStream_t st);
+
+}  // namespace hstu

@@ -1,0 +1,258 @@
+/*
+ * hstu.h -- C ABI of the HSTU layer library for MI355X (gfx950).
+ *
+ * The HSTU layer works on jagged, timestamp-ordered user-history sequences:
+ * a projection into U, V, Q, K; pointwise attention SiLU(Q K^T + relative
+ * bias) with no softmax; a gated output LayerNorm(A V) * U; and an output
+ * projection.  Pages this interface follows:
+ *   [GR]     NVIDIA generative-recommenders summary (quantumzeitgeist.com),
+ *            section "HSTU Architecture: Efficient Attention for User History":
+ *            SiLU weighting instead of softmax, relative attention bias,
+ *            elementwise gating before the output projection.
+ *   [DLRMv4] "DLRMv4 Brings Sequence-Based Recommendation Training to MLPerf"
+ *            (xfinit.ro): "Model Architecture" (projection, pointwise
+ *            attention with positional and temporal-distance bias, gated
+ *            transformation; candidate appended to the history and processed
+ *            in one causal pass), "HSTU Hyperparameters" (jagged attention,
+ *            bf16), "Computation Cost Analysis" Table 7 (U|V|Q|K width
+ *            h*(2*d_qk + 2*d_v); only the lower triangle is evaluated).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Packed jagged layout: sequence b owns rows seq_offsets[b] .. seq_offsets[b+1]-1
+ *   of every [T, ...] tensor.  seq_offsets is int32 [B+1] in device memory,
+ *   non-decreasing, seq_offsets[0] = 0, seq_offsets[B] = T.  Empty sequences
+ *   are allowed.
+ * - timestamps: int64 [T] seconds, device memory.  Within a sequence they are
+ *   expected to be non-decreasing; a negative distance is treated as 0.
+ * - num_candidates: int32 [B] device memory or NULL (no candidates).  The last
+ *   num_candidates[b] rows of sequence b are candidates; 0 <= c_b <= n_b.
+ *   A history row attends to itself and earlier history rows; a candidate row
+ *   attends to the whole history and to itself only.
+ * - Relative bias for a query row i and key row j of one sequence (n_h =
+ *   history length, p(i) = min(i, n_h)):
+ *     bp = min(p(i) - p(j), n_pos_buckets - 1)
+ *     bt = min(floor(log2(dt + 1)), n_time_buckets - 1),
+ *          dt = min(max(t_i - t_j, 0), 2^31 - 1)
+ *     bias = rab_pos[h][bp] + rab_time[h][bt]
+ *   rab_pos/rab_time are fp32, head h's table starts at h * rab_head_stride
+ *   floats (rab_head_stride = 0: one table shared by all heads).
+ * - Attention weight a_ij = SiLU(q_i . k_j + bias) / N for allowed pairs, with
+ *   N = norm_len (norm_mode 0) or the sequence's own length n_b (norm_mode 1).
+ * - Heads are contiguous inside a row: element (row r, head h, channel c) of
+ *   Q is at q[r * ld_qk + h * d_qk + c].
+ * - dtype HSTU_BF16: activations and weights bf16, fp32 accumulation, bf16
+ *   results rounded to nearest even.  HSTU_F32: fp32 throughout.
+ * - Every pointer is device memory owned by the caller.  The library never
+ *   allocates or frees device memory; scratch space is the caller's workspace
+ *   (16-byte aligned, size from the *_workspace_size functions).  All calls
+ *   are asynchronous on `stream` (a hipStream_t passed as void*, NULL = the
+ *   default stream) and never synchronise.  Outputs are fully overwritten.
+ * - Errors: only host-visible arguments are validated (NULL required
+ *   pointers, unsupported sizes, misaligned pointers or strides, workspace
+ *   too small).  On such an error nothing is launched and nothing is written.
+ *   Launch failures return HSTU_ERR_HIP.  Device-side contracts (offsets,
+ *   candidate counts, timestamps) are the caller's; hstu_validate_inputs
+ *   checks them synchronously.
+ * - Supported sizes: d_qk, d_v in {32, 64, 128}; 1 <= H <= 64; T < 2^31;
+ *   1 <= n_pos_buckets, n_time_buckets <= 1024; bf16 row strides multiples of
+ *   8 elements (fp32: 4) and 16-byte aligned base pointers.
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = -1,
+  HSTU_ERR_UNSUPPORTED = -2,
+  HSTU_ERR_WORKSPACE = -3,
+  HSTU_ERR_HIP = -4,
+  HSTU_ERR_VALIDATION = -5
+} hstu_status;
+
+typedef enum { HSTU_F32 = 0, HSTU_BF16 = 1 } hstu_dtype;
+
+/* Shape and options of one pointwise-attention call. */
+typedef struct {
+  int32_t B;               /* sequences */
+  int64_t T;               /* packed rows = seq_offsets[B] */
+  int32_t H;               /* heads */
+  int32_t d_qk;            /* query/key channels per head */
+  int32_t d_v;             /* value channels per head */
+  int32_t n_pos_buckets;   /* entries per position table (e.g. 128) */
+  int32_t n_time_buckets;  /* entries per time table (e.g. 128) */
+  int32_t norm_mode;       /* 0: divide by norm_len; 1: divide by n_b */
+  int32_t norm_len;        /* N for norm_mode 0 (> 0) */
+  int32_t dtype;           /* hstu_dtype */
+  int64_t rab_head_stride; /* floats between heads' tables; 0 = shared */
+} hstu_attn_desc;
+
+/* One layer: attention options plus model width and layer flags. */
+typedef struct {
+  hstu_attn_desc attn;
+  int32_t D;          /* model width (rows of W1, columns of W2) */
+  int32_t proj_silu;  /* 1: U|V|Q|K = SiLU(X W1 + b1); 0: no nonlinearity */
+  int32_t residual;   /* 1: Y = X + G W2 + b2; 0: Y = G W2 + b2 */
+  float ln_eps;       /* LayerNorm epsilon (e.g. 1e-6) */
+} hstu_layer_desc;
+
+/* Weights of one layer (device memory, caller-owned). */
+typedef struct {
+  const void* W1;        /* [D, F1] row-major, dtype; F1 = H*(2*d_v + 2*d_qk), columns U|V|Q|K */
+  const void* W2;        /* [H*d_v, D] row-major, dtype */
+  const float* b1;       /* [F1] fp32 or NULL */
+  const float* b2;       /* [D] fp32 or NULL */
+  const float* ln_gamma; /* [H*d_v] fp32 or NULL (1) */
+  const float* ln_beta;  /* [H*d_v] fp32 or NULL (0) */
+  const float* rab_pos;  /* position tables, see conventions */
+  const float* rab_time; /* time tables, see conventions */
+} hstu_layer_weights;
+
+/* Forward intermediates a training step keeps for the backward pass. */
+typedef struct {
+  void* Z;     /* [T, F1] dtype: X W1 + b1 before the SiLU */
+  void* Zh;    /* [T, F1] dtype: U|V|Q|K after the SiLU */
+  float* O;    /* [T, H*d_v] fp32: attention output (kept in fp32 for the LayerNorm, whose
+                  mean subtraction would otherwise cancel the bits bf16 keeps) */
+  void* G;     /* [T, H*d_v] dtype: LayerNorm(O) * U */
+  float* mu;   /* [T] LayerNorm mean */
+  float* rstd; /* [T] LayerNorm 1/sqrt(var + eps) */
+} hstu_layer_saved;
+
+/* Gradients of one layer's parameters (fp32, overwritten). */
+typedef struct {
+  float* dW1;       /* [D, F1] */
+  float* dW2;       /* [H*d_v, D] */
+  float* db1;       /* [F1], required iff b1 != NULL */
+  float* db2;       /* [D], required iff b2 != NULL */
+  float* dgamma;    /* [H*d_v], required iff ln_gamma != NULL */
+  float* dbeta;     /* [H*d_v], required iff ln_beta != NULL */
+  float* drab_pos;  /* same shape as rab_pos (H tables, or 1 if shared) */
+  float* drab_time; /* same shape as rab_time */
+} hstu_layer_grads;
+
+const char* hstu_status_string(hstu_status s);
+/* Library version string. */
+const char* hstu_version(void);
+
+/* ---- pointwise attention ------------------------------------------------ */
+
+size_t hstu_attn_fwd_workspace_size(const hstu_attn_desc* desc);
+size_t hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc);
+
+/*
+ * O = pointwise attention of Q, K, V ([GR] and [DLRMv4] "Model Architecture";
+ * lower triangle only per [DLRMv4] Table 7's note).
+ * q, k: rows of stride ld_qk; v: rows of stride ld_v (elements), so the three
+ * may be column views into one U|V|Q|K projection buffer.
+ * out: [T, H*d_v] rows of stride ld_out.
+ */
+hstu_status hstu_attn_fwd(const hstu_attn_desc* desc,
+                          const void* q, const void* k, int64_t ld_qk,
+                          const void* v, int64_t ld_v,
+                          const int32_t* seq_offsets, const int64_t* timestamps,
+                          const float* rab_pos, const float* rab_time,
+                          const int32_t* num_candidates,
+                          void* out, int64_t ld_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gradients of hstu_attn_fwd for the output gradient d_out ([T, H*d_v],
+ * stride ld_out).  dq, dk (stride ld_qk) and dv (stride ld_v) are written in
+ * dtype; d_rab_pos / d_rab_time (fp32, same shape as the tables) are
+ * overwritten.  bf16 only.
+ */
+hstu_status hstu_attn_bwd(const hstu_attn_desc* desc,
+                          const void* q, const void* k, int64_t ld_qk,
+                          const void* v, int64_t ld_v,
+                          const int32_t* seq_offsets, const int64_t* timestamps,
+                          const float* rab_pos, const float* rab_time,
+                          const int32_t* num_candidates,
+                          const void* d_out, int64_t ld_out,
+                          void* dq, void* dk, void* dv,
+                          float* d_rab_pos, float* d_rab_time,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- whole layer ------------------------------------------------------------ */
+
+/* training != 0: the forward keeps its intermediates in a caller `saved`. */
+size_t hstu_layer_fwd_workspace_size(const hstu_layer_desc* desc, int training);
+size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc);
+
+/*
+ * Y = HSTU layer(X) ([DLRMv4] "Model Architecture"; [GR]).  x, y: [T, D]
+ * dtype, contiguous rows; y may not alias x.  saved == NULL: inference
+ * (intermediates live in the workspace); otherwise every saved buffer is
+ * required and written.
+ */
+hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x,
+                           const hstu_layer_weights* w,
+                           const int32_t* seq_offsets, const int64_t* timestamps,
+                           const int32_t* num_candidates,
+                           void* y, const hstu_layer_saved* saved,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of hstu_layer_fwd given dy ([T, D] dtype): dx ([T, D] dtype) and
+ * every parameter gradient in g (fp32, overwritten).  `saved` must hold the
+ * intermediates of the matching training forward.  bf16 only.
+ */
+hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const void* x,
+                           const hstu_layer_weights* w,
+                           const int32_t* seq_offsets, const int64_t* timestamps,
+                           const int32_t* num_candidates,
+                           const hstu_layer_saved* saved, const void* dy,
+                           void* dx, const hstu_layer_grads* g,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- inspection entry points (tests, debugging) ------------------------- */
+
+/*
+ * Relative-bias buckets computed by the same device code the attention
+ * kernels use: for each listed pair (sequence pair_seq[p], local query row
+ * pair_i[p], local key row pair_j[p]) writes bp[p], bt[p] (int32).  The pair
+ * must lie inside its sequence.  All arrays are device memory.
+ */
+hstu_status hstu_bias_buckets(const hstu_attn_desc* desc,
+                              const int32_t* seq_offsets, const int64_t* timestamps,
+                              const int32_t* num_candidates,
+                              const int32_t* pair_seq, const int32_t* pair_i,
+                              const int32_t* pair_j, int64_t n_pairs,
+                              int32_t* bp, int32_t* bt,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The jagged work list the forward attention uses for row blocks of
+ * `block_rows` rows: items[2*w] = sequence, items[2*w+1] = block index, for
+ * w < *n_items, ordered by decreasing block cost; *n_items (device int32)
+ * receives the count.  items must hold hstu_schedule_capacity(...) pairs.
+ * reverse != 0 orders blocks by increasing index instead (key-block-major
+ * backward, where earlier blocks are the heavier ones).
+ */
+int64_t hstu_schedule_capacity(int64_t T, int32_t B, int32_t block_rows);
+hstu_status hstu_schedule(int32_t B, int64_t T, const int32_t* seq_offsets,
+                          int32_t block_rows, int32_t reverse,
+                          int32_t* items, int32_t* n_items,
+                          void* workspace, size_t workspace_bytes, void* stream);
+size_t hstu_schedule_workspace_size(int32_t B, int64_t T, int32_t block_rows);
+
+/*
+ * Synchronous check of the device-side contracts (seq_offsets[0] = 0,
+ * offsets non-decreasing, seq_offsets[B] = T, 0 <= c_b <= n_b).  flag_ws is
+ * one device int32 of scratch.  Returns HSTU_OK or HSTU_ERR_VALIDATION.
+ */
+hstu_status hstu_validate_inputs(int32_t B, int64_t T, const int32_t* seq_offsets,
+                                 const int32_t* num_candidates, int32_t* flag_ws, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSTU_H_ */

@@ -125,3 +125,46 @@ def sub_batch(inp: Inputs, seqs) -> Inputs:
                   None if inp.num_candidates is None else inp.num_candidates[seqs],
                   inp.timestamps[rows], inp.X[rows], inp.layers,
                   None if inp.dY is None else inp.dY[rows], inp.norm_len)
+
+
+@dataclasses.dataclass
+class AttnInputs:
+    """Direct inputs of the attention step alone (no projection)."""
+    lengths: np.ndarray
+    seq_offsets: np.ndarray
+    num_candidates: Optional[np.ndarray]
+    timestamps: np.ndarray
+    q: np.ndarray        # [T, H, d_qk] float32 (bf16-representable for bf16)
+    k: np.ndarray
+    v: np.ndarray        # [T, H, d_v]
+    rab_pos: np.ndarray  # [H, P] float32
+    rab_time: np.ndarray
+    d_out: np.ndarray    # [T, H, d_v]
+    norm_len: int
+
+
+def make_attn_inputs(cfg: Config, seed: Optional[int] = None, qk_std: Optional[float] = None,
+                     rab_std: float = 1.0) -> AttnInputs:
+    """Q, K, V, bias tables and an output gradient for the attention step.
+
+    Lengths and timestamps follow `make_inputs`; q, k ~ N(0, d_qk^-1/4) so that
+    q.k has unit scale, v ~ N(0, 1), rab ~ N(0, rab_std), d_out ~ N(0, 1).
+    """
+    rng = np.random.default_rng(cfg.seed + 1000 if seed is None else seed)
+    lengths = make_lengths(cfg, rng)
+    offs = np.zeros(cfg.B + 1, dtype=np.int64)
+    offs[1:] = np.cumsum(lengths)
+    T = int(offs[-1])
+    c = cfg.num_candidates
+    ts = [_timestamps(rng, int(n) - c, c, cfg) for n in lengths]
+    timestamps = np.concatenate(ts) if ts else np.zeros(0, dtype=np.int64)
+    rnd = bf16_round if cfg.dtype == "bf16" else (lambda a: a.astype(np.float32))
+    s = cfg.d_qk ** -0.25 if qk_std is None else qk_std
+    q = rnd(rng.standard_normal((T, cfg.H, cfg.d_qk)) * s)
+    k = rnd(rng.standard_normal((T, cfg.H, cfg.d_qk)) * s)
+    v = rnd(rng.standard_normal((T, cfg.H, cfg.d_v)))
+    rp = (rng.standard_normal((cfg.H, cfg.n_pos_buckets)) * rab_std).astype(np.float32)
+    rt = (rng.standard_normal((cfg.H, cfg.n_time_buckets)) * rab_std).astype(np.float32)
+    dO = rnd(rng.standard_normal((T, cfg.H, cfg.d_v)))
+    nc = np.full(cfg.B, c, dtype=np.int64) if c else None
+    return AttnInputs(lengths, offs, nc, timestamps, q, k, v, rp, rt, dO, cfg.norm_len)
