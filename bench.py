@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Benchmark of the HSTU layer on one MI355X.
+
+One step = one full training step of one HSTU layer (forward with saved
+intermediates + backward, every kernel of the path) on the long-sequence
+training workload: 8 jagged sequences of uniform length in [4096, 8192],
+d_model 512, 4 heads x 128, causal, bf16 with fp32 accumulation, synthetic
+seeded inputs resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is whole-step algorithmic TFLOP/s (the DLRMv4
+page's Table 7 convention: weight GEMMs x3, attention x3.5 for fwd+bwd, S^2/2
+pairs per sequence); tokens/s and the fraction of the 2.5 PFLOP/s bf16 peak
+are reported alongside, with a per-kernel breakdown taken with HIP events
+inside the timed region, the roofline of the dominant kernel, forward-only
+figures for the other workloads, and the fp64 CPU oracle timed on a bounded
+sample (one sequence) of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "HSTU layer fwd+bwd TFLOP/s and tokens/s on 1 MI355X; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "hstu_sequential_transduction_amd", "csrc")
+KERNEL_SOURCES = {
+    "attn_fwd": ["attn_fwd.hip", "common.h", "bias.h"],
+    "attn_bwd_dkdv": ["attn_bwd.hip", "common.h", "bias.h"],
+    "attn_bwd_dq": ["attn_bwd.hip", "common.h", "bias.h"],
+    "ln_gate_fwd": ["ln_gate.hip", "common.h"],
+    "ln_gate_bwd": ["ln_gate.hip", "common.h"],
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, ["gemm.hip", "common.h"]):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_work(cfg, lengths, T, cand=None):
+    """Algorithmic work per launch of each kernel tag: (kind, amount)."""
+    from hstu_sequential_transduction_amd import flops
+    H, dq, dv, D = cfg.H, cfg.d_qk, cfg.d_v, cfg.D
+    W, F1 = H * dv, cfg.f1_width
+    P = flops.attn_pairs(lengths, cand)
+    return {
+        "attn_fwd": ("mfma", 2 * P * H * (dq + dv)),
+        # the products each backward kernel's outputs need: S, dA, dV, dK / S, dA, dQ
+        "attn_bwd_dkdv": ("mfma", 2 * P * H * (2 * dq + 2 * dv)),
+        "attn_bwd_dq": ("mfma", 2 * P * H * (2 * dq + dv)),
+        "gemm_uvqk": ("mfma", 2.0 * T * D * F1),
+        "gemm_out": ("mfma", 2.0 * T * W * D),
+        "gemm_dG": ("mfma", 2.0 * T * D * W),
+        "gemm_dW2": ("mfma", 2.0 * W * D * T),
+        "gemm_dW1": ("mfma", 2.0 * D * F1 * T),
+        "gemm_dX": ("mfma", 2.0 * T * F1 * D),
+        # O (fp32) + U read, G written, mu/rstd written
+        "ln_gate_fwd": ("hbm", T * (4.0 * W + 2 * W + 2 * W + 8)),
+        # O (fp32), U, dG, Z_U read; dU, dO written; mu/rstd read
+        "ln_gate_bwd": ("hbm", T * (4.0 * W + 2 * W * 5 + 8)),
+    }
+
+
+class Timer:
+    def __init__(self, L):
+        self.L = L
+
+    def enable(self, n):
+        from hstu_sequential_transduction_amd._lib import check
+        check("hstu_timer_enable", self.L.hstu_timer_enable(n))
+
+    def reset(self):
+        self.L.hstu_timer_reset()
+
+    def read(self):
+        import ctypes as C
+        out = {}
+        for t in range(self.L.hstu_timer_tag_count()):
+            n, ms = C.c_int64(0), C.c_double(0.0)
+            self.L.hstu_timer_query(t, C.byref(n), C.byref(ms))
+            if n.value:
+                out[self.L.hstu_timer_tag_name(t).decode()] = (n.value, ms.value)
+        return out
+
+
+def upload_layer(inp, cfg, li=0):
+    import numpy as np
+    import torch
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    w = inp.layers[li]
+    return dict(
+        W1=torch.from_numpy(w.W1).to(td).cuda(), W2=torch.from_numpy(w.W2).to(td).cuda(),
+        rp=torch.from_numpy(w.rab_pos).cuda(), rt=torch.from_numpy(w.rab_time).cuda())
+
+
+def bench_train(args, timer):
+    import numpy as np
+    import torch
+
+    import synth
+    from hstu_sequential_transduction_amd import binding as B
+    from hstu_sequential_transduction_amd import flops
+
+    cfg = synth.get_config(4)
+    inp = synth.make_inputs(cfg)
+    T = inp.T
+    td = torch.bfloat16
+    X = torch.from_numpy(inp.X).to(td).cuda()
+    dY = torch.from_numpy(inp.dY).to(td).cuda()
+    offs = torch.from_numpy(inp.seq_offsets.astype(np.int32)).cuda()
+    ts = torch.from_numpy(inp.timestamps).cuda()
+    w = upload_layer(inp, cfg)
+    ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len)
+    lc = B.LayerConfig(D=cfg.D, attn=ac)
+    saved = B.Saved(T, lc, td, "cuda")
+    y = torch.empty_like(X)
+    dx = torch.empty_like(X)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    grads = B.Grads(torch.empty(w["W1"].shape, **f32), torch.empty(w["W2"].shape, **f32),
+                    torch.empty(w["rp"].shape, **f32), torch.empty(w["rt"].shape, **f32))
+    wsf, wsb = B.LayerWorkspace(), B.LayerWorkspace()
+
+    def step():
+        B.hstu_layer_fwd(X, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc, saved=saved, y=y,
+                         workspace=wsf)
+        B.hstu_layer_bwd(X, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc, saved, dY, dx=dx,
+                         grads=grads, workspace=wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: K steps between two events on the stream the library launches on
+    timer.enable(64 * max(args.steps, 1))
+    timer.reset()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(args.steps, 1)
+    kern = timer.read()
+    timer.enable(0)
+    lf = flops.layer_flops(inp.lengths, None, cfg.D, cfg.H, cfg.d_qk, cfg.d_v, backward=True)
+    return cfg, inp, ms, kern, lf
+
+
+def roofline(cfg, inp, kern, steps, traffic_dir):
+    work = kernel_work(cfg, inp.lengths, inp.T)
+    best = max(((ms, name, n) for name, (n, ms) in kern.items() if name in work), default=None)
+    if best is None:
+        return None, {}
+    table = {}
+    for name, (n, ms) in kern.items():
+        per = ms / max(n, 1)
+        entry = {"launches_per_step": n / max(steps, 1), "ms_per_launch": round(per, 5)}
+        if name in work:
+            kind, amt = work[name]
+            if kind == "mfma":
+                entry["tflops"] = round(amt / (per * 1e-3) / 1e12, 2)
+            else:
+                entry["gbs"] = round(amt / (per * 1e-3) / 1e9, 1)
+        table[name] = entry
+    ms, name, n = best
+    kind, amt = work[name]
+    per_s = ms / n * 1e-3
+    if kind == "mfma":
+        achieved, peak, unit = amt / per_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = amt / per_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    traffic = None
+    tf = os.path.join(traffic_dir, f"{name}_traffic.json")
+    if os.path.exists(tf):
+        with open(tf) as fh:
+            rec = json.load(fh)
+        if rec.get("source_hash") == source_hash(name) and rec.get("workload") == cfg.name:
+            traffic = rec.get("bytes_per_launch")
+    roof = {"kernel": name, "bound": "mfma" if kind == "mfma" else "hbm",
+            "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "work_per_launch": amt, "ms_per_launch": round(ms / n, 5),
+            "source_hash": source_hash(name)}
+    return roof, table
+
+
+def bench_fwd_configs(timer, reps=3):
+    """Forward-only figures of the inference workloads (context for the forward kernel)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from hstu_sequential_transduction_amd import binding as B
+    from hstu_sequential_transduction_amd import flops
+    out = {}
+    for ci in (2, 3, 5):
+        cfg = synth.get_config(ci)
+        inp = synth.make_inputs(cfg)
+        td = torch.bfloat16
+        X = torch.from_numpy(inp.X).to(td).cuda()
+        offs = torch.from_numpy(inp.seq_offsets.astype(np.int32)).cuda()
+        ts = torch.from_numpy(inp.timestamps).cuda()
+        nc = None if inp.num_candidates is None else \
+            torch.from_numpy(inp.num_candidates.astype(np.int32)).cuda()
+        layers = [upload_layer(inp, cfg, li) for li in range(cfg.n_layers)]
+        ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len)
+        lc = B.LayerConfig(D=cfg.D, attn=ac)
+        ws = B.LayerWorkspace()
+        bufs = [torch.empty_like(X), torch.empty_like(X)]
+
+        def run():
+            x = X
+            for li, w in enumerate(layers):
+                x = B.hstu_layer_fwd(x, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc,
+                                     num_candidates=nc, y=bufs[li % 2], workspace=ws)
+
+        run()
+        torch.cuda.synchronize()
+        timer.enable(64 * reps * cfg.n_layers)
+        timer.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        kern = timer.read()
+        timer.enable(0)
+        lf = flops.layer_flops(inp.lengths, inp.num_candidates, cfg.D, cfg.H, cfg.d_qk, cfg.d_v,
+                               backward=False)
+        tot = lf["total"] * cfg.n_layers
+        af = lf["attn_fwd"]
+        n_a, ms_a = kern.get("attn_fwd", (0, 0.0))
+        a_tf = af / (ms_a / max(n_a, 1) * 1e-3) / 1e12 if n_a else None
+        out[cfg.name] = {
+            "ms": round(ms, 4), "tokens": inp.T, "layers": cfg.n_layers,
+            "tflops": round(tot / (ms * 1e-3) / 1e12, 2),
+            "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
+            "attn_fwd_tflops": None if a_tf is None else round(a_tf, 2),
+            "attn_fwd_frac_bf16_peak": None if a_tf is None else round(a_tf / PEAK_BF16_TFLOPS, 4),
+            "kernel_ms": {k: round(v[1] / reps, 4) for k, v in kern.items()},
+        }
+        log(f"fwd {cfg.name}: {out[cfg.name]}")
+    return out
+
+
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle on one sequence (the shortest) of the training batch."""
+    import numpy as np
+
+    import synth
+    from hstu_sequential_transduction_amd import flops
+    from oracle import hstu as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        cores = os.cpu_count()
+    b = int(np.argmin(inp.lengths))
+    sub = synth.sub_batch(inp, [b])
+    w = sub.layers[0]
+    f = orc.LayerFlags(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len, eps=1e-6)
+    t0 = time.perf_counter()
+    Y, sv = orc.layer_fwd(sub.X, w.W1, w.W2, w.rab_pos, w.rab_time, sub.seq_offsets,
+                          sub.timestamps, None, f)
+    orc.layer_bwd(sub.dY, sub.X, w.W1, w.W2, w.rab_pos, w.rab_time, sub.seq_offsets,
+                  sub.timestamps, None, f, sv)
+    dt = time.perf_counter() - t0
+    lf = flops.layer_flops(sub.lengths, None, cfg.D, cfg.H, cfg.d_qk, cfg.d_v, backward=True)
+    return {"value": round(lf["total"] / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "tokens_per_s": round(sub.T / dt, 1),
+            "sample": f"one sequence ({sub.T} tokens, the shortest) of the training batch, "
+                      f"fwd+bwd of one layer, fp64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
+              "sharding over GPUs is a design note, not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from hstu_sequential_transduction_amd import _lib
+    timer = Timer(_lib.lib())
+
+    cfg, inp, ms, kern, lf = bench_train(args, timer)
+    tflops = lf["total"] / (ms * 1e-3) / 1e12
+    log(f"train step: {ms:.3f} ms, {tflops:.1f} TFLOP/s")
+    roof, table = roofline(cfg, inp, kern, args.steps, os.path.join(ROOT, "profiles"))
+    extra = None if args.no_extra else bench_fwd_configs(timer)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, inp)
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; inputs resident in HBM)",
+        "config": {"workload": "1 HSTU layer fwd+bwd (training), bf16: batch 8, lengths U[4096,8192],"
+                               " d_model 512, 4 heads x 128, causal",
+                   "global_batch": cfg.B, "tokens": inp.T, "seq_len": "U[4096,8192]",
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
+        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flops_per_step": {k: v for k, v in lf.items()},
+        "kernels": table,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "forward_workloads": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

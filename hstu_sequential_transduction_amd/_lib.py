@@ -24,6 +24,8 @@ EXPORTED = [
     "hstu_layer_fwd", "hstu_layer_bwd",
     "hstu_bias_buckets", "hstu_schedule_capacity", "hstu_schedule",
     "hstu_schedule_workspace_size", "hstu_validate_inputs",
+    "hstu_timer_enable", "hstu_timer_reset", "hstu_timer_tag_count", "hstu_timer_tag_name",
+    "hstu_timer_query",
 ]
 
 
@@ -106,6 +108,16 @@ def lib() -> C.CDLL:
     L.hstu_schedule.argtypes = [i32, i64, vp, i32, i32, vp, vp, vp, sz, vp]
     L.hstu_validate_inputs.restype = C.c_int
     L.hstu_validate_inputs.argtypes = [i32, i64, vp, vp, vp, vp]
+    L.hstu_timer_enable.restype = C.c_int
+    L.hstu_timer_enable.argtypes = [i32]
+    L.hstu_timer_reset.restype = C.c_int
+    L.hstu_timer_reset.argtypes = []
+    L.hstu_timer_tag_count.restype = i32
+    L.hstu_timer_tag_count.argtypes = []
+    L.hstu_timer_tag_name.restype = C.c_char_p
+    L.hstu_timer_tag_name.argtypes = [i32]
+    L.hstu_timer_query.restype = C.c_int
+    L.hstu_timer_query.argtypes = [i32, P(i64), P(C.c_double)]
     _lib = L
     return L
 

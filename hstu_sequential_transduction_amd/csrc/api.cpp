@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "timer.h"
 
 using namespace hstu;
 
@@ -117,9 +118,9 @@ hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   a.out_f32 = out_f32;
   a.items = w.sc.items;
   a.counters = w.sc.counters;
-  HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st));
-  HSTU_TRY(launch_sched(w.sc, d->B, offs, 0, st));
-  HSTU_TRY(launch_attn_fwd(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st));
+  { HSTU_TIMED(TT_PREPASS, st); HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st)); }
+  { HSTU_TIMED(TT_SCHED, st); HSTU_TRY(launch_sched(w.sc, d->B, offs, 0, st)); }
+  { HSTU_TIMED(TT_ATTN_FWD, st); HSTU_TRY(launch_attn_fwd(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st)); }
   return HSTU_OK;
 }
 
@@ -144,19 +145,25 @@ hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   a.zq_col = zq;
   a.zk_col = zk;
   a.zv_col = zv;
-  HSTU_TRY(launch_zero_f32(drp, rab_floats(d), st));
-  HSTU_TRY(launch_zero_f32(drt, rab_floats(d), st));
-  HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st));
-  HSTU_TRY(launch_sched(w.kv, d->B, offs, 1, st));
-  HSTU_TRY(launch_sched(w.q, d->B, offs, 0, st));
+  {
+    HSTU_TIMED(TT_PREPASS, st);
+    HSTU_TRY(launch_zero_f32(drp, rab_floats(d), st));
+    HSTU_TRY(launch_zero_f32(drt, rab_floats(d), st));
+    HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st));
+  }
+  {
+    HSTU_TIMED(TT_SCHED, st);
+    HSTU_TRY(launch_sched(w.kv, d->B, offs, 1, st));
+    HSTU_TRY(launch_sched(w.q, d->B, offs, 0, st));
+  }
   AttnArgs akv = a;
   akv.items = w.kv.items;
   akv.counters = w.kv.counters;
-  HSTU_TRY(launch_attn_bwd_dkdv(akv, d->d_qk, d->d_v, w.kv.cap, st));
+  { HSTU_TIMED(TT_ATTN_BWD_DKDV, st); HSTU_TRY(launch_attn_bwd_dkdv(akv, d->d_qk, d->d_v, w.kv.cap, st)); }
   AttnArgs aq = a;
   aq.items = w.q.items;
   aq.counters = w.q.counters;
-  HSTU_TRY(launch_attn_bwd_dq(aq, d->d_qk, d->d_v, w.q.cap, st));
+  { HSTU_TIMED(TT_ATTN_BWD_DQ, st); HSTU_TRY(launch_attn_bwd_dq(aq, d->d_qk, d->d_v, w.q.cap, st)); }
   return HSTU_OK;
 }
 
@@ -378,7 +385,7 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
     g1.epi = EPI_RESID;  // bias only
     g1.R = nullptr;
   }
-  HSTU_TRY(launch_gemm(g1, d->dtype, st));
+  { HSTU_TIMED(TT_GEMM_UVQK, st); HSTU_TRY(launch_gemm(g1, d->dtype, st)); }
   if (!L->proj_silu && saved) {
     // without the nonlinearity Z and Zh coincide
     GemmArgs gz = g1;
@@ -405,7 +412,7 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
   la.ld_g = W;
   la.mu = saved ? saved->mu : nullptr;
   la.rstd = saved ? saved->rstd : nullptr;
-  HSTU_TRY(launch_ln_gate_fwd(la, d->dtype, st));
+  { HSTU_TIMED(TT_LN_FWD, st); HSTU_TRY(launch_ln_gate_fwd(la, d->dtype, st)); }
   // 4. Y = G W2 (+ b2) (+ X)
   GemmArgs g2;
   g2.M = T;
@@ -423,7 +430,7 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
   g2.bias = w->b2;
   g2.R = L->residual ? x : nullptr;
   g2.ldr = D;
-  HSTU_TRY(launch_gemm(g2, d->dtype, st));
+  { HSTU_TIMED(TT_GEMM_OUT, st); HSTU_TRY(launch_gemm(g2, d->dtype, st)); }
   return HSTU_OK;
 }
 
@@ -467,16 +474,19 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a1.B = w->W2; a1.ldb = D; a1.b_kcont = true;
   a1.C = bw.dG; a1.ldc = W;
   a1.epi = EPI_STORE;
-  HSTU_TRY(launch_gemm(a1, d->dtype, st));
+  { HSTU_TIMED(TT_GEMM_DG, st); HSTU_TRY(launch_gemm(a1, d->dtype, st)); }
   // 2. dW2 = G^T dY (split over T)
   GemmArgs a2;
   a2.M = W; a2.N = D; a2.K = T;
   a2.A = saved->G; a2.lda = W; a2.a_kcont = false;
   a2.B = dy; a2.ldb = D; a2.b_kcont = false;
   a2.epi = EPI_PARTIAL; a2.split_k = bw.s2; a2.partial = bw.part2;
-  HSTU_TRY(launch_gemm(a2, d->dtype, st));
-  HSTU_TRY(launch_splitk_reduce(bw.part2, bw.s2, W, D, g->dW2, D, st));
-  if (w->b2) HSTU_TRY(launch_colsum(dy, T, D, D, d->dtype, g->db2, bw.colws, st));
+  { HSTU_TIMED(TT_GEMM_DW2, st); HSTU_TRY(launch_gemm(a2, d->dtype, st)); }
+  {
+    HSTU_TIMED(TT_REDUCE, st);
+    HSTU_TRY(launch_splitk_reduce(bw.part2, bw.s2, W, D, g->dW2, D, st));
+    if (w->b2) HSTU_TRY(launch_colsum(dy, T, D, D, d->dtype, g->db2, bw.colws, st));
+  }
   // 3. LayerNorm + gate backward: dU (into dZ's U block, times SiLU'(Z)), dO
   LnArgs la;
   la.o_f32 = true;
@@ -492,7 +502,7 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   la.dgamma_part = w->ln_gamma ? bw.lnpg : nullptr;
   la.dbeta_part = w->ln_beta ? bw.lnpb : nullptr;
   la.n_part_blocks = bw.ln_blocks;
-  HSTU_TRY(launch_ln_gate_bwd(la, d->dtype, st));
+  { HSTU_TIMED(TT_LN_BWD, st); HSTU_TRY(launch_ln_gate_bwd(la, d->dtype, st)); }
   if (w->ln_gamma)
     HSTU_TRY(launch_colsum(bw.lnpg, bw.ln_blocks, W, W, HSTU_F32, g->dgamma, bw.colws, st));
   if (w->ln_beta)
@@ -509,9 +519,12 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a3.A = x; a3.lda = D; a3.a_kcont = false;
   a3.B = dz; a3.ldb = F1; a3.b_kcont = false;
   a3.epi = EPI_PARTIAL; a3.split_k = bw.s1; a3.partial = bw.part1;
-  HSTU_TRY(launch_gemm(a3, d->dtype, st));
-  HSTU_TRY(launch_splitk_reduce(bw.part1, bw.s1, D, F1, g->dW1, F1, st));
-  if (w->b1) HSTU_TRY(launch_colsum(dz, T, F1, F1, d->dtype, g->db1, bw.colws, st));
+  { HSTU_TIMED(TT_GEMM_DW1, st); HSTU_TRY(launch_gemm(a3, d->dtype, st)); }
+  {
+    HSTU_TIMED(TT_REDUCE, st);
+    HSTU_TRY(launch_splitk_reduce(bw.part1, bw.s1, D, F1, g->dW1, F1, st));
+    if (w->b1) HSTU_TRY(launch_colsum(dz, T, F1, F1, d->dtype, g->db1, bw.colws, st));
+  }
   // 6. dX = dZ W1^T (+ dY)
   GemmArgs a4;
   a4.M = T; a4.N = D; a4.K = F1;
@@ -520,7 +533,7 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a4.C = dx; a4.ldc = D;
   a4.epi = EPI_RESID;
   a4.R = L->residual ? dy : nullptr; a4.ldr = D;
-  HSTU_TRY(launch_gemm(a4, d->dtype, st));
+  { HSTU_TIMED(TT_GEMM_DX, st); HSTU_TRY(launch_gemm(a4, d->dtype, st)); }
   return HSTU_OK;
 }
 

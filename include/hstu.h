@@ -251,6 +251,24 @@ size_t hstu_schedule_workspace_size(int32_t B, int64_t T, int32_t block_rows);
 hstu_status hstu_validate_inputs(int32_t B, int64_t T, const int32_t* seq_offsets,
                                  const int32_t* num_candidates, int32_t* flag_ws, void* stream);
 
+/* ---- diagnostic kernel timer ------------------------------------------- */
+
+/*
+ * Per-kernel timing for benchmarking: while enabled, every kernel launch site
+ * of the entry points above is bracketed by a pair of HIP events recorded on
+ * the call's stream (at most max_launches pairs; later launches go untimed).
+ * hstu_timer_enable(0) disables timing and releases the events; it creates or
+ * destroys HIP events only (no device memory).  hstu_timer_reset forgets the
+ * recorded launches.  hstu_timer_query waits for the recorded events of one
+ * tag (0 <= tag < hstu_timer_tag_count()) and returns their count and summed
+ * duration.  Not thread-safe: one benchmarking thread at a time.
+ */
+hstu_status hstu_timer_enable(int32_t max_launches);
+hstu_status hstu_timer_reset(void);
+int32_t hstu_timer_tag_count(void);
+const char* hstu_timer_tag_name(int32_t tag);
+hstu_status hstu_timer_query(int32_t tag, int64_t* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif
