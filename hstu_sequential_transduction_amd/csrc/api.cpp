@@ -49,7 +49,6 @@ bool stride_ok(int dtype, const void* p, int64_t ld, int64_t min_ld) {
   return (reinterpret_cast<uintptr_t>(p) & 3) == 0;
 }
 
-int fwd_bm(int dtype) { return dtype == HSTU_BF16 ? ATTN_FWD_BM_BF16 : ATTN_FWD_BM_F32; }
 
 struct FwdWs {
   TimeMeta tm;
@@ -58,7 +57,7 @@ struct FwdWs {
 FwdWs carve_fwd(Carver& c, const hstu_attn_desc* d) {
   FwdWs w;
   w.tm = carve_time(c, d->T, d->B);
-  w.sc = carve_sched(c, d->T, d->B, fwd_bm(d->dtype));
+  w.sc = carve_sched(c, d->T, d->B, attn_fwd_block_rows(d->dtype, d->d_qk, d->d_v));
   return w;
 }
 

@@ -23,28 +23,125 @@
 #include "common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace hstu {
 
 namespace {
 
 constexpr int FWD_BN = 64;  // keys per tile
 
+// 32-row query groups per wave: two when d <= 64 (each K/V fragment read from
+// LDS then feeds two MFMAs), one at d = 128 where registers run out first.
+template <int DQK, int DV>
+struct FwdShape {
+  static constexpr int QG = (DQK <= 64 && DV <= 64) ? 2 : 1;
+  static constexpr int BM = 4 * 32 * QG;  // query rows per workgroup (four waves)
+};
+
+template <int DQK, int DV>
+struct FwdBuf {
+  uint32_t k[LdsTile<DQK>::S_DW * FWD_BN];   // K tile, row-major
+  uint32_t vt[LdsTile<FWD_BN>::S_DW * DV];   // V tile, channel-major, keys permuted
+  int32_t t[FWD_BN];                         // key times (relative, narrow path)
+  int64_t t64[FWD_BN];                       // key times (absolute, spans >= 2^31 s)
+};
+
 template <int DQK, int DV>
 struct FwdSmem {
-  using KT = LdsTile<DQK>;
-  using VT = LdsTile<FWD_BN>;
-  uint32_t k[KT::S_DW * FWD_BN];
-  uint32_t vt[VT::S_DW * DV];
-  int32_t t[FWD_BN];
-  float tfar[32];
-  float ttime[32];
-  float tpos[1024];
+  FwdBuf<DQK, DV> buf[2];
+  float tfar[32];    // (rab_pos[nP-1] + rab_time[bucket(c)]) * -log2 e, by clz index c
+  float ttime[32];   // rab_time[bucket(c)] * -log2 e
+  float tpos[1024];  // rab_pos * -log2 e
 };
+
+// Register staging of one key tile (global -> registers -> LDS).
+template <int DQK, int DV>
+struct FwdStage {
+  static constexpr int KCPR = DQK / 8;
+  static constexpr int KN = (FWD_BN * KCPR) / 256;
+  static constexpr int VCH = DV / 8;
+  static constexpr int VITEMS = (FWD_BN / 2) * VCH;
+  static constexpr int VN = (VITEMS + 255) / 256;
+  u32x4 k[KN];
+  u32x4 va[VN], vb[VN];
+  int32_t t;
+  int64_t t64;
+
+  HSTU_DEV static void vmap(int idx, int& kp, int& cc) {
+    if (VCH >= 8) {
+      const int rest = idx >> 6;
+      kp = (rest & 3) * 8 + ((idx >> 3) & 7);
+      cc = (rest >> 2) * 8 + (idx & 7);
+    } else {
+      cc = idx % VCH;
+      kp = idx / VCH;
+    }
+  }
+  HSTU_DEV void load(const bf16* kh, int64_t ldk, const bf16* vh, int64_t ldv,
+                     const int32_t* rt, const int64_t* t64p, int j0, int n, int tid) {
+#pragma unroll
+    for (int s = 0; s < KN; ++s) {
+      const int idx = tid + 256 * s;
+      const int row = idx / KCPR, ch = idx % KCPR;
+      const int j = j0 + row;
+      k[s] = (j < n) ? ld16(kh + (int64_t)j * ldk + ch * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int s = 0; s < VN; ++s) {
+      const int idx = tid + 256 * s;
+      va[s] = u32x4{0, 0, 0, 0};
+      vb[s] = u32x4{0, 0, 0, 0};
+      if (idx < VITEMS) {
+        int kp, cc;
+        vmap(idx, kp, cc);
+        const int j = j0 + 2 * kp;
+        if (j < n) va[s] = ld16(vh + (int64_t)j * ldv + cc * 8);
+        if (j + 1 < n) vb[s] = ld16(vh + (int64_t)(j + 1) * ldv + cc * 8);
+      }
+    }
+    t = (tid < FWD_BN && rt && j0 + tid < n) ? rt[j0 + tid] : 0;
+    t64 = (tid < FWD_BN && t64p && j0 + tid < n) ? t64p[j0 + tid] : 0;
+  }
+  HSTU_DEV void store(FwdBuf<DQK, DV>& B, int tid) const {
+    using KT = LdsTile<DQK>;
+    using VT = LdsTile<FWD_BN>;
+#pragma unroll
+    for (int s = 0; s < KN; ++s) {
+      const int idx = tid + 256 * s;
+      const int row = idx / KCPR, ch = idx % KCPR;
+      *reinterpret_cast<u32x4*>(&B.k[KT::off(row, ch * 4)]) = k[s];
+    }
+#pragma unroll
+    for (int s = 0; s < VN; ++s) {
+      const int idx = tid + 256 * s;
+      if (idx < VITEMS) {
+        int kp, cc;
+        vmap(idx, kp, cc);
+        const int col = kperm(2 * kp) >> 1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          B.vt[VT::off(cc * 8 + 2 * e, col)] = (va[s][e] & 0xFFFFu) | (vb[s][e] << 16);
+          B.vt[VT::off(cc * 8 + 2 * e + 1, col)] = (va[s][e] >> 16) | (vb[s][e] & 0xFFFF0000u);
+        }
+      }
+    }
+    if (tid < FWD_BN) {
+      B.t[tid] = t;
+      B.t64[tid] = t64;
+    }
+  }
+};
+
+template <bool V>
+using bconst = std::integral_constant<bool, V>;
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
   using KT = LdsTile<DQK>;
   using VT = LdsTile<FWD_BN>;
+  constexpr int QG = FwdShape<DQK, DV>::QG;
+  constexpr int BM = FwdShape<DQK, DV>::BM;
   __shared__ __attribute__((aligned(16))) FwdSmem<DQK, DV> sm;
 
   const int w = blockIdx.x;
@@ -56,191 +153,233 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
   const int n = a.seq_offsets[b + 1] - o0;
   const int c = a.num_cand ? a.num_cand[b] : 0;
   const int nh = n - c;
-  const bool wide = a.seq_flags[b] & 1;
+  const int flags = a.seq_flags[b];
+  const bool wide = flags & 1;
+  const bool sorted = flags & 2;
   const int nP = a.nP, nT = a.nT;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int ql = lane & 31, g = lane >> 5;
 
-  // bias tables (pre-scaled by -log2 e)
   {
     const float* rp = a.rab_pos + h * a.rab_stride;
-    const float* rt = a.rab_time + h * a.rab_stride;
+    const float* rtb = a.rab_time + h * a.rab_stride;
     for (int i = tid; i < nP; i += 256) sm.tpos[i] = rp[i] * HSTU_NEG_LOG2E;
     if (tid < 32) {
-      float tv = rt[tbucket_from_clz(tid, nT)];
+      const float tv = rtb[tbucket_from_clz(tid, nT)];
       sm.ttime[tid] = tv * HSTU_NEG_LOG2E;
       sm.tfar[tid] = (rp[nP - 1] + tv) * HSTU_NEG_LOG2E;
     }
   }
 
-  const int rb0 = m * 128;
-  const int rb1 = min(rb0 + 128, n);
-  const int r0 = rb0 + wave * 32;
-  const int rw1 = min(r0 + 32, n);
-  const int iq = r0 + ql;
-  const bool qvalid = iq < n;
-  const int pI = min(iq, nh);
-  int32_t ti1 = 0;
-  int64_t ti64 = 0;
-  if (qvalid) {
-    if (wide) ti64 = a.ts[o0 + iq];
-    else ti1 = a.rel_t[o0 + iq] + 1;
+  const int rb0 = m * BM;
+  const int rb1 = min(rb0 + BM, n);
+  const int r0 = rb0 + wave * 32 * QG;
+  const int rw1 = min(r0 + 32 * QG, n);
+
+  const bf16* qbase = reinterpret_cast<const bf16*>(a.q) + (int64_t)o0 * a.ld_qk + h * DQK;
+  const bf16* kh = reinterpret_cast<const bf16*>(a.k) + (int64_t)o0 * a.ld_qk + h * DQK;
+  const bf16* vh = reinterpret_cast<const bf16*>(a.v) + (int64_t)o0 * a.ld_v + h * DV;
+  const int32_t* relt = wide ? nullptr : a.rel_t + o0;
+  const int64_t* tsq = a.ts + o0;
+  const int64_t* t64p = wide ? tsq : nullptr;
+
+  int iq[QG], pI[QG];
+  int32_t ti1[QG];
+  int64_t tq64[QG];
+  bf16x8 qr[QG][DQK / 16];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    iq[qg] = r0 + 32 * qg + ql;
+    const bool qv = iq[qg] < n;
+    pI[qg] = min(iq[qg], nh);
+    ti1[qg] = (qv && !wide) ? a.rel_t[o0 + iq[qg]] + 1 : 0;
+    tq64[qg] = (qv && wide) ? tsq[iq[qg]] : 0;
+#pragma unroll
+    for (int ch = 0; ch < DQK / 16; ++ch)
+      qr[qg][ch] = qv ? *reinterpret_cast<const bf16x8*>(qbase + (int64_t)iq[qg] * a.ld_qk +
+                                                         ch * 16 + 8 * g)
+                      : bf16x8{};
   }
 
-  const bf16* qbase = reinterpret_cast<const bf16*>(a.q);
-  const bf16* kbase = reinterpret_cast<const bf16*>(a.k);
-  const bf16* vbase = reinterpret_cast<const bf16*>(a.v);
-
-  bf16x8 qr[DQK / 16];
+  f32x16 oacc[QG][DV / 32];
 #pragma unroll
-  for (int ch = 0; ch < DQK / 16; ++ch) {
-    if (qvalid)
-      qr[ch] = *reinterpret_cast<const bf16x8*>(qbase + (int64_t)(o0 + iq) * a.ld_qk + h * DQK +
-                                                ch * 16 + 8 * g);
-    else
-      qr[ch] = bf16x8{};
-  }
-
-  f32x16 oacc[DV / 32];
+  for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
-  for (int d = 0; d < DV / 32; ++d) oacc[d] = f32x16{};
+    for (int d = 0; d < DV / 32; ++d) oacc[qg][d] = f32x16{};
 
+  // key tiles: 0 .. ktiles-1, skipping tiles that hold only other candidates' keys
   const int ktiles = (rb1 + FWD_BN - 1) / FWD_BN;
-  for (int kt = 0; kt < ktiles; ++kt) {
+  auto next_tile = [&](int kt) {
+    const int nk = kt + 1;
+    const int j0 = nk * FWD_BN;
+    if (j0 >= nh && j0 + FWD_BN <= rb0) return rb0 / FWD_BN;
+    return nk;
+  };
+
+  FwdStage<DQK, DV> stg;
+  int kt = 0;
+  if (kt < ktiles && kt * FWD_BN >= nh && kt * FWD_BN + FWD_BN <= rb0) kt = rb0 / FWD_BN;
+  if (kt < ktiles) {
+    stg.load(kh, a.ld_qk, vh, a.ld_v, relt, t64p, kt * FWD_BN, n, tid);
+    stg.store(sm.buf[0], tid);
+  }
+  __syncthreads();
+  int cur = 0;
+  while (kt < ktiles) {
+    const int nk = next_tile(kt);
+    const bool has_next = nk < ktiles;
+    if (has_next) stg.load(kh, a.ld_qk, vh, a.ld_v, relt, t64p, nk * FWD_BN, n, tid);
+
+    const FwdBuf<DQK, DV>& B = sm.buf[cur];
     const int j0 = kt * FWD_BN;
     const int j1 = min(j0 + FWD_BN, n);
-    if (j0 >= nh && (j1 <= rb0 || j0 >= rb1)) continue;  // only other candidates' keys
-
-    __syncthreads();
-    // ---- stage K (row-major) ----
-    {
-      constexpr int CPR = DQK / 8;
-#pragma unroll
-      for (int s = 0; s < (FWD_BN * CPR + 255) / 256; ++s) {
-        const int idx = tid + 256 * s;
-        if (idx < FWD_BN * CPR) {
-          const int row = idx / CPR, ch = idx % CPR;
-          const int j = j0 + row;
-          u32x4 val = {0, 0, 0, 0};
-          if (j < n) val = ld16(kbase + (int64_t)(o0 + j) * a.ld_qk + h * DQK + ch * 8);
-          *reinterpret_cast<u32x4*>(&sm.k[KT::off(row, ch * 4)]) = val;
-        }
-      }
-    }
-    // ---- stage V transposed: vt[channel][kperm(key)] ----
-    {
-      constexpr int NCH = DV / 8;          // 8-channel chunks
-      constexpr int NITEM = (FWD_BN / 2) * NCH;
-#pragma unroll
-      for (int s = 0; s < (NITEM + 255) / 256; ++s) {
-        const int idx = tid + 256 * s;
-        if (idx < NITEM) {
-          int kp, cc;
-          if (NCH >= 8) {
-            const int rest = idx >> 6;
-            kp = (rest & 3) * 8 + ((idx >> 3) & 7);
-            cc = (rest >> 2) * 8 + (idx & 7);
-          } else {
-            cc = idx % NCH;
-            kp = idx / NCH;
-          }
-          const int j = j0 + 2 * kp;
-          u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-          if (j < n) va = ld16(vbase + (int64_t)(o0 + j) * a.ld_v + h * DV + cc * 8);
-          if (j + 1 < n) vb = ld16(vbase + (int64_t)(o0 + j + 1) * a.ld_v + h * DV + cc * 8);
-          const int col = kperm(2 * kp) >> 1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = (va[e] & 0xFFFFu) | (vb[e] << 16);
-            const uint32_t hi = (va[e] >> 16) | (vb[e] & 0xFFFF0000u);
-            sm.vt[VT::off(cc * 8 + 2 * e, col)] = lo;
-            sm.vt[VT::off(cc * 8 + 2 * e + 1, col)] = hi;
-          }
-        }
-      }
-    }
-    if (tid < FWD_BN) sm.t[tid] = (j0 + tid < n && !wide) ? a.rel_t[o0 + j0 + tid] : 0;
-    __syncthreads();
-
-    // ---- per-wave work on this tile ----
-    if (r0 >= rw1) continue;
     const bool hist_rows = r0 < nh;
     const bool cand_rows = rw1 > nh;
-    const bool active = (hist_rows && j0 <= min(rw1, nh) - 1) ||
-                        (cand_rows && (j0 < nh || (j0 < rw1 && j1 > max(r0, nh))));
-    if (!active) continue;
-    const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh);
-    const bool far = !need_mask && !wide && (min(r0, nh) - min(j1 - 1, nh) >= nP - 1);
+    const bool active = (r0 < rw1) &&
+                        ((hist_rows && j0 <= min(rw1, nh) - 1) ||
+                         (cand_rows && (j0 < nh || (j0 < rw1 && j1 > max(r0, nh)))));
+    if (active) {
+      const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh);
+      const bool far = !need_mask && !wide && (min(r0, nh) - min(j1 - 1, nh) >= nP - 1);
 
-    f32x16 sacc[2];
+      // tile class (wave-uniform): far tiles have position bucket nP-1 everywhere; with
+      // sorted timestamps a row's time bucket usually changes at most once per tile
+      int mode = 3;  // 0: constant per row, 1: one threshold per row, 2: gather, 3: general
+      int cF[QG], cL[QG];
+      if (far) {
+        const int32_t tfirst = B.t[0], tlast = B.t[j1 - 1 - j0];
+        bool one = sorted, cst = sorted;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      sacc[hf] = f32x16{};
-#pragma unroll
-      for (int ch = 0; ch < DQK / 16; ++ch) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&sm.k[KT::off(hf * 32 + ql, ch * 8 + 4 * g)]);
-        sacc[hf] = mfma32(ka, qr[ch], sacc[hf]);
+        for (int qg = 0; qg < QG; ++qg) {
+          cF[qg] = tclz_narrow(ti1[qg], tfirst);
+          cL[qg] = tclz_narrow(ti1[qg], tlast);
+          one = one && (cL[qg] - cF[qg] <= 1);
+          cst = cst && (cL[qg] == cF[qg]);
+        }
+        mode = __all(cst) ? 0 : (__all(one) ? 1 : 2);
       }
-    }
-
-    bf16x8 pk[4];
+      float ba[QG], bb[QG];
+      int32_t thr[QG];
+      if (mode <= 1) {
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        const int kk0 = hf * 32 + 8 * aa + 4 * g;
-        const i32x4 tj = *reinterpret_cast<const i32x4*>(&sm.t[kk0]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float s = sacc[hf][4 * aa + r];
-          float sb;
-          bool ok = true;
-          if (far) {
-            sb = fmaf(s, HSTU_NEG_LOG2E, sm.tfar[tclz_narrow(ti1, tj[r])]);
-          } else {
-            const int j = j0 + kk0 + r;
-            ok = (iq < nh) ? (j <= iq) : (j < nh || j == iq);
-            const int bpv = pbucket(pI, min(j, nh), nP);
-            int cl;
-            if (wide) cl = tclz_wide(ti64, j < n ? a.ts[o0 + j] : ti64);
-            else cl = tclz_narrow(ti1, tj[r]);
-            sb = fmaf(s, HSTU_NEG_LOG2E, sm.tpos[bpv] + sm.ttime[cl]);
-          }
-          float p = sb * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sb));
-          if (need_mask && !ok) p = 0.0f;
-          pk[hf * 2 + (aa >> 1)][(aa & 1) * 4 + r] = (bf16)p;
+        for (int qg = 0; qg < QG; ++qg) {
+          ba[qg] = sm.tfar[cF[qg]];
+          bb[qg] = sm.tfar[min(cF[qg] + 1, 31)];
+          thr[qg] = (cL[qg] == cF[qg]) ? INT32_MAX : ti1[qg] - (1 << (31 - cF[qg]));
         }
       }
-    }
+
+      // per-lane constants of the general path, shifted by 4g (see silu_half)
+      int dI[QG], pmin[QG], lim[QG], slf[QG];
+#pragma unroll
+      for (int qg = 0; qg < QG; ++qg) {
+        const int i = iq[qg];
+        dI[qg] = pI[qg] - j0 - 4 * g;             // p(i) - (j0 + 4g)
+        pmin[qg] = pI[qg] - nh;                   // p(i) - n_h (candidate keys)
+        lim[qg] = (i < nh ? i : nh - 1) - j0 - 4 * g;  // last allowed key of the causal part
+        slf[qg] = i - j0 - 4 * g;                 // the row's own key (candidates)
+      }
 
 #pragma unroll
-    for (int d = 0; d < DV / 32; ++d) {
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x16 sacc[QG];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 vb =
-            *reinterpret_cast<const bf16x8*>(&sm.vt[VT::off(d * 32 + ql, 8 * u + 4 * g)]);
-        oacc[d] = mfma32(pk[u], vb, oacc[d]);
+        for (int qg = 0; qg < QG; ++qg) sacc[qg] = f32x16{};
+#pragma unroll
+        for (int ch = 0; ch < DQK / 16; ++ch) {
+          const bf16x8 ka =
+              *reinterpret_cast<const bf16x8*>(&B.k[KT::off(hf * 32 + ql, ch * 8 + 4 * g)]);
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) sacc[qg] = mfma32(ka, qr[qg][ch], sacc[qg]);
+        }
+
+        bf16x8 pk[QG][2];
+        // P' = s' / (1 + 2^s') with s' = -log2(e) * (q.k + bias).  Key index in the
+        // tile: kk = kc + 4g with kc = hf*32 + 8*aa + r a compile-time constant, so
+        // per-lane limits are pre-shifted by 4g and compared with immediates.
+        // bias_of(qg, kc, key time) returns the pre-scaled bias.
+        auto silu_half = [&](auto bias_of, auto masked) {
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+            for (int aa = 0; aa < 4; ++aa) {
+              const int kk0 = hf * 32 + 8 * aa + 4 * g;
+              const i32x4 tj = *reinterpret_cast<const i32x4*>(&B.t[kk0]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int kc = hf * 32 + 8 * aa + r;
+                const float sb =
+                    fmaf(sacc[qg][4 * aa + r], HSTU_NEG_LOG2E, bias_of(qg, kc, tj[r]));
+                float p = sb * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sb));
+                if constexpr (decltype(masked)::value)
+                  p = (kc <= lim[qg] || kc == slf[qg]) ? p : 0.0f;
+                pk[qg][aa >> 1][(aa & 1) * 4 + r] = (bf16)p;
+              }
+              // keep the scheduler from hoisting every gather of the half at once
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        if (mode == 0) {
+          silu_half([&](int qg, int, int32_t) { return ba[qg]; }, bconst<false>{});
+        } else if (mode == 1) {
+          silu_half([&](int qg, int, int32_t tj) { return tj <= thr[qg] ? ba[qg] : bb[qg]; },
+                    bconst<false>{});
+        } else if (mode == 2) {
+          silu_half([&](int qg, int, int32_t tj) { return sm.tfar[tclz_narrow(ti1[qg], tj)]; },
+                    bconst<false>{});
+        } else if (!wide) {
+          // position bucket: clamp(p(i) - min(j, n_h), 0, nP-1) = med3(max(dI - kc, pI - nh), 0, nP-1)
+          auto bias = [&](int qg, int kc, int32_t tj) {
+            const int bp = min(max(max(dI[qg] - kc, pmin[qg]), 0), nP - 1);
+            return sm.tpos[bp] + sm.ttime[tclz_narrow(ti1[qg], tj)];
+          };
+          if (need_mask) silu_half(bias, bconst<true>{});
+          else silu_half(bias, bconst<false>{});
+        } else {
+          auto bias = [&](int qg, int kc, int32_t) {
+            const int bp = min(max(max(dI[qg] - kc, pmin[qg]), 0), nP - 1);
+            return sm.tpos[bp] + sm.ttime[tclz_wide(tq64[qg], B.t64[kc + 4 * g])];
+          };
+          silu_half(bias, bconst<true>{});
+        }
+
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 vb = *reinterpret_cast<const bf16x8*>(
+                &B.vt[VT::off(d * 32 + ql, 8 * (2 * hf + u) + 4 * g)]);
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) oacc[qg][d] = mfma32(pk[qg][u], vb, oacc[qg][d]);
+          }
       }
     }
+
+    if (has_next) stg.store(sm.buf[cur ^ 1], tid);
+    __syncthreads();
+    kt = nk;
+    cur ^= 1;
   }
 
   // ---- write O * (-ln2 / N) ----
   if (r0 >= rw1) return;
   const float scale = -HSTU_LN2 / (float)(a.norm_mode == 0 ? a.norm_len : n);
 #pragma unroll
-  for (int d = 0; d < DV / 32; ++d) {
+  for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = r0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (i < n) {
-        const int64_t off = (int64_t)(o0 + i) * a.ld_out + h * DV + d * 32 + ql;
-        if (a.out_f32) reinterpret_cast<float*>(a.out)[off] = oacc[d][r] * scale;
-        else reinterpret_cast<bf16*>(a.out)[off] = (bf16)(oacc[d][r] * scale);
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = r0 + 32 * qg + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (i < n) {
+          const int64_t off = (int64_t)(o0 + i) * a.ld_out + h * DV + d * 32 + ql;
+          if (a.out_f32) reinterpret_cast<float*>(a.out)[off] = oacc[qg][d][r] * scale;
+          else reinterpret_cast<bf16*>(a.out)[off] = (bf16)(oacc[qg][d][r] * scale);
+        }
       }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -364,6 +503,11 @@ hipError_t launch_fwd_dv(const AttnArgs& a, int dtype, int d_v, int64_t mi, hipS
 }
 
 }  // namespace
+
+int attn_fwd_block_rows(int dtype, int d_qk, int d_v) {
+  if (dtype != HSTU_BF16) return ATTN_FWD_BM_F32;
+  return (d_qk <= 64 && d_v <= 64) ? FwdShape<64, 64>::BM : FwdShape<128, 128>::BM;
+}
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, int d_qk, int d_v, int64_t max_items,
                            hipStream_t st) {

@@ -89,11 +89,13 @@ struct AttnArgs {
 
 // Row-block sizes of the kernels (rows of Q per forward work item, keys per
 // backward key-block work item).
-constexpr int ATTN_FWD_BM_BF16 = 128;
 constexpr int ATTN_FWD_BM_F32 = 64;
 constexpr int ATTN_BWD_BN = 128;   // keys per dK/dV work item
 constexpr int ATTN_BWD_BM = 128;   // queries per dQ work item
 
+// Query rows per forward work item for a head size (bf16 kernels use 32 or 64
+// rows per wave; fp32 uses 64 rows per workgroup).
+int attn_fwd_block_rows(int dtype, int d_qk, int d_v);
 hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, int d_qk, int d_v,
                            int64_t max_items, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, int d_qk, int d_v, int64_t max_items,
