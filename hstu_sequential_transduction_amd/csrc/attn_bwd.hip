@@ -9,18 +9,25 @@
 //
 // Two kernels, neither materialising S:
 //  * k_attn_bwd_dkdv: one workgroup per (sequence, 128-key block, head), four
-//    waves of 32 keys keeping K and V in registers and dK, dV in accumulators;
-//    it walks the 64-row query tiles that can see its keys (history keys: all
-//    later rows including every candidate; candidate keys: only themselves),
-//    recomputes S and dA on MFMA, and accumulates the rab-table gradients in
-//    LDS histograms (tile sums where the position bucket is constant,
-//    bucket-range reductions for the time buckets of far tiles, LDS atomics
-//    near the diagonal).
+//    waves of 32 keys keeping K and V in registers (B operands) and dK, dV in
+//    accumulators; it walks the 64-row query tiles that can see its keys
+//    (history keys: all later rows including every candidate; candidate keys:
+//    only themselves).  Q and dO tiles are staged once from HBM into both a
+//    row-major copy (A operands of S = Q K^T, dA = dO V^T) and a transposed
+//    copy (B operands of dK += dS^T Q, dV += P^T dO).  The rab-table gradients
+//    go to LDS histograms: on tiles where the position bucket saturates they
+//    are per-lane partial sums split at the row where the time bucket changes,
+//    reduced across the wave once per tile; elsewhere LDS atomics.
 //  * k_attn_bwd_dq: one workgroup per (sequence, 128-row query block, head),
-//    structured like the forward kernel; it recomputes S^T and dA^T and
-//    accumulates dQ = dS K with K^T staged in LDS.  No atomics on dQ.
+//    structured like the forward kernel: S^T = K Q^T and dA^T = V dO^T, then
+//    dQ += dS K with K^T staged in LDS.  No atomics on dQ.
+// SiLU is evaluated as in the forward kernel, s' = -log2(e) s, sigma =
+// 1/(1 + 2^s'), P' = s' sigma = -log2(e) SiLU(s), SiLU'(s) = sigma +
+// P' ln2 (sigma - 1); the -ln2 of P' is applied once to dV.
 // Optional epilogue (layer backward): each gradient is multiplied by
 // SiLU'(Z) of the projection's pre-activation before it is stored.
+#include <type_traits>
+
 #include "bias.h"
 #include "common.h"
 #include "internal.h"
@@ -32,76 +39,81 @@ namespace {
 constexpr int KV_QT = 64;   // query rows per tile in the dK/dV kernel
 constexpr int DQ_BN = 64;   // keys per tile in the dQ kernel
 
-HSTU_DEV float silu_from_parts(float s, float& sig) {
-  sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(s * HSTU_NEG_LOG2E));
-  return s * sig;
+template <bool V>
+using bconst = std::integral_constant<bool, V>;
+
+// sigma and P' from the pre-scaled score s' = -log2(e) * (q.k + bias)
+HSTU_DEV void silu_parts(float sb, float& sig, float& pp) {
+  sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sb));
+  pp = sb * sig;
+}
+// SiLU'(s) from sigma and P'
+HSTU_DEV float silu_deriv(float sig, float pp) {
+  return fmaf(pp, fmaf(sig, HSTU_LN2, -HSTU_LN2), sig);
 }
 
-template <int DQK, int DV>
-struct KvSmem {
-  using QT = LdsTile<DQK>;
-  using OT = LdsTile<DV>;
-  using TT = LdsTile<KV_QT>;
-  uint32_t q[QT::S_DW * KV_QT];    // Q tile row-major  (A operand of S = Q K^T)
-  uint32_t qt[TT::S_DW * DQK];     // Q tile transposed (B operand of dK += dS^T Q)
-  uint32_t o[OT::S_DW * KV_QT];    // dO tile row-major (A operand of dA = dO V^T)
-  uint32_t ot[TT::S_DW * DV];      // dO tile transposed (B operand of dV += P^T dO)
-  int32_t t1[KV_QT];               // query times + 1 (narrow path)
-  float tpos[1024];
-  float ttime[32];
-  float gpos[1024];                // d rab_pos histogram (by bucket)
-  float gtime[32];                 // d rab_time histogram (by clz index)
+// Register staging of R rows x D columns of a bf16 matrix for one tile: each
+// item is a (row pair, 8-column chunk); the same registers feed the row-major
+// LDS copy (two 16-byte writes) and the transposed copy (eight dword writes,
+// rows of the transposed tile are columns, rows permuted by kperm).
+template <int D, int R>
+struct Stage2 {
+  static constexpr int NCH = D / 8;
+  static constexpr int NITEM = (R / 2) * NCH;
+  static constexpr int NPT = (NITEM + 255) / 256;
+  u32x4 va[NPT], vb[NPT];
+
+  HSTU_DEV static void map(int idx, int& kp, int& cc) {
+    if (NCH >= 8) {
+      const int rest = idx >> 6;
+      kp = (rest & 3) * 8 + ((idx >> 3) & 7);
+      cc = (rest >> 2) * 8 + (idx & 7);
+    } else {
+      cc = idx % NCH;
+      kp = idx / NCH;
+    }
+  }
+  // rows [r0, r0+R) of `base` (row stride ld); rows >= rlim read as zero
+  HSTU_DEV void load(const bf16* base, int64_t ld, int r0, int rlim, int tid) {
+#pragma unroll
+    for (int s = 0; s < NPT; ++s) {
+      const int idx = tid + 256 * s;
+      va[s] = u32x4{0, 0, 0, 0};
+      vb[s] = u32x4{0, 0, 0, 0};
+      if (idx < NITEM) {
+        int kp, cc;
+        map(idx, kp, cc);
+        const int r = r0 + 2 * kp;
+        if (r < rlim) va[s] = ld16(base + (int64_t)r * ld + cc * 8);
+        if (r + 1 < rlim) vb[s] = ld16(base + (int64_t)(r + 1) * ld + cc * 8);
+      }
+    }
+  }
+  HSTU_DEV void store(uint32_t* rm, uint32_t* tr, int tid) const {
+    using RM = LdsTile<D>;
+    using TR = LdsTile<R>;
+#pragma unroll
+    for (int s = 0; s < NPT; ++s) {
+      const int idx = tid + 256 * s;
+      if (idx < NITEM) {
+        int kp, cc;
+        map(idx, kp, cc);
+        if (rm) {
+          *reinterpret_cast<u32x4*>(&rm[RM::off(2 * kp, cc * 4)]) = va[s];
+          *reinterpret_cast<u32x4*>(&rm[RM::off(2 * kp + 1, cc * 4)]) = vb[s];
+        }
+        if (tr) {
+          const int col = kperm(2 * kp) >> 1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            tr[TR::off(cc * 8 + 2 * e, col)] = (va[s][e] & 0xFFFFu) | (vb[s][e] << 16);
+            tr[TR::off(cc * 8 + 2 * e + 1, col)] = (va[s][e] >> 16) | (vb[s][e] & 0xFFFF0000u);
+          }
+        }
+      }
+    }
+  }
 };
-
-// Stage rows [i0, i0+RT) of a [*, ld] bf16 matrix (columns col0..col0+D) into
-// a row-major tile and a transposed tile (rows = channels, columns = kperm(row)).
-template <int D, int RT>
-HSTU_DEV void stage_both(const bf16* base, int64_t ld, int o0, int i0, int n, int col0,
-                         uint32_t* rm, uint32_t* tr, int tid) {
-  using RM = LdsTile<D>;
-  using TR = LdsTile<RT>;
-  // row-major copy
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int s = 0; s < (RT * CPR + 255) / 256; ++s) {
-    const int idx = tid + 256 * s;
-    if (idx < RT * CPR) {
-      const int row = idx / CPR, ch = idx % CPR;
-      const int i = i0 + row;
-      u32x4 val = {0, 0, 0, 0};
-      if (i < n) val = ld16(base + (int64_t)(o0 + i) * ld + col0 + ch * 8);
-      *reinterpret_cast<u32x4*>(&rm[RM::off(row, ch * 4)]) = val;
-    }
-  }
-  // transposed copy
-  constexpr int NCH = D / 8;
-  constexpr int NITEM = (RT / 2) * NCH;
-#pragma unroll
-  for (int s = 0; s < (NITEM + 255) / 256; ++s) {
-    const int idx = tid + 256 * s;
-    if (idx < NITEM) {
-      int kp, cc;
-      if (NCH >= 8) {
-        const int rest = idx >> 6;
-        kp = (rest & 3) * 8 + ((idx >> 3) & 7);
-        cc = (rest >> 2) * 8 + (idx & 7);
-      } else {
-        cc = idx % NCH;
-        kp = idx / NCH;
-      }
-      const int i = i0 + 2 * kp;
-      u32x4 va = {0, 0, 0, 0}, vb = {0, 0, 0, 0};
-      if (i < n) va = ld16(base + (int64_t)(o0 + i) * ld + col0 + cc * 8);
-      if (i + 1 < n) vb = ld16(base + (int64_t)(o0 + i + 1) * ld + col0 + cc * 8);
-      const int col = kperm(2 * kp) >> 1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tr[TR::off(cc * 8 + 2 * e, col)] = (va[e] & 0xFFFFu) | (vb[e] << 16);
-        tr[TR::off(cc * 8 + 2 * e + 1, col)] = (va[e] >> 16) | (vb[e] & 0xFFFF0000u);
-      }
-    }
-  }
-}
 
 // Store a 32-row x (32*NB)-column accumulator block (rows 8*(r/4)+4g+r%4,
 // column lane%32 of each 32-column block) as bf16, optionally times SiLU'(Z).
@@ -123,11 +135,41 @@ HSTU_DEV void store_grad(const f32x16* acc, float scale, bf16* dst, int64_t ld, 
   }
 }
 
+// ===========================================================================
+// dK / dV (key-block major)
+// ===========================================================================
 template <int DQK, int DV>
-__global__ __launch_bounds__(256, (DQK >= 128 || DV >= 128) ? 1 : 2) void k_attn_bwd_dkdv(AttnArgs a) {
+struct KvShape {
+  static constexpr bool BIG = (DQK >= 128 || DV >= 128);
+  static constexpr int NBUF = BIG ? 2 : 1;  // d = 128 runs one workgroup per CU anyway
+};
+
+template <int DQK, int DV>
+struct KvBuf {
+  uint32_t q[LdsTile<DQK>::S_DW * KV_QT];   // Q tile row-major  (A of S = Q K^T)
+  uint32_t qt[LdsTile<KV_QT>::S_DW * DQK];  // Q tile transposed (B of dK += dS^T Q)
+  uint32_t o[LdsTile<DV>::S_DW * KV_QT];    // dO tile row-major (A of dA = dO V^T)
+  uint32_t ot[LdsTile<KV_QT>::S_DW * DV];   // dO tile transposed (B of dV += P^T dO)
+  int32_t t1[KV_QT];                        // query times + 1 (relative)
+  int64_t t64[KV_QT];                       // query times (absolute, spans >= 2^31 s)
+};
+
+template <int DQK, int DV>
+struct KvSmem {
+  KvBuf<DQK, DV> buf[KvShape<DQK, DV>::NBUF];
+  float tpos[1024];   // rab_pos * -log2 e
+  float ttime[32];    // rab_time[bucket(c)] * -log2 e, by clz index
+  float tfar[32];     // (rab_pos[nP-1] + rab_time[bucket(c)]) * -log2 e
+  float gpos[1024];   // d rab_pos histogram (by bucket)
+  float gtime[32];    // d rab_time histogram (by clz index)
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_bwd_dkdv(AttnArgs a) {
   using QT = LdsTile<DQK>;
   using OT = LdsTile<DV>;
   using TT = LdsTile<KV_QT>;
+  constexpr int NBUF = KvShape<DQK, DV>::NBUF;
   __shared__ __attribute__((aligned(16))) KvSmem<DQK, DV> sm;
 
   const int w = blockIdx.x;
@@ -139,20 +181,26 @@ __global__ __launch_bounds__(256, (DQK >= 128 || DV >= 128) ? 1 : 2) void k_attn
   const int n = a.seq_offsets[b + 1] - o0;
   const int c = a.num_cand ? a.num_cand[b] : 0;
   const int nh = n - c;
-  const bool wide = a.seq_flags[b] & 1;
+  const int flags = a.seq_flags[b];
+  const bool wide = flags & 1;
+  const bool sorted = flags & 2;
   const int nP = a.nP, nT = a.nT;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int ql = lane & 31, g = lane >> 5;
 
   {
     const float* rp = a.rab_pos + h * a.rab_stride;
-    const float* rt = a.rab_time + h * a.rab_stride;
+    const float* rtb = a.rab_time + h * a.rab_stride;
     for (int i = tid; i < nP; i += 256) {
-      sm.tpos[i] = rp[i];
+      sm.tpos[i] = rp[i] * HSTU_NEG_LOG2E;
       sm.gpos[i] = 0.0f;
     }
     if (tid < 32) {
-      sm.ttime[tid] = rt[tbucket_from_clz(tid, nT)];
+      const float tv = rtb[tbucket_from_clz(tid, nT)];
+      sm.ttime[tid] = tv * HSTU_NEG_LOG2E;
+      sm.tfar[tid] = (rp[nP - 1] + tv) * HSTU_NEG_LOG2E;
       sm.gtime[tid] = 0.0f;
     }
   }
@@ -164,28 +212,24 @@ __global__ __launch_bounds__(256, (DQK >= 128 || DV >= 128) ? 1 : 2) void k_attn
   const int jk = kw0 + ql;  // this lane's key
   const bool kvalid = jk < n;
   const int pJ = min(jk, nh);
-  int32_t tj = 0;
-  int64_t tj64 = 0;
-  if (kvalid) {
-    if (wide) tj64 = a.ts[o0 + jk];
-    else tj = a.rel_t[o0 + jk];
-  }
+  const int64_t* tsq = a.ts + o0;
+  const int32_t tj = (kvalid && !wide) ? a.rel_t[o0 + jk] : 0;
+  const int64_t tj64 = (kvalid && wide) ? tsq[jk] : 0;
 
-  const bf16* qb = reinterpret_cast<const bf16*>(a.q);
-  const bf16* kbp = reinterpret_cast<const bf16*>(a.k);
-  const bf16* vbp = reinterpret_cast<const bf16*>(a.v);
-  const bf16* dob = reinterpret_cast<const bf16*>(a.dout);
+  const bf16* qh_ = reinterpret_cast<const bf16*>(a.q) + (int64_t)o0 * a.ld_qk + h * DQK;
+  const bf16* kh_ = reinterpret_cast<const bf16*>(a.k) + (int64_t)o0 * a.ld_qk + h * DQK;
+  const bf16* vh_ = reinterpret_cast<const bf16*>(a.v) + (int64_t)o0 * a.ld_v + h * DV;
+  const bf16* doh = reinterpret_cast<const bf16*>(a.dout) + (int64_t)o0 * a.ld_dout + h * DV;
 
   bf16x8 kr[DQK / 16], vr[DV / 16];
 #pragma unroll
   for (int ch = 0; ch < DQK / 16; ++ch)
-    kr[ch] = kvalid ? *reinterpret_cast<const bf16x8*>(kbp + (int64_t)(o0 + jk) * a.ld_qk +
-                                                       h * DQK + ch * 16 + 8 * g)
+    kr[ch] = kvalid ? *reinterpret_cast<const bf16x8*>(kh_ + (int64_t)jk * a.ld_qk + ch * 16 +
+                                                       8 * g)
                     : bf16x8{};
 #pragma unroll
   for (int ch = 0; ch < DV / 16; ++ch)
-    vr[ch] = kvalid ? *reinterpret_cast<const bf16x8*>(vbp + (int64_t)(o0 + jk) * a.ld_v +
-                                                       h * DV + ch * 16 + 8 * g)
+    vr[ch] = kvalid ? *reinterpret_cast<const bf16x8*>(vh_ + (int64_t)jk * a.ld_v + ch * 16 + 8 * g)
                     : bf16x8{};
 
   f32x16 dk[DQK / 32], dv[DV / 32];
@@ -194,154 +238,238 @@ __global__ __launch_bounds__(256, (DQK >= 128 || DV >= 128) ? 1 : 2) void k_attn
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) dv[d] = f32x16{};
 
-  const int qend = (k0 >= nh) ? k1 : n;  // candidate keys are seen by themselves only
-  for (int i0 = k0; i0 < qend; i0 += KV_QT) {
-    const int i1 = min(i0 + KV_QT, qend);
-    __syncthreads();
-    stage_both<DQK, KV_QT>(qb, a.ld_qk, o0, i0, i1, h * DQK, sm.q, sm.qt, tid);
-    stage_both<DV, KV_QT>(dob, a.ld_dout, o0, i0, i1, h * DV, sm.o, sm.ot, tid);
-    if (tid < KV_QT) sm.t1[tid] = (i0 + tid < n && !wide) ? a.rel_t[o0 + i0 + tid] + 1 : 0;
-    __syncthreads();
+  // query tiles: [k0, qend); candidate keys are seen by themselves only
+  const int qend = (k0 >= nh) ? k1 : n;
+  Stage2<DQK, KV_QT> sq;
+  Stage2<DV, KV_QT> so;
+  int32_t st1 = 0;
+  int64_t st64 = 0;
+  auto load_tile = [&](int i0) {
+    sq.load(qh_, a.ld_qk, i0, qend, tid);
+    so.load(doh, a.ld_dout, i0, qend, tid);
+    if (tid < KV_QT) {
+      const int i = i0 + tid;
+      st1 = (i < n && !wide) ? a.rel_t[o0 + i] + 1 : 0;
+      st64 = (i < n && wide) ? tsq[i] : 0;
+    }
+  };
+  auto store_tile = [&](KvBuf<DQK, DV>& Bf) {
+    sq.store(Bf.q, Bf.qt, tid);
+    so.store(Bf.o, Bf.ot, tid);
+    if (tid < KV_QT) {
+      Bf.t1[tid] = st1;
+      Bf.t64[tid] = st64;
+    }
+  };
 
-    if (kw0 >= kw1) continue;
-    // some allowed pair for this wave's keys?
-    const bool hist_keys = kw0 < nh;
-    bool active;
-    if (hist_keys) active = (i1 - 1 >= kw0);
-    else active = (i0 < kw1 && i1 > kw0);
-    if (!active) continue;
-    const bool need_mask = (i0 < kw1 - 1) || (kw1 > nh && i1 > nh);
-    const bool far = !need_mask && !wide && (min(i0, nh) - min(kw1 - 1, nh) >= nP - 1);
+  int i0 = k0;
+  if (i0 < qend) load_tile(i0);
+  if (NBUF == 2 && i0 < qend) store_tile(sm.buf[0]);
+  __syncthreads();
+  int cur = 0;
+  while (i0 < qend) {
+    const int ni = i0 + KV_QT;
+    const bool has_next = ni < qend;
+    if (NBUF == 1) {
+      store_tile(sm.buf[0]);
+      __syncthreads();
+      if (has_next) load_tile(ni);
+    } else if (has_next) {
+      load_tile(ni);
+    }
+    const KvBuf<DQK, DV>& B = sm.buf[NBUF == 2 ? cur : 0];
 
-    float dpos_far = 0.0f;
+    if (kw0 < kw1) {
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      int cmin = 32, cmax = -1;
-      float dsv[16];
-      int clv[16];
-      f32x16 sacc = f32x16{}, dacc = f32x16{};
+      for (int qh = 0; qh < 2; ++qh) {
+        const int ir0 = i0 + qh * 32;                 // first row of this half
+        const int ir1 = min(ir0 + 32, qend);          // end of its valid rows
+        bool active;
+        if (kw0 < nh) active = ir1 - 1 >= kw0;        // history keys: rows at or after them
+        else active = ir0 < kw1 && ir1 > kw0;         // candidate keys: themselves
+        if (!active || ir0 >= ir1) continue;
+        const bool need_mask = (ir0 < kw1 - 1) || (kw1 > nh && ir1 > nh) || (ir1 - ir0 < 32) ||
+                               (kw1 - kw0 < 32);
+        const bool far = !need_mask && !wide && (min(ir0, nh) - min(kw1 - 1, nh) >= nP - 1);
+
+        f32x16 sacc = f32x16{}, dacc = f32x16{};
 #pragma unroll
-      for (int ch = 0; ch < DQK / 16; ++ch) {
-        const bf16x8 qa =
-            *reinterpret_cast<const bf16x8*>(&sm.q[QT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
-        sacc = mfma32(qa, kr[ch], sacc);
-      }
+        for (int ch = 0; ch < DQK / 16; ++ch) {
+          const bf16x8 qa =
+              *reinterpret_cast<const bf16x8*>(&B.q[QT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
+          sacc = mfma32(qa, kr[ch], sacc);
+        }
 #pragma unroll
-      for (int ch = 0; ch < DV / 16; ++ch) {
-        const bf16x8 oa =
-            *reinterpret_cast<const bf16x8*>(&sm.o[OT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
-        dacc = mfma32(oa, vr[ch], dacc);
-      }
-      bf16x8 pp[2], dd[2];
+        for (int ch = 0; ch < DV / 16; ++ch) {
+          const bf16x8 oa =
+              *reinterpret_cast<const bf16x8*>(&B.o[OT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
+          dacc = mfma32(oa, vr[ch], dacc);
+        }
+
+        // lane = key jk; element r is row i = ir0 + 4g + kc, kc = 8*(r/4) + r%4
+        bf16x8 pp[2], dd[2];
+        const int ib = ir0 + 4 * g;
+        auto elems = [&](auto bias_of, auto grad_of, auto masked, int lo, int hi) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = qh * 32 + 8 * (r >> 2) + 4 * g + (r & 3);  // row inside the tile
-        const int i = i0 + qi;
-        bool ok = true;
-        int cl;
-        float bias;
-        if (wide) cl = tclz_wide(i < n ? a.ts[o0 + i] : tj64, tj64);
-        else cl = tclz_narrow(sm.t1[qi], tj);
+          for (int aa = 0; aa < 4; ++aa) {
+            const i32x4 t4 = *reinterpret_cast<const i32x4*>(&B.t1[qh * 32 + 8 * aa + 4 * g]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int kc = 8 * aa + r;
+              const int e = 4 * aa + r;
+              const float sb = fmaf(sacc[e], HSTU_NEG_LOG2E, bias_of(kc, t4[r]));
+              float sig, p;
+              silu_parts(sb, sig, p);
+              float ds = dacc[e] * silu_deriv(sig, p);
+              if constexpr (decltype(masked)::value) {
+                const bool ok = kc >= lo && kc <= hi;
+                p = ok ? p : 0.0f;
+                ds = ok ? ds : 0.0f;
+              }
+              grad_of(kc, t4[r], ds);
+              pp[aa >> 1][(aa & 1) * 4 + r] = (bf16)p;
+              dd[aa >> 1][(aa & 1) * 4 + r] = (bf16)ds;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
+
         if (far) {
-          bias = sm.tpos[nP - 1] + sm.ttime[cl];
+          // Position bucket nP-1 everywhere.  Time bucket of (row i, key j) from
+          // x = t1_i - t_j: rows increase in time, so per lane cF = clz at the last
+          // row (smallest clz), cL = clz at the first row.
+          const int32_t tfirst = B.t1[qh * 32], tlast = B.t1[qh * 32 + 31];
+          const int cF = tclz_narrow(tlast, tj), cL = tclz_narrow(tfirst, tj);
+          const bool one = __all(sorted && cL - cF <= 1);
+          float stot = 0.0f, sA = 0.0f;
+          if (one) {
+            // rows with t1 >= thr are in bucket cF, the others in cF+1
+            const float ba = sm.tfar[cF], bb = sm.tfar[min(cF + 1, 31)];
+            const int32_t thr = (cL == cF) ? INT32_MIN : tj + (1 << (31 - cF));
+            elems([&](int, int32_t t) { return t >= thr ? ba : bb; },
+                  [&](int, int32_t t, float ds) {
+                    stot += ds;
+                    sA += t >= thr ? ds : 0.0f;
+                  },
+                  bconst<false>{}, 0, 0);
+            // reduce (bucket cF: sA, bucket cF+1: stot - sA) over the lanes
+            const int lo = wave_min_i(cF), hi = wave_max_i(cF) + 1;
+            for (int v = lo; v <= hi; ++v) {
+              float part = (cF == v ? sA : 0.0f) + (cF + 1 == v ? stot - sA : 0.0f);
+              part = wave_sum(part);
+              if (lane == 0 && part != 0.0f) atomicAdd(&sm.gtime[v], part);
+            }
+          } else {
+            elems([&](int, int32_t t) { return sm.tfar[tclz_narrow(t, tj)]; },
+                  [&](int, int32_t t, float ds) {
+                    stot += ds;
+                    atomicAdd(&sm.gtime[tclz_narrow(t, tj)], ds);
+                  },
+                  bconst<false>{}, 0, 0);
+          }
+          const float tot = wave_sum(stot);
+          if (lane == 0) atomicAdd(&sm.gpos[nP - 1], tot);
         } else {
-          ok = (i < n) && ((i < nh) ? (jk <= i) : (jk < nh || jk == i));
-          bias = sm.tpos[pbucket(min(i, nh), pJ, nP)] + sm.ttime[cl];
+          // general tile: per-element buckets and LDS-atomic histograms
+          // p(i) - p(j) = min(ib + kc, nh) - pJ ; rows allowed: history key -> i >= j,
+          // candidate key -> i == j; rows >= qend and keys >= n never.
+          const int pd0 = ib - pJ, pdmax = nh - pJ;
+          const int d0 = jk - ib;
+          const int lo = kvalid ? d0 : 1 << 20;
+          const int hi = min(jk < nh ? (1 << 20) : d0, qend - 1 - ib);
+          auto bidx = [&](int kc) { return min(max(min(pd0 + kc, pdmax), 0), nP - 1); };
+          if (!wide) {
+            elems([&](int kc, int32_t t) { return sm.tpos[bidx(kc)] + sm.ttime[tclz_narrow(t, tj)]; },
+                  [&](int kc, int32_t t, float ds) {
+                    if (ds != 0.0f) {
+                      atomicAdd(&sm.gpos[bidx(kc)], ds);
+                      atomicAdd(&sm.gtime[tclz_narrow(t, tj)], ds);
+                    }
+                  },
+                  bconst<true>{}, lo, hi);
+          } else {
+            elems([&](int kc, int32_t) {
+                    const int qi = qh * 32 + 4 * g + kc;
+                    return sm.tpos[bidx(kc)] + sm.ttime[tclz_wide(B.t64[qi], tj64)];
+                  },
+                  [&](int kc, int32_t, float ds) {
+                    if (ds != 0.0f) {
+                      const int qi = qh * 32 + 4 * g + kc;
+                      atomicAdd(&sm.gpos[bidx(kc)], ds);
+                      atomicAdd(&sm.gtime[tclz_wide(B.t64[qi], tj64)], ds);
+                    }
+                  },
+                  bconst<true>{}, lo, hi);
+          }
         }
-        const float s = sacc[r] + bias;
-        float sig;
-        float p = silu_from_parts(s, sig);
-        float ds = dacc[r] * fmaf(p, 1.0f - sig, sig);
-        if (need_mask && !ok) {
-          p = 0.0f;
-          ds = 0.0f;
-        }
-        pp[r >> 3][r & 7] = (bf16)p;
-        dd[r >> 3][r & 7] = (bf16)ds;
-        if (far) {
-          dpos_far += ds;
-          cmin = min(cmin, cl);
-          cmax = max(cmax, cl);
-          dsv[r] = ds;
-          clv[r] = cl;
-        } else if (ok && i < n && kvalid) {
-          atomicAdd(&sm.gpos[pbucket(min(i, nh), pJ, nP)], ds);
-          atomicAdd(&sm.gtime[cl], ds);
-        }
-      }
-      // dV += P^T dO ; dK += dS^T Q   (k = 32 query rows of this half)
+
+        // dV += P'^T dO ; dK += dS^T Q   (k = the 32 rows of this half)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int d = 0; d < DV / 32; ++d) {
-          const bf16x8 ob = *reinterpret_cast<const bf16x8*>(
-              &sm.ot[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
-          dv[d] = mfma32(pp[u], ob, dv[d]);
-        }
+          for (int d = 0; d < DV / 32; ++d) {
+            const bf16x8 ob = *reinterpret_cast<const bf16x8*>(
+                &B.ot[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
+            dv[d] = mfma32(pp[u], ob, dv[d]);
+          }
 #pragma unroll
-        for (int d = 0; d < DQK / 32; ++d) {
-          const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(
-              &sm.qt[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
-          dk[d] = mfma32(dd[u], qbv, dk[d]);
-        }
-      }
-      if (far) {
-        // time buckets of a far tile: one wave reduction per bucket in its range
-        const int lo = wave_min_i(cmin), hi = wave_max_i(cmax);
-        for (int cv = lo; cv <= hi; ++cv) {
-          float part = 0.0f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) part += (clv[r] == cv) ? dsv[r] : 0.0f;
-          part = wave_sum(part);
-          if (lane == 0) atomicAdd(&sm.gtime[cv], part);
+          for (int d = 0; d < DQK / 32; ++d) {
+            const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(
+                &B.qt[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
+            dk[d] = mfma32(dd[u], qbv, dk[d]);
+          }
         }
       }
     }
-    if (far) {
-      // the position bucket is constant on a far tile: one sum
-      const float tot = wave_sum(dpos_far);
-      if (lane == 0) atomicAdd(&sm.gpos[nP - 1], tot);
+
+    if (NBUF == 2) {
+      if (has_next) store_tile(sm.buf[cur ^ 1]);
+      cur ^= 1;
     }
+    __syncthreads();
+    i0 = ni;
   }
 
   const float invN = 1.0f / (float)(a.norm_mode == 0 ? a.norm_len : n);
   if (kw0 < kw1) {
-    // dK/dV rows are keys: 8*(r/4)+4g+r%4 inside the wave's 32 keys, columns = channels
-    f32x16 tk[DQK / 32], tv[DV / 32];
-#pragma unroll
-    for (int d = 0; d < DQK / 32; ++d) tk[d] = dk[d];
-#pragma unroll
-    for (int d = 0; d < DV / 32; ++d) tv[d] = dv[d];
-    store_grad<DQK / 32>(tk, invN, reinterpret_cast<bf16*>(a.dk), a.ld_qk, o0, kw0, n, h * DQK,
+    store_grad<DQK / 32>(dk, invN, reinterpret_cast<bf16*>(a.dk), a.ld_qk, o0, kw0, n, h * DQK,
                          reinterpret_cast<const bf16*>(a.zpre), a.ld_z, a.zk_col + h * DQK, ql,
                          g);
-    store_grad<DV / 32>(tv, invN, reinterpret_cast<bf16*>(a.dv), a.ld_v, o0, kw0, n, h * DV,
-                        reinterpret_cast<const bf16*>(a.zpre), a.ld_z, a.zv_col + h * DV, ql, g);
+    store_grad<DV / 32>(dv, -HSTU_LN2 * invN, reinterpret_cast<bf16*>(a.dv), a.ld_v, o0, kw0, n,
+                        h * DV, reinterpret_cast<const bf16*>(a.zpre), a.ld_z,
+                        a.zv_col + h * DV, ql, g);
   }
   __syncthreads();
   float* gp = a.drab_pos + h * a.rab_stride;
   float* gt = a.drab_time + h * a.rab_stride;
   for (int i = tid; i < nP; i += 256)
     if (sm.gpos[i] != 0.0f) atomicAdd(&gp[i], sm.gpos[i] * invN);
-  if (tid < 32 && sm.gtime[tid] != 0.0f) atomicAdd(&gt[tbucket_from_clz(tid, nT)], sm.gtime[tid] * invN);
+  if (tid < 32 && sm.gtime[tid] != 0.0f)
+    atomicAdd(&gt[tbucket_from_clz(tid, nT)], sm.gtime[tid] * invN);
 }
 
-// ---------------------------------------------------------------------------
+// ===========================================================================
+// dQ (query-block major)
+// ===========================================================================
 template <int DQK, int DV>
-struct DqSmem {
-  using KT = LdsTile<DQK>;
-  using VR = LdsTile<DV>;
-  using TT = LdsTile<DQ_BN>;
-  uint32_t k[KT::S_DW * DQ_BN];    // K tile row-major (A operand of S^T = K Q^T)
-  uint32_t kt[TT::S_DW * DQK];     // K tile transposed (B operand of dQ += dS K)
-  uint32_t v[VR::S_DW * DQ_BN];    // V tile row-major (A operand of dA^T = V dO^T)
+struct DqBuf {
+  uint32_t k[LdsTile<DQK>::S_DW * DQ_BN];   // K tile row-major (A of S^T = K Q^T)
+  uint32_t kt[LdsTile<DQ_BN>::S_DW * DQK];  // K tile transposed (B of dQ += dS K)
+  uint32_t v[LdsTile<DV>::S_DW * DQ_BN];    // V tile row-major (A of dA^T = V dO^T)
   int32_t t[DQ_BN];
-  float tpos[1024];
-  float ttime[32];
+  int64_t t64[DQ_BN];
 };
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(256, (DQK >= 128 || DV >= 128) ? 1 : 2) void k_attn_bwd_dq(AttnArgs a) {
+struct DqSmem {
+  DqBuf<DQK, DV> buf[2];
+  float tpos[1024];
+  float ttime[32];
+  float tfar[32];
+};
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
   using KT = LdsTile<DQK>;
   using VR = LdsTile<DV>;
   using TT = LdsTile<DQ_BN>;
@@ -356,15 +484,23 @@ __global__ __launch_bounds__(256, (DQK >= 128 || DV >= 128) ? 1 : 2) void k_attn
   const int n = a.seq_offsets[b + 1] - o0;
   const int c = a.num_cand ? a.num_cand[b] : 0;
   const int nh = n - c;
-  const bool wide = a.seq_flags[b] & 1;
+  const int flags = a.seq_flags[b];
+  const bool wide = flags & 1;
+  const bool sorted = flags & 2;
   const int nP = a.nP, nT = a.nT;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int ql = lane & 31, g = lane >> 5;
   {
     const float* rp = a.rab_pos + h * a.rab_stride;
-    const float* rt = a.rab_time + h * a.rab_stride;
-    for (int i = tid; i < nP; i += 256) sm.tpos[i] = rp[i];
-    if (tid < 32) sm.ttime[tid] = rt[tbucket_from_clz(tid, nT)];
+    const float* rtb = a.rab_time + h * a.rab_stride;
+    for (int i = tid; i < nP; i += 256) sm.tpos[i] = rp[i] * HSTU_NEG_LOG2E;
+    if (tid < 32) {
+      const float tv = rtb[tbucket_from_clz(tid, nT)];
+      sm.ttime[tid] = tv * HSTU_NEG_LOG2E;
+      sm.tfar[tid] = (rp[nP - 1] + tv) * HSTU_NEG_LOG2E;
+    }
   }
   const int rb0 = m * ATTN_BWD_BM;
   const int rb1 = min(rb0 + ATTN_BWD_BM, n);
@@ -373,116 +509,178 @@ __global__ __launch_bounds__(256, (DQK >= 128 || DV >= 128) ? 1 : 2) void k_attn
   const int iq = r0 + ql;
   const bool qvalid = iq < n;
   const int pI = min(iq, nh);
-  int32_t ti1 = 0;
-  int64_t ti64 = 0;
-  if (qvalid) {
-    if (wide) ti64 = a.ts[o0 + iq];
-    else ti1 = a.rel_t[o0 + iq] + 1;
-  }
-  const bf16* qb = reinterpret_cast<const bf16*>(a.q);
-  const bf16* kbp = reinterpret_cast<const bf16*>(a.k);
-  const bf16* vbp = reinterpret_cast<const bf16*>(a.v);
-  const bf16* dob = reinterpret_cast<const bf16*>(a.dout);
+  const int64_t* tsq = a.ts + o0;
+  const int32_t ti1 = (qvalid && !wide) ? a.rel_t[o0 + iq] + 1 : 0;
+  const int64_t tq64 = (qvalid && wide) ? tsq[iq] : 0;
+
+  const bf16* qb = reinterpret_cast<const bf16*>(a.q) + (int64_t)o0 * a.ld_qk + h * DQK;
+  const bf16* kh_ = reinterpret_cast<const bf16*>(a.k) + (int64_t)o0 * a.ld_qk + h * DQK;
+  const bf16* vh_ = reinterpret_cast<const bf16*>(a.v) + (int64_t)o0 * a.ld_v + h * DV;
+  const bf16* dob = reinterpret_cast<const bf16*>(a.dout) + (int64_t)o0 * a.ld_dout + h * DV;
   bf16x8 qr[DQK / 16], orr[DV / 16];
 #pragma unroll
   for (int ch = 0; ch < DQK / 16; ++ch)
-    qr[ch] = qvalid ? *reinterpret_cast<const bf16x8*>(qb + (int64_t)(o0 + iq) * a.ld_qk +
-                                                       h * DQK + ch * 16 + 8 * g)
+    qr[ch] = qvalid ? *reinterpret_cast<const bf16x8*>(qb + (int64_t)iq * a.ld_qk + ch * 16 + 8 * g)
                     : bf16x8{};
 #pragma unroll
   for (int ch = 0; ch < DV / 16; ++ch)
-    orr[ch] = qvalid ? *reinterpret_cast<const bf16x8*>(dob + (int64_t)(o0 + iq) * a.ld_dout +
-                                                        h * DV + ch * 16 + 8 * g)
+    orr[ch] = qvalid ? *reinterpret_cast<const bf16x8*>(dob + (int64_t)iq * a.ld_dout + ch * 16 +
+                                                        8 * g)
                      : bf16x8{};
   f32x16 dq[DQK / 32];
 #pragma unroll
   for (int d = 0; d < DQK / 32; ++d) dq[d] = f32x16{};
 
   const int ktiles = (rb1 + DQ_BN - 1) / DQ_BN;
-  for (int kt = 0; kt < ktiles; ++kt) {
+  auto skip = [&](int kt) {
+    const int j0 = kt * DQ_BN;
+    return j0 >= nh && j0 + DQ_BN <= rb0;
+  };
+  auto next_tile = [&](int kt) { return skip(kt + 1) ? rb0 / DQ_BN : kt + 1; };
+
+  Stage2<DQK, DQ_BN> sk;
+  // V rows: row-major only, 16-byte chunks
+  constexpr int VCPR = DV / 8;
+  constexpr int VN = (DQ_BN * VCPR + 255) / 256;
+  u32x4 svv[VN];
+  int32_t st = 0;
+  int64_t st64 = 0;
+  auto load_tile = [&](int kt) {
+    const int j0 = kt * DQ_BN;
+    sk.load(kh_, a.ld_qk, j0, n, tid);
+#pragma unroll
+    for (int s = 0; s < VN; ++s) {
+      const int idx = tid + 256 * s;
+      const int row = idx / VCPR, ch = idx % VCPR;
+      const int j = j0 + row;
+      svv[s] = (idx < DQ_BN * VCPR && j < n) ? ld16(vh_ + (int64_t)j * a.ld_v + ch * 8)
+                                             : u32x4{0, 0, 0, 0};
+    }
+    if (tid < DQ_BN) {
+      const int j = j0 + tid;
+      st = (j < n && !wide) ? a.rel_t[o0 + j] : 0;
+      st64 = (j < n && wide) ? tsq[j] : 0;
+    }
+  };
+  auto store_tile = [&](DqBuf<DQK, DV>& Bf) {
+    sk.store(Bf.k, Bf.kt, tid);
+#pragma unroll
+    for (int s = 0; s < VN; ++s) {
+      const int idx = tid + 256 * s;
+      if (idx < DQ_BN * VCPR) {
+        const int row = idx / VCPR, ch = idx % VCPR;
+        *reinterpret_cast<u32x4*>(&Bf.v[VR::off(row, ch * 4)]) = svv[s];
+      }
+    }
+    if (tid < DQ_BN) {
+      Bf.t[tid] = st;
+      Bf.t64[tid] = st64;
+    }
+  };
+
+  int kt = 0;
+  if (kt < ktiles && skip(kt)) kt = rb0 / DQ_BN;
+  if (kt < ktiles) {
+    load_tile(kt);
+    store_tile(sm.buf[0]);
+  }
+  __syncthreads();
+  int cur = 0;
+  while (kt < ktiles) {
+    const int nk = next_tile(kt);
+    const bool has_next = nk < ktiles;
+    if (has_next) load_tile(nk);
+    const DqBuf<DQK, DV>& B = sm.buf[cur];
     const int j0 = kt * DQ_BN;
     const int j1 = min(j0 + DQ_BN, n);
-    if (j0 >= nh && (j1 <= rb0 || j0 >= rb1)) continue;
-    __syncthreads();
-    stage_both<DQK, DQ_BN>(kbp, a.ld_qk, o0, j0, j1, h * DQK, sm.k, sm.kt, tid);
-    {
-      constexpr int CPR = DV / 8;
-#pragma unroll
-      for (int s = 0; s < (DQ_BN * CPR + 255) / 256; ++s) {
-        const int idx = tid + 256 * s;
-        if (idx < DQ_BN * CPR) {
-          const int row = idx / CPR, ch = idx % CPR;
-          const int j = j0 + row;
-          u32x4 val = {0, 0, 0, 0};
-          if (j < j1) val = ld16(vbp + (int64_t)(o0 + j) * a.ld_v + h * DV + ch * 8);
-          *reinterpret_cast<u32x4*>(&sm.v[VR::off(row, ch * 4)]) = val;
-        }
-      }
-    }
-    if (tid < DQ_BN) sm.t[tid] = (j0 + tid < n && !wide) ? a.rel_t[o0 + j0 + tid] : 0;
-    __syncthreads();
-
-    if (r0 >= rw1) continue;
     const bool hist_rows = r0 < nh;
     const bool cand_rows = rw1 > nh;
-    const bool active = (hist_rows && j0 <= min(rw1, nh) - 1) ||
-                        (cand_rows && (j0 < nh || (j0 < rw1 && j1 > max(r0, nh))));
-    if (!active) continue;
-    const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh);
-    const bool far = !need_mask && !wide && (min(r0, nh) - min(j1 - 1, nh) >= nP - 1);
+    const bool active = (r0 < rw1) &&
+                        ((hist_rows && j0 <= min(rw1, nh) - 1) ||
+                         (cand_rows && (j0 < nh || (j0 < rw1 && j1 > max(r0, nh)))));
+    if (active) {
+      const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh);
+      const bool far = !need_mask && !wide && (min(r0, nh) - min(j1 - 1, nh) >= nP - 1);
+      int mode = 3;  // 0 constant per row, 1 one threshold, 2 gather, 3 general
+      int cF = 0, cL = 0;
+      if (far) {
+        cF = tclz_narrow(ti1, B.t[0]);
+        cL = tclz_narrow(ti1, B.t[j1 - 1 - j0]);
+        mode = __all(sorted && cL == cF) ? 0 : (__all(sorted && cL - cF <= 1) ? 1 : 2);
+      }
+      const float ba = sm.tfar[cF], bb = sm.tfar[min(cF + 1, 31)];
+      const int32_t thr = (cL == cF) ? INT32_MAX : ti1 - (1 << (31 - cF));
+      const int dI = pI - j0 - 4 * g, pmin = pI - nh;
+      const int lim = (iq < nh ? iq : nh - 1) - j0 - 4 * g, slf = iq - j0 - 4 * g;
 
-    bf16x8 dsk[4];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      f32x16 sacc = f32x16{}, dacc = f32x16{};
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x16 sacc = f32x16{}, dacc = f32x16{};
 #pragma unroll
-      for (int ch = 0; ch < DQK / 16; ++ch) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&sm.k[KT::off(hf * 32 + ql, ch * 8 + 4 * g)]);
-        sacc = mfma32(ka, qr[ch], sacc);
-      }
-#pragma unroll
-      for (int ch = 0; ch < DV / 16; ++ch) {
-        const bf16x8 va =
-            *reinterpret_cast<const bf16x8*>(&sm.v[VR::off(hf * 32 + ql, ch * 8 + 4 * g)]);
-        dacc = mfma32(va, orr[ch], dacc);
-      }
-#pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        const int kk0 = hf * 32 + 8 * aa + 4 * g;
-        const i32x4 tj = *reinterpret_cast<const i32x4*>(&sm.t[kk0]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + kk0 + r;
-          int cl;
-          if (wide) cl = tclz_wide(ti64, j < n ? a.ts[o0 + j] : ti64);
-          else cl = tclz_narrow(ti1, tj[r]);
-          bool ok = true;
-          float bias;
-          if (far) {
-            bias = sm.tpos[nP - 1] + sm.ttime[cl];
-          } else {
-            ok = (iq < nh) ? (j <= iq) : (j < nh || j == iq);
-            bias = sm.tpos[pbucket(pI, min(j, nh), nP)] + sm.ttime[cl];
-          }
-          const float s = sacc[4 * aa + r] + bias;
-          float sig;
-          const float p = silu_from_parts(s, sig);
-          float ds = dacc[4 * aa + r] * fmaf(p, 1.0f - sig, sig);
-          if (need_mask && !ok) ds = 0.0f;
-          dsk[hf * 2 + (aa >> 1)][(aa & 1) * 4 + r] = (bf16)ds;
+        for (int ch = 0; ch < DQK / 16; ++ch) {
+          const bf16x8 ka =
+              *reinterpret_cast<const bf16x8*>(&B.k[KT::off(hf * 32 + ql, ch * 8 + 4 * g)]);
+          sacc = mfma32(ka, qr[ch], sacc);
         }
+#pragma unroll
+        for (int ch = 0; ch < DV / 16; ++ch) {
+          const bf16x8 va =
+              *reinterpret_cast<const bf16x8*>(&B.v[VR::off(hf * 32 + ql, ch * 8 + 4 * g)]);
+          dacc = mfma32(va, orr[ch], dacc);
+        }
+        bf16x8 dsk[2];
+        auto elems = [&](auto bias_of, auto masked) {
+#pragma unroll
+          for (int aa = 0; aa < 4; ++aa) {
+            const int kk0 = hf * 32 + 8 * aa + 4 * g;
+            const i32x4 tj = *reinterpret_cast<const i32x4*>(&B.t[kk0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int kc = hf * 32 + 8 * aa + r;
+              const float sb = fmaf(sacc[4 * aa + r], HSTU_NEG_LOG2E, bias_of(kc, tj[r]));
+              float sig, p;
+              silu_parts(sb, sig, p);
+              float ds = dacc[4 * aa + r] * silu_deriv(sig, p);
+              if constexpr (decltype(masked)::value)
+                ds = (kc <= lim || kc == slf) ? ds : 0.0f;
+              dsk[aa >> 1][(aa & 1) * 4 + r] = (bf16)ds;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
+        auto bgen = [&](int kc) { return min(max(max(dI - kc, pmin), 0), nP - 1); };
+        if (mode == 0) {
+          elems([&](int, int32_t) { return ba; }, bconst<false>{});
+        } else if (mode == 1) {
+          elems([&](int, int32_t t) { return t <= thr ? ba : bb; }, bconst<false>{});
+        } else if (mode == 2) {
+          elems([&](int, int32_t t) { return sm.tfar[tclz_narrow(ti1, t)]; }, bconst<false>{});
+        } else if (!wide) {
+          auto bias = [&](int kc, int32_t t) {
+            return sm.tpos[bgen(kc)] + sm.ttime[tclz_narrow(ti1, t)];
+          };
+          if (need_mask) elems(bias, bconst<true>{});
+          else elems(bias, bconst<false>{});
+        } else {
+          elems([&](int kc, int32_t) {
+                  return sm.tpos[bgen(kc)] + sm.ttime[tclz_wide(tq64, B.t64[kc + 4 * g])];
+                },
+                bconst<true>{});
+        }
+#pragma unroll
+        for (int d = 0; d < DQK / 32; ++d)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 kbv = *reinterpret_cast<const bf16x8*>(
+                &B.kt[TT::off(d * 32 + ql, 8 * (2 * hf + u) + 4 * g)]);
+            dq[d] = mfma32(dsk[u], kbv, dq[d]);
+          }
       }
     }
-#pragma unroll
-    for (int d = 0; d < DQK / 32; ++d) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x8 kb =
-            *reinterpret_cast<const bf16x8*>(&sm.kt[TT::off(d * 32 + ql, 8 * u + 4 * g)]);
-        dq[d] = mfma32(dsk[u], kb, dq[d]);
-      }
-    }
+    if (has_next) store_tile(sm.buf[cur ^ 1]);
+    __syncthreads();
+    kt = nk;
+    cur ^= 1;
   }
   if (r0 >= rw1) return;
   const float invN = 1.0f / (float)(a.norm_mode == 0 ? a.norm_len : n);
