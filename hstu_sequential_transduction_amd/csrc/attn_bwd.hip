@@ -262,173 +262,211 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
     }
   };
 
-  int i0 = k0;
-  if (i0 < qend) load_tile(i0);
-  if (NBUF == 2 && i0 < qend) store_tile(sm.buf[0]);
-  __syncthreads();
-  int cur = 0;
-  while (i0 < qend) {
-    const int ni = i0 + KV_QT;
-    const bool has_next = ni < qend;
-    if (NBUF == 1) {
-      store_tile(sm.buf[0]);
-      __syncthreads();
-      if (has_next) load_tile(ni);
-    } else if (has_next) {
-      load_tile(ni);
+  // Query tiles split into a near phase (tiles that may need masks or per-element
+  // buckets) and a far phase: every row of the tile is at least nP-1 positions
+  // after every key of the workgroup and no candidate key is involved, so the
+  // position bucket is nP-1 and no mask applies (rows past qend and keys past n
+  // are zero-filled and contribute nothing).
+  int far_start = qend;
+  if (!wide && k1 <= nh) {
+    const int need = k1 - 1 + nP - 1;  // first row with p(i) - p(k1-1) >= nP-1
+    if (need <= nh) far_start = min(qend, k0 + ((max(need - k0, 0) + KV_QT - 1) / KV_QT) * KV_QT);
+  }
+
+  // per-lane running sums of the far phase: time buckets (curB, curB+1), position nP-1
+  int curB = -1;
+  float run_tot = 0.0f, run_a = 0.0f, ptot = 0.0f;
+  auto flush_time = [&]() {
+    if (curB >= 0) {
+      if (run_a != 0.0f) atomicAdd(&sm.gtime[curB], run_a);
+      if (run_tot - run_a != 0.0f) atomicAdd(&sm.gtime[curB + 1], run_tot - run_a);
     }
-    const KvBuf<DQK, DV>& B = sm.buf[NBUF == 2 ? cur : 0];
+    ptot += run_tot;
+    run_tot = 0.0f;
+    run_a = 0.0f;
+  };
 
-    if (kw0 < kw1) {
+  // S = Q K^T and dA = dO V^T for the 32-row half qh of the staged tile
+  auto mm_sd = [&](const KvBuf<DQK, DV>& B, int qh, f32x16& sacc, f32x16& dacc) {
+    sacc = f32x16{};
+    dacc = f32x16{};
 #pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        const int ir0 = i0 + qh * 32;                 // first row of this half
-        const int ir1 = min(ir0 + 32, qend);          // end of its valid rows
-        bool active;
-        if (kw0 < nh) active = ir1 - 1 >= kw0;        // history keys: rows at or after them
-        else active = ir0 < kw1 && ir1 > kw0;         // candidate keys: themselves
-        if (!active || ir0 >= ir1) continue;
-        const bool need_mask = (ir0 < kw1 - 1) || (kw1 > nh && ir1 > nh) || (ir1 - ir0 < 32) ||
-                               (kw1 - kw0 < 32);
-        const bool far = !need_mask && !wide && (min(ir0, nh) - min(kw1 - 1, nh) >= nP - 1);
-
-        f32x16 sacc = f32x16{}, dacc = f32x16{};
+    for (int ch = 0; ch < DQK / 16; ++ch) {
+      const bf16x8 qa =
+          *reinterpret_cast<const bf16x8*>(&B.q[QT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
+      sacc = mfma32(qa, kr[ch], sacc);
+    }
 #pragma unroll
-        for (int ch = 0; ch < DQK / 16; ++ch) {
-          const bf16x8 qa =
-              *reinterpret_cast<const bf16x8*>(&B.q[QT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
-          sacc = mfma32(qa, kr[ch], sacc);
-        }
+    for (int ch = 0; ch < DV / 16; ++ch) {
+      const bf16x8 oa =
+          *reinterpret_cast<const bf16x8*>(&B.o[OT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
+      dacc = mfma32(oa, vr[ch], dacc);
+    }
+  };
+  // dV += P'^T dO ; dK += dS^T Q   (k = the 32 rows of half qh)
+  auto mm_grad = [&](const KvBuf<DQK, DV>& B, int qh, const bf16x8 (&pp)[2],
+                     const bf16x8 (&dd)[2]) {
 #pragma unroll
-        for (int ch = 0; ch < DV / 16; ++ch) {
-          const bf16x8 oa =
-              *reinterpret_cast<const bf16x8*>(&B.o[OT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
-          dacc = mfma32(oa, vr[ch], dacc);
-        }
-
-        // lane = key jk; element r is row i = ir0 + 4g + kc, kc = 8*(r/4) + r%4
-        bf16x8 pp[2], dd[2];
-        const int ib = ir0 + 4 * g;
-        auto elems = [&](auto bias_of, auto grad_of, auto masked, int lo, int hi) {
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int aa = 0; aa < 4; ++aa) {
-            const i32x4 t4 = *reinterpret_cast<const i32x4*>(&B.t1[qh * 32 + 8 * aa + 4 * g]);
+      for (int d = 0; d < DV / 32; ++d) {
+        const bf16x8 ob = *reinterpret_cast<const bf16x8*>(
+            &B.ot[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
+        dv[d] = mfma32(pp[u], ob, dv[d]);
+      }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int kc = 8 * aa + r;
-              const int e = 4 * aa + r;
-              const float sb = fmaf(sacc[e], HSTU_NEG_LOG2E, bias_of(kc, t4[r]));
-              float sig, p;
-              silu_parts(sb, sig, p);
-              float ds = dacc[e] * silu_deriv(sig, p);
-              if constexpr (decltype(masked)::value) {
-                const bool ok = kc >= lo && kc <= hi;
-                p = ok ? p : 0.0f;
-                ds = ok ? ds : 0.0f;
-              }
-              grad_of(kc, t4[r], ds);
-              pp[aa >> 1][(aa & 1) * 4 + r] = (bf16)p;
-              dd[aa >> 1][(aa & 1) * 4 + r] = (bf16)ds;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        };
-
-        if (far) {
-          // Position bucket nP-1 everywhere.  Time bucket of (row i, key j) from
-          // x = t1_i - t_j: rows increase in time, so per lane cF = clz at the last
-          // row (smallest clz), cL = clz at the first row.
-          const int32_t tfirst = B.t1[qh * 32], tlast = B.t1[qh * 32 + 31];
-          const int cF = tclz_narrow(tlast, tj), cL = tclz_narrow(tfirst, tj);
-          const bool one = __all(sorted && cL - cF <= 1);
-          float stot = 0.0f, sA = 0.0f;
-          if (one) {
-            // rows with t1 >= thr are in bucket cF, the others in cF+1
-            const float ba = sm.tfar[cF], bb = sm.tfar[min(cF + 1, 31)];
-            const int32_t thr = (cL == cF) ? INT32_MIN : tj + (1 << (31 - cF));
-            elems([&](int, int32_t t) { return t >= thr ? ba : bb; },
-                  [&](int, int32_t t, float ds) {
-                    stot += ds;
-                    sA += t >= thr ? ds : 0.0f;
-                  },
-                  bconst<false>{}, 0, 0);
-            // reduce (bucket cF: sA, bucket cF+1: stot - sA) over the lanes
-            const int lo = wave_min_i(cF), hi = wave_max_i(cF) + 1;
-            for (int v = lo; v <= hi; ++v) {
-              float part = (cF == v ? sA : 0.0f) + (cF + 1 == v ? stot - sA : 0.0f);
-              part = wave_sum(part);
-              if (lane == 0 && part != 0.0f) atomicAdd(&sm.gtime[v], part);
-            }
-          } else {
-            elems([&](int, int32_t t) { return sm.tfar[tclz_narrow(t, tj)]; },
-                  [&](int, int32_t t, float ds) {
-                    stot += ds;
-                    atomicAdd(&sm.gtime[tclz_narrow(t, tj)], ds);
-                  },
-                  bconst<false>{}, 0, 0);
-          }
-          const float tot = wave_sum(stot);
-          if (lane == 0) atomicAdd(&sm.gpos[nP - 1], tot);
-        } else {
-          // general tile: per-element buckets and LDS-atomic histograms
-          // p(i) - p(j) = min(ib + kc, nh) - pJ ; rows allowed: history key -> i >= j,
-          // candidate key -> i == j; rows >= qend and keys >= n never.
-          const int pd0 = ib - pJ, pdmax = nh - pJ;
-          const int d0 = jk - ib;
-          const int lo = kvalid ? d0 : 1 << 20;
-          const int hi = min(jk < nh ? (1 << 20) : d0, qend - 1 - ib);
-          auto bidx = [&](int kc) { return min(max(min(pd0 + kc, pdmax), 0), nP - 1); };
-          if (!wide) {
-            elems([&](int kc, int32_t t) { return sm.tpos[bidx(kc)] + sm.ttime[tclz_narrow(t, tj)]; },
-                  [&](int kc, int32_t t, float ds) {
-                    if (ds != 0.0f) {
-                      atomicAdd(&sm.gpos[bidx(kc)], ds);
-                      atomicAdd(&sm.gtime[tclz_narrow(t, tj)], ds);
-                    }
-                  },
-                  bconst<true>{}, lo, hi);
-          } else {
-            elems([&](int kc, int32_t) {
-                    const int qi = qh * 32 + 4 * g + kc;
-                    return sm.tpos[bidx(kc)] + sm.ttime[tclz_wide(B.t64[qi], tj64)];
-                  },
-                  [&](int kc, int32_t, float ds) {
-                    if (ds != 0.0f) {
-                      const int qi = qh * 32 + 4 * g + kc;
-                      atomicAdd(&sm.gpos[bidx(kc)], ds);
-                      atomicAdd(&sm.gtime[tclz_wide(B.t64[qi], tj64)], ds);
-                    }
-                  },
-                  bconst<true>{}, lo, hi);
-          }
-        }
-
-        // dV += P'^T dO ; dK += dS^T Q   (k = the 32 rows of this half)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-#pragma unroll
-          for (int d = 0; d < DV / 32; ++d) {
-            const bf16x8 ob = *reinterpret_cast<const bf16x8*>(
-                &B.ot[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
-            dv[d] = mfma32(pp[u], ob, dv[d]);
-          }
-#pragma unroll
-          for (int d = 0; d < DQK / 32; ++d) {
-            const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(
-                &B.qt[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
-            dk[d] = mfma32(dd[u], qbv, dk[d]);
-          }
-        }
+      for (int d = 0; d < DQK / 32; ++d) {
+        const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(
+            &B.qt[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
+        dk[d] = mfma32(dd[u], qbv, dk[d]);
       }
     }
+  };
 
-    if (NBUF == 2) {
-      if (has_next) store_tile(sm.buf[cur ^ 1]);
-      cur ^= 1;
+  // Element loop of one half: lane = key jk, element r is row ib + kc with
+  // kc = 8*(r/4) + r%4; bias_of(kc, t1) is pre-scaled, grad_of(kc, t1, ds).
+  auto elems = [&](const KvBuf<DQK, DV>& B, int qh, const f32x16& sacc, const f32x16& dacc,
+                   bf16x8 (&pp)[2], bf16x8 (&dd)[2], auto bias_of, auto grad_of, auto masked,
+                   int lo, int hi) {
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      const i32x4 t4 = *reinterpret_cast<const i32x4*>(&B.t1[qh * 32 + 8 * aa + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kc = 8 * aa + r;
+        const int e = 4 * aa + r;
+        const float sb = fmaf(sacc[e], HSTU_NEG_LOG2E, bias_of(kc, t4[r]));
+        float sig, p;
+        silu_parts(sb, sig, p);
+        float ds = dacc[e] * silu_deriv(sig, p);
+        if constexpr (decltype(masked)::value) {
+          const bool ok = kc >= lo && kc <= hi;
+          p = ok ? p : 0.0f;
+          ds = ok ? ds : 0.0f;
+        }
+        grad_of(kc, t4[r], ds);
+        pp[aa >> 1][(aa & 1) * 4 + r] = (bf16)p;
+        dd[aa >> 1][(aa & 1) * 4 + r] = (bf16)ds;
+      }
     }
+  };
+
+  // near-phase tile: per-half masks, per-element buckets, LDS-atomic histograms
+  auto near_tile = [&](const KvBuf<DQK, DV>& B, int i0) {
+    if (kw0 >= kw1) return;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int ir0 = i0 + qh * 32;
+      const int ir1 = min(ir0 + 32, qend);
+      bool active;
+      if (kw0 < nh) active = ir1 - 1 >= kw0;
+      else active = ir0 < kw1 && ir1 > kw0;
+      if (!active || ir0 >= ir1) continue;
+      f32x16 sacc, dacc;
+      mm_sd(B, qh, sacc, dacc);
+      bf16x8 pp[2], dd[2];
+      const int ib = ir0 + 4 * g;
+      // p(i) - p(j) = min(ib + kc, nh) - pJ ; allowed rows: history key -> i >= j,
+      // candidate key -> i == j; rows >= qend and keys >= n never.
+      const int pd0 = ib - pJ, pdmax = nh - pJ;
+      const int d0 = jk - ib;
+      const int lo = kvalid ? d0 : 1 << 20;
+      const int hi = min(jk < nh ? (1 << 20) : d0, qend - 1 - ib);
+      auto bidx = [&](int kc) { return min(max(min(pd0 + kc, pdmax), 0), nP - 1); };
+      if (!wide) {
+        elems(B, qh, sacc, dacc, pp, dd,
+              [&](int kc, int32_t t) { return sm.tpos[bidx(kc)] + sm.ttime[tclz_narrow(t, tj)]; },
+              [&](int kc, int32_t t, float ds) {
+                atomicAdd(&sm.gpos[bidx(kc)], ds);
+                atomicAdd(&sm.gtime[tclz_narrow(t, tj)], ds);
+              },
+              bconst<true>{}, lo, hi);
+      } else {
+        elems(B, qh, sacc, dacc, pp, dd,
+              [&](int kc, int32_t) {
+                return sm.tpos[bidx(kc)] +
+                       sm.ttime[tclz_wide(B.t64[qh * 32 + 4 * g + kc], tj64)];
+              },
+              [&](int kc, int32_t, float ds) {
+                atomicAdd(&sm.gpos[bidx(kc)], ds);
+                atomicAdd(&sm.gtime[tclz_wide(B.t64[qh * 32 + 4 * g + kc], tj64)], ds);
+              },
+              bconst<true>{}, lo, hi);
+      }
+      mm_grad(B, qh, pp, dd);
+    }
+  };
+
+  // far-phase tile: no masks, position bucket nP-1; with sorted timestamps a
+  // lane's time bucket changes at most once inside a half in the common case
+  auto far_tile = [&](const KvBuf<DQK, DV>& B, int i0) {
+    if (kw0 >= kw1) return;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int ir0 = i0 + qh * 32;
+      if (ir0 >= qend) break;
+      const int last = min(31, qend - 1 - ir0);
+      const int cF = tclz_narrow(B.t1[qh * 32 + last], tj);
+      const int cL = tclz_narrow(B.t1[qh * 32], tj);
+      const bool one = __all(!kvalid || (sorted && cL - cF <= 1));
+      f32x16 sacc, dacc;
+      mm_sd(B, qh, sacc, dacc);
+      bf16x8 pp[2], dd[2];
+      if (one) {
+        if (kvalid && cF != curB) {
+          flush_time();
+          curB = cF;
+        }
+        const float ba = sm.tfar[cF], bb = sm.tfar[min(cF + 1, 31)];
+        const int32_t thr = (cL == cF) ? INT32_MIN : tj + (1 << (31 - cF));
+        elems(B, qh, sacc, dacc, pp, dd, [&](int, int32_t t) { return t >= thr ? ba : bb; },
+              [&](int, int32_t t, float ds) {
+                run_tot += ds;
+                run_a += t >= thr ? ds : 0.0f;
+              },
+              bconst<false>{}, 0, 0);
+      } else {
+        elems(B, qh, sacc, dacc, pp, dd,
+              [&](int, int32_t t) { return sm.tfar[tclz_narrow(t, tj)]; },
+              [&](int, int32_t t, float ds) {
+                ptot += ds;
+                atomicAdd(&sm.gtime[tclz_narrow(t, tj)], ds);
+              },
+              bconst<false>{}, 0, 0);
+      }
+      mm_grad(B, qh, pp, dd);
+    }
+  };
+
+  // staged tile pipeline over [ibeg, iend) in steps of KV_QT
+  auto run_phase = [&](int ibeg, int iend, auto body) {
+    if (ibeg >= iend) return;
+    load_tile(ibeg);
+    if (NBUF == 2) store_tile(sm.buf[0]);
     __syncthreads();
-    i0 = ni;
-  }
+    int cur = 0;
+    for (int i0 = ibeg; i0 < iend; i0 += KV_QT) {
+      const int ni = i0 + KV_QT;
+      const bool has_next = ni < iend;
+      if (NBUF == 1) {
+        store_tile(sm.buf[0]);
+        __syncthreads();
+        if (has_next) load_tile(ni);
+      } else if (has_next) {
+        load_tile(ni);
+      }
+      body(sm.buf[NBUF == 2 ? cur : 0], i0);
+      if (NBUF == 2) {
+        if (has_next) store_tile(sm.buf[cur ^ 1]);
+        cur ^= 1;
+      }
+      __syncthreads();
+    }
+  };
+  run_phase(k0, far_start, near_tile);
+  run_phase(far_start, qend, far_tile);
+  flush_time();
+  if (ptot != 0.0f) atomicAdd(&sm.gpos[nP - 1], ptot);
 
   const float invN = 1.0f / (float)(a.norm_mode == 0 ? a.norm_len : n);
   if (kw0 < kw1) {
