@@ -31,6 +31,7 @@
 #include "bias.h"
 #include "common.h"
 #include "internal.h"
+#include "lds.h"
 
 namespace hstu {
 
@@ -117,20 +118,37 @@ struct Stage2 {
 
 // Store a 32-row x (32*NB)-column accumulator block (rows 8*(r/4)+4g+r%4,
 // column lane%32 of each 32-column block) as bf16, optionally times SiLU'(Z).
+// The Z loads use clamped rows so that they issue back to back without
+// per-element branches; only the stores are predicated.
 template <int NB>
 HSTU_DEV void store_grad(const f32x16* acc, float scale, bf16* dst, int64_t ld, int o0,
                          int row0, int n, int col0, const bf16* z, int64_t ldz, int64_t zcol,
                          int ql, int g) {
+  float f[NB][16];
+#pragma unroll
+  for (int d = 0; d < NB; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) f[d][r] = scale;
+  if (z) {
+    bf16 zv[NB][16];
+#pragma unroll
+    for (int d = 0; d < NB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = min(row0 + 8 * (r >> 2) + 4 * g + (r & 3), n - 1);
+        zv[d][r] = z[(int64_t)(o0 + i) * ldz + zcol + d * 32 + ql];
+      }
+#pragma unroll
+    for (int d = 0; d < NB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) f[d][r] *= silu_grad_f((float)zv[d][r]);
+  }
 #pragma unroll
   for (int d = 0; d < NB; ++d) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = row0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (i < n) {
-        float v = acc[d][r] * scale;
-        if (z) v *= silu_grad_f((float)z[(int64_t)(o0 + i) * ldz + zcol + d * 32 + ql]);
-        dst[(int64_t)(o0 + i) * ld + col0 + d * 32 + ql] = (bf16)v;
-      }
+      if (i < n) dst[(int64_t)(o0 + i) * ld + col0 + d * 32 + ql] = (bf16)(acc[d][r] * f[d][r]);
     }
   }
 }
@@ -140,23 +158,23 @@ HSTU_DEV void store_grad(const f32x16* acc, float scale, bf16* dst, int64_t ld, 
 // ===========================================================================
 template <int DQK, int DV>
 struct KvShape {
-  static constexpr bool BIG = (DQK >= 128 || DV >= 128);
-  static constexpr int NBUF = BIG ? 2 : 1;  // d = 128 runs one workgroup per CU anyway
+  static constexpr bool BIG = (DQK >= 128 || DV >= 128);  // one wave per SIMD
 };
 
+// One staged query tile: row-major Q and dO (filled by DMA, read along rows for
+// S and dA and down columns for the dK and dV products) and the row times.
 template <int DQK, int DV>
 struct KvBuf {
-  uint32_t q[LdsTile<DQK>::S_DW * KV_QT];   // Q tile row-major  (A of S = Q K^T)
-  uint32_t qt[LdsTile<KV_QT>::S_DW * DQK];  // Q tile transposed (B of dK += dS^T Q)
-  uint32_t o[LdsTile<DV>::S_DW * KV_QT];    // dO tile row-major (A of dA = dO V^T)
-  uint32_t ot[LdsTile<KV_QT>::S_DW * DV];   // dO tile transposed (B of dV += P^T dO)
-  int32_t t1[KV_QT];                        // query times + 1 (relative)
-  int64_t t64[KV_QT];                       // query times (absolute, spans >= 2^31 s)
+  uint8_t q[SwzTile<DQK>::bytes(KV_QT)];
+  uint8_t o[SwzTile<DV>::bytes(KV_QT)];
+  int32_t t[KV_QT];    // query times relative to the sequence minimum (narrow)
+  int64_t t64[KV_QT];  // query times (wide sequences)
 };
 
-template <int DQK, int DV>
-struct KvSmem {
-  KvBuf<DQK, DV> buf[KvShape<DQK, DV>::NBUF];
+// Bias tables and gradient histograms (a separate LDS object from the two tile
+// buffers, so that the compiler can see that DMA into one buffer never touches
+// them or the other buffer and needs no wait before their accesses).
+struct KvTables {
   float tpos[1024];   // rab_pos * -log2 e
   float ttime[32];    // rab_time[bucket(c)] * -log2 e, by clz index
   float tfar[32];     // (rab_pos[nP-1] + rab_time[bucket(c)]) * -log2 e
@@ -166,22 +184,23 @@ struct KvSmem {
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_bwd_dkdv(AttnArgs a) {
-  using QT = LdsTile<DQK>;
-  using OT = LdsTile<DV>;
-  using TT = LdsTile<KV_QT>;
-  constexpr int NBUF = KvShape<DQK, DV>::NBUF;
-  __shared__ __attribute__((aligned(16))) KvSmem<DQK, DV> sm;
+  __shared__ __attribute__((aligned(1024))) KvBuf<DQK, DV> kvb0;
+  __shared__ __attribute__((aligned(1024))) KvBuf<DQK, DV> kvb1;
+  __shared__ KvTables sm;
 
   const int w = blockIdx.x;
   const int n_items = a.counters[0];
   if (w >= n_items * a.H) return;
+  // work-item fields are wave-uniform: keep them in scalar registers so that
+  // buffer descriptors built from them need no per-lane handling
   const int it = w / a.H, h = w - it * a.H;
-  const int b = a.items[2 * it], kb = a.items[2 * it + 1];
-  const int o0 = a.seq_offsets[b];
-  const int n = a.seq_offsets[b + 1] - o0;
-  const int c = a.num_cand ? a.num_cand[b] : 0;
+  const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
+  const int kb = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  const int o0 = __builtin_amdgcn_readfirstlane(a.seq_offsets[b]);
+  const int n = __builtin_amdgcn_readfirstlane(a.seq_offsets[b + 1]) - o0;
+  const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;
   const int nh = n - c;
-  const int flags = a.seq_flags[b];
+  const int flags = __builtin_amdgcn_readfirstlane(a.seq_flags[b]);
   const bool wide = flags & 1;
   const bool sorted = flags & 2;
   const int nP = a.nP, nT = a.nT;
@@ -213,7 +232,8 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   const bool kvalid = jk < n;
   const int pJ = min(jk, nh);
   const int64_t* tsq = a.ts + o0;
-  const int32_t tj = (kvalid && !wide) ? a.rel_t[o0 + jk] : 0;
+  // key time minus one: tclz_narrow(t_i - tjm) is the bucket of t_i - t_j
+  const int32_t tjm = ((kvalid && !wide) ? a.rel_t[o0 + jk] : 0) - 1;
   const int64_t tj64 = (kvalid && wide) ? tsq[jk] : 0;
 
   const bf16* qh_ = reinterpret_cast<const bf16*>(a.q) + (int64_t)o0 * a.ld_qk + h * DQK;
@@ -240,25 +260,13 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
 
   // query tiles: [k0, qend); candidate keys are seen by themselves only
   const int qend = (k0 >= nh) ? k1 : n;
-  Stage2<DQK, KV_QT> sq;
-  Stage2<DV, KV_QT> so;
-  int32_t st1 = 0;
-  int64_t st64 = 0;
-  auto load_tile = [&](int i0) {
-    sq.load(qh_, a.ld_qk, i0, qend, tid);
-    so.load(doh, a.ld_dout, i0, qend, tid);
-    if (tid < KV_QT) {
-      const int i = i0 + tid;
-      st1 = (i < n && !wide) ? a.rel_t[o0 + i] + 1 : 0;
-      st64 = (i < n && wide) ? tsq[i] : 0;
-    }
-  };
-  auto store_tile = [&](KvBuf<DQK, DV>& Bf) {
-    sq.store(Bf.q, Bf.qt, tid);
-    so.store(Bf.o, Bf.ot, tid);
-    if (tid < KV_QT) {
-      Bf.t1[tid] = st1;
-      Bf.t64[tid] = st64;
+  // DMA of query tile i0 into Bf; rows >= qend arrive as zeros (times: rows >= n)
+  auto issue = [&](KvBuf<DQK, DV>& Bf, int i0) {
+    dma_tile<DQK, KV_QT, 4>(Bf.q, qh_, a.ld_qk, i0, qend, wave, lane);
+    dma_tile<DV, KV_QT, 4>(Bf.o, doh, a.ld_dout, i0, qend, wave, lane);
+    if (wave == 0) {
+      if (!wide) dma_words64(Bf.t, a.rel_t + o0, i0, n, lane);
+      else dma_dwords64(Bf.t64, tsq, i0, n, lane);
     }
   };
 
@@ -290,47 +298,42 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   auto mm_sd = [&](const KvBuf<DQK, DV>& B, int qh, f32x16& sacc, f32x16& dacc) {
     sacc = f32x16{};
     dacc = f32x16{};
+    bf16x8 qa[DQK / 16], oa[DV / 16];
 #pragma unroll
-    for (int ch = 0; ch < DQK / 16; ++ch) {
-      const bf16x8 qa =
-          *reinterpret_cast<const bf16x8*>(&B.q[QT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
-      sacc = mfma32(qa, kr[ch], sacc);
-    }
+    for (int ch = 0; ch < DQK / 16; ++ch) qa[ch] = lds_row8<DQK>(B.q, qh * 32 + ql, ch, g);
 #pragma unroll
-    for (int ch = 0; ch < DV / 16; ++ch) {
-      const bf16x8 oa =
-          *reinterpret_cast<const bf16x8*>(&B.o[OT::off(qh * 32 + ql, ch * 8 + 4 * g)]);
-      dacc = mfma32(oa, vr[ch], dacc);
-    }
+    for (int ch = 0; ch < DV / 16; ++ch) oa[ch] = lds_row8<DV>(B.o, qh * 32 + ql, ch, g);
+#pragma unroll
+    for (int ch = 0; ch < DQK / 16; ++ch) sacc = mfma32(qa[ch], kr[ch], sacc);
+#pragma unroll
+    for (int ch = 0; ch < DV / 16; ++ch) dacc = mfma32(oa[ch], vr[ch], dacc);
   };
   // dV += P'^T dO ; dK += dS^T Q   (k = the 32 rows of half qh)
   auto mm_grad = [&](const KvBuf<DQK, DV>& B, int qh, const bf16x8 (&pp)[2],
                      const bf16x8 (&dd)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      bf16x8 ob[DV / 32], qb[DQK / 32];
 #pragma unroll
-      for (int d = 0; d < DV / 32; ++d) {
-        const bf16x8 ob = *reinterpret_cast<const bf16x8*>(
-            &B.ot[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
-        dv[d] = mfma32(pp[u], ob, dv[d]);
-      }
+      for (int d = 0; d < DV / 32; ++d) ob[d] = lds_col8<DV>(B.o, qh * 32 + 16 * u, d * 32, lane);
 #pragma unroll
-      for (int d = 0; d < DQK / 32; ++d) {
-        const bf16x8 qbv = *reinterpret_cast<const bf16x8*>(
-            &B.qt[TT::off(d * 32 + ql, 8 * (qh * 2 + u) + 4 * g)]);
-        dk[d] = mfma32(dd[u], qbv, dk[d]);
-      }
+      for (int d = 0; d < DQK / 32; ++d)
+        qb[d] = lds_col8<DQK>(B.q, qh * 32 + 16 * u, d * 32, lane);
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d) dv[d] = mfma32(pp[u], ob[d], dv[d]);
+#pragma unroll
+      for (int d = 0; d < DQK / 32; ++d) dk[d] = mfma32(dd[u], qb[d], dk[d]);
     }
   };
 
   // Element loop of one half: lane = key jk, element r is row ib + kc with
-  // kc = 8*(r/4) + r%4; bias_of(kc, t1) is pre-scaled, grad_of(kc, t1, ds).
+  // kc = 8*(r/4) + r%4; bias_of(kc, t) is pre-scaled, grad_of(kc, t, ds).
   auto elems = [&](const KvBuf<DQK, DV>& B, int qh, const f32x16& sacc, const f32x16& dacc,
                    bf16x8 (&pp)[2], bf16x8 (&dd)[2], auto bias_of, auto grad_of, auto masked,
                    int lo, int hi) {
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
-      const i32x4 t4 = *reinterpret_cast<const i32x4*>(&B.t1[qh * 32 + 8 * aa + 4 * g]);
+      const i32x4 t4 = *reinterpret_cast<const i32x4*>(&B.t[qh * 32 + 8 * aa + 4 * g]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kc = 8 * aa + r;
@@ -375,10 +378,10 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
       auto bidx = [&](int kc) { return min(max(min(pd0 + kc, pdmax), 0), nP - 1); };
       if (!wide) {
         elems(B, qh, sacc, dacc, pp, dd,
-              [&](int kc, int32_t t) { return sm.tpos[bidx(kc)] + sm.ttime[tclz_narrow(t, tj)]; },
+              [&](int kc, int32_t t) { return sm.tpos[bidx(kc)] + sm.ttime[tclz_narrow(t, tjm)]; },
               [&](int kc, int32_t t, float ds) {
                 atomicAdd(&sm.gpos[bidx(kc)], ds);
-                atomicAdd(&sm.gtime[tclz_narrow(t, tj)], ds);
+                atomicAdd(&sm.gtime[tclz_narrow(t, tjm)], ds);
               },
               bconst<true>{}, lo, hi);
       } else {
@@ -406,8 +409,8 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
       const int ir0 = i0 + qh * 32;
       if (ir0 >= qend) break;
       const int last = min(31, qend - 1 - ir0);
-      const int cF = tclz_narrow(B.t1[qh * 32 + last], tj);
-      const int cL = tclz_narrow(B.t1[qh * 32], tj);
+      const int cF = tclz_narrow(B.t[qh * 32 + last], tjm);
+      const int cL = tclz_narrow(B.t[qh * 32], tjm);
       const bool one = __all(!kvalid || (sorted && cL - cF <= 1));
       f32x16 sacc, dacc;
       mm_sd(B, qh, sacc, dacc);
@@ -418,7 +421,8 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
           curB = cF;
         }
         const float ba = sm.tfar[cF], bb = sm.tfar[min(cF + 1, 31)];
-        const int32_t thr = (cL == cF) ? INT32_MIN : tj + (1 << (31 - cF));
+        // rows with t >= thr are in bucket cF, the others in cF + 1
+        const int32_t thr = (cL == cF) ? INT32_MIN : tjm + (1 << (31 - cF));
         elems(B, qh, sacc, dacc, pp, dd, [&](int, int32_t t) { return t >= thr ? ba : bb; },
               [&](int, int32_t t, float ds) {
                 run_tot += ds;
@@ -427,10 +431,10 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
               bconst<false>{}, 0, 0);
       } else {
         elems(B, qh, sacc, dacc, pp, dd,
-              [&](int, int32_t t) { return sm.tfar[tclz_narrow(t, tj)]; },
+              [&](int, int32_t t) { return sm.tfar[tclz_narrow(t, tjm)]; },
               [&](int, int32_t t, float ds) {
                 ptot += ds;
-                atomicAdd(&sm.gtime[tclz_narrow(t, tj)], ds);
+                atomicAdd(&sm.gtime[tclz_narrow(t, tjm)], ds);
               },
               bconst<false>{}, 0, 0);
       }
@@ -438,28 +442,24 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
     }
   };
 
-  // staged tile pipeline over [ibeg, iend) in steps of KV_QT
+  // double-buffered tile pipeline over [ibeg, iend) in steps of KV_QT: the DMA
+  // of tile t+1 runs while tile t is computed
+  // (unrolled by two so that every access names its buffer statically)
   auto run_phase = [&](int ibeg, int iend, auto body) {
     if (ibeg >= iend) return;
-    load_tile(ibeg);
-    if (NBUF == 2) store_tile(sm.buf[0]);
+    issue(kvb0, ibeg);
+    dma_wait();
     __syncthreads();
-    int cur = 0;
-    for (int i0 = ibeg; i0 < iend; i0 += KV_QT) {
-      const int ni = i0 + KV_QT;
-      const bool has_next = ni < iend;
-      if (NBUF == 1) {
-        store_tile(sm.buf[0]);
-        __syncthreads();
-        if (has_next) load_tile(ni);
-      } else if (has_next) {
-        load_tile(ni);
-      }
-      body(sm.buf[NBUF == 2 ? cur : 0], i0);
-      if (NBUF == 2) {
-        if (has_next) store_tile(sm.buf[cur ^ 1]);
-        cur ^= 1;
-      }
+    for (int i0 = ibeg; i0 < iend; i0 += 2 * KV_QT) {
+      const int i1 = i0 + KV_QT;
+      if (i1 < iend) issue(kvb1, i1);
+      body(kvb0, i0);
+      dma_wait();
+      __syncthreads();
+      if (i1 >= iend) break;
+      if (i1 + KV_QT < iend) issue(kvb0, i1 + KV_QT);
+      body(kvb1, i1);
+      dma_wait();
       __syncthreads();
     }
   };
