@@ -12,15 +12,17 @@
 //    waves of 32 keys keeping K and V in registers (B operands) and dK, dV in
 //    accumulators; it walks the 64-row query tiles that can see its keys
 //    (history keys: all later rows including every candidate; candidate keys:
-//    only themselves).  Q and dO tiles are staged once from HBM into both a
-//    row-major copy (A operands of S = Q K^T, dA = dO V^T) and a transposed
-//    copy (B operands of dK += dS^T Q, dV += P^T dO).  The rab-table gradients
-//    go to LDS histograms: on tiles where the position bucket saturates they
-//    are per-lane partial sums split at the row where the time bucket changes,
-//    reduced across the wave once per tile; elsewhere LDS atomics.
+//    only themselves).  Q and dO tiles arrive row-major by buffer->LDS DMA,
+//    double-buffered; they are read along rows as A operands of S = Q K^T and
+//    dA = dO V^T and down columns (transpose reads) as B operands of
+//    dK += dS^T Q and dV += P^T dO.  The rab-table gradients go to LDS
+//    histograms: tiles far enough from the keys (position bucket saturated,
+//    no mask) keep per-lane running sums flushed when a lane's time bucket
+//    changes; the other tiles use LDS atomics.
 //  * k_attn_bwd_dq: one workgroup per (sequence, 128-row query block, head),
 //    structured like the forward kernel: S^T = K Q^T and dA^T = V dO^T, then
-//    dQ += dS K with K^T staged in LDS.  No atomics on dQ.
+//    dQ += dS K with K read down its columns from the same row-major tile.
+//    No atomics on dQ.
 // SiLU is evaluated as in the forward kernel, s' = -log2(e) s, sigma =
 // 1/(1 + 2^s'), P' = s' sigma = -log2(e) SiLU(s), SiLU'(s) = sigma +
 // P' ln2 (sigma - 1); the -ln2 of P' is applied once to dV.
@@ -52,69 +54,6 @@ HSTU_DEV void silu_parts(float sb, float& sig, float& pp) {
 HSTU_DEV float silu_deriv(float sig, float pp) {
   return fmaf(pp, fmaf(sig, HSTU_LN2, -HSTU_LN2), sig);
 }
-
-// Register staging of R rows x D columns of a bf16 matrix for one tile: each
-// item is a (row pair, 8-column chunk); the same registers feed the row-major
-// LDS copy (two 16-byte writes) and the transposed copy (eight dword writes,
-// rows of the transposed tile are columns, rows permuted by kperm).
-template <int D, int R>
-struct Stage2 {
-  static constexpr int NCH = D / 8;
-  static constexpr int NITEM = (R / 2) * NCH;
-  static constexpr int NPT = (NITEM + 255) / 256;
-  u32x4 va[NPT], vb[NPT];
-
-  HSTU_DEV static void map(int idx, int& kp, int& cc) {
-    if (NCH >= 8) {
-      const int rest = idx >> 6;
-      kp = (rest & 3) * 8 + ((idx >> 3) & 7);
-      cc = (rest >> 2) * 8 + (idx & 7);
-    } else {
-      cc = idx % NCH;
-      kp = idx / NCH;
-    }
-  }
-  // rows [r0, r0+R) of `base` (row stride ld); rows >= rlim read as zero
-  HSTU_DEV void load(const bf16* base, int64_t ld, int r0, int rlim, int tid) {
-#pragma unroll
-    for (int s = 0; s < NPT; ++s) {
-      const int idx = tid + 256 * s;
-      va[s] = u32x4{0, 0, 0, 0};
-      vb[s] = u32x4{0, 0, 0, 0};
-      if (idx < NITEM) {
-        int kp, cc;
-        map(idx, kp, cc);
-        const int r = r0 + 2 * kp;
-        if (r < rlim) va[s] = ld16(base + (int64_t)r * ld + cc * 8);
-        if (r + 1 < rlim) vb[s] = ld16(base + (int64_t)(r + 1) * ld + cc * 8);
-      }
-    }
-  }
-  HSTU_DEV void store(uint32_t* rm, uint32_t* tr, int tid) const {
-    using RM = LdsTile<D>;
-    using TR = LdsTile<R>;
-#pragma unroll
-    for (int s = 0; s < NPT; ++s) {
-      const int idx = tid + 256 * s;
-      if (idx < NITEM) {
-        int kp, cc;
-        map(idx, kp, cc);
-        if (rm) {
-          *reinterpret_cast<u32x4*>(&rm[RM::off(2 * kp, cc * 4)]) = va[s];
-          *reinterpret_cast<u32x4*>(&rm[RM::off(2 * kp + 1, cc * 4)]) = vb[s];
-        }
-        if (tr) {
-          const int col = kperm(2 * kp) >> 1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            tr[TR::off(cc * 8 + 2 * e, col)] = (va[s][e] & 0xFFFFu) | (vb[s][e] << 16);
-            tr[TR::off(cc * 8 + 2 * e + 1, col)] = (va[s][e] >> 16) | (vb[s][e] & 0xFFFF0000u);
-          }
-        }
-      }
-    }
-  }
-};
 
 // Store a 32-row x (32*NB)-column accumulator block (rows 8*(r/4)+4g+r%4,
 // column lane%32 of each 32-column block) as bf16, optionally times SiLU'(Z).
@@ -489,18 +428,17 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
 // ===========================================================================
 // dQ (query-block major)
 // ===========================================================================
+// One staged key tile: row-major K (A of S^T = K Q^T along rows, B of
+// dQ += dS K down columns) and V (A of dA^T = V dO^T), and the key times.
 template <int DQK, int DV>
 struct DqBuf {
-  uint32_t k[LdsTile<DQK>::S_DW * DQ_BN];   // K tile row-major (A of S^T = K Q^T)
-  uint32_t kt[LdsTile<DQ_BN>::S_DW * DQK];  // K tile transposed (B of dQ += dS K)
-  uint32_t v[LdsTile<DV>::S_DW * DQ_BN];    // V tile row-major (A of dA^T = V dO^T)
-  int32_t t[DQ_BN];
-  int64_t t64[DQ_BN];
+  uint8_t k[SwzTile<DQK>::bytes(DQ_BN)];
+  uint8_t v[SwzTile<DV>::bytes(DQ_BN)];
+  int32_t t[DQ_BN];    // key times relative to the sequence minimum (narrow)
+  int64_t t64[DQ_BN];  // key times (wide sequences)
 };
 
-template <int DQK, int DV>
-struct DqSmem {
-  DqBuf<DQK, DV> buf[2];
+struct DqTables {
   float tpos[1024];
   float ttime[32];
   float tfar[32];
@@ -508,21 +446,21 @@ struct DqSmem {
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
-  using KT = LdsTile<DQK>;
-  using VR = LdsTile<DV>;
-  using TT = LdsTile<DQ_BN>;
-  __shared__ __attribute__((aligned(16))) DqSmem<DQK, DV> sm;
+  __shared__ __attribute__((aligned(1024))) DqBuf<DQK, DV> dqb0;
+  __shared__ __attribute__((aligned(1024))) DqBuf<DQK, DV> dqb1;
+  __shared__ DqTables sm;
 
   const int w = blockIdx.x;
   const int n_items = a.counters[0];
   if (w >= n_items * a.H) return;
   const int it = w / a.H, h = w - it * a.H;
-  const int b = a.items[2 * it], m = a.items[2 * it + 1];
-  const int o0 = a.seq_offsets[b];
-  const int n = a.seq_offsets[b + 1] - o0;
-  const int c = a.num_cand ? a.num_cand[b] : 0;
+  const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
+  const int m = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  const int o0 = __builtin_amdgcn_readfirstlane(a.seq_offsets[b]);
+  const int n = __builtin_amdgcn_readfirstlane(a.seq_offsets[b + 1]) - o0;
+  const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;
   const int nh = n - c;
-  const int flags = a.seq_flags[b];
+  const int flags = __builtin_amdgcn_readfirstlane(a.seq_flags[b]);
   const bool wide = flags & 1;
   const bool sorted = flags & 2;
   const int nP = a.nP, nT = a.nT;
@@ -576,59 +514,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
   };
   auto next_tile = [&](int kt) { return skip(kt + 1) ? rb0 / DQ_BN : kt + 1; };
 
-  Stage2<DQK, DQ_BN> sk;
-  // V rows: row-major only, 16-byte chunks
-  constexpr int VCPR = DV / 8;
-  constexpr int VN = (DQ_BN * VCPR + 255) / 256;
-  u32x4 svv[VN];
-  int32_t st = 0;
-  int64_t st64 = 0;
-  auto load_tile = [&](int kt) {
+  // DMA of key tile kt; keys >= n arrive as zeros
+  auto issue = [&](DqBuf<DQK, DV>& Bf, int kt) {
     const int j0 = kt * DQ_BN;
-    sk.load(kh_, a.ld_qk, j0, n, tid);
-#pragma unroll
-    for (int s = 0; s < VN; ++s) {
-      const int idx = tid + 256 * s;
-      const int row = idx / VCPR, ch = idx % VCPR;
-      const int j = j0 + row;
-      svv[s] = (idx < DQ_BN * VCPR && j < n) ? ld16(vh_ + (int64_t)j * a.ld_v + ch * 8)
-                                             : u32x4{0, 0, 0, 0};
-    }
-    if (tid < DQ_BN) {
-      const int j = j0 + tid;
-      st = (j < n && !wide) ? a.rel_t[o0 + j] : 0;
-      st64 = (j < n && wide) ? tsq[j] : 0;
-    }
-  };
-  auto store_tile = [&](DqBuf<DQK, DV>& Bf) {
-    sk.store(Bf.k, Bf.kt, tid);
-#pragma unroll
-    for (int s = 0; s < VN; ++s) {
-      const int idx = tid + 256 * s;
-      if (idx < DQ_BN * VCPR) {
-        const int row = idx / VCPR, ch = idx % VCPR;
-        *reinterpret_cast<u32x4*>(&Bf.v[VR::off(row, ch * 4)]) = svv[s];
-      }
-    }
-    if (tid < DQ_BN) {
-      Bf.t[tid] = st;
-      Bf.t64[tid] = st64;
+    dma_tile<DQK, DQ_BN, 4>(Bf.k, kh_, a.ld_qk, j0, n, wave, lane);
+    dma_tile<DV, DQ_BN, 4>(Bf.v, vh_, a.ld_v, j0, n, wave, lane);
+    if (wave == 0) {
+      if (!wide) dma_words64(Bf.t, a.rel_t + o0, j0, n, lane);
+      else dma_dwords64(Bf.t64, tsq, j0, n, lane);
     }
   };
 
-  int kt = 0;
-  if (kt < ktiles && skip(kt)) kt = rb0 / DQ_BN;
-  if (kt < ktiles) {
-    load_tile(kt);
-    store_tile(sm.buf[0]);
-  }
-  __syncthreads();
-  int cur = 0;
-  while (kt < ktiles) {
-    const int nk = next_tile(kt);
-    const bool has_next = nk < ktiles;
-    if (has_next) load_tile(nk);
-    const DqBuf<DQK, DV>& B = sm.buf[cur];
+  auto body = [&](const DqBuf<DQK, DV>& B, int kt) {
     const int j0 = kt * DQ_BN;
     const int j1 = min(j0 + DQ_BN, n);
     const bool hist_rows = r0 < nh;
@@ -636,89 +533,107 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
     const bool active = (r0 < rw1) &&
                         ((hist_rows && j0 <= min(rw1, nh) - 1) ||
                          (cand_rows && (j0 < nh || (j0 < rw1 && j1 > max(r0, nh)))));
-    if (active) {
-      const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh);
-      const bool far = !need_mask && !wide && (min(r0, nh) - min(j1 - 1, nh) >= nP - 1);
-      int mode = 3;  // 0 constant per row, 1 one threshold, 2 gather, 3 general
-      int cF = 0, cL = 0;
-      if (far) {
-        cF = tclz_narrow(ti1, B.t[0]);
-        cL = tclz_narrow(ti1, B.t[j1 - 1 - j0]);
-        mode = __all(sorted && cL == cF) ? 0 : (__all(sorted && cL - cF <= 1) ? 1 : 2);
-      }
-      const float ba = sm.tfar[cF], bb = sm.tfar[min(cF + 1, 31)];
-      const int32_t thr = (cL == cF) ? INT32_MAX : ti1 - (1 << (31 - cF));
-      const int dI = pI - j0 - 4 * g, pmin = pI - nh;
-      const int lim = (iq < nh ? iq : nh - 1) - j0 - 4 * g, slf = iq - j0 - 4 * g;
+    if (!active) return;
+    const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh);
+    const bool far = !need_mask && !wide && (min(r0, nh) - min(j1 - 1, nh) >= nP - 1);
+    int mode = 3;  // 0 constant per row, 1 one threshold, 2 gather, 3 general
+    int cF = 0, cL = 0;
+    if (far) {
+      cF = tclz_narrow(ti1, B.t[0]);
+      cL = tclz_narrow(ti1, B.t[j1 - 1 - j0]);
+      mode = __all(sorted && cL == cF) ? 0 : (__all(sorted && cL - cF <= 1) ? 1 : 2);
+    }
+    const float ba = sm.tfar[cF], bb = sm.tfar[min(cF + 1, 31)];
+    const int32_t thr = (cL == cF) ? INT32_MAX : ti1 - (1 << (31 - cF));
+    const int dI = pI - j0 - 4 * g, pmin = pI - nh;
+    const int lim = (iq < nh ? iq : nh - 1) - j0 - 4 * g, slf = iq - j0 - 4 * g;
 
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x16 sacc = f32x16{}, dacc = f32x16{};
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x16 sacc = f32x16{}, dacc = f32x16{};
+      {
+        bf16x8 ka[DQK / 16], va[DV / 16];
 #pragma unroll
-        for (int ch = 0; ch < DQK / 16; ++ch) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(&B.k[KT::off(hf * 32 + ql, ch * 8 + 4 * g)]);
-          sacc = mfma32(ka, qr[ch], sacc);
-        }
+        for (int ch = 0; ch < DQK / 16; ++ch) ka[ch] = lds_row8<DQK>(B.k, hf * 32 + ql, ch, g);
 #pragma unroll
-        for (int ch = 0; ch < DV / 16; ++ch) {
-          const bf16x8 va =
-              *reinterpret_cast<const bf16x8*>(&B.v[VR::off(hf * 32 + ql, ch * 8 + 4 * g)]);
-          dacc = mfma32(va, orr[ch], dacc);
-        }
-        bf16x8 dsk[2];
-        auto elems = [&](auto bias_of, auto masked) {
+        for (int ch = 0; ch < DV / 16; ++ch) va[ch] = lds_row8<DV>(B.v, hf * 32 + ql, ch, g);
 #pragma unroll
-          for (int aa = 0; aa < 4; ++aa) {
-            const int kk0 = hf * 32 + 8 * aa + 4 * g;
-            const i32x4 tj = *reinterpret_cast<const i32x4*>(&B.t[kk0]);
+        for (int ch = 0; ch < DQK / 16; ++ch) sacc = mfma32(ka[ch], qr[ch], sacc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int kc = hf * 32 + 8 * aa + r;
-              const float sb = fmaf(sacc[4 * aa + r], HSTU_NEG_LOG2E, bias_of(kc, tj[r]));
-              float sig, p;
-              silu_parts(sb, sig, p);
-              float ds = dacc[4 * aa + r] * silu_deriv(sig, p);
-              if constexpr (decltype(masked)::value)
-                ds = (kc <= lim || kc == slf) ? ds : 0.0f;
-              dsk[aa >> 1][(aa & 1) * 4 + r] = (bf16)ds;
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int ch = 0; ch < DV / 16; ++ch) dacc = mfma32(va[ch], orr[ch], dacc);
+      }
+      bf16x8 dsk[2];
+      auto elems = [&](auto bias_of, auto masked) {
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) {
+          const int kk0 = hf * 32 + 8 * aa + 4 * g;
+          const i32x4 tj = *reinterpret_cast<const i32x4*>(&B.t[kk0]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int kc = hf * 32 + 8 * aa + r;
+            const float sb = fmaf(sacc[4 * aa + r], HSTU_NEG_LOG2E, bias_of(kc, tj[r]));
+            float sig, p;
+            silu_parts(sb, sig, p);
+            float ds = dacc[4 * aa + r] * silu_deriv(sig, p);
+            if constexpr (decltype(masked)::value)
+              ds = (kc <= lim || kc == slf) ? ds : 0.0f;
+            dsk[aa >> 1][(aa & 1) * 4 + r] = (bf16)ds;
           }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto bgen = [&](int kc) { return min(max(max(dI - kc, pmin), 0), nP - 1); };
+      if (mode == 0) {
+        elems([&](int, int32_t) { return ba; }, bconst<false>{});
+      } else if (mode == 1) {
+        elems([&](int, int32_t t) { return t <= thr ? ba : bb; }, bconst<false>{});
+      } else if (mode == 2) {
+        elems([&](int, int32_t t) { return sm.tfar[tclz_narrow(ti1, t)]; }, bconst<false>{});
+      } else if (!wide) {
+        auto bias = [&](int kc, int32_t t) {
+          return sm.tpos[bgen(kc)] + sm.ttime[tclz_narrow(ti1, t)];
         };
-        auto bgen = [&](int kc) { return min(max(max(dI - kc, pmin), 0), nP - 1); };
-        if (mode == 0) {
-          elems([&](int, int32_t) { return ba; }, bconst<false>{});
-        } else if (mode == 1) {
-          elems([&](int, int32_t t) { return t <= thr ? ba : bb; }, bconst<false>{});
-        } else if (mode == 2) {
-          elems([&](int, int32_t t) { return sm.tfar[tclz_narrow(ti1, t)]; }, bconst<false>{});
-        } else if (!wide) {
-          auto bias = [&](int kc, int32_t t) {
-            return sm.tpos[bgen(kc)] + sm.ttime[tclz_narrow(ti1, t)];
-          };
-          if (need_mask) elems(bias, bconst<true>{});
-          else elems(bias, bconst<false>{});
-        } else {
-          elems([&](int kc, int32_t) {
-                  return sm.tpos[bgen(kc)] + sm.ttime[tclz_wide(tq64, B.t64[kc + 4 * g])];
-                },
-                bconst<true>{});
-        }
+        if (need_mask) elems(bias, bconst<true>{});
+        else elems(bias, bconst<false>{});
+      } else {
+        elems([&](int kc, int32_t) {
+                return sm.tpos[bgen(kc)] + sm.ttime[tclz_wide(tq64, B.t64[kc + 4 * g])];
+              },
+              bconst<true>{});
+      }
+      // dQ += dS K: K read down its columns (keys are the k index)
 #pragma unroll
-        for (int d = 0; d < DQK / 32; ++d)
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 kb[DQK / 32];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 kbv = *reinterpret_cast<const bf16x8*>(
-                &B.kt[TT::off(d * 32 + ql, 8 * (2 * hf + u) + 4 * g)]);
-            dq[d] = mfma32(dsk[u], kbv, dq[d]);
-          }
+        for (int d = 0; d < DQK / 32; ++d) kb[d] = lds_col8<DQK>(B.k, hf * 32 + 16 * u, d * 32, lane);
+#pragma unroll
+        for (int d = 0; d < DQK / 32; ++d) dq[d] = mfma32(dsk[u], kb[d], dq[d]);
       }
     }
-    if (has_next) store_tile(sm.buf[cur ^ 1]);
+  };
+
+  // double-buffered key-tile pipeline, unrolled by two so that every access
+  // names its buffer statically
+  int kt = 0;
+  if (kt < ktiles && skip(kt)) kt = rb0 / DQ_BN;
+  if (kt < ktiles) issue(dqb0, kt);
+  dma_wait();
+  __syncthreads();
+  while (kt < ktiles) {
+    int nk = next_tile(kt);
+    if (nk < ktiles) issue(dqb1, nk);
+    body(dqb0, kt);
+    dma_wait();
     __syncthreads();
     kt = nk;
-    cur ^= 1;
+    if (kt >= ktiles) break;
+    nk = next_tile(kt);
+    if (nk < ktiles) issue(dqb0, nk);
+    body(dqb1, kt);
+    dma_wait();
+    __syncthreads();
+    kt = nk;
   }
   if (r0 >= rw1) return;
   const float invN = 1.0f / (float)(a.norm_mode == 0 ? a.norm_len : n);
