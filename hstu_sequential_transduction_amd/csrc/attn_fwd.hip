@@ -7,12 +7,13 @@
 // "DLRMv4 Brings Sequence-Based Recommendation Training to MLPerf", "Model
 // Architecture"; lower triangle only: its Table 7 note).
 //
-// bf16 kernel (gfx950 MFMA): one workgroup = one (sequence, 128-row query
-// block, head) work item, four waves of 32 query rows.  Q stays in registers
-// as the B operand of S^T = K Q^T (32x32x16 MFMA), K tiles of 64 keys are
-// staged row-major in LDS, V tiles transposed (channel-major, keys permuted
-// so each lane group's eight keys are contiguous), so the S^T accumulator is
-// consumed directly as the A operand of O += P V without any shuffle.  Per
+// bf16 kernel (gfx950 MFMA): one workgroup = one (sequence, query block,
+// head) work item, four waves of 32 (d = 128) or 64 (d <= 64) query rows.  Q
+// stays in registers as the B operand of S^T = K Q^T (32x32x16 MFMA).  Tiles
+// of 64 keys of K and V arrive row-major by buffer->LDS DMA, double-buffered;
+// K is read along rows (A operand of S^T) and V down its columns with
+// transpose reads, in the key order the S^T accumulator leaves in each lane,
+// so the accumulator is consumed directly as the A operand of O += P V.  Per
 // score element the VALU adds the bias (LDS table gathers indexed by the
 // position distance and by clz of the time distance), evaluates
 // SiLU(s) = s / (1 + 2^(-s log2 e)) with one v_exp and one v_rcp, applies the
@@ -22,6 +23,7 @@
 #include "bias.h"
 #include "common.h"
 #include "internal.h"
+#include "lds.h"
 
 #include <type_traits>
 
@@ -39,98 +41,20 @@ struct FwdShape {
   static constexpr int BM = 4 * 32 * QG;  // query rows per workgroup (four waves)
 };
 
+// One staged key tile: row-major K and V and the key times.
 template <int DQK, int DV>
 struct FwdBuf {
-  uint32_t k[LdsTile<DQK>::S_DW * FWD_BN];   // K tile, row-major
-  uint32_t vt[LdsTile<FWD_BN>::S_DW * DV];   // V tile, channel-major, keys permuted
-  int32_t t[FWD_BN];                         // key times (relative, narrow path)
-  int64_t t64[FWD_BN];                       // key times (absolute, spans >= 2^31 s)
+  uint8_t k[SwzTile<DQK>::bytes(FWD_BN)];
+  uint8_t v[SwzTile<DV>::bytes(FWD_BN)];
+  int32_t t[FWD_BN];    // key times relative to the sequence minimum (narrow)
+  int64_t t64[FWD_BN];  // key times (wide sequences)
 };
 
-template <int DQK, int DV>
-struct FwdSmem {
-  FwdBuf<DQK, DV> buf[2];
+// Bias tables, a separate LDS object from the tile buffers.
+struct FwdTables {
   float tfar[32];    // (rab_pos[nP-1] + rab_time[bucket(c)]) * -log2 e, by clz index c
   float ttime[32];   // rab_time[bucket(c)] * -log2 e
   float tpos[1024];  // rab_pos * -log2 e
-};
-
-// Register staging of one key tile (global -> registers -> LDS).
-template <int DQK, int DV>
-struct FwdStage {
-  static constexpr int KCPR = DQK / 8;
-  static constexpr int KN = (FWD_BN * KCPR) / 256;
-  static constexpr int VCH = DV / 8;
-  static constexpr int VITEMS = (FWD_BN / 2) * VCH;
-  static constexpr int VN = (VITEMS + 255) / 256;
-  u32x4 k[KN];
-  u32x4 va[VN], vb[VN];
-  int32_t t;
-  int64_t t64;
-
-  HSTU_DEV static void vmap(int idx, int& kp, int& cc) {
-    if (VCH >= 8) {
-      const int rest = idx >> 6;
-      kp = (rest & 3) * 8 + ((idx >> 3) & 7);
-      cc = (rest >> 2) * 8 + (idx & 7);
-    } else {
-      cc = idx % VCH;
-      kp = idx / VCH;
-    }
-  }
-  HSTU_DEV void load(const bf16* kh, int64_t ldk, const bf16* vh, int64_t ldv,
-                     const int32_t* rt, const int64_t* t64p, int j0, int n, int tid) {
-#pragma unroll
-    for (int s = 0; s < KN; ++s) {
-      const int idx = tid + 256 * s;
-      const int row = idx / KCPR, ch = idx % KCPR;
-      const int j = j0 + row;
-      k[s] = (j < n) ? ld16(kh + (int64_t)j * ldk + ch * 8) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int s = 0; s < VN; ++s) {
-      const int idx = tid + 256 * s;
-      va[s] = u32x4{0, 0, 0, 0};
-      vb[s] = u32x4{0, 0, 0, 0};
-      if (idx < VITEMS) {
-        int kp, cc;
-        vmap(idx, kp, cc);
-        const int j = j0 + 2 * kp;
-        if (j < n) va[s] = ld16(vh + (int64_t)j * ldv + cc * 8);
-        if (j + 1 < n) vb[s] = ld16(vh + (int64_t)(j + 1) * ldv + cc * 8);
-      }
-    }
-    t = (tid < FWD_BN && rt && j0 + tid < n) ? rt[j0 + tid] : 0;
-    t64 = (tid < FWD_BN && t64p && j0 + tid < n) ? t64p[j0 + tid] : 0;
-  }
-  HSTU_DEV void store(FwdBuf<DQK, DV>& B, int tid) const {
-    using KT = LdsTile<DQK>;
-    using VT = LdsTile<FWD_BN>;
-#pragma unroll
-    for (int s = 0; s < KN; ++s) {
-      const int idx = tid + 256 * s;
-      const int row = idx / KCPR, ch = idx % KCPR;
-      *reinterpret_cast<u32x4*>(&B.k[KT::off(row, ch * 4)]) = k[s];
-    }
-#pragma unroll
-    for (int s = 0; s < VN; ++s) {
-      const int idx = tid + 256 * s;
-      if (idx < VITEMS) {
-        int kp, cc;
-        vmap(idx, kp, cc);
-        const int col = kperm(2 * kp) >> 1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          B.vt[VT::off(cc * 8 + 2 * e, col)] = (va[s][e] & 0xFFFFu) | (vb[s][e] << 16);
-          B.vt[VT::off(cc * 8 + 2 * e + 1, col)] = (va[s][e] >> 16) | (vb[s][e] & 0xFFFF0000u);
-        }
-      }
-    }
-    if (tid < FWD_BN) {
-      B.t[tid] = t;
-      B.t64[tid] = t64;
-    }
-  }
 };
 
 template <bool V>
@@ -138,22 +62,23 @@ using bconst = std::integral_constant<bool, V>;
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
-  using KT = LdsTile<DQK>;
-  using VT = LdsTile<FWD_BN>;
   constexpr int QG = FwdShape<DQK, DV>::QG;
   constexpr int BM = FwdShape<DQK, DV>::BM;
-  __shared__ __attribute__((aligned(16))) FwdSmem<DQK, DV> sm;
+  __shared__ __attribute__((aligned(1024))) FwdBuf<DQK, DV> fwb0;
+  __shared__ __attribute__((aligned(1024))) FwdBuf<DQK, DV> fwb1;
+  __shared__ FwdTables sm;
 
   const int w = blockIdx.x;
   const int n_items = a.counters[0];
   if (w >= n_items * a.H) return;
   const int it = w / a.H, h = w - it * a.H;
-  const int b = a.items[2 * it], m = a.items[2 * it + 1];
-  const int o0 = a.seq_offsets[b];
-  const int n = a.seq_offsets[b + 1] - o0;
-  const int c = a.num_cand ? a.num_cand[b] : 0;
+  const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
+  const int m = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  const int o0 = __builtin_amdgcn_readfirstlane(a.seq_offsets[b]);
+  const int n = __builtin_amdgcn_readfirstlane(a.seq_offsets[b + 1]) - o0;
+  const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;
   const int nh = n - c;
-  const int flags = a.seq_flags[b];
+  const int flags = __builtin_amdgcn_readfirstlane(a.seq_flags[b]);
   const bool wide = flags & 1;
   const bool sorted = flags & 2;
   const int nP = a.nP, nT = a.nT;
@@ -182,9 +107,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
   const bf16* qbase = reinterpret_cast<const bf16*>(a.q) + (int64_t)o0 * a.ld_qk + h * DQK;
   const bf16* kh = reinterpret_cast<const bf16*>(a.k) + (int64_t)o0 * a.ld_qk + h * DQK;
   const bf16* vh = reinterpret_cast<const bf16*>(a.v) + (int64_t)o0 * a.ld_v + h * DV;
-  const int32_t* relt = wide ? nullptr : a.rel_t + o0;
   const int64_t* tsq = a.ts + o0;
-  const int64_t* t64p = wide ? tsq : nullptr;
 
   int iq[QG], pI[QG];
   int32_t ti1[QG];
@@ -219,21 +142,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
     return nk;
   };
 
-  FwdStage<DQK, DV> stg;
-  int kt = 0;
-  if (kt < ktiles && kt * FWD_BN >= nh && kt * FWD_BN + FWD_BN <= rb0) kt = rb0 / FWD_BN;
-  if (kt < ktiles) {
-    stg.load(kh, a.ld_qk, vh, a.ld_v, relt, t64p, kt * FWD_BN, n, tid);
-    stg.store(sm.buf[0], tid);
-  }
-  __syncthreads();
-  int cur = 0;
-  while (kt < ktiles) {
-    const int nk = next_tile(kt);
-    const bool has_next = nk < ktiles;
-    if (has_next) stg.load(kh, a.ld_qk, vh, a.ld_v, relt, t64p, nk * FWD_BN, n, tid);
+  // DMA of key tile kt; keys >= n arrive as zeros
+  auto issue = [&](FwdBuf<DQK, DV>& Bf, int kt) {
+    const int j0 = kt * FWD_BN;
+    dma_tile<DQK, FWD_BN, 4>(Bf.k, kh, a.ld_qk, j0, n, wave, lane);
+    dma_tile<DV, FWD_BN, 4>(Bf.v, vh, a.ld_v, j0, n, wave, lane);
+    if (wave == 0) {
+      if (!wide) dma_words64(Bf.t, a.rel_t + o0, j0, n, lane);
+      else dma_dwords64(Bf.t64, tsq, j0, n, lane);
+    }
+  };
 
-    const FwdBuf<DQK, DV>& B = sm.buf[cur];
+  auto body = [&](const FwdBuf<DQK, DV>& B, int kt) {
     const int j0 = kt * FWD_BN;
     const int j1 = min(j0 + FWD_BN, n);
     const bool hist_rows = r0 < nh;
@@ -288,12 +208,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
         f32x16 sacc[QG];
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) sacc[qg] = f32x16{};
+        {
+          bf16x8 ka[DQK / 16];
 #pragma unroll
-        for (int ch = 0; ch < DQK / 16; ++ch) {
-          const bf16x8 ka =
-              *reinterpret_cast<const bf16x8*>(&B.k[KT::off(hf * 32 + ql, ch * 8 + 4 * g)]);
+          for (int ch = 0; ch < DQK / 16; ++ch) ka[ch] = lds_row8<DQK>(B.k, hf * 32 + ql, ch, g);
 #pragma unroll
-          for (int qg = 0; qg < QG; ++qg) sacc[qg] = mfma32(ka, qr[qg][ch], sacc[qg]);
+          for (int ch = 0; ch < DQK / 16; ++ch)
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) sacc[qg] = mfma32(ka[ch], qr[qg][ch], sacc[qg]);
         }
 
         bf16x8 pk[QG][2];
@@ -346,22 +268,44 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
           silu_half(bias, bconst<true>{});
         }
 
+        // O += P V: V read down its columns (keys are the k index)
 #pragma unroll
-        for (int d = 0; d < DV / 32; ++d)
+        for (int u = 0; u < 2; ++u) {
+          bf16x8 vb[DV / 32];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 vb = *reinterpret_cast<const bf16x8*>(
-                &B.vt[VT::off(d * 32 + ql, 8 * (2 * hf + u) + 4 * g)]);
+          for (int d = 0; d < DV / 32; ++d) vb[d] = lds_col8<DV>(B.v, hf * 32 + 16 * u, d * 32, lane);
 #pragma unroll
-            for (int qg = 0; qg < QG; ++qg) oacc[qg][d] = mfma32(pk[qg][u], vb, oacc[qg][d]);
-          }
+          for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+            for (int qg = 0; qg < QG; ++qg) oacc[qg][d] = mfma32(pk[qg][u], vb[d], oacc[qg][d]);
+        }
       }
     }
 
-    if (has_next) stg.store(sm.buf[cur ^ 1], tid);
+  };
+
+  // double-buffered key-tile pipeline, unrolled by two so that every access
+  // names its buffer statically (the DMA into one buffer then needs no wait
+  // before reads of the other)
+  int kt = 0;
+  if (kt < ktiles && kt * FWD_BN >= nh && kt * FWD_BN + FWD_BN <= rb0) kt = rb0 / FWD_BN;
+  if (kt < ktiles) issue(fwb0, kt);
+  dma_wait();
+  __syncthreads();
+  while (kt < ktiles) {
+    int nk = next_tile(kt);
+    if (nk < ktiles) issue(fwb1, nk);
+    body(fwb0, kt);
+    dma_wait();
     __syncthreads();
     kt = nk;
-    cur ^= 1;
+    if (kt >= ktiles) break;
+    nk = next_tile(kt);
+    if (nk < ktiles) issue(fwb0, nk);
+    body(fwb1, kt);
+    dma_wait();
+    __syncthreads();
+    kt = nk;
   }
 
   // ---- write O * (-ln2 / N) ----
