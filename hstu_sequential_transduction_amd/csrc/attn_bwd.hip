@@ -39,11 +39,21 @@ namespace hstu {
 
 namespace {
 
-constexpr int KV_QT = 64;   // query rows per tile in the dK/dV kernel
+constexpr int KV_QT = 64;   // query rows per tile in the dK/dV kernel (halves of 32 rows)
+constexpr int KV_NH = KV_QT / 32;
 constexpr int DQ_BN = 64;   // keys per tile in the dQ kernel
 
 template <bool V>
 using bconst = std::integral_constant<bool, V>;
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int I, int N, typename F>
+HSTU_DEV void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // sigma and P' from the pre-scaled score s' = -log2(e) * (q.k + bias)
 HSTU_DEV void silu_parts(float sb, float& sig, float& pp) {
@@ -200,12 +210,13 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   // query tiles: [k0, qend); candidate keys are seen by themselves only
   const int qend = (k0 >= nh) ? k1 : n;
   // DMA of query tile i0 into Bf; rows >= qend arrive as zeros (times: rows >= n)
-  auto issue = [&](KvBuf<DQK, DV>& Bf, int i0) {
+  auto issue = [&](KvBuf<DQK, DV>& Bf, int i0) HSTU_INLINE_LAMBDA {
     dma_tile<DQK, KV_QT, 4>(Bf.q, qh_, a.ld_qk, i0, qend, wave, lane);
     dma_tile<DV, KV_QT, 4>(Bf.o, doh, a.ld_dout, i0, qend, wave, lane);
-    if (wave == 0) {
-      if (!wide) dma_words64(Bf.t, a.rel_t + o0, i0, n, lane);
-      else dma_dwords64(Bf.t64, tsq, i0, n, lane);
+    if (wave < KV_QT / 64) {
+      const int r = i0 + 64 * wave;
+      if (!wide) dma_words64(Bf.t + 64 * wave, a.rel_t + o0, r, n, lane);
+      else dma_dwords64(Bf.t64 + 64 * wave, tsq, r, n, lane);
     }
   };
 
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   // per-lane running sums of the far phase: time buckets (curB, curB+1), position nP-1
   int curB = -1;
   float run_tot = 0.0f, run_a = 0.0f, ptot = 0.0f;
-  auto flush_time = [&]() {
+  auto flush_time = [&]() HSTU_INLINE_LAMBDA {
     if (curB >= 0) {
       if (run_a != 0.0f) atomicAdd(&sm.gtime[curB], run_a);
       if (run_tot - run_a != 0.0f) atomicAdd(&sm.gtime[curB + 1], run_tot - run_a);
@@ -234,7 +245,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   };
 
   // S = Q K^T and dA = dO V^T for the 32-row half qh of the staged tile
-  auto mm_sd = [&](const KvBuf<DQK, DV>& B, int qh, f32x16& sacc, f32x16& dacc) {
+  auto mm_sd = [&](const KvBuf<DQK, DV>& B, int qh, f32x16& sacc, f32x16& dacc) HSTU_INLINE_LAMBDA {
     sacc = f32x16{};
     dacc = f32x16{};
     bf16x8 qa[DQK / 16], oa[DV / 16];
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   };
   // dV += P'^T dO ; dK += dS^T Q   (k = the 32 rows of half qh)
   auto mm_grad = [&](const KvBuf<DQK, DV>& B, int qh, const bf16x8 (&pp)[2],
-                     const bf16x8 (&dd)[2]) {
+                     const bf16x8 (&dd)[2]) HSTU_INLINE_LAMBDA {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       bf16x8 ob[DV / 32], qb[DQK / 32];
@@ -269,7 +280,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   // kc = 8*(r/4) + r%4; bias_of(kc, t) is pre-scaled, grad_of(kc, t, ds).
   auto elems = [&](const KvBuf<DQK, DV>& B, int qh, const f32x16& sacc, const f32x16& dacc,
                    bf16x8 (&pp)[2], bf16x8 (&dd)[2], auto bias_of, auto grad_of, auto masked,
-                   int lo, int hi) {
+                   int lo, int hi) HSTU_INLINE_LAMBDA {
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
       const i32x4 t4 = *reinterpret_cast<const i32x4*>(&B.t[qh * 32 + 8 * aa + 4 * g]);
@@ -293,17 +304,39 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
     }
   };
 
-  // near-phase tile: per-half masks, per-element buckets, LDS-atomic histograms
-  auto near_tile = [&](const KvBuf<DQK, DV>& B, int i0) {
+  // Near-phase rab gradients.  Position buckets below nP-1 differ across the
+  // lanes of one element (one key per lane), so their LDS atomics do not
+  // collide; saturated elements go to the per-lane sum ptot and masked ones
+  // (dS = 0) are skipped.  Time buckets are shared by neighbouring keys, so
+  // each lane run-length encodes them instead: along a lane the rows come in
+  // order, and the running sum is flushed to the histogram only when the
+  // lane's bucket changes (for sorted timestamps a handful of times per tile).
+  int nb_cur = 0;
+  float nb_acc = 0.0f;
+  auto near_pos_grad = [&](int bp, float ds) HSTU_INLINE_LAMBDA {
+    if (bp < nP - 1 && ds != 0.0f) atomicAdd(&sm.gpos[bp], ds);
+    ptot += (bp >= nP - 1) ? ds : 0.0f;
+  };
+  auto near_time_grad = [&](int ct, float ds) HSTU_INLINE_LAMBDA {
+    if (ct != nb_cur) {
+      if (nb_acc != 0.0f) atomicAdd(&sm.gtime[nb_cur], nb_acc);
+      nb_acc = 0.0f;
+      nb_cur = ct;
+    }
+    nb_acc += ds;
+  };
+
+  // near-phase tile: per-half masks and per-element buckets
+  auto near_tile = [&](const KvBuf<DQK, DV>& B, int i0) HSTU_INLINE_LAMBDA {
     if (kw0 >= kw1) return;
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
+    static_for<0, KV_NH>([&](auto qhc) HSTU_INLINE_LAMBDA {
+      constexpr int qh = decltype(qhc)::value;
       const int ir0 = i0 + qh * 32;
       const int ir1 = min(ir0 + 32, qend);
       bool active;
       if (kw0 < nh) active = ir1 - 1 >= kw0;
       else active = ir0 < kw1 && ir1 > kw0;
-      if (!active || ir0 >= ir1) continue;
+      if (!active || ir0 >= ir1) return;
       f32x16 sacc, dacc;
       mm_sd(B, qh, sacc, dacc);
       bf16x8 pp[2], dd[2];
@@ -314,13 +347,13 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
       const int d0 = jk - ib;
       const int lo = kvalid ? d0 : 1 << 20;
       const int hi = min(jk < nh ? (1 << 20) : d0, qend - 1 - ib);
-      auto bidx = [&](int kc) { return min(max(min(pd0 + kc, pdmax), 0), nP - 1); };
+      auto bidx = [&](int kc) HSTU_INLINE_LAMBDA { return min(max(min(pd0 + kc, pdmax), 0), nP - 1); };
       if (!wide) {
         elems(B, qh, sacc, dacc, pp, dd,
               [&](int kc, int32_t t) { return sm.tpos[bidx(kc)] + sm.ttime[tclz_narrow(t, tjm)]; },
               [&](int kc, int32_t t, float ds) {
-                atomicAdd(&sm.gpos[bidx(kc)], ds);
-                atomicAdd(&sm.gtime[tclz_narrow(t, tjm)], ds);
+                near_pos_grad(bidx(kc), ds);
+                near_time_grad(tclz_narrow(t, tjm), ds);
               },
               bconst<true>{}, lo, hi);
       } else {
@@ -330,23 +363,23 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
                        sm.ttime[tclz_wide(B.t64[qh * 32 + 4 * g + kc], tj64)];
               },
               [&](int kc, int32_t, float ds) {
-                atomicAdd(&sm.gpos[bidx(kc)], ds);
-                atomicAdd(&sm.gtime[tclz_wide(B.t64[qh * 32 + 4 * g + kc], tj64)], ds);
+                near_pos_grad(bidx(kc), ds);
+                near_time_grad(tclz_wide(B.t64[qh * 32 + 4 * g + kc], tj64), ds);
               },
               bconst<true>{}, lo, hi);
       }
       mm_grad(B, qh, pp, dd);
-    }
+    });
   };
 
   // far-phase tile: no masks, position bucket nP-1; with sorted timestamps a
   // lane's time bucket changes at most once inside a half in the common case
-  auto far_tile = [&](const KvBuf<DQK, DV>& B, int i0) {
+  auto far_tile = [&](const KvBuf<DQK, DV>& B, int i0) HSTU_INLINE_LAMBDA {
     if (kw0 >= kw1) return;
-#pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
+    static_for<0, KV_NH>([&](auto qhc) HSTU_INLINE_LAMBDA {
+      constexpr int qh = decltype(qhc)::value;
       const int ir0 = i0 + qh * 32;
-      if (ir0 >= qend) break;
+      if (ir0 >= qend) return;
       const int last = min(31, qend - 1 - ir0);
       const int cF = tclz_narrow(B.t[qh * 32 + last], tjm);
       const int cL = tclz_narrow(B.t[qh * 32], tjm);
@@ -378,13 +411,13 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
               bconst<false>{}, 0, 0);
       }
       mm_grad(B, qh, pp, dd);
-    }
+    });
   };
 
   // double-buffered tile pipeline over [ibeg, iend) in steps of KV_QT: the DMA
   // of tile t+1 runs while tile t is computed
   // (unrolled by two so that every access names its buffer statically)
-  auto run_phase = [&](int ibeg, int iend, auto body) {
+  auto run_phase = [&](int ibeg, int iend, auto body) HSTU_INLINE_LAMBDA {
     if (ibeg >= iend) return;
     issue(kvb0, ibeg);
     dma_wait();
@@ -403,6 +436,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
     }
   };
   run_phase(k0, far_start, near_tile);
+  if (nb_acc != 0.0f) atomicAdd(&sm.gtime[nb_cur], nb_acc);
   run_phase(far_start, qend, far_tile);
   flush_time();
   if (ptot != 0.0f) atomicAdd(&sm.gpos[nP - 1], ptot);
@@ -508,14 +542,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
   for (int d = 0; d < DQK / 32; ++d) dq[d] = f32x16{};
 
   const int ktiles = (rb1 + DQ_BN - 1) / DQ_BN;
-  auto skip = [&](int kt) {
+  auto skip = [&](int kt) HSTU_INLINE_LAMBDA {
     const int j0 = kt * DQ_BN;
     return j0 >= nh && j0 + DQ_BN <= rb0;
   };
-  auto next_tile = [&](int kt) { return skip(kt + 1) ? rb0 / DQ_BN : kt + 1; };
+  auto next_tile = [&](int kt) HSTU_INLINE_LAMBDA { return skip(kt + 1) ? rb0 / DQ_BN : kt + 1; };
 
   // DMA of key tile kt; keys >= n arrive as zeros
-  auto issue = [&](DqBuf<DQK, DV>& Bf, int kt) {
+  auto issue = [&](DqBuf<DQK, DV>& Bf, int kt) HSTU_INLINE_LAMBDA {
     const int j0 = kt * DQ_BN;
     dma_tile<DQK, DQ_BN, 4>(Bf.k, kh_, a.ld_qk, j0, n, wave, lane);
     dma_tile<DV, DQ_BN, 4>(Bf.v, vh_, a.ld_v, j0, n, wave, lane);
@@ -525,7 +559,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
     }
   };
 
-  auto body = [&](const DqBuf<DQK, DV>& B, int kt) {
+  auto body = [&](const DqBuf<DQK, DV>& B, int kt) HSTU_INLINE_LAMBDA {
     const int j0 = kt * DQ_BN;
     const int j1 = min(j0 + DQ_BN, n);
     const bool hist_rows = r0 < nh;
@@ -563,7 +597,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
         for (int ch = 0; ch < DV / 16; ++ch) dacc = mfma32(va[ch], orr[ch], dacc);
       }
       bf16x8 dsk[2];
-      auto elems = [&](auto bias_of, auto masked) {
+      auto elems = [&](auto bias_of, auto masked) HSTU_INLINE_LAMBDA {
 #pragma unroll
         for (int aa = 0; aa < 4; ++aa) {
           const int kk0 = hf * 32 + 8 * aa + 4 * g;
@@ -582,7 +616,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
           __builtin_amdgcn_sched_barrier(0);
         }
       };
-      auto bgen = [&](int kc) { return min(max(max(dI - kc, pmin), 0), nP - 1); };
+      auto bgen = [&](int kc) HSTU_INLINE_LAMBDA { return min(max(max(dI - kc, pmin), 0), nP - 1); };
       if (mode == 0) {
         elems([&](int, int32_t) { return ba; }, bconst<false>{});
       } else if (mode == 1) {
@@ -590,7 +624,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
       } else if (mode == 2) {
         elems([&](int, int32_t t) { return sm.tfar[tclz_narrow(ti1, t)]; }, bconst<false>{});
       } else if (!wide) {
-        auto bias = [&](int kc, int32_t t) {
+        auto bias = [&](int kc, int32_t t) HSTU_INLINE_LAMBDA {
           return sm.tpos[bgen(kc)] + sm.ttime[tclz_narrow(ti1, t)];
         };
         if (need_mask) elems(bias, bconst<true>{});

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
 
   // key tiles: 0 .. ktiles-1, skipping tiles that hold only other candidates' keys
   const int ktiles = (rb1 + FWD_BN - 1) / FWD_BN;
-  auto next_tile = [&](int kt) {
+  auto next_tile = [&](int kt) HSTU_INLINE_LAMBDA {
     const int nk = kt + 1;
     const int j0 = nk * FWD_BN;
     if (j0 >= nh && j0 + FWD_BN <= rb0) return rb0 / FWD_BN;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
   };
 
   // DMA of key tile kt; keys >= n arrive as zeros
-  auto issue = [&](FwdBuf<DQK, DV>& Bf, int kt) {
+  auto issue = [&](FwdBuf<DQK, DV>& Bf, int kt) HSTU_INLINE_LAMBDA {
     const int j0 = kt * FWD_BN;
     dma_tile<DQK, FWD_BN, 4>(Bf.k, kh, a.ld_qk, j0, n, wave, lane);
     dma_tile<DV, FWD_BN, 4>(Bf.v, vh, a.ld_v, j0, n, wave, lane);
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
     }
   };
 
-  auto body = [&](const FwdBuf<DQK, DV>& B, int kt) {
+  auto body = [&](const FwdBuf<DQK, DV>& B, int kt) HSTU_INLINE_LAMBDA {
     const int j0 = kt * FWD_BN;
     const int j1 = min(j0 + FWD_BN, n);
     const bool hist_rows = r0 < nh;
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
         // tile: kk = kc + 4g with kc = hf*32 + 8*aa + r a compile-time constant, so
         // per-lane limits are pre-shifted by 4g and compared with immediates.
         // bias_of(qg, kc, key time) returns the pre-scaled bias.
-        auto silu_half = [&](auto bias_of, auto masked) {
+        auto silu_half = [&](auto bias_of, auto masked) HSTU_INLINE_LAMBDA {
 #pragma unroll
           for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
@@ -254,14 +254,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
                     bconst<false>{});
         } else if (!wide) {
           // position bucket: clamp(p(i) - min(j, n_h), 0, nP-1) = med3(max(dI - kc, pI - nh), 0, nP-1)
-          auto bias = [&](int qg, int kc, int32_t tj) {
+          auto bias = [&](int qg, int kc, int32_t tj) HSTU_INLINE_LAMBDA {
             const int bp = min(max(max(dI[qg] - kc, pmin[qg]), 0), nP - 1);
             return sm.tpos[bp] + sm.ttime[tclz_narrow(ti1[qg], tj)];
           };
           if (need_mask) silu_half(bias, bconst<true>{});
           else silu_half(bias, bconst<false>{});
         } else {
-          auto bias = [&](int qg, int kc, int32_t) {
+          auto bias = [&](int qg, int kc, int32_t) HSTU_INLINE_LAMBDA {
             const int bp = min(max(max(dI[qg] - kc, pmin[qg]), 0), nP - 1);
             return sm.tpos[bp] + sm.ttime[tclz_wide(tq64[qg], B.t64[kc + 4 * g])];
           };

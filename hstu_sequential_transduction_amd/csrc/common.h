@@ -13,6 +13,8 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define HSTU_DEV __device__ __forceinline__
+// for lambdas inside kernels: an outlined lambda would move captured arrays to scratch
+#define HSTU_INLINE_LAMBDA __attribute__((always_inline))
 
 // -log2(e): the attention kernels evaluate exp(-s) as exp2(s * -log2(e)).
 #define HSTU_NEG_LOG2E (-1.4426950408889634f)
