@@ -13,6 +13,7 @@
 // of the next k-step are issued before the MFMAs of the current one.
 #include "common.h"
 #include "internal.h"
+#include "lds.h"
 
 namespace hstu {
 
@@ -171,6 +172,359 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// DMA-staged bf16 GEMM, BM x BN output tile per workgroup of four waves
+// (2 x 2), each wave a (BM/2) x (BN/2) block of 32x32x16 MFMAs, k-step 64.
+// Two shapes: 256x256 (one workgroup per CU, the whole register file per
+// wave, eight 16-byte LDS operand reads per sixteen MFMAs) for GEMMs large
+// enough to fill the GPU several times over, and 128x128 (two workgroups per
+// CU, so one's epilogue overlaps the other's main loop) for the rest.
+// Operand tiles arrive by buffer->LDS DMA into a static double buffer.  A
+// k-contiguous operand is stored [rows][64 k] and read along rows; a k-major
+// operand ([k][rows] in memory) is stored as [64 k][128]-column tiles and read
+// down columns with transpose reads, so no operand is ever transposed in
+// memory.  Workgroups are ordered so that the tiles sharing one row block of
+// A run on the same XCD (workgroup w runs on XCD w % 8) and share its L2.
+// ---------------------------------------------------------------------------
+constexpr int G2_BK = 64;
+constexpr int G2_NW = 4;  // waves: 2 (m) x 2 (n)
+
+// DMA of one operand tile: R rows r0.. (the m or n index) x k0..k0+63
+template <bool KCONT, int R>
+HSTU_DEV void g2_issue(uint8_t* t, const bf16* X, int64_t ld, int64_t r0, int64_t Rmax,
+                       int64_t k0, int64_t kend, int wave, int lane) {
+  if (KCONT) {
+    // [rows][k]: rows beyond Rmax arrive as zeros; k0 + 64 <= K (checked on the host)
+    dma_tile<64, R, G2_NW>(t, X + k0, ld, (int)r0, (int)Rmax, wave, lane);
+  } else {
+    // [k][rows]: 128-column pieces; k rows beyond kend arrive as zeros and the
+    // last k row is cut at the matrix's right edge
+#pragma unroll
+    for (int hf = 0; hf < R / 128; ++hf) {
+      const int64_t c0 = r0 + 128 * hf;
+      const int cols = (int)max<int64_t>(0, min<int64_t>(128, Rmax - c0));
+      dma_tile<128, 64, G2_NW>(t + hf * (64 * 256), X + c0, ld, (int)k0, (int)kend, wave, lane,
+                               cols);
+    }
+  }
+}
+
+// Per-lane byte offsets of a wave's MFMA operand reads within a staged tile,
+// for the wave's NF x 32 rows starting at r0.  The swizzle makes the
+// lane-dependent part of every address one of a few values; the rest (row
+// block, k-chunk, stage) is a constant that rides in the instruction's
+// immediate offset, so the whole main loop needs only these registers.
+template <bool KCONT, int NF>
+struct G2Off {
+  int o[KCONT ? 4 : 2 * NF];
+  HSTU_DEV void init(int r0, int lane) {
+    const int ql = lane & 31, g = lane >> 5;
+    if (KCONT) {
+      // SwzTile<64>: row r0 + 32 i + ql, logical chunk 2 kc + g; the swizzle of
+      // these rows depends on ql only
+      const int s = SwzTile<64>::swz(ql);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) o[kc] = (r0 + ql) * 128 + (((2 * kc + g) ^ s) << 4);
+    } else {
+      // SwzTile<128> pieces [64 k][128]; fragment i covers columns r0 + 32 i ..,
+      // k rows 16 kc + 8 g + j/4 (+4 for the upper read)
+      const int j = lane & 15;
+      const int cl = 2 * ((lane >> 4) & 1) + ((j & 3) >> 1);
+      const int cb = (j & 1) * 8;
+#pragma unroll
+      for (int i = 0; i < NF; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int col = r0 + 32 * i;
+          const int r = 8 * g + (j >> 2) + 4 * h;
+          const int c = (col & 127) / 8 + cl;  // logical chunk (column / 8)
+          o[2 * i + h] =
+              (col >> 7) * (64 * 256) + r * 256 + ((c ^ SwzTile<128>::swz(r)) << 4) + cb;
+        }
+    }
+  }
+  // operand of row block i (32 rows), k-chunk kc
+  HSTU_DEV bf16x8 frag(const uint8_t* t, int i, int kc) const {
+    if (KCONT) {
+      return *reinterpret_cast<const bf16x8*>(t + o[kc] + i * 32 * 128);
+    } else {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (HSTU_LDS bf16x4*)(t + o[2 * i] + kc * 16 * 256));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (HSTU_LDS bf16x4*)(t + o[2 * i + 1] + kc * 16 * 256));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+};
+
+template <int BM, int BN>
+struct G2Shape {
+  static constexpr int FM = BM / 64, FN = BN / 64;  // 32-row fragments per wave
+  static constexpr int TA = BM * G2_BK * 2, TB = BN * G2_BK * 2;  // tile bytes
+  static constexpr int WPC = BM * BN >= 256 * 256 ? 1 : 2;        // workgroups per CU
+};
+
+template <int BM, int BN, bool AK, bool BK, int EPI, bool OUTF32>
+__global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN>::WPC)) void k_gemm2_bf16(
+    GemmArgs g, int mt, int nt, int slots) {
+  using SH = G2Shape<BM, BN>;
+  constexpr int FM = SH::FM, FN = SH::FN;
+  // four tiles as separate LDS objects: the DMA into one stage then provably
+  // does not touch the stage being read
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[SH::TA];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[SH::TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t a1[SH::TA];
+  __shared__ __attribute__((aligned(1024))) uint8_t b1[SH::TB];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, ql = lane & 31, gq = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int w = blockIdx.x;
+  const int t = (w & 7) * slots + (w >> 3);
+  if (t >= mt * nt) return;
+  const int mb = t / nt, nb = t - mb * nt;
+  const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * BN;
+  const bf16* A = reinterpret_cast<const bf16*>(g.A);
+  const bf16* B = reinterpret_cast<const bf16*>(g.B);
+
+  int64_t kbeg = 0, kend = g.K;
+  if (EPI == EPI_PARTIAL) {
+    const int64_t per = ((g.K + g.split_k - 1) / g.split_k + G2_BK - 1) / G2_BK * G2_BK;
+    kbeg = (int64_t)blockIdx.y * per;
+    kend = kbeg + per < g.K ? kbeg + per : g.K;
+  }
+
+  G2Off<AK, FM> ao;
+  G2Off<BK, FN> bo;
+  ao.init(wm * 32 * FM, lane);
+  bo.init(wn * 32 * FN, lane);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  auto issue = [&](uint8_t* ta, uint8_t* tb, int64_t k0) HSTU_INLINE_LAMBDA {
+    g2_issue<AK, BM>(ta, A, g.lda, m0, g.M, k0, kend, wave, lane);
+    g2_issue<BK, BN>(tb, B, g.ldb, n0, g.N, k0, kend, wave, lane);
+  };
+  // fragments of k-chunk kc+1 are read while the MFMAs of chunk kc run
+  auto compute = [&](const uint8_t* ta, const uint8_t* tb) HSTU_INLINE_LAMBDA {
+    bf16x8 af[2][FM], bfr[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[0][i] = ao.frag(ta, i, 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[0][j] = bo.frag(tb, j, 0);
+#pragma unroll
+    for (int kc = 0; kc < G2_BK / 16; ++kc) {
+      const int cu = kc & 1;
+      if (kc + 1 < G2_BK / 16) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[cu ^ 1][i] = ao.frag(ta, i, kc + 1);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bfr[cu ^ 1][j] = bo.frag(tb, j, kc + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(af[cu][i], bfr[cu][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // double buffer, two stages per iteration so that every access names its
+  // stage statically (and no exit in the middle of the iteration, which would
+  // make the register allocator shuffle the accumulators)
+  // k-steps of this split (an empty last split has kend < kbeg)
+  const int nks = kend > kbeg ? (int)((kend - kbeg + G2_BK - 1) / G2_BK) : 0;
+  if (nks > 0) issue(a0, b0, kbeg);
+  dma_wait();
+  __syncthreads();
+  for (int ks = 0; ks + 1 < nks; ks += 2) {
+    issue(a1, b1, kbeg + (int64_t)(ks + 1) * G2_BK);
+    compute(a0, b0);
+    dma_wait();
+    __syncthreads();
+    if (ks + 2 < nks) issue(a0, b0, kbeg + (int64_t)(ks + 2) * G2_BK);
+    compute(a1, b1);
+    dma_wait();
+    __syncthreads();
+  }
+  if (nks & 1) compute(a0, b0);
+
+  // Epilogue.  The accumulator layout gives each lane one column and rows
+  // 8*(r/4) + 4*gq + r%4, so writing it straight to memory takes one 2-byte
+  // store per element.  Instead each wave stages one 32-row block of its fp32
+  // results at a time in its own LDS region (row stride ES floats: rows 4
+  // apart fall on different banks), then reads rows back as four consecutive
+  // columns per lane and applies the epilogue in fp32 with 8- or 16-byte
+  // vector accesses.  Every wave is past the main loop (and its last LDS
+  // read) before any staging write.
+  __syncthreads();
+  constexpr int WN = 32 * FN;        // columns of the wave's block
+  constexpr int ES = WN + 8;         // staging row stride (floats)
+  constexpr int LPR = WN / 4;        // lanes per staged row
+  constexpr int RPI = 64 / LPR;      // rows per read instruction
+  static_assert(32 * ES * 4 <= SH::TA && 32 * ES * 4 <= SH::TB, "staging region");
+  uint8_t* const region = wave == 0 ? a0 : wave == 1 ? b0 : wave == 2 ? a1 : b1;
+  float* const stg = reinterpret_cast<float*>(region);
+  const int lr = lane / LPR, lc = lane % LPR;
+  const int64_t ncol = n0 + wn * WN + 4 * lc;  // this lane's four output columns
+  float bias4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (g.bias && (EPI == EPI_SILU || EPI == EPI_RESID)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bias4[e] = ncol + e < g.N ? g.bias[ncol + e] : 0.0f;
+  }
+  const bool vec = ncol + 3 < g.N;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        stg[(8 * (r >> 2) + 4 * gq + (r & 3)) * ES + j * 32 + ql] = acc[i][j][r];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int rr = 0; rr < 32 / RPI; ++rr) {
+      const int rho = RPI * rr + lr;
+      const int64_t m = m0 + wm * 32 * FM + i * 32 + rho;
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>(&stg[rho * ES + 4 * lc]);
+      if (m >= g.M) continue;
+      float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+      if (EPI == EPI_PARTIAL) {
+        float* dst = g.partial + ((int64_t)blockIdx.y * g.M + m) * g.N + ncol;
+        if (vec) {
+          *reinterpret_cast<f32x4*>(dst) = v4;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ncol + e < g.N) dst[e] = v[e];
+        }
+        continue;
+      }
+      if (EPI == EPI_SILU || EPI == EPI_RESID) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += bias4[e];
+      }
+      if (EPI == EPI_RESID && g.R) {
+        const bf16* rp = reinterpret_cast<const bf16*>(g.R) + m * g.ldr + ncol;
+        if (vec) {
+          const uint2 rv = *reinterpret_cast<const uint2*>(rp);
+          v[0] += __builtin_bit_cast(float, rv.x << 16);
+          v[1] += __builtin_bit_cast(float, rv.x & 0xFFFF0000u);
+          v[2] += __builtin_bit_cast(float, rv.y << 16);
+          v[3] += __builtin_bit_cast(float, rv.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ncol + e < g.N) v[e] += (float)rp[e];
+        }
+      }
+      auto put = [&](void* base, const float (&x)[4], bool f32) HSTU_INLINE_LAMBDA {
+        if (f32) {
+          float* dst = reinterpret_cast<float*>(base) + m * g.ldc + ncol;
+          if (vec) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (ncol + e < g.N) dst[e] = x[e];
+          }
+        } else {
+          bf16* dst = reinterpret_cast<bf16*>(base) + m * g.ldc + ncol;
+          if (vec) {
+            uint2 o;
+            o.x = pack_bf16x2(x[0], x[1]);
+            o.y = pack_bf16x2(x[2], x[3]);
+            *reinterpret_cast<uint2*>(dst) = o;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (ncol + e < g.N) dst[e] = (bf16)x[e];
+          }
+        }
+      };
+      if (EPI == EPI_SILU) {
+        if (g.C2) put(g.C2, v, false);
+        float sv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[e] = silu_f(v[e]);
+        put(g.C, sv, false);
+      } else {
+        put(g.C, v, OUTF32);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Whether the DMA-staged kernel's layout assumptions hold for g: 16-byte
+// aligned operands and rows, k-contiguous operands with K a multiple of 64,
+// k-major operands with a row count (m or n) that is a multiple of 8, and
+// 8-byte aligned output rows for the vector epilogue.
+bool gemm2_ok(const GemmArgs& g) {
+  auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (!al(g.A) || !al(g.B) || (g.lda & 7) || (g.ldb & 7)) return false;
+  if ((g.a_kcont || g.b_kcont) && (g.K % G2_BK)) return false;
+  if (!g.a_kcont && (g.M & 7)) return false;
+  if (!g.b_kcont && (g.N & 7)) return false;
+  if (g.epi != EPI_PARTIAL) {
+    if (!al(g.C) || (g.ldc & 3)) return false;
+    if (g.C2 && !al(g.C2)) return false;
+    if (g.R && (!al(g.R) || (g.ldr & 3))) return false;
+  } else if (!al(g.partial) || (g.N & 3)) {
+    return false;
+  }
+  // 32-bit DMA offsets: a staged tile spans at most 256 rows of the stride
+  if (g.lda > (1 << 22) || g.ldb > (1 << 22)) return false;
+  if (g.M > INT32_MAX || g.N > INT32_MAX || g.K > INT32_MAX) return false;
+  return true;
+}
+
+template <int BM, int BN, bool AK, bool BK>
+hipError_t gemm2_launch(const GemmArgs& g, hipStream_t st) {
+  const int mt = (int)((g.M + BM - 1) / BM), nt = (int)((g.N + BN - 1) / BN);
+  const int slots = (mt * nt + 7) / 8;
+  dim3 grid((unsigned)(8 * slots), (unsigned)(g.epi == EPI_PARTIAL ? g.split_k : 1));
+  constexpr int NT = 64 * G2_NW;
+  switch (g.epi) {
+    case EPI_STORE:
+      if (g.c_f32) k_gemm2_bf16<BM, BN, AK, BK, EPI_STORE, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      else k_gemm2_bf16<BM, BN, AK, BK, EPI_STORE, false><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      break;
+    case EPI_SILU:
+      k_gemm2_bf16<BM, BN, AK, BK, EPI_SILU, false><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      break;
+    case EPI_RESID:
+      if (g.c_f32) k_gemm2_bf16<BM, BN, AK, BK, EPI_RESID, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      else k_gemm2_bf16<BM, BN, AK, BK, EPI_RESID, false><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      break;
+    case EPI_PARTIAL:
+      k_gemm2_bf16<BM, BN, AK, BK, EPI_PARTIAL, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Tile shape: the large tile when it fills the GPU's 256 CUs in several
+// nearly full rounds, else the small one (two workgroups per CU).  The large
+// tile is credited with a higher per-tile efficiency (fewer LDS reads per
+// MFMA); both are discounted by the idle share of their last round.
+template <bool AK, bool BK>
+hipError_t gemm2_ab(const GemmArgs& g, hipStream_t st) {
+  const int64_t split = g.epi == EPI_PARTIAL ? g.split_k : 1;
+  auto fill = [&](int64_t bm, int64_t bn, int64_t per_round) {
+    const int64_t tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn) * split;
+    const int64_t rounds = (tiles + per_round - 1) / per_round;
+    return (double)tiles / (double)(rounds * per_round);
+  };
+  const double big = 1.0 * fill(256, 256, 256), small = 0.8 * fill(128, 128, 512);
+  if (big >= small) return gemm2_launch<256, 256, AK, BK>(g, st);
+  return gemm2_launch<128, 128, AK, BK>(g, st);
+}
+
 // fp32 GEMM on the VALU: 64x64 tile, 4x4 outputs per thread, k-step 16.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(GemmArgs g) {
@@ -293,6 +647,12 @@ __global__ void k_colsum_final(const float* __restrict__ part, int nb, int64_t c
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (dtype == HSTU_BF16) {
+    if (gemm2_ok(g)) {
+      if (g.a_kcont && g.b_kcont) return gemm2_ab<true, true>(g, st);
+      if (g.a_kcont && !g.b_kcont) return gemm2_ab<true, false>(g, st);
+      if (!g.a_kcont && g.b_kcont) return gemm2_ab<false, true>(g, st);
+      return gemm2_ab<false, false>(g, st);
+    }
     if (g.a_kcont && g.b_kcont) return gemm_bf16_ab<true, true>(g, st);
     if (g.a_kcont && !g.b_kcont) return gemm_bf16_ab<true, false>(g, st);
     if (!g.a_kcont && g.b_kcont) return gemm_bf16_ab<false, true>(g, st);

@@ -62,6 +62,21 @@ HSTU_DEV bf16x8 lds_col8(const uint8_t* t, int k0, int n0, int lane) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Same, with the eight k rows in natural order k0 + 8g + {0..7}, for products
+// whose other operand is read along rows with lds_row8.
+template <int D>
+HSTU_DEV bf16x8 lds_col8_nat(const uint8_t* t, int k0, int n0, int lane) {
+  const int j = lane & 15;
+  const int r = k0 + 8 * (lane >> 5) + (j >> 2);
+  const int col = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int cb = (col & 7) * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (HSTU_LDS bf16x4*)(t + SwzTile<D>::off(r, col >> 3) + cb));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (HSTU_LDS bf16x4*)(t + SwzTile<D>::off(r + 4, col >> 3) + cb));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Buffer resource over `bytes` bytes from `base` (word 3 of the gfx9 format:
 // 32-bit raw addressing); loads at offsets past the range return zero.  The
 // arguments must be wave-uniform; they are moved to scalar registers
@@ -80,13 +95,18 @@ HSTU_DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
 // as zeros.  NW waves share the work.  One wave instruction fills 1 KiB of the
 // tile, lane l's 16 bytes landing at byte 16 l, so each lane fetches the
 // global chunk that the swizzle puts there.  Completion: dma_wait().
+// `last_cols` (default: the whole row stride) bounds how many elements of the
+// last valid row may be touched, so that a tile reaching past the right edge
+// of a matrix never reads past the end of its allocation.
 template <int D, int R, int NW>
 HSTU_DEV void dma_tile(uint8_t* t, const bf16* base, int64_t ld, int r0, int rlim, int wave,
-                       int lane) {
+                       int lane, int last_cols = -1) {
   constexpr int NI = R * D * 2 / 1024;
   static_assert(NI * 1024 == R * D * 2, "tile must be a whole number of KiB");
   const int nrows = max(0, min(rlim - r0, R));
-  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(base + (int64_t)r0 * ld, nrows * (int)ld * 2);
+  const int lc_el = last_cols < 0 ? (int)ld : last_cols;
+  const int nbytes = nrows > 0 ? ((nrows - 1) * (int)ld + lc_el) * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(base + (int64_t)r0 * ld, nbytes);
 #pragma unroll
   for (int i0 = 0; i0 < NI; i0 += NW) {
     const int i = i0 + wave;
