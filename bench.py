@@ -18,7 +18,6 @@ sample (one sequence) of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -31,14 +30,6 @@ if ROOT not in sys.path:
 METRIC = "HSTU layer fwd+bwd TFLOP/s and tokens/s on 1 MI355X; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-CSRC = os.path.join(ROOT, "hstu_sequential_transduction_amd", "csrc")
-KERNEL_SOURCES = {
-    "attn_fwd": ["attn_fwd.hip", "common.h", "bias.h"],
-    "attn_bwd_dkdv": ["attn_bwd.hip", "common.h", "bias.h"],
-    "attn_bwd_dq": ["attn_bwd.hip", "common.h", "bias.h"],
-    "ln_gate_fwd": ["ln_gate.hip", "common.h"],
-    "ln_gate_bwd": ["ln_gate.hip", "common.h"],
-}
 
 
 def log(msg):
@@ -46,11 +37,8 @@ def log(msg):
 
 
 def source_hash(kernel: str) -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES.get(kernel, ["gemm.hip", "common.h"]):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from hstu_sequential_transduction_amd.traffic import source_hash as sh
+    return sh(kernel)
 
 
 def kernel_work(cfg, lengths, T, cand=None):
