@@ -21,20 +21,69 @@ namespace {
 template <typename T>
 HSTU_DEV float ldf(const T* p) { return (float)(*p); }
 
-template <int EPL, typename T>
+// Row chunk loads/stores.  With VEC (every lane's EPL elements inside the
+// row and 16-byte aligned rows; checked on the host) a lane moves its chunk
+// with 16- or 8-byte accesses; otherwise element by element with bounds checks.
+HSTU_DEV void unpack4(const uint32_t* w, float* x, int nw, bool bf) {
+  for (int i = 0; i < nw; ++i) {
+    if (bf) {
+      x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+    } else {
+      x[i] = __builtin_bit_cast(float, w[i]);
+    }
+  }
+}
+
+template <int EPL, bool VEC, typename T>
 HSTU_DEV void load_row(const T* row, int c0, int W, float* x) {
+  constexpr int BYTES = EPL * (int)sizeof(T);
+  constexpr bool BF = sizeof(T) == 2;
+  if constexpr (VEC && BYTES % 16 == 0) {
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) x[e] = (c0 + e < W) ? (float)row[c0 + e] : 0.0f;
+    for (int q = 0; q < BYTES / 16; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(row + c0) + 16 * q);
+      const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+      unpack4(w, x + q * (BF ? 8 : 4), 4, BF);
+    }
+  } else if constexpr (VEC && BYTES == 8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(row + c0);
+    const uint32_t w[2] = {v.x, v.y};
+    unpack4(w, x, 2, BF);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = (c0 + e < W) ? (float)row[c0 + e] : 0.0f;
+  }
 }
 
-template <int EPL, typename T>
+HSTU_DEV uint32_t packw(const float* x, int i, bool bf) {
+  return bf ? pack_bf16x2(x[2 * i], x[2 * i + 1]) : __builtin_bit_cast(uint32_t, x[i]);
+}
+
+template <int EPL, bool VEC, typename T>
 HSTU_DEV void store_row(T* row, int c0, int W, const float* x) {
+  constexpr int BYTES = EPL * (int)sizeof(T);
+  constexpr bool BF = sizeof(T) == 2;
+  if constexpr (VEC && BYTES % 16 == 0) {
 #pragma unroll
-  for (int e = 0; e < EPL; ++e)
-    if (c0 + e < W) row[c0 + e] = (T)x[e];
+    for (int q = 0; q < BYTES / 16; ++q) {
+      const float* xq = x + q * (BF ? 8 : 4);
+      const u32x4 v = {packw(xq, 0, BF), packw(xq, 1, BF), packw(xq, 2, BF), packw(xq, 3, BF)};
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(row + c0) + 16 * q) = v;
+    }
+  } else if constexpr (VEC && BYTES == 8) {
+    uint2 v;
+    v.x = packw(x, 0, BF);
+    v.y = packw(x, 1, BF);
+    *reinterpret_cast<uint2*>(row + c0) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      if (c0 + e < W) row[c0 + e] = (T)x[e];
+  }
 }
 
-template <int EPL, typename T, typename TO>
+template <int EPL, bool VEC, typename T, typename TO>
 __global__ __launch_bounds__(256) void k_ln_gate_fwd(LnArgs a) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
@@ -49,35 +98,47 @@ __global__ __launch_bounds__(256) void k_ln_gate_fwd(LnArgs a) {
     gam[e] = (a.gamma && c0 + e < W) ? a.gamma[c0 + e] : 1.0f;
     bet[e] = (a.beta && c0 + e < W) ? a.beta[c0 + e] : 0.0f;
   }
-  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < a.T;
-       r += (int64_t)gridDim.x * 4) {
-    float x[EPL], u[EPL];
-    load_row<EPL>(O + r * a.ld_o, c0, W, x);
-    load_row<EPL>(U + r * a.ld_u, c0, W, u);
-    float s = 0.0f;
+  // two rows per wave and iteration: both rows' loads are in flight together
+  const int64_t step = (int64_t)gridDim.x * 4;
+  for (int64_t r0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r0 < a.T; r0 += 2 * step) {
+    const int64_t rr[2] = {r0, r0 + step};
+    float x[2][EPL], u[2][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s += x[e];
-    const float mean = wave_sum(s) * invW;
-    float v = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float d = (c0 + e < W) ? x[e] - mean : 0.0f;
-      v = fmaf(d, d, v);
+    for (int k = 0; k < 2; ++k) {
+      if (rr[k] < a.T) {
+        load_row<EPL, VEC>(O + rr[k] * a.ld_o, c0, W, x[k]);
+        load_row<EPL, VEC>(U + rr[k] * a.ld_u, c0, W, u[k]);
+      }
     }
-    const float var = wave_sum(v) * invW;
-    const float rstd = 1.0f / sqrtf(var + a.eps);
-    float gv[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) gv[e] = fmaf((x[e] - mean) * rstd, gam[e], bet[e]) * u[e];
-    store_row<EPL>(G + r * a.ld_g, c0, W, gv);
-    if (lane == 0) {
-      if (a.mu) a.mu[r] = mean;
-      if (a.rstd) a.rstd[r] = rstd;
+    for (int k = 0; k < 2; ++k) {
+      if (rr[k] >= a.T) break;
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s += x[k][e];
+      const float mean = wave_sum(s) * invW;
+      float v = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float d = (c0 + e < W) ? x[k][e] - mean : 0.0f;
+        v = fmaf(d, d, v);
+      }
+      const float var = wave_sum(v) * invW;
+      const float rstd = 1.0f / sqrtf(var + a.eps);
+      float gv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        gv[e] = fmaf((x[k][e] - mean) * rstd, gam[e], bet[e]) * u[k][e];
+      store_row<EPL, VEC>(G + rr[k] * a.ld_g, c0, W, gv);
+      if (lane == 0) {
+        if (a.mu) a.mu[rr[k]] = mean;
+        if (a.rstd) a.rstd[rr[k]] = rstd;
+      }
     }
   }
 }
 
-template <int EPL, typename T, typename TO>
+template <int EPL, bool VEC, typename T, typename TO>
 __global__ __launch_bounds__(256) void k_ln_gate_bwd(LnArgs a) {
   __shared__ float sg[4][64 * EPL], sb[4][64 * EPL];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -98,38 +159,51 @@ __global__ __launch_bounds__(256) void k_ln_gate_bwd(LnArgs a) {
     pg[e] = 0.0f;
     pb[e] = 0.0f;
   }
-  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < a.T; r += (int64_t)gridDim.x * 4) {
-    float x[EPL], u[EPL], dg[EPL];
-    load_row<EPL>(O + r * a.ld_o, c0, W, x);
-    load_row<EPL>(U + r * a.ld_u, c0, W, u);
-    load_row<EPL>(dG + r * a.ld_dg, c0, W, dg);
-    const float mean = a.mu[r], rstd = a.rstd[r];
-    float xh[EPL], dxh[EPL], du[EPL];
-    float s1 = 0.0f, s2 = 0.0f;
+  // two rows per wave and iteration: both rows' loads are in flight together
+  const int64_t step = (int64_t)gridDim.x * 4;
+  for (int64_t r0 = (int64_t)blockIdx.x * 4 + wave; r0 < a.T; r0 += 2 * step) {
+    const int64_t rr[2] = {r0, r0 + step};
+    float x[2][EPL], u[2][EPL], dg[2][EPL], z[2][EPL];
+    float mean[2] = {0.f, 0.f}, rstd[2] = {0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      xh[e] = (c0 + e < W) ? (x[e] - mean) * rstd : 0.0f;
-      const float y = fmaf(xh[e], gam[e], bet[e]);
-      du[e] = dg[e] * y;
-      const float dy = dg[e] * u[e];
-      pg[e] = fmaf(dy, xh[e], pg[e]);
-      pb[e] += dy;
-      dxh[e] = dy * gam[e];
-      s1 += dxh[e];
-      s2 = fmaf(dxh[e], xh[e], s2);
+    for (int k = 0; k < 2; ++k) {
+      if (rr[k] < a.T) {
+        load_row<EPL, VEC>(O + rr[k] * a.ld_o, c0, W, x[k]);
+        load_row<EPL, VEC>(U + rr[k] * a.ld_u, c0, W, u[k]);
+        load_row<EPL, VEC>(dG + rr[k] * a.ld_dg, c0, W, dg[k]);
+        if (zu) load_row<EPL, VEC>(zu + rr[k] * a.ld_zu, c0, W, z[k]);
+        mean[k] = a.mu[rr[k]];
+        rstd[k] = a.rstd[rr[k]];
+      }
     }
-    const float m1 = wave_sum(s1) * invW, m2 = wave_sum(s2) * invW;
-    float dx[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dx[e] = rstd * (dxh[e] - m1 - xh[e] * m2);
-    if (zu) {
-      float z[EPL];
-      load_row<EPL>(zu + r * a.ld_zu, c0, W, z);
+    for (int k = 0; k < 2; ++k) {
+      if (rr[k] >= a.T) break;
+      float xh[EPL], dxh[EPL], du[EPL];
+      float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) du[e] *= silu_grad_f(z[e]);
+      for (int e = 0; e < EPL; ++e) {
+        xh[e] = (c0 + e < W) ? (x[k][e] - mean[k]) * rstd[k] : 0.0f;
+        const float y = fmaf(xh[e], gam[e], bet[e]);
+        du[e] = dg[k][e] * y;
+        const float dy = dg[k][e] * u[k][e];
+        pg[e] = fmaf(dy, xh[e], pg[e]);
+        pb[e] += dy;
+        dxh[e] = dy * gam[e];
+        s1 += dxh[e];
+        s2 = fmaf(dxh[e], xh[e], s2);
+      }
+      const float m1 = wave_sum(s1) * invW, m2 = wave_sum(s2) * invW;
+      float dx[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dx[e] = rstd[k] * (dxh[e] - m1 - xh[e] * m2);
+      if (zu) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) du[e] *= silu_grad_f(z[k][e]);
+      }
+      store_row<EPL, VEC>(dU + rr[k] * a.ld_du, c0, W, du);
+      store_row<EPL, VEC>(dO + rr[k] * a.ld_do, c0, W, dx);
     }
-    store_row<EPL>(dU + r * a.ld_du, c0, W, du);
-    store_row<EPL>(dO + r * a.ld_do, c0, W, dx);
   }
   if (a.dgamma_part || a.dbeta_part) {
 #pragma unroll
@@ -153,18 +227,41 @@ int epl_for(int W) {
   return e;
 }
 
+// The vector path needs every lane's chunk inside the row (W = 64 * EPL),
+// 8- or 16-byte chunks, and 16-byte aligned rows of every tensor.
+template <typename T, typename TO>
+bool vec_ok(const LnArgs& a, int epl) {
+  if (a.W != 64 * epl) return false;
+  const int bt = epl * (int)sizeof(T), bo = epl * (int)sizeof(TO);
+  if (!(bt == 8 || bt % 16 == 0) || !(bo == 8 || bo % 16 == 0)) return false;
+  auto ok = [](const void* p, int64_t ld, size_t es) {
+    return !p || ((reinterpret_cast<uintptr_t>(p) & 15) == 0 && ((uint64_t)ld * es) % 16 == 0);
+  };
+  return ok(a.O, a.ld_o, sizeof(TO)) && ok(a.U, a.ld_u, sizeof(T)) && ok(a.G, a.ld_g, sizeof(T)) &&
+         ok(a.dG, a.ld_dg, sizeof(T)) && ok(a.zu, a.ld_zu, sizeof(T)) &&
+         ok(a.dU, a.ld_du, sizeof(T)) && ok(a.dO, a.ld_do, sizeof(T));
+}
+
+#define HSTU_LN_CASES(K, T, TO, VEC, grid)                                    \
+  switch (epl_for(a.W)) {                                                    \
+    case 1: K<1, VEC, T, TO><<<grid, 256, 0, st>>>(a); break;                \
+    case 2: K<2, VEC, T, TO><<<grid, 256, 0, st>>>(a); break;                \
+    case 4: K<4, VEC, T, TO><<<grid, 256, 0, st>>>(a); break;                \
+    case 8: K<8, VEC, T, TO><<<grid, 256, 0, st>>>(a); break;                \
+    case 16: K<16, VEC, T, TO><<<grid, 256, 0, st>>>(a); break;              \
+    default: return hipErrorInvalidValue;                                    \
+  }
+
 template <typename T, typename TO>
 hipError_t fwd_t(const LnArgs& a, hipStream_t st) {
   int64_t blocks = (a.T + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
+  if (blocks > 4096) blocks = 4096;
   if (blocks <= 0) return hipSuccess;
-  switch (epl_for(a.W)) {
-    case 1: k_ln_gate_fwd<1, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    case 2: k_ln_gate_fwd<2, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    case 4: k_ln_gate_fwd<4, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    case 8: k_ln_gate_fwd<8, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    case 16: k_ln_gate_fwd<16, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    default: return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)blocks;
+  if (vec_ok<T, TO>(a, epl_for(a.W))) {
+    HSTU_LN_CASES(k_ln_gate_fwd, T, TO, true, grid)
+  } else {
+    HSTU_LN_CASES(k_ln_gate_fwd, T, TO, false, grid)
   }
   return hipGetLastError();
 }
@@ -173,13 +270,11 @@ template <typename T, typename TO>
 hipError_t bwd_t(const LnArgs& a, hipStream_t st) {
   const int64_t blocks = a.n_part_blocks;
   if (blocks <= 0) return hipSuccess;
-  switch (epl_for(a.W)) {
-    case 1: k_ln_gate_bwd<1, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    case 2: k_ln_gate_bwd<2, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    case 4: k_ln_gate_bwd<4, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    case 8: k_ln_gate_bwd<8, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    case 16: k_ln_gate_bwd<16, T, TO><<<(unsigned)blocks, 256, 0, st>>>(a); break;
-    default: return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)blocks;
+  if (vec_ok<T, TO>(a, epl_for(a.W))) {
+    HSTU_LN_CASES(k_ln_gate_bwd, T, TO, true, grid)
+  } else {
+    HSTU_LN_CASES(k_ln_gate_bwd, T, TO, false, grid)
   }
   return hipGetLastError();
 }
