@@ -105,9 +105,26 @@ HSTU_DEV void store_grad(const f32x16* acc, float scale, bf16* dst, int64_t ld, 
 // ===========================================================================
 // dK / dV (key-block major)
 // ===========================================================================
+// d <= 64: four waves, each a 32-key group holding K, V, dK and dV in
+// registers and walking both 32-row halves of every query tile.
+// d_qk = d_v = 128 (WIDE): those registers would leave one wave per SIMD, so the
+// workgroup has eight waves (two per SIMD): K and V of the 128-key block sit
+// in LDS, wave w owns key group w % 4 and row half w / 4 of every tile, and
+// the two waves of a key group add their dK, dV partials at the end.
 template <int DQK, int DV>
 struct KvShape {
-  static constexpr bool BIG = (DQK >= 128 || DV >= 128);  // one wave per SIMD
+  static constexpr bool WIDE = (DQK == 128 && DV == 128);
+  static constexpr int NW = WIDE ? 8 : 4;   // waves per workgroup
+  static constexpr int NT = 64 * NW;        // threads
+  // workgroups per CU the registers allow (mixed widths with a 128 side: one)
+  static constexpr int OCC = (WIDE || DQK >= 128 || DV >= 128) ? 1 : 2;
+};
+
+// K and V of the workgroup's keys (WIDE shape only)
+template <int DQK, int DV>
+struct KvKeys {
+  uint8_t k[SwzTile<DQK>::bytes(ATTN_BWD_BN)];
+  uint8_t v[SwzTile<DV>::bytes(ATTN_BWD_BN)];
 };
 
 // One staged query tile: row-major Q and dO (filled by DMA, read along rows for
@@ -132,9 +149,12 @@ struct KvTables {
 };
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_bwd_dkdv(AttnArgs a) {
+__global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) void k_attn_bwd_dkdv(AttnArgs a) {
+  constexpr bool WIDE = KvShape<DQK, DV>::WIDE;
+  constexpr int NW = KvShape<DQK, DV>::NW, NT = KvShape<DQK, DV>::NT;
   __shared__ __attribute__((aligned(1024))) KvBuf<DQK, DV> kvb0;
   __shared__ __attribute__((aligned(1024))) KvBuf<DQK, DV> kvb1;
+  __shared__ __attribute__((aligned(1024))) KvKeys<WIDE ? DQK : 32, WIDE ? DV : 32> keys;
   __shared__ KvTables sm;
 
   const int w = blockIdx.x;
@@ -161,7 +181,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   {
     const float* rp = a.rab_pos + h * a.rab_stride;
     const float* rtb = a.rab_time + h * a.rab_stride;
-    for (int i = tid; i < nP; i += 256) {
+    for (int i = tid; i < nP; i += NT) {
       sm.tpos[i] = rp[i] * HSTU_NEG_LOG2E;
       sm.gpos[i] = 0.0f;
     }
@@ -175,7 +195,9 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
 
   const int k0 = kb * ATTN_BWD_BN;
   const int k1 = min(k0 + ATTN_BWD_BN, n);
-  const int kw0 = k0 + wave * 32;
+  const int kg = WIDE ? (wave & 3) : wave;  // key group
+  const int rh = WIDE ? (wave >> 2) : 0;    // row half of each tile (WIDE)
+  const int kw0 = k0 + kg * 32;
   const int kw1 = min(kw0 + 32, n);
   const int jk = kw0 + ql;  // this lane's key
   const bool kvalid = jk < n;
@@ -190,16 +212,24 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   const bf16* vh_ = reinterpret_cast<const bf16*>(a.v) + (int64_t)o0 * a.ld_v + h * DV;
   const bf16* doh = reinterpret_cast<const bf16*>(a.dout) + (int64_t)o0 * a.ld_dout + h * DV;
 
-  bf16x8 kr[DQK / 16], vr[DV / 16];
+  bf16x8 kr[WIDE ? 1 : DQK / 16], vr[WIDE ? 1 : DV / 16];
+  if constexpr (WIDE) {
+    // the block's K and V rows go to LDS (keys >= n arrive as zeros); complete
+    // before the first tile's barrier
+    dma_tile<DQK, ATTN_BWD_BN, NW>(keys.k, kh_, a.ld_qk, k0, n, wave, lane);
+    dma_tile<DV, ATTN_BWD_BN, NW>(keys.v, vh_, a.ld_v, k0, n, wave, lane);
+  } else {
 #pragma unroll
-  for (int ch = 0; ch < DQK / 16; ++ch)
-    kr[ch] = kvalid ? *reinterpret_cast<const bf16x8*>(kh_ + (int64_t)jk * a.ld_qk + ch * 16 +
-                                                       8 * g)
-                    : bf16x8{};
+    for (int ch = 0; ch < DQK / 16; ++ch)
+      kr[ch] = kvalid ? *reinterpret_cast<const bf16x8*>(kh_ + (int64_t)jk * a.ld_qk + ch * 16 +
+                                                         8 * g)
+                      : bf16x8{};
 #pragma unroll
-  for (int ch = 0; ch < DV / 16; ++ch)
-    vr[ch] = kvalid ? *reinterpret_cast<const bf16x8*>(vh_ + (int64_t)jk * a.ld_v + ch * 16 + 8 * g)
-                    : bf16x8{};
+    for (int ch = 0; ch < DV / 16; ++ch)
+      vr[ch] = kvalid ? *reinterpret_cast<const bf16x8*>(vh_ + (int64_t)jk * a.ld_v + ch * 16 +
+                                                         8 * g)
+                      : bf16x8{};
+  }
 
   f32x16 dk[DQK / 32], dv[DV / 32];
 #pragma unroll
@@ -211,8 +241,8 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   const int qend = (k0 >= nh) ? k1 : n;
   // DMA of query tile i0 into Bf; rows >= qend arrive as zeros (times: rows >= n)
   auto issue = [&](KvBuf<DQK, DV>& Bf, int i0) HSTU_INLINE_LAMBDA {
-    dma_tile<DQK, KV_QT, 4>(Bf.q, qh_, a.ld_qk, i0, qend, wave, lane);
-    dma_tile<DV, KV_QT, 4>(Bf.o, doh, a.ld_dout, i0, qend, wave, lane);
+    dma_tile<DQK, KV_QT, NW>(Bf.q, qh_, a.ld_qk, i0, qend, wave, lane);
+    dma_tile<DV, KV_QT, NW>(Bf.o, doh, a.ld_dout, i0, qend, wave, lane);
     if (wave < KV_QT / 64) {
       const int r = i0 + 64 * wave;
       if (!wide) dma_words64(Bf.t + 64 * wave, a.rel_t + o0, r, n, lane);
@@ -248,15 +278,34 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   auto mm_sd = [&](const KvBuf<DQK, DV>& B, int qh, f32x16& sacc, f32x16& dacc) HSTU_INLINE_LAMBDA {
     sacc = f32x16{};
     dacc = f32x16{};
-    bf16x8 qa[DQK / 16], oa[DV / 16];
+    if constexpr (WIDE) {
+      // both operands from LDS; reads run at most two k-chunks ahead (the
+      // other wave on the SIMD covers the latency) to stay within 256 registers
+      static_assert(DQK == DV, "wide shape");
 #pragma unroll
-    for (int ch = 0; ch < DQK / 16; ++ch) qa[ch] = lds_row8<DQK>(B.q, qh * 32 + ql, ch, g);
+      for (int c2 = 0; c2 < DQK / 16; c2 += 2) {
 #pragma unroll
-    for (int ch = 0; ch < DV / 16; ++ch) oa[ch] = lds_row8<DV>(B.o, qh * 32 + ql, ch, g);
+        for (int ch = c2; ch < c2 + 2; ++ch) {
+          const bf16x8 qa = lds_row8<DQK>(B.q, qh * 32 + ql, ch, g);
+          const bf16x8 ka = lds_row8<DQK>(keys.k, kg * 32 + ql, ch, g);
+          const bf16x8 oa = lds_row8<DV>(B.o, qh * 32 + ql, ch, g);
+          const bf16x8 va = lds_row8<DV>(keys.v, kg * 32 + ql, ch, g);
+          sacc = mfma32(qa, ka, sacc);
+          dacc = mfma32(oa, va, dacc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      bf16x8 qa[DQK / 16], oa[DV / 16];
 #pragma unroll
-    for (int ch = 0; ch < DQK / 16; ++ch) sacc = mfma32(qa[ch], kr[ch], sacc);
+      for (int ch = 0; ch < DQK / 16; ++ch) qa[ch] = lds_row8<DQK>(B.q, qh * 32 + ql, ch, g);
 #pragma unroll
-    for (int ch = 0; ch < DV / 16; ++ch) dacc = mfma32(oa[ch], vr[ch], dacc);
+      for (int ch = 0; ch < DV / 16; ++ch) oa[ch] = lds_row8<DV>(B.o, qh * 32 + ql, ch, g);
+#pragma unroll
+      for (int ch = 0; ch < DQK / 16; ++ch) sacc = mfma32(qa[ch], kr[ch], sacc);
+#pragma unroll
+      for (int ch = 0; ch < DV / 16; ++ch) dacc = mfma32(oa[ch], vr[ch], dacc);
+    }
   };
   // dV += P'^T dO ; dK += dS^T Q   (k = the 32 rows of half qh)
   auto mm_grad = [&](const KvBuf<DQK, DV>& B, int qh, const bf16x8 (&pp)[2],
@@ -331,6 +380,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
     if (kw0 >= kw1) return;
     static_for<0, KV_NH>([&](auto qhc) HSTU_INLINE_LAMBDA {
       constexpr int qh = decltype(qhc)::value;
+      if (WIDE && qh != rh) return;
       const int ir0 = i0 + qh * 32;
       const int ir1 = min(ir0 + 32, qend);
       bool active;
@@ -378,6 +428,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
     if (kw0 >= kw1) return;
     static_for<0, KV_NH>([&](auto qhc) HSTU_INLINE_LAMBDA {
       constexpr int qh = decltype(qhc)::value;
+      if (WIDE && qh != rh) return;
       const int ir0 = i0 + qh * 32;
       if (ir0 >= qend) return;
       const int last = min(31, qend - 1 - ir0);
@@ -441,8 +492,44 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   flush_time();
   if (ptot != 0.0f) atomicAdd(&sm.gpos[nP - 1], ptot);
 
+  if constexpr (WIDE) {
+    // the row-half-1 waves hand their dK, dV partials to the row-half-0 waves
+    // of the same key group through LDS (tile buffers and key block are free
+    // after the last barrier of the tile loop)
+    dma_wait();  // the key-block DMA, if no tile ran
+    __syncthreads();
+    float* xk = reinterpret_cast<float*>(kg < 2 ? (uint8_t*)keys.k : (uint8_t*)keys.v) +
+                (kg & 1) * (DQK / 32) * 16 * 64;
+    float* xv = reinterpret_cast<float*>(kg < 2 ? (uint8_t*)&kvb0 : (uint8_t*)&kvb1) +
+                (kg & 1) * (DV / 32) * 16 * 64;
+    static_assert((DQK / 32) * 16 * 64 * 4 * 2 <= (int)sizeof(KvKeys<WIDE ? DQK : 32, WIDE ? DV : 32>) / 2 || !WIDE,
+                  "dK exchange fits the key block");
+    static_assert((DV / 32) * 16 * 64 * 4 * 2 <= (int)sizeof(kvb0.q) + (int)sizeof(kvb0.o) || !WIDE,
+                  "dV exchange fits a tile buffer");
+    if (rh == 1) {
+#pragma unroll
+      for (int d = 0; d < DQK / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xk[(d * 16 + r) * 64 + lane] = dk[d][r];
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xv[(d * 16 + r) * 64 + lane] = dv[d][r];
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+      for (int d = 0; d < DQK / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dk[d][r] += xk[(d * 16 + r) * 64 + lane];
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dv[d][r] += xv[(d * 16 + r) * 64 + lane];
+    }
+  }
   const float invN = 1.0f / (float)(a.norm_mode == 0 ? a.norm_len : n);
-  if (kw0 < kw1) {
+  if (kw0 < kw1 && rh == 0) {
     store_grad<DQK / 32>(dk, invN, reinterpret_cast<bf16*>(a.dk), a.ld_qk, o0, kw0, n, h * DQK,
                          reinterpret_cast<const bf16*>(a.zpre), a.ld_z, a.zk_col + h * DQK, ql,
                          g);
@@ -453,7 +540,7 @@ __global__ __launch_bounds__(256, (KvShape<DQK, DV>::BIG ? 1 : 2)) void k_attn_b
   __syncthreads();
   float* gp = a.drab_pos + h * a.rab_stride;
   float* gt = a.drab_time + h * a.rab_stride;
-  for (int i = tid; i < nP; i += 256)
+  for (int i = tid; i < nP; i += NT)
     if (sm.gpos[i] != 0.0f) atomicAdd(&gp[i], sm.gpos[i] * invN);
   if (tid < 32 && sm.gtime[tid] != 0.0f)
     atomicAdd(&gt[tbucket_from_clz(tid, nT)], sm.gtime[tid] * invN);
@@ -679,7 +766,7 @@ template <int DQK, int DV>
 hipError_t launch_kv_t(const AttnArgs& a, int64_t mi, hipStream_t st) {
   const int64_t grid = mi * a.H;
   if (grid <= 0) return hipSuccess;
-  k_attn_bwd_dkdv<DQK, DV><<<(unsigned)grid, 256, 0, st>>>(a);
+  k_attn_bwd_dkdv<DQK, DV><<<(unsigned)grid, KvShape<DQK, DV>::NT, 0, st>>>(a);
   return hipGetLastError();
 }
 template <int DQK, int DV>
