@@ -175,10 +175,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // DMA-staged bf16 GEMM, BM x BN output tile per workgroup of four waves
 // (2 x 2), each wave a (BM/2) x (BN/2) block of 32x32x16 MFMAs, k-step 64.
-// Two shapes: 256x256 (one workgroup per CU, the whole register file per
-// wave, eight 16-byte LDS operand reads per sixteen MFMAs) for GEMMs large
-// enough to fill the GPU several times over, and 128x128 (two workgroups per
-// CU, so one's epilogue overlaps the other's main loop) for the rest.
+// The layer uses 128x128 (two workgroups per CU, so one's epilogue and DMA
+// waits overlap the other's main loop); 256x256 (one workgroup per CU, eight
+// 16-byte LDS operand reads per sixteen MFMAs) is available to the template.
 // Operand tiles arrive by buffer->LDS DMA into a static double buffer.  A
 // k-contiguous operand is stored [rows][64 k] and read along rows; a k-major
 // operand ([k][rows] in memory) is stored as [64 k][128]-column tiles and read
@@ -508,20 +507,15 @@ hipError_t gemm2_launch(const GemmArgs& g, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Tile shape: the large tile when it fills the GPU's 256 CUs in several
-// nearly full rounds, else the small one (two workgroups per CU).  The large
-// tile is credited with a higher per-tile efficiency (fewer LDS reads per
-// MFMA); both are discounted by the idle share of their last round.
+// Tile shape.  Measured on the layer's six GEMMs (M = 34K..57K tokens,
+// N, K in 512..2048): 128x128 tiles with two workgroups per CU beat 256x256
+// tiles with one in every case (UVQK 0.28 vs 0.31 ms, output projection 0.11
+// vs 0.15 ms, 8-layer UVQK 0.98 vs 1.34 ms): the second workgroup hides the
+// other's epilogue and DMA latency, which outweighs the larger tile's halved
+// LDS reads per MFMA.  The template still accepts 256x256 (one workgroup
+// per CU) for shapes where that measures faster.
 template <bool AK, bool BK>
 hipError_t gemm2_ab(const GemmArgs& g, hipStream_t st) {
-  const int64_t split = g.epi == EPI_PARTIAL ? g.split_k : 1;
-  auto fill = [&](int64_t bm, int64_t bn, int64_t per_round) {
-    const int64_t tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn) * split;
-    const int64_t rounds = (tiles + per_round - 1) / per_round;
-    return (double)tiles / (double)(rounds * per_round);
-  };
-  const double big = 1.0 * fill(256, 256, 256), small = 0.8 * fill(128, 128, 512);
-  if (big >= small) return gemm2_launch<256, 256, AK, BK>(g, st);
   return gemm2_launch<128, 128, AK, BK>(g, st);
 }
 
