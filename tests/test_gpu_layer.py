@@ -153,6 +153,30 @@ def test_layer_bwd_small(B, ci, hist, c, variant):
     check_close(host(g.drab_time), want["drab_time"], "bf16", "drab_time")
 
 
+def test_layer_train_unaligned_width(B):
+    """d_model = 72: the projection's k extent is not a multiple of the DMA
+    GEMM's k-step, so the forward and input-gradient GEMMs take the
+    register-staged GEMM kernel; the weight gradients (k-major operands) keep
+    the DMA kernel.  Both paths against the oracle in one training step."""
+    cfg = dataclasses.replace(synth.get_config(2), D=72, H=2, d_qk=32, d_v=32)
+    cfg = cfg.shrunk(B=3, lengths=("list", [70, 257, 33])).unit_scale()
+    say("layer train d_model=72")
+    inp = synth.make_inputs(cfg, seed=72, with_dy=True)
+    d = Dev(inp, cfg)
+    lc = _lcfg(B, cfg)
+    dx, g = _train_step(B, d, lc, inp.T)
+    w = inp.layers[0]
+    f = _flags(cfg)
+    Y, sv = orc.layer_fwd(inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                          inp.timestamps, None, f)
+    want = orc.layer_bwd(inp.dY, inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                         inp.timestamps, None, f, sv)
+    check_close(host(dx), want["dX"], "bf16", "dX")
+    check_close(host(dx) - inp.dY, want["dX"] - inp.dY, "bf16", "dX - dY")
+    for k in ("dW1", "dW2", "drab_pos", "drab_time"):
+        check_close(host(getattr(g, k)), want[k], "bf16", k)
+
+
 def test_layer_bwd_affine_and_biases(B):
     cfg = synth.get_config(2).shrunk(B=3, lengths=("list", [64, 257, 31])).unit_scale()
     inp = synth.make_inputs(cfg, seed=77, with_dy=True)
