@@ -212,6 +212,16 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
   const bf16* vh_ = reinterpret_cast<const bf16*>(a.v) + (int64_t)o0 * a.ld_v + h * DV;
   const bf16* doh = reinterpret_cast<const bf16*>(a.dout) + (int64_t)o0 * a.ld_dout + h * DV;
 
+  // WIDE: per-lane byte offsets of the S/dA row operands (row ql of a 32-row
+  // block, chunk 2 ch + g); the swizzle of rows 32 apart is the same
+  int roff[WIDE ? DQK / 16 : 1], koff[WIDE ? DQK / 16 : 1];
+  if constexpr (WIDE) {
+#pragma unroll
+    for (int ch = 0; ch < DQK / 16; ++ch) {
+      roff[ch] = SwzTile<DQK>::off(ql, 2 * ch + g);
+      koff[ch] = kg * 32 * 2 * DQK + roff[ch];
+    }
+  }
   bf16x8 kr[WIDE ? 1 : DQK / 16], vr[WIDE ? 1 : DV / 16];
   if constexpr (WIDE) {
     // the block's K and V rows go to LDS (keys >= n arrive as zeros); complete
@@ -280,16 +290,18 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
     dacc = f32x16{};
     if constexpr (WIDE) {
       // both operands from LDS; reads run at most two k-chunks ahead (the
-      // other wave on the SIMD covers the latency) to stay within 256 registers
+      // other wave on the SIMD covers the latency) to stay within 256 registers.
+      // Addresses: the per-lane offsets roff/koff plus constants (tile, row
+      // block) that the compiler folds into the instructions' immediates.
       static_assert(DQK == DV, "wide shape");
 #pragma unroll
       for (int c2 = 0; c2 < DQK / 16; c2 += 2) {
 #pragma unroll
         for (int ch = c2; ch < c2 + 2; ++ch) {
-          const bf16x8 qa = lds_row8<DQK>(B.q, qh * 32 + ql, ch, g);
-          const bf16x8 ka = lds_row8<DQK>(keys.k, kg * 32 + ql, ch, g);
-          const bf16x8 oa = lds_row8<DV>(B.o, qh * 32 + ql, ch, g);
-          const bf16x8 va = lds_row8<DV>(keys.v, kg * 32 + ql, ch, g);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(B.q + qh * 32 * 2 * DQK + roff[ch]);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(keys.k + koff[ch]);
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(B.o + qh * 32 * 2 * DV + roff[ch]);
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(keys.v + koff[ch]);
           sacc = mfma32(qa, ka, sacc);
           dacc = mfma32(oa, va, dacc);
         }
