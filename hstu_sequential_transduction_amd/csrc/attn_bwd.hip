@@ -271,15 +271,19 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
     if (need <= nh) far_start = min(qend, k0 + ((max(need - k0, 0) + KV_QT - 1) / KV_QT) * KV_QT);
   }
 
-  // per-lane running sums of the far phase: time buckets (curB, curB+1), position nP-1
+  // per-lane running sums of the far phase (position bucket nP-1): run_u holds
+  // rows of time bucket curB from halves where no lane changes bucket; run_tot
+  // and run_a the rows of halves with one change (run_a: those in bucket curB,
+  // the rest in curB + 1)
   int curB = -1;
-  float run_tot = 0.0f, run_a = 0.0f, ptot = 0.0f;
+  float run_u = 0.0f, run_tot = 0.0f, run_a = 0.0f, ptot = 0.0f;
   auto flush_time = [&]() HSTU_INLINE_LAMBDA {
     if (curB >= 0) {
-      if (run_a != 0.0f) atomicAdd(&sm.gtime[curB], run_a);
+      if (run_a + run_u != 0.0f) atomicAdd(&sm.gtime[curB], run_a + run_u);
       if (run_tot - run_a != 0.0f) atomicAdd(&sm.gtime[curB + 1], run_tot - run_a);
     }
-    ptot += run_tot;
+    ptot += run_tot + run_u;
+    run_u = 0.0f;
     run_tot = 0.0f;
     run_a = 0.0f;
   };
@@ -446,11 +450,21 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       const int last = min(31, qend - 1 - ir0);
       const int cF = tclz_narrow(B.t[qh * 32 + last], tjm);
       const int cL = tclz_narrow(B.t[qh * 32], tjm);
+      const bool uni = __all(!kvalid || (sorted && cL == cF));
       const bool one = __all(!kvalid || (sorted && cL - cF <= 1));
       f32x16 sacc, dacc;
       mm_sd(B, qh, sacc, dacc);
       bf16x8 pp[2], dd[2];
-      if (one) {
+      if (uni) {
+        // every lane sees one time bucket on this half: constant bias, one sum
+        if (kvalid && cF != curB) {
+          flush_time();
+          curB = cF;
+        }
+        const float ba = sm.tfar[cF];
+        elems(B, qh, sacc, dacc, pp, dd, [&](int, int32_t) { return ba; },
+              [&](int, int32_t, float ds) { run_u += ds; }, bconst<false>{}, 0, 0);
+      } else if (one) {
         if (kvalid && cF != curB) {
           flush_time();
           curB = cF;
