@@ -55,6 +55,13 @@ HSTU_DEV void static_for(F&& f) {
   }
 }
 
+// The value held by the next lane (lane + 1) of each 16-lane row; 0 in the
+// last lane of a row (DPP row shift with out-of-row reads bound to zero).
+HSTU_DEV float dpp_row_next(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x101, 0xF, 0xF, true));
+}
+
 // sigma and P' from the pre-scaled score s' = -log2(e) * (q.k + bias)
 HSTU_DEV void silu_parts(float sb, float& sig, float& pp) {
   sig = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sb));
@@ -120,19 +127,19 @@ struct KvShape {
   static constexpr int OCC = (WIDE || DQK >= 128 || DV >= 128) ? 1 : 2;
 };
 
-// K and V of the workgroup's keys (WIDE shape only)
-template <int DQK, int DV>
+// K and V of the workgroup's keys (WIDE shape only; read along rows)
+template <int DQK, int DV, bool USED>
 struct KvKeys {
-  uint8_t k[SwzTile<DQK>::bytes(ATTN_BWD_BN)];
-  uint8_t v[SwzTile<DV>::bytes(ATTN_BWD_BN)];
+  uint8_t k[USED ? PadTile<DQK, false>::bytes(ATTN_BWD_BN) : 16];
+  uint8_t v[USED ? PadTile<DV, false>::bytes(ATTN_BWD_BN) : 16];
 };
 
 // One staged query tile: row-major Q and dO (filled by DMA, read along rows for
 // S and dA and down columns for the dK and dV products) and the row times.
 template <int DQK, int DV>
 struct KvBuf {
-  uint8_t q[SwzTile<DQK>::bytes(KV_QT)];
-  uint8_t o[SwzTile<DV>::bytes(KV_QT)];
+  uint8_t q[PadTile<DQK, true>::bytes(KV_QT)];
+  uint8_t o[PadTile<DV, true>::bytes(KV_QT)];
   int32_t t[KV_QT];    // query times relative to the sequence minimum (narrow)
   int64_t t64[KV_QT];  // query times (wide sequences)
 };
@@ -154,7 +161,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
   constexpr int NW = KvShape<DQK, DV>::NW, NT = KvShape<DQK, DV>::NT;
   __shared__ __attribute__((aligned(1024))) KvBuf<DQK, DV> kvb0;
   __shared__ __attribute__((aligned(1024))) KvBuf<DQK, DV> kvb1;
-  __shared__ __attribute__((aligned(1024))) KvKeys<WIDE ? DQK : 32, WIDE ? DV : 32> keys;
+  __shared__ __attribute__((aligned(1024))) KvKeys<DQK, DV, WIDE> keys;
   __shared__ KvTables sm;
 
   const int w = blockIdx.x;
@@ -212,22 +219,18 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
   const bf16* vh_ = reinterpret_cast<const bf16*>(a.v) + (int64_t)o0 * a.ld_v + h * DV;
   const bf16* doh = reinterpret_cast<const bf16*>(a.dout) + (int64_t)o0 * a.ld_dout + h * DV;
 
-  // WIDE: per-lane byte offsets of the S/dA row operands (row ql of a 32-row
-  // block, chunk 2 ch + g); the swizzle of rows 32 apart is the same
-  int roff[WIDE ? DQK / 16 : 1], koff[WIDE ? DQK / 16 : 1];
-  if constexpr (WIDE) {
-#pragma unroll
-    for (int ch = 0; ch < DQK / 16; ++ch) {
-      roff[ch] = SwzTile<DQK>::off(ql, 2 * ch + g);
-      koff[ch] = kg * 32 * 2 * DQK + roff[ch];
-    }
-  }
+  // per-lane byte offsets of the S/dA row operands (row ql of a 32-row block,
+  // chunk g; k-chunk ch adds 32 ch bytes): tile rows and (WIDE) key rows
+  constexpr int SQ = PadTile<DQK, true>::STRIDE, SO = PadTile<DV, true>::STRIDE;
+  constexpr int SK = PadTile<DQK, false>::STRIDE;
+  const int roff = ql * SQ + 16 * g;
+  const int koff = (kg * 32 + ql) * SK + 16 * g;
   bf16x8 kr[WIDE ? 1 : DQK / 16], vr[WIDE ? 1 : DV / 16];
   if constexpr (WIDE) {
     // the block's K and V rows go to LDS (keys >= n arrive as zeros); complete
     // before the first tile's barrier
-    dma_tile<DQK, ATTN_BWD_BN, NW>(keys.k, kh_, a.ld_qk, k0, n, wave, lane);
-    dma_tile<DV, ATTN_BWD_BN, NW>(keys.v, vh_, a.ld_v, k0, n, wave, lane);
+    dma_pad_tile<DQK, false, ATTN_BWD_BN, NW>(keys.k, kh_, a.ld_qk, k0, n, wave, lane);
+    dma_pad_tile<DV, false, ATTN_BWD_BN, NW>(keys.v, vh_, a.ld_v, k0, n, wave, lane);
   } else {
 #pragma unroll
     for (int ch = 0; ch < DQK / 16; ++ch)
@@ -251,8 +254,8 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
   const int qend = (k0 >= nh) ? k1 : n;
   // DMA of query tile i0 into Bf; rows >= qend arrive as zeros (times: rows >= n)
   auto issue = [&](KvBuf<DQK, DV>& Bf, int i0) HSTU_INLINE_LAMBDA {
-    dma_tile<DQK, KV_QT, NW>(Bf.q, qh_, a.ld_qk, i0, qend, wave, lane);
-    dma_tile<DV, KV_QT, NW>(Bf.o, doh, a.ld_dout, i0, qend, wave, lane);
+    dma_pad_tile<DQK, true, KV_QT, NW>(Bf.q, qh_, a.ld_qk, i0, qend, wave, lane);
+    dma_pad_tile<DV, true, KV_QT, NW>(Bf.o, doh, a.ld_dout, i0, qend, wave, lane);
     if (wave < KV_QT / 64) {
       const int r = i0 + 64 * wave;
       if (!wide) dma_words64(Bf.t + 64 * wave, a.rel_t + o0, r, n, lane);
@@ -302,10 +305,10 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       for (int c2 = 0; c2 < DQK / 16; c2 += 2) {
 #pragma unroll
         for (int ch = c2; ch < c2 + 2; ++ch) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(B.q + qh * 32 * 2 * DQK + roff[ch]);
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(keys.k + koff[ch]);
-          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(B.o + qh * 32 * 2 * DV + roff[ch]);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(keys.v + koff[ch]);
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(B.q + qh * 32 * SQ + roff + 32 * ch);
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(keys.k + koff + 32 * ch);
+          const bf16x8 oa = *reinterpret_cast<const bf16x8*>(B.o + qh * 32 * SO + roff + 32 * ch);
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(keys.v + koff + 32 * ch);
           sacc = mfma32(qa, ka, sacc);
           dacc = mfma32(oa, va, dacc);
         }
@@ -314,9 +317,11 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
     } else {
       bf16x8 qa[DQK / 16], oa[DV / 16];
 #pragma unroll
-      for (int ch = 0; ch < DQK / 16; ++ch) qa[ch] = lds_row8<DQK>(B.q, qh * 32 + ql, ch, g);
+      for (int ch = 0; ch < DQK / 16; ++ch)
+        qa[ch] = *reinterpret_cast<const bf16x8*>(B.q + qh * 32 * SQ + roff + 32 * ch);
 #pragma unroll
-      for (int ch = 0; ch < DV / 16; ++ch) oa[ch] = lds_row8<DV>(B.o, qh * 32 + ql, ch, g);
+      for (int ch = 0; ch < DV / 16; ++ch)
+        oa[ch] = *reinterpret_cast<const bf16x8*>(B.o + qh * 32 * SO + ql * SO + 16 * g + 32 * ch);
 #pragma unroll
       for (int ch = 0; ch < DQK / 16; ++ch) sacc = mfma32(qa[ch], kr[ch], sacc);
 #pragma unroll
@@ -330,10 +335,10 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
     for (int u = 0; u < 2; ++u) {
       bf16x8 ob[DV / 32], qb[DQK / 32];
 #pragma unroll
-      for (int d = 0; d < DV / 32; ++d) ob[d] = lds_col8<DV>(B.o, qh * 32 + 16 * u, d * 32, lane);
+      for (int d = 0; d < DV / 32; ++d) ob[d] = pad_col8<DV>(B.o, qh * 32 + 16 * u, d * 32, lane);
 #pragma unroll
       for (int d = 0; d < DQK / 32; ++d)
-        qb[d] = lds_col8<DQK>(B.q, qh * 32 + 16 * u, d * 32, lane);
+        qb[d] = pad_col8<DQK>(B.q, qh * 32 + 16 * u, d * 32, lane);
 #pragma unroll
       for (int d = 0; d < DV / 32; ++d) dv[d] = mfma32(pp[u], ob[d], dv[d]);
 #pragma unroll
@@ -343,12 +348,14 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
 
   // Element loop of one half: lane = key jk, element r is row ib + kc with
   // kc = 8*(r/4) + r%4; bias_of(kc, t) is pre-scaled, grad_of(kc, t, ds).
+  // grad4(aa, x) receives the dS of the four consecutive rows 8 aa + {0..3}.
   auto elems = [&](const KvBuf<DQK, DV>& B, int qh, const f32x16& sacc, const f32x16& dacc,
                    bf16x8 (&pp)[2], bf16x8 (&dd)[2], auto bias_of, auto grad_of, auto masked,
-                   int lo, int hi) HSTU_INLINE_LAMBDA {
+                   int lo, int hi, auto grad4) HSTU_INLINE_LAMBDA {
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
       const i32x4 t4 = *reinterpret_cast<const i32x4*>(&B.t[qh * 32 + 8 * aa + 4 * g]);
+      float x4[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kc = 8 * aa + r;
@@ -363,9 +370,25 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
           ds = ok ? ds : 0.0f;
         }
         grad_of(kc, t4[r], ds);
+        x4[r] = ds;
         pp[aa >> 1][(aa & 1) * 4 + r] = (bf16)p;
         dd[aa >> 1][(aa & 1) * 4 + r] = (bf16)ds;
       }
+      grad4(aa, x4);
+      // masked tiles: keep the table reads of later groups from being hoisted
+      // (their addresses and results would all be live at once)
+      if constexpr (decltype(masked)::value) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto no4 = [&](int, const float (&)[4]) HSTU_INLINE_LAMBDA {};
+
+  // The 32-row halves of a staged tile this wave computes: both (d <= 64), or
+  // its own (WIDE; one copy of the code with the half index in a register).
+  auto for_halves = [&](auto f) HSTU_INLINE_LAMBDA {
+    if constexpr (WIDE) {
+      f(rh);
+    } else {
+      static_for<0, KV_NH>([&](auto qhc) HSTU_INLINE_LAMBDA { f(decltype(qhc)::value); });
     }
   };
 
@@ -390,13 +413,30 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
     }
     nb_acc += ds;
   };
+  // Position gradient of four consecutive rows 8 aa + {0..3} when the bucket is
+  // a function of i - j alone (history rows and keys): element (row r, lane l)
+  // shares its bucket with (row r + 1, lane l + 1), so the four rows are summed
+  // along diagonals within each 16-lane row first (three DPP shifts) and the
+  // LDS float atomics, which cost a few clocks per active lane, drop from four
+  // full-wave instructions to one plus three at the first lane of each row
+  // (whose diagonals leave the row).
+  auto near_pos4 = [&](int aa, const float (&x)[4], auto bidx) HSTU_INLINE_LAMBDA {
+    const float p3 = x[3];
+    const float p2 = x[2] + dpp_row_next(p3);
+    const float p1 = x[1] + dpp_row_next(p2);
+    const float y = x[0] + dpp_row_next(p1);
+    near_pos_grad(bidx(8 * aa), y);
+    if ((lane & 15) == 0) {
+      near_pos_grad(bidx(8 * aa + 1), p1);
+      near_pos_grad(bidx(8 * aa + 2), p2);
+      near_pos_grad(bidx(8 * aa + 3), p3);
+    }
+  };
 
   // near-phase tile: per-half masks and per-element buckets
   auto near_tile = [&](const KvBuf<DQK, DV>& B, int i0) HSTU_INLINE_LAMBDA {
     if (kw0 >= kw1) return;
-    static_for<0, KV_NH>([&](auto qhc) HSTU_INLINE_LAMBDA {
-      constexpr int qh = decltype(qhc)::value;
-      if (WIDE && qh != rh) return;
+    for_halves([&](const int qh) HSTU_INLINE_LAMBDA {
       const int ir0 = i0 + qh * 32;
       const int ir1 = min(ir0 + 32, qend);
       bool active;
@@ -404,7 +444,11 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       else active = ir0 < kw1 && ir1 > kw0;
       if (!active || ir0 >= ir1) return;
       f32x16 sacc, dacc;
+      // keep the element loop's address arithmetic out of the product block,
+      // which needs the registers for operand read-ahead
+      __builtin_amdgcn_sched_barrier(0);
       mm_sd(B, qh, sacc, dacc);
+      __builtin_amdgcn_sched_barrier(0);
       bf16x8 pp[2], dd[2];
       const int ib = ir0 + 4 * g;
       // p(i) - p(j) = min(ib + kc, nh) - pJ ; allowed rows: history key -> i >= j,
@@ -414,14 +458,20 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       const int lo = kvalid ? d0 : 1 << 20;
       const int hi = min(jk < nh ? (1 << 20) : d0, qend - 1 - ib);
       auto bidx = [&](int kc) HSTU_INLINE_LAMBDA { return min(max(min(pd0 + kc, pdmax), 0), nP - 1); };
+      // history keys and rows (or masked rows): the bucket depends on i - j only
+      const bool diag = k1 <= nh && min(ir0 + 32, qend) <= nh;
       if (!wide) {
         elems(B, qh, sacc, dacc, pp, dd,
               [&](int kc, int32_t t) { return sm.tpos[bidx(kc)] + sm.ttime[tclz_narrow(t, tjm)]; },
-              [&](int kc, int32_t t, float ds) {
-                near_pos_grad(bidx(kc), ds);
-                near_time_grad(tclz_narrow(t, tjm), ds);
-              },
-              bconst<true>{}, lo, hi);
+              [&](int, int32_t t, float ds) { near_time_grad(tclz_narrow(t, tjm), ds); },
+              bconst<true>{}, lo, hi, [&](int aa, const float (&x)[4]) {
+                if (diag) {
+                  near_pos4(aa, x, bidx);
+                } else {
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) near_pos_grad(bidx(8 * aa + r), x[r]);
+                }
+              });
       } else {
         elems(B, qh, sacc, dacc, pp, dd,
               [&](int kc, int32_t) {
@@ -432,7 +482,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
                 near_pos_grad(bidx(kc), ds);
                 near_time_grad(tclz_wide(B.t64[qh * 32 + 4 * g + kc], tj64), ds);
               },
-              bconst<true>{}, lo, hi);
+              bconst<true>{}, lo, hi, no4);
       }
       mm_grad(B, qh, pp, dd);
     });
@@ -442,9 +492,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
   // lane's time bucket changes at most once inside a half in the common case
   auto far_tile = [&](const KvBuf<DQK, DV>& B, int i0) HSTU_INLINE_LAMBDA {
     if (kw0 >= kw1) return;
-    static_for<0, KV_NH>([&](auto qhc) HSTU_INLINE_LAMBDA {
-      constexpr int qh = decltype(qhc)::value;
-      if (WIDE && qh != rh) return;
+    for_halves([&](const int qh) HSTU_INLINE_LAMBDA {
       const int ir0 = i0 + qh * 32;
       if (ir0 >= qend) return;
       const int last = min(31, qend - 1 - ir0);
@@ -463,7 +511,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
         }
         const float ba = sm.tfar[cF];
         elems(B, qh, sacc, dacc, pp, dd, [&](int, int32_t) { return ba; },
-              [&](int, int32_t, float ds) { run_u += ds; }, bconst<false>{}, 0, 0);
+              [&](int, int32_t, float ds) { run_u += ds; }, bconst<false>{}, 0, 0, no4);
       } else if (one) {
         if (kvalid && cF != curB) {
           flush_time();
@@ -477,7 +525,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
                 run_tot += ds;
                 run_a += t >= thr ? ds : 0.0f;
               },
-              bconst<false>{}, 0, 0);
+              bconst<false>{}, 0, 0, no4);
       } else {
         elems(B, qh, sacc, dacc, pp, dd,
               [&](int, int32_t t) { return sm.tfar[tclz_narrow(t, tjm)]; },
@@ -485,7 +533,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
                 ptot += ds;
                 atomicAdd(&sm.gtime[tclz_narrow(t, tjm)], ds);
               },
-              bconst<false>{}, 0, 0);
+              bconst<false>{}, 0, 0, no4);
       }
       mm_grad(B, qh, pp, dd);
     });
@@ -528,7 +576,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
                 (kg & 1) * (DQK / 32) * 16 * 64;
     float* xv = reinterpret_cast<float*>(kg < 2 ? (uint8_t*)&kvb0 : (uint8_t*)&kvb1) +
                 (kg & 1) * (DV / 32) * 16 * 64;
-    static_assert((DQK / 32) * 16 * 64 * 4 * 2 <= (int)sizeof(KvKeys<WIDE ? DQK : 32, WIDE ? DV : 32>) / 2 || !WIDE,
+    static_assert((DQK / 32) * 16 * 64 * 4 * 2 <= (int)sizeof(KvKeys<DQK, DV, WIDE>) / 2 || !WIDE,
                   "dK exchange fits the key block");
     static_assert((DV / 32) * 16 * 64 * 4 * 2 <= (int)sizeof(kvb0.q) + (int)sizeof(kvb0.o) || !WIDE,
                   "dV exchange fits a tile buffer");

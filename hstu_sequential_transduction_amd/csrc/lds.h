@@ -77,6 +77,53 @@ HSTU_DEV bf16x8 lds_col8_nat(const uint8_t* t, int k0, int n0, int lane) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Row-major bf16 tile of D columns whose rows are padded to STRIDE bytes, so
+// that neither read form needs a per-lane swizzle: every operand address is
+// one per-lane base plus a compile-time offset.  With rows 16 * odd bytes apart
+// (modulo the 256-byte bank cycle), 16 consecutive rows at one 16-byte chunk
+// fall on 16 distinct bank groups (row reads); for tiles also read down columns
+// (TR) the stride is chosen so that 4 consecutive rows x one 32-byte piece, what
+// a 16-lane group of a transpose read touches, fall on distinct banks as well.
+template <int D, bool TR>
+struct PadTile {
+  static_assert(D == 32 || D == 64 || D == 128, "tile width");
+  static constexpr int STRIDE = D == 128 ? (TR ? 304 : 272) : D == 64 ? 144 : (TR ? 112 : 80);
+  static constexpr int SPR = STRIDE / 16;  // 16-byte slots per row
+  static constexpr int CPR = D / 8;        // of which hold data
+  // whole KiB: the last DMA instruction fills a full KiB
+  static constexpr int bytes(int rows) { return (rows * STRIDE + 1023) / 1024 * 1024; }
+  HSTU_DEV static int off(int r, int c) { return r * STRIDE + c * 16; }
+};
+
+// PadTile operand reads: the same lane layouts as lds_row8 / lds_col8 /
+// lds_col8_nat above.
+template <int D, bool TR>
+HSTU_DEV bf16x8 pad_row8(const uint8_t* t, int row, int ch, int g) {
+  return *reinterpret_cast<const bf16x8*>(t + PadTile<D, TR>::off(row, 2 * ch + g));
+}
+template <int D>
+HSTU_DEV bf16x8 pad_col8(const uint8_t* t, int k0, int n0, int lane) {
+  constexpr int S = PadTile<D, true>::STRIDE;
+  const int j = lane & 15;
+  const int r = k0 + 4 * (lane >> 5) + (j >> 2);
+  const int col = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const uint8_t* p = t + r * S + col * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HSTU_LDS bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HSTU_LDS bf16x4*)(p + 8 * S));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int D>
+HSTU_DEV bf16x8 pad_col8_nat(const uint8_t* t, int k0, int n0, int lane) {
+  constexpr int S = PadTile<D, true>::STRIDE;
+  const int j = lane & 15;
+  const int r = k0 + 8 * (lane >> 5) + (j >> 2);
+  const int col = n0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const uint8_t* p = t + r * S + col * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HSTU_LDS bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((HSTU_LDS bf16x4*)(p + 4 * S));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Buffer resource over `bytes` bytes from `base` (word 3 of the gfx9 format:
 // 32-bit raw addressing); loads at offsets past the range return zero.  The
 // arguments must be wave-uniform; they are moved to scalar registers
@@ -116,6 +163,31 @@ HSTU_DEV void dma_tile(uint8_t* t, const bf16* base, int64_t ld, int r0, int rli
       const int lc = ((p % (2 * D)) >> 4) ^ SwzTile<D>::swz(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (HSTU_LDS void*)(t + i * 1024), 16,
                                                row * (int)ld * 2 + lc * 16, 0, 0, 0);
+    }
+  }
+}
+
+// dma_tile for a PadTile: slot s = 64 i + lane of wave instruction i lands at
+// byte 16 s, i.e. row s / SPR, chunk s % SPR.  Padding slots fetch whatever
+// follows the row (or zeros past the range) and are never read.
+template <int D, bool TR, int R, int NW>
+HSTU_DEV void dma_pad_tile(uint8_t* t, const bf16* base, int64_t ld, int r0, int rlim, int wave,
+                           int lane, int last_cols = -1) {
+  using P = PadTile<D, TR>;
+  constexpr int NI = P::bytes(R) / 1024;
+  const int nrows = max(0, min(rlim - r0, R));
+  const int lc_el = last_cols < 0 ? (int)ld : last_cols;
+  const int nbytes = nrows > 0 ? ((nrows - 1) * (int)ld + lc_el) * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rs = buf_rsrc(base + (int64_t)r0 * ld, nbytes);
+#pragma unroll
+  for (int i0 = 0; i0 < NI; i0 += NW) {
+    const int i = i0 + wave;
+    if (NI % NW == 0 || i < NI) {
+      const int sl = i * 64 + lane;
+      const int row = sl / P::SPR;
+      const int c = sl - row * P::SPR;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (HSTU_LDS void*)(t + i * 1024), 16,
+                                               row * (int)ld * 2 + c * 16, 0, 0, 0);
     }
   }
 }
