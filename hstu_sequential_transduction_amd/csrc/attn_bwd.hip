@@ -625,10 +625,11 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
 // ===========================================================================
 // One staged key tile: row-major K (A of S^T = K Q^T along rows, B of
 // dQ += dS K down columns) and V (A of dA^T = V dO^T), and the key times.
+// Padded rows (PadTile): K is read both ways, V along rows only.
 template <int DQK, int DV>
 struct DqBuf {
-  uint8_t k[SwzTile<DQK>::bytes(DQ_BN)];
-  uint8_t v[SwzTile<DV>::bytes(DQ_BN)];
+  uint8_t k[PadTile<DQK, true>::bytes(DQ_BN)];
+  uint8_t v[PadTile<DV, false>::bytes(DQ_BN)];
   int32_t t[DQ_BN];    // key times relative to the sequence minimum (narrow)
   int64_t t64[DQ_BN];  // key times (wide sequences)
 };
@@ -712,8 +713,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
   // DMA of key tile kt; keys >= n arrive as zeros
   auto issue = [&](DqBuf<DQK, DV>& Bf, int kt) HSTU_INLINE_LAMBDA {
     const int j0 = kt * DQ_BN;
-    dma_tile<DQK, DQ_BN, 4>(Bf.k, kh_, a.ld_qk, j0, n, wave, lane);
-    dma_tile<DV, DQ_BN, 4>(Bf.v, vh_, a.ld_v, j0, n, wave, lane);
+    dma_pad_tile<DQK, true, DQ_BN, 4>(Bf.k, kh_, a.ld_qk, j0, n, wave, lane);
+    dma_pad_tile<DV, false, DQ_BN, 4>(Bf.v, vh_, a.ld_v, j0, n, wave, lane);
     if (wave == 0) {
       if (!wide) dma_words64(Bf.t, a.rel_t + o0, j0, n, lane);
       else dma_dwords64(Bf.t64, tsq, j0, n, lane);
@@ -749,9 +750,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
       {
         bf16x8 ka[DQK / 16], va[DV / 16];
 #pragma unroll
-        for (int ch = 0; ch < DQK / 16; ++ch) ka[ch] = lds_row8<DQK>(B.k, hf * 32 + ql, ch, g);
+        for (int ch = 0; ch < DQK / 16; ++ch) ka[ch] = pad_row8<DQK, true>(B.k, hf * 32 + ql, ch, g);
 #pragma unroll
-        for (int ch = 0; ch < DV / 16; ++ch) va[ch] = lds_row8<DV>(B.v, hf * 32 + ql, ch, g);
+        for (int ch = 0; ch < DV / 16; ++ch) va[ch] = pad_row8<DV, false>(B.v, hf * 32 + ql, ch, g);
 #pragma unroll
         for (int ch = 0; ch < DQK / 16; ++ch) sacc = mfma32(ka[ch], qr[ch], sacc);
 #pragma unroll
@@ -801,7 +802,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
       for (int u = 0; u < 2; ++u) {
         bf16x8 kb[DQK / 32];
 #pragma unroll
-        for (int d = 0; d < DQK / 32; ++d) kb[d] = lds_col8<DQK>(B.k, hf * 32 + 16 * u, d * 32, lane);
+        for (int d = 0; d < DQK / 32; ++d) kb[d] = pad_col8<DQK>(B.k, hf * 32 + 16 * u, d * 32, lane);
 #pragma unroll
         for (int d = 0; d < DQK / 32; ++d) dq[d] = mfma32(dsk[u], kb[d], dq[d]);
       }

@@ -168,8 +168,8 @@ HSTU_DEV void dma_tile(uint8_t* t, const bf16* base, int64_t ld, int r0, int rli
 }
 
 // dma_tile for a PadTile: slot s = 64 i + lane of wave instruction i lands at
-// byte 16 s, i.e. row s / SPR, chunk s % SPR.  Padding slots fetch whatever
-// follows the row (or zeros past the range) and are never read.
+// byte 16 s, i.e. row s / SPR, chunk s % SPR.  Padding slots (never read) are
+// pointed past the buffer range, which returns zeros without a memory access.
 template <int D, bool TR, int R, int NW>
 HSTU_DEV void dma_pad_tile(uint8_t* t, const bf16* base, int64_t ld, int r0, int rlim, int wave,
                            int lane, int last_cols = -1) {
@@ -186,8 +186,9 @@ HSTU_DEV void dma_pad_tile(uint8_t* t, const bf16* base, int64_t ld, int r0, int
       const int sl = i * 64 + lane;
       const int row = sl / P::SPR;
       const int c = sl - row * P::SPR;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (HSTU_LDS void*)(t + i * 1024), 16,
-                                               row * (int)ld * 2 + c * 16, 0, 0, 0);
+      const int off = c < P::CPR ? row * (int)ld * 2 + c * 16 : 0x7FFFFFF0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (HSTU_LDS void*)(t + i * 1024), 16, off, 0,
+                                               0, 0);
     }
   }
 }
