@@ -146,14 +146,11 @@ hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   a.zv_col = zv;
   {
     HSTU_TIMED(TT_PREPASS, st);
-    HSTU_TRY(launch_zero_f32(drp, rab_floats(d), st));
-    HSTU_TRY(launch_zero_f32(drt, rab_floats(d), st));
-    HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st));
+    HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st, drp, drt, rab_floats(d)));
   }
   {
     HSTU_TIMED(TT_SCHED, st);
-    HSTU_TRY(launch_sched(w.kv, d->B, offs, 1, st));
-    HSTU_TRY(launch_sched(w.q, d->B, offs, 0, st));
+    HSTU_TRY(launch_sched2(w.kv, 1, w.q, 0, d->B, offs, st));
   }
   AttnArgs akv = a;
   akv.items = w.kv.items;

@@ -43,6 +43,9 @@ inline int64_t sched_capacity(int64_t T, int64_t B, int block_rows) {
 Sched carve_sched(Carver& c, int64_t T, int64_t B, int block_rows);
 hipError_t launch_sched(const Sched& s, int B, const int32_t* seq_offsets, int reverse,
                         hipStream_t st);
+// two schedules of the same sequences in one launch (one workgroup each)
+hipError_t launch_sched2(const Sched& s0, int reverse0, const Sched& s1, int reverse1, int B,
+                         const int32_t* seq_offsets, hipStream_t st);
 
 // Per-token relative timestamps and per-sequence flags.
 struct TimeMeta {
@@ -50,8 +53,10 @@ struct TimeMeta {
   int32_t* seq_flags = nullptr;  // [B] bit0: span >= 2^31 ("wide"), bit1: non-decreasing
 };
 TimeMeta carve_time(Carver& c, int64_t T, int64_t B);
+// Also clears z0[0..nz) and z1[0..nz) (the backward's rab-gradient sums) when given.
 hipError_t launch_time_prepass(const TimeMeta& tm, int B, const int32_t* seq_offsets,
-                               const int64_t* ts, hipStream_t st);
+                               const int64_t* ts, hipStream_t st, float* z0 = nullptr,
+                               float* z1 = nullptr, int64_t nz = 0);
 
 struct AttnArgs {
   const void* q = nullptr;

@@ -46,24 +46,34 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st) {
 // ---------------------------------------------------------------------------
 // Timestamp pre-pass: one workgroup per sequence.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_time_prepass(const int32_t* __restrict__ offs,
-                                                      const int64_t* __restrict__ ts,
-                                                      int32_t* __restrict__ rel_t,
-                                                      int32_t* __restrict__ flags) {
-  __shared__ int64_t smin[4], smax[4];
-  __shared__ int sunsorted[4];
+__global__ __launch_bounds__(1024) void k_time_prepass(const int32_t* __restrict__ offs,
+                                                       const int64_t* __restrict__ ts,
+                                                       int32_t* __restrict__ rel_t,
+                                                       int32_t* __restrict__ flags,
+                                                       float* __restrict__ z0,
+                                                       float* __restrict__ z1, int64_t nz) {
+  __shared__ int64_t smin[16], smax[16];
+  __shared__ int sunsorted[16];
   const int b = blockIdx.x;
+  // the backward's rab-gradient accumulators, cleared by the grid on the way
+  for (int64_t i = (int64_t)b * 1024 + threadIdx.x; i < nz; i += (int64_t)gridDim.x * 1024) {
+    z0[i] = 0.0f;
+    z1[i] = 0.0f;
+  }
   const int64_t o0 = offs[b], o1 = offs[b + 1];
   int64_t mn = INT64_MAX, mx = INT64_MIN;
   int unsorted = 0;
-  for (int64_t r = o0 + threadIdx.x; r < o1; r += 256) {
-    int64_t t = ts[r];
+  // 1024 threads, four strided loads in flight per thread: a few memory round
+  // trips per sequence rather than one per 256 tokens
+#pragma unroll 4
+  for (int64_t r = o0 + threadIdx.x; r < o1; r += 1024) {
+    const int64_t t = ts[r];
     mn = t < mn ? t : mn;
     mx = t > mx ? t : mx;
     if (r > o0 && t < ts[r - 1]) unsorted = 1;
   }
   for (int o = 32; o > 0; o >>= 1) {
-    int64_t a = __shfl_xor(mn, o, 64), c = __shfl_xor(mx, o, 64);
+    const int64_t a = __shfl_xor(mn, o, 64), c = __shfl_xor(mx, o, 64);
     mn = a < mn ? a : mn;
     mx = c > mx ? c : mx;
     unsorted |= __shfl_xor(unsorted, o, 64);
@@ -78,13 +88,14 @@ __global__ __launch_bounds__(256) void k_time_prepass(const int32_t* __restrict_
   mn = smin[0];
   mx = smax[0];
   unsorted = sunsorted[0];
-  for (int i = 1; i < 4; ++i) {
+  for (int i = 1; i < 16; ++i) {
     mn = smin[i] < mn ? smin[i] : mn;
     mx = smax[i] > mx ? smax[i] : mx;
     unsorted |= sunsorted[i];
   }
   const bool wide = (o1 > o0) && (mx - mn > HSTU_NARROW_SPAN_MAX);
-  for (int64_t r = o0 + threadIdx.x; r < o1; r += 256)
+#pragma unroll 4
+  for (int64_t r = o0 + threadIdx.x; r < o1; r += 1024)
     rel_t[r] = wide ? 0 : (int32_t)(ts[r] - mn);
   if (threadIdx.x == 0) flags[b] = (wide ? 1 : 0) | (unsorted ? 0 : 2);
 }
@@ -97,25 +108,23 @@ TimeMeta carve_time(Carver& c, int64_t T, int64_t B) {
 }
 
 hipError_t launch_time_prepass(const TimeMeta& tm, int B, const int32_t* offs,
-                               const int64_t* ts, hipStream_t st) {
-  if (B <= 0) return hipSuccess;
-  k_time_prepass<<<B, 256, 0, st>>>(offs, ts, tm.rel_t, tm.seq_flags);
+                               const int64_t* ts, hipStream_t st, float* z0, float* z1,
+                               int64_t nz) {
+  if (B <= 0) {
+    if (nz > 0) {
+      hipError_t e = launch_zero_f32(z0, nz, st);
+      if (e == hipSuccess) e = launch_zero_f32(z1, nz, st);
+      return e;
+    }
+    return hipSuccess;
+  }
+  k_time_prepass<<<B, 1024, 0, st>>>(offs, ts, tm.rel_t, tm.seq_flags, z0, z1, nz);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Work list.
 // ---------------------------------------------------------------------------
-__global__ void k_sched_count(int B, const int32_t* __restrict__ offs, int bm,
-                              int32_t* __restrict__ hist, int32_t* __restrict__ counters) {
-  int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  int n = offs[b + 1] - offs[b];
-  int nb = (n + bm - 1) / bm;
-  atomicAdd(&hist[nb], 1);
-  atomicMax(&counters[1], nb);
-}
-
 // Exclusive suffix sum of in[0..len) into out[0..len) by one workgroup of 1024.
 __device__ void block_suffix_excl(const int32_t* in, int32_t* out, int len, int32_t* total) {
   __shared__ int32_t part[1024];
@@ -143,39 +152,77 @@ __device__ void block_suffix_excl(const int32_t* in, int32_t* out, int len, int3
   __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void k_sched_levels(int32_t* __restrict__ hist,
-                                                       int32_t* __restrict__ cnt,
-                                                       int32_t* __restrict__ levelstart,
-                                                       int32_t* __restrict__ counters) {
-  const int maxblk = counters[1];
-  // cnt[m] = #sequences with more than m blocks, m in [0, maxblk]
-  block_suffix_excl(hist, cnt, maxblk + 1, nullptr);
+// One workgroup builds one schedule (the launch carries one or two): clear,
+// count sequences per block count, the two suffix sums, then the items.  The
+// steps communicate through global memory inside the workgroup, so each is
+// separated by a barrier and an agent-scope acquire (the vector L1 holds no
+// stale line of what other threads wrote or atomically updated).
+struct SchedJob {
+  int32_t* items;
+  int32_t* counters;
+  int32_t* hist;
+  int32_t* cnt;
+  int32_t* levelstart;
+  int32_t* tie;
+  int cap, bm, reverse;
+};
+
+__device__ void sched_step_barrier() {
   __syncthreads();
-  // levelstart[L] = sum of cnt[L'] for L' in (L, maxblk); n_items = sum over [0, maxblk)
-  block_suffix_excl(cnt, levelstart, maxblk, &counters[0]);
-  if (threadIdx.x == 0 && maxblk == 0) counters[0] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-__global__ __launch_bounds__(256) void k_sched_items(const int32_t* __restrict__ offs, int bm,
-                                                     int reverse,
-                                                     const int32_t* __restrict__ cnt,
-                                                     const int32_t* __restrict__ levelstart,
-                                                     int32_t* __restrict__ tie,
-                                                     int32_t* __restrict__ items) {
-  __shared__ int spos;
-  const int b = blockIdx.x;
-  const int n = offs[b + 1] - offs[b];
-  const int nb = (n + bm - 1) / bm;
-  if (nb == 0) return;
-  if (threadIdx.x == 0) spos = cnt[nb] + atomicAdd(&tie[nb], 1);
-  __syncthreads();
-  const int pos = spos;
-  for (int m = threadIdx.x; m < nb; m += 256) {
-    const int L = reverse ? (nb - 1 - m) : m;
-    const int64_t w = (int64_t)levelstart[L] + pos;
-    items[2 * w] = b;
-    items[2 * w + 1] = m;
+__global__ __launch_bounds__(1024) void k_sched(int B, const int32_t* __restrict__ offs,
+                                                SchedJob j0, SchedJob j1) {
+  const SchedJob j = blockIdx.x == 0 ? j0 : j1;
+  const int t = threadIdx.x;
+  for (int i = t; i < j.cap + 2; i += 1024) {
+    j.hist[i] = 0;
+    j.tie[i] = 0;
   }
+  if (t < 4) j.counters[t] = 0;
+  sched_step_barrier();
+  for (int b = t; b < B; b += 1024) {
+    const int n = offs[b + 1] - offs[b];
+    const int nb = (n + j.bm - 1) / j.bm;
+    atomicAdd(&j.hist[nb], 1);
+    atomicMax(&j.counters[1], nb);
+  }
+  sched_step_barrier();
+  const int maxblk = j.counters[1];
+  // cnt[m] = #sequences with more than m blocks, m in [0, maxblk]
+  block_suffix_excl(j.hist, j.cnt, maxblk + 1, nullptr);
+  sched_step_barrier();
+  // levelstart[L] = sum of cnt[L'] for L' in (L, maxblk); n_items = sum over [0, maxblk)
+  block_suffix_excl(j.cnt, j.levelstart, maxblk, &j.counters[0]);
+  if (t == 0 && maxblk == 0) j.counters[0] = 0;
+  sched_step_barrier();
+  for (int b = t; b < B; b += 1024) {
+    const int n = offs[b + 1] - offs[b];
+    const int nb = (n + j.bm - 1) / j.bm;
+    if (nb == 0) continue;
+    const int pos = j.cnt[nb] + atomicAdd(&j.tie[nb], 1);
+    for (int m = 0; m < nb; ++m) {
+      const int L = j.reverse ? (nb - 1 - m) : m;
+      const int64_t w = (int64_t)j.levelstart[L] + pos;
+      j.items[2 * w] = b;
+      j.items[2 * w + 1] = m;
+    }
+  }
+}
+
+static SchedJob sched_job(const Sched& s, int reverse) {
+  SchedJob j;
+  j.items = s.items;
+  j.counters = s.counters;
+  j.hist = s.hist;
+  j.cnt = s.cnt;
+  j.levelstart = s.levelstart;
+  j.tie = s.tie;
+  j.cap = (int)s.cap;
+  j.bm = s.block_rows;
+  j.reverse = reverse;
+  return j;
 }
 
 Sched carve_sched(Carver& c, int64_t T, int64_t B, int block_rows) {
@@ -192,15 +239,13 @@ Sched carve_sched(Carver& c, int64_t T, int64_t B, int block_rows) {
 }
 
 hipError_t launch_sched(const Sched& s, int B, const int32_t* offs, int reverse, hipStream_t st) {
-  hipError_t e;
-  if ((e = launch_zero_i32(s.counters, 4, st)) != hipSuccess) return e;
-  if ((e = launch_zero_i32(s.hist, s.cap + 2, st)) != hipSuccess) return e;
-  if ((e = launch_zero_i32(s.tie, s.cap + 2, st)) != hipSuccess) return e;
-  if (B <= 0) return hipSuccess;
-  k_sched_count<<<(B + 255) / 256, 256, 0, st>>>(B, offs, s.block_rows, s.hist, s.counters);
-  k_sched_levels<<<1, 1024, 0, st>>>(s.hist, s.cnt, s.levelstart, s.counters);
-  k_sched_items<<<B, 256, 0, st>>>(offs, s.block_rows, reverse, s.cnt, s.levelstart, s.tie,
-                                   s.items);
+  const SchedJob j = sched_job(s, reverse);
+  k_sched<<<1, 1024, 0, st>>>(B, offs, j, j);
+  return hipGetLastError();
+}
+hipError_t launch_sched2(const Sched& s0, int reverse0, const Sched& s1, int reverse1, int B,
+                         const int32_t* offs, hipStream_t st) {
+  k_sched<<<2, 1024, 0, st>>>(B, offs, sched_job(s0, reverse0), sched_job(s1, reverse1));
   return hipGetLastError();
 }
 
