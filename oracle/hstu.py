@@ -10,6 +10,8 @@ Pages cited (their text, not line numbers):
   [DLRMv4] "DLRMv4 Brings Sequence-Based Recommendation Training to MLPerf"
            (xfinit.ro), sections "Model Architecture", "HSTU Hyperparameters",
            "Computation Cost Analysis" (Tables 6 and 7).
+  [ULTRA]  Telegram summary of "Bending the Scaling Law Curve in Large-Scale
+           Recommendation Systems" (ULTRA-HSTU), item "Semi-Local Attention".
 
 What is computed (every array is float64; integer work is exact):
 
@@ -27,7 +29,11 @@ What is computed (every array is float64; integer work is exact):
        a_ij = SiLU(s_ij) / N   if allowed(i, j), else 0
        O_i  = sum_j a_ij v_j
    allowed(i, j): history row i sees history j <= i; a candidate row sees all
-   history and itself only.  p(i) = min(i, n_h); bp = min(p(i) - p(j), P-1);
+   history and itself only.  Semi-local attention ([ULTRA]: a local and a
+   global window instead of the full causal mask; window sizes not given, so
+   they are parameters W_l, W_g): when W_l > 0 a pair is also required to
+   satisfy p(i) - p(j) < W_l (the W_l most recent positions) or j < W_g (the
+   first W_g tokens of the sequence).  p(i) = min(i, n_h); bp = min(p(i) - p(j), P-1);
    dt = min(max(ts_i - ts_j, 0), 2^31 - 1); bt = min(floor(log2(dt + 1)), Tb-1).
    N = norm_len (norm_mode 0) or the sequence's own n (norm_mode 1).
 3. Gated output ([GR]: elementwise gating before the output projection;
@@ -101,15 +107,23 @@ def positions(n: int, c: int) -> np.ndarray:
     return np.minimum(np.arange(n, dtype=np.int64), n - c)
 
 
-def allowed_mask(n: int, c: int, rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Boolean [len(rows), n]: causal for history rows, history+self for candidates."""
+def allowed_mask(n: int, c: int, rows: Optional[np.ndarray] = None,
+                 win_local: int = 0, win_global: int = 0) -> np.ndarray:
+    """Boolean [len(rows), n]: causal for history rows, history+self for candidates;
+    with win_local > 0 also the semi-local window ([ULTRA] "Semi-Local Attention")."""
     n_h = n - c
     i = np.arange(n) if rows is None else np.asarray(rows)
     j = np.arange(n)
     hist_row = (i < n_h)[:, None]
     causal = j[None, :] <= i[:, None]
     cand = (j[None, :] < n_h) | (j[None, :] == i[:, None])
-    return np.where(hist_row, causal, cand)
+    M = np.where(hist_row, causal, cand)
+    if win_local > 0:
+        p = positions(n, c)
+        local = (p[i][:, None] - p[None, :]) < win_local
+        glob = (j < win_global)[None, :]
+        M = M & (local | glob)
+    return M
 
 
 def bias_buckets(ts: np.ndarray, c: int, rows: np.ndarray, n_pos: int, n_time: int):
@@ -144,7 +158,7 @@ def _rab(tab: np.ndarray, H: int) -> np.ndarray:
 
 def attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time,
              num_candidates=None, norm_mode=0, norm_len=1, row_block=1024,
-             return_rows=None):
+             return_rows=None, win_local=0, win_global=0):
     """O[T, H, d_v] of the pointwise attention (step 2 above).
 
     q, k: [T, H, d_qk]; v: [T, H, d_v]; rab_pos/rab_time: [H, P] or [P].
@@ -165,7 +179,7 @@ def attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time,
         all_rows = np.arange(n) if return_rows is None else np.asarray(return_rows[b], np.int64)
         for r0 in range(0, len(all_rows), row_block):
             rows = all_rows[r0:r0 + row_block]
-            M = allowed_mask(n, c, rows)
+            M = allowed_mask(n, c, rows, win_local, win_global)
             bp, bt = bias_buckets(ts, c, rows, rp.shape[1], rt.shape[1])
             for h in range(H):
                 s = q[o0 + rows, h, :] @ k[o0:o1, h, :].T + rp[h][bp] + rt[h][bt]
@@ -175,7 +189,8 @@ def attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time,
 
 
 def attn_bwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, d_out,
-             num_candidates=None, norm_mode=0, norm_len=1, row_block=1024):
+             num_candidates=None, norm_mode=0, norm_len=1, row_block=1024,
+             win_local=0, win_global=0):
     """(dq, dk, dv, d_rab_pos[H,P], d_rab_time[H,Tb]) for attn_fwd's output gradient."""
     q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
     dO = np.asarray(d_out, np.float64)
@@ -192,7 +207,7 @@ def attn_bwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, d_out,
         ts = np.asarray(timestamps[o0:o1], np.int64)
         for r0 in range(0, n, row_block):
             rows = np.arange(r0, min(n, r0 + row_block))
-            M = allowed_mask(n, c, rows)
+            M = allowed_mask(n, c, rows, win_local, win_global)
             bp, bt = bias_buckets(ts, c, rows, P, Tb)
             for h in range(H):
                 s = q[o0 + rows, h, :] @ k[o0:o1, h, :].T + rp[h][bp] + rt[h][bt]
@@ -252,6 +267,8 @@ class LayerFlags:
     proj_silu: bool = True
     residual: bool = True
     eps: float = 1e-6
+    win_local: int = 0     # semi-local attention windows (0: full causal)
+    win_global: int = 0
 
 
 def split_uvqk(Zh: np.ndarray, f: LayerFlags):
@@ -274,7 +291,7 @@ def layer_fwd(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candida
     Zh = silu(Z) if f.proj_silu else Z
     U, V, Q, K = split_uvqk(Zh, f)
     O = attn_fwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
-                 f.norm_mode, f.norm_len)
+                 f.norm_mode, f.norm_len, win_local=f.win_local, win_global=f.win_global)
     T = X.shape[0]
     O2 = O.reshape(T, f.H * f.d_v)
     Yn, mu, rstd, xhat = layernorm_fwd(O2, f.eps, gamma, beta)
@@ -307,7 +324,8 @@ def layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_can
     dO2, dgamma, dbeta = layernorm_bwd(dYn, saved["xhat"], saved["rstd"], gamma)
     dO = dO2.reshape(T, f.H, f.d_v)
     dQ, dK, dV, drp, drt = attn_bwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, dO,
-                                    num_candidates, f.norm_mode, f.norm_len)
+                                    num_candidates, f.norm_mode, f.norm_len,
+                                    win_local=f.win_local, win_global=f.win_global)
     dZh = np.concatenate([dU, dV.reshape(T, -1), dQ.reshape(T, -1), dK.reshape(T, -1)], axis=1)
     dZ = dZh * silu_grad(saved["Z"]) if f.proj_silu else dZh
     dW1 = X.T @ dZ

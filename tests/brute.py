@@ -28,10 +28,20 @@ def _silu_prime(s: float) -> float:
     return sg + s * sg * (1.0 - sg)
 
 
-def _pair_ok(i, j, n_h):
+def _pair_ok(i, j, n_h, win_local=0, win_global=0):
     if i < n_h:            # history token: itself and everything before it
-        return j <= i
-    return j < n_h or j == i   # candidate: whole history plus itself
+        ok = j <= i
+    else:
+        ok = j < n_h or j == i   # candidate: whole history plus itself
+    if ok and win_local > 0:
+        # semi-local: the key is one of the win_local most recent positions
+        # seen from the query, or one of the first win_global tokens
+        pi = i if i < n_h else n_h
+        pj = j if j < n_h else n_h
+        in_local = (pi - pj) < win_local
+        in_global = j < win_global
+        ok = in_local or in_global
+    return ok
 
 
 def _bias(i, j, n_h, ts, h, rp, rt):
@@ -51,7 +61,8 @@ def _bias(i, j, n_h, ts, h, rp, rt):
     return rp[h, dp] + rt[h, bt], dp, bt
 
 
-def brute_attn_fwd(q, k, v, offs, ts, rp, rt, cands, norm_mode, norm_len):
+def brute_attn_fwd(q, k, v, offs, ts, rp, rt, cands, norm_mode, norm_len, win_local=0,
+                   win_global=0):
     T, H, dqk = q.shape
     dv = v.shape[2]
     out = np.zeros((T, H, dv))
@@ -65,7 +76,7 @@ def brute_attn_fwd(q, k, v, offs, ts, rp, rt, cands, norm_mode, norm_len):
             for h in range(H):
                 acc = [0.0] * dv
                 for j in range(n):
-                    if not _pair_ok(i, j, n_h):
+                    if not _pair_ok(i, j, n_h, win_local, win_global):
                         continue
                     s = 0.0
                     for cc in range(dqk):
@@ -78,7 +89,8 @@ def brute_attn_fwd(q, k, v, offs, ts, rp, rt, cands, norm_mode, norm_len):
     return out
 
 
-def brute_attn_bwd(q, k, v, offs, ts, rp, rt, dO, cands, norm_mode, norm_len):
+def brute_attn_bwd(q, k, v, offs, ts, rp, rt, dO, cands, norm_mode, norm_len, win_local=0,
+                   win_global=0):
     """Gradients accumulated pair by pair: dV_j += a dO_i, dq_i += ds k_j, ..."""
     T, H, dqk = q.shape
     dv_ = v.shape[2]
@@ -92,7 +104,7 @@ def brute_attn_bwd(q, k, v, offs, ts, rp, rt, dO, cands, norm_mode, norm_len):
         N = norm_len if norm_mode == 0 else n
         for i in range(n):
             for j in range(n):
-                if not _pair_ok(i, j, n_h):
+                if not _pair_ok(i, j, n_h, win_local, win_global):
                     continue
                 for h in range(H):
                     s = sum(q[o0 + i, h, cc] * k[o0 + j, h, cc] for cc in range(dqk))

@@ -231,3 +231,65 @@ def test_row_blocking_does_not_change_result():
     a = orc.attn_fwd(q, k, v, offs, ts, rp, rt, [5, 0], 0, 40, row_block=1024)
     b = orc.attn_fwd(q, k, v, offs, ts, rp, rt, [5, 0], 0, 40, row_block=7)
     np.testing.assert_allclose(a, b, rtol=1e-14, atol=1e-16)
+
+
+# ----------------------------------------------------------------------------
+# Semi-local attention ([ULTRA] "Semi-Local Attention": a local and a global
+# window instead of the full causal mask; the window sizes are parameters)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cands", [None, [0, 3, 2]])
+@pytest.mark.parametrize("wl,wg", [(1, 0), (3, 0), (2, 2), (4, 1), (6, 3)])
+def test_semilocal_matches_brute_force(cands, wl, wg):
+    rng = np.random.default_rng(21)
+    lengths = [7, 9, 6]
+    q, k, v, offs, ts, rp, rt = _rand_case(rng, lengths, cands=cands, scale=0.7, gap=3.0)
+    got = orc.attn_fwd(q, k, v, offs, ts, rp, rt, cands, 0, 11, win_local=wl, win_global=wg)
+    want = brute_attn_fwd(q, k, v, offs, ts, rp, rt, cands, 0, 11, win_local=wl, win_global=wg)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_semilocal_window_covering_the_sequence_is_full_causal():
+    rng = np.random.default_rng(22)
+    lengths = [9, 13]
+    cands = [0, 4]
+    q, k, v, offs, ts, rp, rt = _rand_case(rng, lengths, cands=cands, gap=5.0)
+    full = orc.attn_fwd(q, k, v, offs, ts, rp, rt, cands, 0, 16)
+    for wl, wg in [(13, 0), (40, 0), (13, 5)]:
+        got = orc.attn_fwd(q, k, v, offs, ts, rp, rt, cands, 0, 16, win_local=wl,
+                           win_global=wg)
+        assert np.array_equal(got, full)
+
+
+def test_semilocal_self_only_closed_form():
+    # W_l = 1, W_g = 0: every token attends to itself only
+    rng = np.random.default_rng(23)
+    q, k, v, offs, ts, rp, rt = _rand_case(rng, [6], H=2, dqk=3, dv=4)
+    got = orc.attn_fwd(q, k, v, offs, ts, rp, rt, None, 0, 5, win_local=1)
+    for i in range(6):
+        for h in range(2):
+            s = float(q[i, h] @ k[i, h]) + rp[h, 0] + rt[h, 0]
+            w = s / (1.0 + math.exp(-s)) / 5
+            np.testing.assert_allclose(got[i, h], w * v[i, h], rtol=1e-12, atol=1e-15)
+
+
+def test_semilocal_keys_outside_both_windows_do_not_matter():
+    rng = np.random.default_rng(24)
+    n, wl, wg = 20, 4, 3
+    q, k, v, offs, ts, rp, rt = _rand_case(rng, [n], H=1, dqk=4, dv=3)
+    base = orc.attn_fwd(q, k, v, offs, ts, rp, rt, None, 0, 8, win_local=wl, win_global=wg)
+    i = 15
+    outside = [j for j in range(n) if j <= i and not (i - j < wl or j < wg)]
+    assert outside == list(range(3, 12))
+    k2, v2 = k.copy(), v.copy()
+    k2[outside] += 5.0
+    v2[outside] *= -3.0
+    pert = orc.attn_fwd(q, k2, v2, offs, ts, rp, rt, None, 0, 8, win_local=wl, win_global=wg)
+    np.testing.assert_array_equal(pert[i], base[i])
+    # rows 12.. have some of those keys in their local window
+    assert not np.allclose(pert[12:i], base[12:i])
+    # and a key inside the global window does matter to the last row
+    k3 = k.copy()
+    k3[1] += 5.0
+    pert3 = orc.attn_fwd(q, k3, v, offs, ts, rp, rt, None, 0, 8, win_local=wl, win_global=wg)
+    assert not np.allclose(pert3[n - 1], base[n - 1])

@@ -161,3 +161,20 @@ def test_stack_feeds_outputs_forward():
     y2, _ = orc.layer_fwd(y1, W1 * 0.5, W2 * 2, rt, rp, offs, ts, None, f)
     np.testing.assert_array_equal(outs[0], y1)
     np.testing.assert_array_equal(outs[1], y2)
+
+
+@pytest.mark.parametrize("wl,wg", [(2, 0), (3, 2)])
+def test_semilocal_attn_bwd_matches_pairwise_loops(wl, wg):
+    rng = np.random.default_rng(14)
+    offs = np.array([0, 6, 11])
+    cands = [2, 0]
+    q = rng.standard_normal((11, 2, 3)); k = rng.standard_normal((11, 2, 3))
+    v = rng.standard_normal((11, 2, 2)); dO = rng.standard_normal((11, 2, 2))
+    ts = np.array([0, 3, 9, 20, 20, 20, 100, 250, 1000, 1100, 4000], dtype=np.int64)
+    rp = rng.standard_normal((2, 128)); rt = rng.standard_normal((2, 128))
+    got = orc.attn_bwd(q, k, v, offs, ts, rp, rt, dO, cands, 0, 6, win_local=wl,
+                       win_global=wg)
+    want = brute_attn_bwd(q, k, v, offs, ts, rp, rt, dO, cands, 0, 6, win_local=wl,
+                          win_global=wg)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-11, atol=1e-13)
