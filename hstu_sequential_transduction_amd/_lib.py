@@ -34,7 +34,8 @@ class AttnDesc(C.Structure):
                 ("d_v", C.c_int32), ("n_pos_buckets", C.c_int32),
                 ("n_time_buckets", C.c_int32), ("norm_mode", C.c_int32),
                 ("norm_len", C.c_int32), ("dtype", C.c_int32),
-                ("rab_head_stride", C.c_int64)]
+                ("rab_head_stride", C.c_int64), ("win_local", C.c_int32),
+                ("win_global", C.c_int32)]
 
 
 class LayerDesc(C.Structure):

@@ -45,11 +45,14 @@ class AttnConfig:
     norm_mode: int = 0
     n_pos_buckets: int = 128
     n_time_buckets: int = 128
+    win_local: int = 0    # semi-local attention windows (0: full causal)
+    win_global: int = 0
 
 
 def attn_desc(cfg: AttnConfig, B: int, T: int, dtype: torch.dtype, rab_stride: int) -> AttnDesc:
     return AttnDesc(B, T, cfg.H, cfg.d_qk, cfg.d_v, cfg.n_pos_buckets, cfg.n_time_buckets,
-                    cfg.norm_mode, cfg.norm_len, _DT[dtype], rab_stride)
+                    cfg.norm_mode, cfg.norm_len, _DT[dtype], rab_stride, cfg.win_local,
+                    cfg.win_global)
 
 
 def _rab_stride(rab_pos: torch.Tensor, rab_time: torch.Tensor) -> int:

@@ -34,6 +34,7 @@ hstu_status check_attn_desc(const hstu_attn_desc* d) {
   if (d->n_time_buckets < 1 || d->n_time_buckets > 1024) return HSTU_ERR_UNSUPPORTED;
   if (d->norm_mode != 0 && d->norm_mode != 1) return HSTU_ERR_INVALID_ARG;
   if (d->norm_mode == 0 && d->norm_len <= 0) return HSTU_ERR_INVALID_ARG;
+  if (d->win_local < 0 || d->win_global < 0) return HSTU_ERR_INVALID_ARG;
   if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
   if (d->rab_head_stride < 0) return HSTU_ERR_INVALID_ARG;
   if (d->rab_head_stride != 0 &&
@@ -95,6 +96,8 @@ AttnArgs base_args(const hstu_attn_desc* d, const void* q, const void* k, int64_
   a.nT = d->n_time_buckets;
   a.norm_mode = d->norm_mode;
   a.norm_len = d->norm_len;
+  a.win_local = d->win_local;
+  a.win_global = d->win_local > 0 ? d->win_global : 0;
   return a;
 }
 

@@ -155,7 +155,7 @@ struct KvTables {
   float gtime[32];    // d rab_time histogram (by clz index)
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool WIN>
 __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) void k_attn_bwd_dkdv(AttnArgs a) {
   constexpr bool WIDE = KvShape<DQK, DV>::WIDE;
   constexpr int NW = KvShape<DQK, DV>::NW, NT = KvShape<DQK, DV>::NT;
@@ -273,6 +273,23 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
     const int need = k1 - 1 + nP - 1;  // first row with p(i) - p(k1-1) >= nP-1
     if (need <= nh) far_start = min(qend, k0 + ((max(need - k0, 0) + KV_QT - 1) / KV_QT) * KV_QT);
   }
+  // Semi-local windows (history key j is seen by row i only if p(i) - j < W_l
+  // or j < W_g): rows past the window of every key of the block see none of
+  // it (unless some key is global or within W_l of the candidates' position),
+  // and the far phase keeps only whole tiles whose rows see every key of the
+  // block; the rows after it up to qend_w run the masked near body again.
+  // WIN: semi-local windows compiled in (otherwise every window term folds away)
+  const int wl = WIN ? a.win_local : 0, wg = WIN ? a.win_global : 0;
+  int qend_w = qend, fw_end = qend;
+  if (wl > 0 && k1 > wg && k1 <= nh) {
+    if (k0 >= wg && nh - (k1 - 1) >= wl) qend_w = min(qend, k1 - 1 + wl);
+    const int jng = max(k0, wg);  // smallest key subject to the local window
+    fw_end = far_start + max((jng + wl - far_start) / KV_QT, 0) * KV_QT;
+    fw_end = min(max(fw_end, far_start), qend_w);
+  }
+  // last row that sees this lane's key: past its local window, unless the key
+  // is global or within W_l of the candidates' position
+  const int wrow = (wl > 0 && jk >= wg && jk < nh && nh - jk >= wl) ? jk + wl - 1 : (1 << 30);
 
   // per-lane running sums of the far phase (position bucket nP-1): run_u holds
   // rows of time bucket curB from halves where no lane changes bucket; run_tot
@@ -443,6 +460,8 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       if (kw0 < nh) active = ir1 - 1 >= kw0;
       else active = ir0 < kw1 && ir1 > kw0;
       if (!active || ir0 >= ir1) return;
+      // window: every row of the half past the window of every key of the wave
+      if (wl > 0 && kw0 >= wg && kw1 <= nh && nh - (kw1 - 1) >= wl && ir0 >= kw1 - 1 + wl) return;
       f32x16 sacc, dacc;
       // keep the element loop's address arithmetic out of the product block,
       // which needs the registers for operand read-ahead
@@ -456,7 +475,9 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       const int pd0 = ib - pJ, pdmax = nh - pJ;
       const int d0 = jk - ib;
       const int lo = kvalid ? d0 : 1 << 20;
-      const int hi = min(jk < nh ? (1 << 20) : d0, qend - 1 - ib);
+      // window: rows past the key's local window, unless the key is global or
+      // within W_l of the candidates' position (then every row may see it)
+      const int hi = min(min(jk < nh ? (1 << 20) : d0, qend - 1 - ib), wrow - ib);
       auto bidx = [&](int kc) HSTU_INLINE_LAMBDA { return min(max(min(pd0 + kc, pdmax), 0), nP - 1); };
       // history keys and rows (or masked rows): the bucket depends on i - j only
       const bool diag = k1 <= nh && min(ir0 + 32, qend) <= nh;
@@ -539,30 +560,36 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
     });
   };
 
-  // double-buffered tile pipeline over [ibeg, iend) in steps of KV_QT: the DMA
-  // of tile t+1 runs while tile t is computed
-  // (unrolled by two so that every access names its buffer statically)
-  auto run_phase = [&](int ibeg, int iend, auto body) HSTU_INLINE_LAMBDA {
+  // double-buffered tile pipeline over [ibeg, iend) in steps of KV_QT, jumping
+  // from tile sk0 to tile sk1: the DMA of tile t+1 runs while tile t is
+  // computed (unrolled by two so that every access names its buffer statically)
+  auto run_phase = [&](int ibeg, int iend, auto body, int sk0, int sk1) HSTU_INLINE_LAMBDA {
     if (ibeg >= iend) return;
+    auto next_row = [&](int i) HSTU_INLINE_LAMBDA {
+      i += KV_QT;
+      return (i >= sk0 && i < sk1) ? sk1 : i;
+    };
     issue(kvb0, ibeg);
     dma_wait();
     __syncthreads();
-    for (int i0 = ibeg; i0 < iend; i0 += 2 * KV_QT) {
-      const int i1 = i0 + KV_QT;
+    for (int i0 = ibeg; i0 < iend;) {
+      const int i1 = next_row(i0);
       if (i1 < iend) issue(kvb1, i1);
       body(kvb0, i0);
       dma_wait();
       __syncthreads();
       if (i1 >= iend) break;
-      if (i1 + KV_QT < iend) issue(kvb0, i1 + KV_QT);
+      const int i2 = next_row(i1);
+      if (i2 < iend) issue(kvb0, i2);
       body(kvb1, i1);
       dma_wait();
       __syncthreads();
+      i0 = i2;
     }
   };
-  run_phase(k0, far_start, near_tile);
+  run_phase(k0, qend_w, near_tile, far_start, fw_end);
   if (nb_acc != 0.0f) atomicAdd(&sm.gtime[nb_cur], nb_acc);
-  run_phase(far_start, qend, far_tile);
+  run_phase(far_start, fw_end, far_tile, 0, 0);
   flush_time();
   if (ptot != 0.0f) atomicAdd(&sm.gpos[nP - 1], ptot);
 
@@ -640,7 +667,7 @@ struct DqTables {
   float tfar[32];
 };
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool WIN>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) DqBuf<DQK, DV> dqb0;
   __shared__ __attribute__((aligned(1024))) DqBuf<DQK, DV> dqb1;
@@ -704,11 +731,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
   for (int d = 0; d < DQK / 32; ++d) dq[d] = f32x16{};
 
   const int ktiles = (rb1 + DQ_BN - 1) / DQ_BN;
-  auto skip = [&](int kt) HSTU_INLINE_LAMBDA {
+  // semi-local windows: history key j is allowed for row i only if
+  // j >= p(i) - W_l + 1 or j < W_g; tiles past the global window and below
+  // the band of every row of the workgroup hold no allowed pair
+  // WIN: semi-local windows compiled in (otherwise every window term folds away)
+  const int wl = WIN ? a.win_local : 0, wg = WIN ? a.win_global : 0;
+  const int gtiles = (wg + DQ_BN - 1) / DQ_BN;
+  const int btile = (wl > 0 ? max(min(rb0, nh) - wl + 1, 0) : 0) / DQ_BN;
+  auto first_from = [&](int kt) HSTU_INLINE_LAMBDA {
+    if (wl > 0 && kt >= gtiles && kt < btile) kt = btile;
     const int j0 = kt * DQ_BN;
-    return j0 >= nh && j0 + DQ_BN <= rb0;
+    if (j0 >= nh && j0 + DQ_BN <= rb0) kt = rb0 / DQ_BN;  // only other candidates' keys
+    return kt;
   };
-  auto next_tile = [&](int kt) HSTU_INLINE_LAMBDA { return skip(kt + 1) ? rb0 / DQ_BN : kt + 1; };
+  auto next_tile = [&](int kt) HSTU_INLINE_LAMBDA { return first_from(kt + 1); };
 
   // DMA of key tile kt; keys >= n arrive as zeros
   auto issue = [&](DqBuf<DQK, DV>& Bf, int kt) HSTU_INLINE_LAMBDA {
@@ -726,11 +762,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
     const int j1 = min(j0 + DQ_BN, n);
     const bool hist_rows = r0 < nh;
     const bool cand_rows = rw1 > nh;
-    const bool active = (r0 < rw1) &&
+    const int band_lo = wl > 0 ? min(r0, nh) - wl + 1 : 0;
+    const int band_hi = wl > 0 ? min(rw1 - 1, nh) - wl + 1 : 0;
+    const bool win_out = wl > 0 && j0 >= wg && j1 - 1 < band_lo && j1 <= nh;
+    const bool active = (r0 < rw1) && !win_out &&
                         ((hist_rows && j0 <= min(rw1, nh) - 1) ||
                          (cand_rows && (j0 < nh || (j0 < rw1 && j1 > max(r0, nh)))));
     if (!active) return;
-    const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh);
+    const bool win_mask = wl > 0 && j1 > wg && j0 < band_hi;
+    const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh) || win_mask;
     const bool far = !need_mask && !wide && (min(r0, nh) - min(j1 - 1, nh) >= nP - 1);
     int mode = 3;  // 0 constant per row, 1 one threshold, 2 gather, 3 general
     int cF = 0, cL = 0;
@@ -743,6 +783,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
     const int32_t thr = (cL == cF) ? INT32_MAX : ti1 - (1 << (31 - cF));
     const int dI = pI - j0 - 4 * g, pmin = pI - nh;
     const int lim = (iq < nh ? iq : nh - 1) - j0 - 4 * g, slf = iq - j0 - 4 * g;
+    // window: keys >= wlo (local band) or < wgl (global window) pass
+    const int wlo = (wl > 0 ? pI - wl + 1 : INT32_MIN / 2) - j0 - 4 * g;
+    const int wgl = wg - j0 - 4 * g;
 
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
@@ -771,8 +814,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
             float sig, p;
             silu_parts(sb, sig, p);
             float ds = dacc[4 * aa + r] * silu_deriv(sig, p);
-            if constexpr (decltype(masked)::value)
-              ds = (kc <= lim || kc == slf) ? ds : 0.0f;
+            if constexpr (decltype(masked)::value) {
+              bool ok = kc <= lim || kc == slf;
+              if constexpr (WIN) ok = ok && (kc >= wlo || kc < wgl);
+              ds = ok ? ds : 0.0f;
+            }
             dsk[aa >> 1][(aa & 1) * 4 + r] = (bf16)ds;
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -811,8 +857,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
 
   // double-buffered key-tile pipeline, unrolled by two so that every access
   // names its buffer statically
-  int kt = 0;
-  if (kt < ktiles && skip(kt)) kt = rb0 / DQ_BN;
+  int kt = first_from(0);
   if (kt < ktiles) issue(dqb0, kt);
   dma_wait();
   __syncthreads();
@@ -841,14 +886,16 @@ template <int DQK, int DV>
 hipError_t launch_kv_t(const AttnArgs& a, int64_t mi, hipStream_t st) {
   const int64_t grid = mi * a.H;
   if (grid <= 0) return hipSuccess;
-  k_attn_bwd_dkdv<DQK, DV><<<(unsigned)grid, KvShape<DQK, DV>::NT, 0, st>>>(a);
+  if (a.win_local > 0) k_attn_bwd_dkdv<DQK, DV, true><<<(unsigned)grid, KvShape<DQK, DV>::NT, 0, st>>>(a);
+  else k_attn_bwd_dkdv<DQK, DV, false><<<(unsigned)grid, KvShape<DQK, DV>::NT, 0, st>>>(a);
   return hipGetLastError();
 }
 template <int DQK, int DV>
 hipError_t launch_dq_t(const AttnArgs& a, int64_t mi, hipStream_t st) {
   const int64_t grid = mi * a.H;
   if (grid <= 0) return hipSuccess;
-  k_attn_bwd_dq<DQK, DV><<<(unsigned)grid, 256, 0, st>>>(a);
+  if (a.win_local > 0) k_attn_bwd_dq<DQK, DV, true><<<(unsigned)grid, 256, 0, st>>>(a);
+  else k_attn_bwd_dq<DQK, DV, false><<<(unsigned)grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ struct FwdTables {
 template <bool V>
 using bconst = std::integral_constant<bool, V>;
 
-template <int DQK, int DV>
+template <int DQK, int DV, bool WIN>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
   constexpr int QG = FwdShape<DQK, DV>::QG;
   constexpr int BM = FwdShape<DQK, DV>::BM;
@@ -133,10 +133,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d) oacc[qg][d] = f32x16{};
 
+  // Semi-local windows: history key j is allowed for row i only if
+  // j >= p(i) - W_l + 1 or j < W_g.  Key tiles past the global window and
+  // below the band of every row of the workgroup hold no allowed pair.
+  // WIN: semi-local windows compiled in (otherwise every window term folds away)
+  const int wl = WIN ? a.win_local : 0, wg = WIN ? a.win_global : 0;
+  const int band_wg = wl > 0 ? max(min(rb0, nh) - wl + 1, 0) : 0;  // lowest band key of the WG
+  const int gtiles = (wg + FWD_BN - 1) / FWD_BN;                     // tiles touching [0, W_g)
+  const int btile = band_wg / FWD_BN;
+  auto skip_window = [&](int kt) HSTU_INLINE_LAMBDA {
+    return (wl > 0 && kt >= gtiles && kt < btile) ? btile : kt;
+  };
+
   // key tiles: 0 .. ktiles-1, skipping tiles that hold only other candidates' keys
   const int ktiles = (rb1 + FWD_BN - 1) / FWD_BN;
   auto next_tile = [&](int kt) HSTU_INLINE_LAMBDA {
-    const int nk = kt + 1;
+    const int nk = skip_window(kt + 1);
     const int j0 = nk * FWD_BN;
     if (j0 >= nh && j0 + FWD_BN <= rb0) return rb0 / FWD_BN;
     return nk;
@@ -158,11 +170,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
     const int j1 = min(j0 + FWD_BN, n);
     const bool hist_rows = r0 < nh;
     const bool cand_rows = rw1 > nh;
-    const bool active = (r0 < rw1) &&
+    // window: lowest band key of the wave's first and last rows
+    const int band_lo = wl > 0 ? min(r0, nh) - wl + 1 : 0;
+    const int band_hi = wl > 0 ? min(rw1 - 1, nh) - wl + 1 : 0;
+    const bool win_out = wl > 0 && j0 >= wg && j1 - 1 < band_lo && j1 <= nh;
+    const bool active = (r0 < rw1) && !win_out &&
                         ((hist_rows && j0 <= min(rw1, nh) - 1) ||
                          (cand_rows && (j0 < nh || (j0 < rw1 && j1 > max(r0, nh)))));
     if (active) {
-      const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh);
+      const bool win_mask = wl > 0 && j1 > wg && j0 < band_hi;
+      const bool need_mask = (hist_rows && j1 - 1 > r0) || (j1 > nh) || win_mask;
       const bool far = !need_mask && !wide && (min(r0, nh) - min(j1 - 1, nh) >= nP - 1);
 
       // tile class (wave-uniform): far tiles have position bucket nP-1 everywhere; with
@@ -193,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
       }
 
       // per-lane constants of the general path, shifted by 4g (see silu_half)
-      int dI[QG], pmin[QG], lim[QG], slf[QG];
+      int dI[QG], pmin[QG], lim[QG], slf[QG], wlo[QG], wgl[QG];
 #pragma unroll
       for (int qg = 0; qg < QG; ++qg) {
         const int i = iq[qg];
@@ -201,6 +218,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
         pmin[qg] = pI[qg] - nh;                   // p(i) - n_h (candidate keys)
         lim[qg] = (i < nh ? i : nh - 1) - j0 - 4 * g;  // last allowed key of the causal part
         slf[qg] = i - j0 - 4 * g;                 // the row's own key (candidates)
+        // window: keys >= wlo (local band) or < wgl (global window) pass
+        wlo[qg] = (wl > 0 ? pI[qg] - wl + 1 : INT32_MIN / 2) - j0 - 4 * g;
+        wgl[qg] = wg - j0 - 4 * g;
       }
 
 #pragma unroll
@@ -236,8 +256,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
                 const float sb =
                     fmaf(sacc[qg][4 * aa + r], HSTU_NEG_LOG2E, bias_of(qg, kc, tj[r]));
                 float p = sb * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sb));
-                if constexpr (decltype(masked)::value)
-                  p = (kc <= lim[qg] || kc == slf[qg]) ? p : 0.0f;
+                if constexpr (decltype(masked)::value) {
+                  bool ok = kc <= lim[qg] || kc == slf[qg];
+                  if constexpr (WIN) ok = ok && (kc >= wlo[qg] || kc < wgl[qg]);
+                  p = ok ? p : 0.0f;
+                }
                 pk[qg][aa >> 1][(aa & 1) * 4 + r] = (bf16)p;
               }
               // keep the scheduler from hoisting every gather of the half at once
@@ -287,7 +310,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
   // double-buffered key-tile pipeline, unrolled by two so that every access
   // names its buffer statically (the DMA into one buffer then needs no wait
   // before reads of the other)
-  int kt = 0;
+  int kt = skip_window(0);
   if (kt < ktiles && kt * FWD_BN >= nh && kt * FWD_BN + FWD_BN <= rb0) kt = rb0 / FWD_BN;
   if (kt < ktiles) issue(fwb0, kt);
   dma_wait();
@@ -407,7 +430,8 @@ __global__ __launch_bounds__(256) void k_attn_fwd_f32(AttnArgs a) {
       for (int cc = 0; cc < QC; ++cc) dot = fmaf(q[cc], sk[jj][part * QC + cc], dot);
       dot += __shfl_xor(dot, 1, 64);
       dot += __shfl_xor(dot, 2, 64);
-      const bool ok = (j < n) && ((iq < nh) ? (j <= iq) : (j < nh || j == iq));
+      const bool ok = (j < n) && ((iq < nh) ? (j <= iq) : (j < nh || j == iq)) &&
+                      (a.win_local <= 0 || j >= nh || pI - j < a.win_local || j < a.win_global);
       const int bpv = pbucket(pI, min(j, nh), a.nP);
       const int cl = wide ? tclz_wide(ti64, st64[jj]) : tclz_narrow(ti1, st[jj]);
       const float s = dot + spos[bpv] + stime[cl];
@@ -430,7 +454,8 @@ hipError_t launch_fwd_t(const AttnArgs& a, int dtype, int64_t max_items, hipStre
   const int64_t grid = max_items * a.H;
   if (grid <= 0) return hipSuccess;
   if (dtype == HSTU_BF16)
-    k_attn_fwd_bf16<DQK, DV><<<(unsigned)grid, 256, 0, st>>>(a);
+    if (a.win_local > 0) k_attn_fwd_bf16<DQK, DV, true><<<(unsigned)grid, 256, 0, st>>>(a);
+    else k_attn_fwd_bf16<DQK, DV, false><<<(unsigned)grid, 256, 0, st>>>(a);
   else
     k_attn_fwd_f32<DQK, DV><<<(unsigned)grid, 256, 0, st>>>(a);
   return hipGetLastError();

@@ -77,6 +77,8 @@ struct AttnArgs {
   const float* rab_time = nullptr;
   int64_t rab_stride = 0;
   int H = 0, nP = 0, nT = 0, norm_mode = 0, norm_len = 1;
+  // semi-local windows (win_local 0: full causal)
+  int win_local = 0, win_global = 0;
   // backward
   const void* dout = nullptr;
   int64_t ld_dout = 0;

@@ -92,6 +92,15 @@ typedef struct {
   int32_t norm_len;        /* N for norm_mode 0 (> 0) */
   int32_t dtype;           /* hstu_dtype */
   int64_t rab_head_stride; /* floats between heads' tables; 0 = shared */
+  /* Semi-local attention ("Bending the Scaling Law Curve in Large-Scale
+   * Recommendation Systems", Semi-Local Attention: a local and a global window
+   * instead of the full causal mask).  win_local > 0 additionally requires of
+   * every allowed pair p(i) - p(j) < win_local (the win_local most recent
+   * positions, the token itself included) or j < win_global (the first
+   * win_global tokens of the sequence).  win_local = 0: full causal /
+   * target-aware attention (win_global is then ignored).  Both >= 0. */
+  int32_t win_local;
+  int32_t win_global;
 } hstu_attn_desc;
 
 /* One layer: attention options plus model width and layer flags. */

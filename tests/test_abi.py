@@ -44,7 +44,8 @@ def test_version_and_status_strings(L):
 
 def _desc(**kw):
     base = dict(B=4, T=300, H=2, d_qk=32, d_v=32, n_pos_buckets=128, n_time_buckets=128,
-                norm_mode=0, norm_len=128, dtype=1, rab_head_stride=128)
+                norm_mode=0, norm_len=128, dtype=1, rab_head_stride=128, win_local=0,
+                win_global=0)
     base.update(kw)
     return _lib.AttnDesc(*[base[f] for f, _ in _lib.AttnDesc._fields_])
 
@@ -109,3 +110,46 @@ def test_fp32_backward_is_reported_unsupported(L):
 def test_schedule_capacity_bound(L):
     # sum_b ceil(n_b / BM) <= (T + B*(BM-1)) / BM
     assert L.hstu_schedule_capacity(1000, 10, 128) >= (1000 + 10 * 127) // 128
+
+
+def test_descriptor_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors have the sizes and field offsets the C compiler gives
+    the structs of include/hstu.h (a C program built here prints them)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc") or shutil.which("cc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    structs = {"hstu_attn_desc": _lib.AttnDesc, "hstu_layer_desc": _lib.LayerDesc,
+               "hstu_layer_weights": _lib.LayerWeights}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hstu.h"', "int main(void) {"]
+    for cname, ct in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in ct._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("  return 0;\n}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([gcc, "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line.strip():
+            a, b, c = line.split()
+            got[(a, b)] = int(c)
+    for cname, ct in structs.items():
+        assert got[(cname, "size")] == C.sizeof(ct), cname
+        for fname, _ in ct._fields_:
+            assert got[(cname, fname)] == getattr(ct, fname).offset, (cname, fname)
+
+
+def test_negative_windows_rejected(L):
+    buf = C.create_string_buffer(1 << 16)
+    ws = C.c_void_p((C.addressof(buf) + 255) & ~255)
+    p = C.c_void_p(1 << 20)
+    for wl, wg in ((-1, 0), (4, -2)):
+        d = _desc(win_local=wl, win_global=wg)
+        st = L.hstu_attn_fwd(C.byref(d), p, p, 64, p, 64, p, p, p, p, None, p, 64, ws, 1 << 15,
+                             None)
+        assert st == -1
