@@ -97,7 +97,7 @@ def upload_layer(inp, cfg, li=0):
         rp=torch.from_numpy(w.rab_pos).cuda(), rt=torch.from_numpy(w.rab_time).cuda())
 
 
-def bench_train(args, timer):
+def bench_train(args, timer, window=(0, 0)):
     import numpy as np
     import torch
 
@@ -114,7 +114,8 @@ def bench_train(args, timer):
     offs = torch.from_numpy(inp.seq_offsets.astype(np.int32)).cuda()
     ts = torch.from_numpy(inp.timestamps).cuda()
     w = upload_layer(inp, cfg)
-    ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len)
+    ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len,
+                      win_local=window[0], win_global=window[1])
     lc = B.LayerConfig(D=cfg.D, attn=ac)
     saved = B.Saved(T, lc, td, "cuda")
     y = torch.empty_like(X)
@@ -146,8 +147,33 @@ def bench_train(args, timer):
     ms = e0.elapsed_time(e1) / max(args.steps, 1)
     kern = timer.read()
     timer.enable(0)
-    lf = flops.layer_flops(inp.lengths, None, cfg.D, cfg.H, cfg.d_qk, cfg.d_v, backward=True)
+    lf = flops.layer_flops(inp.lengths, None, cfg.D, cfg.H, cfg.d_qk, cfg.d_v, backward=True,
+                           window=window if window[0] > 0 else None)
     return cfg, inp, ms, kern, lf
+
+
+# Semi-local attention windows of the extra training-step measurement: the
+# pages give no sizes, so these are chosen parameters (a local window of 1024
+# positions and the first 128 tokens), stated with the result.
+SEMILOCAL_WINDOW = (1024, 128)
+
+
+def bench_semilocal(args, timer, full_ms):
+    """The same training step with semi-local attention; TFLOP/s on the
+    windowed work (exact pair count), and the speedup over full causal."""
+    from hstu_sequential_transduction_amd import flops
+    cfg, inp, ms, kern, lf = bench_train(args, timer, window=SEMILOCAL_WINDOW)
+    full_pairs = flops.attn_pairs_window(inp.lengths, None, 0, 0)
+    win_pairs = flops.attn_pairs_window(inp.lengths, None, *SEMILOCAL_WINDOW)
+    out = {"win_local": SEMILOCAL_WINDOW[0], "win_global": SEMILOCAL_WINDOW[1],
+           "ms_per_step": round(ms, 4), "tflops": round(lf["total"] / (ms * 1e-3) / 1e12, 2),
+           "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
+           "attn_pairs_frac": round(win_pairs / full_pairs, 4),
+           "speedup_vs_full_causal": round(full_ms / ms, 3),
+           "kernel_ms_per_launch": {k: round(v[1] / v[0], 4) for k, v in kern.items()}}
+    log(f"semi-local step (W_l={SEMILOCAL_WINDOW[0]}, W_g={SEMILOCAL_WINDOW[1]}): "
+        f"{ms:.3f} ms, x{full_ms / ms:.2f} vs full causal")
+    return out
 
 
 def roofline(cfg, inp, kern, steps, traffic_dir):
@@ -285,7 +311,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the forward-only workloads")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the forward-only workloads and the semi-local training step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
@@ -303,6 +330,7 @@ def main():
     log(f"train step: {ms:.3f} ms, {tflops:.1f} TFLOP/s")
     roof, table = roofline(cfg, inp, kern, args.steps, os.path.join(ROOT, "profiles"))
     extra = None if args.no_extra else bench_fwd_configs(timer)
+    semi = None if args.no_extra else bench_semilocal(args, timer, ms)
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, inp)
     line = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -320,6 +348,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "forward_workloads": extra,
+        "semilocal": semi,
     }
     print(json.dumps(line), flush=True)
 

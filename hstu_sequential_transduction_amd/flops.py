@@ -44,18 +44,55 @@ def attn_pairs(lengths: Sequence[int], num_candidates: Optional[Sequence[int]] =
     return float((nh ** 2 / 2 + c * nh + c).sum())
 
 
+def _tri_min(K: int, cap: int) -> int:
+    """sum_{t=1..K} min(t, cap) for K >= 0."""
+    if K <= 0:
+        return 0
+    if K <= cap:
+        return K * (K + 1) // 2
+    return cap * (cap + 1) // 2 + (K - cap) * cap
+
+
+def attn_pairs_window(lengths: Sequence[int], num_candidates: Optional[Sequence[int]],
+                      win_local: int, win_global: int) -> float:
+    """Exact allowed query-key pairs per head under semi-local attention (a local
+    window of win_local positions and the first win_global tokens; "Bending the
+    Scaling Law Curve in Large-Scale Recommendation Systems", Semi-Local
+    Attention).  With win_local = 0 (no window) the exact causal count."""
+    total = 0
+    cands = [0] * len(lengths) if num_candidates is None else list(num_candidates)
+    for n, c in zip(lengths, cands):
+        n, c = int(n), int(c)
+        nh = n - c
+        if win_local <= 0:
+            total += nh * (nh + 1) // 2 + c * (nh + 1)
+            continue
+        # history row i: local keys min(i+1, W_l); global keys below the band
+        # min(W_g, max(0, i - W_l + 1))
+        total += _tri_min(nh, win_local) + _tri_min(nh - win_local, win_global)
+        # candidate row: history keys within W_l of position n_h, global keys
+        # below them, and itself
+        band = max(0, nh - win_local + 1)
+        total += c * ((nh - band) + min(win_global, band) + 1)
+    return float(total)
+
+
 def attn_fwd_flops(lengths, num_candidates, H: int, d_qk: int, d_v: int) -> float:
     return 2.0 * attn_pairs(lengths, num_candidates) * H * (d_qk + d_v)
 
 
 def layer_flops(lengths, num_candidates, D: int, H: int, d_qk: int, d_v: int,
-                backward: bool) -> Dict[str, float]:
-    """Algorithmic FLOPs of one layer over a jagged batch (fwd, or fwd+bwd)."""
+                backward: bool, window=None) -> Dict[str, float]:
+    """Algorithmic FLOPs of one layer over a jagged batch (fwd, or fwd+bwd);
+    window = (win_local, win_global) counts the semi-local pairs exactly."""
     T = float(np.sum(lengths))
     w = 3.0 if backward else 1.0
     uvqk = w * 2 * T * D * H * (2 * d_qk + 2 * d_v)
     outp = w * 2 * T * H * d_v * D
-    af = attn_fwd_flops(lengths, num_candidates, H, d_qk, d_v)
+    if window is not None and window[0] > 0:
+        af = 2.0 * attn_pairs_window(lengths, num_candidates, window[0], window[1]) * H * (d_qk + d_v)
+    else:
+        af = attn_fwd_flops(lengths, num_candidates, H, d_qk, d_v)
     attn = 3.5 * af if backward else af
     return {"uvqk": uvqk, "outproj": outp, "attn": attn, "attn_fwd": af,
             "attn_bwd": (2.5 * af if backward else 0.0), "total": uvqk + outp + attn}
