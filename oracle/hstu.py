@@ -11,7 +11,8 @@ Pages cited (their text, not line numbers):
            (xfinit.ro), sections "Model Architecture", "HSTU Hyperparameters",
            "Computation Cost Analysis" (Tables 6 and 7).
   [ULTRA]  Telegram summary of "Bending the Scaling Law Curve in Large-Scale
-           Recommendation Systems" (ULTRA-HSTU), item "Semi-Local Attention".
+           Recommendation Systems" (ULTRA-HSTU), items "Semi-Local Attention"
+           and "Attention Truncation".
 
 What is computed (every array is float64; integer work is exact):
 
@@ -40,6 +41,13 @@ What is computed (every array is float64; integer work is exact):
    [DLRMv4] third bullet): LayerNorm over the H*d_v vector of each token
    (biased variance, eps; optional gamma/beta), G = LN(O) * U.
 4. Y = G W2 (+ b2) (+ X when residual).  Layers stack Y -> next X.
+   Attention truncation ([ULTRA]: after N layers over whole sequences, M
+   further layers see only a segment of length L' of each history, taken
+   from its most recent events): the segment is read as the last
+   min(n_h, L') history tokens followed by the sequence's c candidates, a
+   contiguous tail of the sequence that keeps its own timestamps; it is
+   attended as a sequence of its own (positions restart, which changes no
+   bucket since buckets depend on position differences only).
 5. Backward: the chain rule of 1-4 written out by hand (no autograd).
 
 Readings where the pages are silent (each is a flag here):
@@ -350,3 +358,78 @@ def stack_fwd(X, layers: List, seq_offsets, timestamps, num_candidates, f: Layer
                          num_candidates, f)
         outs.append(x)
     return outs
+
+
+# ----------------------------------------------------------------------------
+# Attention truncation ([ULTRA] "Attention Truncation")
+# ----------------------------------------------------------------------------
+
+def truncate_rows(seq_offsets, num_candidates, keep: int):
+    """(seg_offsets [B+1], rows [T_seg]) of the truncated batch: sequence b's
+    segment is its last min(n_h, keep) history rows followed by its c_b
+    candidate rows; rows[r] is the source row of segment row r."""
+    offs = np.asarray(seq_offsets, np.int64)
+    B = len(offs) - 1
+    seg = np.zeros(B + 1, np.int64)
+    parts = []
+    for b in range(B):
+        n = int(offs[b + 1] - offs[b])
+        c = 0 if num_candidates is None else int(num_candidates[b])
+        m = min(n - c, keep) + c
+        parts.append(np.arange(offs[b + 1] - m, offs[b + 1], dtype=np.int64))
+        seg[b + 1] = seg[b] + m
+    rows = np.concatenate(parts) if parts else np.zeros(0, np.int64)
+    return seg, rows
+
+
+def truncated_stack_fwd(X, full_layers: List, tail_layers: List, seq_offsets, timestamps,
+                        num_candidates, f_full: LayerFlags, f_tail: LayerFlags, keep: int):
+    """N layers over the whole sequences, then M layers over the truncated
+    segments.  Returns (Y_seg [T_seg, D], record for truncated_stack_bwd)."""
+    x = np.asarray(X, np.float64)
+    ts = np.asarray(timestamps, np.int64)
+    full = []
+    for w in full_layers:
+        y, sv = layer_fwd(x, w.W1, w.W2, w.rab_pos, w.rab_time, seq_offsets, ts,
+                          num_candidates, f_full)
+        full.append((x, sv))
+        x = y
+    seg, rows = truncate_rows(seq_offsets, num_candidates, keep)
+    ts_seg = ts[rows]
+    x = x[rows]
+    tail = []
+    for w in tail_layers:
+        y, sv = layer_fwd(x, w.W1, w.W2, w.rab_pos, w.rab_time, seg, ts_seg, num_candidates,
+                          f_tail)
+        tail.append((x, sv))
+        x = y
+    rec = dict(full=full, tail=tail, seg_offsets=seg, rows=rows, ts_seg=ts_seg,
+               T=int(np.asarray(X).shape[0]))
+    return x, rec
+
+
+def truncated_stack_bwd(dY_seg, full_layers: List, tail_layers: List, seq_offsets, timestamps,
+                        num_candidates, f_full: LayerFlags, f_tail: LayerFlags, rec: Dict):
+    """Gradients of truncated_stack_fwd for the segment-output gradient dY_seg:
+    (dX [T, D], per-layer gradient dicts of the full layers, of the tail layers).
+    Rows outside the segments receive no gradient from the tail layers."""
+    g = np.asarray(dY_seg, np.float64)
+    g_tail = [None] * len(tail_layers)
+    for l in range(len(tail_layers) - 1, -1, -1):
+        w = tail_layers[l]
+        x, sv = rec["tail"][l]
+        r = layer_bwd(g, x, w.W1, w.W2, w.rab_pos, w.rab_time, rec["seg_offsets"],
+                      rec["ts_seg"], num_candidates, f_tail, sv)
+        g_tail[l] = r
+        g = r["dX"]
+    dx = np.zeros((rec["T"], g.shape[1]), np.float64)
+    dx[rec["rows"]] = g
+    g_full = [None] * len(full_layers)
+    for l in range(len(full_layers) - 1, -1, -1):
+        w = full_layers[l]
+        x, sv = rec["full"][l]
+        r = layer_bwd(dx, x, w.W1, w.W2, w.rab_pos, w.rab_time, seq_offsets, timestamps,
+                      num_candidates, f_full, sv)
+        g_full[l] = r
+        dx = r["dX"]
+    return dx, g_full, g_tail
