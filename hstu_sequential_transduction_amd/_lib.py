@@ -24,6 +24,7 @@ EXPORTED = [
     "hstu_layer_fwd", "hstu_layer_bwd",
     "hstu_bias_buckets", "hstu_schedule_capacity", "hstu_schedule",
     "hstu_schedule_workspace_size", "hstu_validate_inputs",
+    "hstu_truncate_offsets", "hstu_truncate_gather", "hstu_truncate_scatter",
     "hstu_timer_enable", "hstu_timer_reset", "hstu_timer_tag_count", "hstu_timer_tag_name",
     "hstu_timer_query",
 ]
@@ -109,6 +110,12 @@ def lib() -> C.CDLL:
     L.hstu_schedule.argtypes = [i32, i64, vp, i32, i32, vp, vp, vp, sz, vp]
     L.hstu_validate_inputs.restype = C.c_int
     L.hstu_validate_inputs.argtypes = [i32, i64, vp, vp, vp, vp]
+    L.hstu_truncate_offsets.restype = C.c_int
+    L.hstu_truncate_offsets.argtypes = [i32, vp, vp, i32, vp, vp]
+    L.hstu_truncate_gather.restype = C.c_int
+    L.hstu_truncate_gather.argtypes = [i32, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    L.hstu_truncate_scatter.restype = C.c_int
+    L.hstu_truncate_scatter.argtypes = [i32, i64, i64, i32, i32, vp, vp, vp, vp, vp]
     L.hstu_timer_enable.restype = C.c_int
     L.hstu_timer_enable.argtypes = [i32]
     L.hstu_timer_reset.restype = C.c_int

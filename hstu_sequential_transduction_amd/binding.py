@@ -229,6 +229,46 @@ def hstu_layer_bwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: L
     return dx, grads
 
 
+def hstu_truncate_offsets(seq_offsets, keep: int, num_candidates=None, T_seg: Optional[int] = None,
+                          stream=None):
+    """(seg_offsets [B+1] int32, T_seg) of attention truncation's segments.
+    When T_seg is not given it is read back from the device (a synchronisation)."""
+    B = seq_offsets.shape[0] - 1
+    seg = torch.empty((B + 1,), dtype=torch.int32, device=seq_offsets.device)
+    st = _lib.lib().hstu_truncate_offsets(B, _ptr(seq_offsets), _ptr(num_candidates), int(keep),
+                                          _ptr(seg), _stream(stream))
+    check("hstu_truncate_offsets", st)
+    if T_seg is None:
+        T_seg = int(seg[B].item())
+    return seg, T_seg
+
+
+def hstu_truncate_gather(x, seq_offsets, seg_offsets, T_seg: int, timestamps=None, stream=None):
+    """(x_seg [T_seg, D], ts_seg [T_seg] or None): the rows of the truncated batch."""
+    B = seq_offsets.shape[0] - 1
+    T, D = x.shape
+    xs = torch.empty((T_seg, D), dtype=x.dtype, device=x.device)
+    tss = None if timestamps is None else torch.empty((T_seg,), dtype=torch.int64,
+                                                       device=x.device)
+    st = _lib.lib().hstu_truncate_gather(B, T, T_seg, D, _DT[x.dtype], _ptr(x), _ptr(seq_offsets),
+                                         _ptr(seg_offsets), _ptr(timestamps), _ptr(xs), _ptr(tss),
+                                         _stream(stream))
+    check("hstu_truncate_gather", st)
+    return xs, tss
+
+
+def hstu_truncate_scatter(dx_seg, seq_offsets, seg_offsets, T: int, stream=None):
+    """dx [T, D]: dx_seg's rows back at their full-batch rows, zeros elsewhere."""
+    B = seq_offsets.shape[0] - 1
+    T_seg, D = dx_seg.shape
+    dx = torch.empty((T, D), dtype=dx_seg.dtype, device=dx_seg.device)
+    st = _lib.lib().hstu_truncate_scatter(B, T, T_seg, D, _DT[dx_seg.dtype], _ptr(dx_seg),
+                                          _ptr(seq_offsets), _ptr(seg_offsets), _ptr(dx),
+                                          _stream(stream))
+    check("hstu_truncate_scatter", st)
+    return dx
+
+
 def hstu_bias_buckets(seq_offsets, timestamps, pair_seq, pair_i, pair_j, cfg: AttnConfig,
                       num_candidates=None, stream=None):
     """(bp, bt) int32 device tensors for the listed (sequence, query row, key row) pairs."""

@@ -245,6 +245,20 @@ hstu_status check_layer(const hstu_layer_desc* L) {
   return HSTU_OK;
 }
 
+hstu_status check_trunc_copy(int32_t B, int64_t T, int64_t T_seg, int32_t D, int32_t dtype,
+                             const void* a, const void* b, const int32_t* offs,
+                             const int32_t* seg) {
+  if (dtype != HSTU_F32 && dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
+  if (B < 0 || T < 0 || T_seg < 0 || D <= 0 || T >= (int64_t(1) << 31) ||
+      T_seg >= (int64_t(1) << 31))
+    return HSTU_ERR_INVALID_ARG;
+  if ((int64_t(D) * esize(dtype)) % 16 != 0) return HSTU_ERR_INVALID_ARG;
+  if (!offs || !seg) return HSTU_ERR_INVALID_ARG;
+  if ((T > 0 && !a) || (T_seg > 0 && !b)) return HSTU_ERR_INVALID_ARG;
+  if ((a && !aligned16(a)) || (b && !aligned16(b))) return HSTU_ERR_INVALID_ARG;
+  return HSTU_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -580,6 +594,41 @@ hstu_status hstu_bias_buckets(const hstu_attn_desc* d, const int32_t* offs, cons
   AttnArgs a = base_args(d, nullptr, nullptr, 0, nullptr, 0, offs, ts, nullptr, nullptr, nc, w.tm);
   HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st));
   HSTU_TRY(launch_bias_buckets(a, ps, pi, pj, n_pairs, bp, bt, st));
+  return HSTU_OK;
+}
+
+hstu_status hstu_truncate_offsets(int32_t B, const int32_t* offs, const int32_t* nc,
+                                  int32_t keep, int32_t* seg, void* stream) {
+  if (B < 0 || keep < 0 || !offs || !seg) return HSTU_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  { HSTU_TIMED(TT_TRUNCATE, st); HSTU_TRY(launch_trunc_offsets(B, offs, nc, keep, seg, st)); }
+  return HSTU_OK;
+}
+
+
+hstu_status hstu_truncate_gather(int32_t B, int64_t T, int64_t T_seg, int32_t D, int32_t dtype,
+                                 const void* x, const int32_t* offs, const int32_t* seg,
+                                 const int64_t* ts, void* x_seg, int64_t* ts_seg,
+                                 void* stream) {
+  hstu_status s = check_trunc_copy(B, T, T_seg, D, dtype, x, x_seg, offs, seg);
+  if (s != HSTU_OK) return s;
+  if (T_seg > 0 && (ts == nullptr) != (ts_seg == nullptr)) return HSTU_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  HSTU_TIMED(TT_TRUNCATE, st);
+  HSTU_TRY(launch_trunc_gather(B, T, T_seg, int64_t(D) * esize(dtype), offs, seg, x, x_seg, ts,
+                               ts_seg, st));
+  return HSTU_OK;
+}
+
+hstu_status hstu_truncate_scatter(int32_t B, int64_t T, int64_t T_seg, int32_t D, int32_t dtype,
+                                  const void* dx_seg, const int32_t* offs, const int32_t* seg,
+                                  void* dx, void* stream) {
+  hstu_status s = check_trunc_copy(B, T, T_seg, D, dtype, dx, dx_seg, offs, seg);
+  if (s != HSTU_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HSTU_TIMED(TT_TRUNCATE, st);
+  HSTU_TRY(launch_trunc_scatter(B, T, T_seg, int64_t(D) * esize(dtype), offs, seg, dx_seg, dx,
+                                st));
   return HSTU_OK;
 }
 

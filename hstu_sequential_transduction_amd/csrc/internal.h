@@ -183,4 +183,15 @@ int64_t ln_bwd_part_blocks(int64_t T);
 hipError_t launch_validate(int B, const int32_t* seq_offsets, const int32_t* num_cand,
                            int64_t T, int32_t* flag, hipStream_t st);
 
+// Attention truncation: segment offsets, row gather, gradient scatter.
+hipError_t launch_trunc_offsets(int B, const int32_t* seq_offsets, const int32_t* num_cand,
+                                int keep, int32_t* seg_offsets, hipStream_t st);
+hipError_t launch_trunc_gather(int B, int64_t T, int64_t T_seg, int64_t row_bytes,
+                               const int32_t* seq_offsets, const int32_t* seg_offsets,
+                               const void* x, void* x_seg, const int64_t* ts, int64_t* ts_seg,
+                               hipStream_t st);
+hipError_t launch_trunc_scatter(int B, int64_t T, int64_t T_seg, int64_t row_bytes,
+                                const int32_t* seq_offsets, const int32_t* seg_offsets,
+                                const void* dx_seg, void* dx, hipStream_t st);
+
 }  // namespace hstu

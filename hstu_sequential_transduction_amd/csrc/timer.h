@@ -21,6 +21,7 @@ enum TimerTag {
   TT_LN_FWD,
   TT_LN_BWD,
   TT_REDUCE,
+  TT_TRUNCATE,
   TT_COUNT
 };
 

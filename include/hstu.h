@@ -221,6 +221,57 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const void* x,
                            void* dx, const hstu_layer_grads* g,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- attention truncation ---------------------------------------------- */
+/*
+ * "Bending the Scaling Law Curve in Large-Scale Recommendation Systems",
+ * Attention Truncation: after N layers over whole sequences, M further
+ * layers run only on a segment of each history made of its most recent
+ * events.  The segment of sequence b is its last min(n_b - c_b, keep)
+ * history rows followed by its c_b candidate rows: a contiguous tail of the
+ * sequence, attended as a sequence of its own (same num_candidates, its own
+ * timestamps; relative position buckets are unchanged because they depend
+ * on position differences only).  Segment row r of sequence b comes from
+ * full row seq_offsets[b+1] - seg_offsets[b+1] + r.
+ */
+
+/*
+ * seg_offsets[0..B] (device int32, written on `stream`) of the segments.
+ * seq_offsets: [B+1] device int32; num_candidates: [B] device int32 or NULL
+ * (no candidates; values are clamped to [0, n_b]); keep >= 0.  The segment
+ * total T_seg = seg_offsets[B] is needed on the host to size the truncated
+ * batch: the caller reads it back or knows it from the lengths.
+ * Errors: HSTU_ERR_INVALID_ARG for B < 0, keep < 0 or a NULL pointer.
+ */
+hstu_status hstu_truncate_offsets(int32_t B, const int32_t* seq_offsets,
+                                  const int32_t* num_candidates, int32_t keep,
+                                  int32_t* seg_offsets, void* stream);
+
+/*
+ * Gather of the truncated batch: x_seg[r] = x[src(r)] for r < T_seg and,
+ * when both are given, ts_seg[r] = timestamps[src(r)] (for T_seg > 0,
+ * neither or both must be given).  x: [T, D] dtype,
+ * x_seg: [T_seg, D] dtype, rows contiguous, both 16-byte aligned, D times
+ * the element size a multiple of 16 bytes; T = seq_offsets[B],
+ * T_seg = seg_offsets[B] (from hstu_truncate_offsets with the same
+ * seq_offsets).  Rows whose source would fall outside [0, T) are written as
+ * zeros.  x_seg may not overlap x.  Errors: HSTU_ERR_INVALID_ARG (sizes,
+ * NULL pointers, alignment), HSTU_ERR_UNSUPPORTED (dtype).
+ */
+hstu_status hstu_truncate_gather(int32_t B, int64_t T, int64_t T_seg, int32_t D, int32_t dtype,
+                                 const void* x, const int32_t* seq_offsets,
+                                 const int32_t* seg_offsets, const int64_t* timestamps,
+                                 void* x_seg, int64_t* ts_seg, void* stream);
+
+/*
+ * Backward of the gather: dx[i] = dx_seg[r] for the segment row r taken from
+ * full row i, and dx[i] = 0 for every row outside the segments (all T rows
+ * are written).  Shapes and alignment as for hstu_truncate_gather; dx may
+ * not overlap dx_seg.
+ */
+hstu_status hstu_truncate_scatter(int32_t B, int64_t T, int64_t T_seg, int32_t D, int32_t dtype,
+                                  const void* dx_seg, const int32_t* seq_offsets,
+                                  const int32_t* seg_offsets, void* dx, void* stream);
+
 /* ---- inspection entry points (tests, debugging) ------------------------- */
 
 /*

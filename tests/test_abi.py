@@ -153,3 +153,26 @@ def test_negative_windows_rejected(L):
         st = L.hstu_attn_fwd(C.byref(d), p, p, 64, p, 64, p, p, p, p, None, p, 64, ws, 1 << 15,
                              None)
         assert st == -1
+
+
+def test_truncation_argument_errors(L):
+    """Host-side checks of the truncation entry points (nothing is launched)."""
+    p = C.c_void_p(1 << 20)            # 16-byte aligned, never dereferenced
+    odd = C.c_void_p((1 << 20) + 8)    # not 16-byte aligned
+    assert L.hstu_truncate_offsets(-1, p, None, 4, p, None) == -1
+    assert L.hstu_truncate_offsets(2, p, None, -1, p, None) == -1
+    assert L.hstu_truncate_offsets(2, None, None, 4, p, None) == -1
+    g = L.hstu_truncate_gather
+    # dtype, D not a multiple of 16 bytes, misaligned rows, NULL seg_offsets
+    assert g(2, 10, 4, 64, 9, p, p, p, None, p, None, None) == -2
+    assert g(2, 10, 4, 4, 1, p, p, p, None, p, None, None) == -1
+    assert g(2, 10, 4, 64, 1, odd, p, p, None, p, None, None) == -1
+    assert g(2, 10, 4, 64, 1, p, p, None, None, p, None, None) == -1
+    # timestamps without their output (or the reverse)
+    assert g(2, 10, 4, 64, 1, p, p, p, p, p, None, None) == -1
+    assert g(2, 10, 1 << 31, 64, 1, p, p, p, None, p, None, None) == -1
+    s = L.hstu_truncate_scatter
+    assert s(2, 10, 4, 64, 1, odd, p, p, p, None) == -1
+    assert s(2, -1, 4, 64, 1, p, p, p, p, None) == -1
+    assert s(2, 10, 4, 6, 0, p, p, p, p, None) == -1    # fp32 rows of 24 bytes
+    assert s(2, 10, 4, 64, 1, p, p, p, None, None) == -1  # NULL dx
