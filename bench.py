@@ -176,6 +176,99 @@ def bench_semilocal(args, timer, full_ms):
     return out
 
 
+# Attention truncation on the ranking workload (16 x (4096 history + 512
+# candidates), d_model 256, 4 heads x 64), in the pages' 3 + 6 layer scheme
+# against 6 full layers.  The segment length L' is not on the pages: 1024
+# history events (plus the candidates) is a chosen parameter.
+TRUNC_KEEP = 1024
+TRUNC_SCHEME = (3, 6)
+
+
+def bench_truncation(timer, reps=3):
+    """Inference forward of (a) 6 full layers, (b) 3 full + 6 truncated
+    layers, (c) as (b) with semi-local windows in the full layers."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import synth
+    from hstu_sequential_transduction_amd import binding as B
+    from hstu_sequential_transduction_amd import flops
+    from hstu_sequential_transduction_amd import truncation as TR
+    nf, nt = TRUNC_SCHEME
+    cfg = dataclasses.replace(synth.get_config(5), n_layers=max(nf + nt, 6))
+    inp = synth.make_inputs(cfg)
+    td = torch.bfloat16
+    X = torch.from_numpy(inp.X).to(td).cuda()
+    offs = torch.from_numpy(inp.seq_offsets.astype(np.int32)).cuda()
+    ts = torch.from_numpy(inp.timestamps).cuda()
+    nc = torch.from_numpy(inp.num_candidates.astype(np.int32)).cuda()
+    lay = [tuple(upload_layer(inp, cfg, li).values()) for li in range(cfg.n_layers)]
+    c = int(inp.num_candidates[0])
+    seg_len = np.minimum(inp.lengths - inp.num_candidates, TRUNC_KEEP) + inp.num_candidates
+    T_seg = int(seg_len.sum())     # known on the host from the batch's lengths, like T
+    ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len)
+    lc_full = B.LayerConfig(D=cfg.D, attn=ac)
+    lc_semi = B.LayerConfig(D=cfg.D, attn=dataclasses.replace(
+        ac, win_local=SEMILOCAL_WINDOW[0], win_global=SEMILOCAL_WINDOW[1]))
+    # the truncated batch's length normaliser: its own maximum length
+    lc_tail = B.LayerConfig(D=cfg.D, attn=dataclasses.replace(ac, norm_len=TRUNC_KEEP + c))
+    ws = B.LayerWorkspace()
+    bufs = [torch.empty_like(X), torch.empty_like(X)]
+
+    def full6():
+        x = X
+        for li in range(6):
+            W1, W2, rp, rt = lay[li]
+            x = B.hstu_layer_fwd(x, W1, W2, rp, rt, offs, ts, lc_full, num_candidates=nc,
+                                 y=bufs[li % 2], workspace=ws)
+
+    def trunc(lc_first):
+        return lambda: TR.truncated_stack_fwd(X, lay[:nf], lay[nf:nf + nt], offs, ts, lc_first,
+                                              lc_tail, TRUNC_KEEP, num_candidates=nc,
+                                              T_seg=T_seg, workspace=ws)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        timer.enable(64 * reps * 10)
+        timer.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        kern = timer.read()
+        timer.enable(0)
+        return e0.elapsed_time(e1) / reps, kern
+
+    def lf(lengths, window=None):
+        return flops.layer_flops(lengths, inp.num_candidates, cfg.D, cfg.H, cfg.d_qk, cfg.d_v,
+                                 backward=False, window=window)["total"]
+
+    f_full, f_tail = lf(inp.lengths), lf(seg_len)
+    f_semi = lf(inp.lengths, SEMILOCAL_WINDOW)
+    work = {"6_full": 6 * f_full, "3_full_6_trunc": nf * f_full + nt * f_tail,
+            "3_semilocal_6_trunc": nf * f_semi + nt * f_tail}
+    out = {"workload": "ranking batch 16 x (4096 history + 512 candidates), d_model 256, "
+                       "4 heads x 64, bf16, inference forward",
+           "keep": TRUNC_KEEP, "scheme": f"{nf} full + {nt} truncated vs 6 full",
+           "semilocal_window": list(SEMILOCAL_WINDOW), "tokens": inp.T, "tokens_truncated": T_seg}
+    for name, fn in (("6_full", full6), ("3_full_6_trunc", trunc(lc_full)),
+                     ("3_semilocal_6_trunc", trunc(lc_semi))):
+        ms, kern = timed(fn)
+        out[name] = {"ms": round(ms, 4), "tflops": round(work[name] / (ms * 1e-3) / 1e12, 2),
+                     "truncate_ms": round(kern.get("truncate", (0, 0.0))[1] / reps, 4)}
+    base = out["6_full"]["ms"]
+    for name in ("3_full_6_trunc", "3_semilocal_6_trunc"):
+        out[name]["speedup_vs_6_full"] = round(base / out[name]["ms"], 3)
+        out[name]["flop_ratio_vs_6_full"] = round(work["6_full"] / work[name], 3)
+    log(f"truncation: {out}")
+    return out
+
+
 def roofline(cfg, inp, kern, steps, traffic_dir):
     work = kernel_work(cfg, inp.lengths, inp.T)
     best = max(((ms, name, n) for name, (n, ms) in kern.items() if name in work), default=None)
@@ -312,7 +405,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the forward-only workloads and the semi-local training step")
+                    help="skip the forward-only workloads, the semi-local training step and "
+                         "the attention-truncation forward")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
@@ -331,6 +425,7 @@ def main():
     roof, table = roofline(cfg, inp, kern, args.steps, os.path.join(ROOT, "profiles"))
     extra = None if args.no_extra else bench_fwd_configs(timer)
     semi = None if args.no_extra else bench_semilocal(args, timer, ms)
+    trunc = None if args.no_extra else bench_truncation(timer)
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, inp)
     line = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -349,6 +444,7 @@ def main():
         "cpu_baseline": cpu,
         "forward_workloads": extra,
         "semilocal": semi,
+        "truncation": trunc,
     }
     print(json.dumps(line), flush=True)
 
