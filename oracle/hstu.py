@@ -48,6 +48,14 @@ What is computed (every array is float64; integer work is exact):
    contiguous tail of the sequence that keeps its own timestamps; it is
    attended as a sequence of its own (positions restart, which changes no
    bucket since buckets depend on position differences only).
+   Ranking against a cached history: a history row never attends to a
+   candidate, so each layer's history keys and values, and the history's
+   layer outputs, do not depend on the candidates ([DLRMv4] "Model
+   Architecture": candidates appended and compared with the history in one
+   pass).  Computed once per history, the per-layer K and V let a batch of
+   candidates run through the layers alone: candidate rows at position n_h
+   attend to the cached keys and to themselves.  This equals the candidate
+   rows of the full target-aware stack when N is a fixed norm_len.
 5. Backward: the chain rule of 1-4 written out by hand (no autograd).
 
 Readings where the pages are silent (each is a flag here):
@@ -433,3 +441,90 @@ def truncated_stack_bwd(dY_seg, full_layers: List, tail_layers: List, seq_offset
         g_full[l] = r
         dx = r["dX"]
     return dx, g_full, g_tail
+
+
+# ----------------------------------------------------------------------------
+# Ranking against a cached history ([DLRMv4] "Model Architecture": appended
+# candidates compared with the history; the history part computed once)
+# ----------------------------------------------------------------------------
+
+def attn_fwd_cached(q, k, v, cand_offsets, cand_ts, k_hist, v_hist, hist_offsets, hist_ts,
+                    rab_pos, rab_time, norm_len=1, win_local=0, win_global=0):
+    """O[T_c, H, d_v] of candidate rows scored against a cached history.
+
+    User b's candidates (rows cand_offsets[b] .. cand_offsets[b+1]) sit at
+    position n_h = hist_offsets[b+1] - hist_offsets[b] and attend to each
+    history key j of the user (when W_l > 0 only if n_h - j < W_l or
+    j < W_g) and to their own key, never to another candidate.
+    q, k, v: the candidates' own rows [T_c, H, d]; k_hist, v_hist: [T_h, H, d].
+    """
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    kh = np.asarray(k_hist, np.float64); vh = np.asarray(v_hist, np.float64)
+    Tc, H, _ = q.shape
+    rp, rt = _rab(rab_pos, H), _rab(rab_time, H)
+    P, Tb = rp.shape[1], rt.shape[1]
+    O = np.zeros((Tc, H, v.shape[2]))
+    N = float(norm_len)
+    bp_self = pos_bucket(np.array(0), P)
+    bt_self = time_bucket(np.array(0), Tb)
+    for b in range(len(cand_offsets) - 1):
+        c0, c1 = int(cand_offsets[b]), int(cand_offsets[b + 1])
+        h0, h1 = int(hist_offsets[b]), int(hist_offsets[b + 1])
+        if c1 == c0:
+            continue
+        nh = h1 - h0
+        j = np.arange(nh)
+        keep = np.ones(nh, bool) if win_local <= 0 else (nh - j < win_local) | (j < win_global)
+        bp = pos_bucket(nh - j, P)                                            # [n_h]
+        bt = time_bucket(np.asarray(cand_ts[c0:c1], np.int64)[:, None]
+                         - np.asarray(hist_ts[h0:h1], np.int64)[None, :], Tb)  # [c, n_h]
+        for h in range(H):
+            s_hist = q[c0:c1, h, :] @ kh[h0:h1, h, :].T + rp[h][bp][None, :] + rt[h][bt]
+            a_hist = np.where(keep[None, :], silu(s_hist), 0.0) / N
+            s_self = np.sum(q[c0:c1, h, :] * k[c0:c1, h, :], axis=1) + rp[h][bp_self] + rt[h][bt_self]
+            O[c0:c1, h, :] = a_hist @ vh[h0:h1, h, :] + (silu(s_self) / N)[:, None] * v[c0:c1, h, :]
+    return O
+
+
+def layer_fwd_cached(Xc, W1, W2, rab_pos, rab_time, k_hist, v_hist, hist_offsets, hist_ts,
+                     cand_offsets, cand_ts, f: LayerFlags, b1=None, b2=None, gamma=None,
+                     beta=None):
+    """One layer over candidate rows only, attention against this layer's
+    cached history keys and values (steps 1-4 with attn_fwd_cached)."""
+    Xc = np.asarray(Xc, np.float64)
+    Z = Xc @ np.asarray(W1, np.float64)
+    if b1 is not None:
+        Z = Z + np.asarray(b1, np.float64)
+    Zh = silu(Z) if f.proj_silu else Z
+    U, V, Q, K = split_uvqk(Zh, f)
+    O = attn_fwd_cached(Q, K, V, cand_offsets, cand_ts, k_hist, v_hist, hist_offsets, hist_ts,
+                        rab_pos, rab_time, f.norm_len, f.win_local, f.win_global)
+    Yn, _, _, _ = layernorm_fwd(O.reshape(Xc.shape[0], f.H * f.d_v), f.eps, gamma, beta)
+    Y = (Yn * U) @ np.asarray(W2, np.float64)
+    if b2 is not None:
+        Y = Y + np.asarray(b2, np.float64)
+    if f.residual:
+        Y = Y + Xc
+    return Y
+
+
+def history_cache(Xh, layers: List, hist_offsets, hist_ts, f: LayerFlags):
+    """Per layer (K_hist, V_hist) of the history run through the stack alone."""
+    caches = []
+    x = np.asarray(Xh, np.float64)
+    for w in layers:
+        y, sv = layer_fwd(x, w.W1, w.W2, w.rab_pos, w.rab_time, hist_offsets, hist_ts, None, f)
+        _, V, _, K = split_uvqk(sv["Zh"], f)
+        caches.append((K, V))
+        x = y
+    return caches
+
+
+def cached_stack_fwd(Xc, layers: List, caches: List, hist_offsets, hist_ts, cand_offsets,
+                     cand_ts, f: LayerFlags):
+    """Candidate rows through the stack against the per-layer history caches."""
+    x = np.asarray(Xc, np.float64)
+    for w, (K, V) in zip(layers, caches):
+        x = layer_fwd_cached(x, w.W1, w.W2, w.rab_pos, w.rab_time, K, V, hist_offsets, hist_ts,
+                             cand_offsets, cand_ts, f)
+    return x
