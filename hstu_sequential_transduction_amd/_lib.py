@@ -25,6 +25,8 @@ EXPORTED = [
     "hstu_bias_buckets", "hstu_schedule_capacity", "hstu_schedule",
     "hstu_schedule_workspace_size", "hstu_validate_inputs",
     "hstu_truncate_offsets", "hstu_truncate_gather", "hstu_truncate_scatter",
+    "hstu_attn_cached_workspace_size", "hstu_attn_cached_fwd",
+    "hstu_layer_cached_workspace_size", "hstu_layer_fwd_cached",
     "hstu_timer_enable", "hstu_timer_reset", "hstu_timer_tag_count", "hstu_timer_tag_name",
     "hstu_timer_query",
 ]
@@ -59,6 +61,11 @@ class LayerGrads(C.Structure):
     _fields_ = [("dW1", C.c_void_p), ("dW2", C.c_void_p), ("db1", C.c_void_p),
                 ("db2", C.c_void_p), ("dgamma", C.c_void_p), ("dbeta", C.c_void_p),
                 ("drab_pos", C.c_void_p), ("drab_time", C.c_void_p)]
+
+
+class HistoryKV(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("ld_k", C.c_int64), ("ld_v", C.c_int64),
+                ("offsets", C.c_void_p), ("timestamps", C.c_void_p), ("T", C.c_int64)]
 
 
 _lib = None
@@ -110,6 +117,16 @@ def lib() -> C.CDLL:
     L.hstu_schedule.argtypes = [i32, i64, vp, i32, i32, vp, vp, vp, sz, vp]
     L.hstu_validate_inputs.restype = C.c_int
     L.hstu_validate_inputs.argtypes = [i32, i64, vp, vp, vp, vp]
+    L.hstu_attn_cached_workspace_size.restype = sz
+    L.hstu_attn_cached_workspace_size.argtypes = [P(AttnDesc), i64]
+    L.hstu_attn_cached_fwd.restype = C.c_int
+    L.hstu_attn_cached_fwd.argtypes = [P(AttnDesc), vp, vp, i64, vp, i64, vp, vp, P(HistoryKV),
+                                       vp, vp, vp, i64, vp, sz, vp]
+    L.hstu_layer_cached_workspace_size.restype = sz
+    L.hstu_layer_cached_workspace_size.argtypes = [P(LayerDesc), i64]
+    L.hstu_layer_fwd_cached.restype = C.c_int
+    L.hstu_layer_fwd_cached.argtypes = [P(LayerDesc), vp, P(LayerWeights), vp, vp,
+                                        P(HistoryKV), vp, vp, sz, vp]
     L.hstu_truncate_offsets.restype = C.c_int
     L.hstu_truncate_offsets.argtypes = [i32, vp, vp, i32, vp, vp]
     L.hstu_truncate_gather.restype = C.c_int

@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import AttnDesc, LayerDesc, LayerGrads, LayerSaved, LayerWeights, check
+from ._lib import AttnDesc, HistoryKV, LayerDesc, LayerGrads, LayerSaved, LayerWeights, check
 
 _DT = {torch.float32: _lib.HSTU_F32, torch.bfloat16: _lib.HSTU_BF16}
 
@@ -164,8 +164,9 @@ class LayerWorkspace:
 def hstu_layer_fwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: LayerConfig,
                    num_candidates=None, b1=None, b2=None, gamma=None, beta=None,
                    saved: Optional[Saved] = None, y=None, workspace: Optional[LayerWorkspace] = None,
-                   stream=None):
-    """Y = HSTU layer(x); fills `saved` when given (training)."""
+                   stream=None, keep_zh: Optional[torch.Tensor] = None):
+    """Y = HSTU layer(x); fills `saved` when given (training), or only the
+    U|V|Q|K tensor `keep_zh` [T, F1] (inference that keeps the projections)."""
     T = x.shape[0]
     B = seq_offsets.shape[0] - 1
     if y is None:
@@ -176,6 +177,10 @@ def hstu_layer_fwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: L
     ws = workspace.get(nb, x.device) if workspace is not None else _ws(nb, x.device)
     w = _weights(W1, W2, rab_pos, rab_time, b1, b2, gamma, beta)
     sv = saved.c() if saved is not None else None
+    if keep_zh is not None:
+        if saved is not None:
+            raise ValueError("keep_zh and saved are exclusive")
+        sv = LayerSaved(None, _ptr(keep_zh), None, None, None, None)
     st = L.hstu_layer_fwd(C.byref(d), _ptr(x), C.byref(w), _ptr(seq_offsets), _ptr(timestamps),
                           _ptr(num_candidates), _ptr(y), C.byref(sv) if sv is not None else None,
                           _ptr(ws), ws.numel(), _stream(stream))
@@ -227,6 +232,66 @@ def hstu_layer_bwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: L
                           _ptr(ws), ws.numel(), _stream(stream))
     check("hstu_layer_bwd", st)
     return dx, grads
+
+
+@dataclasses.dataclass
+class History:
+    """One layer's cached history keys and values (device tensors; k and v
+    may be strided column views, e.g. of the Zh a history forward kept)."""
+    k: torch.Tensor           # [T_hist, H*d_qk]
+    v: torch.Tensor           # [T_hist, H*d_v]
+    offsets: torch.Tensor     # [B+1] int32
+    timestamps: torch.Tensor  # [T_hist] int64
+
+    def c(self) -> HistoryKV:
+        return HistoryKV(_ptr(self.k), _ptr(self.v), self.k.stride(0), self.v.stride(0),
+                         _ptr(self.offsets), _ptr(self.timestamps), self.k.shape[0])
+
+
+def history_from_zh(Zh: torch.Tensor, cfg: LayerConfig, offsets, timestamps) -> History:
+    """The K and V column blocks of a history forward's U|V|Q|K output."""
+    W, HQ = cfg.attn.H * cfg.attn.d_v, cfg.attn.H * cfg.attn.d_qk
+    return History(Zh[:, 2 * W + HQ:2 * W + 2 * HQ], Zh[:, W:2 * W], offsets, timestamps)
+
+
+def hstu_attn_cached_fwd(q, k, v, cand_offsets, cand_ts, hist: History, rab_pos, rab_time,
+                         cfg: AttnConfig, out=None, stream=None):
+    """O [T_c, H*d_v] of candidates against a cached history (see include/hstu.h)."""
+    T = q.shape[0]
+    B = cand_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, cfg.H * cfg.d_v), dtype=q.dtype, device=q.device)
+    d = attn_desc(cfg, B, T, q.dtype, _rab_stride(rab_pos, rab_time))
+    L = _lib.lib()
+    h = hist.c()
+    ws = _ws(L.hstu_attn_cached_workspace_size(C.byref(d), h.T), q.device)
+    st = L.hstu_attn_cached_fwd(C.byref(d), _ptr(q), _ptr(k), q.stride(0), _ptr(v), v.stride(0),
+                                _ptr(cand_offsets), _ptr(cand_ts), C.byref(h), _ptr(rab_pos),
+                                _ptr(rab_time), _ptr(out), out.stride(0), _ptr(ws), ws.numel(),
+                                _stream(stream))
+    check("hstu_attn_cached_fwd", st)
+    return out
+
+
+def hstu_layer_fwd_cached(x, W1, W2, rab_pos, rab_time, cand_offsets, cand_ts, hist: History,
+                          cfg: LayerConfig, b1=None, b2=None, gamma=None, beta=None, y=None,
+                          workspace: Optional[LayerWorkspace] = None, stream=None):
+    """Y of one layer over candidate rows against this layer's cached history."""
+    T = x.shape[0]
+    B = cand_offsets.shape[0] - 1
+    if y is None:
+        y = torch.empty_like(x)
+    d = layer_desc(cfg, B, T, x.dtype, _rab_stride(rab_pos, rab_time))
+    L = _lib.lib()
+    h = hist.c()
+    nb = L.hstu_layer_cached_workspace_size(C.byref(d), h.T)
+    ws = workspace.get(nb, x.device) if workspace is not None else _ws(nb, x.device)
+    w = _weights(W1, W2, rab_pos, rab_time, b1, b2, gamma, beta)
+    st = L.hstu_layer_fwd_cached(C.byref(d), _ptr(x), C.byref(w), _ptr(cand_offsets),
+                                 _ptr(cand_ts), C.byref(h), _ptr(y), _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    check("hstu_layer_fwd_cached", st)
+    return y
 
 
 def hstu_truncate_offsets(seq_offsets, keep: int, num_candidates=None, T_seg: Optional[int] = None,

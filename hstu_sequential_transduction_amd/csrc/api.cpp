@@ -126,6 +126,83 @@ hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   return HSTU_OK;
 }
 
+// Ranking against a cached history: key splits per (user, candidate block)
+// chosen from the average history length so that about two workgroups per
+// compute unit run (512), with at least four key tiles per split.
+int cached_splits(const hstu_attn_desc* d, int64_t T_hist) {
+  const int bm = attn_cached_block_rows(d->dtype, d->d_qk, d->d_v);
+  const int64_t B = std::max<int64_t>(d->B, 1);
+  const int64_t items = d->T / bm + B;
+  const int64_t tile = d->dtype == HSTU_BF16 ? 64 : 32;
+  const int64_t tiles_per_user = (T_hist / B + tile - 1) / tile;
+  int64_t S = (512 + items * d->H - 1) / (items * d->H);
+  S = std::min<int64_t>(S, std::max<int64_t>(tiles_per_user / 4, 1));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(S, 16));
+}
+
+struct CachedWs {
+  int32_t* rel_h = nullptr;
+  int32_t* rel_c = nullptr;
+  int32_t* flags = nullptr;
+  Sched sc;
+  float* part = nullptr;
+  int splits = 1;
+};
+CachedWs carve_cached(Carver& c, const hstu_attn_desc* d, int64_t T_hist) {
+  CachedWs w;
+  w.rel_h = c.take<int32_t>(std::max<int64_t>(T_hist, 1));
+  w.rel_c = c.take<int32_t>(std::max<int64_t>(d->T, 1));
+  w.flags = c.take<int32_t>(std::max<int64_t>(d->B, 1));
+  w.sc = carve_sched(c, d->T, d->B, attn_cached_block_rows(d->dtype, d->d_qk, d->d_v));
+  w.splits = cached_splits(d, T_hist);
+  if (w.splits > 1) w.part = c.take<float>(w.splits * std::max<int64_t>(d->T, 1) * d->H * d->d_v);
+  return w;
+}
+
+hstu_status attn_cached_impl(const hstu_attn_desc* d, const void* q, const void* k,
+                             int64_t ld_qk, const void* v, int64_t ld_v, const int32_t* coffs,
+                             const int64_t* cts, const hstu_history_kv* hist, const float* rp,
+                             const float* rt, void* out, int64_t ld_out, bool out_f32, void* ws,
+                             hipStream_t st) {
+  Carver c(ws);
+  CachedWs w = carve_cached(c, d, hist->T);
+  CachedArgs a;
+  a.q = q; a.k = k; a.v = v; a.ld_qk = ld_qk; a.ld_v = ld_v;
+  a.cand_offsets = coffs; a.cand_ts = cts;
+  a.kh = hist->k; a.vh = hist->v; a.ld_kh = hist->ld_k; a.ld_vh = hist->ld_v;
+  a.hist_offsets = hist->offsets; a.hist_ts = hist->timestamps;
+  a.rel_h = w.rel_h; a.rel_c = w.rel_c; a.flags = w.flags;
+  a.items = w.sc.items; a.counters = w.sc.counters;
+  a.out = out; a.ld_out = ld_out; a.out_f32 = out_f32;
+  a.part = w.part; a.Tc = d->T; a.splits = w.splits;
+  a.rab_pos = rp; a.rab_time = rt; a.rab_stride = d->rab_head_stride;
+  a.H = d->H; a.nP = d->n_pos_buckets; a.nT = d->n_time_buckets; a.norm_len = d->norm_len;
+  a.win_local = d->win_local; a.win_global = d->win_global;
+  {
+    HSTU_TIMED(TT_PREPASS, st);
+    HSTU_TRY(launch_time_prepass_cached(d->B, hist->offsets, hist->timestamps, coffs, cts,
+                                        w.rel_h, w.rel_c, w.flags, st));
+  }
+  { HSTU_TIMED(TT_SCHED, st); HSTU_TRY(launch_sched(w.sc, d->B, coffs, 0, st)); }
+  {
+    HSTU_TIMED(TT_ATTN_CACHED, st);
+    HSTU_TRY(launch_attn_cached(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st));
+  }
+  return HSTU_OK;
+}
+
+hstu_status check_history(const hstu_attn_desc* d, const hstu_history_kv* hist) {
+  if (!hist || !hist->offsets || hist->T < 0 || hist->T >= (int64_t(1) << 31))
+    return HSTU_ERR_INVALID_ARG;
+  if (hist->T > 0 && (!hist->k || !hist->v || !hist->timestamps)) return HSTU_ERR_INVALID_ARG;
+  const int64_t hq = (int64_t)d->H * d->d_qk, hv = (int64_t)d->H * d->d_v;
+  if (hist->T > 0 && (!stride_ok(d->dtype, hist->k, hist->ld_k, hq) ||
+                      !stride_ok(d->dtype, hist->v, hist->ld_v, hv)))
+    return HSTU_ERR_INVALID_ARG;
+  if (d->norm_mode != 0) return HSTU_ERR_UNSUPPORTED;
+  return HSTU_OK;
+}
+
 hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
                           const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
                           const float* rp, const float* rt, const int32_t* nc, const void* dout,
@@ -190,6 +267,21 @@ LayerFwdWs carve_layer_fwd(Carver& c, const hstu_layer_desc* L, int training) {
   }
   w.attn = c.take<char>(0);
   carve_fwd(c, d);
+  return w;
+}
+
+// Candidate-only layer: Zh, O, G of the candidate rows, then the cached
+// attention's own workspace.
+LayerFwdWs carve_layer_cached(Carver& c, const hstu_layer_desc* L, int64_t T_hist) {
+  LayerFwdWs w;
+  const hstu_attn_desc* d = &L->attn;
+  const size_t es = esize(d->dtype);
+  const int64_t T = std::max<int64_t>(d->T, 1);
+  w.Zh = c.take<char>(T * f1_width(L) * es);
+  w.O = c.take<float>(T * (int64_t)d->H * d->d_v);
+  w.G = c.take<char>(T * (int64_t)d->H * d->d_v * es);
+  w.attn = c.take<char>(0);
+  carve_cached(c, d, T_hist);
   return w;
 }
 
@@ -259,6 +351,88 @@ hstu_status check_trunc_copy(int32_t B, int64_t T, int64_t T_seg, int32_t D, int
   return HSTU_OK;
 }
 
+// Steps 1-4 of one layer on T rows, with the attention step supplied by the
+// caller (causal / target-aware over the rows' own sequences, or candidates
+// against a cached history).  Zsave, mu, rstd: optional saved intermediates.
+template <typename Attn>
+hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
+                            void* y, void* Zsave, void* Zh, float* O, void* G, float* mu,
+                            float* rstd, Attn attention, hipStream_t st) {
+  const hstu_attn_desc* d = &L->attn;
+  const int64_t T = d->T, D = L->D, F1 = f1_width(L);
+  const int64_t W = (int64_t)d->H * d->d_v, HQ = (int64_t)d->H * d->d_qk;
+  const size_t es = esize(d->dtype);
+  char* zh = static_cast<char*>(Zh);
+
+  // 1. Z = X W1 (+ b1); Zh = SiLU(Z)
+  GemmArgs g1;
+  g1.M = T;
+  g1.N = F1;
+  g1.K = D;
+  g1.A = x;
+  g1.lda = D;
+  g1.a_kcont = true;
+  g1.B = w->W1;
+  g1.ldb = F1;
+  g1.b_kcont = false;
+  g1.C = Zh;
+  g1.ldc = F1;
+  g1.bias = w->b1;
+  if (L->proj_silu) {
+    g1.epi = EPI_SILU;
+    g1.C2 = Zsave;
+  } else {
+    g1.epi = EPI_RESID;  // bias only
+    g1.R = nullptr;
+  }
+  { HSTU_TIMED(TT_GEMM_UVQK, st); HSTU_TRY(launch_gemm(g1, d->dtype, st)); }
+  if (!L->proj_silu && Zsave) {
+    // without the nonlinearity Z and Zh coincide
+    GemmArgs gz = g1;
+    gz.C = Zsave;
+    HSTU_TRY(launch_gemm(gz, d->dtype, st));
+  }
+  // 2. attention on the V, Q, K column blocks (q, k, v, ld; O fp32)
+  hstu_status s = attention(zh + 2 * W * es, zh + (2 * W + HQ) * es, zh + W * es, F1);
+  if (s != HSTU_OK) return s;
+  // 3. G = LN(O) * U
+  LnArgs la;
+  la.o_f32 = true;
+  la.T = T;
+  la.W = (int)W;
+  la.O = O;
+  la.ld_o = W;
+  la.U = Zh;
+  la.ld_u = F1;
+  la.gamma = w->ln_gamma;
+  la.beta = w->ln_beta;
+  la.eps = L->ln_eps;
+  la.G = G;
+  la.ld_g = W;
+  la.mu = mu;
+  la.rstd = rstd;
+  { HSTU_TIMED(TT_LN_FWD, st); HSTU_TRY(launch_ln_gate_fwd(la, d->dtype, st)); }
+  // 4. Y = G W2 (+ b2) (+ X)
+  GemmArgs g2;
+  g2.M = T;
+  g2.N = D;
+  g2.K = W;
+  g2.A = G;
+  g2.lda = W;
+  g2.a_kcont = true;
+  g2.B = w->W2;
+  g2.ldb = D;
+  g2.b_kcont = false;
+  g2.C = y;
+  g2.ldc = D;
+  g2.epi = EPI_RESID;
+  g2.bias = w->b2;
+  g2.R = L->residual ? x : nullptr;
+  g2.ldr = D;
+  { HSTU_TIMED(TT_GEMM_OUT, st); HSTU_TRY(launch_gemm(g2, d->dtype, st)); }
+  return HSTU_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,6 +483,37 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* d, const void* q, const void* k,
                        (hipStream_t)stream);
 }
 
+size_t hstu_attn_cached_workspace_size(const hstu_attn_desc* d, int64_t T_hist) {
+  if (check_attn_desc(d) != HSTU_OK || T_hist < 0) return 0;
+  Carver c(nullptr);
+  carve_cached(c, d, T_hist);
+  return c.off + 256;
+}
+
+hstu_status hstu_attn_cached_fwd(const hstu_attn_desc* d, const void* q, const void* k,
+                                 int64_t ld_qk, const void* v, int64_t ld_v, const int32_t* coffs,
+                                 const int64_t* cts, const hstu_history_kv* hist,
+                                 const float* rp, const float* rt, void* out, int64_t ld_out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  hstu_status s = check_attn_desc(d);
+  if (s != HSTU_OK) return s;
+  s = check_history(d, hist);
+  if (s != HSTU_OK) return s;
+  if (d->T > 0 && (!q || !k || !v || !out || !cts)) return HSTU_ERR_INVALID_ARG;
+  if (!coffs || !rp || !rt || !ws) return HSTU_ERR_INVALID_ARG;
+  const int64_t hq = (int64_t)d->H * d->d_qk, hv = (int64_t)d->H * d->d_v;
+  if (d->T > 0 && (!stride_ok(d->dtype, q, ld_qk, hq) || !stride_ok(d->dtype, k, ld_qk, hq) ||
+                   !stride_ok(d->dtype, v, ld_v, hv) || ld_out < hv))
+    return HSTU_ERR_INVALID_ARG;
+  // fp32 outputs are written four at a time
+  if (d->T > 0 && d->dtype == HSTU_F32 && (!aligned16(out) || ld_out % 4 != 0))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_attn_cached_workspace_size(d, hist->T)) return HSTU_ERR_WORKSPACE;
+  return attn_cached_impl(d, q, k, ld_qk, v, ld_v, coffs, cts, hist, rp, rt, out, ld_out, false,
+                          ws, (hipStream_t)stream);
+}
+
 hstu_status hstu_attn_bwd(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
                           const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
                           const float* rp, const float* rt, const int32_t* nc, const void* dout,
@@ -355,8 +560,13 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
     return HSTU_ERR_INVALID_ARG;
   if (d->T > 0 && (!x || !y || !ts)) return HSTU_ERR_INVALID_ARG;
   if (x == y && d->T > 0) return HSTU_ERR_INVALID_ARG;
-  if (saved && (!saved->Z || !saved->Zh || !saved->O || !saved->G || !saved->mu || !saved->rstd))
-    return HSTU_ERR_INVALID_ARG;
+  // saved: every buffer (training), or Zh alone (keeping U|V|Q|K, e.g. the
+  // keys and values of a history for later cached ranking)
+  const bool full = saved && saved->Z && saved->Zh && saved->O && saved->G && saved->mu &&
+                    saved->rstd;
+  const bool zh_only = saved && saved->Zh && !saved->Z && !saved->O && !saved->G &&
+                       !saved->mu && !saved->rstd;
+  if (saved && !full && !zh_only) return HSTU_ERR_INVALID_ARG;
   if (d->dtype == HSTU_BF16) {
     if (!aligned16(x) || !aligned16(y) || !aligned16(w->W1) || !aligned16(w->W2))
       return HSTU_ERR_INVALID_ARG;
@@ -364,87 +574,59 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
       return HSTU_ERR_INVALID_ARG;
   }
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
-  if (ws_bytes < hstu_layer_fwd_workspace_size(L, saved != nullptr)) return HSTU_ERR_WORKSPACE;
+  if (ws_bytes < hstu_layer_fwd_workspace_size(L, full)) return HSTU_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
 
   Carver c(ws);
-  LayerFwdWs lw = carve_layer_fwd(c, L, saved != nullptr);
-  const int64_t T = d->T, D = L->D, F1 = f1_width(L);
-  const int64_t W = (int64_t)d->H * d->d_v, HQ = (int64_t)d->H * d->d_qk;
+  LayerFwdWs lw = carve_layer_fwd(c, L, full);
+  const int64_t W = (int64_t)d->H * d->d_v;
   void* Zh = saved ? saved->Zh : lw.Zh;
-  void* O = saved ? saved->O : lw.O;
-  void* G = saved ? saved->G : lw.G;
-  const size_t es = esize(d->dtype);
-  char* zh = static_cast<char*>(Zh);
+  float* O = full ? saved->O : static_cast<float*>(lw.O);
+  void* G = full ? saved->G : lw.G;
+  auto attention = [&](const void* q, const void* k, const void* v, int64_t ld) {
+    return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, O, W,
+                         /*out_f32=*/true, lw.attn, st);
+  };
+  return layer_fwd_steps(L, x, w, y, full ? saved->Z : nullptr, Zh, O, G,
+                         full ? saved->mu : nullptr, full ? saved->rstd : nullptr, attention, st);
+}
 
-  // 1. Z = X W1 (+ b1); Zh = SiLU(Z)
-  GemmArgs g1;
-  g1.M = T;
-  g1.N = F1;
-  g1.K = D;
-  g1.A = x;
-  g1.lda = D;
-  g1.a_kcont = true;
-  g1.B = w->W1;
-  g1.ldb = F1;
-  g1.b_kcont = false;
-  g1.C = Zh;
-  g1.ldc = F1;
-  g1.bias = w->b1;
-  if (L->proj_silu) {
-    g1.epi = EPI_SILU;
-    g1.C2 = saved ? saved->Z : nullptr;
-  } else {
-    g1.epi = EPI_RESID;  // bias only
-    g1.R = nullptr;
-  }
-  { HSTU_TIMED(TT_GEMM_UVQK, st); HSTU_TRY(launch_gemm(g1, d->dtype, st)); }
-  if (!L->proj_silu && saved) {
-    // without the nonlinearity Z and Zh coincide
-    GemmArgs gz = g1;
-    gz.C = saved->Z;
-    HSTU_TRY(launch_gemm(gz, d->dtype, st));
-  }
-  // 2. attention on the V, Q, K column blocks
-  s = attn_fwd_impl(d, zh + 2 * W * es, zh + (2 * W + HQ) * es, F1, zh + W * es, F1, offs, ts,
-                    w->rab_pos, w->rab_time, nc, O, W, /*out_f32=*/true, lw.attn, st);
+size_t hstu_layer_cached_workspace_size(const hstu_layer_desc* L, int64_t T_hist) {
+  if (check_layer(L) != HSTU_OK || T_hist < 0) return 0;
+  Carver c(nullptr);
+  carve_layer_cached(c, L, T_hist);
+  return c.off + 256;
+}
+
+hstu_status hstu_layer_fwd_cached(const hstu_layer_desc* L, const void* x,
+                                  const hstu_layer_weights* w, const int32_t* coffs,
+                                  const int64_t* cts, const hstu_history_kv* hist, void* y,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  hstu_status s = check_layer(L);
   if (s != HSTU_OK) return s;
-  // 3. G = LN(O) * U
-  LnArgs la;
-  la.o_f32 = true;
-  la.T = T;
-  la.W = (int)W;
-  la.O = O;
-  la.ld_o = W;
-  la.U = Zh;
-  la.ld_u = F1;
-  la.gamma = w->ln_gamma;
-  la.beta = w->ln_beta;
-  la.eps = L->ln_eps;
-  la.G = G;
-  la.ld_g = W;
-  la.mu = saved ? saved->mu : nullptr;
-  la.rstd = saved ? saved->rstd : nullptr;
-  { HSTU_TIMED(TT_LN_FWD, st); HSTU_TRY(launch_ln_gate_fwd(la, d->dtype, st)); }
-  // 4. Y = G W2 (+ b2) (+ X)
-  GemmArgs g2;
-  g2.M = T;
-  g2.N = D;
-  g2.K = W;
-  g2.A = G;
-  g2.lda = W;
-  g2.a_kcont = true;
-  g2.B = w->W2;
-  g2.ldb = D;
-  g2.b_kcont = false;
-  g2.C = y;
-  g2.ldc = D;
-  g2.epi = EPI_RESID;
-  g2.bias = w->b2;
-  g2.R = L->residual ? x : nullptr;
-  g2.ldr = D;
-  { HSTU_TIMED(TT_GEMM_OUT, st); HSTU_TRY(launch_gemm(g2, d->dtype, st)); }
-  return HSTU_OK;
+  const hstu_attn_desc* d = &L->attn;
+  s = check_history(d, hist);
+  if (s != HSTU_OK) return s;
+  if (!w || !w->W1 || !w->W2 || !w->rab_pos || !w->rab_time || !coffs || !ws)
+    return HSTU_ERR_INVALID_ARG;
+  if (d->T > 0 && (!x || !y || !cts)) return HSTU_ERR_INVALID_ARG;
+  if (x == y && d->T > 0) return HSTU_ERR_INVALID_ARG;
+  if (d->dtype == HSTU_BF16 &&
+      (!aligned16(x) || !aligned16(y) || !aligned16(w->W1) || !aligned16(w->W2)))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_layer_cached_workspace_size(L, hist->T)) return HSTU_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+
+  Carver c(ws);
+  LayerFwdWs lw = carve_layer_cached(c, L, hist->T);
+  const int64_t W = (int64_t)d->H * d->d_v;
+  float* O = static_cast<float*>(lw.O);
+  auto attention = [&](const void* q, const void* k, const void* v, int64_t ld) {
+    return attn_cached_impl(d, q, k, ld, v, ld, coffs, cts, hist, w->rab_pos, w->rab_time, O, W,
+                            /*out_f32=*/true, lw.attn, st);
+  };
+  return layer_fwd_steps(L, x, w, y, nullptr, lw.Zh, O, lw.G, nullptr, nullptr, attention, st);
 }
 
 hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,

@@ -183,6 +183,44 @@ int64_t ln_bwd_part_blocks(int64_t T);
 hipError_t launch_validate(int B, const int32_t* seq_offsets, const int32_t* num_cand,
                            int64_t T, int32_t* flag, hipStream_t st);
 
+// Ranking against a cached history: candidate rows (q, k, v: their own
+// projections) against the user's cached history keys and values.
+struct CachedArgs {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t ld_qk = 0, ld_v = 0;
+  const int32_t* cand_offsets = nullptr;
+  const int64_t* cand_ts = nullptr;
+  const void* kh = nullptr;
+  const void* vh = nullptr;
+  int64_t ld_kh = 0, ld_vh = 0;
+  const int32_t* hist_offsets = nullptr;
+  const int64_t* hist_ts = nullptr;
+  const int32_t* rel_h = nullptr;   // history times relative to the user's minimum
+  const int32_t* rel_c = nullptr;   // candidate times relative to the same minimum
+  const int32_t* flags = nullptr;   // per user: bit0 wide, bit1 history sorted
+  const int32_t* items = nullptr;   // work list over (user, candidate block)
+  const int32_t* counters = nullptr;
+  void* out = nullptr;
+  int64_t ld_out = 0;
+  bool out_f32 = false;
+  float* part = nullptr;            // [splits, Tc, H*d_v] partial sums when splits > 1
+  int64_t Tc = 0;
+  int splits = 1;
+  const float* rab_pos = nullptr;
+  const float* rab_time = nullptr;
+  int64_t rab_stride = 0;
+  int H = 0, nP = 0, nT = 0, norm_len = 1, win_local = 0, win_global = 0;
+};
+int attn_cached_block_rows(int dtype, int d_qk, int d_v);
+hipError_t launch_time_prepass_cached(int B, const int32_t* hist_offsets, const int64_t* hist_ts,
+                                      const int32_t* cand_offsets, const int64_t* cand_ts,
+                                      int32_t* rel_h, int32_t* rel_c, int32_t* flags,
+                                      hipStream_t st);
+hipError_t launch_attn_cached(const CachedArgs& a, int dtype, int d_qk, int d_v,
+                              int64_t max_items, hipStream_t st);
+
 // Attention truncation: segment offsets, row gather, gradient scatter.
 hipError_t launch_trunc_offsets(int B, const int32_t* seq_offsets, const int32_t* num_cand,
                                 int keep, int32_t* seg_offsets, hipStream_t st);

@@ -22,6 +22,7 @@ enum TimerTag {
   TT_LN_BWD,
   TT_REDUCE,
   TT_TRUNCATE,
+  TT_ATTN_CACHED,
   TT_COUNT
 };
 

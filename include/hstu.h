@@ -198,8 +198,11 @@ size_t hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc);
 /*
  * Y = HSTU layer(X) ([DLRMv4] "Model Architecture"; [GR]).  x, y: [T, D]
  * dtype, contiguous rows; y may not alias x.  saved == NULL: inference
- * (intermediates live in the workspace); otherwise every saved buffer is
- * required and written.
+ * (intermediates live in the workspace); saved with every buffer set: a
+ * training forward, all written (workspace sized with training = 1);
+ * saved with only Zh set: inference that keeps U|V|Q|K in Zh, e.g. the
+ * keys and values of a history for hstu_layer_fwd_cached (workspace sized
+ * with training = 0).
  */
 hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x,
                            const hstu_layer_weights* w,
@@ -220,6 +223,62 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const void* x,
                            const hstu_layer_saved* saved, const void* dy,
                            void* dx, const hstu_layer_grads* g,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- ranking against a cached history --------------------------------- */
+/*
+ * "DLRMv4 Brings Sequence-Based Recommendation Training to MLPerf", "Model
+ * Architecture": candidates are appended to the history and compared with
+ * it in one pass.  A history row never attends to a candidate, so each
+ * layer's history keys and values (and the history's layer outputs) do not
+ * depend on the candidates: computed once (hstu_layer_fwd over the history
+ * alone, keeping Zh), they let later candidate batches run through the
+ * layers alone.  Candidate r of user b sits at position n_h (the user's
+ * history length) and attends to every cached history key of the user
+ * (under semi-local windows: n_h - j < win_local or j < win_global) and to
+ * its own key; this equals the candidate rows of the target-aware pass over
+ * [history; candidates] when N is the fixed norm_len (norm_mode 0 only).
+ */
+
+/* One layer's cached history keys and values (device memory, caller-owned). */
+typedef struct {
+  const void* k;               /* [T, ld_k] dtype: H*d_qk key columns, head-major */
+  const void* v;               /* [T, ld_v] dtype: H*d_v value columns */
+  int64_t ld_k;                /* row strides in elements (bf16: multiples of 8) */
+  int64_t ld_v;
+  const int32_t* offsets;      /* [B+1] device int32: user b's history rows */
+  const int64_t* timestamps;   /* [T] device int64 seconds */
+  int64_t T;                   /* history rows = offsets[B] */
+} hstu_history_kv;
+
+/*
+ * O [T, ld_out] dtype (desc->T = candidate rows, desc->B = users) of the
+ * candidates against the cached history `hist` of the same users.  q, k, v:
+ * the candidates' own projections ([T, ld] views as in hstu_attn_fwd);
+ * cand_offsets [B+1], cand_timestamps [T] device arrays.  fp32 outputs must
+ * be 16-byte aligned with ld_out a multiple of 4.  Errors as hstu_attn_fwd;
+ * HSTU_ERR_UNSUPPORTED for norm_mode 1.
+ */
+size_t hstu_attn_cached_workspace_size(const hstu_attn_desc* desc, int64_t T_hist);
+hstu_status hstu_attn_cached_fwd(const hstu_attn_desc* desc, const void* q, const void* k,
+                                 int64_t ld_qk, const void* v, int64_t ld_v,
+                                 const int32_t* cand_offsets, const int64_t* cand_timestamps,
+                                 const hstu_history_kv* hist, const float* rab_pos,
+                                 const float* rab_time, void* out, int64_t ld_out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Y = HSTU layer over candidate rows x ([T, D], desc->T = candidate rows)
+ * with the attention against this layer's cached history (the K and V
+ * column blocks of the Zh that hstu_layer_fwd kept for the history).
+ * Inference only.  Errors as hstu_layer_fwd; HSTU_ERR_UNSUPPORTED for
+ * norm_mode 1.
+ */
+size_t hstu_layer_cached_workspace_size(const hstu_layer_desc* desc, int64_t T_hist);
+hstu_status hstu_layer_fwd_cached(const hstu_layer_desc* desc, const void* x,
+                                  const hstu_layer_weights* w, const int32_t* cand_offsets,
+                                  const int64_t* cand_timestamps, const hstu_history_kv* hist,
+                                  void* y, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* ---- attention truncation ---------------------------------------------- */
 /*

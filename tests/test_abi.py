@@ -121,7 +121,8 @@ def test_descriptor_layouts_match_the_header(tmp_path):
     if gcc is None:
         pytest.skip("no C compiler")
     structs = {"hstu_attn_desc": _lib.AttnDesc, "hstu_layer_desc": _lib.LayerDesc,
-               "hstu_layer_weights": _lib.LayerWeights}
+               "hstu_layer_weights": _lib.LayerWeights, "hstu_layer_saved": _lib.LayerSaved,
+               "hstu_layer_grads": _lib.LayerGrads, "hstu_history_kv": _lib.HistoryKV}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hstu.h"', "int main(void) {"]
     for cname, ct in structs.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -176,3 +177,25 @@ def test_truncation_argument_errors(L):
     assert s(2, -1, 4, 64, 1, p, p, p, p, None) == -1
     assert s(2, 10, 4, 6, 0, p, p, p, p, None) == -1    # fp32 rows of 24 bytes
     assert s(2, 10, 4, 64, 1, p, p, p, None, None) == -1  # NULL dx
+
+
+def test_cached_ranking_argument_errors(L):
+    """Host-side checks of the cached-history entry points (nothing is launched)."""
+    buf = C.create_string_buffer(1 << 20)
+    ws = C.c_void_p((C.addressof(buf) + 255) & ~255)
+    p = C.c_void_p(1 << 20)
+    hist = _lib.HistoryKV(p, p, 64, 64, p, p, 100)
+    d = _desc()
+    assert L.hstu_attn_cached_workspace_size(C.byref(d), 100) > 0
+    assert L.hstu_attn_cached_workspace_size(C.byref(d), -1) == 0
+    call = lambda d_, h_: L.hstu_attn_cached_fwd(C.byref(d_), p, p, 64, p, 64, p, p,
+                                                 None if h_ is None else C.byref(h_), p, p, p,
+                                                 64, ws, 1 << 19, None)
+    assert call(d, None) == -1                                   # no history
+    assert call(_desc(norm_mode=1), hist) == -2                  # N must be fixed
+    assert call(d, _lib.HistoryKV(p, p, 60, 64, p, p, 100)) == -1  # bf16 row stride
+    assert call(d, _lib.HistoryKV(None, p, 64, 64, p, p, 100)) == -1
+    assert call(d, _lib.HistoryKV(p, p, 64, 64, None, p, 100)) == -1
+    small = L.hstu_attn_cached_fwd(C.byref(d), p, p, 64, p, 64, p, p, C.byref(hist), p, p, p, 64,
+                                   ws, 16, None)
+    assert small == -3
