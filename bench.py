@@ -269,6 +269,99 @@ def bench_truncation(timer, reps=3):
     return out
 
 
+def bench_cached(timer, reps=5):
+    """Ranking workload (16 users x (4096 history + 512 candidates), 4 layers,
+    inference): the full target-aware pass against the cached path, which
+    runs the histories once (cache build) and then only the candidates."""
+    import numpy as np
+    import torch
+
+    import synth
+    from hstu_sequential_transduction_amd import binding as B
+    from hstu_sequential_transduction_amd import ranking as RK
+    cfg = synth.get_config(5)
+    inp = synth.make_inputs(cfg)
+    nc_h = inp.num_candidates
+    rows_h = np.concatenate([np.arange(inp.seq_offsets[b], inp.seq_offsets[b + 1] - nc_h[b])
+                             for b in range(cfg.B)])
+    rows_c = np.concatenate([np.arange(inp.seq_offsets[b + 1] - nc_h[b], inp.seq_offsets[b + 1])
+                             for b in range(cfg.B)])
+    n_hist = inp.lengths - nc_h
+    hist_off = np.concatenate([[0], np.cumsum(n_hist)]).astype(np.int32)
+    cand_off = np.concatenate([[0], np.cumsum(nc_h)]).astype(np.int32)
+    td = torch.bfloat16
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    X = cu(inp.X).to(td)
+    Xh, Xc = cu(inp.X[rows_h]).to(td), cu(inp.X[rows_c]).to(td)
+    offs, ts = cu(inp.seq_offsets.astype(np.int32)), cu(inp.timestamps)
+    nc = cu(nc_h.astype(np.int32))
+    h_off, h_ts = cu(hist_off), cu(inp.timestamps[rows_h])
+    c_off, c_ts = cu(cand_off), cu(inp.timestamps[rows_c])
+    lay = [tuple(upload_layer(inp, cfg, li).values()) for li in range(cfg.n_layers)]
+    ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len)
+    lc = B.LayerConfig(D=cfg.D, attn=ac)
+    ws = B.LayerWorkspace()
+    bufs = [torch.empty_like(X), torch.empty_like(X)]
+    cbufs = [torch.empty_like(Xc), torch.empty_like(Xc)]
+
+    def full():
+        x = X
+        for li, (W1, W2, rp, rt) in enumerate(lay):
+            x = B.hstu_layer_fwd(x, W1, W2, rp, rt, offs, ts, lc, num_candidates=nc,
+                                 y=bufs[li % 2], workspace=ws)
+
+    cache = RK.build_history_cache(Xh, lay, h_off, h_ts, lc, workspace=ws)
+
+    def build():
+        RK.build_history_cache(Xh, lay, h_off, h_ts, lc, workspace=ws)
+
+    def cand():
+        RK.cached_stack_fwd(Xc, lay, cache, c_off, c_ts, lc, workspace=ws, out_bufs=cbufs)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        timer.enable(64 * reps * cfg.n_layers)
+        timer.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        kern = timer.read()
+        timer.enable(0)
+        return e0.elapsed_time(e1) / reps, kern
+
+    ms_full, _ = timed(full)
+    ms_build, _ = timed(build)
+    ms_cand, kern = timed(cand)
+    # algorithmic work of the cached attention: every candidate x its history
+    # keys, plus its own key, 2 (d_qk + d_v) flops per pair and head
+    pairs = float(np.sum(nc_h * n_hist) + np.sum(nc_h))
+    attn_flops = 2.0 * pairs * cfg.H * (cfg.d_qk + cfg.d_v)
+    n_a, ms_a = kern.get("attn_cached", (0, 0.0))
+    a_ms = ms_a / max(n_a, 1)
+    a_tf = attn_flops / (a_ms * 1e-3) / 1e12 if n_a else None
+    Tc = int(cand_off[-1])
+    gemm = 2.0 * Tc * cfg.D * cfg.f1_width + 2.0 * Tc * cfg.H * cfg.d_v * cfg.D
+    tot = cfg.n_layers * (attn_flops + gemm)
+    out = {"workload": "ranking batch 16 x (4096 history + 512 candidates), d_model 256, "
+                       "4 heads x 64, 4 layers, bf16, inference",
+           "full_target_aware_ms": round(ms_full, 4),
+           "history_cache_build_ms": round(ms_build, 4),
+           "cached_candidates_ms": round(ms_cand, 4),
+           "speedup_vs_full": round(ms_full / ms_cand, 2),
+           "candidates_per_s": round(Tc / (ms_cand * 1e-3), 1),
+           "cached_tflops": round(tot / (ms_cand * 1e-3) / 1e12, 2),
+           "attn_cached_ms_per_launch": round(a_ms, 4),
+           "attn_cached_tflops": None if a_tf is None else round(a_tf, 2),
+           "attn_cached_frac_bf16_peak": None if a_tf is None else round(a_tf / PEAK_BF16_TFLOPS, 4),
+           "kernel_ms": {k: round(v[1] / reps, 4) for k, v in kern.items()}}
+    log(f"cached ranking: {out}")
+    return out
+
+
 def roofline(cfg, inp, kern, steps, traffic_dir):
     work = kernel_work(cfg, inp.lengths, inp.T)
     best = max(((ms, name, n) for name, (n, ms) in kern.items() if name in work), default=None)
@@ -405,8 +498,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the forward-only workloads, the semi-local training step and "
-                         "the attention-truncation forward")
+                    help="skip the forward-only workloads, the semi-local training step, "
+                         "the attention-truncation forward and the cached ranking")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
@@ -426,6 +519,7 @@ def main():
     extra = None if args.no_extra else bench_fwd_configs(timer)
     semi = None if args.no_extra else bench_semilocal(args, timer, ms)
     trunc = None if args.no_extra else bench_truncation(timer)
+    cached = None if args.no_extra else bench_cached(timer)
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, inp)
     line = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -445,6 +539,7 @@ def main():
         "forward_workloads": extra,
         "semilocal": semi,
         "truncation": trunc,
+        "cached_ranking": cached,
     }
     print(json.dumps(line), flush=True)
 

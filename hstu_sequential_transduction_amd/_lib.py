@@ -17,7 +17,7 @@ STATUS_NAMES = {0: "HSTU_OK", -1: "HSTU_ERR_INVALID_ARG", -2: "HSTU_ERR_UNSUPPOR
 HSTU_F32, HSTU_BF16 = 0, 1
 
 EXPORTED = [
-    "hstu_status_string", "hstu_version",
+    "hstu_status_string", "hstu_version", "hstu_last_hip_error",
     "hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size",
     "hstu_attn_fwd", "hstu_attn_bwd",
     "hstu_layer_fwd_workspace_size", "hstu_layer_bwd_workspace_size",
@@ -81,11 +81,19 @@ def lib() -> C.CDLL:
             f"{LIB_PATH} is missing: build it first "
             "(python -c 'import __graft_entry__ as g; g.build()' or "
             "python hstu_sequential_transduction_amd/build.py)")
+    # torch ships its own HIP runtime (torch/lib/libamdhip64.so, soname
+    # libamdhip64.so.7).  Loaded first, it satisfies this library's
+    # libamdhip64.so.7 dependency, so both share one runtime (and so one view
+    # of device memory and streams).  Loaded the other way round, the process
+    # would hold two HIP runtimes and the second would find no device.
+    import torch  # noqa: F401
     L = C.CDLL(LIB_PATH)
     vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     P = C.POINTER
     L.hstu_status_string.restype = C.c_char_p
     L.hstu_status_string.argtypes = [C.c_int]
+    L.hstu_last_hip_error.restype = C.c_char_p
+    L.hstu_last_hip_error.argtypes = []
     L.hstu_version.restype = C.c_char_p
     L.hstu_version.argtypes = []
     for f in ("hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size"):
@@ -152,6 +160,8 @@ class HstuError(RuntimeError):
         name = STATUS_NAMES.get(status, str(status))
         try:
             msg = lib().hstu_status_string(status).decode()
+            if status == -4:
+                msg += ": " + lib().hstu_last_hip_error().decode()
         except Exception:  # pragma: no cover
             msg = ""
         super().__init__(f"{fn} failed: {name} ({msg})")

@@ -15,11 +15,25 @@ using namespace hstu;
 
 namespace {
 
+// HIP error behind the calling thread's last HSTU_ERR_HIP (hstu_last_hip_error)
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
 #define HSTU_TRY(expr)                                  \
   do {                                                  \
     hipError_t e_ = (expr);                             \
-    if (e_ != hipSuccess) return HSTU_ERR_HIP;          \
+    if (e_ != hipSuccess) {                             \
+      g_last_hip_error = e_;                            \
+      return HSTU_ERR_HIP;                              \
+    }                                                   \
   } while (0)
+
+// Every entry point that launches work starts here: it clears an error that
+// an earlier HIP call of another library may have left behind, so that a
+// launch error the entry point reports is its own.
+hipStream_t entry_stream(void* stream) {
+  (void)hipGetLastError();
+  return (hipStream_t)stream;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 size_t esize(int dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
@@ -132,7 +146,7 @@ hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
 int cached_splits(const hstu_attn_desc* d, int64_t T_hist) {
   const int bm = attn_cached_block_rows(d->dtype, d->d_qk, d->d_v);
   const int64_t B = std::max<int64_t>(d->B, 1);
-  const int64_t items = d->T / bm + B;
+  const int64_t items = std::max<int64_t>((d->T + bm - 1) / bm, B);  // work items (estimate)
   const int64_t tile = d->dtype == HSTU_BF16 ? 64 : 32;
   const int64_t tiles_per_user = (T_hist / B + tile - 1) / tile;
   int64_t S = (512 + items * d->H - 1) / (items * d->H);
@@ -449,6 +463,8 @@ const char* hstu_status_string(hstu_status s) {
   return "unknown status";
 }
 
+const char* hstu_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
+
 const char* hstu_version(void) { return "hstu-mi355x 0.1 (gfx950)"; }
 
 size_t hstu_attn_fwd_workspace_size(const hstu_attn_desc* d) {
@@ -480,7 +496,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* d, const void* q, const void* k,
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_fwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
   return attn_fwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, false, ws,
-                       (hipStream_t)stream);
+                       entry_stream(stream));
 }
 
 size_t hstu_attn_cached_workspace_size(const hstu_attn_desc* d, int64_t T_hist) {
@@ -511,7 +527,7 @@ hstu_status hstu_attn_cached_fwd(const hstu_attn_desc* d, const void* q, const v
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_cached_workspace_size(d, hist->T)) return HSTU_ERR_WORKSPACE;
   return attn_cached_impl(d, q, k, ld_qk, v, ld_v, coffs, cts, hist, rp, rt, out, ld_out, false,
-                          ws, (hipStream_t)stream);
+                          ws, entry_stream(stream));
 }
 
 hstu_status hstu_attn_bwd(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
@@ -532,7 +548,7 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* d, const void* q, const void* k,
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_bwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
   return attn_bwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, dout, ld_dout, dq, dk, dv,
-                       drp, drt, nullptr, 0, 0, 0, 0, ws, (hipStream_t)stream);
+                       drp, drt, nullptr, 0, 0, 0, 0, ws, entry_stream(stream));
 }
 
 size_t hstu_layer_fwd_workspace_size(const hstu_layer_desc* L, int training) {
@@ -575,7 +591,7 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
   }
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_layer_fwd_workspace_size(L, full)) return HSTU_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
 
   Carver c(ws);
   LayerFwdWs lw = carve_layer_fwd(c, L, full);
@@ -616,7 +632,7 @@ hstu_status hstu_layer_fwd_cached(const hstu_layer_desc* L, const void* x,
     return HSTU_ERR_INVALID_ARG;
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_layer_cached_workspace_size(L, hist->T)) return HSTU_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
 
   Carver c(ws);
   LayerFwdWs lw = carve_layer_cached(c, L, hist->T);
@@ -651,7 +667,7 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
       !aligned16(saved->O) || !aligned16(saved->G) || !aligned16(ws))
     return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_layer_bwd_workspace_size(L)) return HSTU_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
 
   Carver c(ws);
   LayerBwdWs bw = carve_layer_bwd(c, L);
@@ -751,7 +767,7 @@ hstu_status hstu_schedule(int32_t B, int64_t T, const int32_t* offs, int32_t blo
       !n_items || !ws)
     return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_schedule_workspace_size(B, T, block_rows)) return HSTU_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
   Carver c(ws);
   Sched sc = carve_sched(c, T, B, block_rows);
   HSTU_TRY(launch_sched(sc, B, offs, reverse, st));
@@ -770,7 +786,7 @@ hstu_status hstu_bias_buckets(const hstu_attn_desc* d, const int32_t* offs, cons
   if (!offs || !ws || n_pairs < 0) return HSTU_ERR_INVALID_ARG;
   if (n_pairs > 0 && (!ts || !ps || !pi || !pj || !bp || !bt)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_fwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
   Carver c(ws);
   FwdWs w = carve_fwd(c, d);
   AttnArgs a = base_args(d, nullptr, nullptr, 0, nullptr, 0, offs, ts, nullptr, nullptr, nc, w.tm);
@@ -782,7 +798,7 @@ hstu_status hstu_bias_buckets(const hstu_attn_desc* d, const int32_t* offs, cons
 hstu_status hstu_truncate_offsets(int32_t B, const int32_t* offs, const int32_t* nc,
                                   int32_t keep, int32_t* seg, void* stream) {
   if (B < 0 || keep < 0 || !offs || !seg) return HSTU_ERR_INVALID_ARG;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
   { HSTU_TIMED(TT_TRUNCATE, st); HSTU_TRY(launch_trunc_offsets(B, offs, nc, keep, seg, st)); }
   return HSTU_OK;
 }
@@ -795,7 +811,7 @@ hstu_status hstu_truncate_gather(int32_t B, int64_t T, int64_t T_seg, int32_t D,
   hstu_status s = check_trunc_copy(B, T, T_seg, D, dtype, x, x_seg, offs, seg);
   if (s != HSTU_OK) return s;
   if (T_seg > 0 && (ts == nullptr) != (ts_seg == nullptr)) return HSTU_ERR_INVALID_ARG;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
   HSTU_TIMED(TT_TRUNCATE, st);
   HSTU_TRY(launch_trunc_gather(B, T, T_seg, int64_t(D) * esize(dtype), offs, seg, x, x_seg, ts,
                                ts_seg, st));
@@ -807,7 +823,7 @@ hstu_status hstu_truncate_scatter(int32_t B, int64_t T, int64_t T_seg, int32_t D
                                   void* dx, void* stream) {
   hstu_status s = check_trunc_copy(B, T, T_seg, D, dtype, dx, dx_seg, offs, seg);
   if (s != HSTU_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
   HSTU_TIMED(TT_TRUNCATE, st);
   HSTU_TRY(launch_trunc_scatter(B, T, T_seg, int64_t(D) * esize(dtype), offs, seg, dx_seg, dx,
                                 st));
@@ -817,7 +833,7 @@ hstu_status hstu_truncate_scatter(int32_t B, int64_t T, int64_t T_seg, int32_t D
 hstu_status hstu_validate_inputs(int32_t B, int64_t T, const int32_t* offs, const int32_t* nc,
                                  int32_t* flag_ws, void* stream) {
   if (B < 0 || T < 0 || !offs || !flag_ws) return HSTU_ERR_INVALID_ARG;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = entry_stream(stream);
   HSTU_TRY(launch_zero_i32(flag_ws, 1, st));
   HSTU_TRY(launch_validate(B, offs, nc, T, flag_ws, st));
   int32_t h = 0;

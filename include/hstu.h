@@ -148,6 +148,8 @@ typedef struct {
 } hstu_layer_grads;
 
 const char* hstu_status_string(hstu_status s);
+/* Text of the HIP error behind the calling thread's last HSTU_ERR_HIP. */
+const char* hstu_last_hip_error(void);
 /* Library version string. */
 const char* hstu_version(void);
 
