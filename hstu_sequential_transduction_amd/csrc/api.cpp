@@ -134,8 +134,12 @@ hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   a.out_f32 = out_f32;
   a.items = w.sc.items;
   a.counters = w.sc.counters;
-  { HSTU_TIMED(TT_PREPASS, st); HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st)); }
-  { HSTU_TIMED(TT_SCHED, st); HSTU_TRY(launch_sched(w.sc, d->B, offs, 0, st)); }
+  {
+    HSTU_TIMED(TT_PREPASS, st);
+    PlanArgs p = plan_prepass(w.tm, d->B, offs, ts);
+    plan_add_job(p, w.sc, 0, offs);
+    HSTU_TRY(launch_plan(p, st));
+  }
   { HSTU_TIMED(TT_ATTN_FWD, st); HSTU_TRY(launch_attn_fwd(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st)); }
   return HSTU_OK;
 }
@@ -194,10 +198,20 @@ hstu_status attn_cached_impl(const hstu_attn_desc* d, const void* q, const void*
   a.win_local = d->win_local; a.win_global = d->win_global;
   {
     HSTU_TIMED(TT_PREPASS, st);
-    HSTU_TRY(launch_time_prepass_cached(d->B, hist->offsets, hist->timestamps, coffs, cts,
-                                        w.rel_h, w.rel_c, w.flags, st));
+    PlanArgs p;
+    p.npre = d->B;
+    p.mode = 1;
+    p.offs = hist->offsets;
+    p.ts = hist->timestamps;
+    p.rel_t = w.rel_h;
+    p.flags = w.flags;
+    p.coffs = coffs;
+    p.cts = cts;
+    p.rel_c = w.rel_c;
+    p.B = d->B;
+    plan_add_job(p, w.sc, 0, coffs);
+    HSTU_TRY(launch_plan(p, st));
   }
-  { HSTU_TIMED(TT_SCHED, st); HSTU_TRY(launch_sched(w.sc, d->B, coffs, 0, st)); }
   {
     HSTU_TIMED(TT_ATTN_CACHED, st);
     HSTU_TRY(launch_attn_cached(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st));
@@ -240,11 +254,10 @@ hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   a.zv_col = zv;
   {
     HSTU_TIMED(TT_PREPASS, st);
-    HSTU_TRY(launch_time_prepass(w.tm, d->B, offs, ts, st, drp, drt, rab_floats(d)));
-  }
-  {
-    HSTU_TIMED(TT_SCHED, st);
-    HSTU_TRY(launch_sched2(w.kv, 1, w.q, 0, d->B, offs, st));
+    PlanArgs p = plan_prepass(w.tm, d->B, offs, ts, drp, drt, rab_floats(d));
+    plan_add_job(p, w.kv, 1, offs);
+    plan_add_job(p, w.q, 0, offs);
+    HSTU_TRY(launch_plan(p, st));
   }
   AttnArgs akv = a;
   akv.items = w.kv.items;

@@ -59,62 +59,6 @@ template <bool V>
 using bconst = std::integral_constant<bool, V>;
 
 // ---------------------------------------------------------------------------
-// Time pre-pass: one workgroup per user over its history and candidate
-// times: relative times (32-bit) when the span allows, the "wide" flag
-// otherwise, and whether the history times are non-decreasing.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_time_prepass_cached(
-    const int32_t* __restrict__ hoffs, const int64_t* __restrict__ hts,
-    const int32_t* __restrict__ coffs, const int64_t* __restrict__ cts,
-    int32_t* __restrict__ rel_h, int32_t* __restrict__ rel_c, int32_t* __restrict__ flags) {
-  __shared__ int64_t smin[16], smax[16];
-  __shared__ int sunsorted[16];
-  const int b = blockIdx.x;
-  const int64_t h0 = hoffs[b], h1 = hoffs[b + 1], c0 = coffs[b], c1 = coffs[b + 1];
-  int64_t mn = INT64_MAX, mx = INT64_MIN;
-  int unsorted = 0;
-  for (int64_t r = h0 + threadIdx.x; r < h1; r += 1024) {
-    const int64_t t = hts[r];
-    mn = t < mn ? t : mn;
-    mx = t > mx ? t : mx;
-    if (r > h0 && t < hts[r - 1]) unsorted = 1;
-  }
-  for (int64_t r = c0 + threadIdx.x; r < c1; r += 1024) {
-    const int64_t t = cts[r];
-    mn = t < mn ? t : mn;
-    mx = t > mx ? t : mx;
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    const int64_t x = __shfl_xor(mn, o, 64), y = __shfl_xor(mx, o, 64);
-    mn = x < mn ? x : mn;
-    mx = y > mx ? y : mx;
-    unsorted |= __shfl_xor(unsorted, o, 64);
-  }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
-    smin[w] = mn;
-    smax[w] = mx;
-    sunsorted[w] = unsorted;
-  }
-  __syncthreads();
-  mn = smin[0];
-  mx = smax[0];
-  unsorted = sunsorted[0];
-  for (int i = 1; i < 16; ++i) {
-    mn = smin[i] < mn ? smin[i] : mn;
-    mx = smax[i] > mx ? smax[i] : mx;
-    unsorted |= sunsorted[i];
-  }
-  const bool any = (h1 > h0) || (c1 > c0);
-  const bool wide = any && (mx - mn > HSTU_NARROW_SPAN_MAX);
-  for (int64_t r = h0 + threadIdx.x; r < h1; r += 1024)
-    rel_h[r] = wide ? 0 : (int32_t)(hts[r] - mn);
-  for (int64_t r = c0 + threadIdx.x; r < c1; r += 1024)
-    rel_c[r] = wide ? 0 : (int32_t)(cts[r] - mn);
-  if (threadIdx.x == 0) flags[b] = (wide ? 1 : 0) | (unsorted ? 0 : 2);
-}
-
-// ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
 template <int DQK, int DV, bool WIN>
@@ -572,14 +516,6 @@ hipError_t launch_cached_dv(const CachedArgs& a, int dtype, int d_v, int64_t mi,
 int attn_cached_block_rows(int dtype, int d_qk, int d_v) {
   if (dtype != HSTU_BF16) return ATTN_FWD_BM_F32;
   return (d_qk <= 64 && d_v <= 64) ? CShape<64, 64>::BM : CShape<128, 128>::BM;
-}
-
-hipError_t launch_time_prepass_cached(int B, const int32_t* hoffs, const int64_t* hts,
-                                      const int32_t* coffs, const int64_t* cts, int32_t* rel_h,
-                                      int32_t* rel_c, int32_t* flags, hipStream_t st) {
-  if (B <= 0) return hipSuccess;
-  k_time_prepass_cached<<<B, 1024, 0, st>>>(hoffs, hts, coffs, cts, rel_h, rel_c, flags);
-  return hipGetLastError();
 }
 
 hipError_t launch_attn_cached(const CachedArgs& a, int dtype, int d_qk, int d_v,

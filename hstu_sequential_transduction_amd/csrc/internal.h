@@ -43,9 +43,6 @@ inline int64_t sched_capacity(int64_t T, int64_t B, int block_rows) {
 Sched carve_sched(Carver& c, int64_t T, int64_t B, int block_rows);
 hipError_t launch_sched(const Sched& s, int B, const int32_t* seq_offsets, int reverse,
                         hipStream_t st);
-// two schedules of the same sequences in one launch (one workgroup each)
-hipError_t launch_sched2(const Sched& s0, int reverse0, const Sched& s1, int reverse1, int B,
-                         const int32_t* seq_offsets, hipStream_t st);
 
 // Per-token relative timestamps and per-sequence flags.
 struct TimeMeta {
@@ -57,6 +54,45 @@ TimeMeta carve_time(Carver& c, int64_t T, int64_t B);
 hipError_t launch_time_prepass(const TimeMeta& tm, int B, const int32_t* seq_offsets,
                                const int64_t* ts, hipStream_t st, float* z0 = nullptr,
                                float* z1 = nullptr, int64_t nz = 0);
+
+// One schedule to build: its arrays, block rows and order.
+struct SchedJob {
+  int32_t* items = nullptr;
+  int32_t* counters = nullptr;
+  int32_t* hist = nullptr;
+  int32_t* cnt = nullptr;
+  int32_t* levelstart = nullptr;
+  int32_t* tie = nullptr;
+  int cap = 0, bm = 1, reverse = 0;
+};
+
+// A call's plan in one launch: the time pre-pass over npre sequences (mode
+// 0: one timestamp array; mode 1: a user's history offs/ts and candidates
+// coffs/cts) and up to two work lists over sched_offs.
+struct PlanArgs {
+  int npre = 0;
+  int mode = 0;
+  const int32_t* offs = nullptr;
+  const int64_t* ts = nullptr;
+  int32_t* rel_t = nullptr;
+  int32_t* flags = nullptr;
+  const int32_t* coffs = nullptr;
+  const int64_t* cts = nullptr;
+  int32_t* rel_c = nullptr;
+  float* z0 = nullptr;
+  float* z1 = nullptr;
+  int64_t nz = 0;
+  int B = 0;
+  const int32_t* sched_offs = nullptr;
+  int njobs = 0;
+  int lds_sched = 0;
+  SchedJob job[2];
+};
+PlanArgs plan_prepass(const TimeMeta& tm, int B, const int32_t* seq_offsets,
+                      const int64_t* ts, float* z0 = nullptr, float* z1 = nullptr,
+                      int64_t nz = 0);
+void plan_add_job(PlanArgs& p, const Sched& s, int reverse, const int32_t* sched_offs);
+hipError_t launch_plan(PlanArgs p, hipStream_t st);
 
 struct AttnArgs {
   const void* q = nullptr;
@@ -214,10 +250,6 @@ struct CachedArgs {
   int H = 0, nP = 0, nT = 0, norm_len = 1, win_local = 0, win_global = 0;
 };
 int attn_cached_block_rows(int dtype, int d_qk, int d_v);
-hipError_t launch_time_prepass_cached(int B, const int32_t* hist_offsets, const int64_t* hist_ts,
-                                      const int32_t* cand_offsets, const int64_t* cand_ts,
-                                      int32_t* rel_h, int32_t* rel_c, int32_t* flags,
-                                      hipStream_t st);
 hipError_t launch_attn_cached(const CachedArgs& a, int dtype, int d_qk, int d_v,
                               int64_t max_items, hipStream_t st);
 

@@ -44,34 +44,14 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Timestamp pre-pass: one workgroup per sequence.
+// Timestamp pre-pass: one workgroup per sequence (or per user of a cached
+// history: its history and candidate times together).  Relative times
+// t - min fit in int32 unless the span is "wide"; bit 1 of the flags says
+// the (history) times are non-decreasing.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_time_prepass(const int32_t* __restrict__ offs,
-                                                       const int64_t* __restrict__ ts,
-                                                       int32_t* __restrict__ rel_t,
-                                                       int32_t* __restrict__ flags,
-                                                       float* __restrict__ z0,
-                                                       float* __restrict__ z1, int64_t nz) {
+__device__ void minmax_reduce(int64_t& mn, int64_t& mx, int& unsorted) {
   __shared__ int64_t smin[16], smax[16];
   __shared__ int sunsorted[16];
-  const int b = blockIdx.x;
-  // the backward's rab-gradient accumulators, cleared by the grid on the way
-  for (int64_t i = (int64_t)b * 1024 + threadIdx.x; i < nz; i += (int64_t)gridDim.x * 1024) {
-    z0[i] = 0.0f;
-    z1[i] = 0.0f;
-  }
-  const int64_t o0 = offs[b], o1 = offs[b + 1];
-  int64_t mn = INT64_MAX, mx = INT64_MIN;
-  int unsorted = 0;
-  // 1024 threads, four strided loads in flight per thread: a few memory round
-  // trips per sequence rather than one per 256 tokens
-#pragma unroll 4
-  for (int64_t r = o0 + threadIdx.x; r < o1; r += 1024) {
-    const int64_t t = ts[r];
-    mn = t < mn ? t : mn;
-    mx = t > mx ? t : mx;
-    if (r > o0 && t < ts[r - 1]) unsorted = 1;
-  }
   for (int o = 32; o > 0; o >>= 1) {
     const int64_t a = __shfl_xor(mn, o, 64), c = __shfl_xor(mx, o, 64);
     mn = a < mn ? a : mn;
@@ -93,11 +73,53 @@ __global__ __launch_bounds__(1024) void k_time_prepass(const int32_t* __restrict
     mx = smax[i] > mx ? smax[i] : mx;
     unsorted |= sunsorted[i];
   }
+}
+
+__device__ void prepass_seq(int b, const PlanArgs& p) {
+  const int64_t o0 = p.offs[b], o1 = p.offs[b + 1];
+  int64_t mn = INT64_MAX, mx = INT64_MIN;
+  int unsorted = 0;
+  // 1024 threads, four strided loads in flight per thread: a few memory round
+  // trips per sequence rather than one per 256 tokens
+#pragma unroll 4
+  for (int64_t r = o0 + threadIdx.x; r < o1; r += 1024) {
+    const int64_t t = p.ts[r];
+    mn = t < mn ? t : mn;
+    mx = t > mx ? t : mx;
+    if (r > o0 && t < p.ts[r - 1]) unsorted = 1;
+  }
+  minmax_reduce(mn, mx, unsorted);
   const bool wide = (o1 > o0) && (mx - mn > HSTU_NARROW_SPAN_MAX);
 #pragma unroll 4
   for (int64_t r = o0 + threadIdx.x; r < o1; r += 1024)
-    rel_t[r] = wide ? 0 : (int32_t)(ts[r] - mn);
-  if (threadIdx.x == 0) flags[b] = (wide ? 1 : 0) | (unsorted ? 0 : 2);
+    p.rel_t[r] = wide ? 0 : (int32_t)(p.ts[r] - mn);
+  if (threadIdx.x == 0) p.flags[b] = (wide ? 1 : 0) | (unsorted ? 0 : 2);
+}
+
+__device__ void prepass_user(int b, const PlanArgs& p) {
+  const int64_t h0 = p.offs[b], h1 = p.offs[b + 1], c0 = p.coffs[b], c1 = p.coffs[b + 1];
+  int64_t mn = INT64_MAX, mx = INT64_MIN;
+  int unsorted = 0;
+#pragma unroll 4
+  for (int64_t r = h0 + threadIdx.x; r < h1; r += 1024) {
+    const int64_t t = p.ts[r];
+    mn = t < mn ? t : mn;
+    mx = t > mx ? t : mx;
+    if (r > h0 && t < p.ts[r - 1]) unsorted = 1;
+  }
+  for (int64_t r = c0 + threadIdx.x; r < c1; r += 1024) {
+    const int64_t t = p.cts[r];
+    mn = t < mn ? t : mn;
+    mx = t > mx ? t : mx;
+  }
+  minmax_reduce(mn, mx, unsorted);
+  const bool wide = (h1 > h0 || c1 > c0) && (mx - mn > HSTU_NARROW_SPAN_MAX);
+#pragma unroll 4
+  for (int64_t r = h0 + threadIdx.x; r < h1; r += 1024)
+    p.rel_t[r] = wide ? 0 : (int32_t)(p.ts[r] - mn);
+  for (int64_t r = c0 + threadIdx.x; r < c1; r += 1024)
+    p.rel_c[r] = wide ? 0 : (int32_t)(p.cts[r] - mn);
+  if (threadIdx.x == 0) p.flags[b] = (wide ? 1 : 0) | (unsorted ? 0 : 2);
 }
 
 TimeMeta carve_time(Carver& c, int64_t T, int64_t B) {
@@ -107,96 +129,86 @@ TimeMeta carve_time(Carver& c, int64_t T, int64_t B) {
   return m;
 }
 
-hipError_t launch_time_prepass(const TimeMeta& tm, int B, const int32_t* offs,
-                               const int64_t* ts, hipStream_t st, float* z0, float* z1,
-                               int64_t nz) {
-  if (B <= 0) {
-    if (nz > 0) {
-      hipError_t e = launch_zero_f32(z0, nz, st);
-      if (e == hipSuccess) e = launch_zero_f32(z1, nz, st);
-      return e;
-    }
-    return hipSuccess;
-  }
-  k_time_prepass<<<B, 1024, 0, st>>>(offs, ts, tm.rel_t, tm.seq_flags, z0, z1, nz);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // Work list.
 // ---------------------------------------------------------------------------
-// Exclusive suffix sum of in[0..len) into out[0..len) by one workgroup of 1024.
+// Exclusive suffix sum of in[0..len) into out[0..len) by one workgroup of
+// 1024: contiguous chunks per thread, suffix scans inside each wave by
+// shuffles, wave totals through LDS (two barriers).
 __device__ void block_suffix_excl(const int32_t* in, int32_t* out, int len, int32_t* total) {
-  __shared__ int32_t part[1024];
-  const int t = threadIdx.x;
+  __shared__ int32_t wsum[16];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int chunk = (len + 1023) / 1024;
-  const int lo = t * chunk, hi = min(len, lo + chunk);
+  const int lo = min(t * chunk, len), hi = min(len, lo + chunk);
   int s = 0;
   for (int i = lo; i < hi; ++i) s += in[i];
-  part[t] = s;
-  __syncthreads();
-  // inclusive suffix scan of part[] (Hillis-Steele)
-  for (int o = 1; o < 1024; o <<= 1) {
-    int v = (t + o < 1024) ? part[t + o] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
+  int x = s;  // inclusive suffix sum over the lanes >= this one
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(x, o, 64);
+    if (lane + o < 64) x += y;
   }
-  int acc = (t + 1 < 1024) ? part[t + 1] : 0;  // sum of later chunks
+  if (lane == 0) wsum[w] = x;
+  __syncthreads();
+  int later = 0;  // totals of the later waves
+  for (int v = w + 1; v < 16; ++v) later += wsum[v];
+  int acc = x - s + later;  // sum over the later threads' chunks
   for (int i = hi - 1; i >= lo; --i) {
-    int v = in[i];
+    const int v = in[i];
     out[i] = acc;
     acc += v;
   }
-  if (t == 0 && total) *total = part[0];
+  if (t == 0 && total) *total = x + later;
   __syncthreads();
 }
 
-// One workgroup builds one schedule (the launch carries one or two): clear,
-// count sequences per block count, the two suffix sums, then the items.  The
-// steps communicate through global memory inside the workgroup, so each is
-// separated by a barrier and an agent-scope acquire (the vector L1 holds no
-// stale line of what other threads wrote or atomically updated).
-struct SchedJob {
-  int32_t* items;
-  int32_t* counters;
-  int32_t* hist;
-  int32_t* cnt;
-  int32_t* levelstart;
-  int32_t* tie;
-  int cap, bm, reverse;
-};
-
+// The steps communicate through memory inside the workgroup (LDS, or global
+// memory for long lists), so each is separated by a barrier and an
+// agent-scope acquire (the vector L1 then holds no stale line).
 __device__ void sched_step_barrier() {
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-__global__ __launch_bounds__(1024) void k_sched(int B, const int32_t* __restrict__ offs,
-                                                SchedJob j0, SchedJob j1) {
-  const SchedJob j = blockIdx.x == 0 ? j0 : j1;
+// One workgroup builds one schedule: clear, count sequences per block count,
+// the two suffix sums, then the items.  `lds` (4 (cap + 2) ints) replaces
+// the job's global scratch arrays when given.
+__device__ void build_schedule(int B, const int32_t* __restrict__ offs, const SchedJob& jg,
+                               int32_t* lds) {
+  SchedJob j = jg;
+  if (lds) {
+    const int E = j.cap + 2;
+    j.hist = lds;
+    j.cnt = lds + E;
+    j.levelstart = lds + 2 * E;
+    j.tie = lds + 3 * E;
+  }
+  __shared__ int32_t s_maxblk, s_items;
   const int t = threadIdx.x;
   for (int i = t; i < j.cap + 2; i += 1024) {
     j.hist[i] = 0;
     j.tie[i] = 0;
   }
-  if (t < 4) j.counters[t] = 0;
+  if (t == 0) s_maxblk = 0;
   sched_step_barrier();
   for (int b = t; b < B; b += 1024) {
     const int n = offs[b + 1] - offs[b];
     const int nb = (n + j.bm - 1) / j.bm;
     atomicAdd(&j.hist[nb], 1);
-    atomicMax(&j.counters[1], nb);
+    atomicMax(&s_maxblk, nb);
   }
   sched_step_barrier();
-  const int maxblk = j.counters[1];
+  const int maxblk = s_maxblk;
   // cnt[m] = #sequences with more than m blocks, m in [0, maxblk]
   block_suffix_excl(j.hist, j.cnt, maxblk + 1, nullptr);
   sched_step_barrier();
   // levelstart[L] = sum of cnt[L'] for L' in (L, maxblk); n_items = sum over [0, maxblk)
-  block_suffix_excl(j.cnt, j.levelstart, maxblk, &j.counters[0]);
-  if (t == 0 && maxblk == 0) j.counters[0] = 0;
+  block_suffix_excl(j.cnt, j.levelstart, maxblk, &s_items);
   sched_step_barrier();
+  if (t == 0) {
+    j.counters[0] = maxblk == 0 ? 0 : s_items;
+    j.counters[1] = maxblk;
+  }
   for (int b = t; b < B; b += 1024) {
     const int n = offs[b + 1] - offs[b];
     const int nb = (n + j.bm - 1) / j.bm;
@@ -211,7 +223,26 @@ __global__ __launch_bounds__(1024) void k_sched(int B, const int32_t* __restrict
   }
 }
 
-static SchedJob sched_job(const Sched& s, int reverse) {
+// One launch for a call's plan: workgroups [0, npre) run the time pre-pass
+// (and clear the backward's rab-gradient sums on the way), the next njobs
+// build the work lists.
+__global__ __launch_bounds__(1024) void k_plan(PlanArgs p) {
+  extern __shared__ int32_t plan_lds[];
+  const int wg = blockIdx.x;
+  if (wg < p.npre) {
+    for (int64_t i = (int64_t)wg * 1024 + threadIdx.x; i < p.nz; i += (int64_t)p.npre * 1024) {
+      p.z0[i] = 0.0f;
+      p.z1[i] = 0.0f;
+    }
+    if (p.mode == 0) prepass_seq(wg, p);
+    else prepass_user(wg, p);
+    return;
+  }
+  const int job = wg - p.npre;
+  build_schedule(p.B, p.sched_offs, p.job[job], p.lds_sched ? plan_lds : nullptr);
+}
+
+SchedJob sched_job(const Sched& s, int reverse) {
   SchedJob j;
   j.items = s.items;
   j.counters = s.counters;
@@ -238,15 +269,58 @@ Sched carve_sched(Carver& c, int64_t T, int64_t B, int block_rows) {
   return s;
 }
 
-hipError_t launch_sched(const Sched& s, int B, const int32_t* offs, int reverse, hipStream_t st) {
-  const SchedJob j = sched_job(s, reverse);
-  k_sched<<<1, 1024, 0, st>>>(B, offs, j, j);
+// schedule arrays up to this many entries each live in LDS (4 x 12 KiB)
+constexpr int SCHED_LDS_ENTRIES = 3072;
+
+hipError_t launch_plan(PlanArgs p, hipStream_t st) {
+  int max_e = 0;
+  for (int k = 0; k < p.njobs; ++k) max_e = max(max_e, p.job[k].cap + 2);
+  p.lds_sched = (p.njobs > 0 && max_e <= SCHED_LDS_ENTRIES) ? 1 : 0;
+  if (p.npre == 0 && p.nz > 0) {
+    hipError_t e = launch_zero_f32(p.z0, p.nz, st);
+    if (e == hipSuccess) e = launch_zero_f32(p.z1, p.nz, st);
+    if (e != hipSuccess) return e;
+    p.nz = 0;
+  }
+  const int grid = p.npre + p.njobs;
+  if (grid <= 0) return hipSuccess;
+  const size_t lds = p.lds_sched ? (size_t)4 * max_e * sizeof(int32_t) : 0;
+  k_plan<<<grid, 1024, lds, st>>>(p);
   return hipGetLastError();
 }
-hipError_t launch_sched2(const Sched& s0, int reverse0, const Sched& s1, int reverse1, int B,
-                         const int32_t* offs, hipStream_t st) {
-  k_sched<<<2, 1024, 0, st>>>(B, offs, sched_job(s0, reverse0), sched_job(s1, reverse1));
-  return hipGetLastError();
+
+PlanArgs plan_prepass(const TimeMeta& tm, int B, const int32_t* offs, const int64_t* ts,
+                      float* z0, float* z1, int64_t nz) {
+  PlanArgs p;
+  p.npre = B > 0 ? B : 0;
+  p.mode = 0;
+  p.offs = offs;
+  p.ts = ts;
+  p.rel_t = tm.rel_t;
+  p.flags = tm.seq_flags;
+  p.z0 = z0;
+  p.z1 = z1;
+  p.nz = (z0 && z1) ? nz : 0;
+  p.B = B;
+  return p;
+}
+
+void plan_add_job(PlanArgs& p, const Sched& s, int reverse, const int32_t* sched_offs) {
+  p.sched_offs = sched_offs;
+  p.job[p.njobs++] = sched_job(s, reverse);
+}
+
+hipError_t launch_time_prepass(const TimeMeta& tm, int B, const int32_t* offs,
+                               const int64_t* ts, hipStream_t st, float* z0, float* z1,
+                               int64_t nz) {
+  return launch_plan(plan_prepass(tm, B, offs, ts, z0, z1, nz), st);
+}
+
+hipError_t launch_sched(const Sched& s, int B, const int32_t* offs, int reverse, hipStream_t st) {
+  PlanArgs p;
+  p.B = B;
+  plan_add_job(p, s, reverse, offs);
+  return launch_plan(p, st);
 }
 
 // ---------------------------------------------------------------------------

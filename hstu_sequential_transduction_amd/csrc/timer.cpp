@@ -19,7 +19,7 @@ struct Pool {
 Pool g_pool;
 
 const char* kNames[TT_COUNT] = {
-    "prepass", "sched", "attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm_uvqk", "gemm_out",
+    "plan", "sched", "attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm_uvqk", "gemm_out",
     "gemm_dG", "gemm_dW2", "gemm_dW1", "gemm_dX", "ln_gate_fwd", "ln_gate_bwd", "reduce",
     "truncate", "attn_cached"};
 
