@@ -11,8 +11,10 @@ Pages cited (their text, not line numbers):
            (xfinit.ro), sections "Model Architecture", "HSTU Hyperparameters",
            "Computation Cost Analysis" (Tables 6 and 7).
   [ULTRA]  Telegram summary of "Bending the Scaling Law Curve in Large-Scale
-           Recommendation Systems" (ULTRA-HSTU), items "Semi-Local Attention"
-           and "Attention Truncation".
+           Recommendation Systems" (ULTRA-HSTU), items "Semi-Local Attention",
+           "Mixed precision" and "Attention Truncation".
+  [MX]     OCP Microscaling Formats (MX) Specification v1.0: FP8 E4M3 element
+           encoding, E8M0 shared block scales, the block-scale choice.
 
 What is computed (every array is float64; integer work is exact):
 
@@ -56,6 +58,13 @@ What is computed (every array is float64; integer work is exact):
    candidates run through the layers alone: candidate rows at position n_h
    attend to the cached keys and to themselves.  This equals the candidate
    rows of the full target-aware stack when N is a fixed norm_len.
+   FP8 matmuls ([ULTRA] "Mixed precision": BF16 for most operations, FP8
+   for the matrix products; no scaling recipe given): the projection and
+   output matrices are multiplied as MXFP8 ([MX]): every 32 consecutive
+   values along the contraction share a power-of-two scale
+   2^(floor(log2 amax) - 8) and are rounded to E4M3 (nearest, ties to even,
+   saturating at 448); the product of two such operands is computed exactly
+   here.  Attention and everything else stay as above.
 5. Backward: the chain rule of 1-4 written out by hand (no autograd).
 
 Readings where the pages are silent (each is a flag here):
@@ -528,3 +537,102 @@ def cached_stack_fwd(Xc, layers: List, caches: List, hist_offsets, hist_ts, cand
         x = layer_fwd_cached(x, w.W1, w.W2, w.rab_pos, w.rab_time, K, V, hist_offsets, hist_ts,
                              cand_offsets, cand_ts, f)
     return x
+
+
+# ----------------------------------------------------------------------------
+# MXFP8 matmuls ([ULTRA] "Mixed precision"; [MX] element and scale formats)
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+MX_BLOCK = 32
+E4M3_EMAX = 8          # exponent of the largest power of two in E4M3 (256)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of FP8 E4M3 codes ([MX] element format: 1 sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits, subnormals at exponent 0, no
+    infinities, S.1111.111 is NaN)."""
+    c = np.asarray(codes, np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F))    # the 127 non-negative finite values, increasing
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Codes of x rounded to the nearest E4M3 value, ties to the even code
+    (even mantissa), magnitudes above 448 saturated to 448."""
+    x = np.asarray(x, np.float64)
+    ax = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_E4M3_POS, ax)            # first value >= |x|
+    hi = np.minimum(hi, len(_E4M3_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = ax - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - ax
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(_E4M3_POS[hi] == ax, hi, np.where(pick_hi, hi, lo))
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def mx_quantize(x, axis=-1):
+    """MXFP8 of x along `axis` (its length a multiple of 32): (codes uint8
+    like x, E8M0 scale bytes with one entry per block of 32 along the axis).
+    Block scale X = 2^(floor(log2(amax)) - 8) ([MX]: shared exponent from the
+    largest magnitude minus the element format's largest exponent); an
+    all-zero block gets the smallest scale 2^-127 and zero codes."""
+    x = np.asarray(x, np.float64)
+    xm = np.moveaxis(x, axis, -1)
+    n = xm.shape[-1]
+    assert n % MX_BLOCK == 0
+    blk = xm.reshape(xm.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))      # amax = f * 2^ex, f in [0.5, 1)
+    shared = np.where(amax > 0, (ex - 1) - E4M3_EMAX, -127)
+    shared = np.clip(shared, -127, 127)
+    codes = e4m3_encode(blk / np.exp2(shared)[..., None])
+    codes = np.moveaxis(codes.reshape(xm.shape), -1, axis)
+    scales = np.moveaxis((shared + 127).astype(np.uint8), -1, axis)
+    return codes, scales
+
+
+def mx_dequantize(codes, scales, axis=-1):
+    """Values of MXFP8 data (inverse of mx_quantize's encoding)."""
+    c = np.moveaxis(np.asarray(codes), axis, -1)
+    s = np.moveaxis(np.asarray(scales, np.int64), axis, -1)
+    v = e4m3_decode(c).reshape(c.shape[:-1] + (s.shape[-1], MX_BLOCK))
+    v = v * np.exp2(s - 127.0)[..., None]
+    return np.moveaxis(v.reshape(c.shape), -1, axis)
+
+
+def mx_matmul(a, b):
+    """a @ b with both operands rounded to MXFP8 along the contraction (a's
+    rows, b's columns), the products summed exactly."""
+    qa, sa = mx_quantize(a, axis=1)
+    qb, sb = mx_quantize(b, axis=0)
+    return mx_dequantize(qa, sa, axis=1) @ mx_dequantize(qb, sb, axis=0)
+
+
+def layer_fwd_mx(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
+                 f: LayerFlags, b1=None, b2=None, gamma=None, beta=None):
+    """One layer with MXFP8 projection and output matmuls (steps 1 and 4);
+    attention, LayerNorm and gating as in layer_fwd."""
+    X = np.asarray(X, np.float64)
+    Z = mx_matmul(X, W1)
+    if b1 is not None:
+        Z = Z + np.asarray(b1, np.float64)
+    Zh = silu(Z) if f.proj_silu else Z
+    U, V, Q, K = split_uvqk(Zh, f)
+    O = attn_fwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
+                 f.norm_mode, f.norm_len, win_local=f.win_local, win_global=f.win_global)
+    Yn, _, _, _ = layernorm_fwd(O.reshape(X.shape[0], f.H * f.d_v), f.eps, gamma, beta)
+    Y = mx_matmul(Yn * U, W2)
+    if b2 is not None:
+        Y = Y + np.asarray(b2, np.float64)
+    if f.residual:
+        Y = Y + X
+    return Y
