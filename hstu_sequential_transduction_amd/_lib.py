@@ -26,6 +26,8 @@ EXPORTED = [
     "hstu_schedule_workspace_size", "hstu_validate_inputs",
     "hstu_truncate_offsets", "hstu_truncate_gather", "hstu_truncate_scatter",
     "hstu_attn_cached_workspace_size", "hstu_attn_cached_fwd",
+    "hstu_mx_quantize", "hstu_mx_quantize_weight", "hstu_mx_gemm",
+    "hstu_layer_fwd_mx_workspace_size", "hstu_layer_fwd_mx",
     "hstu_layer_cached_workspace_size", "hstu_layer_fwd_cached",
     "hstu_timer_enable", "hstu_timer_reset", "hstu_timer_tag_count", "hstu_timer_tag_name",
     "hstu_timer_query",
@@ -61,6 +63,11 @@ class LayerGrads(C.Structure):
     _fields_ = [("dW1", C.c_void_p), ("dW2", C.c_void_p), ("db1", C.c_void_p),
                 ("db2", C.c_void_p), ("dgamma", C.c_void_p), ("dbeta", C.c_void_p),
                 ("drab_pos", C.c_void_p), ("drab_time", C.c_void_p)]
+
+
+class MxWeights(C.Structure):
+    _fields_ = [("W1", C.c_void_p), ("W1_scales", C.c_void_p), ("W2", C.c_void_p),
+                ("W2_scales", C.c_void_p)]
 
 
 class HistoryKV(C.Structure):
@@ -125,6 +132,17 @@ def lib() -> C.CDLL:
     L.hstu_schedule.argtypes = [i32, i64, vp, i32, i32, vp, vp, vp, sz, vp]
     L.hstu_validate_inputs.restype = C.c_int
     L.hstu_validate_inputs.argtypes = [i32, i64, vp, vp, vp, vp]
+    L.hstu_mx_quantize.restype = C.c_int
+    L.hstu_mx_quantize.argtypes = [i64, i64, vp, i64, vp, vp, vp]
+    L.hstu_mx_quantize_weight.restype = C.c_int
+    L.hstu_mx_quantize_weight.argtypes = [i64, i64, vp, vp, vp, vp]
+    L.hstu_mx_gemm.restype = C.c_int
+    L.hstu_mx_gemm.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+    L.hstu_layer_fwd_mx_workspace_size.restype = sz
+    L.hstu_layer_fwd_mx_workspace_size.argtypes = [P(LayerDesc)]
+    L.hstu_layer_fwd_mx.restype = C.c_int
+    L.hstu_layer_fwd_mx.argtypes = [P(LayerDesc), vp, P(LayerWeights), P(MxWeights), vp, vp, vp,
+                                    vp, vp, vp, vp, sz, vp]
     L.hstu_attn_cached_workspace_size.restype = sz
     L.hstu_attn_cached_workspace_size.argtypes = [P(AttnDesc), i64]
     L.hstu_attn_cached_fwd.restype = C.c_int

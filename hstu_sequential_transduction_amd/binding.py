@@ -13,7 +13,8 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import AttnDesc, HistoryKV, LayerDesc, LayerGrads, LayerSaved, LayerWeights, check
+from ._lib import (AttnDesc, HistoryKV, LayerDesc, LayerGrads, LayerSaved, LayerWeights,
+                   MxWeights, check)
 
 _DT = {torch.float32: _lib.HSTU_F32, torch.bfloat16: _lib.HSTU_BF16}
 
@@ -291,6 +292,84 @@ def hstu_layer_fwd_cached(x, W1, W2, rab_pos, rab_time, cand_offsets, cand_ts, h
                                  _ptr(cand_ts), C.byref(h), _ptr(y), _ptr(ws), ws.numel(),
                                  _stream(stream))
     check("hstu_layer_fwd_cached", st)
+    return y
+
+
+def hstu_mx_quantize(x, stream=None):
+    """(codes uint8 [rows, K], scales uint8 [rows, K/32]) of bf16 rows (MXFP8)."""
+    rows, K = x.shape
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=x.device)
+    st = _lib.lib().hstu_mx_quantize(rows, K, _ptr(x), x.stride(0), _ptr(codes), _ptr(scales),
+                                     _stream(stream))
+    check("hstu_mx_quantize", st)
+    return codes, scales
+
+
+def hstu_mx_quantize_weight(w, stream=None):
+    """(codes [N, K], scales [N, K/32]) of a bf16 [K, N] weight, blocks along K."""
+    K, N = w.shape
+    w = w.contiguous()
+    codes = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    st = _lib.lib().hstu_mx_quantize_weight(K, N, _ptr(w), _ptr(codes), _ptr(scales),
+                                            _stream(stream))
+    check("hstu_mx_quantize_weight", st)
+    return codes, scales
+
+
+def hstu_mx_gemm(a, a_scales, b, b_scales, stream=None):
+    """C [M, N] fp32 = A B^T of MXFP8 A [M, K] and B [N, K]."""
+    M, K = a.shape
+    N = b.shape[0]
+    ldc = (N + 3) // 4 * 4           # fp32 rows are written four values at a time
+    c = torch.empty((M, ldc), dtype=torch.float32, device=a.device)
+    st = _lib.lib().hstu_mx_gemm(M, N, K, _ptr(a), _ptr(a_scales), _ptr(b), _ptr(b_scales),
+                                 _ptr(c), ldc, _stream(stream))
+    check("hstu_mx_gemm", st)
+    return c[:, :N]
+
+
+@dataclasses.dataclass
+class MxLayerWeights:
+    """A layer's MXFP8 weights (codes transposed, blocks along the contraction)."""
+    W1: torch.Tensor
+    W1_scales: torch.Tensor
+    W2: torch.Tensor
+    W2_scales: torch.Tensor
+
+    @staticmethod
+    def from_bf16(W1, W2, stream=None) -> "MxLayerWeights":
+        c1, s1 = hstu_mx_quantize_weight(W1, stream)
+        c2, s2 = hstu_mx_quantize_weight(W2, stream)
+        return MxLayerWeights(c1, s1, c2, s2)
+
+    def c(self) -> MxWeights:
+        return MxWeights(_ptr(self.W1), _ptr(self.W1_scales), _ptr(self.W2), _ptr(self.W2_scales))
+
+
+def hstu_layer_fwd_mx(x, wm: MxLayerWeights, rab_pos, rab_time, seq_offsets, timestamps,
+                      cfg: LayerConfig, num_candidates=None, b1=None, b2=None, gamma=None,
+                      beta=None, y=None, workspace: Optional[LayerWorkspace] = None, stream=None,
+                      g_out=None):
+    """Y of one layer with MXFP8 projection and output products (inference);
+    g_out = (codes [T, H*d_v] uint8, scales [T, H*d_v/32] uint8) receives the
+    quantized gated output the output product used."""
+    T = x.shape[0]
+    B = seq_offsets.shape[0] - 1
+    if y is None:
+        y = torch.empty_like(x)
+    d = layer_desc(cfg, B, T, x.dtype, _rab_stride(rab_pos, rab_time))
+    L = _lib.lib()
+    nb = L.hstu_layer_fwd_mx_workspace_size(C.byref(d))
+    ws = workspace.get(nb, x.device) if workspace is not None else _ws(nb, x.device)
+    w = _weights(None, None, rab_pos, rab_time, b1, b2, gamma, beta)
+    m = wm.c()
+    gc, gs = (None, None) if g_out is None else g_out
+    st = L.hstu_layer_fwd_mx(C.byref(d), _ptr(x), C.byref(w), C.byref(m), _ptr(seq_offsets),
+                             _ptr(timestamps), _ptr(num_candidates), _ptr(y), _ptr(gc), _ptr(gs),
+                             _ptr(ws), ws.numel(), _stream(stream))
+    check("hstu_layer_fwd_mx", st)
     return y
 
 

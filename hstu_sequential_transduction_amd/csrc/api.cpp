@@ -381,10 +381,21 @@ hstu_status check_trunc_copy(int32_t B, int64_t T, int64_t T_seg, int32_t D, int
 // Steps 1-4 of one layer on T rows, with the attention step supplied by the
 // caller (causal / target-aware over the rows' own sequences, or candidates
 // against a cached history).  Zsave, mu, rstd: optional saved intermediates.
+// MXFP8 projection and output products: the weights' codes and scales and
+// workspace for the quantized activations (X and G).
+struct MxPlan {
+  const hstu_mx_weights* wm = nullptr;
+  uint8_t* x8 = nullptr;
+  uint8_t* xs = nullptr;
+  uint8_t* g8 = nullptr;
+  uint8_t* gs = nullptr;
+};
+
 template <typename Attn>
 hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
                             void* y, void* Zsave, void* Zh, float* O, void* G, float* mu,
-                            float* rstd, Attn attention, hipStream_t st) {
+                            float* rstd, Attn attention, hipStream_t st,
+                            const MxPlan* mx = nullptr) {
   const hstu_attn_desc* d = &L->attn;
   const int64_t T = d->T, D = L->D, F1 = f1_width(L);
   const int64_t W = (int64_t)d->H * d->d_v, HQ = (int64_t)d->H * d->d_qk;
@@ -411,6 +422,19 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
   } else {
     g1.epi = EPI_RESID;  // bias only
     g1.R = nullptr;
+  }
+  if (mx) {
+    // X -> MXFP8 (blocks of 32 along d_model), W1 given as [F1][D] codes
+    { HSTU_TIMED(TT_MX_QUANT, st); HSTU_TRY(launch_mx_quant_rows(x, D, T, D, mx->x8, mx->xs, st)); }
+    g1.mx = true;
+    g1.A = mx->x8;
+    g1.lda = D / 2;
+    g1.K = D / 2;
+    g1.B = mx->wm->W1;
+    g1.ldb = D / 2;
+    g1.b_kcont = true;
+    g1.scale_a = mx->xs;
+    g1.scale_b = static_cast<const uint8_t*>(mx->wm->W1_scales);
   }
   { HSTU_TIMED(TT_GEMM_UVQK, st); HSTU_TRY(launch_gemm(g1, d->dtype, st)); }
   if (!L->proj_silu && Zsave) {
@@ -456,6 +480,19 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
   g2.bias = w->b2;
   g2.R = L->residual ? x : nullptr;
   g2.ldr = D;
+  if (mx) {
+    // G -> MXFP8 (blocks of 32 along H d_v), W2 given as [D][H d_v] codes
+    { HSTU_TIMED(TT_MX_QUANT, st); HSTU_TRY(launch_mx_quant_rows(G, W, T, W, mx->g8, mx->gs, st)); }
+    g2.mx = true;
+    g2.A = mx->g8;
+    g2.lda = W / 2;
+    g2.K = W / 2;
+    g2.B = mx->wm->W2;
+    g2.ldb = W / 2;
+    g2.b_kcont = true;
+    g2.scale_a = mx->gs;
+    g2.scale_b = static_cast<const uint8_t*>(mx->wm->W2_scales);
+  }
   { HSTU_TIMED(TT_GEMM_OUT, st); HSTU_TRY(launch_gemm(g2, d->dtype, st)); }
   return HSTU_OK;
 }
@@ -618,6 +655,129 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
   };
   return layer_fwd_steps(L, x, w, y, full ? saved->Z : nullptr, Zh, O, G,
                          full ? saved->mu : nullptr, full ? saved->rstd : nullptr, attention, st);
+}
+
+// MXFP8 layer: the inference workspace plus the quantized X and G
+struct MxWs {
+  uint8_t *x8, *xs, *g8, *gs;
+};
+MxWs carve_mx(Carver& c, const hstu_layer_desc* L) {
+  const hstu_attn_desc* d = &L->attn;
+  const int64_t T = std::max<int64_t>(d->T, 1), D = L->D, W = (int64_t)d->H * d->d_v;
+  MxWs m;
+  m.x8 = c.take<uint8_t>(T * D);
+  m.xs = c.take<uint8_t>(T * D / 32);
+  m.g8 = c.take<uint8_t>(T * W);
+  m.gs = c.take<uint8_t>(T * W / 32);
+  return m;
+}
+
+hstu_status check_mx_layer(const hstu_layer_desc* L) {
+  hstu_status s = check_layer(L);
+  if (s != HSTU_OK) return s;
+  const int64_t W = (int64_t)L->attn.H * L->attn.d_v;
+  if (L->attn.dtype != HSTU_BF16 || L->D % 128 != 0 || W % 128 != 0) return HSTU_ERR_UNSUPPORTED;
+  return HSTU_OK;
+}
+
+size_t hstu_layer_fwd_mx_workspace_size(const hstu_layer_desc* L) {
+  if (check_mx_layer(L) != HSTU_OK) return 0;
+  Carver c(nullptr);
+  carve_mx(c, L);
+  carve_layer_fwd(c, L, 0);
+  return c.off + 256;
+}
+
+hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
+                              const hstu_mx_weights* wm, const int32_t* offs, const int64_t* ts,
+                              const int32_t* nc, void* y, void* g_codes, void* g_scales,
+                              void* ws, size_t ws_bytes, void* stream) {
+  hstu_status s = check_mx_layer(L);
+  if (s != HSTU_OK) return s;
+  const hstu_attn_desc* d = &L->attn;
+  if (!w || !w->rab_pos || !w->rab_time || !offs || !ws || !wm || !wm->W1 || !wm->W1_scales ||
+      !wm->W2 || !wm->W2_scales)
+    return HSTU_ERR_INVALID_ARG;
+  if (d->T > 0 && (!x || !y || !ts)) return HSTU_ERR_INVALID_ARG;
+  if (x == y && d->T > 0) return HSTU_ERR_INVALID_ARG;
+  if ((g_codes == nullptr) != (g_scales == nullptr) || !aligned16(g_codes) ||
+      (reinterpret_cast<uintptr_t>(g_scales) & 3))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(wm->W1) || !aligned16(wm->W2) ||
+      (reinterpret_cast<uintptr_t>(wm->W1_scales) & 3) ||
+      (reinterpret_cast<uintptr_t>(wm->W2_scales) & 3))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_layer_fwd_mx_workspace_size(L)) return HSTU_ERR_WORKSPACE;
+  hipStream_t st = entry_stream(stream);
+
+  Carver c(ws);
+  MxWs m = carve_mx(c, L);
+  LayerFwdWs lw = carve_layer_fwd(c, L, 0);
+  const int64_t W = (int64_t)d->H * d->d_v;
+  float* O = static_cast<float*>(lw.O);
+  auto attention = [&](const void* q, const void* k, const void* v, int64_t ld) {
+    return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, O, W,
+                         /*out_f32=*/true, lw.attn, st);
+  };
+  MxPlan plan;
+  plan.wm = wm;
+  plan.x8 = m.x8;
+  plan.xs = m.xs;
+  plan.g8 = g_codes ? static_cast<uint8_t*>(g_codes) : m.g8;
+  plan.gs = g_scales ? static_cast<uint8_t*>(g_scales) : m.gs;
+  return layer_fwd_steps(L, x, w, y, nullptr, lw.Zh, O, lw.G, nullptr, nullptr, attention, st,
+                         &plan);
+}
+
+hstu_status hstu_mx_quantize(int64_t rows, int64_t K, const void* x, int64_t ld, void* codes,
+                             void* scales, void* stream) {
+  if (rows < 0 || K < 0 || K % 32 != 0 || ld < K) return HSTU_ERR_INVALID_ARG;
+  if (rows > 0 && K > 0 && (!x || !codes || !scales)) return HSTU_ERR_INVALID_ARG;
+  if (rows > 0 && K > 0 && (!aligned16(x) || ld % 8 != 0 || !aligned16(codes)))
+    return HSTU_ERR_INVALID_ARG;
+  hipStream_t st = entry_stream(stream);
+  HSTU_TIMED(TT_MX_QUANT, st);
+  HSTU_TRY(launch_mx_quant_rows(x, ld, rows, K, static_cast<uint8_t*>(codes),
+                                static_cast<uint8_t*>(scales), st));
+  return HSTU_OK;
+}
+
+hstu_status hstu_mx_quantize_weight(int64_t K, int64_t N, const void* w, void* codes,
+                                    void* scales, void* stream) {
+  if (K < 0 || N < 0 || K % 32 != 0) return HSTU_ERR_INVALID_ARG;
+  if (K > 0 && N > 0 && (!w || !codes || !scales || !aligned16(codes)))
+    return HSTU_ERR_INVALID_ARG;
+  hipStream_t st = entry_stream(stream);
+  HSTU_TIMED(TT_MX_QUANT, st);
+  HSTU_TRY(launch_mx_quant_cols(w, K, N, static_cast<uint8_t*>(codes),
+                                static_cast<uint8_t*>(scales), st));
+  return HSTU_OK;
+}
+
+hstu_status hstu_mx_gemm(int64_t M, int64_t N, int64_t K, const void* a, const void* a_scales,
+                         const void* b, const void* b_scales, float* c, int64_t ldc,
+                         void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || ldc < N) return HSTU_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return HSTU_OK;
+  if (!a || !b || !a_scales || !b_scales || !c || !aligned16(a) || !aligned16(b) ||
+      !aligned16(c) || ldc % 4 != 0 || (reinterpret_cast<uintptr_t>(a_scales) & 3) ||
+      (reinterpret_cast<uintptr_t>(b_scales) & 3))
+    return HSTU_ERR_INVALID_ARG;
+  if (K == 0) return HSTU_ERR_INVALID_ARG;
+  hipStream_t st = entry_stream(stream);
+  GemmArgs g;
+  g.M = M; g.N = N; g.K = K / 2;
+  g.A = a; g.lda = K / 2; g.a_kcont = true;
+  g.B = b; g.ldb = K / 2; g.b_kcont = true;
+  g.C = c; g.ldc = ldc; g.c_f32 = true;
+  g.epi = EPI_STORE;
+  g.mx = true;
+  g.scale_a = static_cast<const uint8_t*>(a_scales);
+  g.scale_b = static_cast<const uint8_t*>(b_scales);
+  HSTU_TIMED(TT_GEMM_MX, st);
+  HSTU_TRY(launch_gemm(g, HSTU_BF16, st));
+  return HSTU_OK;
 }
 
 size_t hstu_layer_cached_workspace_size(const hstu_layer_desc* L, int64_t T_hist) {

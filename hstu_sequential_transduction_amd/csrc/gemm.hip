@@ -257,6 +257,30 @@ struct G2Off {
   }
 };
 
+// MXFP8 operand reads from the same k-contiguous tiles (128-byte rows of E4M3
+// codes).  The scaled 32x32x64 FP8 MFMA (established with an in-bounds probe)
+// takes from lane half g bytes 0-15 as k = 16 g + e and bytes 16-31 as
+// k = 32 + 16 g + e, and the scale of its k-block b (k in [32 b, 32 b + 32))
+// from lane half b.  So for MFMA half kh (MX blocks 2 kh and 2 kh + 1 of the
+// k-step) a lane reads logical chunks 4 kh + g and 4 kh + 2 + g, and its
+// scale byte is that of block 2 kh + g.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+struct G2OffMX {
+  int o[4];
+  HSTU_DEV void init(int r0, int lane) {
+    const int ql = lane & 31, g = lane >> 5;
+    const int s = SwzTile<64>::swz(ql);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      o[c] = (r0 + ql) * 128 + (((4 * (c >> 1) + 2 * (c & 1) + g) ^ s) << 4);
+  }
+  HSTU_DEV i32x8 frag(const uint8_t* t, int i, int kh) const {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(t + o[2 * kh] + i * 32 * 128);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(t + o[2 * kh + 1] + i * 32 * 128);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 // NST operand stages: 2 = double buffer (the DMA of step k+1 runs under the
 // MFMAs of step k); 1 = a single stage, which halves the LDS of a workgroup so
 // that twice as many are resident and hide each other's DMA and epilogue.
@@ -267,7 +291,7 @@ struct G2Shape {
   static constexpr int WPC = (BM * BN >= 256 * 256 ? 1 : 2) * (NST == 1 ? 2 : 1);  // WGs per CU
 };
 
-template <int BM, int BN, bool AK, bool BK, int EPI, bool OUTF32, int NST>
+template <int BM, int BN, bool AK, bool BK, int EPI, bool OUTF32, int NST, bool MX = false>
 __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gemm2_bf16(
     GemmArgs g, int mt, int nt, int slots) {
   using SH = G2Shape<BM, BN, NST>;
@@ -336,6 +360,56 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
     }
   };
 
+  // MXFP8: per k-step (128 codes = four MX blocks) each lane needs the scales
+  // of its rows' blocks g and 2 + g: one 32-bit word of four scale bytes per
+  // row, shifted so that bytes 0 and 2 are the two blocks (MFMA op_sel)
+  G2OffMX amx, bmx;
+  uint32_t sa[FM], sb[FN];
+  const int64_t kblk = g.K / 16;  // MX blocks per row (K counts pairs of codes)
+  if constexpr (MX) {
+    amx.init(wm * 32 * FM, lane);
+    bmx.init(wn * 32 * FN, lane);
+  }
+  auto load_scales = [&](int64_t k0) HSTU_INLINE_LAMBDA {
+    const int64_t b0 = k0 / 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t r = m0 + wm * 32 * FM + 32 * i + ql;
+      const uint32_t wd = r < g.M ? *reinterpret_cast<const uint32_t*>(g.scale_a + r * kblk + b0)
+                                  : 0x7F7F7F7Fu;
+      sa[i] = wd >> (8 * gq);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t r = n0 + wn * 32 * FN + 32 * j + ql;
+      const uint32_t wd = r < g.N ? *reinterpret_cast<const uint32_t*>(g.scale_b + r * kblk + b0)
+                                  : 0x7F7F7F7Fu;
+      sb[j] = wd >> (8 * gq);
+    }
+  };
+  auto compute_mx = [&](const uint8_t* ta, const uint8_t* tb) HSTU_INLINE_LAMBDA {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      i32x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = amx.frag(ta, i, kh);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = bmx.frag(tb, j, kh);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if (kh == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[i], bfr[j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[i], bfr[j], acc[i][j], 0, 0, 2, (int)sa[i], 2, (int)sb[j]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // double buffer, two stages per iteration so that every access names its
   // stage statically (and no exit in the middle of the iteration, which would
   // make the register allocator shuffle the accumulators)
@@ -359,9 +433,11 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
   } else {
     for (int ks = 0; ks < nks; ++ks) {
       issue(a0, b0, kbeg + (int64_t)ks * G2_BK);
+      if constexpr (MX) load_scales(kbeg + (int64_t)ks * G2_BK);
       dma_wait();
       __syncthreads();
-      compute(a0, b0);
+      if constexpr (MX) compute_mx(a0, b0);
+      else compute(a0, b0);
       __syncthreads();
     }
   }
@@ -665,8 +741,38 @@ __global__ void k_colsum_final(const float* __restrict__ part, int nb, int64_t c
 
 }  // namespace
 
+// MXFP8 GEMM: both operands k-contiguous E4M3 codes (k-steps of 128 codes),
+// the DMA-staged kernel with the scaled MFMA; one operand stage.
+hipError_t gemm2_mx(const GemmArgs& g, hipStream_t st) {
+  if (!g.a_kcont || !g.b_kcont || !g.scale_a || !g.scale_b || !gemm2_ok(g))
+    return hipErrorInvalidValue;
+  if ((reinterpret_cast<uintptr_t>(g.scale_a) & 3) || (reinterpret_cast<uintptr_t>(g.scale_b) & 3))
+    return hipErrorInvalidValue;
+  constexpr int BM = 128, BN = 128, NT = 64 * G2_NW;
+  const int mt = (int)((g.M + BM - 1) / BM), nt = (int)((g.N + BN - 1) / BN);
+  const int slots = (mt * nt + 7) / 8;
+  dim3 grid((unsigned)(8 * slots), 1);
+  switch (g.epi) {
+    case EPI_STORE:
+      if (g.c_f32)
+        k_gemm2_bf16<BM, BN, true, true, EPI_STORE, true, 1, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      else
+        k_gemm2_bf16<BM, BN, true, true, EPI_STORE, false, 1, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      break;
+    case EPI_SILU:
+      k_gemm2_bf16<BM, BN, true, true, EPI_SILU, false, 1, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      break;
+    case EPI_RESID:
+      k_gemm2_bf16<BM, BN, true, true, EPI_RESID, false, 1, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.mx) return gemm2_mx(g, st);
   if (dtype == HSTU_BF16) {
     if (gemm2_ok(g)) {
       if (g.a_kcont && g.b_kcont) return gemm2_ab<true, true>(g, st);

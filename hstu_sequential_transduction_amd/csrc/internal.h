@@ -178,6 +178,12 @@ struct GemmArgs {
   int epi = EPI_STORE;
   int split_k = 1;
   float* partial = nullptr;     // EPI_PARTIAL workspace [split_k][M][N]
+  // MXFP8 operands (both k-contiguous): A, B hold E4M3 codes, lda/ldb/K count
+  // pairs of codes (2 bytes), scale_a [M][K/32] and scale_b [N][K/32] are the
+  // E8M0 block scales (K here in codes)
+  bool mx = false;
+  const uint8_t* scale_a = nullptr;
+  const uint8_t* scale_b = nullptr;
 };
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st);
 // Split-K reduction: out[m*ldo + n] = sum_z partial[z][m][n]  (fp32)
@@ -252,6 +258,12 @@ struct CachedArgs {
 int attn_cached_block_rows(int dtype, int d_qk, int d_v);
 hipError_t launch_attn_cached(const CachedArgs& a, int dtype, int d_qk, int d_v,
                               int64_t max_items, hipStream_t st);
+
+// MXFP8 quantization (blocks of 32 along the contraction, k-contiguous output)
+hipError_t launch_mx_quant_rows(const void* x, int64_t ld, int64_t rows, int64_t K,
+                                uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_mx_quant_cols(const void* w, int64_t K, int64_t N, uint8_t* codes,
+                                uint8_t* scales, hipStream_t st);
 
 // Attention truncation: segment offsets, row gather, gradient scatter.
 hipError_t launch_trunc_offsets(int B, const int32_t* seq_offsets, const int32_t* num_cand,

@@ -21,7 +21,7 @@ Pool g_pool;
 const char* kNames[TT_COUNT] = {
     "plan", "sched", "attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq", "gemm_uvqk", "gemm_out",
     "gemm_dG", "gemm_dW2", "gemm_dW1", "gemm_dX", "ln_gate_fwd", "ln_gate_bwd", "reduce",
-    "truncate", "attn_cached"};
+    "truncate", "attn_cached", "mx_quant", "gemm_mx"};
 
 void destroy() {
   for (auto e : g_pool.start) (void)hipEventDestroy(e);

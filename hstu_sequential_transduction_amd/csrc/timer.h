@@ -23,6 +23,8 @@ enum TimerTag {
   TT_REDUCE,
   TT_TRUNCATE,
   TT_ATTN_CACHED,
+  TT_MX_QUANT,
+  TT_GEMM_MX,
   TT_COUNT
 };
 

@@ -226,6 +226,59 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const void* x,
                            void* dx, const hstu_layer_grads* g,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- MXFP8 matmuls ------------------------------------------------------- */
+/*
+ * "Bending the Scaling Law Curve in Large-Scale Recommendation Systems",
+ * Mixed precision: most operations stay in BF16, the matrix products run in
+ * FP8.  The scaling recipe is not given there; these entry points use the
+ * OCP Microscaling (MX) format: every 32 consecutive values along the
+ * contraction index share one E8M0 scale byte e (2^(e-127)), chosen as
+ * 2^(floor(log2 amax) - 8), and are stored as E4M3 codes rounded to nearest
+ * (ties to even) with saturation at 448; an all-zero block has e = 0.  The
+ * matrix cores apply the block scales (scaled 32x32x64 FP8 MFMA), so a
+ * product needs no separate rescaling.  Codes and scales are k-contiguous:
+ * codes [rows][K] bytes, scales [rows][K/32] bytes.
+ */
+
+/* One layer's MXFP8 weights (device memory, caller-owned). */
+typedef struct {
+  const void* W1;         /* [F1][D] E4M3 codes: W1 transposed, blocks along D */
+  const void* W1_scales;  /* [F1][D/32] E8M0 */
+  const void* W2;         /* [D][H*d_v] codes: W2 transposed, blocks along H*d_v */
+  const void* W2_scales;  /* [D][H*d_v/32] */
+} hstu_mx_weights;
+
+/* MXFP8 of rows x K bf16 values (row stride ld, blocks along each row;
+ * K a multiple of 32, x and codes 16-byte aligned, ld a multiple of 8). */
+hstu_status hstu_mx_quantize(int64_t rows, int64_t K, const void* x, int64_t ld, void* codes,
+                             void* scales, void* stream);
+/* MXFP8 of a [K][N] bf16 weight along K, written transposed: codes [N][K],
+ * scales [N][K/32] (K a multiple of 32). */
+hstu_status hstu_mx_quantize_weight(int64_t K, int64_t N, const void* w, void* codes,
+                                    void* scales, void* stream);
+/* C [M][ldc] fp32 = A B^T for MXFP8 A [M][K] and B [N][K] (K a multiple of
+ * 128; codes and C 16-byte aligned, scale arrays 4-byte aligned). */
+hstu_status hstu_mx_gemm(int64_t M, int64_t N, int64_t K, const void* a, const void* a_scales,
+                         const void* b, const void* b_scales, float* c, int64_t ldc,
+                         void* stream);
+/*
+ * Inference forward of one layer with MXFP8 projection and output products
+ * (X and the gated LayerNorm G are quantized on the fly; attention,
+ * LayerNorm and gating in bf16 / fp32 as in hstu_layer_fwd).  `w` supplies
+ * the biases, LayerNorm affine and bias tables (its W1, W2 are not read);
+ * `wm` the MXFP8 weights.  g_codes [T][H*d_v] and g_scales [T][H*d_v/32],
+ * both NULL or both given (16- and 4-byte aligned), receive the quantized
+ * gated output G that the output product consumed.  bf16 only, D and H*d_v
+ * multiples of 128.
+ */
+size_t hstu_layer_fwd_mx_workspace_size(const hstu_layer_desc* desc);
+hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* desc, const void* x,
+                              const hstu_layer_weights* w, const hstu_mx_weights* wm,
+                              const int32_t* seq_offsets, const int64_t* timestamps,
+                              const int32_t* num_candidates, void* y, void* g_codes,
+                              void* g_scales, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* ---- ranking against a cached history --------------------------------- */
 /*
  * "DLRMv4 Brings Sequence-Based Recommendation Training to MLPerf", "Model

@@ -618,9 +618,10 @@ def mx_matmul(a, b):
 
 
 def layer_fwd_mx(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
-                 f: LayerFlags, b1=None, b2=None, gamma=None, beta=None):
+                 f: LayerFlags, b1=None, b2=None, gamma=None, beta=None, return_g=False):
     """One layer with MXFP8 projection and output matmuls (steps 1 and 4);
-    attention, LayerNorm and gating as in layer_fwd."""
+    attention, LayerNorm and gating as in layer_fwd.  return_g: also the
+    gated output G before its quantization."""
     X = np.asarray(X, np.float64)
     Z = mx_matmul(X, W1)
     if b1 is not None:
@@ -630,9 +631,10 @@ def layer_fwd_mx(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_cand
     O = attn_fwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
                  f.norm_mode, f.norm_len, win_local=f.win_local, win_global=f.win_global)
     Yn, _, _, _ = layernorm_fwd(O.reshape(X.shape[0], f.H * f.d_v), f.eps, gamma, beta)
-    Y = mx_matmul(Yn * U, W2)
+    G = Yn * U
+    Y = mx_matmul(G, W2)
     if b2 is not None:
         Y = Y + np.asarray(b2, np.float64)
     if f.residual:
         Y = Y + X
-    return Y
+    return (Y, G) if return_g else Y
