@@ -362,6 +362,87 @@ def bench_cached(timer, reps=5):
     return out
 
 
+def bench_mx(timer, reps=5):
+    """Inference forward of the ranking workload (4 layers) with bf16 products
+    against MXFP8 projection and output products (attention bf16 in both)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from hstu_sequential_transduction_amd import binding as B
+    from hstu_sequential_transduction_amd import flops
+    cfg = synth.get_config(5)
+    inp = synth.make_inputs(cfg)
+    td = torch.bfloat16
+    X = torch.from_numpy(inp.X).to(td).cuda()
+    offs = torch.from_numpy(inp.seq_offsets.astype(np.int32)).cuda()
+    ts = torch.from_numpy(inp.timestamps).cuda()
+    nc = torch.from_numpy(inp.num_candidates.astype(np.int32)).cuda()
+    lay = [upload_layer(inp, cfg, li) for li in range(cfg.n_layers)]
+    mxw = [B.MxLayerWeights.from_bf16(w["W1"], w["W2"]) for w in lay]
+    ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len)
+    lc = B.LayerConfig(D=cfg.D, attn=ac)
+    ws = B.LayerWorkspace()
+    bufs = [torch.empty_like(X), torch.empty_like(X)]
+
+    def run_bf16():
+        x = X
+        for li, w in enumerate(lay):
+            x = B.hstu_layer_fwd(x, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc,
+                                 num_candidates=nc, y=bufs[li % 2], workspace=ws)
+
+    # each layer's output product also writes its Y in MXFP8 for the next
+    # layer, so only the first layer quantizes its input
+    T, D = inp.T, cfg.D
+    mxb = [(torch.empty((T, D), dtype=torch.uint8, device="cuda"),
+            torch.empty((T, D // 32), dtype=torch.uint8, device="cuda")) for _ in range(2)]
+
+    def run_mx():
+        x, x_mx = X, None
+        for li, (w, m) in enumerate(zip(lay, mxw)):
+            y_mx = mxb[li % 2] if li + 1 < len(lay) else None
+            x = B.hstu_layer_fwd_mx(x, m, w["rp"], w["rt"], offs, ts, lc, num_candidates=nc,
+                                    y=bufs[li % 2], workspace=ws, x_mx=x_mx, y_mx=y_mx)
+            x_mx = y_mx
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        timer.enable(64 * reps * cfg.n_layers)
+        timer.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        kern = timer.read()
+        timer.enable(0)
+        return e0.elapsed_time(e1) / reps, {k: round(v[1] / reps, 4) for k, v in kern.items()}
+
+    ms_b, kb = timed(run_bf16)
+    ms_m, km = timed(run_mx)
+    proj = 2.0 * T * cfg.D * cfg.f1_width * cfg.n_layers
+    outp = 2.0 * T * cfg.H * cfg.d_v * cfg.D * cfg.n_layers
+    tf = lambda fl, ms: round(fl / (ms * 1e-3) / 1e12, 2) if ms else None
+    lf = flops.layer_flops(inp.lengths, inp.num_candidates, cfg.D, cfg.H, cfg.d_qk, cfg.d_v,
+                           backward=False)["total"] * cfg.n_layers
+    out = {"workload": "ranking batch 16 x (4096 history + 512 candidates), d_model 256, "
+                       "4 heads x 64, 4 layers, inference",
+           "format": "MXFP8 (E4M3, E8M0 scale per 32 along the contraction) for the "
+                     "projection and output products; attention bf16",
+           "bf16_ms": round(ms_b, 4), "mx_ms": round(ms_m, 4),
+           "speedup": round(ms_b / ms_m, 3),
+           "tflops_bf16": tf(lf, ms_b), "tflops_mx": tf(lf, ms_m),
+           "proj_gemm_tflops_bf16": tf(proj, kb.get("gemm_uvqk")),
+           "proj_gemm_tflops_mx": tf(proj, km.get("gemm_uvqk")),
+           "out_gemm_tflops_bf16": tf(outp, kb.get("gemm_out")),
+           "out_gemm_tflops_mx": tf(outp, km.get("gemm_out")),
+           "kernel_ms_bf16": kb, "kernel_ms_mx": km}
+    log(f"mxfp8: {out}")
+    return out
+
+
 def roofline(cfg, inp, kern, steps, traffic_dir):
     work = kernel_work(cfg, inp.lengths, inp.T)
     best = max(((ms, name, n) for name, (n, ms) in kern.items() if name in work), default=None)
@@ -499,7 +580,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the forward-only workloads, the semi-local training step, "
-                         "the attention-truncation forward and the cached ranking")
+                         "the attention-truncation forward, the cached ranking and the MXFP8 forward")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
@@ -520,6 +601,7 @@ def main():
     semi = None if args.no_extra else bench_semilocal(args, timer, ms)
     trunc = None if args.no_extra else bench_truncation(timer)
     cached = None if args.no_extra else bench_cached(timer)
+    mx = None if args.no_extra else bench_mx(timer)
     cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, inp)
     line = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -540,6 +622,7 @@ def main():
         "semilocal": semi,
         "truncation": trunc,
         "cached_ranking": cached,
+        "mxfp8": mx,
     }
     print(json.dumps(line), flush=True)
 

@@ -70,6 +70,11 @@ class MxWeights(C.Structure):
                 ("W2_scales", C.c_void_p)]
 
 
+class MxIO(C.Structure):
+    _fields_ = [("x_codes", C.c_void_p), ("x_scales", C.c_void_p), ("y_codes", C.c_void_p),
+                ("y_scales", C.c_void_p), ("g_codes", C.c_void_p), ("g_scales", C.c_void_p)]
+
+
 class HistoryKV(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("ld_k", C.c_int64), ("ld_v", C.c_int64),
                 ("offsets", C.c_void_p), ("timestamps", C.c_void_p), ("T", C.c_int64)]
@@ -142,7 +147,7 @@ def lib() -> C.CDLL:
     L.hstu_layer_fwd_mx_workspace_size.argtypes = [P(LayerDesc)]
     L.hstu_layer_fwd_mx.restype = C.c_int
     L.hstu_layer_fwd_mx.argtypes = [P(LayerDesc), vp, P(LayerWeights), P(MxWeights), vp, vp, vp,
-                                    vp, vp, vp, vp, sz, vp]
+                                    vp, P(MxIO), vp, sz, vp]
     L.hstu_attn_cached_workspace_size.restype = sz
     L.hstu_attn_cached_workspace_size.argtypes = [P(AttnDesc), i64]
     L.hstu_attn_cached_fwd.restype = C.c_int

@@ -14,7 +14,7 @@ import torch
 
 from . import _lib
 from ._lib import (AttnDesc, HistoryKV, LayerDesc, LayerGrads, LayerSaved, LayerWeights,
-                   MxWeights, check)
+                   MxIO, MxWeights, check)
 
 _DT = {torch.float32: _lib.HSTU_F32, torch.bfloat16: _lib.HSTU_BF16}
 
@@ -351,10 +351,11 @@ class MxLayerWeights:
 def hstu_layer_fwd_mx(x, wm: MxLayerWeights, rab_pos, rab_time, seq_offsets, timestamps,
                       cfg: LayerConfig, num_candidates=None, b1=None, b2=None, gamma=None,
                       beta=None, y=None, workspace: Optional[LayerWorkspace] = None, stream=None,
-                      g_out=None):
-    """Y of one layer with MXFP8 projection and output products (inference);
-    g_out = (codes [T, H*d_v] uint8, scales [T, H*d_v/32] uint8) receives the
-    quantized gated output the output product used."""
+                      g_out=None, x_mx=None, y_mx=None):
+    """Y of one layer with MXFP8 projection and output products (inference).
+    Optional (codes, scales) pairs: x_mx holds x already in MXFP8 (e.g. the
+    previous layer's y_mx), y_mx receives y in MXFP8, g_out the quantized
+    gated output the output product used."""
     T = x.shape[0]
     B = seq_offsets.shape[0] - 1
     if y is None:
@@ -365,9 +366,10 @@ def hstu_layer_fwd_mx(x, wm: MxLayerWeights, rab_pos, rab_time, seq_offsets, tim
     ws = workspace.get(nb, x.device) if workspace is not None else _ws(nb, x.device)
     w = _weights(None, None, rab_pos, rab_time, b1, b2, gamma, beta)
     m = wm.c()
-    gc, gs = (None, None) if g_out is None else g_out
+    pair = lambda p: (None, None) if p is None else (_ptr(p[0]), _ptr(p[1]))
+    io = MxIO(*pair(x_mx), *pair(y_mx), *pair(g_out))
     st = L.hstu_layer_fwd_mx(C.byref(d), _ptr(x), C.byref(w), C.byref(m), _ptr(seq_offsets),
-                             _ptr(timestamps), _ptr(num_candidates), _ptr(y), _ptr(gc), _ptr(gs),
+                             _ptr(timestamps), _ptr(num_candidates), _ptr(y), C.byref(io),
                              _ptr(ws), ws.numel(), _stream(stream))
     check("hstu_layer_fwd_mx", st)
     return y

@@ -387,8 +387,11 @@ struct MxPlan {
   const hstu_mx_weights* wm = nullptr;
   uint8_t* x8 = nullptr;
   uint8_t* xs = nullptr;
+  bool x_ready = false;   // x8/xs already hold X (given by the caller)
   uint8_t* g8 = nullptr;
   uint8_t* gs = nullptr;
+  uint8_t* y8 = nullptr;  // optional MXFP8 copy of Y (the next layer's X)
+  uint8_t* ys = nullptr;
 };
 
 template <typename Attn>
@@ -425,7 +428,10 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
   }
   if (mx) {
     // X -> MXFP8 (blocks of 32 along d_model), W1 given as [F1][D] codes
-    { HSTU_TIMED(TT_MX_QUANT, st); HSTU_TRY(launch_mx_quant_rows(x, D, T, D, mx->x8, mx->xs, st)); }
+    if (!mx->x_ready) {
+      HSTU_TIMED(TT_MX_QUANT, st);
+      HSTU_TRY(launch_mx_quant_rows(x, D, T, D, mx->x8, mx->xs, st));
+    }
     g1.mx = true;
     g1.A = mx->x8;
     g1.lda = D / 2;
@@ -462,6 +468,11 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
   la.ld_g = W;
   la.mu = mu;
   la.rstd = rstd;
+  if (mx) {
+    // G straight to MXFP8 for the output product
+    la.g_codes = mx->g8;
+    la.g_scales = mx->gs;
+  }
   { HSTU_TIMED(TT_LN_FWD, st); HSTU_TRY(launch_ln_gate_fwd(la, d->dtype, st)); }
   // 4. Y = G W2 (+ b2) (+ X)
   GemmArgs g2;
@@ -481,8 +492,8 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
   g2.R = L->residual ? x : nullptr;
   g2.ldr = D;
   if (mx) {
-    // G -> MXFP8 (blocks of 32 along H d_v), W2 given as [D][H d_v] codes
-    { HSTU_TIMED(TT_MX_QUANT, st); HSTU_TRY(launch_mx_quant_rows(G, W, T, W, mx->g8, mx->gs, st)); }
+    // G as MXFP8 (blocks of 32 along H d_v, written by the LayerNorm
+    // kernel), W2 given as [D][H d_v] codes
     g2.mx = true;
     g2.A = mx->g8;
     g2.lda = W / 2;
@@ -492,6 +503,8 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
     g2.b_kcont = true;
     g2.scale_a = mx->gs;
     g2.scale_b = static_cast<const uint8_t*>(mx->wm->W2_scales);
+    g2.c_codes = mx->y8;
+    g2.c_scales = mx->ys;
   }
   { HSTU_TIMED(TT_GEMM_OUT, st); HSTU_TRY(launch_gemm(g2, d->dtype, st)); }
   return HSTU_OK;
@@ -690,8 +703,8 @@ size_t hstu_layer_fwd_mx_workspace_size(const hstu_layer_desc* L) {
 
 hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
                               const hstu_mx_weights* wm, const int32_t* offs, const int64_t* ts,
-                              const int32_t* nc, void* y, void* g_codes, void* g_scales,
-                              void* ws, size_t ws_bytes, void* stream) {
+                              const int32_t* nc, void* y, const hstu_mx_io* io, void* ws,
+                              size_t ws_bytes, void* stream) {
   hstu_status s = check_mx_layer(L);
   if (s != HSTU_OK) return s;
   const hstu_attn_desc* d = &L->attn;
@@ -700,9 +713,15 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
     return HSTU_ERR_INVALID_ARG;
   if (d->T > 0 && (!x || !y || !ts)) return HSTU_ERR_INVALID_ARG;
   if (x == y && d->T > 0) return HSTU_ERR_INVALID_ARG;
-  if ((g_codes == nullptr) != (g_scales == nullptr) || !aligned16(g_codes) ||
-      (reinterpret_cast<uintptr_t>(g_scales) & 3))
-    return HSTU_ERR_INVALID_ARG;
+  if (io) {
+    auto pair_ok = [](const void* c, const void* sc) {
+      return (c == nullptr) == (sc == nullptr) && aligned16(c) &&
+             (reinterpret_cast<uintptr_t>(sc) & 3) == 0;
+    };
+    if (!pair_ok(io->x_codes, io->x_scales) || !pair_ok(io->y_codes, io->y_scales) ||
+        !pair_ok(io->g_codes, io->g_scales))
+      return HSTU_ERR_INVALID_ARG;
+  }
   if (!aligned16(x) || !aligned16(y) || !aligned16(wm->W1) || !aligned16(wm->W2) ||
       (reinterpret_cast<uintptr_t>(wm->W1_scales) & 3) ||
       (reinterpret_cast<uintptr_t>(wm->W2_scales) & 3))
@@ -724,8 +743,21 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
   plan.wm = wm;
   plan.x8 = m.x8;
   plan.xs = m.xs;
-  plan.g8 = g_codes ? static_cast<uint8_t*>(g_codes) : m.g8;
-  plan.gs = g_scales ? static_cast<uint8_t*>(g_scales) : m.gs;
+  plan.g8 = m.g8;
+  plan.gs = m.gs;
+  if (io && io->x_codes) {
+    plan.x8 = static_cast<uint8_t*>(const_cast<void*>(io->x_codes));
+    plan.xs = static_cast<uint8_t*>(const_cast<void*>(io->x_scales));
+    plan.x_ready = true;
+  }
+  if (io && io->g_codes) {
+    plan.g8 = static_cast<uint8_t*>(io->g_codes);
+    plan.gs = static_cast<uint8_t*>(io->g_scales);
+  }
+  if (io && io->y_codes) {
+    plan.y8 = static_cast<uint8_t*>(io->y_codes);
+    plan.ys = static_cast<uint8_t*>(io->y_scales);
+  }
   return layer_fwd_steps(L, x, w, y, nullptr, lw.Zh, O, lw.G, nullptr, nullptr, attention, st,
                          &plan);
 }

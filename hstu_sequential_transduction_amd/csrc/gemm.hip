@@ -14,6 +14,7 @@
 #include "common.h"
 #include "internal.h"
 #include "lds.h"
+#include "mx.h"
 
 namespace hstu {
 
@@ -552,6 +553,25 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
       } else {
         put(g.C, v, OUTF32);
       }
+      if constexpr (MX && EPI == EPI_RESID && !OUTF32) {
+        if (g.c_codes) {
+          // MXFP8 copy of the stored (bf16-rounded) row values: the eight
+          // lanes of a 32-column block share the row, so their amax is a
+          // three-step shuffle (all eight skip rows past M together)
+          float q[4], am = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            q[e] = (float)(bf16)v[e];
+            am = fmaxf(am, fabsf(q[e]));
+          }
+#pragma unroll
+          for (int o = 1; o < 8; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+          const int sh = mx_shared_exp(am);
+          *reinterpret_cast<uint32_t*>(g.c_codes + m * g.N + ncol) =
+              mx_cvt4(q[0], q[1], q[2], q[3], sh);
+          if ((lc & 7) == 0) g.c_scales[m * (g.N / 32) + ncol / 32] = (uint8_t)(sh + 127);
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -747,6 +767,9 @@ hipError_t gemm2_mx(const GemmArgs& g, hipStream_t st) {
   if (!g.a_kcont || !g.b_kcont || !g.scale_a || !g.scale_b || !gemm2_ok(g))
     return hipErrorInvalidValue;
   if ((reinterpret_cast<uintptr_t>(g.scale_a) & 3) || (reinterpret_cast<uintptr_t>(g.scale_b) & 3))
+    return hipErrorInvalidValue;
+  if (g.c_codes && (g.epi != EPI_RESID || g.c_f32 || (g.N % 32) || !g.c_scales ||
+                    (reinterpret_cast<uintptr_t>(g.c_codes) & 3)))
     return hipErrorInvalidValue;
   constexpr int BM = 128, BN = 128, NT = 64 * G2_NW;
   const int mt = (int)((g.M + BM - 1) / BM), nt = (int)((g.N + BN - 1) / BN);

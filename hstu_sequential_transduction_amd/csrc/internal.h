@@ -184,6 +184,10 @@ struct GemmArgs {
   bool mx = false;
   const uint8_t* scale_a = nullptr;
   const uint8_t* scale_b = nullptr;
+  // MX kernels, EPI_RESID with bf16 C: also write C as MXFP8 along N
+  // (codes [M][N], scales [M][N/32]; N a multiple of 32)
+  uint8_t* c_codes = nullptr;
+  uint8_t* c_scales = nullptr;
 };
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st);
 // Split-K reduction: out[m*ldo + n] = sum_z partial[z][m][n]  (fp32)
@@ -209,6 +213,10 @@ struct LnArgs {
   int64_t ld_g = 0;
   float* mu = nullptr;       // [T] or null
   float* rstd = nullptr;     // [T] or null
+  // forward, bf16: write G as MXFP8 (codes [T][W], scales [T][W/32]) instead
+  // of G itself (the rounding of the bf16 value G would have been stored as)
+  uint8_t* g_codes = nullptr;
+  uint8_t* g_scales = nullptr;
   // backward
   const void* dG = nullptr;  int64_t ld_dg = 0;
   void* dU = nullptr;        int64_t ld_du = 0;   // written as dU * SiLU'(Zu) if zu != null

@@ -13,6 +13,9 @@
 // and per-workgroup partial column sums for dgamma/dbeta.
 #include "common.h"
 #include "internal.h"
+#include "mx.h"
+
+#include <type_traits>
 
 namespace hstu {
 
@@ -83,7 +86,7 @@ HSTU_DEV void store_row(T* row, int c0, int W, const float* x) {
   }
 }
 
-template <int EPL, bool VEC, typename T, typename TO>
+template <int EPL, bool VEC, typename T, typename TO, bool MXO = false>
 __global__ __launch_bounds__(256) void k_ln_gate_fwd(LnArgs a) {
   const int lane = threadIdx.x & 63;
   const int W = a.W;
@@ -129,7 +132,36 @@ __global__ __launch_bounds__(256) void k_ln_gate_fwd(LnArgs a) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e)
         gv[e] = fmaf((x[k][e] - mean) * rstd, gam[e], bet[e]) * u[k][e];
-      store_row<EPL, VEC>(G + rr[k] * a.ld_g, c0, W, gv);
+      if constexpr (MXO) {
+        // MXFP8 of the bf16-rounded G: a 32-value block spans 32 / EPL lanes
+        constexpr int LPB = 32 / EPL;
+        float am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          gv[e] = (float)(bf16)gv[e];
+          am = fmaxf(am, fabsf(gv[e]));
+        }
+#pragma unroll
+        for (int o = 1; o < LPB; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+        const int sh = mx_shared_exp(am);
+        uint32_t cw[EPL / 4];
+#pragma unroll
+        for (int q = 0; q < EPL / 4; ++q)
+          cw[q] = mx_cvt4(gv[4 * q], gv[4 * q + 1], gv[4 * q + 2], gv[4 * q + 3], sh);
+        uint8_t* dst = a.g_codes + rr[k] * W + c0;
+        if constexpr (EPL == 4) {
+          *reinterpret_cast<uint32_t*>(dst) = cw[0];
+        } else if constexpr (EPL == 8) {
+          *reinterpret_cast<uint2*>(dst) = uint2{cw[0], cw[1]};
+        } else {
+#pragma unroll
+          for (int q = 0; q < EPL / 16; ++q)
+            reinterpret_cast<u32x4*>(dst)[q] = u32x4{cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]};
+        }
+        if (lane % LPB == 0) a.g_scales[rr[k] * (W / 32) + c0 / 32] = (uint8_t)(sh + 127);
+      } else {
+        store_row<EPL, VEC>(G + rr[k] * a.ld_g, c0, W, gv);
+      }
       if (lane == 0) {
         if (a.mu) a.mu[rr[k]] = mean;
         if (a.rstd) a.rstd[rr[k]] = rstd;
@@ -258,7 +290,17 @@ hipError_t fwd_t(const LnArgs& a, hipStream_t st) {
   if (blocks > 4096) blocks = 4096;
   if (blocks <= 0) return hipSuccess;
   const unsigned grid = (unsigned)blocks;
-  if (vec_ok<T, TO>(a, epl_for(a.W))) {
+  if (a.g_codes) {
+    // MXFP8 output: bf16, whole rows of 4, 8 or 16 values per lane
+    if (!std::is_same<T, bf16>::value || !vec_ok<T, TO>(a, epl_for(a.W)) || !a.g_scales)
+      return hipErrorInvalidValue;
+    switch (epl_for(a.W)) {
+      case 4: k_ln_gate_fwd<4, true, T, TO, true><<<grid, 256, 0, st>>>(a); break;
+      case 8: k_ln_gate_fwd<8, true, T, TO, true><<<grid, 256, 0, st>>>(a); break;
+      case 16: k_ln_gate_fwd<16, true, T, TO, true><<<grid, 256, 0, st>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (vec_ok<T, TO>(a, epl_for(a.W))) {
     HSTU_LN_CASES(k_ln_gate_fwd, T, TO, true, grid)
   } else {
     HSTU_LN_CASES(k_ln_gate_fwd, T, TO, false, grid)

@@ -6,16 +6,15 @@
 // Every 32 consecutive values along the contraction index form a block with
 // one E8M0 scale byte e (value 2^(e-127)): the block's shared exponent is
 // floor(log2(amax)) - 8 (8 = the exponent of E4M3's largest power of two),
-// so value / 2^shared lies in [0, 512) and is rounded to E4M3 (nearest,
-// ties to even, the 448 saturation applied in fp32 before the conversion
-// instruction, which rounds to nearest even).  Division by the power of two
-// is exact, so the codes depend on the inputs alone.  An all-zero block
-// gets e = 0 and zero codes.
+// so value / 2^shared lies in [0, 512) and is rounded to E4M3 (see mx.h).
+// Division by the power of two is exact, so the codes depend on the inputs
+// alone.  An all-zero block gets e = 0 and zero codes.
 //
 // Outputs are k-contiguous: codes [rows][K] bytes, scales [rows][K/32]
 // bytes, the layout the MX GEMM streams into LDS.
 #include "common.h"
 #include "internal.h"
+#include "mx.h"
 
 namespace hstu {
 namespace {
@@ -25,22 +24,10 @@ HSTU_DEV int mx_block(const float (&v)[32], uint32_t (&out)[8]) {
   float amax = 0.0f;
 #pragma unroll
   for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(v[e]));
-  int shared = -127;
-  if (amax > 0.0f) {
-    // frexp: amax = f 2^x with f in [0.5, 1), so floor(log2(amax)) = x - 1
-    shared = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
-    shared = min(max(shared, -127), 127);
-  }
+  const int shared = mx_shared_exp(amax);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    float x[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      x[e] = fminf(fmaxf(ldexpf(v[4 * q + e], -shared), -448.0f), 448.0f);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], w, true);
-    out[q] = (uint32_t)w;
-  }
+  for (int q = 0; q < 8; ++q)
+    out[q] = mx_cvt4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], shared);
   return shared + 127;
 }
 

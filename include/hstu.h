@@ -266,18 +266,27 @@ hstu_status hstu_mx_gemm(int64_t M, int64_t N, int64_t K, const void* a, const v
  * (X and the gated LayerNorm G are quantized on the fly; attention,
  * LayerNorm and gating in bf16 / fp32 as in hstu_layer_fwd).  `w` supplies
  * the biases, LayerNorm affine and bias tables (its W1, W2 are not read);
- * `wm` the MXFP8 weights.  g_codes [T][H*d_v] and g_scales [T][H*d_v/32],
- * both NULL or both given (16- and 4-byte aligned), receive the quantized
- * gated output G that the output product consumed.  bf16 only, D and H*d_v
- * multiples of 128.
+ * `wm` the MXFP8 weights; `io` (may be NULL) the optional MXFP8 inputs and
+ * outputs below.  bf16 only, D and H*d_v multiples of 128.
  */
+typedef struct {
+  /* x already in MXFP8 ([T][D] codes, [T][D/32] scales): skips its
+   * quantization, e.g. the y_codes/y_scales of the previous layer */
+  const void* x_codes;
+  const void* x_scales;
+  /* also write y in MXFP8 (same layout), for the next layer */
+  void* y_codes;
+  void* y_scales;
+  /* receive the quantized gated output G ([T][H*d_v], [T][H*d_v/32]) */
+  void* g_codes;
+  void* g_scales;
+} hstu_mx_io;  /* each pair NULL or both given; codes 16-, scales 4-byte aligned */
 size_t hstu_layer_fwd_mx_workspace_size(const hstu_layer_desc* desc);
 hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* desc, const void* x,
                               const hstu_layer_weights* w, const hstu_mx_weights* wm,
                               const int32_t* seq_offsets, const int64_t* timestamps,
-                              const int32_t* num_candidates, void* y, void* g_codes,
-                              void* g_scales, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              const int32_t* num_candidates, void* y, const hstu_mx_io* io,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- ranking against a cached history --------------------------------- */
 /*

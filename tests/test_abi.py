@@ -122,7 +122,8 @@ def test_descriptor_layouts_match_the_header(tmp_path):
         pytest.skip("no C compiler")
     structs = {"hstu_attn_desc": _lib.AttnDesc, "hstu_layer_desc": _lib.LayerDesc,
                "hstu_layer_weights": _lib.LayerWeights, "hstu_layer_saved": _lib.LayerSaved,
-               "hstu_layer_grads": _lib.LayerGrads, "hstu_history_kv": _lib.HistoryKV}
+               "hstu_layer_grads": _lib.LayerGrads, "hstu_history_kv": _lib.HistoryKV,
+               "hstu_mx_weights": _lib.MxWeights, "hstu_mx_io": _lib.MxIO}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hstu.h"', "int main(void) {"]
     for cname, ct in structs.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')

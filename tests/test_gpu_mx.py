@@ -147,3 +147,34 @@ def test_mx_layer_fwd(B, ci, hist, c, variant):
     # FP8's own rounding (3 mantissa bits, two chained products): an accuracy
     # figure of the format, not a parity bound
     assert rel < 0.15
+
+
+def test_mx_layer_chain_hands_y_codes_to_the_next_layer(B):
+    """The output product's epilogue writes Y in MXFP8 for the next layer:
+    those codes equal the quantizer's on the stored bf16 Y, and a two-layer
+    chain that passes them on is bit-identical to one quantizing X itself."""
+    import torch
+    cfg = synth.get_config(5).shrunk(B=4, lengths=("list", [100, 300, 0, 64]), num_candidates=40,
+                                     n_layers=2).unit_scale()
+    say("mx layer chain cfg5 2 layers")
+    inp = synth.make_inputs(cfg, seed=1800)
+    td = torch.bfloat16
+    T, D = inp.T, cfg.D
+    lc = _lcfg(B, cfg)
+    offs, ts = dev(inp.seq_offsets.astype(np.int32)), dev(inp.timestamps)
+    nc = dev(inp.num_candidates.astype(np.int32))
+    ws = [(dev(w.rab_pos), dev(w.rab_time),
+           B.MxLayerWeights.from_bf16(dev(w.W1, td), dev(w.W2, td))) for w in inp.layers]
+    x0 = dev(inp.X, td)
+    yc = torch.empty((T, D), dtype=torch.uint8, device="cuda")
+    ys = torch.empty((T, D // 32), dtype=torch.uint8, device="cuda")
+    y1 = B.hstu_layer_fwd_mx(x0, ws[0][2], ws[0][0], ws[0][1], offs, ts, lc, num_candidates=nc,
+                             y_mx=(yc, ys))
+    qc, qs = B.hstu_mx_quantize(y1)
+    np.testing.assert_array_equal(host(ys), host(qs))
+    np.testing.assert_array_equal(host(yc), host(qc))
+    chained = B.hstu_layer_fwd_mx(y1, ws[1][2], ws[1][0], ws[1][1], offs, ts, lc,
+                                  num_candidates=nc, x_mx=(yc, ys))
+    plain = B.hstu_layer_fwd_mx(y1, ws[1][2], ws[1][0], ws[1][1], offs, ts, lc,
+                                num_candidates=nc)
+    np.testing.assert_array_equal(host(chained), host(plain))
