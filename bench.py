@@ -41,8 +41,10 @@ def source_hash(kernel: str) -> str:
     return sh(kernel)
 
 
-def kernel_work(cfg, lengths, T, cand=None):
-    """Algorithmic work per launch of each kernel tag: (kind, amount)."""
+def kernel_work(cfg, lengths, T, cand=None, keep_ds=True):
+    """Algorithmic work per launch of each kernel tag: (kind, amount).  With
+    dS kept by the dK/dV kernel, dQ is the single product dS K (and the dK/dV
+    kernel also writes dS: 2 bytes per pair and head of the causal blocks)."""
     from hstu_sequential_transduction_amd import flops
     H, dq, dv, D = cfg.H, cfg.d_qk, cfg.d_v, cfg.D
     W, F1 = H * dv, cfg.f1_width
@@ -51,7 +53,7 @@ def kernel_work(cfg, lengths, T, cand=None):
         "attn_fwd": ("mfma", 2 * P * H * (dq + dv)),
         # the products each backward kernel's outputs need: S, dA, dV, dK / S, dA, dQ
         "attn_bwd_dkdv": ("mfma", 2 * P * H * (2 * dq + 2 * dv)),
-        "attn_bwd_dq": ("mfma", 2 * P * H * (2 * dq + dv)),
+        "attn_bwd_dq": ("mfma", 2 * P * H * (dq if keep_ds else (2 * dq + dv))),
         "gemm_uvqk": ("mfma", 2.0 * T * D * F1),
         "gemm_out": ("mfma", 2.0 * T * W * D),
         "gemm_dG": ("mfma", 2.0 * T * D * W),
@@ -114,8 +116,10 @@ def bench_train(args, timer, window=(0, 0)):
     offs = torch.from_numpy(inp.seq_offsets.astype(np.int32)).cuda()
     ts = torch.from_numpy(inp.timestamps).cuda()
     w = upload_layer(inp, cfg)
+    # max_len: the workload's longest sequence, which lets the backward keep dS
     ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len,
-                      win_local=window[0], win_global=window[1])
+                      win_local=window[0], win_global=window[1],
+                      max_len=int(inp.lengths.max()))
     lc = B.LayerConfig(D=cfg.D, attn=ac)
     saved = B.Saved(T, lc, td, "cuda")
     y = torch.empty_like(X)

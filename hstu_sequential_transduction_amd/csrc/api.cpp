@@ -48,7 +48,7 @@ hstu_status check_attn_desc(const hstu_attn_desc* d) {
   if (d->n_time_buckets < 1 || d->n_time_buckets > 1024) return HSTU_ERR_UNSUPPORTED;
   if (d->norm_mode != 0 && d->norm_mode != 1) return HSTU_ERR_INVALID_ARG;
   if (d->norm_mode == 0 && d->norm_len <= 0) return HSTU_ERR_INVALID_ARG;
-  if (d->win_local < 0 || d->win_global < 0) return HSTU_ERR_INVALID_ARG;
+  if (d->win_local < 0 || d->win_global < 0 || d->max_len < 0) return HSTU_ERR_INVALID_ARG;
   if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
   if (d->rab_head_stride < 0) return HSTU_ERR_INVALID_ARG;
   if (d->rab_head_stride != 0 &&
@@ -76,15 +76,38 @@ FwdWs carve_fwd(Carver& c, const hstu_attn_desc* d) {
   return w;
 }
 
+// The backward keeps dS (the scores' gradient) when max_len bounds the
+// batch: 128 x 128 bf16 blocks of the causal part; with n_b <= max_len the
+// blocks number at most H (R + 1) / 2 sum_b ceil(n_b / 128), R = ceil(max_len / 128).
+bool keeps_ds(const hstu_attn_desc* d) {
+  return d->max_len > 0 && d->dtype == HSTU_BF16 && d->d_qk == 128 && d->d_v == 128 &&
+         d->win_local == 0;
+}
+int64_t ds_capacity_blocks(const hstu_attn_desc* d) {
+  const int64_t R = (d->max_len + 127) / 128;
+  const int64_t rows = (d->T + 127) / 128 + d->B;
+  return (int64_t)d->H * ((R + 1) * rows + 1) / 2;
+}
+
 struct BwdWs {
   TimeMeta tm;
   Sched kv, q;
+  uint16_t* ds = nullptr;
+  int32_t* ds_base = nullptr;
+  int32_t* ds_flag = nullptr;
+  int64_t ds_cap = 0;
 };
 BwdWs carve_bwd(Carver& c, const hstu_attn_desc* d) {
   BwdWs w;
   w.tm = carve_time(c, d->T, d->B);
   w.kv = carve_sched(c, d->T, d->B, ATTN_BWD_BN);
   w.q = carve_sched(c, d->T, d->B, ATTN_BWD_BM);
+  if (keeps_ds(d)) {
+    w.ds_cap = ds_capacity_blocks(d);
+    w.ds_base = c.take<int32_t>(std::max<int64_t>(d->B, 1));
+    w.ds_flag = c.take<int32_t>(1);
+    w.ds = c.take<uint16_t>(w.ds_cap * 128 * 128);
+  }
   return w;
 }
 
@@ -257,8 +280,17 @@ hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
     PlanArgs p = plan_prepass(w.tm, d->B, offs, ts, drp, drt, rab_floats(d));
     plan_add_job(p, w.kv, 1, offs);
     plan_add_job(p, w.q, 0, offs);
+    if (w.ds) {
+      p.ds_base = w.ds_base;
+      p.ds_flag = w.ds_flag;
+      p.ds_cap = w.ds_cap;
+      p.H = d->H;
+    }
     HSTU_TRY(launch_plan(p, st));
   }
+  a.ds = w.ds;
+  a.ds_base = w.ds_base;
+  a.ds_flag = w.ds_flag;
   AttnArgs akv = a;
   akv.items = w.kv.items;
   akv.counters = w.kv.counters;

@@ -155,7 +155,7 @@ struct KvTables {
   float gtime[32];    // d rab_time histogram (by clz index)
 };
 
-template <int DQK, int DV, bool WIN>
+template <int DQK, int DV, bool WIN, bool KEEP_DS = false>
 __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) void k_attn_bwd_dkdv(AttnArgs a) {
   constexpr bool WIDE = KvShape<DQK, DV>::WIDE;
   constexpr int NW = KvShape<DQK, DV>::NW, NT = KvShape<DQK, DV>::NT;
@@ -218,6 +218,19 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
   const bf16* kh_ = reinterpret_cast<const bf16*>(a.k) + (int64_t)o0 * a.ld_qk + h * DQK;
   const bf16* vh_ = reinterpret_cast<const bf16*>(a.v) + (int64_t)o0 * a.ld_v + h * DV;
   const bf16* doh = reinterpret_cast<const bf16*>(a.dout) + (int64_t)o0 * a.ld_dout + h * DV;
+
+  // kept dS (WIDE shape): the 128 x 128 blocks (key-major) of this key block
+  // kb, one per 128-row block rb >= kb (a wave-uniform base; each lane adds
+  // its key's row when it stores)
+  bf16* ds_kb = nullptr;
+  if constexpr (WIDE && KEEP_DS) {
+    if (a.ds && __builtin_amdgcn_readfirstlane(*a.ds_flag) == 0) {
+      const int64_t nrb = (n + 127) / 128;
+      const int64_t blk = __builtin_amdgcn_readfirstlane(a.ds_base[b]) + h * (nrb * (nrb + 1) / 2) +
+                          kb * nrb - (int64_t)kb * (kb - 1) / 2 - kb;
+      ds_kb = reinterpret_cast<bf16*>(a.ds) + blk * (128 * 128);
+    }
+  }
 
   // per-lane byte offsets of the S/dA row operands (row ql of a 32-row block,
   // chunk g; k-chunk ch adds 32 ch bytes): tile rows and (WIDE) key rows
@@ -451,6 +464,27 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
   };
 
   // near-phase tile: per-half masks and per-element buckets
+  // kept dS of one 32-row half (rows i0 + 32 qh .. of the tile starting at
+  // row i0): four 8-byte stores of four consecutive rows each.  ds_stores
+  // counts them for the tile's DMA wait (see run_phase).
+  int ds_stores = 0;
+  auto store_ds = [&](int i0, int qh, const bf16x8 (&dd)[2]) HSTU_INLINE_LAMBDA {
+    if constexpr (WIDE && KEEP_DS) {
+      if (ds_kb) {
+        ds_stores = 4;
+        bf16* dst = ds_kb + (int64_t)(i0 >> 7) * (128 * 128) +
+                    (((kg * 32 + (lane & 31)) * 128) + (i0 & 127) + qh * 32 + 4 * (lane >> 5));
+#pragma unroll
+        for (int aa = 0; aa < 4; ++aa) {
+          const bf16x8 v = dd[aa >> 1];
+          const bf16x4 q4 = (aa & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7)
+                                     : __builtin_shufflevector(v, v, 0, 1, 2, 3);
+          *reinterpret_cast<uint2*>(dst + 8 * aa) = __builtin_bit_cast(uint2, q4);
+        }
+      }
+    }
+  };
+
   auto near_tile = [&](const KvBuf<DQK, DV>& B, int i0) HSTU_INLINE_LAMBDA {
     if (kw0 >= kw1) return;
     for_halves([&](const int qh) HSTU_INLINE_LAMBDA {
@@ -459,6 +493,13 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       bool active;
       if (kw0 < nh) active = ir1 - 1 >= kw0;
       else active = ir0 < kw1 && ir1 > kw0;
+      if constexpr (KEEP_DS) {
+        if (!active && ir0 < ir1) {
+          // every pair of the half is masked: the kept dS block holds zeros there
+          const bf16x8 z[2] = {bf16x8{}, bf16x8{}};
+          store_ds(i0, qh, z);
+        }
+      }
       if (!active || ir0 >= ir1) return;
       // window: every row of the half past the window of every key of the wave
       if (wl > 0 && kw0 >= wg && kw1 <= nh && nh - (kw1 - 1) >= wl && ir0 >= kw1 - 1 + wl) return;
@@ -505,6 +546,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
               },
               bconst<true>{}, lo, hi, no4);
       }
+      store_ds(i0, qh, dd);
       mm_grad(B, qh, pp, dd);
     });
   };
@@ -556,6 +598,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
               },
               bconst<false>{}, 0, 0, no4);
       }
+      store_ds(i0, qh, dd);
       mm_grad(B, qh, pp, dd);
     });
   };
@@ -569,6 +612,19 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       i += KV_QT;
       return (i >= sk0 && i < sk1) ? sk1 : i;
     };
+    // The next tile's DMA is issued before the body, whose only vector-memory
+    // operations are the four kept-dS stores (when a half stored them).  The
+    // vector-memory counter retires in issue order, so vmcnt(4) means the DMA
+    // has landed while the stores may still be in flight.
+    auto tile_wait = [&]() HSTU_INLINE_LAMBDA {
+      if constexpr (KEEP_DS) {
+        if (ds_stores == 4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        else dma_wait();
+        ds_stores = 0;
+      } else {
+        dma_wait();
+      }
+    };
     issue(kvb0, ibeg);
     dma_wait();
     __syncthreads();
@@ -576,13 +632,13 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       const int i1 = next_row(i0);
       if (i1 < iend) issue(kvb1, i1);
       body(kvb0, i0);
-      dma_wait();
+      tile_wait();
       __syncthreads();
       if (i1 >= iend) break;
       const int i2 = next_row(i1);
       if (i2 < iend) issue(kvb0, i2);
       body(kvb1, i1);
-      dma_wait();
+      tile_wait();
       __syncthreads();
       i0 = i2;
     }
@@ -669,6 +725,8 @@ struct DqTables {
 
 template <int DQK, int DV, bool WIN>
 __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
+  // dS kept by the dK/dV kernel: dQ comes from k_attn_bwd_dq_ds instead
+  if (a.ds_flag && __builtin_amdgcn_readfirstlane(*a.ds_flag) == 0) return;
   __shared__ __attribute__((aligned(1024))) DqBuf<DQK, DV> dqb0;
   __shared__ __attribute__((aligned(1024))) DqBuf<DQK, DV> dqb1;
   __shared__ DqTables sm;
@@ -882,11 +940,126 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
                        reinterpret_cast<const bf16*>(a.zpre), a.ld_z, a.zq_col + h * DQK, ql, g);
 }
 
+// ===========================================================================
+// dQ from the kept dS (d_qk = 128): dQ_i = (1/N) sum_j dS_ij k_j as a tiled
+// product over the causal 128 x 128 blocks, with no recomputation of S, dA
+// or the SiLU terms.  Workgroup = (sequence, 128-row block rb, head), four
+// waves of 64 rows x 64 columns.  Per 64-key step the dS block rows (keys)
+// and the K rows arrive by DMA (rows past the sequence as zeros) and both are
+// read down their columns (transpose reads, the same k order for both).
+// Key blocks that hold only candidates are skipped except the diagonal one
+// (a candidate key is seen by its own row only).
+// ===========================================================================
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_ds(AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int TB = SwzTile<128>::bytes(64);  // one 64-key stage of dS or K
+  __shared__ __attribute__((aligned(1024))) uint8_t ta0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t tb0[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t ta1[TB];
+  __shared__ __attribute__((aligned(1024))) uint8_t tb1[TB];
+  if (__builtin_amdgcn_readfirstlane(*a.ds_flag) != 0) return;
+  const int w = blockIdx.x;
+  const int n_items = a.counters[0];
+  if (w >= n_items * a.H) return;
+  const int it = w / a.H, h = w - it * a.H;
+  const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
+  const int rb = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  const int o0 = __builtin_amdgcn_readfirstlane(a.seq_offsets[b]);
+  const int n = __builtin_amdgcn_readfirstlane(a.seq_offsets[b + 1]) - o0;
+  const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;
+  const int nh = n - c;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, ql = lane & 31, g = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t nrb = (n + 127) / 128;
+  const bf16* base = reinterpret_cast<const bf16*>(a.ds) +
+                     (__builtin_amdgcn_readfirstlane(a.ds_base[b]) + h * (nrb * (nrb + 1) / 2)) *
+                         (128 * 128);
+  const bf16* kh_ = reinterpret_cast<const bf16*>(a.k) + (int64_t)o0 * a.ld_qk + h * D;
+  // key blocks: the history blocks below rb, then rb itself (blocks holding
+  // only candidates are seen by their own rows only); a step is one 64-key
+  // half of a block, step index q -> block kb(q), half q & 1
+  const int kh_end = min(rb, (nh + 127) / 128);
+  const int nsteps = 2 * (kh_end + 1);
+  auto step_kb = [&](int q) HSTU_INLINE_LAMBDA { return (q >> 1) < kh_end ? (q >> 1) : rb; };
+  auto step_rows = [&](int q) HSTU_INLINE_LAMBDA {
+    return min(64, n - (step_kb(q) * 128 + 64 * (q & 1)));
+  };
+  auto issue = [&](uint8_t* ta, uint8_t* tb, int q) HSTU_INLINE_LAMBDA {
+    const int kb = step_kb(q);
+    const int krow = kb * 128 + 64 * (q & 1);
+    const int rlim = step_rows(q);
+    const bf16* blk = base + (kb * nrb - (int64_t)kb * (kb - 1) / 2 + rb - kb) * (128 * 128);
+    dma_tile<128, 64, 4>(ta, blk + 64 * (q & 1) * 128, 128, 0, rlim, wave, lane);
+    dma_tile<128, 64, 4>(tb, kh_ + (int64_t)krow * a.ld_qk, a.ld_qk, 0, rlim, wave, lane, D);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](const uint8_t* ta, const uint8_t* tb) HSTU_INLINE_LAMBDA {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = lds_col8<128>(ta, 16 * kc, wm * 64 + 32 * i, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[j] = lds_col8<128>(tb, 16 * kc, wn * 64 + 32 * j, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+  };
+
+  // double buffer over the steps (a second half past the sequence's end has
+  // no rows and is skipped), unrolled by two so that every access names its
+  // stage statically
+  auto next_step = [&](int q) HSTU_INLINE_LAMBDA {
+    ++q;
+    while (q < nsteps && step_rows(q) <= 0) ++q;
+    return q;
+  };
+  int q = next_step(-1);
+  if (q < nsteps) issue(ta0, tb0, q);
+  dma_wait();
+  __syncthreads();
+  while (q < nsteps) {
+    int nq = next_step(q);
+    if (nq < nsteps) issue(ta1, tb1, nq);
+    compute(ta0, tb0);
+    dma_wait();
+    __syncthreads();
+    q = nq;
+    if (q >= nsteps) break;
+    nq = next_step(q);
+    if (nq < nsteps) issue(ta0, tb0, nq);
+    compute(ta1, tb1);
+    dma_wait();
+    __syncthreads();
+    q = nq;
+  }
+  const float invN = 1.0f / (float)(a.norm_mode == 0 ? a.norm_len : n);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row0 = rb * 128 + wm * 64 + 32 * i;
+    if (row0 >= n) continue;
+    store_grad<2>(acc[i], invN, reinterpret_cast<bf16*>(a.dq), a.ld_qk, o0, row0, n,
+                  h * D + wn * 64, reinterpret_cast<const bf16*>(a.zpre), a.ld_z,
+                  a.zq_col + h * D + wn * 64, ql, g);
+  }
+}
+
 template <int DQK, int DV>
 hipError_t launch_kv_t(const AttnArgs& a, int64_t mi, hipStream_t st) {
   const int64_t grid = mi * a.H;
   if (grid <= 0) return hipSuccess;
   if (a.win_local > 0) k_attn_bwd_dkdv<DQK, DV, true><<<(unsigned)grid, KvShape<DQK, DV>::NT, 0, st>>>(a);
+  else if (a.ds && DQK == 128 && DV == 128)
+    k_attn_bwd_dkdv<DQK, DV, false, true><<<(unsigned)grid, KvShape<DQK, DV>::NT, 0, st>>>(a);
   else k_attn_bwd_dkdv<DQK, DV, false><<<(unsigned)grid, KvShape<DQK, DV>::NT, 0, st>>>(a);
   return hipGetLastError();
 }
@@ -920,6 +1093,13 @@ hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, int d_qk, int d_v, int64_t mi
   HSTU_DISPATCH_D(launch_kv_t, d_qk, d_v, a, mi, st)
 }
 hipError_t launch_attn_bwd_dq(const AttnArgs& a, int d_qk, int d_v, int64_t mi, hipStream_t st) {
+  if (a.ds) {
+    // from the kept dS when it fit (the recomputing kernel then exits at once)
+    if (d_qk != 128 || d_v != 128) return hipErrorInvalidValue;
+    if (mi * a.H > 0) k_attn_bwd_dq_ds<<<(unsigned)(mi * a.H), 256, 0, st>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   HSTU_DISPATCH_D(launch_dq_t, d_qk, d_v, a, mi, st)
 }
 

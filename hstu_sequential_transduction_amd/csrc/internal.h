@@ -87,6 +87,13 @@ struct PlanArgs {
   int njobs = 0;
   int lds_sched = 0;
   SchedJob job[2];
+  // kept dS of the backward: per-sequence first block (H * nrb (nrb + 1) / 2
+  // blocks of 128 x 128 per sequence, nrb = ceil(n / 128)) and the overflow
+  // flag against the capacity (one more workgroup when ds_base is given)
+  int32_t* ds_base = nullptr;
+  int32_t* ds_flag = nullptr;
+  int64_t ds_cap = 0;
+  int H = 0;
 };
 PlanArgs plan_prepass(const TimeMeta& tm, int B, const int32_t* seq_offsets,
                       const int64_t* ts, float* z0 = nullptr, float* z1 = nullptr,
@@ -115,6 +122,12 @@ struct AttnArgs {
   int H = 0, nP = 0, nT = 0, norm_mode = 0, norm_len = 1;
   // semi-local windows (win_local 0: full causal)
   int win_local = 0, win_global = 0;
+  // backward with dS kept: 128 x 128 bf16 blocks (key-major) of the causal
+  // part, per sequence and head; ds_base[b] = first block of sequence b;
+  // *ds_flag != 0: the blocks did not fit, dQ is recomputed instead
+  uint16_t* ds = nullptr;   // bf16 bits
+  const int32_t* ds_base = nullptr;
+  const int32_t* ds_flag = nullptr;
   // backward
   const void* dout = nullptr;
   int64_t ld_dout = 0;

@@ -223,6 +223,37 @@ __device__ void build_schedule(int B, const int32_t* __restrict__ offs, const Sc
   }
 }
 
+// First kept-dS block of every sequence (exclusive prefix sums of
+// H nrb (nrb + 1) / 2) and the flag that says whether they fit ds_cap.  The
+// total is summed in 64 bits, so the int32 bases are used only when it fits.
+__device__ void ds_offsets(const PlanArgs& p) {
+  __shared__ int64_t wtot[16];
+  const int t = threadIdx.x;
+  int64_t mine = 0;
+  for (int b = t; b < p.B; b += 1024) {
+    const int64_t nrb = (p.offs[b + 1] - p.offs[b] + 127) / 128;
+    const int64_t cnt = (int64_t)p.H * nrb * (nrb + 1) / 2;
+    mine += cnt;
+    p.ds_base[b] = (int32_t)min<int64_t>(cnt, INT32_MAX / 2);
+  }
+  for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o, 64);
+  if ((t & 63) == 0) wtot[t >> 6] = mine;
+  sched_step_barrier();
+  int64_t total = 0;
+  for (int i = 0; i < 16; ++i) total += wtot[i];
+  const bool fits = total <= p.ds_cap;
+  if (t == 0) *p.ds_flag = fits ? 0 : 1;
+  if (!fits) return;
+  int32_t tot32 = 0;
+  block_suffix_excl(p.ds_base, p.ds_base, p.B, &tot32);   // in place: later sequences' blocks
+  sched_step_barrier();
+  for (int b = t; b < p.B; b += 1024) {
+    const int64_t nrb = (p.offs[b + 1] - p.offs[b] + 127) / 128;
+    const int32_t cnt = (int32_t)((int64_t)p.H * nrb * (nrb + 1) / 2);
+    p.ds_base[b] = (int32_t)total - p.ds_base[b] - cnt;
+  }
+}
+
 // One launch for a call's plan: workgroups [0, npre) run the time pre-pass
 // (and clear the backward's rab-gradient sums on the way), the next njobs
 // build the work lists.
@@ -239,6 +270,10 @@ __global__ __launch_bounds__(1024) void k_plan(PlanArgs p) {
     return;
   }
   const int job = wg - p.npre;
+  if (job == p.njobs) {
+    ds_offsets(p);
+    return;
+  }
   build_schedule(p.B, p.sched_offs, p.job[job], p.lds_sched ? plan_lds : nullptr);
 }
 
@@ -282,7 +317,7 @@ hipError_t launch_plan(PlanArgs p, hipStream_t st) {
     if (e != hipSuccess) return e;
     p.nz = 0;
   }
-  const int grid = p.npre + p.njobs;
+  const int grid = p.npre + p.njobs + (p.ds_base ? 1 : 0);
   if (grid <= 0) return hipSuccess;
   const size_t lds = p.lds_sched ? (size_t)4 * max_e * sizeof(int32_t) : 0;
   k_plan<<<grid, 1024, lds, st>>>(p);

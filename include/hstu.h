@@ -101,6 +101,13 @@ typedef struct {
    * target-aware attention (win_global is then ignored).  Both >= 0. */
   int32_t win_local;
   int32_t win_global;
+  /* Longest sequence of the batch (rows), or 0 if not given.  With d_qk =
+   * d_v = 128, bf16 and no windows, a positive max_len lets the backward keep
+   * dS, the gradient of the scores, in its workspace (bf16, 128 x 128 blocks
+   * of the causal part, about 2 T max_len H bytes) and form dQ from it instead
+   * of recomputing S and dA.  If the batch's blocks do not fit (a sequence
+   * longer than max_len), the backward recomputes; results agree either way. */
+  int32_t max_len;
 } hstu_attn_desc;
 
 /* One layer: attention options plus model width and layer flags. */

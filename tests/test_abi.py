@@ -45,7 +45,7 @@ def test_version_and_status_strings(L):
 def _desc(**kw):
     base = dict(B=4, T=300, H=2, d_qk=32, d_v=32, n_pos_buckets=128, n_time_buckets=128,
                 norm_mode=0, norm_len=128, dtype=1, rab_head_stride=128, win_local=0,
-                win_global=0)
+                win_global=0, max_len=0)
     base.update(kw)
     return _lib.AttnDesc(*[base[f] for f, _ in _lib.AttnDesc._fields_])
 
