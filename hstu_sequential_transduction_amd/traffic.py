@@ -30,13 +30,19 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
-# kernel tag -> (symbol fragment in the trace, sources whose hash keys the record)
+# kernel tag -> (symbol fragments in the trace, sources whose hash keys the
+# record).  A tag's launch may run several kernels (dQ from a kept dS runs
+# the product kernel, then the recomputing kernel, which exits at once when
+# the kept dS was used): the first fragment names the kernel launched exactly
+# once per tag launch, and the traffic of one launch is the sum over all the
+# fragments' dispatches divided by the number of those launches.
+_ATTN_SRC = ["attn_bwd.hip", "common.h", "bias.h", "lds.h"]
 KERNELS = {
-    "attn_fwd": ("k_attn_fwd_bf16", ["attn_fwd.hip", "common.h", "bias.h", "lds.h"]),
-    "attn_bwd_dkdv": ("k_attn_bwd_dkdv", ["attn_bwd.hip", "common.h", "bias.h", "lds.h"]),
-    "attn_bwd_dq": ("k_attn_bwd_dq", ["attn_bwd.hip", "common.h", "bias.h", "lds.h"]),
-    "ln_gate_fwd": ("k_ln_gate_fwd", ["ln_gate.hip", "common.h"]),
-    "ln_gate_bwd": ("k_ln_gate_bwd", ["ln_gate.hip", "common.h"]),
+    "attn_fwd": (["k_attn_fwd_bf16"], ["attn_fwd.hip", "common.h", "bias.h", "lds.h"]),
+    "attn_bwd_dkdv": (["k_attn_bwd_dkdv"], _ATTN_SRC),
+    "attn_bwd_dq": (["k_attn_bwd_dq<", "k_attn_bwd_dq_ds"], _ATTN_SRC),
+    "ln_gate_fwd": (["k_ln_gate_fwd"], ["ln_gate.hip", "common.h"]),
+    "ln_gate_bwd": (["k_ln_gate_bwd"], ["ln_gate.hip", "common.h"]),
 }
 GEMM_SOURCES = ["gemm.hip", "common.h", "lds.h"]
 COPY_SYMBOL = "copyBuffer"
@@ -85,7 +91,7 @@ def cmd_copy(args) -> int:
 
 
 def cmd_reduce(args) -> int:
-    sym = KERNELS.get(args.kernel, (args.kernel,))[0]
+    syms = KERNELS.get(args.kernel, ([args.kernel],))[0]
     copy_bytes = args.mib << 20
     cf = per_dispatch(args.copy_fetch, "FETCH_SIZE", COPY_SYMBOL)
     cw = per_dispatch(args.copy_write, "WRITE_SIZE", COPY_SYMBOL)
@@ -96,21 +102,24 @@ def cmd_reduce(args) -> int:
     f_copy = sorted(cf)[-1] * 1024.0
     w_copy = sorted(cw)[-1] * 1024.0
     f_scale, w_scale = copy_bytes / f_copy, copy_bytes / w_copy
-    kf = per_dispatch(args.fetch_run, "FETCH_SIZE", sym)
-    kw = per_dispatch(args.write_run, "WRITE_SIZE", sym)
-    if not kf or not kw:
-        print(f"no dispatches of {sym} found", file=sys.stderr)
+    kf = [per_dispatch(args.fetch_run, "FETCH_SIZE", s) for s in syms]
+    kw = [per_dispatch(args.write_run, "WRITE_SIZE", s) for s in syms]
+    if not kf[0] or not kw[0]:
+        print(f"no dispatches of {syms[0]} found", file=sys.stderr)
         return 1
-    fetch = sum(kf) / len(kf) * 1024.0 * f_scale
-    write = sum(kw) / len(kw) * 1024.0 * w_scale
+    nf, nw = len(kf[0]), len(kw[0])
+    kf_sum, kw_sum = sum(map(sum, kf)), sum(map(sum, kw))
+    fetch = kf_sum / nf * 1024.0 * f_scale
+    write = kw_sum / nw * 1024.0 * w_scale
     rec = {
         "kernel": args.kernel, "workload": args.workload, "source_hash": source_hash(args.kernel),
         "bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
-        "write_bytes": round(write), "dispatches": [len(kf), len(kw)],
+        "write_bytes": round(write), "dispatches": [nf, nw],
+        "kernels": {s: [len(a), len(b)] for s, a, b in zip(syms, kf, kw)},
         "copy_scale": {"fetch": round(f_scale, 4), "write": round(w_scale, 4),
                        "copy_bytes": copy_bytes},
-        "counters_kib_per_dispatch": {"FETCH_SIZE": round(sum(kf) / len(kf), 1),
-                                      "WRITE_SIZE": round(sum(kw) / len(kw), 1)},
+        "counters_kib_per_launch": {"FETCH_SIZE": round(kf_sum / nf, 1),
+                                    "WRITE_SIZE": round(kw_sum / nw, 1)},
         "command": args.command,
     }
     os.makedirs(args.out, exist_ok=True)
