@@ -465,21 +465,25 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
 
   // near-phase tile: per-half masks and per-element buckets
   // kept dS of one 32-row half (rows i0 + 32 qh .. of the tile starting at
-  // row i0): four 8-byte stores of four consecutive rows each.  ds_stores
-  // counts them for the tile's DMA wait (see run_phase).
+  // row i0).  Lane (key ql, half g) holds rows 8 aa + 4 g + {0..3}; one swap
+  // between the wave's halves (v_permlane32_swap) of the aa = 1 pieces of
+  // half 0 and the aa = 0 pieces of half 1 (likewise aa = 3 and 2) leaves
+  // each lane eight consecutive rows twice, so a half is two 16-byte stores
+  // per lane.  ds_stores counts them for the tile's DMA wait (see run_phase).
   int ds_stores = 0;
   auto store_ds = [&](int i0, int qh, const bf16x8 (&dd)[2]) HSTU_INLINE_LAMBDA {
     if constexpr (WIDE && KEEP_DS) {
       if (ds_kb) {
-        ds_stores = 4;
+        ds_stores = 2;
         bf16* dst = ds_kb + (int64_t)(i0 >> 7) * (128 * 128) +
-                    (((kg * 32 + (lane & 31)) * 128) + (i0 & 127) + qh * 32 + 4 * (lane >> 5));
+                    (((kg * 32 + (lane & 31)) * 128) + (i0 & 127) + qh * 32 + 8 * (lane >> 5));
 #pragma unroll
-        for (int aa = 0; aa < 4; ++aa) {
-          const bf16x8 v = dd[aa >> 1];
-          const bf16x4 q4 = (aa & 1) ? __builtin_shufflevector(v, v, 4, 5, 6, 7)
-                                     : __builtin_shufflevector(v, v, 0, 1, 2, 3);
-          *reinterpret_cast<uint2*>(dst + 8 * aa) = __builtin_bit_cast(uint2, q4);
+        for (int hh = 0; hh < 2; ++hh) {
+          // dwords 0, 1: rows 16 hh + 4 g + {0..3}; dwords 2, 3: rows 16 hh + 8 + 4 g + {0..3}
+          const u32x4 d = __builtin_bit_cast(u32x4, dd[hh]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+          *reinterpret_cast<u32x4*>(dst + 16 * hh) = u32x4{s0[0], s1[0], s0[1], s1[1]};
         }
       }
     }
@@ -613,12 +617,12 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
       return (i >= sk0 && i < sk1) ? sk1 : i;
     };
     // The next tile's DMA is issued before the body, whose only vector-memory
-    // operations are the four kept-dS stores (when a half stored them).  The
-    // vector-memory counter retires in issue order, so vmcnt(4) means the DMA
+    // operations are the two kept-dS stores (when a half stored them).  The
+    // vector-memory counter retires in issue order, so vmcnt(2) means the DMA
     // has landed while the stores may still be in flight.
     auto tile_wait = [&]() HSTU_INLINE_LAMBDA {
       if constexpr (KEEP_DS) {
-        if (ds_stores == 4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+        if (ds_stores == 2) __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
         else dma_wait();
         ds_stores = 0;
       } else {
@@ -991,7 +995,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_ds(AttnArgs a) {
     const int krow = kb * 128 + 64 * (q & 1);
     const int rlim = step_rows(q);
     const bf16* blk = base + (kb * nrb - (int64_t)kb * (kb - 1) / 2 + rb - kb) * (128 * 128);
-    dma_tile<128, 64, 4>(ta, blk + 64 * (q & 1) * 128, 128, 0, rlim, wave, lane);
+    // dS is read once: non-temporal, so that the K tiles the other row
+    // blocks of the sequence re-read stay in the L2
+    dma_tile<128, 64, 4, 2>(ta, blk + 64 * (q & 1) * 128, 128, 0, rlim, wave, lane);
     dma_tile<128, 64, 4>(tb, kh_ + (int64_t)krow * a.ld_qk, a.ld_qk, 0, rlim, wave, lane, D);
   };
 

@@ -144,8 +144,10 @@ HSTU_DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
 // global chunk that the swizzle puts there.  Completion: dma_wait().
 // `last_cols` (default: the whole row stride) bounds how many elements of the
 // last valid row may be touched, so that a tile reaching past the right edge
-// of a matrix never reads past the end of its allocation.
-template <int D, int R, int NW>
+// of a matrix never reads past the end of its allocation.  AUX is the loads'
+// cache policy (0: default; 2: non-temporal, for data read exactly once, so
+// that it does not push reused tiles out of the L2).
+template <int D, int R, int NW, int AUX = 0>
 HSTU_DEV void dma_tile(uint8_t* t, const bf16* base, int64_t ld, int r0, int rlim, int wave,
                        int lane, int last_cols = -1) {
   constexpr int NI = R * D * 2 / 1024;
@@ -162,7 +164,7 @@ HSTU_DEV void dma_tile(uint8_t* t, const bf16* base, int64_t ld, int r0, int rli
       const int row = p / (2 * D);
       const int lc = ((p % (2 * D)) >> 4) ^ SwzTile<D>::swz(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (HSTU_LDS void*)(t + i * 1024), 16,
-                                               row * (int)ld * 2 + lc * 16, 0, 0, 0);
+                                               row * (int)ld * 2 + lc * 16, 0, 0, AUX);
     }
   }
 }
