@@ -11,10 +11,16 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 // Tile rows hold D bf16 (2D bytes, no padding).  The 16-byte chunks of row r
 // are XOR-permuted by swz(r), chosen so that
-//  * 16 consecutive rows read at one logical chunk (one MFMA operand row per
-//    lane, 16 lanes per LDS cycle) land on 16 distinct 16-byte bank groups;
-//  * 4 consecutive rows (aligned to 4) x one 32-byte chunk pair, what a
-//    16-lane group of a transpose read touches, land on distinct banks.
+//  * 16 consecutive rows (aligned to 16) read at one logical chunk (one MFMA
+//    operand row per lane, 16 lanes per 256-byte LDS cycle) land on 16
+//    distinct 16-byte bank groups;
+//  * 4 consecutive rows (aligned to 4) x one 64-byte piece (four chunks
+//    aligned to four), what 32 lanes of a transpose read touch in one
+//    cycle, land on four distinct 64-byte bank groups (so do the 32-byte
+//    pieces of each 16-lane half).
+// For D = 128 the row's chunk group of four is picked by r & 3 and the chunk
+// within it by (r >> 2) & 3; for D = 64 (two rows per 256 bytes) the group
+// by the row's parity and bit 0 of q = (r >> 1) & 7, the chunk by q >> 1.
 template <int D>
 struct SwzTile {
   static_assert(D == 32 || D == 64 || D == 128, "tile width");
@@ -22,10 +28,10 @@ struct SwzTile {
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
   HSTU_DEV static int swz(int r) {
     if constexpr (D == 128) {
-      return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+      return ((r & 3) << 2) | ((r >> 2) & 3);
     } else if constexpr (D == 64) {
       const int q = (r >> 1) & 7;
-      return ((q & 1) << 1) | ((q >> 1) & 1) | (q & 4);
+      return ((q & 1) << 2) | (q >> 1);
     } else {
       return (r >> 2) & 3;
     }
