@@ -33,6 +33,8 @@ namespace {
 
 constexpr int FWD_BN = 64;  // keys per tile
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // 32-row query groups per wave: two when d <= 64 (each K/V fragment read from
 // LDS then feeds two MFMAs), one at d = 128 where registers run out first.
 template <int DQK, int DV>
@@ -51,14 +53,23 @@ struct FwdBuf {
 };
 
 // Bias tables, a separate LDS object from the tile buffers.
+// Position table with saturated margins: tposx[TPOS_PADL + x] holds
+// rab_pos[clamp(x, 0, nP-1)] for x in [-TPOS_PADL, nP + TPOS_PADH).  Tiles of
+// history keys near the diagonal see position distances in [-126, nP + 125]
+// (a 64-row wave against a 64-key tile that is active and not far), so their
+// gathers need no clamp and no per-element address arithmetic.
+constexpr int TPOS_PADL = 192, TPOS_PADH = 128;
+
 struct FwdTables {
   float tfar[32];    // (rab_pos[nP-1] + rab_time[bucket(c)]) * -log2 e, by clz index c
   float ttime[32];   // rab_time[bucket(c)] * -log2 e
-  float tpos[1024];  // rab_pos * -log2 e
+  float tposx[TPOS_PADL + 1024 + TPOS_PADH];  // rab_pos * -log2 e, saturated margins
 };
 
-template <bool V>
-using bconst = std::integral_constant<bool, V>;
+// mask kinds: 0 none, 1 causal only (tiles of history keys), 2 causal,
+// candidate and window terms
+template <int V>
+using mconst = std::integral_constant<int, V>;
 
 template <int DQK, int DV, bool WIN>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
@@ -91,7 +102,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
   {
     const float* rp = a.rab_pos + h * a.rab_stride;
     const float* rtb = a.rab_time + h * a.rab_stride;
-    for (int i = tid; i < nP; i += 256) sm.tpos[i] = rp[i] * HSTU_NEG_LOG2E;
+    for (int i = tid; i < nP + TPOS_PADL + TPOS_PADH; i += 256)
+      sm.tposx[i] = rp[min(max(i - TPOS_PADL, 0), nP - 1)] * HSTU_NEG_LOG2E;
     if (tid < 32) {
       const float tv = rtb[tbucket_from_clz(tid, nT)];
       sm.ttime[tid] = tv * HSTU_NEG_LOG2E;
@@ -250,45 +262,68 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
             for (int aa = 0; aa < 4; ++aa) {
               const int kk0 = hf * 32 + 8 * aa + 4 * g;
               const i32x4 tj = *reinterpret_cast<const i32x4*>(&B.t[kk0]);
+              float pv[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const int kc = hf * 32 + 8 * aa + r;
                 const float sb =
                     fmaf(sacc[qg][4 * aa + r], HSTU_NEG_LOG2E, bias_of(qg, kc, tj[r]));
                 float p = sb * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sb));
-                if constexpr (decltype(masked)::value) {
-                  bool ok = kc <= lim[qg] || kc == slf[qg];
-                  if constexpr (WIN) ok = ok && (kc >= wlo[qg] || kc < wgl[qg]);
+                if constexpr (decltype(masked)::value != 0) {
+                  bool ok = kc <= lim[qg];
+                  if constexpr (decltype(masked)::value == 2) {
+                    ok = ok || kc == slf[qg];
+                    if constexpr (WIN) ok = ok && (kc >= wlo[qg] || kc < wgl[qg]);
+                  }
                   p = ok ? p : 0.0f;
                 }
-                pk[qg][aa >> 1][(aa & 1) * 4 + r] = (bf16)p;
+                pv[r] = p;
+              }
+              // round pairs to bf16 (one v_cvt_pk_bf16_f32 per two scores)
+#pragma unroll
+              for (int r = 0; r < 4; r += 2) {
+                const bf16x2 two = __builtin_convertvector(f32x2{pv[r], pv[r + 1]}, bf16x2);
+                pk[qg][aa >> 1][(aa & 1) * 4 + r] = two[0];
+                pk[qg][aa >> 1][(aa & 1) * 4 + r + 1] = two[1];
               }
               // keep the scheduler from hoisting every gather of the half at once
               __builtin_amdgcn_sched_barrier(0);
             }
         };
         if (mode == 0) {
-          silu_half([&](int qg, int, int32_t) { return ba[qg]; }, bconst<false>{});
+          silu_half([&](int qg, int, int32_t) { return ba[qg]; }, mconst<0>{});
         } else if (mode == 1) {
           silu_half([&](int qg, int, int32_t tj) { return tj <= thr[qg] ? ba[qg] : bb[qg]; },
-                    bconst<false>{});
+                    mconst<0>{});
         } else if (mode == 2) {
           silu_half([&](int qg, int, int32_t tj) { return sm.tfar[tclz_narrow(ti1[qg], tj)]; },
-                    bconst<false>{});
+                    mconst<0>{});
+        } else if (!wide && j1 <= nh && wl == 0) {
+          // history keys only, no windows: p(i) - j = dI - kc stays inside the
+          // padded table, read at a per-lane base plus an immediate offset;
+          // the only mask term is causality (no key of the tile is a candidate)
+          const float* pb[QG];
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) pb[qg] = &sm.tposx[TPOS_PADL + dI[qg] - (FWD_BN - 1)];
+          auto bias = [&](int qg, int kc, int32_t tj) HSTU_INLINE_LAMBDA {
+            return pb[qg][(FWD_BN - 1) - kc] + sm.ttime[tclz_narrow(ti1[qg], tj)];
+          };
+          if (need_mask) silu_half(bias, mconst<1>{});
+          else silu_half(bias, mconst<0>{});
         } else if (!wide) {
           // position bucket: clamp(p(i) - min(j, n_h), 0, nP-1) = med3(max(dI - kc, pI - nh), 0, nP-1)
           auto bias = [&](int qg, int kc, int32_t tj) HSTU_INLINE_LAMBDA {
             const int bp = min(max(max(dI[qg] - kc, pmin[qg]), 0), nP - 1);
-            return sm.tpos[bp] + sm.ttime[tclz_narrow(ti1[qg], tj)];
+            return sm.tposx[TPOS_PADL + bp] + sm.ttime[tclz_narrow(ti1[qg], tj)];
           };
-          if (need_mask) silu_half(bias, bconst<true>{});
-          else silu_half(bias, bconst<false>{});
+          if (need_mask) silu_half(bias, mconst<2>{});
+          else silu_half(bias, mconst<0>{});
         } else {
           auto bias = [&](int qg, int kc, int32_t) HSTU_INLINE_LAMBDA {
             const int bp = min(max(max(dI[qg] - kc, pmin[qg]), 0), nP - 1);
-            return sm.tpos[bp] + sm.ttime[tclz_wide(tq64[qg], B.t64[kc + 4 * g])];
+            return sm.tposx[TPOS_PADL + bp] + sm.ttime[tclz_wide(tq64[qg], B.t64[kc + 4 * g])];
           };
-          silu_half(bias, bconst<true>{});
+          silu_half(bias, mconst<2>{});
         }
 
         // O += P V: V read down its columns (keys are the k index)
