@@ -473,8 +473,27 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
     for (int e = 0; e < 4; ++e) bias4[e] = ncol + e < g.N ? g.bias[ncol + e] : 0.0f;
   }
   const bool vec = ncol + 3 < g.N;
+  // Residual (EPI_RESID): every load of the wave's block is issued here, ahead
+  // of the staging rounds, so one memory latency is paid per workgroup
+  // instead of one per round (the accumulators' operand registers are free)
+  constexpr int NRND = FM * (32 / SR), NRR = SR / RPI;
+  uint2 rres[EPI == EPI_RESID ? NRND : 1][EPI == EPI_RESID ? NRR : 1];
+  if constexpr (EPI == EPI_RESID) {
+    if (g.R && vec) {
 #pragma unroll
-  for (int ih = 0; ih < FM * (32 / SR); ++ih) {
+      for (int ih = 0; ih < NRND; ++ih)
+#pragma unroll
+        for (int rr = 0; rr < NRR; ++rr) {
+          const int64_t m = m0 + wm * 32 * FM + (ih / (32 / SR)) * 32 + (ih % (32 / SR)) * SR +
+                            RPI * rr + lr;
+          rres[ih][rr] = m < g.M ? *reinterpret_cast<const uint2*>(
+                                       reinterpret_cast<const bf16*>(g.R) + m * g.ldr + ncol)
+                                 : uint2{0u, 0u};
+        }
+    }
+  }
+#pragma unroll
+  for (int ih = 0; ih < NRND; ++ih) {
     const int i = ih / (32 / SR), hh = ih % (32 / SR);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
@@ -509,7 +528,7 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
       if (EPI == EPI_RESID && g.R) {
         const bf16* rp = reinterpret_cast<const bf16*>(g.R) + m * g.ldr + ncol;
         if (vec) {
-          const uint2 rv = *reinterpret_cast<const uint2*>(rp);
+          const uint2 rv = rres[EPI == EPI_RESID ? ih : 0][EPI == EPI_RESID ? rr : 0];
           v[0] += __builtin_bit_cast(float, rv.x << 16);
           v[1] += __builtin_bit_cast(float, rv.x & 0xFFFF0000u);
           v[2] += __builtin_bit_cast(float, rv.y << 16);
