@@ -35,6 +35,43 @@ hipStream_t entry_stream(void* stream) {
   return (hipStream_t)stream;
 }
 
+// Work inside one call that does not depend on the steps before it (the
+// attention plan reads only offsets and timestamps; a weight gradient needs
+// only its two operands) runs on a side stream: one per host thread and
+// device, default priority, created on first use and kept until the process
+// ends.  It is ordered after everything queued on the caller's stream before
+// the call and joined back by an event before the call returns, so the caller
+// sees the order of its own stream.  If the stream or its events cannot be
+// created, that work stays on the caller's stream.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t ev[4] = {};
+  int state = 0;  // 0 untried, 1 ready, -1 unavailable
+};
+SideStream* side_stream() {
+  thread_local SideStream sides[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  SideStream& sd = sides[dev];
+  if (sd.state == 0) {
+    bool ok = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; ok && i < 4; ++i)
+      ok = hipEventCreateWithFlags(&sd.ev[i], hipEventDisableTiming) == hipSuccess;
+    sd.state = ok ? 1 : -1;
+    (void)hipGetLastError();
+  }
+  return sd.state == 1 ? &sd : nullptr;
+}
+// work queued on `to` from now on runs after all work queued on `from` so far
+hipError_t order_after(hipStream_t to, hipStream_t from, hipEvent_t ev) {
+  hipError_t e = hipEventRecord(ev, from);
+  if (e == hipSuccess) e = hipStreamWaitEvent(to, ev, 0);
+  return e;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 size_t esize(int dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
 
@@ -145,10 +182,23 @@ int64_t rab_floats(const hstu_attn_desc* d) {
 
 // ---- attention forward/backward bodies (shared with the layer) -------------
 
-hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
-                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
-                          const float* rp, const float* rt, const int32_t* nc, void* out,
-                          int64_t ld_out, bool out_f32, void* ws, hipStream_t st) {
+// The plan of a forward call (time pre-pass and work list, in the workspace)
+hstu_status attn_fwd_plan(const hstu_attn_desc* d, const int32_t* offs, const int64_t* ts,
+                          void* ws, hipStream_t st) {
+  Carver c(ws);
+  FwdWs w = carve_fwd(c, d);
+  HSTU_TIMED(TT_PREPASS, st);
+  PlanArgs p = plan_prepass(w.tm, d->B, offs, ts);
+  plan_add_job(p, w.sc, 0, offs);
+  HSTU_TRY(launch_plan(p, st));
+  return HSTU_OK;
+}
+
+// The attention kernel of a forward call whose plan is already in `ws`
+hstu_status attn_fwd_run(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                         const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                         const float* rp, const float* rt, const int32_t* nc, void* out,
+                         int64_t ld_out, bool out_f32, void* ws, hipStream_t st) {
   Carver c(ws);
   FwdWs w = carve_fwd(c, d);
   AttnArgs a = base_args(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, w.tm);
@@ -157,14 +207,17 @@ hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   a.out_f32 = out_f32;
   a.items = w.sc.items;
   a.counters = w.sc.counters;
-  {
-    HSTU_TIMED(TT_PREPASS, st);
-    PlanArgs p = plan_prepass(w.tm, d->B, offs, ts);
-    plan_add_job(p, w.sc, 0, offs);
-    HSTU_TRY(launch_plan(p, st));
-  }
   { HSTU_TIMED(TT_ATTN_FWD, st); HSTU_TRY(launch_attn_fwd(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st)); }
   return HSTU_OK;
+}
+
+hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                          const float* rp, const float* rt, const int32_t* nc, void* out,
+                          int64_t ld_out, bool out_f32, void* ws, hipStream_t st) {
+  hstu_status s = attn_fwd_plan(d, offs, ts, ws, st);
+  if (s != HSTU_OK) return s;
+  return attn_fwd_run(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, out_f32, ws, st);
 }
 
 // Ranking against a cached history: key splits per (user, candidate block)
@@ -254,12 +307,33 @@ hstu_status check_history(const hstu_attn_desc* d, const hstu_history_kv* hist) 
   return HSTU_OK;
 }
 
-hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
-                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
-                          const float* rp, const float* rt, const int32_t* nc, const void* dout,
-                          int64_t ld_dout, void* dq, void* dk, void* dv, float* drp, float* drt,
-                          const void* zpre, int64_t ld_z, int64_t zq, int64_t zk, int64_t zv,
-                          void* ws, hipStream_t st) {
+// The plan of a backward call (time pre-pass, both work lists, kept-dS
+// offsets; zeroes the rab gradients)
+hstu_status attn_bwd_plan(const hstu_attn_desc* d, const int32_t* offs, const int64_t* ts,
+                          float* drp, float* drt, void* ws, hipStream_t st) {
+  Carver c(ws);
+  BwdWs w = carve_bwd(c, d);
+  HSTU_TIMED(TT_PREPASS, st);
+  PlanArgs p = plan_prepass(w.tm, d->B, offs, ts, drp, drt, rab_floats(d));
+  plan_add_job(p, w.kv, 1, offs);
+  plan_add_job(p, w.q, 0, offs);
+  if (w.ds) {
+    p.ds_base = w.ds_base;
+    p.ds_flag = w.ds_flag;
+    p.ds_cap = w.ds_cap;
+    p.H = d->H;
+  }
+  HSTU_TRY(launch_plan(p, st));
+  return HSTU_OK;
+}
+
+// The attention kernels of a backward call whose plan is already in `ws`
+hstu_status attn_bwd_run(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                         const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                         const float* rp, const float* rt, const int32_t* nc, const void* dout,
+                         int64_t ld_dout, void* dq, void* dk, void* dv, float* drp, float* drt,
+                         const void* zpre, int64_t ld_z, int64_t zq, int64_t zk, int64_t zv,
+                         void* ws, hipStream_t st) {
   Carver c(ws);
   BwdWs w = carve_bwd(c, d);
   AttnArgs a = base_args(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, w.tm);
@@ -275,19 +349,6 @@ hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   a.zq_col = zq;
   a.zk_col = zk;
   a.zv_col = zv;
-  {
-    HSTU_TIMED(TT_PREPASS, st);
-    PlanArgs p = plan_prepass(w.tm, d->B, offs, ts, drp, drt, rab_floats(d));
-    plan_add_job(p, w.kv, 1, offs);
-    plan_add_job(p, w.q, 0, offs);
-    if (w.ds) {
-      p.ds_base = w.ds_base;
-      p.ds_flag = w.ds_flag;
-      p.ds_cap = w.ds_cap;
-      p.H = d->H;
-    }
-    HSTU_TRY(launch_plan(p, st));
-  }
   a.ds = w.ds;
   a.ds_base = w.ds_base;
   a.ds_flag = w.ds_flag;
@@ -300,6 +361,18 @@ hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   aq.counters = w.q.counters;
   { HSTU_TIMED(TT_ATTN_BWD_DQ, st); HSTU_TRY(launch_attn_bwd_dq(aq, d->d_qk, d->d_v, w.q.cap, st)); }
   return HSTU_OK;
+}
+
+hstu_status attn_bwd_impl(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
+                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                          const float* rp, const float* rt, const int32_t* nc, const void* dout,
+                          int64_t ld_dout, void* dq, void* dk, void* dv, float* drp, float* drt,
+                          const void* zpre, int64_t ld_z, int64_t zq, int64_t zk, int64_t zv,
+                          void* ws, hipStream_t st) {
+  hstu_status s = attn_bwd_plan(d, offs, ts, drp, drt, ws, st);
+  if (s != HSTU_OK) return s;
+  return attn_bwd_run(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, dout, ld_dout, dq, dk, dv,
+                      drp, drt, zpre, ld_z, zq, zk, zv, ws, st);
 }
 
 // ---- layer workspace layout --------------------------------------------------
@@ -694,6 +767,9 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
   void* Zh = saved ? saved->Zh : lw.Zh;
   float* O = full ? saved->O : static_cast<float*>(lw.O);
   void* G = full ? saved->G : lw.G;
+  // (the plan stays on the caller's stream: moving it under the projection
+  // GEMM on the side stream measured slower, the two events costing more
+  // than the ~18 us plan)
   auto attention = [&](const void* q, const void* k, const void* v, int64_t ld) {
     return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, O, W,
                          /*out_f32=*/true, lw.attn, st);
@@ -915,6 +991,18 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   const char* zh = static_cast<const char*>(saved->Zh);
   const void* zpre = L->proj_silu ? saved->Z : nullptr;
 
+  // Side stream (when available): the attention plan and dW2 = G^T dY run
+  // there from the start, dW1 once dZ is complete; the caller's stream waits
+  // for the plan before the attention kernels and for everything before the
+  // call returns.  The column sums (shared scratch) stay on the caller's
+  // stream.
+  SideStream* sd = side_stream();
+  hipStream_t ss = sd ? sd->s : st;
+  if (sd) HSTU_TRY(order_after(ss, st, sd->ev[0]));
+  s = attn_bwd_plan(d, offs, ts, g->drab_pos, g->drab_time, bw.attn, ss);
+  if (s != HSTU_OK) return s;
+  if (sd) HSTU_TRY(hipEventRecord(sd->ev[1], ss));
+
   // 1. dG = dY W2^T
   GemmArgs a1;
   a1.M = T; a1.N = W; a1.K = D;
@@ -929,12 +1017,12 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a2.A = saved->G; a2.lda = W; a2.a_kcont = false;
   a2.B = dy; a2.ldb = D; a2.b_kcont = false;
   a2.epi = EPI_PARTIAL; a2.split_k = bw.s2; a2.partial = bw.part2;
-  { HSTU_TIMED(TT_GEMM_DW2, st); HSTU_TRY(launch_gemm(a2, d->dtype, st)); }
+  { HSTU_TIMED(TT_GEMM_DW2, ss); HSTU_TRY(launch_gemm(a2, d->dtype, ss)); }
   {
-    HSTU_TIMED(TT_REDUCE, st);
-    HSTU_TRY(launch_splitk_reduce(bw.part2, bw.s2, W, D, g->dW2, D, st));
-    if (w->b2) HSTU_TRY(launch_colsum(dy, T, D, D, d->dtype, g->db2, bw.colws, st));
+    HSTU_TIMED(TT_REDUCE, ss);
+    HSTU_TRY(launch_splitk_reduce(bw.part2, bw.s2, W, D, g->dW2, D, ss));
   }
+  if (w->b2) HSTU_TRY(launch_colsum(dy, T, D, D, d->dtype, g->db2, bw.colws, st));
   // 3. LayerNorm + gate backward: dU (into dZ's U block, times SiLU'(Z)), dO
   LnArgs la;
   la.o_f32 = true;
@@ -956,7 +1044,8 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   if (w->ln_beta)
     HSTU_TRY(launch_colsum(bw.lnpb, bw.ln_blocks, W, W, HSTU_F32, g->dbeta, bw.colws, st));
   // 4. attention backward into dZ's V, Q, K blocks (times SiLU'(Z))
-  s = attn_bwd_impl(d, zh + 2 * W * es, zh + (2 * W + HQ) * es, F1, zh + W * es, F1, offs, ts,
+  if (sd) HSTU_TRY(hipStreamWaitEvent(st, sd->ev[1], 0));
+  s = attn_bwd_run(d, zh + 2 * W * es, zh + (2 * W + HQ) * es, F1, zh + W * es, F1, offs, ts,
                     w->rab_pos, w->rab_time, nc, bw.dO, W, dz + 2 * W * es,
                     dz + (2 * W + HQ) * es, dz + W * es, g->drab_pos, g->drab_time, zpre, F1,
                     2 * W, 2 * W + HQ, W, bw.attn, st);
@@ -967,12 +1056,13 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a3.A = x; a3.lda = D; a3.a_kcont = false;
   a3.B = dz; a3.ldb = F1; a3.b_kcont = false;
   a3.epi = EPI_PARTIAL; a3.split_k = bw.s1; a3.partial = bw.part1;
-  { HSTU_TIMED(TT_GEMM_DW1, st); HSTU_TRY(launch_gemm(a3, d->dtype, st)); }
+  if (sd) HSTU_TRY(order_after(ss, st, sd->ev[2]));
+  { HSTU_TIMED(TT_GEMM_DW1, ss); HSTU_TRY(launch_gemm(a3, d->dtype, ss)); }
   {
-    HSTU_TIMED(TT_REDUCE, st);
-    HSTU_TRY(launch_splitk_reduce(bw.part1, bw.s1, D, F1, g->dW1, F1, st));
-    if (w->b1) HSTU_TRY(launch_colsum(dz, T, F1, F1, d->dtype, g->db1, bw.colws, st));
+    HSTU_TIMED(TT_REDUCE, ss);
+    HSTU_TRY(launch_splitk_reduce(bw.part1, bw.s1, D, F1, g->dW1, F1, ss));
   }
+  if (w->b1) HSTU_TRY(launch_colsum(dz, T, F1, F1, d->dtype, g->db1, bw.colws, st));
   // 6. dX = dZ W1^T (+ dY)
   GemmArgs a4;
   a4.M = T; a4.N = D; a4.K = F1;
@@ -982,6 +1072,7 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a4.epi = EPI_RESID;
   a4.R = L->residual ? dy : nullptr; a4.ldr = D;
   { HSTU_TIMED(TT_GEMM_DX, st); HSTU_TRY(launch_gemm(a4, d->dtype, st)); }
+  if (sd) HSTU_TRY(order_after(st, ss, sd->ev[3]));
   return HSTU_OK;
 }
 
