@@ -224,6 +224,14 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const void* x,
  * Backward of hstu_layer_fwd given dy ([T, D] dtype): dx ([T, D] dtype) and
  * every parameter gradient in g (fp32, overwritten).  `saved` must hold the
  * intermediates of the matching training forward.  bf16 only.
+ * Part of the work (the attention work lists, dW1, dW2) runs on a side
+ * stream that the library keeps per host thread and device (created on first
+ * use, default priority, held until the process ends); it starts after all
+ * work queued on `stream` before the call, and `stream` waits for all of it
+ * before the call returns, so every output is ordered on `stream` as if the
+ * whole call had run there.  A capture of `stream` into a graph includes the
+ * side work.  If the side stream cannot be created, everything runs on
+ * `stream`.
  */
 hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const void* x,
                            const hstu_layer_weights* w,
