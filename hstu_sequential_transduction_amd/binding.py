@@ -49,12 +49,13 @@ class AttnConfig:
     win_local: int = 0    # semi-local attention windows (0: full causal)
     win_global: int = 0
     max_len: int = 0      # longest sequence, if known (lets the backward keep dS)
+    reuse_plan: int = 0   # forward: the workspace already holds this batch's plan
 
 
 def attn_desc(cfg: AttnConfig, B: int, T: int, dtype: torch.dtype, rab_stride: int) -> AttnDesc:
     return AttnDesc(B, T, cfg.H, cfg.d_qk, cfg.d_v, cfg.n_pos_buckets, cfg.n_time_buckets,
                     cfg.norm_mode, cfg.norm_len, _DT[dtype], rab_stride, cfg.win_local,
-                    cfg.win_global, cfg.max_len)
+                    cfg.win_global, cfg.max_len, cfg.reuse_plan)
 
 
 def _rab_stride(rab_pos: torch.Tensor, rab_time: torch.Tensor) -> int:

@@ -86,6 +86,7 @@ hstu_status check_attn_desc(const hstu_attn_desc* d) {
   if (d->norm_mode != 0 && d->norm_mode != 1) return HSTU_ERR_INVALID_ARG;
   if (d->norm_mode == 0 && d->norm_len <= 0) return HSTU_ERR_INVALID_ARG;
   if (d->win_local < 0 || d->win_global < 0 || d->max_len < 0) return HSTU_ERR_INVALID_ARG;
+  if (d->reuse_plan != 0 && d->reuse_plan != 1) return HSTU_ERR_INVALID_ARG;
   if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
   if (d->rab_head_stride < 0) return HSTU_ERR_INVALID_ARG;
   if (d->rab_head_stride != 0 &&
@@ -215,8 +216,10 @@ hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
                           const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
                           const float* rp, const float* rt, const int32_t* nc, void* out,
                           int64_t ld_out, bool out_f32, void* ws, hipStream_t st) {
-  hstu_status s = attn_fwd_plan(d, offs, ts, ws, st);
-  if (s != HSTU_OK) return s;
+  if (!d->reuse_plan) {
+    hstu_status s = attn_fwd_plan(d, offs, ts, ws, st);
+    if (s != HSTU_OK) return s;
+  }
   return attn_fwd_run(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, out_f32, ws, st);
 }
 

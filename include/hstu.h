@@ -108,6 +108,16 @@ typedef struct {
    * of recomputing S and dA.  If the batch's blocks do not fit (a sequence
    * longer than max_len), the backward recomputes; results agree either way. */
   int32_t max_len;
+  /* Forward only (hstu_attn_fwd, hstu_layer_fwd, hstu_layer_fwd_mx): 1
+   * asserts that the workspace of this call already holds the plan (time
+   * pre-pass and work list) that an earlier forward call with the same
+   * descriptor apart from this field, the same workspace layout and the same
+   * seq_offsets, timestamps and num_candidates wrote, e.g. the previous
+   * layer of a stack run with one workspace; the call then skips the plan.
+   * The library cannot check the assertion: a wrong one gives wrong
+   * results.  0 (default): plan.  Other values: HSTU_ERR_INVALID_ARG.
+   * Ignored by backward and cached-history calls, which always plan. */
+  int32_t reuse_plan;
 } hstu_attn_desc;
 
 /* One layer: attention options plus model width and layer flags. */

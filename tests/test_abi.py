@@ -45,7 +45,7 @@ def test_version_and_status_strings(L):
 def _desc(**kw):
     base = dict(B=4, T=300, H=2, d_qk=32, d_v=32, n_pos_buckets=128, n_time_buckets=128,
                 norm_mode=0, norm_len=128, dtype=1, rab_head_stride=128, win_local=0,
-                win_global=0, max_len=0)
+                win_global=0, max_len=0, reuse_plan=0)
     base.update(kw)
     return _lib.AttnDesc(*[base[f] for f, _ in _lib.AttnDesc._fields_])
 
@@ -65,7 +65,7 @@ def test_workspace_sizes_grow_with_T(L):
     (dict(d_qk=48), -2), (dict(d_v=256), -2), (dict(H=0), -2), (dict(H=65), -2),
     (dict(n_pos_buckets=0), -2), (dict(n_time_buckets=2000), -2), (dict(norm_mode=2), -1),
     (dict(norm_len=0), -1), (dict(dtype=7), -2), (dict(T=1 << 31), -1), (dict(B=-1), -1),
-    (dict(rab_head_stride=64), -1),
+    (dict(rab_head_stride=64), -1), (dict(max_len=-1), -1), (dict(reuse_plan=2), -1),
 ])
 def test_host_side_argument_errors(L, bad, code):
     d = _desc(**bad)
