@@ -69,8 +69,11 @@ def _rab_stride(rab_pos: torch.Tensor, rab_time: torch.Tensor) -> int:
 
 
 def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, cfg: AttnConfig,
-                  num_candidates=None, out=None, stream=None):
-    """O [T, H*d_v] of the pointwise attention (see include/hstu.h)."""
+                  num_candidates=None, out=None, stream=None,
+                  workspace: Optional["LayerWorkspace"] = None):
+    """O [T, H*d_v] of the pointwise attention (see include/hstu.h).  With
+    cfg.reuse_plan = 1 the call needs the `workspace` of an earlier planning
+    call on the same batch."""
     for n_, t_ in (("q", q), ("k", k), ("v", v), ("seq_offsets", seq_offsets),
                    ("timestamps", timestamps), ("rab_pos", rab_pos), ("rab_time", rab_time),
                    ("num_candidates", num_candidates)):
@@ -81,7 +84,8 @@ def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, cfg: Attn
         out = torch.empty((T, cfg.H * cfg.d_v), dtype=q.dtype, device=q.device)
     d = attn_desc(cfg, B, T, q.dtype, _rab_stride(rab_pos, rab_time))
     L = _lib.lib()
-    ws = _ws(L.hstu_attn_fwd_workspace_size(C.byref(d)), q.device)
+    nb = L.hstu_attn_fwd_workspace_size(C.byref(d))
+    ws = _layer_ws(workspace, nb, q.device, cfg.reuse_plan)
     st = L.hstu_attn_fwd(C.byref(d), _ptr(q), _ptr(k), q.stride(0), _ptr(v), v.stride(0),
                          _ptr(seq_offsets), _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time),
                          _ptr(num_candidates), _ptr(out), out.stride(0), _ptr(ws), ws.numel(),
@@ -158,10 +162,21 @@ class LayerWorkspace:
     def __init__(self):
         self.buf = None
 
-    def get(self, nbytes: int, device) -> torch.Tensor:
+    def get(self, nbytes: int, device, reuse_plan: int = 0) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            if reuse_plan:
+                raise ValueError("reuse_plan=1 needs the workspace an earlier forward call on "
+                                 "the same batch planned into; this one would be reallocated")
             self.buf = _ws(nbytes, device)
         return self.buf
+
+
+def _layer_ws(workspace: Optional[LayerWorkspace], nbytes: int, device, reuse_plan: int = 0):
+    if workspace is None:
+        if reuse_plan:
+            raise ValueError("reuse_plan=1 needs the persistent workspace of the planning call")
+        return _ws(nbytes, device)
+    return workspace.get(nbytes, device, reuse_plan)
 
 
 def hstu_layer_fwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: LayerConfig,
@@ -177,7 +192,7 @@ def hstu_layer_fwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: L
     d = layer_desc(cfg, B, T, x.dtype, _rab_stride(rab_pos, rab_time))
     L = _lib.lib()
     nb = L.hstu_layer_fwd_workspace_size(C.byref(d), 1 if saved is not None else 0)
-    ws = workspace.get(nb, x.device) if workspace is not None else _ws(nb, x.device)
+    ws = _layer_ws(workspace, nb, x.device, cfg.attn.reuse_plan)
     w = _weights(W1, W2, rab_pos, rab_time, b1, b2, gamma, beta)
     sv = saved.c() if saved is not None else None
     if keep_zh is not None:
@@ -365,7 +380,7 @@ def hstu_layer_fwd_mx(x, wm: MxLayerWeights, rab_pos, rab_time, seq_offsets, tim
     d = layer_desc(cfg, B, T, x.dtype, _rab_stride(rab_pos, rab_time))
     L = _lib.lib()
     nb = L.hstu_layer_fwd_mx_workspace_size(C.byref(d))
-    ws = workspace.get(nb, x.device) if workspace is not None else _ws(nb, x.device)
+    ws = _layer_ws(workspace, nb, x.device, cfg.attn.reuse_plan)
     w = _weights(None, None, rab_pos, rab_time, b1, b2, gamma, beta)
     m = wm.c()
     pair = lambda p: (None, None) if p is None else (_ptr(p[0]), _ptr(p[1]))

@@ -7,6 +7,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "internal.h"
 #include "timer.h"
@@ -72,6 +74,23 @@ hipError_t order_after(hipStream_t to, hipStream_t from, hipEvent_t ev) {
   return e;
 }
 
+// Once a call has forked work onto the side stream, the caller's stream waits
+// for that work on every way out of the call, error returns included, so no
+// side work runs unordered after the call has returned.
+struct SideJoin {
+  SideStream* sd = nullptr;
+  hipStream_t st = nullptr;
+  bool forked = false;
+  hipError_t join() {
+    if (!forked) return hipSuccess;
+    forked = false;
+    return order_after(st, sd->s, sd->ev[3]);
+  }
+  ~SideJoin() {
+    if (forked && join() != hipSuccess) (void)hipGetLastError();
+  }
+};
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 size_t esize(int dtype) { return dtype == HSTU_BF16 ? 2 : 4; }
 
@@ -112,6 +131,95 @@ FwdWs carve_fwd(Carver& c, const hstu_attn_desc* d) {
   w.tm = carve_time(c, d->T, d->B);
   w.sc = carve_sched(c, d->T, d->B, attn_fwd_block_rows(d->dtype, d->d_qk, d->d_v));
   return w;
+}
+
+// ---- plans left in workspaces (reuse_plan) ---------------------------------
+// A forward call that plans records what its plan depends on: the device, the
+// plan's bytes in the workspace, B, T, the row-block size (dtype and head
+// sizes) and the seq_offsets / timestamps buffers.  A later forward that sets
+// reuse_plan must name the same workspace bytes and the same inputs, else it
+// is rejected before anything is launched.  Every other call that is handed
+// a workspace forgets the plans recorded in the bytes it may write.  The
+// registry cannot see writes made outside the library (e.g. the caller
+// reusing the memory for another tensor), nor a change of the offsets' or
+// timestamps' contents; kernels still skip work items that name rows outside
+// the batch, so a stale plan gives wrong rows, never an out-of-bounds access.
+struct PlanTag {
+  int dev = -1;
+  uintptr_t p0 = 0, p1 = 0;  // plan bytes [p0, p1)
+  int32_t B = 0, H = 0, d_qk = 0, d_v = 0, dtype = 0;
+  int64_t T = 0;
+  const void* offs = nullptr;
+  const void* ts = nullptr;
+};
+std::mutex g_plan_mu;
+std::vector<PlanTag> g_plan_tags;
+constexpr size_t kMaxPlanTags = 256;
+
+int current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return dev;
+}
+
+size_t fwd_plan_bytes(const hstu_attn_desc* d) {
+  Carver c(nullptr);
+  carve_fwd(c, d);
+  return c.off;
+}
+
+// forget the plans recorded in [p, p + bytes) of the current device
+void plans_forget(const void* p, size_t bytes) {
+  if (!p || bytes == 0) return;
+  const int dev = current_device();
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + bytes;
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  g_plan_tags.erase(std::remove_if(g_plan_tags.begin(), g_plan_tags.end(),
+                                   [&](const PlanTag& t) {
+                                     return t.dev == dev && t.p0 < a1 && a0 < t.p1;
+                                   }),
+                    g_plan_tags.end());
+}
+
+PlanTag plan_tag(const hstu_attn_desc* d, const void* ws, const int32_t* offs,
+                 const int64_t* ts) {
+  PlanTag t;
+  t.dev = current_device();
+  t.p0 = reinterpret_cast<uintptr_t>(ws);
+  t.p1 = t.p0 + fwd_plan_bytes(d);
+  t.B = d->B;
+  t.H = d->H;
+  t.d_qk = d->d_qk;
+  t.d_v = d->d_v;
+  t.dtype = d->dtype;
+  t.T = d->T;
+  t.offs = offs;
+  t.ts = ts;
+  return t;
+}
+
+void plan_record(const hstu_attn_desc* d, const void* ws, const int32_t* offs,
+                 const int64_t* ts) {
+  const PlanTag t = plan_tag(d, ws, offs, ts);
+  plans_forget(ws, t.p1 - t.p0);
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  if (g_plan_tags.size() >= kMaxPlanTags) g_plan_tags.erase(g_plan_tags.begin());
+  g_plan_tags.push_back(t);
+}
+
+bool plan_recorded(const hstu_attn_desc* d, const void* ws, const int32_t* offs,
+                   const int64_t* ts) {
+  const PlanTag q = plan_tag(d, ws, offs, ts);
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  for (const PlanTag& t : g_plan_tags)
+    if (t.dev == q.dev && t.p0 == q.p0 && t.p1 == q.p1 && t.B == q.B && t.T == q.T &&
+        t.H == q.H && t.d_qk == q.d_qk && t.d_v == q.d_v && t.dtype == q.dtype &&
+        t.offs == q.offs && t.ts == q.ts)
+      return true;
+  return false;
 }
 
 // The backward keeps dS (the scores' gradient) when max_len bounds the
@@ -166,6 +274,7 @@ AttnArgs base_args(const hstu_attn_desc* d, const void* q, const void* k, int64_
   a.rab_pos = rp;
   a.rab_time = rt;
   a.rab_stride = d->rab_head_stride;
+  a.B = d->B;
   a.H = d->H;
   a.nP = d->n_pos_buckets;
   a.nT = d->n_time_buckets;
@@ -219,6 +328,7 @@ hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
   if (!d->reuse_plan) {
     hstu_status s = attn_fwd_plan(d, offs, ts, ws, st);
     if (s != HSTU_OK) return s;
+    plan_record(d, ws, offs, ts);
   }
   return attn_fwd_run(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, out_f32, ws, st);
 }
@@ -273,6 +383,7 @@ hstu_status attn_cached_impl(const hstu_attn_desc* d, const void* q, const void*
   a.out = out; a.ld_out = ld_out; a.out_f32 = out_f32;
   a.part = w.part; a.Tc = d->T; a.splits = w.splits;
   a.rab_pos = rp; a.rab_time = rt; a.rab_stride = d->rab_head_stride;
+  a.B = d->B;
   a.H = d->H; a.nP = d->n_pos_buckets; a.nT = d->n_time_buckets; a.norm_len = d->norm_len;
   a.win_local = d->win_local; a.win_global = d->win_global;
   {
@@ -666,6 +777,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* d, const void* q, const void* k,
     return HSTU_ERR_INVALID_ARG;
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_fwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
+  if (d->reuse_plan && !plan_recorded(d, ws, offs, ts)) return HSTU_ERR_INVALID_ARG;
   return attn_fwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, false, ws,
                        entry_stream(stream));
 }
@@ -697,6 +809,7 @@ hstu_status hstu_attn_cached_fwd(const hstu_attn_desc* d, const void* q, const v
     return HSTU_ERR_INVALID_ARG;
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_cached_workspace_size(d, hist->T)) return HSTU_ERR_WORKSPACE;
+  plans_forget(ws, ws_bytes);
   return attn_cached_impl(d, q, k, ld_qk, v, ld_v, coffs, cts, hist, rp, rt, out, ld_out, false,
                           ws, entry_stream(stream));
 }
@@ -718,6 +831,7 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* d, const void* q, const void* k,
     return HSTU_ERR_INVALID_ARG;
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_bwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
+  plans_forget(ws, ws_bytes);
   return attn_bwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, dout, ld_dout, dq, dk, dv,
                        drp, drt, nullptr, 0, 0, 0, 0, ws, entry_stream(stream));
 }
@@ -766,6 +880,12 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
 
   Carver c(ws);
   LayerFwdWs lw = carve_layer_fwd(c, L, full);
+  if (d->reuse_plan) {
+    if (!plan_recorded(d, lw.attn, offs, ts)) return HSTU_ERR_INVALID_ARG;
+    plans_forget(ws, static_cast<char*>(lw.attn) - static_cast<char*>(ws));
+  } else {
+    plans_forget(ws, ws_bytes);
+  }
   const int64_t W = (int64_t)d->H * d->d_v;
   void* Zh = saved ? saved->Zh : lw.Zh;
   float* O = full ? saved->O : static_cast<float*>(lw.O);
@@ -844,6 +964,12 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
   Carver c(ws);
   MxWs m = carve_mx(c, L);
   LayerFwdWs lw = carve_layer_fwd(c, L, 0);
+  if (d->reuse_plan) {
+    if (!plan_recorded(d, lw.attn, offs, ts)) return HSTU_ERR_INVALID_ARG;
+    plans_forget(ws, static_cast<char*>(lw.attn) - static_cast<char*>(ws));
+  } else {
+    plans_forget(ws, ws_bytes);
+  }
   const int64_t W = (int64_t)d->H * d->d_v;
   float* O = static_cast<float*>(lw.O);
   auto attention = [&](const void* q, const void* k, const void* v, int64_t ld) {
@@ -948,6 +1074,7 @@ hstu_status hstu_layer_fwd_cached(const hstu_layer_desc* L, const void* x,
     return HSTU_ERR_INVALID_ARG;
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_layer_cached_workspace_size(L, hist->T)) return HSTU_ERR_WORKSPACE;
+  plans_forget(ws, ws_bytes);
   hipStream_t st = entry_stream(stream);
 
   Carver c(ws);
@@ -983,6 +1110,7 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
       !aligned16(saved->O) || !aligned16(saved->G) || !aligned16(ws))
     return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_layer_bwd_workspace_size(L)) return HSTU_ERR_WORKSPACE;
+  plans_forget(ws, ws_bytes);
   hipStream_t st = entry_stream(stream);
 
   Carver c(ws);
@@ -1001,7 +1129,11 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   // stream.
   SideStream* sd = side_stream();
   hipStream_t ss = sd ? sd->s : st;
-  if (sd) HSTU_TRY(order_after(ss, st, sd->ev[0]));
+  SideJoin side{sd, st};
+  if (sd) {
+    HSTU_TRY(order_after(ss, st, sd->ev[0]));
+    side.forked = true;
+  }
   s = attn_bwd_plan(d, offs, ts, g->drab_pos, g->drab_time, bw.attn, ss);
   if (s != HSTU_OK) return s;
   if (sd) HSTU_TRY(hipEventRecord(sd->ev[1], ss));
@@ -1075,7 +1207,7 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a4.epi = EPI_RESID;
   a4.R = L->residual ? dy : nullptr; a4.ldr = D;
   { HSTU_TIMED(TT_GEMM_DX, st); HSTU_TRY(launch_gemm(a4, d->dtype, st)); }
-  if (sd) HSTU_TRY(order_after(st, ss, sd->ev[3]));
+  HSTU_TRY(side.join());
   return HSTU_OK;
 }
 
@@ -1098,6 +1230,7 @@ hstu_status hstu_schedule(int32_t B, int64_t T, const int32_t* offs, int32_t blo
       !n_items || !ws)
     return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_schedule_workspace_size(B, T, block_rows)) return HSTU_ERR_WORKSPACE;
+  plans_forget(ws, ws_bytes);
   hipStream_t st = entry_stream(stream);
   Carver c(ws);
   Sched sc = carve_sched(c, T, B, block_rows);
@@ -1117,6 +1250,7 @@ hstu_status hstu_bias_buckets(const hstu_attn_desc* d, const int32_t* offs, cons
   if (!offs || !ws || n_pairs < 0) return HSTU_ERR_INVALID_ARG;
   if (n_pairs > 0 && (!ts || !ps || !pi || !pj || !bp || !bt)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_fwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
+  plans_forget(ws, ws_bytes);
   hipStream_t st = entry_stream(stream);
   Carver c(ws);
   FwdWs w = carve_fwd(c, d);

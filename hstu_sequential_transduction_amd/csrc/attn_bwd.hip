@@ -172,6 +172,7 @@ __global__ __launch_bounds__((KvShape<DQK, DV>::NT), (KvShape<DQK, DV>::OCC)) vo
   const int it = w / a.H, h = w - it * a.H;
   const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
   const int kb = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  if (b < 0 || b >= a.B || kb < 0) return;  // not an item of this batch
   const int o0 = __builtin_amdgcn_readfirstlane(a.seq_offsets[b]);
   const int n = __builtin_amdgcn_readfirstlane(a.seq_offsets[b + 1]) - o0;
   const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;
@@ -741,6 +742,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(AttnArgs a) {
   const int it = w / a.H, h = w - it * a.H;
   const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
   const int m = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  if (b < 0 || b >= a.B || m < 0) return;  // not an item of this batch
   const int o0 = __builtin_amdgcn_readfirstlane(a.seq_offsets[b]);
   const int n = __builtin_amdgcn_readfirstlane(a.seq_offsets[b + 1]) - o0;
   const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;
@@ -968,6 +970,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq_ds(AttnArgs a) {
   const int it = w / a.H, h = w - it * a.H;
   const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
   const int rb = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  if (b < 0 || b >= a.B || rb < 0) return;  // not an item of this batch
   const int o0 = __builtin_amdgcn_readfirstlane(a.seq_offsets[b]);
   const int n = __builtin_amdgcn_readfirstlane(a.seq_offsets[b + 1]) - o0;
   const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;

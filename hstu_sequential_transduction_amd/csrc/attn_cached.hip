@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_cached_bf16(CachedArgs a) {
   const int h = rem / S, sp = rem - h * S;
   const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
   const int m = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  if (b < 0 || b >= a.B || m < 0) return;  // not an item of this batch
   const int c0 = __builtin_amdgcn_readfirstlane(a.cand_offsets[b]);
   const int nc = __builtin_amdgcn_readfirstlane(a.cand_offsets[b + 1]) - c0;
   const int h0 = __builtin_amdgcn_readfirstlane(a.hist_offsets[b]);
@@ -366,6 +367,7 @@ __global__ __launch_bounds__(256) void k_attn_cached_f32(CachedArgs a) {
   const int rem = w - it * per_item;
   const int h = rem / S, sp = rem - h * S;
   const int b = a.items[2 * it], m = a.items[2 * it + 1];
+  if (b < 0 || b >= a.B || m < 0) return;  // not an item of this batch
   const int c0 = a.cand_offsets[b];
   const int nc = a.cand_offsets[b + 1] - c0;
   const int h0 = a.hist_offsets[b];

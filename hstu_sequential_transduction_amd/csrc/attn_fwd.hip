@@ -85,8 +85,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
   const int it = w / a.H, h = w - it * a.H;
   const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
   const int m = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
+  if (b < 0 || b >= a.B || m < 0) return;  // not an item of this batch
   const int o0 = __builtin_amdgcn_readfirstlane(a.seq_offsets[b]);
   const int n = __builtin_amdgcn_readfirstlane(a.seq_offsets[b + 1]) - o0;
+  if (m >= (n + BM - 1) / BM) return;
   const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;
   const int nh = n - c;
   const int flags = __builtin_amdgcn_readfirstlane(a.seq_flags[b]);
@@ -403,8 +405,10 @@ __global__ __launch_bounds__(256) void k_attn_fwd_f32(AttnArgs a) {
   if (w >= n_items * a.H) return;
   const int it = w / a.H, h = w - it * a.H;
   const int b = a.items[2 * it], m = a.items[2 * it + 1];
+  if (b < 0 || b >= a.B || m < 0) return;  // not an item of this batch
   const int o0 = a.seq_offsets[b];
   const int n = a.seq_offsets[b + 1] - o0;
+  if (m * 64 >= n) return;
   const int c = a.num_cand ? a.num_cand[b] : 0;
   const int nh = n - c;
   const bool wide = a.seq_flags[b] & 1;

@@ -119,6 +119,7 @@ struct AttnArgs {
   const float* rab_pos = nullptr;
   const float* rab_time = nullptr;
   int64_t rab_stride = 0;
+  int B = 0;  // sequences: a work item naming another sequence is skipped
   int H = 0, nP = 0, nT = 0, norm_mode = 0, norm_len = 1;
   // semi-local windows (win_local 0: full causal)
   int win_local = 0, win_global = 0;
@@ -274,6 +275,7 @@ struct CachedArgs {
   const float* rab_pos = nullptr;
   const float* rab_time = nullptr;
   int64_t rab_stride = 0;
+  int B = 0;  // users: a work item naming another user is skipped
   int H = 0, nP = 0, nT = 0, norm_len = 1, win_local = 0, win_global = 0;
 };
 int attn_cached_block_rows(int dtype, int d_qk, int d_v);

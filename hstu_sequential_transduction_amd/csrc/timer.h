@@ -43,4 +43,7 @@ struct TimedScope {
 
 }  // namespace hstu
 
-#define HSTU_TIMED(tag, st) ::hstu::TimedScope hstu_timed_scope_##__LINE__((tag), (st))
+// two-level paste so that __LINE__ expands: one distinct scope object per line
+#define HSTU_CAT_(a, b) a##b
+#define HSTU_CAT(a, b) HSTU_CAT_(a, b)
+#define HSTU_TIMED(tag, st) ::hstu::TimedScope HSTU_CAT(hstu_timed_scope_, __LINE__)((tag), (st))

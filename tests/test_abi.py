@@ -200,3 +200,34 @@ def test_cached_ranking_argument_errors(L):
     small = L.hstu_attn_cached_fwd(C.byref(d), p, p, 64, p, 64, p, p, C.byref(hist), p, p, p, 64,
                                    ws, 16, None)
     assert small == -3
+
+
+def test_reuse_plan_without_a_recorded_plan_is_rejected(L):
+    """reuse_plan = 1 is checked against the plans the library recorded; a
+    workspace no forward call planned into is refused before any launch."""
+    buf = C.create_string_buffer(1 << 20)
+    ws = C.c_void_p((C.addressof(buf) + 255) & ~255)
+    p = C.c_void_p(1 << 20)
+    d = _desc(reuse_plan=1)
+    st = L.hstu_attn_fwd(C.byref(d), p, p, 64, p, 64, p, p, p, p, None, p, 64, ws, 1 << 19, None)
+    assert st == -1
+    ld = _lib.LayerDesc(_desc(reuse_plan=1, d_qk=32, d_v=32, H=2), 64, 1, 1, 1e-6)
+    w = _lib.LayerWeights(p, p, None, None, None, None, p, p)
+    st = L.hstu_layer_fwd(C.byref(ld), p, C.byref(w), p, p, None, C.c_void_p((1 << 20) + 4096),
+                          None, ws, 1 << 19, None)
+    assert st == -1
+
+
+def test_binding_refuses_reuse_plan_without_its_workspace():
+    import torch
+
+    from hstu_sequential_transduction_amd import binding as B
+    with pytest.raises(ValueError):
+        B._layer_ws(None, 1024, torch.device("cpu"), 1)
+    lw = B.LayerWorkspace()
+    with pytest.raises(ValueError):   # nothing planned into it yet: it would be allocated now
+        lw.get(1024, torch.device("cpu"), 1)
+    buf = lw.get(1024, torch.device("cpu"))
+    assert lw.get(512, torch.device("cpu"), 1) is buf
+    with pytest.raises(ValueError):   # too small: would be reallocated
+        lw.get(4096, torch.device("cpu"), 1)
