@@ -94,6 +94,27 @@ def hstu_attn_fwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, cfg: Attn
     return out
 
 
+def hstu_attn_fwd_noalloc(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, cfg: AttnConfig,
+                          num_candidates=None, out=None, stream=None):
+    """hstu_attn_fwd without a workspace: the library's per-GPU scratch holds
+    the plan (see include/hstu.h).  `out` is allocated here unless given."""
+    for n_, t_ in (("q", q), ("k", k), ("v", v), ("seq_offsets", seq_offsets),
+                   ("timestamps", timestamps), ("rab_pos", rab_pos), ("rab_time", rab_time),
+                   ("num_candidates", num_candidates), ("out", out)):
+        _dev(t_, n_)
+    T = q.shape[0]
+    B = seq_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, cfg.H * cfg.d_v), dtype=q.dtype, device=q.device)
+    d = attn_desc(cfg, B, T, q.dtype, _rab_stride(rab_pos, rab_time))
+    st = _lib.lib().hstu_attn_fwd_noalloc(
+        C.byref(d), _ptr(q), _ptr(k), q.stride(0), _ptr(v), v.stride(0), _ptr(seq_offsets),
+        _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time), _ptr(num_candidates), _ptr(out),
+        out.stride(0), _stream(stream))
+    check("hstu_attn_fwd_noalloc", st)
+    return out
+
+
 def hstu_attn_bwd(q, k, v, seq_offsets, timestamps, rab_pos, rab_time, d_out, cfg: AttnConfig,
                   num_candidates=None, stream=None):
     """(dq, dk, dv, d_rab_pos, d_rab_time) for the output gradient d_out."""

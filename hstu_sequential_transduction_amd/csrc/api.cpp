@@ -729,6 +729,36 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
   return HSTU_OK;
 }
 
+// ---- scratch of hstu_attn_fwd_noalloc ---------------------------------------
+// The plan of the no-allocation forward lives in this array: one copy per GPU
+// (each device holds its own, at its own address, until the process ends).
+// In host code the name is only a stand-in for the symbol: device addresses
+// come from hipGetSymbolAddress, taken once per device with that device
+// current, and only those are handed to kernels.
+__device__ __align__(256) unsigned char scratch[HSTU_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's scratch, resolved on first use
+hipError_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -777,6 +807,26 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* d, const void* q, const void* k,
     return HSTU_ERR_INVALID_ARG;
   if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
   if (ws_bytes < hstu_attn_fwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
+  if (d->reuse_plan && !plan_recorded(d, ws, offs, ts)) return HSTU_ERR_INVALID_ARG;
+  return attn_fwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, false, ws,
+                       entry_stream(stream));
+}
+
+hstu_status hstu_attn_fwd_noalloc(const hstu_attn_desc* d, const void* q, const void* k,
+                                  int64_t ld_qk, const void* v, int64_t ld_v, const int32_t* offs,
+                                  const int64_t* ts, const float* rp, const float* rt,
+                                  const int32_t* nc, void* out, int64_t ld_out, void* stream) {
+  hstu_status s = check_attn_desc(d);
+  if (s != HSTU_OK) return s;
+  if (d->T > 0 && (!q || !k || !v || !out || !ts)) return HSTU_ERR_INVALID_ARG;
+  if (!offs || !rp || !rt) return HSTU_ERR_INVALID_ARG;
+  const int64_t hq = (int64_t)d->H * d->d_qk, hv = (int64_t)d->H * d->d_v;
+  if (d->T > 0 && (!stride_ok(d->dtype, q, ld_qk, hq) || !stride_ok(d->dtype, k, ld_qk, hq) ||
+                   !stride_ok(d->dtype, v, ld_v, hv) || ld_out < hv))
+    return HSTU_ERR_INVALID_ARG;
+  if (hstu_attn_fwd_workspace_size(d) > HSTU_NOALLOC_SCRATCH_BYTES) return HSTU_ERR_WORKSPACE;
+  void* ws = nullptr;
+  HSTU_TRY(scratch_for_current_device(&ws));
   if (d->reuse_plan && !plan_recorded(d, ws, offs, ts)) return HSTU_ERR_INVALID_ARG;
   return attn_fwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, false, ws,
                        entry_stream(stream));

@@ -192,6 +192,30 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * hstu_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and kernels, with no workspace argument.  The plan
+ * (time pre-pass and work list) goes to a library-owned scratch array of
+ * HSTU_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; the call
+ * itself never allocates or frees.  Problems whose forward workspace
+ * (hstu_attn_fwd_workspace_size) exceeds that size are rejected with
+ * HSTU_ERR_WORKSPACE before anything is launched (8 MiB holds the plan of
+ * about 1.9 million rows).  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (other streams, other threads)
+ * race and must be ordered by the caller.  reuse_plan = 1 refers to the
+ * plan the previous no-allocation call on the device left there.  Other
+ * arguments and errors as hstu_attn_fwd.
+ */
+#define HSTU_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+hstu_status hstu_attn_fwd_noalloc(const hstu_attn_desc* desc,
+                                  const void* q, const void* k, int64_t ld_qk,
+                                  const void* v, int64_t ld_v,
+                                  const int32_t* seq_offsets, const int64_t* timestamps,
+                                  const float* rab_pos, const float* rab_time,
+                                  const int32_t* num_candidates,
+                                  void* out, int64_t ld_out, void* stream);
+
+/*
  * Gradients of hstu_attn_fwd for the output gradient d_out ([T, H*d_v],
  * stride ld_out).  dq, dk (stride ld_qk) and dv (stride ld_v) are written in
  * dtype; d_rab_pos / d_rab_time (fp32, same shape as the tables) are
