@@ -8,7 +8,7 @@
 // Architecture"; lower triangle only: its Table 7 note).
 //
 // bf16 kernel (gfx950 MFMA): one workgroup = one (sequence, query block,
-// head) work item, four waves of 32 (d = 128) or 64 (d <= 64) query rows.  Q
+// head) work item, four waves of 32 query rows.  Q
 // stays in registers as the B operand of S^T = K Q^T (32x32x16 MFMA).  Tiles
 // of 64 keys of K and V arrive row-major by buffer->LDS DMA, double-buffered;
 // K is read along rows (A operand of S^T) and V down its columns with
@@ -35,12 +35,18 @@ constexpr int FWD_BN = 64;  // keys per tile
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// 32-row query groups per wave: two when d <= 64 (each K/V fragment read from
-// LDS then feeds two MFMAs), one at d = 128 where registers run out first.
+// One 32-row query group per wave.  The kernel is bound by latency inside
+// each wave (LDS reads -> S MFMAs -> VALU -> P V MFMAs), so what pays is
+// waves per SIMD: at d <= 64 a wave fits in 159 VGPRs and three workgroups
+// share a compute unit (three waves per SIMD); at d = 128 registers allow
+// two.  (Two 32-row groups per wave at d <= 64, which let every K/V fragment
+// read from LDS feed two MFMAs, needed 240 VGPRs and two workgroups per
+// compute unit, and was 1.26x slower on the 8-layer Zipf workload.)
 template <int DQK, int DV>
 struct FwdShape {
-  static constexpr int QG = (DQK <= 64 && DV <= 64) ? 2 : 1;
+  static constexpr int QG = 1;
   static constexpr int BM = 4 * 32 * QG;  // query rows per workgroup (four waves)
+  static constexpr int OCC = (DQK <= 64 && DV <= 64) ? 3 : 2;  // workgroups per CU
 };
 
 // One staged key tile: row-major K and V and the key times.
@@ -72,7 +78,7 @@ template <int V>
 using mconst = std::integral_constant<int, V>;
 
 template <int DQK, int DV, bool WIN>
-__global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16(AttnArgs a) {
   constexpr int QG = FwdShape<DQK, DV>::QG;
   constexpr int BM = FwdShape<DQK, DV>::BM;
   __shared__ __attribute__((aligned(1024))) FwdBuf<DQK, DV> fwb0;
@@ -514,7 +520,9 @@ hipError_t launch_fwd_dv(const AttnArgs& a, int dtype, int d_v, int64_t mi, hipS
 
 int attn_fwd_block_rows(int dtype, int d_qk, int d_v) {
   if (dtype != HSTU_BF16) return ATTN_FWD_BM_F32;
-  return (d_qk <= 64 && d_v <= 64) ? FwdShape<64, 64>::BM : FwdShape<128, 128>::BM;
+  (void)d_qk;
+  (void)d_v;
+  return FwdShape<64, 64>::BM;  // the same for every head size
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, int d_qk, int d_v, int64_t max_items,
