@@ -9,11 +9,16 @@ seeded inputs resident in HBM before timing starts.
 
 Prints one JSON line.  `value` is whole-step algorithmic TFLOP/s (the DLRMv4
 page's Table 7 convention: weight GEMMs x3, attention x3.5 for fwd+bwd, S^2/2
-pairs per sequence); tokens/s and the fraction of the 2.5 PFLOP/s bf16 peak
-are reported alongside, with a per-kernel breakdown taken with HIP events
-inside the timed region, the roofline of the dominant kernel, forward-only
-figures for the other workloads, and the fp64 CPU oracle timed on a bounded
-sample (one sequence) of the same workload.
+pairs per sequence) over exactly --steps steps timed between two events with
+no instrumentation in the region; per-step events give the median and
+p10/p90.  A separate instrumented pass of the same steps (the library's HIP
+event pairs around every launch) gives the per-kernel table and the roofline
+of the dominant kernel.  Alongside: the step with dQ recomputed instead of
+formed from the kept score gradient, forward-only figures of the other
+workloads, the LayerNorm-gate epilogue's bandwidth warm, after a cache flush
+and with a working set larger than the last-level cache, a measured MFMA
+rate and copy bandwidth beside the nominal peaks, and the fp64 CPU oracle
+timed on bounded samples of every workload.
 """
 from __future__ import annotations
 
@@ -69,6 +74,9 @@ def kernel_work(cfg, lengths, T, cand=None, keep_ds=True):
 
 
 class Timer:
+    """The library's diagnostic per-kernel timer (HIP event pairs around each
+    launch site, on the stream the launch uses)."""
+
     def __init__(self, L):
         self.L = L
 
@@ -90,6 +98,60 @@ class Timer:
         return out
 
 
+def time_region(fn, steps, warmup, between=None):
+    """Runs `warmup` untimed calls, then `steps` calls between events on the
+    current stream (one event per call boundary; nothing else in the region
+    unless `between` is given, which runs before each call and is excluded
+    from the per-call times but not from the total).  Returns mean (total /
+    steps), median, p10, p90 in ms."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    steps = max(int(steps), 1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        if between is not None:
+            between()
+        ev[2 * i].record()
+        fn()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)])
+    total = ev[0].elapsed_time(ev[-1])
+    return {"ms_mean": round(float(total / steps) if between is None else float(per.mean()), 4),
+            "ms_median": round(float(np.median(per)), 4),
+            "ms_p10": round(float(np.percentile(per, 10)), 4),
+            "ms_p90": round(float(np.percentile(per, 90)), 4), "reps": steps}
+
+
+def instrumented(fn, timer, steps, per_call_launches=64):
+    """Per-kernel times of `steps` calls of fn with the library timer on."""
+    import torch
+    torch.cuda.synchronize()
+    timer.enable(per_call_launches * max(steps, 1))
+    timer.reset()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    kern = timer.read()
+    timer.enable(0)
+    return kern, e0.elapsed_time(e1) / max(steps, 1)
+
+
+def timed_pair(fn, timer, reps, per_call_launches):
+    """Mean ms of `reps` uninstrumented calls, then the per-kernel times of
+    `reps` instrumented calls (summed: {tag: (launches, ms)})."""
+    st = time_region(fn, reps, 1)
+    kern, _ = instrumented(fn, timer, reps, per_call_launches)
+    return st["ms_mean"], kern
+
+
 def upload_layer(inp, cfg, li=0):
     import numpy as np
     import torch
@@ -100,7 +162,10 @@ def upload_layer(inp, cfg, li=0):
         rp=torch.from_numpy(w.rab_pos).cuda(), rt=torch.from_numpy(w.rab_time).cuda())
 
 
-def bench_train(args, timer, window=(0, 0)):
+def train_setup(window=(0, 0), keep_ds=True):
+    """The training workload on the device and one step (layer fwd + bwd) as a
+    closure.  keep_ds: pass the longest sequence as max_len, which lets the
+    backward keep the score gradient dS and form dQ from it."""
     import numpy as np
     import torch
 
@@ -117,10 +182,9 @@ def bench_train(args, timer, window=(0, 0)):
     offs = torch.from_numpy(inp.seq_offsets.astype(np.int32)).cuda()
     ts = torch.from_numpy(inp.timestamps).cuda()
     w = upload_layer(inp, cfg)
-    # max_len: the workload's longest sequence, which lets the backward keep dS
     ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len,
                       win_local=window[0], win_global=window[1],
-                      max_len=int(inp.lengths.max()))
+                      max_len=int(inp.lengths.max()) if keep_ds else 0)
     lc = B.LayerConfig(D=cfg.D, attn=ac)
     saved = B.Saved(T, lc, td, "cuda")
     y = torch.empty_like(X)
@@ -136,25 +200,40 @@ def bench_train(args, timer, window=(0, 0)):
         B.hstu_layer_bwd(X, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc, saved, dY, dx=dx,
                          grads=grads, workspace=wsb)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # timed region: K steps between two events on the stream the library launches on
-    timer.enable(64 * max(args.steps, 1))
-    timer.reset()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / max(args.steps, 1)
-    kern = timer.read()
-    timer.enable(0)
     lf = flops.layer_flops(inp.lengths, None, cfg.D, cfg.H, cfg.d_qk, cfg.d_v, backward=True,
                            window=window if window[0] > 0 else None)
-    return cfg, inp, ms, kern, lf
+    return cfg, inp, step, lf
+
+
+def bench_train(args, timer, window=(0, 0), keep_ds=True):
+    """Uninstrumented timed region of --steps steps, then an instrumented pass
+    of the same number of steps (at most 20) for the per-kernel table."""
+    cfg, inp, step, lf = train_setup(window, keep_ds)
+    stats = time_region(step, args.steps, args.warmup)
+    kern, ms_instr = instrumented(step, timer, min(args.steps, 20))
+    stats["ms_instrumented"] = round(ms_instr, 4)
+    stats["instrumented_steps"] = min(args.steps, 20)
+    return cfg, inp, stats, kern, lf
+
+
+def bench_recompute(args, timer, kept_ms):
+    """The same training step without max_len: dQ recomputes S and dA instead
+    of reading the kept score gradient (no O(sum n^2) buffer)."""
+    cfg, inp, stats, kern, lf = bench_train(args, timer, keep_ds=False)
+    ms = stats["ms_mean"]
+    work = kernel_work(cfg, inp.lengths, inp.T, keep_ds=False)
+    kt = {}
+    for name in ("attn_bwd_dkdv", "attn_bwd_dq"):
+        if name in kern:
+            n, t = kern[name]
+            kt[name] = {"ms_per_launch": round(t / n, 5),
+                        "tflops": round(work[name][1] / (t / n * 1e-3) / 1e12, 2)}
+    out = {"ms_per_step": ms, **{k: v for k, v in stats.items() if k != "ms_mean"},
+           "tflops": round(lf["total"] / (ms * 1e-3) / 1e12, 2),
+           "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
+           "slowdown_vs_kept_ds": round(ms / kept_ms, 3), "kernels": kt}
+    log(f"train step, dQ recomputed: {ms:.3f} ms ({out['tflops']} TFLOP/s)")
+    return out
 
 
 # Semi-local attention windows of the extra training-step measurement: the
@@ -167,11 +246,13 @@ def bench_semilocal(args, timer, full_ms):
     """The same training step with semi-local attention; TFLOP/s on the
     windowed work (exact pair count), and the speedup over full causal."""
     from hstu_sequential_transduction_amd import flops
-    cfg, inp, ms, kern, lf = bench_train(args, timer, window=SEMILOCAL_WINDOW)
+    cfg, inp, stats, kern, lf = bench_train(args, timer, window=SEMILOCAL_WINDOW)
+    ms = stats["ms_mean"]
     full_pairs = flops.attn_pairs_window(inp.lengths, None, 0, 0)
     win_pairs = flops.attn_pairs_window(inp.lengths, None, *SEMILOCAL_WINDOW)
     out = {"win_local": SEMILOCAL_WINDOW[0], "win_global": SEMILOCAL_WINDOW[1],
-           "ms_per_step": round(ms, 4), "tflops": round(lf["total"] / (ms * 1e-3) / 1e12, 2),
+           "ms_per_step": ms, "ms_median": stats["ms_median"],
+           "tflops": round(lf["total"] / (ms * 1e-3) / 1e12, 2),
            "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
            "attn_pairs_frac": round(win_pairs / full_pairs, 4),
            "speedup_vs_full_causal": round(full_ms / ms, 3),
@@ -189,7 +270,7 @@ TRUNC_KEEP = 1024
 TRUNC_SCHEME = (3, 6)
 
 
-def bench_truncation(timer, reps=3):
+def bench_truncation(timer, reps=5):
     """Inference forward of (a) 6 full layers, (b) 3 full + 6 truncated
     layers, (c) as (b) with semi-local windows in the full layers."""
     import dataclasses
@@ -235,19 +316,7 @@ def bench_truncation(timer, reps=3):
                                               T_seg=T_seg, workspace=ws)
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        timer.enable(64 * reps * 10)
-        timer.reset()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        kern = timer.read()
-        timer.enable(0)
-        return e0.elapsed_time(e1) / reps, kern
+        return timed_pair(fn, timer, reps, 64 * 10)
 
     def lf(lengths, window=None):
         return flops.layer_flops(lengths, inp.num_candidates, cfg.D, cfg.H, cfg.d_qk, cfg.d_v,
@@ -274,7 +343,7 @@ def bench_truncation(timer, reps=3):
     return out
 
 
-def bench_cached(timer, reps=5):
+def bench_cached(timer, reps=10):
     """Ranking workload (16 users x (4096 history + 512 candidates), 4 layers,
     inference): the full target-aware pass against the cached path, which
     runs the histories once (cache build) and then only the candidates."""
@@ -324,19 +393,7 @@ def bench_cached(timer, reps=5):
         RK.cached_stack_fwd(Xc, lay, cache, c_off, c_ts, lc, workspace=ws, out_bufs=cbufs)
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        timer.enable(64 * reps * cfg.n_layers)
-        timer.reset()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        kern = timer.read()
-        timer.enable(0)
-        return e0.elapsed_time(e1) / reps, kern
+        return timed_pair(fn, timer, reps, 64 * cfg.n_layers)
 
     ms_full, _ = timed(full)
     ms_build, _ = timed(build)
@@ -367,7 +424,7 @@ def bench_cached(timer, reps=5):
     return out
 
 
-def bench_mx(timer, reps=5):
+def bench_mx(timer, reps=10):
     """Inference forward of the ranking workload (4 layers) with bf16 products
     against MXFP8 projection and output products (attention bf16 in both)."""
     import numpy as np
@@ -411,19 +468,8 @@ def bench_mx(timer, reps=5):
             x_mx = y_mx
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        timer.enable(64 * reps * cfg.n_layers)
-        timer.reset()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        kern = timer.read()
-        timer.enable(0)
-        return e0.elapsed_time(e1) / reps, {k: round(v[1] / reps, 4) for k, v in kern.items()}
+        ms, kern = timed_pair(fn, timer, reps, 64 * cfg.n_layers)
+        return ms, {k: round(v[1] / reps, 4) for k, v in kern.items()}
 
     ms_b, kb = timed(run_bf16)
     ms_m, km = timed(run_mx)
@@ -486,8 +532,10 @@ def roofline(cfg, inp, kern, steps, traffic_dir):
     return roof, table
 
 
-def bench_fwd_configs(timer, reps=3):
-    """Forward-only figures of the inference workloads (context for the forward kernel)."""
+def bench_fwd_configs(timer, configs=(2, 3, 5), reps=20):
+    """Forward-only figures of the inference workloads (context for the forward
+    kernel): uninstrumented median of `reps` runs, per-kernel times from an
+    instrumented pass."""
     import numpy as np
     import torch
 
@@ -495,7 +543,7 @@ def bench_fwd_configs(timer, reps=3):
     from hstu_sequential_transduction_amd import binding as B
     from hstu_sequential_transduction_amd import flops
     out = {}
-    for ci in (2, 3, 5):
+    for ci in configs:
         cfg = synth.get_config(ci)
         inp = synth.make_inputs(cfg)
         td = torch.bfloat16
@@ -521,19 +569,9 @@ def bench_fwd_configs(timer, reps=3):
                                      lc if li == 0 else lc_r, num_candidates=nc,
                                      y=bufs[li % 2], workspace=ws)
 
-        run()
-        torch.cuda.synchronize()
-        timer.enable(64 * reps * cfg.n_layers)
-        timer.reset()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        kern = timer.read()
-        timer.enable(0)
+        st = time_region(run, reps, 2)
+        kern, _ = instrumented(run, timer, reps, 64 * cfg.n_layers)
+        ms = st["ms_median"]
         lf = flops.layer_flops(inp.lengths, inp.num_candidates, cfg.D, cfg.H, cfg.d_qk, cfg.d_v,
                                backward=False)
         tot = lf["total"] * cfg.n_layers
@@ -541,15 +579,115 @@ def bench_fwd_configs(timer, reps=3):
         n_a, ms_a = kern.get("attn_fwd", (0, 0.0))
         a_tf = af / (ms_a / max(n_a, 1) * 1e-3) / 1e12 if n_a else None
         out[cfg.name] = {
-            "ms": round(ms, 4), "tokens": inp.T, "layers": cfg.n_layers,
+            "ms": ms, "ms_mean": st["ms_mean"], "ms_p10": st["ms_p10"], "ms_p90": st["ms_p90"],
+            "reps": reps, "tokens": inp.T, "layers": cfg.n_layers,
             "tflops": round(tot / (ms * 1e-3) / 1e12, 2),
             "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
+            "attn_fwd_ms_per_layer": None if not n_a else round(ms_a / n_a, 5),
             "attn_fwd_tflops": None if a_tf is None else round(a_tf, 2),
             "attn_fwd_frac_bf16_peak": None if a_tf is None else round(a_tf / PEAK_BF16_TFLOPS, 4),
             "kernel_ms": {k: round(v[1] / reps, 4) for k, v in kern.items()},
         }
         log(f"fwd {cfg.name}: {out[cfg.name]}")
     return out
+
+
+def bench_epilogue(timer, reps=20):
+    """Bandwidth of the LayerNorm + gating epilogue (forward) inside the
+    inference forward of the training workload's batch: warm (calls back to
+    back), after a 1 GiB write between calls (last-level cache flushed; O and
+    U still come straight from the kernels of the same call that produced
+    them), and on a batch of four times as many tokens, whose O, U and G
+    (0.94 GB) exceed the 256 MB last-level cache."""
+    import numpy as np
+    import torch
+
+    import synth
+    from hstu_sequential_transduction_amd import binding as B
+    cfg = synth.get_config(4)
+    out = {}
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for name, mult in (("warm", 1), ("flushed", 1), ("working_set_4x", 4)):
+        inp = synth.make_inputs(cfg)
+        X = torch.from_numpy(inp.X).to(torch.bfloat16).cuda()
+        lengths = inp.lengths
+        offs_np = inp.seq_offsets.astype(np.int64)
+        ts_np = inp.timestamps
+        if mult > 1:
+            X = X.repeat(mult, 1)
+            lengths = np.tile(lengths, mult)
+            offs_np = np.concatenate([[0], np.cumsum(lengths)])
+            ts_np = np.tile(ts_np, mult)
+        offs = torch.from_numpy(offs_np.astype(np.int32)).cuda()
+        ts = torch.from_numpy(ts_np).cuda()
+        w = upload_layer(inp, cfg)
+        lc = B.LayerConfig(D=cfg.D, attn=B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v,
+                                                      norm_len=cfg.norm_len))
+        ws = B.LayerWorkspace()
+        y = torch.empty_like(X)
+
+        def run():
+            B.hstu_layer_fwd(X, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc, y=y,
+                             workspace=ws)
+
+        run()
+        torch.cuda.synchronize()
+        timer.enable(64 * reps)
+        timer.reset()
+        for _ in range(reps):
+            if name == "flushed":
+                flush.fill_(1)
+            run()
+        torch.cuda.synchronize()
+        kern = timer.read()
+        timer.enable(0)
+        n, ms = kern["ln_gate_fwd"]
+        T = int(offs_np[-1])
+        W = cfg.H * cfg.d_v
+        byts = T * (4.0 * W + 2 * W + 2 * W)     # O fp32 + U read, G written (no stats)
+        gbs = byts / (ms / n * 1e-3) / 1e9
+        out[name] = {"tokens": T, "ms": round(ms / n, 5), "bytes": byts, "gbs": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        del X, y, ws
+    log(f"LayerNorm-gate epilogue: {out}")
+    return out
+
+
+def bench_peaks(reps=10):
+    """Measured MFMA rate (the library's MFMA-loop diagnostic) and device-copy
+    bandwidth (a 2 GiB tensor copy), beside the nominal peaks."""
+    import ctypes as C
+
+    import torch
+
+    from hstu_sequential_transduction_amd import _lib
+    L = _lib.lib()
+    wg, iters = 1024, 2000
+    buf = torch.empty(4 * wg, dtype=torch.float32, device="cuda")
+    st = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    run = lambda: _lib.check("hstu_diag_mfma_loop",
+                             L.hstu_diag_mfma_loop(iters, wg, C.c_void_p(buf.data_ptr()), st))
+    t = time_region(run, reps, 2)
+    flop = wg * 4.0 * iters * 4 * 32768
+    mfma = flop / (t["ms_median"] * 1e-3) / 1e12
+    a = torch.empty(1 << 30, dtype=torch.uint16, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    tc = time_region(lambda: b.copy_(a), reps, 2)
+    gbs = 2 * a.numel() * 2 / (tc["ms_median"] * 1e-3) / 1e9
+    out = {"mfma_bf16_tflops_measured": round(mfma, 1), "mfma_bf16_tflops_nominal": PEAK_BF16_TFLOPS,
+           "copy_gbs_measured": round(gbs, 1), "hbm_gbs_nominal": PEAK_HBM_GBS,
+           "mfma_probe": f"{wg} workgroups x 4 waves x {iters} x 4 independent 32x32x16 bf16 MFMAs",
+           "copy_probe": "2 GiB device-to-device tensor copy (read + write counted)"}
+    log(f"peaks: {out}")
+    return out
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
+    except Exception:
+        return os.cpu_count()
 
 
 CPU_SAMPLE_SEQS = 3
@@ -563,11 +701,6 @@ def cpu_baseline(cfg, inp):
     import synth
     from hstu_sequential_transduction_amd import flops
     from oracle import hstu as orc
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=os.cpu_count())
-    except Exception:
-        cores = os.cpu_count()
     idx = sorted(int(i) for i in np.argsort(inp.lengths, kind="stable")[:CPU_SAMPLE_SEQS])
     sub = synth.sub_batch(inp, idx)
     w = sub.layers[0]
@@ -579,22 +712,67 @@ def cpu_baseline(cfg, inp):
                   sub.timestamps, None, f, sv)
     dt = time.perf_counter() - t0
     lf = flops.layer_flops(sub.lengths, None, cfg.D, cfg.H, cfg.d_qk, cfg.d_v, backward=True)
-    return {"value": round(lf["total"] / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+    return {"value": round(lf["total"] / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(_cores()),
             "kind": "oracle", "seconds": round(dt, 2),
             "tokens_per_s": round(sub.T / dt, 1),
             "sample": f"the {len(idx)} shortest sequences ({sub.T} tokens) of the training "
                       f"batch, fwd+bwd of one layer, fp64 numpy"}
 
 
+# Bounded oracle samples of the forward workloads: config -> (first sequences
+# or None for the whole batch, layers); about 6 s on 16 host threads
+CPU_FWD_SAMPLES = {1: (None, 1), 2: (None, 1), 3: (None, 1), 5: (4, 1)}
+
+
+def cpu_baseline_configs():
+    """The fp64 oracle's forward on a bounded sample of each inference workload
+    (whole batch for the small fp32 workload, the first sequences otherwise,
+    one layer), as GFLOP/s and tokens/s with the same algorithmic FLOPs."""
+    import numpy as np
+
+    import synth
+    from hstu_sequential_transduction_amd import flops
+    from oracle import hstu as orc
+    out = {}
+    for ci, (nseq, nl) in CPU_FWD_SAMPLES.items():
+        cfg = synth.get_config(ci)
+        inp = synth.make_inputs(cfg)
+        sub = inp if nseq is None else synth.sub_batch(inp, list(range(nseq)))
+        f = orc.LayerFlags(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len, eps=1e-6)
+        t0 = time.perf_counter()
+        x = sub.X
+        for li in range(nl):
+            w = sub.layers[li]
+            x, _ = orc.layer_fwd(x, w.W1, w.W2, w.rab_pos, w.rab_time, sub.seq_offsets,
+                                 sub.timestamps, sub.num_candidates, f)
+        dt = time.perf_counter() - t0
+        lf = flops.layer_flops(sub.lengths, sub.num_candidates, cfg.D, cfg.H, cfg.d_qk, cfg.d_v,
+                               backward=False)
+        out[cfg.name] = {"seconds": round(dt, 3), "gflops": round(nl * lf["total"] / dt / 1e9, 3),
+                         "tokens_per_s": round(sub.T * nl / dt, 1), "cores": int(_cores()),
+                         "sample": ("whole batch" if nseq is None else f"first {nseq} sequences "
+                                    f"({sub.T} tokens)") + f", {nl} layer(s), forward"}
+    log(f"cpu oracle per workload: {out}")
+    return out
+
+
+ALL_PARTS = ("train", "recompute", "fwd", "semilocal", "trunc", "cached", "mx", "epilogue",
+             "peaks", "cpu")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the forward-only workloads, the semi-local training step, "
-                         "the attention-truncation forward, the cached ranking and the MXFP8 forward")
+                    help="only the training step (and the CPU baseline)")
+    ap.add_argument("--reps", type=int, default=20,
+                    help="timed runs of each forward-only workload")
+    ap.add_argument("--only", default="",
+                    help="comma list of parts to run (" + ",".join(ALL_PARTS) + "); "
+                         "fwd may name workloads, e.g. fwd3 or fwd2+fwd5")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
@@ -607,37 +785,69 @@ def main():
     from hstu_sequential_transduction_amd import _lib
     timer = Timer(_lib.lib())
 
-    cfg, inp, ms, kern, lf = bench_train(args, timer)
-    tflops = lf["total"] / (ms * 1e-3) / 1e12
-    log(f"train step: {ms:.3f} ms, {tflops:.1f} TFLOP/s")
-    roof, table = roofline(cfg, inp, kern, args.steps, os.path.join(ROOT, "profiles"))
-    extra = None if args.no_extra else bench_fwd_configs(timer)
-    semi = None if args.no_extra else bench_semilocal(args, timer, ms)
-    trunc = None if args.no_extra else bench_truncation(timer)
-    cached = None if args.no_extra else bench_cached(timer)
-    mx = None if args.no_extra else bench_mx(timer)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(cfg, inp)
-    line = {
-        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded; inputs resident in HBM)",
-        "config": {"workload": "1 HSTU layer fwd+bwd (training), bf16: batch 8, lengths U[4096,8192],"
-                               " d_model 512, 4 heads x 128, causal",
-                   "global_batch": cfg.B, "tokens": inp.T, "seq_len": "U[4096,8192]",
-                   "parallelism": "single GPU"},
-        "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
-        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
-        "flops_per_step": {k: v for k, v in lf.items()},
-        "kernels": table,
-        "roofline": roof,
-        "cpu_baseline": cpu,
-        "forward_workloads": extra,
-        "semilocal": semi,
-        "truncation": trunc,
-        "cached_ranking": cached,
-        "mxfp8": mx,
-    }
+    parts = set(ALL_PARTS)
+    fwd_cfgs = (2, 3, 5)
+    if args.only:
+        parts, picked = set(), []
+        for tok in args.only.replace("+", ",").split(","):
+            tok = tok.strip()
+            if tok.startswith("fwd") and tok != "fwd":
+                picked.append(int(tok[3:]))
+                parts.add("fwd")
+            elif tok:
+                parts.add(tok)
+        if picked:
+            fwd_cfgs = tuple(picked)
+    if args.no_extra:
+        parts &= {"train", "cpu"}
+    if args.no_cpu_baseline:
+        parts.discard("cpu")
+
+    line = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded; inputs resident in HBM)"}
+    ms = None
+    if "train" in parts:
+        cfg, inp, stats, kern, lf = bench_train(args, timer)
+        ms = stats["ms_mean"]
+        tflops = lf["total"] / (ms * 1e-3) / 1e12
+        log(f"train step: {ms:.3f} ms (median {stats['ms_median']:.3f}, p10 {stats['ms_p10']:.3f},"
+            f" p90 {stats['ms_p90']:.3f}), {tflops:.1f} TFLOP/s")
+        roof, table = roofline(cfg, inp, kern, stats["instrumented_steps"],
+                               os.path.join(ROOT, "profiles"))
+        line.update({
+            "value": round(tflops, 3), "ms_per_step": round(ms, 4),
+            "config": {"workload": "1 HSTU layer fwd+bwd (training), bf16: batch 8, lengths "
+                                   "U[4096,8192], d_model 512, 4 heads x 128, causal",
+                       "global_batch": cfg.B, "tokens": inp.T, "seq_len": "U[4096,8192]",
+                       "parallelism": "single GPU"},
+            "step_ms": stats,
+            "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
+            "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "flops_per_step": {k: v for k, v in lf.items()},
+            "kernels": table, "roofline": roof})
+    if "recompute" in parts:
+        line["train_dq_recomputed"] = bench_recompute(args, timer, ms or float("nan"))
+    if "fwd" in parts:
+        line["forward_workloads"] = bench_fwd_configs(timer, fwd_cfgs, reps=args.reps)
+    if "semilocal" in parts:
+        line["semilocal"] = bench_semilocal(args, timer, ms or float("nan"))
+    if "trunc" in parts:
+        line["truncation"] = bench_truncation(timer)
+    if "cached" in parts:
+        line["cached_ranking"] = bench_cached(timer)
+    if "mx" in parts:
+        line["mxfp8"] = bench_mx(timer)
+    if "epilogue" in parts:
+        line["ln_gate_epilogue"] = bench_epilogue(timer)
+    if "peaks" in parts:
+        line["measured_peaks"] = bench_peaks()
+    if "cpu" in parts:
+        import synth
+        cfg4 = synth.get_config(4)
+        line["cpu_baseline"] = cpu_baseline(cfg4, synth.make_inputs(cfg4))
+        line["cpu_baseline"]["per_workload"] = cpu_baseline_configs()
     print(json.dumps(line), flush=True)
 
 

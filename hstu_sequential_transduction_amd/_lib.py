@@ -19,7 +19,7 @@ HSTU_F32, HSTU_BF16 = 0, 1
 EXPORTED = [
     "hstu_status_string", "hstu_version", "hstu_last_hip_error",
     "hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size",
-    "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_fwd_noalloc",
+    "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_fwd_noalloc", "hstu_diag_mfma_loop",
     "hstu_layer_fwd_workspace_size", "hstu_layer_bwd_workspace_size",
     "hstu_layer_fwd", "hstu_layer_bwd",
     "hstu_bias_buckets", "hstu_schedule_capacity", "hstu_schedule",
@@ -118,6 +118,8 @@ def lib() -> C.CDLL:
     L.hstu_attn_fwd.restype = C.c_int
     L.hstu_attn_fwd.argtypes = [P(AttnDesc), vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp, i64,
                                 vp, sz, vp]
+    L.hstu_diag_mfma_loop.restype = C.c_int
+    L.hstu_diag_mfma_loop.argtypes = [i32, i32, vp, vp]
     L.hstu_attn_fwd_noalloc.restype = C.c_int
     L.hstu_attn_fwd_noalloc.argtypes = [P(AttnDesc), vp, vp, i64, vp, i64, vp, vp, vp, vp, vp,
                                         vp, i64, vp]

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libhstu.so")
 ARCH = os.environ.get("HSTU_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.cpp", "timer.cpp", "sched.hip", "attn_fwd.hip", "attn_bwd.hip", "ln_gate.hip", "gemm.hip",
-           "truncate.hip", "attn_cached.hip", "mx.hip"]
+           "truncate.hip", "attn_cached.hip", "mx.hip", "diag.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

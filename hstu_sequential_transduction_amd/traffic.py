@@ -6,7 +6,7 @@ Two sub-commands, each meant to run under `rocprofv3 --pmc <COUNTER>`:
       device-to-device copy of N MiB (torch's copy of two contiguous buffers,
       the runtime's copy kernel), three times: the reference of known size.
 
-and one that reads the counter CSVs afterwards (no GPU needed):
+and two that read counter CSVs afterwards (no GPU needed):
 
   python -m hstu_sequential_transduction_amd.traffic reduce \
       --fetch-run DIR --write-run DIR --copy-fetch DIR --copy-write DIR \
@@ -16,6 +16,13 @@ FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Each is scaled by the
 ratio of the bytes the copy moves (read and written, N MiB each) to what the
 same counter reports for it, and the per-launch traffic of the kernel is the
 mean over its dispatches of scaled FETCH + scaled WRITE.
+
+  python -m hstu_sequential_transduction_amd.traffic counters \
+      --run DIR [--run DIR ...] --kernel k_attn_fwd_bf16 [--out FILE.json]
+
+prints, for every kernel whose name contains the fragment, the number of
+dispatches and the mean per dispatch of every counter found in the runs
+(one run per rocprofv3 --pmc pass).
 """
 from __future__ import annotations
 
@@ -75,6 +82,29 @@ def per_dispatch(run_dir: str, counter: str, symbol: str):
         key = (r["Dispatch_Id"], r["Kernel_Name"])
         acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
     return list(acc.values())
+
+
+def cmd_counters(args) -> int:
+    """Mean per dispatch of every counter, per kernel name matching args.kernel."""
+    per = {}   # kernel -> counter -> {dispatch: value}
+    for run in args.run:
+        for r in _rows(run):
+            if args.kernel not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], {})
+            key = (run, r["Dispatch_Id"])
+            d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for k, cs in sorted(per.items()):
+        n = max(len(v) for v in cs.values())
+        out[k] = {"dispatches": n,
+                  "mean_per_dispatch": {c: sum(v.values()) / len(v) for c, v in sorted(cs.items())}}
+    text = json.dumps(out, indent=1)
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text + "\n")
+    print(text)
+    return 0 if out else 1
 
 
 def cmd_copy(args) -> int:
@@ -143,8 +173,14 @@ def main(argv=None) -> int:
     r.add_argument("--mib", type=int, default=512)
     r.add_argument("--out", default=os.path.join(os.path.dirname(HERE), "profiles"))
     r.add_argument("--command", default="")
+    k = sub.add_parser("counters")
+    k.add_argument("--run", action="append", required=True)
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--out", default="")
     args = ap.parse_args(argv)
-    return cmd_copy(args) if args.cmd == "copy" else cmd_reduce(args)
+    if args.cmd == "copy":
+        return cmd_copy(args)
+    return cmd_counters(args) if args.cmd == "counters" else cmd_reduce(args)
 
 
 if __name__ == "__main__":

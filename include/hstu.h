@@ -108,15 +108,22 @@ typedef struct {
    * of recomputing S and dA.  If the batch's blocks do not fit (a sequence
    * longer than max_len), the backward recomputes; results agree either way. */
   int32_t max_len;
-  /* Forward only (hstu_attn_fwd, hstu_layer_fwd, hstu_layer_fwd_mx): 1
-   * asserts that the workspace of this call already holds the plan (time
-   * pre-pass and work list) that an earlier forward call with the same
-   * descriptor apart from this field, the same workspace layout and the same
-   * seq_offsets, timestamps and num_candidates wrote, e.g. the previous
-   * layer of a stack run with one workspace; the call then skips the plan.
-   * The library cannot check the assertion: a wrong one gives wrong
-   * results.  0 (default): plan.  Other values: HSTU_ERR_INVALID_ARG.
-   * Ignored by backward and cached-history calls, which always plan. */
+  /* Forward only (hstu_attn_fwd, hstu_attn_fwd_noalloc, hstu_layer_fwd,
+   * hstu_layer_fwd_mx): 1 asks to skip the plan (time pre-pass and work
+   * list) because the workspace already holds the plan an earlier forward
+   * call on the same batch wrote, e.g. the previous layer of a stack run
+   * with one workspace.  The plan depends on B, T, dtype, d_qk, d_v and the
+   * contents of seq_offsets and timestamps.  The library records, per device,
+   * every plan a forward call writes (its bytes in the workspace, those
+   * sizes and the offsets and timestamps pointers) and forgets the plans in
+   * any workspace bytes a later call may write; a reuse_plan call whose
+   * workspace bytes, sizes or pointers match no recorded plan returns
+   * HSTU_ERR_INVALID_ARG before anything is launched.  The caller still
+   * asserts that the contents of seq_offsets and timestamps are unchanged,
+   * that nothing outside the library wrote the plan's bytes, and that the
+   * planning call is ordered before this one (e.g. the same stream).
+   * 0 (default): plan.  Other values: HSTU_ERR_INVALID_ARG.  Ignored by
+   * backward and cached-history calls, which always plan. */
   int32_t reuse_plan;
 } hstu_attn_desc;
 
@@ -482,6 +489,16 @@ size_t hstu_schedule_workspace_size(int32_t B, int64_t T, int32_t block_rows);
  */
 hstu_status hstu_validate_inputs(int32_t B, int64_t T, const int32_t* seq_offsets,
                                  const int32_t* num_candidates, int32_t* flag_ws, void* stream);
+
+/*
+ * MFMA-rate microbenchmark (a measured denominator for utilisation figures,
+ * beside the nominal peak): `workgroups` workgroups of four waves each run
+ * `iters` x 4 independent bf16 32x32x16 MFMAs (32768 flops each), so one
+ * launch performs workgroups * 4 * iters * 4 * 32768 flops; out (device,
+ * 4 * workgroups floats) receives a checksum per wave.  Time it with events
+ * on `stream`.  HSTU_ERR_INVALID_ARG for iters or workgroups < 1 or out NULL.
+ */
+hstu_status hstu_diag_mfma_loop(int32_t iters, int32_t workgroups, float* out, void* stream);
 
 /* ---- diagnostic kernel timer ------------------------------------------- */
 
