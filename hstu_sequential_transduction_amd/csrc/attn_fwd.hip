@@ -294,8 +294,6 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
                 pk[qg][aa >> 1][(aa & 1) * 4 + r] = two[0];
                 pk[qg][aa >> 1][(aa & 1) * 4 + r + 1] = two[1];
               }
-              // keep the scheduler from hoisting every gather of the half at once
-              __builtin_amdgcn_sched_barrier(0);
             }
         };
         if (mode == 0) {
