@@ -334,15 +334,17 @@ hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k,
 }
 
 // Ranking against a cached history: key splits per (user, candidate block)
-// chosen from the average history length so that about two workgroups per
-// compute unit run (512), with at least four key tiles per split.
+// chosen from the average history length so that the compute units are
+// filled (256 times the workgroups one unit holds), with at least four key
+// tiles per split.
 int cached_splits(const hstu_attn_desc* d, int64_t T_hist) {
   const int bm = attn_cached_block_rows(d->dtype, d->d_qk, d->d_v);
   const int64_t B = std::max<int64_t>(d->B, 1);
   const int64_t items = std::max<int64_t>((d->T + bm - 1) / bm, B);  // work items (estimate)
   const int64_t tile = d->dtype == HSTU_BF16 ? 64 : 32;
   const int64_t tiles_per_user = (T_hist / B + tile - 1) / tile;
-  int64_t S = (512 + items * d->H - 1) / (items * d->H);
+  const int64_t slots = 256 * (int64_t)attn_cached_occupancy(d->dtype, d->d_qk, d->d_v);
+  int64_t S = (slots + items * d->H - 1) / (items * d->H);
   S = std::min<int64_t>(S, std::max<int64_t>(tiles_per_user / 4, 1));
   return (int)std::max<int64_t>(1, std::min<int64_t>(S, 16));
 }

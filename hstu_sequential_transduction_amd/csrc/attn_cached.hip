@@ -35,10 +35,14 @@ namespace {
 
 constexpr int CBN = 64;  // history keys per tile
 
+// One 32-row candidate group per wave; as in the forward kernel, waves per
+// SIMD decide the speed (latency inside each wave), so d <= 64 runs three
+// workgroups per compute unit.
 template <int DQK, int DV>
 struct CShape {
-  static constexpr int QG = (DQK <= 64 && DV <= 64) ? 2 : 1;
+  static constexpr int QG = 1;
   static constexpr int BM = 4 * 32 * QG;
+  static constexpr int OCC = (DQK <= 64 && DV <= 64) ? 3 : 2;  // workgroups per CU
 };
 
 template <int DQK, int DV>
@@ -62,7 +66,7 @@ using bconst = std::integral_constant<bool, V>;
 // bf16 kernel
 // ---------------------------------------------------------------------------
 template <int DQK, int DV, bool WIN>
-__global__ __launch_bounds__(256, 2) void k_attn_cached_bf16(CachedArgs a) {
+__global__ __launch_bounds__(256, (CShape<DQK, DV>::OCC)) void k_attn_cached_bf16(CachedArgs a) {
   constexpr int QG = CShape<DQK, DV>::QG;
   constexpr int BM = CShape<DQK, DV>::BM;
   __shared__ __attribute__((aligned(1024))) CBuf<DQK, DV> cb0;
@@ -228,7 +232,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_cached_bf16(CachedArgs a) {
                 if constexpr (decltype(masked)::value) p = (kc >= wlo || kc < wgl) ? p : 0.0f;
                 pk[qg][aa >> 1][(aa & 1) * 4 + r] = (bf16)p;
               }
-              __builtin_amdgcn_sched_barrier(0);
             }
         };
         if (mode == 0) {
@@ -518,6 +521,11 @@ hipError_t launch_cached_dv(const CachedArgs& a, int dtype, int d_v, int64_t mi,
 int attn_cached_block_rows(int dtype, int d_qk, int d_v) {
   if (dtype != HSTU_BF16) return ATTN_FWD_BM_F32;
   return (d_qk <= 64 && d_v <= 64) ? CShape<64, 64>::BM : CShape<128, 128>::BM;
+}
+
+int attn_cached_occupancy(int dtype, int d_qk, int d_v) {
+  if (dtype != HSTU_BF16) return 2;
+  return (d_qk <= 64 && d_v <= 64) ? CShape<64, 64>::OCC : CShape<128, 128>::OCC;
 }
 
 hipError_t launch_attn_cached(const CachedArgs& a, int dtype, int d_qk, int d_v,

@@ -279,6 +279,8 @@ struct CachedArgs {
   int H = 0, nP = 0, nT = 0, norm_len = 1, win_local = 0, win_global = 0;
 };
 int attn_cached_block_rows(int dtype, int d_qk, int d_v);
+// workgroups of the cached-attention kernel that share one compute unit
+int attn_cached_occupancy(int dtype, int d_qk, int d_v);
 hipError_t launch_attn_cached(const CachedArgs& a, int dtype, int d_qk, int d_v,
                               int64_t max_items, hipStream_t st);
 
