@@ -40,7 +40,8 @@ class AttnDesc(C.Structure):
                 ("n_time_buckets", C.c_int32), ("norm_mode", C.c_int32),
                 ("norm_len", C.c_int32), ("dtype", C.c_int32),
                 ("rab_head_stride", C.c_int64), ("win_local", C.c_int32),
-                ("win_global", C.c_int32), ("max_len", C.c_int32), ("reuse_plan", C.c_int32)]
+                ("win_global", C.c_int32), ("max_len", C.c_int32), ("reuse_plan", C.c_int32),
+                ("key_splits", C.c_int32)]
 
 
 class LayerDesc(C.Structure):

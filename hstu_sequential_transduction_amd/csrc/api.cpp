@@ -106,6 +106,7 @@ hstu_status check_attn_desc(const hstu_attn_desc* d) {
   if (d->norm_mode == 0 && d->norm_len <= 0) return HSTU_ERR_INVALID_ARG;
   if (d->win_local < 0 || d->win_global < 0 || d->max_len < 0) return HSTU_ERR_INVALID_ARG;
   if (d->reuse_plan != 0 && d->reuse_plan != 1) return HSTU_ERR_INVALID_ARG;
+  if (d->key_splits < 0 || d->key_splits > 8) return HSTU_ERR_INVALID_ARG;
   if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
   if (d->rab_head_stride < 0) return HSTU_ERR_INVALID_ARG;
   if (d->rab_head_stride != 0 &&
@@ -122,14 +123,35 @@ bool stride_ok(int dtype, const void* p, int64_t ld, int64_t min_ld) {
 }
 
 
+// Parts the forward splits long query blocks' keys into (1: none): bf16
+// without windows, when the descriptor asks for it.  The default is not to
+// split: on the 1-layer (32 sequences of U[64,1024]) and 8-layer Zipf
+// workloads, whose work lists hold fewer items than the GPU holds
+// workgroups or about twice as many, every split from 2 to 8 parts was
+// slower (extra workgroups' start-up, the partial sums' round trip and the
+// combine launch cost more than the shorter longest run saves).
+int fwd_splits(const hstu_attn_desc* d) {
+  if (d->dtype != HSTU_BF16 || d->win_local > 0) return 1;
+  return d->key_splits >= 2 ? d->key_splits : 1;
+}
+
 struct FwdWs {
   TimeMeta tm;
   Sched sc;
+  int splits = 1;
+  float* part = nullptr;       // [cap * H][splits][block rows][d_v]
+  int32_t* part_cnt = nullptr; // [cap * H] parts per work item (written by the kernel)
 };
 FwdWs carve_fwd(Carver& c, const hstu_attn_desc* d) {
   FwdWs w;
   w.tm = carve_time(c, d->T, d->B);
-  w.sc = carve_sched(c, d->T, d->B, attn_fwd_block_rows(d->dtype, d->d_qk, d->d_v));
+  const int bm = attn_fwd_block_rows(d->dtype, d->d_qk, d->d_v);
+  w.sc = carve_sched(c, d->T, d->B, bm);
+  w.splits = fwd_splits(d);
+  if (w.splits > 1) {
+    w.part = c.take<float>(w.sc.cap * d->H * w.splits * bm * d->d_v);
+    w.part_cnt = c.take<int32_t>(w.sc.cap * d->H);
+  }
   return w;
 }
 
@@ -317,6 +339,9 @@ hstu_status attn_fwd_run(const hstu_attn_desc* d, const void* q, const void* k, 
   a.out_f32 = out_f32;
   a.items = w.sc.items;
   a.counters = w.sc.counters;
+  a.splits = w.splits;
+  a.part = w.part;
+  a.part_cnt = w.part_cnt;
   { HSTU_TIMED(TT_ATTN_FWD, st); HSTU_TRY(launch_attn_fwd(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st)); }
   return HSTU_OK;
 }

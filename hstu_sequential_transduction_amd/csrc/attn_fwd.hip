@@ -77,7 +77,12 @@ struct FwdTables {
 template <int V>
 using mconst = std::integral_constant<int, V>;
 
-template <int DQK, int DV, bool WIN>
+// SPLIT: workgroup w takes part w / I of work item w % I (S = a.splits parts
+// of I = gridDim.x / S items): the
+// item's visited key tiles are cut into np <= S contiguous runs of at least
+// four tiles.  With np = 1 the one part writes O; otherwise each part writes
+// its scaled partial sum of O to a.part and k_attn_fwd_combine adds them.
+template <int DQK, int DV, bool WIN, bool SPLIT>
 __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16(AttnArgs a) {
   constexpr int QG = FwdShape<DQK, DV>::QG;
   constexpr int BM = FwdShape<DQK, DV>::BM;
@@ -85,10 +90,17 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
   __shared__ __attribute__((aligned(1024))) FwdBuf<DQK, DV> fwb1;
   __shared__ FwdTables sm;
 
-  const int w = blockIdx.x;
+  // part-major numbering (parts 0 of every item first): consecutive workgroups
+  // go to different XCDs, and with item-major numbering and S a power of two
+  // the parts 0 of all items (all of the unsplit items' work) would share
+  // S-th of the XCDs
+  const int S = SPLIT ? a.splits : 1;
+  const int nwi = SPLIT ? (int)(gridDim.x / (unsigned)S) : 0;
+  const int part = SPLIT ? (int)(blockIdx.x / (unsigned)nwi) : 0;
+  const int wi = SPLIT ? (int)blockIdx.x - part * nwi : (int)blockIdx.x;
   const int n_items = a.counters[0];
-  if (w >= n_items * a.H) return;
-  const int it = w / a.H, h = w - it * a.H;
+  if (wi >= n_items * a.H) return;
+  const int it = wi / a.H, h = wi - it * a.H;
   const int b = __builtin_amdgcn_readfirstlane(a.items[2 * it]);
   const int m = __builtin_amdgcn_readfirstlane(a.items[2 * it + 1]);
   if (b < 0 || b >= a.B || m < 0) return;  // not an item of this batch
@@ -97,6 +109,22 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
   if (m >= (n + BM - 1) / BM) return;
   const int c = a.num_cand ? __builtin_amdgcn_readfirstlane(a.num_cand[b]) : 0;
   const int nh = n - c;
+  // SPLIT: this part's run of visited key tiles, [kt_a, kt_b), decided before
+  // anything else is loaded so that parts with no run leave at once.  Visited
+  // tiles: [0, ceil(rb1 / BN)) minus the tiles of candidate keys that end
+  // before the block, [ceil(nh / BN), rb0 / BN) (the order next_tile walks).
+  int np = 1, kt_a = 0, kt_b = 0;
+  if constexpr (SPLIT) {
+    const int b0 = m * BM, kt_all = (min(b0 + BM, n) + FWD_BN - 1) / FWD_BN;
+    const int s0 = (nh + FWD_BN - 1) / FWD_BN, nskip = max(0, b0 / FWD_BN - s0);
+    const int nv = kt_all - nskip;
+    np = min(S, max(1, nv / 4));
+    if (part >= np) return;
+    const int lo = nv * part / np, hi = nv * (part + 1) / np;
+    auto tile_of = [&](int v) HSTU_INLINE_LAMBDA { return v < s0 ? v : v + nskip; };
+    kt_a = tile_of(lo);
+    kt_b = hi < nv ? tile_of(hi) : kt_all;
+  }
   const int flags = __builtin_amdgcn_readfirstlane(a.seq_flags[b]);
   const bool wide = flags & 1;
   const bool sorted = flags & 2;
@@ -353,28 +381,54 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
   // before reads of the other)
   int kt = skip_window(0);
   if (kt < ktiles && kt * FWD_BN >= nh && kt * FWD_BN + FWD_BN <= rb0) kt = rb0 / FWD_BN;
-  if (kt < ktiles) issue(fwb0, kt);
+  // kend: the first visited tile past this workgroup's run (any value >= ktiles
+  // when the run goes to the end)
+  int kend = ktiles;
+  if constexpr (SPLIT) {
+    kt = kt_a;
+    kend = kt_b;
+  }
+  if (kt < kend) issue(fwb0, kt);
   dma_wait();
   __syncthreads();
-  while (kt < ktiles) {
+  while (kt < kend) {
     int nk = next_tile(kt);
-    if (nk < ktiles) issue(fwb1, nk);
+    if (nk < kend) issue(fwb1, nk);
     body(fwb0, kt);
     dma_wait();
     __syncthreads();
     kt = nk;
-    if (kt >= ktiles) break;
+    if (kt >= kend) break;
     nk = next_tile(kt);
-    if (nk < ktiles) issue(fwb0, nk);
+    if (nk < kend) issue(fwb0, nk);
     body(fwb1, kt);
     dma_wait();
     __syncthreads();
     kt = nk;
   }
 
+  const float scale = -HSTU_LN2 / (float)(a.norm_mode == 0 ? a.norm_len : n);
+  if constexpr (SPLIT) {
+    static_assert(QG == 1, "split partials assume one query group per wave");
+    if (part == 0 && tid == 0) a.part_cnt[wi] = np;  // read by k_attn_fwd_combine
+    if (np > 1) {
+      // scaled partial sums of rows rb0 .. rb1-1, [BM][DV] per part; the
+      // combine kernel that runs next adds them (no fence or counter here:
+      // on this GPU a device-scope fence writes back the whole L2)
+      float* pw = a.part + ((int64_t)wi * S + part) * (BM * DV);
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = r0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (i < n) pw[(i - rb0) * DV + d * 32 + ql] = oacc[0][d][r] * scale;
+        }
+      return;
+    }
+  }
+
   // ---- write O * (-ln2 / N) ----
   if (r0 >= rw1) return;
-  const float scale = -HSTU_LN2 / (float)(a.norm_mode == 0 ? a.norm_len : n);
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
@@ -388,6 +442,75 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
           else reinterpret_cast<bf16*>(a.out)[off] = (bf16)(oacc[qg][d][r] * scale);
         }
       }
+}
+
+// Sum of the np partial sums of each split work item (np = part_cnt[item],
+// written by the item's part 0; items with np = 1 wrote O themselves).  One
+// wave per 16 rows of a work item, every load of a part in flight at once.
+constexpr int CMB_ROWS = 16;
+
+template <int BM, int DV>
+__global__ __launch_bounds__(64) void k_attn_fwd_combine(AttnArgs a) {
+  constexpr int CPI = BM / CMB_ROWS;        // waves per work item
+  constexpr int PER = CMB_ROWS * DV / 4 / 64;  // float4s per lane and part
+  const int wi = blockIdx.x / CPI;
+  const int rg = blockIdx.x - wi * CPI;
+  if (wi >= a.counters[0] * a.H) return;
+  const int np = a.part_cnt[wi];
+  if (np <= 1) return;
+  const int it = wi / a.H, h = wi - it * a.H;
+  const int b = a.items[2 * it], m = a.items[2 * it + 1];
+  if (b < 0 || b >= a.B || m < 0) return;
+  const int o0 = a.seq_offsets[b];
+  const int n = a.seq_offsets[b + 1] - o0;
+  const int lr0 = rg * CMB_ROWS;  // first row of this wave within the block
+  const int rows = min(CMB_ROWS, n - m * BM - lr0);
+  if (rows <= 0) return;
+  constexpr int P4 = BM * DV / 4;  // float4s per part
+  const float4* pr = reinterpret_cast<const float4*>(a.part + (int64_t)wi * a.splits * (BM * DV)) +
+                     lr0 * (DV / 4);
+  const int ne = rows * (DV / 4);
+  float4 acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = threadIdx.x + 64 * k;
+    acc[k] = e < ne ? pr[e] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  for (int p = 1; p < np; ++p) {
+    float4 x[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e = threadIdx.x + 64 * k;
+      x[k] = e < ne ? pr[p * P4 + e] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      acc[k].x += x[k].x;
+      acc[k].y += x[k].y;
+      acc[k].z += x[k].z;
+      acc[k].w += x[k].w;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e = threadIdx.x + 64 * k;
+    if (e >= ne) continue;
+    const int i = m * BM + lr0 + e / (DV / 4), col = 4 * (e % (DV / 4));
+    const int64_t off = (int64_t)(o0 + i) * a.ld_out + h * DV + col;
+    if (a.out_f32) {  // (ld_out need not keep rows 16-byte aligned)
+      float* o = reinterpret_cast<float*>(a.out) + off;
+      o[0] = acc[k].x;
+      o[1] = acc[k].y;
+      o[2] = acc[k].z;
+      o[3] = acc[k].w;
+    } else {
+      bf16* o = reinterpret_cast<bf16*>(a.out) + off;
+      o[0] = (bf16)acc[k].x;
+      o[1] = (bf16)acc[k].y;
+      o[2] = (bf16)acc[k].z;
+      o[3] = (bf16)acc[k].w;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -496,11 +619,19 @@ template <int DQK, int DV>
 hipError_t launch_fwd_t(const AttnArgs& a, int dtype, int64_t max_items, hipStream_t st) {
   const int64_t grid = max_items * a.H;
   if (grid <= 0) return hipSuccess;
-  if (dtype == HSTU_BF16)
-    if (a.win_local > 0) k_attn_fwd_bf16<DQK, DV, true><<<(unsigned)grid, 256, 0, st>>>(a);
-    else k_attn_fwd_bf16<DQK, DV, false><<<(unsigned)grid, 256, 0, st>>>(a);
-  else
+  if (dtype == HSTU_BF16) {
+    if (a.splits > 1 && (a.win_local > 0 || !a.part || !a.part_cnt)) return hipErrorInvalidValue;
+    if (a.win_local > 0)
+      k_attn_fwd_bf16<DQK, DV, true, false><<<(unsigned)grid, 256, 0, st>>>(a);
+    else if (a.splits > 1) {
+      k_attn_fwd_bf16<DQK, DV, false, true><<<(unsigned)(grid * a.splits), 256, 0, st>>>(a);
+      constexpr int BM = FwdShape<DQK, DV>::BM;
+      k_attn_fwd_combine<BM, DV><<<(unsigned)(grid * (BM / CMB_ROWS)), 64, 0, st>>>(a);
+    } else
+      k_attn_fwd_bf16<DQK, DV, false, false><<<(unsigned)grid, 256, 0, st>>>(a);
+  } else {
     k_attn_fwd_f32<DQK, DV><<<(unsigned)grid, 256, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -123,6 +123,13 @@ struct AttnArgs {
   int H = 0, nP = 0, nT = 0, norm_mode = 0, norm_len = 1;
   // semi-local windows (win_local 0: full causal)
   int win_local = 0, win_global = 0;
+  // forward key splits: workgroup w = (item, head) * splits + part; the parts
+  // of one block write fp32 partial sums to part[(item, head)][part][BM][d_v],
+  // part 0 writes their number to part_cnt[(item, head)], and a combine
+  // kernel adds them into out
+  int splits = 1;
+  float* part = nullptr;
+  int32_t* part_cnt = nullptr;
   // backward with dS kept: 128 x 128 bf16 blocks (key-major) of the causal
   // part, per sequence and head; ds_base[b] = first block of sequence b;
   // *ds_flag != 0: the blocks did not fit, dQ is recomputed instead

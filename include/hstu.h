@@ -125,6 +125,16 @@ typedef struct {
    * 0 (default): plan.  Other values: HSTU_ERR_INVALID_ARG.  Ignored by
    * backward and cached-history calls, which always plan. */
   int32_t reuse_plan;
+  /* Forward (bf16, no semi-local windows): split the keys of long query
+   * blocks over several workgroups whose partial sums add (no softmax, so
+   * the parts add exactly up to rounding order), meant for batches too small
+   * to fill the GPU.  0: library default (currently no split: it measured
+   * slower on every workload tried); 1: never; 2..8: split every query
+   * block into up to this many runs of at least 4 key tiles of 64; the
+   * parts write fp32 partial sums to the workspace and a second kernel adds
+   * them.  Other values: HSTU_ERR_INVALID_ARG.  The workspace size depends
+   * on it. */
+  int32_t key_splits;
 } hstu_attn_desc;
 
 /* One layer: attention options plus model width and layer flags. */
@@ -207,7 +217,8 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc,
  * itself never allocates or frees.  Problems whose forward workspace
  * (hstu_attn_fwd_workspace_size) exceeds that size are rejected with
  * HSTU_ERR_WORKSPACE before anything is launched (8 MiB holds the plan of
- * about 1.9 million rows).  Every call on one GPU shares that GPU's array:
+ * about 1.9 million rows).  A key split (key_splits 2..8) counts its
+ * partial sums against the same limit.  Every call on one GPU shares that GPU's array:
  * calls that overlap in time on one GPU (other streams, other threads)
  * race and must be ordered by the caller.  reuse_plan = 1 refers to the
  * plan the previous no-allocation call on the device left there.  Other

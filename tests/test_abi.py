@@ -45,15 +45,25 @@ def test_version_and_status_strings(L):
 def _desc(**kw):
     base = dict(B=4, T=300, H=2, d_qk=32, d_v=32, n_pos_buckets=128, n_time_buckets=128,
                 norm_mode=0, norm_len=128, dtype=1, rab_head_stride=128, win_local=0,
-                win_global=0, max_len=0, reuse_plan=0)
+                win_global=0, max_len=0, reuse_plan=0, key_splits=0)
     base.update(kw)
     return _lib.AttnDesc(*[base[f] for f, _ in _lib.AttnDesc._fields_])
 
 
 def test_workspace_sizes_grow_with_T(L):
-    a = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000)))
-    b = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=100000)))
+    a = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=1)))
+    b = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=100000, key_splits=1)))
     assert 0 < a < b
+    # split keys keep partial sums of [block rows x d_v] per part and work item;
+    # the default is not to split
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000))) == a
+    s4 = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=4)))
+    s2 = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=2)))
+    assert a < s2 < s4
+    # fp32 and windowed attention never split
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=4, dtype=0))) == \
+        L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=1, dtype=0)))
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=4, win_local=64))) == a
     assert L.hstu_attn_bwd_workspace_size(C.byref(_desc(T=1000))) > 0
     ld = _lib.LayerDesc(_desc(T=1000), 64, 1, 1, 1e-6)
     assert L.hstu_layer_fwd_workspace_size(C.byref(ld), 0) > \
@@ -66,6 +76,7 @@ def test_workspace_sizes_grow_with_T(L):
     (dict(n_pos_buckets=0), -2), (dict(n_time_buckets=2000), -2), (dict(norm_mode=2), -1),
     (dict(norm_len=0), -1), (dict(dtype=7), -2), (dict(T=1 << 31), -1), (dict(B=-1), -1),
     (dict(rab_head_stride=64), -1), (dict(max_len=-1), -1), (dict(reuse_plan=2), -1),
+    (dict(key_splits=-1), -1), (dict(key_splits=9), -1),
 ])
 def test_host_side_argument_errors(L, bad, code):
     d = _desc(**bad)
@@ -205,16 +216,16 @@ def test_cached_ranking_argument_errors(L):
 def test_reuse_plan_without_a_recorded_plan_is_rejected(L):
     """reuse_plan = 1 is checked against the plans the library recorded; a
     workspace no forward call planned into is refused before any launch."""
-    buf = C.create_string_buffer(1 << 20)
+    buf = C.create_string_buffer(1 << 22)
     ws = C.c_void_p((C.addressof(buf) + 255) & ~255)
     p = C.c_void_p(1 << 20)
     d = _desc(reuse_plan=1)
-    st = L.hstu_attn_fwd(C.byref(d), p, p, 64, p, 64, p, p, p, p, None, p, 64, ws, 1 << 19, None)
+    st = L.hstu_attn_fwd(C.byref(d), p, p, 64, p, 64, p, p, p, p, None, p, 64, ws, 1 << 21, None)
     assert st == -1
     ld = _lib.LayerDesc(_desc(reuse_plan=1, d_qk=32, d_v=32, H=2), 64, 1, 1, 1e-6)
     w = _lib.LayerWeights(p, p, None, None, None, None, p, p)
     st = L.hstu_layer_fwd(C.byref(ld), p, C.byref(w), p, p, None, C.c_void_p((1 << 20) + 4096),
-                          None, ws, 1 << 19, None)
+                          None, ws, 1 << 21, None)
     assert st == -1
 
 

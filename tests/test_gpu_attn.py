@@ -124,6 +124,52 @@ def test_attn_fwd_unsorted_and_wide_timestamps(B):
     check_close(got, want, "bf16", "O unsorted/wide")
 
 
+SPLIT_CASES = {
+    3: [2048, 33, 1500, 520, 1],
+    5: [1900, 700, 64, 0],
+    4: [1300, 129],
+}
+
+
+@pytest.mark.parametrize("ci", [3, 5, 4])
+@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+def test_attn_fwd_key_splits(B, ci, splits):
+    """Long query blocks' keys cut into `splits` runs (1: never): the same O."""
+    hist = SPLIT_CASES[ci]
+    cfg = synth.get_config(ci).shrunk(B=len(hist), lengths=("list", hist))
+    say(f"attn fwd key_splits={splits} cfg{ci} lengths={hist} c={cfg.num_candidates}")
+    a = synth.make_attn_inputs(cfg, seed=300 + ci)
+    ac = _cfgobj(B, cfg)
+    ac.key_splits = splits
+    got = _fwd(B, a, cfg, ac)
+    want = orc.attn_fwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
+                        a.num_candidates, 0, cfg.norm_len)
+    check_close(got, want, cfg.dtype, f"O cfg{ci} splits={splits}")
+
+
+def test_attn_fwd_key_splits_reused_plan(B):
+    """The split counters return to zero after each call: a stack of calls on
+    one plan gives the first call's output every time."""
+    import torch
+    hist = SPLIT_CASES[3]
+    cfg = synth.get_config(3).shrunk(B=len(hist), lengths=("list", hist))
+    a = synth.make_attn_inputs(cfg, seed=310)
+    u = _upload(a, cfg)
+    ac = _cfgobj(B, cfg)
+    ac.key_splits = 4
+    ws = B.LayerWorkspace()
+    first = B.hstu_attn_fwd(u["q"], u["k"], u["v"], u["offs"], u["ts"], u["rp"], u["rt"], ac,
+                            workspace=ws)
+    ac.reuse_plan = 1
+    for _ in range(3):
+        again = B.hstu_attn_fwd(u["q"], u["k"], u["v"], u["offs"], u["ts"], u["rp"], u["rt"],
+                                ac, workspace=ws)
+        assert torch.equal(again, first)
+    want = orc.attn_fwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
+                        None, 0, cfg.norm_len)
+    check_close(host(first).reshape(a.v.shape), want, "bf16", "O split reused plan")
+
+
 @pytest.mark.parametrize("ci", [2, 3, 4, 5])
 def test_attn_fwd_full_size_sampled_rows(B, ci):
     cfg = synth.get_config(ci)

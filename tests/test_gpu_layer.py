@@ -82,6 +82,24 @@ def test_layer_stack_fwd_small(B, ci, variant):
         check_close(g, w, cfg.dtype, f"Y[{li}] cfg{ci} {variant}")
 
 
+@pytest.mark.parametrize("ci,splits", [(3, 3), (5, 2), (4, 4)])
+def test_layer_stack_fwd_key_splits(B, ci, splits):
+    """The layer's attention (fp32 output) with long blocks' keys split."""
+    hist = {3: [2048, 33, 1500], 5: [1900, 64], 4: [1300, 129]}[ci]
+    cfg = synth.get_config(ci).shrunk(B=len(hist), lengths=("list", hist)).unit_scale()
+    say(f"layer fwd cfg{ci} key_splits={splits} lengths={hist}")
+    inp = synth.make_inputs(cfg, seed=520 + ci)
+    d = Dev(inp, cfg)
+    lc = _lcfg(B, cfg)
+    lc.attn.key_splits = splits
+    n_layers = min(cfg.n_layers, 2)
+    got = _stack_gpu(B, d, lc, n_layers)
+    want = orc.stack_fwd(inp.X, inp.layers[:n_layers], inp.seq_offsets, inp.timestamps,
+                         inp.num_candidates, _flags(cfg))
+    for li, (g, w) in enumerate(zip(got, want)):
+        check_close(g, w, cfg.dtype, f"Y[{li}] cfg{ci} key_splits={splits}")
+
+
 def test_layer_fwd_saved_intermediates(B):
     cfg = synth.get_config(4).shrunk(B=3, lengths=("list", [300, 1100, 129])).unit_scale()
     inp = synth.make_inputs(cfg, seed=41)
