@@ -558,11 +558,15 @@ LayerFwdWs carve_layer_cached(Carver& c, const hstu_layer_desc* L, int64_t T_his
   return w;
 }
 
+// Splits of the weight-gradient GEMMs' k (token) range: enough workgroups to
+// fill the GPU twice over, at least 512 tokens each, at most 32; a multiple
+// of 8 from 8 up, so that every XCD takes whole splits (see the GEMM kernel).
 int splitk_for(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   int64_t s = (512 + tiles - 1) / tiles;
   s = std::min<int64_t>(s, std::max<int64_t>(1, K / 512));
-  return (int)std::max<int64_t>(1, std::min<int64_t>(s, 32));
+  s = std::max<int64_t>(1, std::min<int64_t>(s, 32));
+  return (int)(s >= 8 ? s / 8 * 8 : s);
 }
 
 struct LayerBwdWs {

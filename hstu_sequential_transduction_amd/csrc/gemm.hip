@@ -292,6 +292,155 @@ struct G2Shape {
   static constexpr int WPC = (BM * BN >= 256 * 256 ? 1 : 2) * (NST == 1 ? 2 : 1);  // WGs per CU
 };
 
+// GEMM epilogue of one wave's (32 FM) x (32 FN) accumulator block at rows
+// m0 + wm 32 FM.., columns n0 + wn 32 FN..: the accumulator layout gives each
+// lane one column and rows 8*(r/4) + 4*gq + r%4, so writing it straight to
+// memory would take one 2-byte store per element.  Instead the wave stages SR
+// rows of its fp32 results at a time in its own LDS region `stg` (row stride
+// ES floats: rows 4 apart fall on different banks), then reads rows back as
+// four consecutive columns per lane and applies the epilogue in fp32 with 8-
+// or 16-byte vector accesses.  The caller has every wave past its last read
+// of the region's memory.  z: the split of EPI_PARTIAL.
+template <int FM, int FN, int EPI, bool OUTF32, bool MX, int SR>
+HSTU_DEV void g2_epilogue(const GemmArgs& g, f32x16 (&acc)[FM][FN], float* stg, int64_t m0,
+                          int64_t n0, int wm, int wn, int lane, int z) {
+  constexpr int WN = 32 * FN;        // columns of the wave's block
+  constexpr int ES = WN + 8;         // staging row stride (floats)
+  constexpr int LPR = WN / 4;        // lanes per staged row
+  constexpr int RPI = 64 / LPR;      // rows per read instruction
+  constexpr int GPR = SR / 8;  // accumulator register groups (of four) per round
+  const int ql = lane & 31, gq = lane >> 5;
+  const int lr = lane / LPR, lc = lane % LPR;
+  const int64_t ncol = n0 + wn * WN + 4 * lc;  // this lane's four output columns
+  float bias4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (g.bias && (EPI == EPI_SILU || EPI == EPI_RESID)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bias4[e] = ncol + e < g.N ? g.bias[ncol + e] : 0.0f;
+  }
+  const bool vec = ncol + 3 < g.N;
+  // Residual (EPI_RESID): every load of the wave's block is issued here, ahead
+  // of the staging rounds, so one memory latency is paid per workgroup
+  // instead of one per round (the accumulators' operand registers are free)
+  constexpr int NRND = FM * (32 / SR), NRR = SR / RPI;
+  uint2 rres[EPI == EPI_RESID ? NRND : 1][EPI == EPI_RESID ? NRR : 1];
+  if constexpr (EPI == EPI_RESID) {
+    if (g.R && vec) {
+#pragma unroll
+      for (int ih = 0; ih < NRND; ++ih)
+#pragma unroll
+        for (int rr = 0; rr < NRR; ++rr) {
+          const int64_t m = m0 + wm * 32 * FM + (ih / (32 / SR)) * 32 + (ih % (32 / SR)) * SR +
+                            RPI * rr + lr;
+          rres[ih][rr] = m < g.M ? *reinterpret_cast<const uint2*>(
+                                       reinterpret_cast<const bf16*>(g.R) + m * g.ldr + ncol)
+                                 : uint2{0u, 0u};
+        }
+    }
+  }
+#pragma unroll
+  for (int ih = 0; ih < NRND; ++ih) {
+    const int i = ih / (32 / SR), hh = ih % (32 / SR);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < GPR; ++q)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          stg[(8 * q + 4 * gq + rr) * ES + j * 32 + ql] = acc[i][j][4 * (hh * GPR + q) + rr];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int rr = 0; rr < SR / RPI; ++rr) {
+      const int rho = RPI * rr + lr;
+      const int64_t m = m0 + wm * 32 * FM + i * 32 + hh * SR + rho;
+      const f32x4 v4 = *reinterpret_cast<const f32x4*>(&stg[rho * ES + 4 * lc]);
+      if (m >= g.M) continue;
+      float v[4] = {v4[0], v4[1], v4[2], v4[3]};
+      if (EPI == EPI_PARTIAL) {
+        float* dst = g.partial + ((int64_t)z * g.M + m) * g.N + ncol;
+        if (vec) {
+          *reinterpret_cast<f32x4*>(dst) = v4;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ncol + e < g.N) dst[e] = v[e];
+        }
+        continue;
+      }
+      if (EPI == EPI_SILU || EPI == EPI_RESID) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += bias4[e];
+      }
+      if (EPI == EPI_RESID && g.R) {
+        const bf16* rp = reinterpret_cast<const bf16*>(g.R) + m * g.ldr + ncol;
+        if (vec) {
+          const uint2 rv = rres[EPI == EPI_RESID ? ih : 0][EPI == EPI_RESID ? rr : 0];
+          v[0] += __builtin_bit_cast(float, rv.x << 16);
+          v[1] += __builtin_bit_cast(float, rv.x & 0xFFFF0000u);
+          v[2] += __builtin_bit_cast(float, rv.y << 16);
+          v[3] += __builtin_bit_cast(float, rv.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ncol + e < g.N) v[e] += (float)rp[e];
+        }
+      }
+      auto put = [&](void* base, const float (&x)[4], bool f32) HSTU_INLINE_LAMBDA {
+        if (f32) {
+          float* dst = reinterpret_cast<float*>(base) + m * g.ldc + ncol;
+          if (vec) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (ncol + e < g.N) dst[e] = x[e];
+          }
+        } else {
+          bf16* dst = reinterpret_cast<bf16*>(base) + m * g.ldc + ncol;
+          if (vec) {
+            uint2 o;
+            o.x = pack_bf16x2(x[0], x[1]);
+            o.y = pack_bf16x2(x[2], x[3]);
+            *reinterpret_cast<uint2*>(dst) = o;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (ncol + e < g.N) dst[e] = (bf16)x[e];
+          }
+        }
+      };
+      if (EPI == EPI_SILU) {
+        if (g.C2) put(g.C2, v, false);
+        float sv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[e] = silu_f(v[e]);
+        put(g.C, sv, false);
+      } else {
+        put(g.C, v, OUTF32);
+      }
+      if constexpr (MX && EPI == EPI_RESID && !OUTF32) {
+        if (g.c_codes) {
+          // MXFP8 copy of the stored (bf16-rounded) row values: the eight
+          // lanes of a 32-column block share the row, so their amax is a
+          // three-step shuffle (all eight skip rows past M together)
+          float q[4], am = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            q[e] = (float)(bf16)v[e];
+            am = fmaxf(am, fabsf(q[e]));
+          }
+#pragma unroll
+          for (int o = 1; o < 8; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+          const int sh = mx_shared_exp(am);
+          *reinterpret_cast<uint32_t*>(g.c_codes + m * g.N + ncol) =
+              mx_cvt4(q[0], q[1], q[2], q[3], sh);
+          if ((lc & 7) == 0) g.c_scales[m * (g.N / 32) + ncol / 32] = (uint8_t)(sh + 127);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <int BM, int BN, bool AK, bool BK, int EPI, bool OUTF32, int NST, bool MX = false>
 __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gemm2_bf16(
     GemmArgs g, int mt, int nt, int slots) {
@@ -308,7 +457,19 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
   const int lane = tid & 63, ql = lane & 31, gq = lane >> 5;
   const int wm = wave >> 1, wn = wave & 1;
   const int w = blockIdx.x;
-  const int t = (w & 7) * slots + (w >> 3);
+  int t, z = 0;
+  if (EPI == EPI_PARTIAL && g.split_k % 8 == 0) {
+    // one-dimensional grid, split z on XCD z % 8 with every tile of it: the
+    // XCD's workgroups walk the same k-slice of both operands together, so
+    // each operand byte comes from HBM once and is shared through that L2
+    // (tile-major order instead reads A once per column block)
+    const int r = w >> 3, tiles = mt * nt;
+    z = (w & 7) + 8 * (r / tiles);
+    t = r - (r / tiles) * tiles;
+  } else {
+    t = (w & 7) * slots + (w >> 3);
+    z = blockIdx.y;
+  }
   if (t >= mt * nt) return;
   const int mb = t / nt, nb = t - mb * nt;
   const int64_t m0 = (int64_t)mb * BM, n0 = (int64_t)nb * BN;
@@ -318,7 +479,7 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
   int64_t kbeg = 0, kend = g.K;
   if (EPI == EPI_PARTIAL) {
     const int64_t per = ((g.K + g.split_k - 1) / g.split_k + G2_BK - 1) / G2_BK * G2_BK;
-    kbeg = (int64_t)blockIdx.y * per;
+    kbeg = (int64_t)z * per;
     kend = kbeg + per < g.K ? kbeg + per : g.K;
   }
 
@@ -452,148 +613,15 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
   // vector accesses.  Every wave is past the main loop (and its last LDS
   // read) before any staging write.
   __syncthreads();
-  constexpr int WN = 32 * FN;        // columns of the wave's block
-  constexpr int ES = WN + 8;         // staging row stride (floats)
-  constexpr int LPR = WN / 4;        // lanes per staged row
-  constexpr int RPI = 64 / LPR;      // rows per read instruction
   constexpr int SR = NST == 2 ? 32 : 16;  // rows staged per round (region: a tile, or half of one)
-  constexpr int GPR = SR / 8;             // accumulator register groups (of four) per round
-  static_assert(SR * ES * 4 <= (NST == 2 ? SH::TA : SH::TA / 2) &&
-                    SR * ES * 4 <= (NST == 2 ? SH::TB : SH::TB / 2),
+  static_assert(SR * (32 * FN + 8) * 4 <= (NST == 2 ? SH::TA : SH::TA / 2) &&
+                    SR * (32 * FN + 8) * 4 <= (NST == 2 ? SH::TB : SH::TB / 2),
                 "staging region");
   uint8_t* const region = NST == 2 ? (wave == 0 ? a0 : wave == 1 ? b0 : wave == 2 ? a1 : b1)
                                    : (wave < 2 ? a0 + (wave & 1) * (SH::TA / 2)
                                                : b0 + (wave & 1) * (SH::TB / 2));
-  float* const stg = reinterpret_cast<float*>(region);
-  const int lr = lane / LPR, lc = lane % LPR;
-  const int64_t ncol = n0 + wn * WN + 4 * lc;  // this lane's four output columns
-  float bias4[4] = {0.f, 0.f, 0.f, 0.f};
-  if (g.bias && (EPI == EPI_SILU || EPI == EPI_RESID)) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) bias4[e] = ncol + e < g.N ? g.bias[ncol + e] : 0.0f;
-  }
-  const bool vec = ncol + 3 < g.N;
-  // Residual (EPI_RESID): every load of the wave's block is issued here, ahead
-  // of the staging rounds, so one memory latency is paid per workgroup
-  // instead of one per round (the accumulators' operand registers are free)
-  constexpr int NRND = FM * (32 / SR), NRR = SR / RPI;
-  uint2 rres[EPI == EPI_RESID ? NRND : 1][EPI == EPI_RESID ? NRR : 1];
-  if constexpr (EPI == EPI_RESID) {
-    if (g.R && vec) {
-#pragma unroll
-      for (int ih = 0; ih < NRND; ++ih)
-#pragma unroll
-        for (int rr = 0; rr < NRR; ++rr) {
-          const int64_t m = m0 + wm * 32 * FM + (ih / (32 / SR)) * 32 + (ih % (32 / SR)) * SR +
-                            RPI * rr + lr;
-          rres[ih][rr] = m < g.M ? *reinterpret_cast<const uint2*>(
-                                       reinterpret_cast<const bf16*>(g.R) + m * g.ldr + ncol)
-                                 : uint2{0u, 0u};
-        }
-    }
-  }
-#pragma unroll
-  for (int ih = 0; ih < NRND; ++ih) {
-    const int i = ih / (32 / SR), hh = ih % (32 / SR);
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < GPR; ++q)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          stg[(8 * q + 4 * gq + rr) * ES + j * 32 + ql] = acc[i][j][4 * (hh * GPR + q) + rr];
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int rr = 0; rr < SR / RPI; ++rr) {
-      const int rho = RPI * rr + lr;
-      const int64_t m = m0 + wm * 32 * FM + i * 32 + hh * SR + rho;
-      const f32x4 v4 = *reinterpret_cast<const f32x4*>(&stg[rho * ES + 4 * lc]);
-      if (m >= g.M) continue;
-      float v[4] = {v4[0], v4[1], v4[2], v4[3]};
-      if (EPI == EPI_PARTIAL) {
-        float* dst = g.partial + ((int64_t)blockIdx.y * g.M + m) * g.N + ncol;
-        if (vec) {
-          *reinterpret_cast<f32x4*>(dst) = v4;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (ncol + e < g.N) dst[e] = v[e];
-        }
-        continue;
-      }
-      if (EPI == EPI_SILU || EPI == EPI_RESID) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += bias4[e];
-      }
-      if (EPI == EPI_RESID && g.R) {
-        const bf16* rp = reinterpret_cast<const bf16*>(g.R) + m * g.ldr + ncol;
-        if (vec) {
-          const uint2 rv = rres[EPI == EPI_RESID ? ih : 0][EPI == EPI_RESID ? rr : 0];
-          v[0] += __builtin_bit_cast(float, rv.x << 16);
-          v[1] += __builtin_bit_cast(float, rv.x & 0xFFFF0000u);
-          v[2] += __builtin_bit_cast(float, rv.y << 16);
-          v[3] += __builtin_bit_cast(float, rv.y & 0xFFFF0000u);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (ncol + e < g.N) v[e] += (float)rp[e];
-        }
-      }
-      auto put = [&](void* base, const float (&x)[4], bool f32) HSTU_INLINE_LAMBDA {
-        if (f32) {
-          float* dst = reinterpret_cast<float*>(base) + m * g.ldc + ncol;
-          if (vec) {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (ncol + e < g.N) dst[e] = x[e];
-          }
-        } else {
-          bf16* dst = reinterpret_cast<bf16*>(base) + m * g.ldc + ncol;
-          if (vec) {
-            uint2 o;
-            o.x = pack_bf16x2(x[0], x[1]);
-            o.y = pack_bf16x2(x[2], x[3]);
-            *reinterpret_cast<uint2*>(dst) = o;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (ncol + e < g.N) dst[e] = (bf16)x[e];
-          }
-        }
-      };
-      if (EPI == EPI_SILU) {
-        if (g.C2) put(g.C2, v, false);
-        float sv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sv[e] = silu_f(v[e]);
-        put(g.C, sv, false);
-      } else {
-        put(g.C, v, OUTF32);
-      }
-      if constexpr (MX && EPI == EPI_RESID && !OUTF32) {
-        if (g.c_codes) {
-          // MXFP8 copy of the stored (bf16-rounded) row values: the eight
-          // lanes of a 32-column block share the row, so their amax is a
-          // three-step shuffle (all eight skip rows past M together)
-          float q[4], am = 0.0f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            q[e] = (float)(bf16)v[e];
-            am = fmaxf(am, fabsf(q[e]));
-          }
-#pragma unroll
-          for (int o = 1; o < 8; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-          const int sh = mx_shared_exp(am);
-          *reinterpret_cast<uint32_t*>(g.c_codes + m * g.N + ncol) =
-              mx_cvt4(q[0], q[1], q[2], q[3], sh);
-          if ((lc & 7) == 0) g.c_scales[m * (g.N / 32) + ncol / 32] = (uint8_t)(sh + 127);
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
+  g2_epilogue<FM, FN, EPI, OUTF32, MX, SR>(g, acc, reinterpret_cast<float*>(region), m0, n0, wm,
+                                           wn, lane, z);
 }
 
 // Whether the DMA-staged kernel's layout assumptions hold for g: 16-byte
@@ -628,6 +656,7 @@ hipError_t gemm2_launch(const GemmArgs& g, hipStream_t st) {
   const int mt = (int)((g.M + BM - 1) / BM), nt = (int)((g.N + BN - 1) / BN);
   const int slots = (mt * nt + 7) / 8;
   dim3 grid((unsigned)(8 * slots), (unsigned)(g.epi == EPI_PARTIAL ? g.split_k : 1));
+  if (g.epi == EPI_PARTIAL && g.split_k % 8 == 0) grid = dim3((unsigned)(g.split_k * mt * nt), 1);
   constexpr int NT = 64 * G2_NW;
   switch (g.epi) {
     case EPI_STORE:
@@ -655,7 +684,12 @@ hipError_t gemm2_launch(const GemmArgs& g, hipStream_t st) {
 // vs 0.15 ms, 8-layer UVQK 0.98 vs 1.34 ms): the second workgroup hides the
 // other's epilogue and DMA latency, which outweighs the larger tile's halved
 // LDS reads per MFMA.  The template still accepts 256x256 (one workgroup
-// per CU) for shapes where that measures faster.
+// per CU) for shapes where that measures faster.  A persistent variant (one
+// workgroup per CU walking its tiles through a four-stage LDS ring, the DMA
+// running three k-steps ahead across tiles and under the epilogue) measured
+// 1.3-1.8x slower than four resident one-stage workgroups (training-workload
+// UVQK 0.36 vs 0.23 ms, dX 0.23 vs 0.17 ms): with one wave per SIMD nothing
+// hides the LDS-read and MFMA dependency latencies inside a k-step.
 template <bool AK, bool BK>
 hipError_t gemm2_ab(const GemmArgs& g, hipStream_t st) {
   return gemm2_launch<128, 128, AK, BK>(g, st);
@@ -755,6 +789,42 @@ __global__ void k_splitk_reduce(const float* __restrict__ part, int split, int64
   }
 }
 
+// The same with four consecutive columns per thread (N, ldo and both base
+// addresses multiples of four floats) and the loads of eight splits in
+// flight at once: the partials are read once, at memory rate, instead of one
+// latency per split.
+__global__ __launch_bounds__(256) void k_splitk_reduce4(const float4* __restrict__ part, int split,
+                                                         int64_t M, int64_t N4,
+                                                         float* __restrict__ out, int64_t ldo) {
+  const int64_t total = M * N4;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+    int z = 0;
+    for (; z + 8 <= split; z += 8) {
+      float4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = part[(z + u) * total + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        s.x += x[u].x;
+        s.y += x[u].y;
+        s.z += x[u].z;
+        s.w += x[u].w;
+      }
+    }
+    for (; z < split; ++z) {
+      const float4 x = part[z * total + i];
+      s.x += x.x;
+      s.y += x.y;
+      s.z += x.z;
+      s.w += x.w;
+    }
+    const int64_t m = i / N4, n = 4 * (i % N4);
+    *reinterpret_cast<float4*>(out + m * ldo + n) = s;
+  }
+}
+
 // Column sums: stage 1 writes per-block partials [blocks][cols], stage 2 sums them.
 template <typename T>
 __global__ void k_colsum_part(const T* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -843,9 +913,15 @@ hipError_t launch_splitk_reduce(const float* partial, int split, int64_t M, int6
                                 float* out, int64_t ldo, hipStream_t st) {
   const int64_t total = M * N;
   if (total <= 0) return hipSuccess;
-  int64_t blocks = (total + 255) / 256;
+  const bool v4 = (N & 3) == 0 && (ldo & 3) == 0 &&
+                  ((reinterpret_cast<uintptr_t>(partial) | reinterpret_cast<uintptr_t>(out)) & 15) == 0;
+  int64_t blocks = ((v4 ? total / 4 : total) + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  k_splitk_reduce<<<(unsigned)blocks, 256, 0, st>>>(partial, split, M, N, out, ldo);
+  if (v4)
+    k_splitk_reduce4<<<(unsigned)blocks, 256, 0, st>>>(reinterpret_cast<const float4*>(partial),
+                                                        split, M, N / 4, out, ldo);
+  else
+    k_splitk_reduce<<<(unsigned)blocks, 256, 0, st>>>(partial, split, M, N, out, ldo);
   return hipGetLastError();
 }
 

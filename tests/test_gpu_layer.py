@@ -265,6 +265,7 @@ def test_layer_train_full_size_config4(B):
     check_close(host(g1.dW1), want["dW1"], "bf16", "dW1 seq")
     check_close(host(g1.dW2), want["dW2"], "bf16", "dW2 seq")
     check_close(host(g1.drab_time), want["drab_time"], "bf16", "drab_time seq")
+    check_close(host(g1.drab_pos), want["drab_pos"], "bf16", "drab_pos seq")
     tot = {k: 0.0 for k in ("dW1", "dW2", "drab_pos", "drab_time")}
     for bb in range(cfg.B):
         s = synth.sub_batch(inp, [bb])
