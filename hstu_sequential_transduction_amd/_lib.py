@@ -17,7 +17,8 @@ STATUS_NAMES = {0: "HSTU_OK", -1: "HSTU_ERR_INVALID_ARG", -2: "HSTU_ERR_UNSUPPOR
 HSTU_F32, HSTU_BF16 = 0, 1
 
 EXPORTED = [
-    "hstu_status_string", "hstu_version", "hstu_last_hip_error",
+    "hstu_status_string", "hstu_version", "hstu_last_hip_error", "hstu_last_error_site",
+    "hstu_set_check_mode", "hstu_check_mode",
     "hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size",
     "hstu_attn_fwd", "hstu_attn_bwd", "hstu_attn_fwd_noalloc", "hstu_diag_mfma_loop",
     "hstu_layer_fwd_workspace_size", "hstu_layer_bwd_workspace_size",
@@ -107,6 +108,12 @@ def lib() -> C.CDLL:
     L.hstu_status_string.argtypes = [C.c_int]
     L.hstu_last_hip_error.restype = C.c_char_p
     L.hstu_last_hip_error.argtypes = []
+    L.hstu_last_error_site.restype = C.c_char_p
+    L.hstu_last_error_site.argtypes = []
+    L.hstu_set_check_mode.restype = C.c_int
+    L.hstu_set_check_mode.argtypes = [C.c_int32]
+    L.hstu_check_mode.restype = C.c_int32
+    L.hstu_check_mode.argtypes = []
     L.hstu_version.restype = C.c_char_p
     L.hstu_version.argtypes = []
     for f in ("hstu_attn_fwd_workspace_size", "hstu_attn_bwd_workspace_size"):
@@ -191,6 +198,9 @@ class HstuError(RuntimeError):
             msg = lib().hstu_status_string(status).decode()
             if status == -4:
                 msg += ": " + lib().hstu_last_hip_error().decode()
+                site = lib().hstu_last_error_site().decode()
+                if site:
+                    msg += " at " + site
         except Exception:  # pragma: no cover
             msg = ""
         super().__init__(f"{fn} failed: {name} ({msg})")

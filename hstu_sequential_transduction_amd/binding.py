@@ -53,6 +53,16 @@ class AttnConfig:
     key_splits: int = 0   # forward: 0 auto, 1 never, k >= 2 split long query blocks' keys
 
 
+def set_check_mode(on: bool) -> None:
+    """Debug mode of the library: wait for the device and read the launch
+    error after every launch (see hstu_set_check_mode in include/hstu.h)."""
+    check("hstu_set_check_mode", _lib.lib().hstu_set_check_mode(1 if on else 0))
+
+
+def check_mode() -> bool:
+    return bool(_lib.lib().hstu_check_mode())
+
+
 def attn_desc(cfg: AttnConfig, B: int, T: int, dtype: torch.dtype, rab_stride: int) -> AttnDesc:
     return AttnDesc(B, T, cfg.H, cfg.d_qk, cfg.d_v, cfg.n_pos_buckets, cfg.n_time_buckets,
                     cfg.norm_mode, cfg.norm_len, _DT[dtype], rab_stride, cfg.win_local,

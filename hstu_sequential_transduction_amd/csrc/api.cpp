@@ -6,7 +6,10 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <stdlib.h>
+
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -18,15 +21,39 @@ using namespace hstu;
 namespace {
 
 // HIP error behind the calling thread's last HSTU_ERR_HIP (hstu_last_hip_error)
+// and the step that reported it (hstu_last_error_site)
 thread_local hipError_t g_last_hip_error = hipSuccess;
+thread_local const char* g_last_error_site = "";
 
-#define HSTU_TRY(expr)                                  \
-  do {                                                  \
-    hipError_t e_ = (expr);                             \
-    if (e_ != hipSuccess) {                             \
-      g_last_hip_error = e_;                            \
-      return HSTU_ERR_HIP;                              \
-    }                                                   \
+// Check mode (hstu_set_check_mode, or HSTU_CHECK=1 in the environment when
+// the library loads): after every launch or stream operation the library
+// waits for the device and reads the launch error, so that a failing kernel
+// is reported by the call and the step that launched it.
+std::atomic<int> g_check_mode{0};
+const int g_check_from_env = [] {
+  const char* e = getenv("HSTU_CHECK");
+  if (e && e[0] && strcmp(e, "0") != 0) g_check_mode.store(1);
+  return 0;
+}();
+
+hipError_t check_step() {
+  hipError_t e = hipDeviceSynchronize();
+  const hipError_t l = hipGetLastError();
+  return e != hipSuccess ? e : l;
+}
+
+#define HSTU_STR_(x) #x
+#define HSTU_STR(x) HSTU_STR_(x)
+#define HSTU_TRY(expr)                                                          \
+  do {                                                                          \
+    hipError_t e_ = (expr);                                                     \
+    if (e_ == hipSuccess && g_check_mode.load(std::memory_order_relaxed))       \
+      e_ = check_step();                                                        \
+    if (e_ != hipSuccess) {                                                     \
+      g_last_hip_error = e_;                                                    \
+      g_last_error_site = "api.cpp:" HSTU_STR(__LINE__) ": " #expr;             \
+      return HSTU_ERR_HIP;                                                      \
+    }                                                                           \
   } while (0)
 
 // Every entry point that launches work starts here: it clears an error that
@@ -247,14 +274,21 @@ bool plan_recorded(const hstu_attn_desc* d, const void* ws, const int32_t* offs,
 // The backward keeps dS (the scores' gradient) when max_len bounds the
 // batch: 128 x 128 bf16 blocks of the causal part; with n_b <= max_len the
 // blocks number at most H (R + 1) / 2 sum_b ceil(n_b / 128), R = ceil(max_len / 128).
+// A batch whose bound exceeds kMaxDsBlocks (4 TiB of blocks, more than the
+// device holds) never keeps dS; the bound is computed in 64 bits from
+// max_len clamped to T, so no size arithmetic can overflow.
+constexpr int64_t kMaxDsBlocks = int64_t(1) << 27;
+int64_t ds_capacity_blocks(const hstu_attn_desc* d) {
+  const int64_t R = (std::min<int64_t>(d->max_len, d->T) + 127) / 128;
+  const int64_t rows = (d->T + 127) / 128 + d->B;
+  const int64_t per_head = ((R + 1) * rows + 1) / 2;  // < 2^25 * 2^32
+  if (per_head > kMaxDsBlocks) return 0;
+  const int64_t blocks = (int64_t)d->H * per_head;
+  return blocks > kMaxDsBlocks ? 0 : blocks;
+}
 bool keeps_ds(const hstu_attn_desc* d) {
   return d->max_len > 0 && d->dtype == HSTU_BF16 && d->d_qk == 128 && d->d_v == 128 &&
-         d->win_local == 0;
-}
-int64_t ds_capacity_blocks(const hstu_attn_desc* d) {
-  const int64_t R = (d->max_len + 127) / 128;
-  const int64_t rows = (d->T + 127) / 128 + d->B;
-  return (int64_t)d->H * ((R + 1) * rows + 1) / 2;
+         d->win_local == 0 && ds_capacity_blocks(d) > 0;
 }
 
 struct BwdWs {
@@ -807,6 +841,16 @@ const char* hstu_status_string(hstu_status s) {
 }
 
 const char* hstu_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
+
+const char* hstu_last_error_site(void) { return g_last_error_site; }
+
+hstu_status hstu_set_check_mode(int32_t on) {
+  if (on != 0 && on != 1) return HSTU_ERR_INVALID_ARG;
+  g_check_mode.store(on);
+  return HSTU_OK;
+}
+
+int32_t hstu_check_mode(void) { return g_check_mode.load(); }
 
 const char* hstu_version(void) { return "hstu-mi355x 0.1 (gfx950)"; }
 

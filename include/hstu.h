@@ -106,7 +106,9 @@ typedef struct {
    * dS, the gradient of the scores, in its workspace (bf16, 128 x 128 blocks
    * of the causal part, about 2 T max_len H bytes) and form dQ from it instead
    * of recomputing S and dA.  If the batch's blocks do not fit (a sequence
-   * longer than max_len), the backward recomputes; results agree either way. */
+   * longer than max_len), the backward recomputes; results agree either way.
+   * A shape whose bound (max_len taken at most T) exceeds 2^27 blocks of
+   * 32 KiB never keeps dS and asks for no such workspace. */
   int32_t max_len;
   /* Forward only (hstu_attn_fwd, hstu_attn_fwd_noalloc, hstu_layer_fwd,
    * hstu_layer_fwd_mx): 1 asks to skip the plan (time pre-pass and work
@@ -184,6 +186,22 @@ typedef struct {
 const char* hstu_status_string(hstu_status s);
 /* Text of the HIP error behind the calling thread's last HSTU_ERR_HIP. */
 const char* hstu_last_hip_error(void);
+/* The library step ("api.cpp:<line>: <call>") whose HIP call or launch
+ * returned that error; "" if none did. */
+const char* hstu_last_error_site(void);
+/*
+ * Check mode, for debugging: with it on, every entry point waits for the
+ * device after each kernel launch and stream operation it makes and reads
+ * the launch error, so that an asynchronous kernel failure is reported as
+ * HSTU_ERR_HIP by the call that caused it, with hstu_last_error_site naming
+ * the launching step.  Calls become synchronous and slow; not for use under
+ * HIP graph capture (the wait is not allowed there).  Process-wide; off by
+ * default, on at load when the environment variable HSTU_CHECK is set to a
+ * value other than "0".  hstu_set_check_mode: on = 0 or 1, other values
+ * HSTU_ERR_INVALID_ARG.  hstu_check_mode: the current setting.
+ */
+hstu_status hstu_set_check_mode(int32_t on);
+int32_t hstu_check_mode(void);
 /* Library version string. */
 const char* hstu_version(void);
 

@@ -242,3 +242,23 @@ def test_binding_refuses_reuse_plan_without_its_workspace():
     assert lw.get(512, torch.device("cpu"), 1) is buf
     with pytest.raises(ValueError):   # too small: would be reallocated
         lw.get(4096, torch.device("cpu"), 1)
+
+
+def test_check_mode_switch(L):
+    """Check mode (sync + launch-error read after every launch) is a
+    process-wide switch; HSTU_CHECK in the environment turns it on at load."""
+    import subprocess
+    import sys
+    assert L.hstu_check_mode() == 0
+    assert L.hstu_set_check_mode(1) == 0 and L.hstu_check_mode() == 1
+    assert L.hstu_set_check_mode(0) == 0 and L.hstu_check_mode() == 0
+    assert L.hstu_set_check_mode(2) == -1 and L.hstu_check_mode() == 0
+    assert L.hstu_last_error_site() == b""
+    code = ("from hstu_sequential_transduction_amd import _lib; "
+            "print(_lib.lib().hstu_check_mode())")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for val, want in (("1", "1"), ("0", "0")):
+        env = dict(os.environ, HSTU_CHECK=val)
+        out = subprocess.run([sys.executable, "-c", code], cwd=root, env=env,
+                             capture_output=True, text=True, timeout=120)
+        assert out.stdout.strip().splitlines()[-1] == want, out.stderr[-2000:]

@@ -274,3 +274,32 @@ def test_layer_train_full_size_config4(B):
             tot[k] = tot[k] + host(getattr(gb, k))
     for k in tot:
         check_close(host(getattr(g, k)), tot[k], "bf16", f"{k} additivity")
+
+
+def test_check_mode_gives_the_same_results(B):
+    """Check mode (wait + launch-error read after every launch) changes only
+    the timing: a training step with it on is bit-identical to one without."""
+    import torch
+    cfg = synth.get_config(4).shrunk(B=3, lengths=("list", [300, 1100, 129])).unit_scale()
+    inp = synth.make_inputs(cfg, seed=610)
+    d = Dev(inp, cfg)
+    lc = _lcfg(B, cfg)
+    lc.attn.max_len = 1100
+    dx0, g0 = _train_step(B, d, lc, inp.T)
+    torch.cuda.synchronize()
+    B.set_check_mode(True)
+    try:
+        assert B.check_mode()
+        dx1, g1 = _train_step(B, d, lc, inp.T)
+        torch.cuda.synchronize()
+    finally:
+        B.set_check_mode(False)
+    assert not B.check_mode()
+    assert torch.equal(dx0, dx1)
+    for k in ("dW1", "dW2"):
+        assert torch.equal(getattr(g0, k), getattr(g1, k)), k
+    # the rab-table gradients are sums of float atomics: same values up to
+    # the order of the additions
+    for k in ("drab_pos", "drab_time"):
+        a, b = getattr(g0, k), getattr(g1, k)
+        assert torch.allclose(a, b, rtol=1e-5, atol=1e-6 * float(a.abs().max())), k
