@@ -252,6 +252,56 @@ def test_schedule_covers_every_block_once(B, reverse):
         assert all(cost[i] >= cost[i + 1] for i in range(n - 1)), "not longest-first"
 
 
+@pytest.mark.parametrize("bm", [64, 128])
+def test_schedule_in_global_memory(B, bm):
+    """More than 3 070 entries: the work-list builder keeps its arrays in the
+    workspace instead of LDS (T = 260k rows at 64-row blocks)."""
+    import torch
+    rng = np.random.default_rng(13)
+    lens = np.concatenate([[0, 1, 64, 65], rng.integers(0, 2600, size=200)])
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(offs[-1])
+    from hstu_sequential_transduction_amd import _lib
+    cap = _lib.lib().hstu_schedule_capacity(T, len(lens), bm)
+    if bm == 64:
+        assert cap + 2 > 3072, cap
+    items, n = B.hstu_schedule(dev(offs), T, bm, False)
+    torch.cuda.synchronize()
+    items, n = items.cpu().numpy(), int(n.cpu().numpy()[0])
+    nb = (lens + bm - 1) // bm
+    assert n == int(nb.sum())
+    got = sorted(map(tuple, items[:n].tolist()))
+    want = sorted((b, m) for b in range(len(lens)) for m in range(nb[b]))
+    assert got == want
+    cost = [m for _, m in items[:n].tolist()]
+    assert all(cost[i] >= cost[i + 1] for i in range(n - 1)), "not longest-first"
+
+
+def test_attn_fwd_plan_in_global_memory(B):
+    """A forward whose work list exceeds the LDS-resident builder (T = 400k
+    rows at 128-row blocks), against the oracle on sampled rows."""
+    rng = np.random.default_rng(14)
+    lens = rng.integers(1000, 5600, size=120)
+    cfg = synth.get_config(2).shrunk(B=len(lens), lengths=("list", lens.tolist()))
+    cfg = dataclasses.replace(cfg, H=1, d_qk=32, d_v=32)
+    say(f"attn fwd global-memory plan: T={int(lens.sum())}")
+    a = synth.make_attn_inputs(cfg, seed=15)
+    from hstu_sequential_transduction_amd import _lib
+    assert _lib.lib().hstu_schedule_capacity(int(lens.sum()), len(lens), 128) + 2 > 3072
+    ac = _cfgobj(B, cfg)
+    got = _fwd(B, a, cfg, ac)
+    sub = [0, 7, 55, 119]
+    rows = [[0, int(lens[b]) // 2, int(lens[b]) - 1] for b in sub]
+    offs = a.seq_offsets
+    keep = np.concatenate([np.arange(offs[b], offs[b + 1]) for b in sub])
+    sub_offs = np.concatenate([[0], np.cumsum([lens[b] for b in sub])])
+    want = orc.attn_fwd(a.q[keep], a.k[keep], a.v[keep], sub_offs, a.timestamps[keep],
+                        a.rab_pos, a.rab_time, None, 0, cfg.norm_len, return_rows=rows)
+    sel = np.concatenate([offs[b] + np.asarray(r) for b, r in zip(sub, rows)])
+    wsel = np.concatenate([sub_offs[i] + np.asarray(r) for i, r in enumerate(rows)])
+    check_close(got[sel], want[wsel], "bf16", "O global-memory plan", scale_ref=want[wsel])
+
+
 def test_validate_inputs(B):
     offs = dev(np.array([0, 5, 9], np.int32))
     assert B.hstu_validate_inputs(offs, 9) == 0

@@ -236,6 +236,26 @@ def test_layer_stack_full_size_sampled_sequences(B, ci):
     check_close(got[-1][rows], want[-1], cfg.dtype, f"Y[last] full cfg{ci} seqs {pick}")
 
 
+def test_layer_stack_full_size_config3_literal_scale(B):
+    """The 8-layer Zipf workload at its literal scales (inputs and weights
+    N(0, 1/sqrt(d)), rab N(0, 0.02)): the full batch through the GPU stack,
+    every layer's output compared with the oracle on three whole sequences
+    (the shortest, the median and the 90th-percentile length)."""
+    cfg = synth.get_config(3)
+    say("layer stack full cfg3 (literal scale)")
+    inp = synth.make_inputs(cfg)
+    d = Dev(inp, cfg)
+    got = _stack_gpu(B, d, _lcfg(B, cfg))
+    order = np.argsort(inp.lengths)
+    pick = sorted({int(order[0]), int(order[len(order) // 2]), int(order[(9 * len(order)) // 10])})
+    sub = synth.sub_batch(inp, pick)
+    want = orc.stack_fwd(sub.X, sub.layers, sub.seq_offsets, sub.timestamps, sub.num_candidates,
+                         _flags(cfg))
+    rows = np.concatenate([np.arange(inp.seq_offsets[b], inp.seq_offsets[b + 1]) for b in pick])
+    for li in range(cfg.n_layers):
+        check_close(got[li][rows], want[li], cfg.dtype, f"Y[{li}] literal cfg3 seqs {pick}")
+
+
 def test_layer_train_full_size_config4(B):
     """Full config-4 training step on the GPU against the oracle on one sequence
     (dX rows) and on the whole batch for the weight gradients."""

@@ -124,23 +124,58 @@ def test_mx_layer_fwd(B, ci, hist, c, variant):
                          np.maximum(np.abs(deq) * 2.0 ** -4, 2.0 ** -10 * X))
     slack = 2e-2 * np.abs(G) + 2e-2 * np.abs(G).max()
     assert np.all(np.abs(deq - G) <= half_step + slack), "G codes not a rounding of G"
+    # Which codes may differ from the oracle's rounding, derived: the GPU's G
+    # differs from the oracle's by at most the bf16 tolerance tol, so a code
+    # may differ only where the band G +- tol holds a rounding boundary of
+    # the block's E4M3 grid (same block scale), and a block's scale only
+    # where its largest magnitude lies within tol of the power of two
+    # between the two scales.  Every difference must be of one of these kinds.
     oc, osc = orc.mx_quantize(G, axis=1)
-    flips = float(np.mean(orc.mx_dequantize(oc, osc, axis=1) != deq))
-    say(f"  G codes differing from the oracle's rounding: {100 * flips:.2f} %")
-    assert flips < 0.15
+    odeq = orc.mx_dequantize(oc, osc, axis=1)
+    tol = 2e-2 * np.abs(G) + 2e-2 * np.sqrt(np.mean(G * G))
+    nblk = W // 32
+    same = (osc.astype(np.int64) == scales.astype(np.int64)).repeat(32, axis=1)
+    amax = np.abs(G).reshape(T, nblk, 32).max(axis=2)
+    tol_blk = tol.reshape(T, nblk, 32).max(axis=2)
+    d_sc = np.abs(osc.astype(np.int64) - scales.astype(np.int64))
+    bad_blk = d_sc != 0
+    assert np.all(d_sc[bad_blk] == 1), "block scales differ by more than one binade"
+    edge = np.exp2(np.maximum(osc, scales)[bad_blk].astype(np.float64) - 127 + 8)
+    assert np.all(np.abs(amax[bad_blk] - edge) <= tol_blk[bad_blk]), "scale flip not at an edge"
+    flip = same & (odeq != deq)
+    # a code may differ only where the band G +- tol holds a rounding
+    # boundary: its ends round to different E4M3 values on the block's grid
+    lo_c = orc.e4m3_encode((G - tol) / X)
+    hi_c = orc.e4m3_encode((G + tol) / X)
+    spans = lo_c != hi_c
+    assert np.all(spans[flip]), "a code differs where no rounding boundary is within tol"
+    allowed = float(np.mean(spans[same]))
+    flips = float(np.mean(flip[same]))
+    say(f"  G codes differing from the oracle's rounding: {100 * flips:.2f} % "
+        f"(the tolerance allows up to {100 * allowed:.2f} %); blocks with another scale: "
+        f"{int(bad_blk.sum())} of {bad_blk.size}")
+    assert flips <= allowed
     # (2) Y from the GPU's own quantized G (at the literal scale the layer's
     # contribution is below bf16 resolution next to X, so Y itself is
     # compared; the unit-scale variants also compare Y - X)
     w2c, w2s = orc.mx_quantize(w.W2, axis=0)
     want2 = deq @ orc.mx_dequantize(w2c, w2s, axis=0) + inp.X
     check_close(got, want2, "bf16", "Y from the GPU's G")
+    exact, _ = orc.layer_fwd(inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                             inp.timestamps, inp.num_candidates, f)
     if variant != "unit":
+        # at the literal scale the layer's contribution sits below bf16
+        # resolution next to X: end to end, Y itself against the oracle's MX
+        # layer and the exact layer
+        check_close(got, want, "bf16", "Y vs the oracle's MX layer")
+        rel_y = np.linalg.norm(got - want) / np.linalg.norm(want)
+        rel_ye = np.linalg.norm(got - exact) / np.linalg.norm(exact)
+        say(f"  relative L2 of Y: {rel_y:.2e} vs the oracle's MX layer, {rel_ye:.2e} vs exact")
+        assert rel_y < 2e-2 and rel_ye < 2e-2
         return
     check_close(got - inp.X, want2 - inp.X, "bf16", "Y - X from the GPU's G")
     # end to end
     rel_mx = np.linalg.norm((got - inp.X) - (want - inp.X)) / np.linalg.norm(want - inp.X)
-    exact, _ = orc.layer_fwd(inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
-                             inp.timestamps, inp.num_candidates, f)
     rel = np.linalg.norm((got - inp.X) - (exact - inp.X)) / np.linalg.norm(exact - inp.X)
     say(f"  relative L2 of Y - X: {rel_mx:.4f} vs the oracle's MX layer, {rel:.4f} vs exact")
     assert rel_mx < 2e-2
