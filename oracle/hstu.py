@@ -331,15 +331,20 @@ def layer_fwd(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candida
 
 
 def layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
-              f: LayerFlags, saved: Dict, b1=None, b2=None, gamma=None, beta=None):
-    """All gradients of one layer, by the chain rule written out (step 5)."""
+              f: LayerFlags, saved: Dict, b1=None, b2=None, gamma=None, beta=None,
+              act_matmul=None):
+    """All gradients of one layer, by the chain rule written out (step 5).
+    act_matmul (default: the exact product) computes the two products that
+    carry the activation gradients back, dG = dY W2^T and dX = dZ W1^T
+    (layer_bwd_mx passes the MXFP8 product)."""
+    mm = act_matmul if act_matmul is not None else (lambda a, b: a @ b)
     dY = np.asarray(dY, np.float64)
     X = np.asarray(X, np.float64)
     W1 = np.asarray(W1, np.float64); W2 = np.asarray(W2, np.float64)
     T = X.shape[0]
     U, V, Q, K = split_uvqk(saved["Zh"], f)
     # Y = G W2 + b2 (+ X)
-    dG = dY @ W2.T
+    dG = mm(dY, W2.T)
     dW2 = saved["G"].T @ dY
     db2 = dY.sum(axis=0)
     # G = Yn * U
@@ -355,7 +360,7 @@ def layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_can
     dZ = dZh * silu_grad(saved["Z"]) if f.proj_silu else dZh
     dW1 = X.T @ dZ
     db1 = dZ.sum(axis=0)
-    dX = dZ @ W1.T
+    dX = mm(dZ, W1.T)
     if f.residual:
         dX = dX + dY
     return dict(dX=dX, dW1=dW1, dW2=dW2, db1=db1, db2=db2, dgamma=dgamma, dbeta=dbeta,
@@ -618,10 +623,12 @@ def mx_matmul(a, b):
 
 
 def layer_fwd_mx(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
-                 f: LayerFlags, b1=None, b2=None, gamma=None, beta=None, return_g=False):
+                 f: LayerFlags, b1=None, b2=None, gamma=None, beta=None, return_g=False,
+                 return_saved=False):
     """One layer with MXFP8 projection and output matmuls (steps 1 and 4);
     attention, LayerNorm and gating as in layer_fwd.  return_g: also the
-    gated output G before its quantization."""
+    gated output G before its quantization; return_saved: also the
+    intermediates layer_bwd_mx needs (as layer_fwd's)."""
     X = np.asarray(X, np.float64)
     Z = mx_matmul(X, W1)
     if b1 is not None:
@@ -630,11 +637,28 @@ def layer_fwd_mx(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_cand
     U, V, Q, K = split_uvqk(Zh, f)
     O = attn_fwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
                  f.norm_mode, f.norm_len, win_local=f.win_local, win_global=f.win_global)
-    Yn, _, _, _ = layernorm_fwd(O.reshape(X.shape[0], f.H * f.d_v), f.eps, gamma, beta)
+    O2 = O.reshape(X.shape[0], f.H * f.d_v)
+    Yn, mu, rstd, xhat = layernorm_fwd(O2, f.eps, gamma, beta)
     G = Yn * U
     Y = mx_matmul(G, W2)
     if b2 is not None:
         Y = Y + np.asarray(b2, np.float64)
     if f.residual:
         Y = Y + X
+    if return_saved:
+        return Y, dict(Z=Z, Zh=Zh, O=O2, mu=mu, rstd=rstd, xhat=xhat, Yn=Yn, G=G)
     return (Y, G) if return_g else Y
+
+
+def layer_bwd_mx(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
+                 f: LayerFlags, saved: Dict, b1=None, b2=None, gamma=None, beta=None):
+    """Gradients of layer_fwd_mx for training with FP8 matmuls ([ULTRA] "Mixed
+    precision": the matrix products in FP8, the rest in BF16).  Reading:
+    the two products that carry the activation gradients back, dG = dY W2^T
+    and dX = dZ W1^T, are MXFP8 products, each operand rounded along its own
+    contraction (the forward's recipe); the weight gradients dW2 = G^T dY and
+    dW1 = X^T dZ stay exact here (bf16 on the device); the quantizers count
+    as the identity in the chain rule (the forward's rounding is not
+    differentiated).  `saved` from layer_fwd_mx(..., return_saved=True)."""
+    return layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps,
+                     num_candidates, f, saved, b1, b2, gamma, beta, act_matmul=mx_matmul)

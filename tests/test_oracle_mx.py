@@ -149,3 +149,89 @@ def test_mx_layer_equals_the_plain_layer_on_representable_operands():
     np.testing.assert_allclose(Y, want, rtol=1e-12, atol=1e-13)
     # and the MX layer stays within a few percent of the plain one
     assert np.linalg.norm((Y - X) - (Yp - X)) <= 0.08 * np.linalg.norm(Yp - X)
+
+
+def _mx_err_bound(x, axis):
+    """Largest rounding error MXFP8 can make on each element of x (blocks of
+    32 along `axis`): half a spacing of the E4M3 grid scaled by the block's
+    power of two X = 2^(floor(log2 amax) - 8) -- 2^-4 |x| for normal values,
+    2^-10 X below E4M3's normal range -- or the clamp to 448 X above it."""
+    x = np.asarray(x, np.float64)
+    xm = np.moveaxis(x, axis, -1)
+    blocks = np.abs(xm).reshape(xm.shape[:-1] + (xm.shape[-1] // 32, 32))
+    amax = blocks.max(axis=-1, keepdims=True)
+    X = np.where(amax > 0, np.exp2(np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8), 0.0)
+    e = np.maximum(np.maximum(2.0 ** -4 * blocks, 2.0 ** -10 * X), blocks - 448 * X)
+    return np.moveaxis(e.reshape(xm.shape), -1, axis)
+
+
+def _mx_case(seed, representable=False):
+    rng = np.random.default_rng(seed)
+    H, dqk, dv, D = 2, 32, 32, 64
+    lengths = [7, 12, 3]
+    offs = np.concatenate([[0], np.cumsum(lengths)])
+    T = int(offs[-1])
+    ts = np.concatenate([1_600_000_000 + np.arange(n) * 50 for n in lengths]).astype(np.int64)
+    F1 = H * (2 * dv + 2 * dqk)
+    if representable:
+        X = _representable(rng, (T, D), axis=1)
+        W1 = _representable(rng, (D, F1), axis=1)   # rows along F1: dX's operand
+        W2 = _representable(rng, (H * dv, D), axis=1)  # rows along D: dG's operand
+        dY = _representable(rng, (T, D), axis=1)
+    else:
+        X = rng.standard_normal((T, D))
+        W1 = rng.standard_normal((D, F1)) / 8
+        W2 = rng.standard_normal((H * dv, D)) / 8
+        dY = rng.standard_normal((T, D))
+    rp, rt = rng.standard_normal((H, 128)) * 0.1, rng.standard_normal((H, 128)) * 0.1
+    f = orc.LayerFlags(H=H, d_qk=dqk, d_v=dv, norm_len=16, eps=1e-3)
+    return X, W1, W2, dY, rp, rt, offs, ts, f
+
+
+def test_mx_backward_products_within_the_rounding_bound():
+    """dG and dX of the MX backward differ from the exact products of the
+    same operands by at most the bound the per-element rounding allows:
+    |MX(a) MX(b) - a b| <= sum_k e_a |b| + |a| e_b + e_a e_b, each operand
+    rounded along the contraction."""
+    X, W1, W2, dY, rp, rt, offs, ts, f = _mx_case(21)
+    _, sv = orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f, return_saved=True)
+    g = orc.layer_bwd_mx(dY, X, W1, W2, rp, rt, offs, ts, None, f, sv)
+
+    def check(a, b, got):
+        ea, eb = _mx_err_bound(a, axis=1), _mx_err_bound(b, axis=0)
+        bound = ea @ np.abs(b) + np.abs(a) @ eb + ea @ eb
+        assert np.all(np.abs(got - a @ b) <= bound * (1 + 1e-9) + 1e-300)
+        # and the bound is not vacuous: the rounding changed the product
+        assert np.abs(got - a @ b).max() > 0
+
+    check(dY, W2.T, g["dG"])
+    check(g["dZ"], W1.T, g["dX"] - dY)
+
+
+def test_mx_backward_exact_on_representable_operands():
+    """With dY and W2 on the MXFP8 grid along D (the contraction of dG), dG is
+    the exact product; the weight gradients are the exact products of the
+    chain's operands."""
+    X, W1, W2, dY, rp, rt, offs, ts, f = _mx_case(22, representable=True)
+    _, sv = orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f, return_saved=True)
+    g = orc.layer_bwd_mx(dY, X, W1, W2, rp, rt, offs, ts, None, f, sv)
+    np.testing.assert_allclose(g["dG"], dY @ W2.T, rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(g["dW2"], sv["G"].T @ dY, rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(g["dW1"], X.T @ g["dZ"], rtol=1e-13, atol=1e-300)
+    # quantizing along the other axis would not be exact here
+    q, s = orc.mx_quantize(W2.T, axis=1)
+    assert np.abs(orc.mx_dequantize(q, s, axis=1) - W2.T).max() > 0
+
+
+def test_mx_backward_close_to_the_exact_backward():
+    """The FP8 error of the backward on ordinary operands: a few percent of
+    the exact gradients (accuracy of the format, not a parity bound)."""
+    X, W1, W2, dY, rp, rt, offs, ts, f = _mx_case(23)
+    _, sv = orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f, return_saved=True)
+    g = orc.layer_bwd_mx(dY, X, W1, W2, rp, rt, offs, ts, None, f, sv)
+    ex = orc.layer_bwd(dY, X, W1, W2, rp, rt, offs, ts, None, f, sv)
+    for k in ("dX", "dW1", "dW2", "drab_pos", "drab_time"):
+        rel = np.linalg.norm(g[k] - ex[k]) / np.linalg.norm(ex[k])
+        assert rel < 0.1, (k, rel)
+    # the weight gradient of the output product uses the same operands
+    np.testing.assert_allclose(g["dW2"], ex["dW2"], rtol=1e-13)
