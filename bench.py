@@ -162,10 +162,12 @@ def upload_layer(inp, cfg, li=0):
         rp=torch.from_numpy(w.rab_pos).cuda(), rt=torch.from_numpy(w.rab_time).cuda())
 
 
-def train_setup(window=(0, 0), keep_ds=True):
+def train_setup(window=(0, 0), keep_ds=True, mx=False):
     """The training workload on the device and one step (layer fwd + bwd) as a
     closure.  keep_ds: pass the longest sequence as max_len, which lets the
-    backward keep the score gradient dS and form dQ from it."""
+    backward keep the score gradient dS and form dQ from it.  mx: the MXFP8
+    step (hstu_layer_fwd_mx + hstu_layer_bwd_mx; the weights are quantized
+    inside the step, as they change every step)."""
     import numpy as np
     import torch
 
@@ -195,20 +197,25 @@ def train_setup(window=(0, 0), keep_ds=True):
     wsf, wsb = B.LayerWorkspace(), B.LayerWorkspace()
 
     def step():
-        B.hstu_layer_fwd(X, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc, saved=saved, y=y,
-                         workspace=wsf)
+        if mx:
+            wm = B.MxLayerWeights.from_bf16(w["W1"], w["W2"])
+            B.hstu_layer_fwd_mx(X, wm, w["rp"], w["rt"], offs, ts, lc, saved=saved, y=y,
+                                workspace=wsf)
+        else:
+            B.hstu_layer_fwd(X, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc, saved=saved,
+                             y=y, workspace=wsf)
         B.hstu_layer_bwd(X, w["W1"], w["W2"], w["rp"], w["rt"], offs, ts, lc, saved, dY, dx=dx,
-                         grads=grads, workspace=wsb)
+                         grads=grads, workspace=wsb, mx=mx)
 
     lf = flops.layer_flops(inp.lengths, None, cfg.D, cfg.H, cfg.d_qk, cfg.d_v, backward=True,
                            window=window if window[0] > 0 else None)
     return cfg, inp, step, lf
 
 
-def bench_train(args, timer, window=(0, 0), keep_ds=True):
+def bench_train(args, timer, window=(0, 0), keep_ds=True, mx=False):
     """Uninstrumented timed region of --steps steps, then an instrumented pass
     of the same number of steps (at most 20) for the per-kernel table."""
-    cfg, inp, step, lf = train_setup(window, keep_ds)
+    cfg, inp, step, lf = train_setup(window, keep_ds, mx)
     stats = time_region(step, args.steps, args.warmup)
     kern, ms_instr = instrumented(step, timer, min(args.steps, 20))
     stats["ms_instrumented"] = round(ms_instr, 4)
@@ -233,6 +240,22 @@ def bench_recompute(args, timer, kept_ms):
            "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
            "slowdown_vs_kept_ds": round(ms / kept_ms, 3), "kernels": kt}
     log(f"train step, dQ recomputed: {ms:.3f} ms ({out['tflops']} TFLOP/s)")
+    return out
+
+
+def bench_train_mx(args, timer, bf16_ms):
+    """The training step with MXFP8 products: forward projection and output
+    products, backward dG and dX (weight gradients, attention and LayerNorm
+    in bf16 / fp32).  TFLOP/s on the same work as the bf16 step."""
+    cfg, inp, stats, kern, lf = bench_train(args, timer, mx=True)
+    ms = stats["ms_mean"]
+    out = {"ms_per_step": ms, **{k: v for k, v in stats.items() if k != "ms_mean"},
+           "tflops": round(lf["total"] / (ms * 1e-3) / 1e12, 2),
+           "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
+           "speedup_vs_bf16": round(bf16_ms / ms, 3),
+           "kernel_ms_per_launch": {k: round(v[1] / v[0], 4) for k, v in kern.items()}}
+    log(f"train step, MXFP8 products: {ms:.3f} ms ({out['tflops']} TFLOP/s, "
+        f"{out['speedup_vs_bf16']}x the bf16 step)")
     return out
 
 
@@ -766,8 +789,8 @@ def cpu_baseline_configs():
     return out
 
 
-ALL_PARTS = ("train", "recompute", "fwd", "semilocal", "trunc", "cached", "mx", "epilogue",
-             "peaks", "cpu")
+ALL_PARTS = ("train", "recompute", "trainmx", "fwd", "semilocal", "trunc", "cached", "mx",
+             "epilogue", "peaks", "cpu")
 
 
 def main():
@@ -839,6 +862,8 @@ def main():
             "kernels": table, "roofline": roof})
     if "recompute" in parts:
         line["train_dq_recomputed"] = bench_recompute(args, timer, ms or float("nan"))
+    if "trainmx" in parts:
+        line["train_mxfp8"] = bench_train_mx(args, timer, ms or float("nan"))
     if "fwd" in parts:
         line["forward_workloads"] = bench_fwd_configs(timer, fwd_cfgs, reps=args.reps)
     if "semilocal" in parts:

@@ -29,6 +29,7 @@ EXPORTED = [
     "hstu_attn_cached_workspace_size", "hstu_attn_cached_fwd",
     "hstu_mx_quantize", "hstu_mx_quantize_weight", "hstu_mx_gemm",
     "hstu_layer_fwd_mx_workspace_size", "hstu_layer_fwd_mx",
+    "hstu_layer_bwd_mx_workspace_size", "hstu_layer_bwd_mx",
     "hstu_layer_cached_workspace_size", "hstu_layer_fwd_cached",
     "hstu_timer_enable", "hstu_timer_reset", "hstu_timer_tag_count", "hstu_timer_tag_name",
     "hstu_timer_query",
@@ -160,7 +161,12 @@ def lib() -> C.CDLL:
     L.hstu_layer_fwd_mx_workspace_size.argtypes = [P(LayerDesc)]
     L.hstu_layer_fwd_mx.restype = C.c_int
     L.hstu_layer_fwd_mx.argtypes = [P(LayerDesc), vp, P(LayerWeights), P(MxWeights), vp, vp, vp,
-                                    vp, P(MxIO), vp, sz, vp]
+                                    vp, P(MxIO), P(LayerSaved), vp, sz, vp]
+    L.hstu_layer_bwd_mx_workspace_size.restype = sz
+    L.hstu_layer_bwd_mx_workspace_size.argtypes = [P(LayerDesc)]
+    L.hstu_layer_bwd_mx.restype = C.c_int
+    L.hstu_layer_bwd_mx.argtypes = [P(LayerDesc), vp, P(LayerWeights), vp, vp, vp, P(LayerSaved),
+                                    vp, vp, P(LayerGrads), vp, sz, vp]
     L.hstu_attn_cached_workspace_size.restype = sz
     L.hstu_attn_cached_workspace_size.argtypes = [P(AttnDesc), i64]
     L.hstu_attn_cached_fwd.restype = C.c_int

@@ -253,8 +253,9 @@ class Grads:
 def hstu_layer_bwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: LayerConfig,
                    saved: Saved, dy, num_candidates=None, b1=None, b2=None, gamma=None,
                    beta=None, dx=None, grads: Optional[Grads] = None,
-                   workspace: Optional[LayerWorkspace] = None, stream=None):
-    """(dx, Grads) of the layer for the output gradient dy."""
+                   workspace: Optional[LayerWorkspace] = None, stream=None, mx: bool = False):
+    """(dx, Grads) of the layer for the output gradient dy.  mx: the backward
+    of hstu_layer_fwd_mx (hstu_layer_bwd_mx: dG and dX as MXFP8 products)."""
     T = x.shape[0]
     B = seq_offsets.shape[0] - 1
     dev = x.device
@@ -270,17 +271,19 @@ def hstu_layer_bwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: L
                       None if beta is None else torch.empty(beta.shape, **f32))
     d = layer_desc(cfg, B, T, x.dtype, _rab_stride(rab_pos, rab_time))
     L = _lib.lib()
-    nb = L.hstu_layer_bwd_workspace_size(C.byref(d))
+    nb = (L.hstu_layer_bwd_mx_workspace_size if mx else L.hstu_layer_bwd_workspace_size)(
+        C.byref(d))
     ws = workspace.get(nb, dev) if workspace is not None else _ws(nb, dev)
     w = _weights(W1, W2, rab_pos, rab_time, b1, b2, gamma, beta)
     g = LayerGrads(_ptr(grads.dW1), _ptr(grads.dW2), _ptr(grads.db1), _ptr(grads.db2),
                    _ptr(grads.dgamma), _ptr(grads.dbeta), _ptr(grads.drab_pos),
                    _ptr(grads.drab_time))
     sv = saved.c()
-    st = L.hstu_layer_bwd(C.byref(d), _ptr(x), C.byref(w), _ptr(seq_offsets), _ptr(timestamps),
-                          _ptr(num_candidates), C.byref(sv), _ptr(dy), _ptr(dx), C.byref(g),
-                          _ptr(ws), ws.numel(), _stream(stream))
-    check("hstu_layer_bwd", st)
+    fn = L.hstu_layer_bwd_mx if mx else L.hstu_layer_bwd
+    st = fn(C.byref(d), _ptr(x), C.byref(w), _ptr(seq_offsets), _ptr(timestamps),
+            _ptr(num_candidates), C.byref(sv), _ptr(dy), _ptr(dx), C.byref(g),
+            _ptr(ws), ws.numel(), _stream(stream))
+    check("hstu_layer_bwd_mx" if mx else "hstu_layer_bwd", st)
     return dx, grads
 
 
@@ -400,11 +403,12 @@ class MxLayerWeights:
 def hstu_layer_fwd_mx(x, wm: MxLayerWeights, rab_pos, rab_time, seq_offsets, timestamps,
                       cfg: LayerConfig, num_candidates=None, b1=None, b2=None, gamma=None,
                       beta=None, y=None, workspace: Optional[LayerWorkspace] = None, stream=None,
-                      g_out=None, x_mx=None, y_mx=None):
-    """Y of one layer with MXFP8 projection and output products (inference).
+                      g_out=None, x_mx=None, y_mx=None, saved: Optional["Saved"] = None):
+    """Y of one layer with MXFP8 projection and output products.
     Optional (codes, scales) pairs: x_mx holds x already in MXFP8 (e.g. the
     previous layer's y_mx), y_mx receives y in MXFP8, g_out the quantized
-    gated output the output product used."""
+    gated output the output product used.  saved (training): receives the
+    intermediates for hstu_layer_bwd(..., mx=True)."""
     T = x.shape[0]
     B = seq_offsets.shape[0] - 1
     if y is None:
@@ -417,8 +421,10 @@ def hstu_layer_fwd_mx(x, wm: MxLayerWeights, rab_pos, rab_time, seq_offsets, tim
     m = wm.c()
     pair = lambda p: (None, None) if p is None else (_ptr(p[0]), _ptr(p[1]))
     io = MxIO(*pair(x_mx), *pair(y_mx), *pair(g_out))
+    sv = saved.c() if saved is not None else None
     st = L.hstu_layer_fwd_mx(C.byref(d), _ptr(x), C.byref(w), C.byref(m), _ptr(seq_offsets),
                              _ptr(timestamps), _ptr(num_candidates), _ptr(y), C.byref(io),
+                             C.byref(sv) if sv is not None else None,
                              _ptr(ws), ws.numel(), _stream(stream))
     check("hstu_layer_fwd_mx", st)
     return y

@@ -753,9 +753,11 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
   la.mu = mu;
   la.rstd = rstd;
   if (mx) {
-    // G straight to MXFP8 for the output product
+    // G straight to MXFP8 for the output product; the bf16 G only when the
+    // call keeps the intermediates for training
     la.g_codes = mx->g8;
     la.g_scales = mx->gs;
+    if (!mu) la.G = nullptr;
   }
   { HSTU_TIMED(TT_LN_FWD, st); HSTU_TRY(launch_ln_gate_fwd(la, d->dtype, st)); }
   // 4. Y = G W2 (+ b2) (+ X)
@@ -1059,10 +1061,15 @@ size_t hstu_layer_fwd_mx_workspace_size(const hstu_layer_desc* L) {
 
 hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
                               const hstu_mx_weights* wm, const int32_t* offs, const int64_t* ts,
-                              const int32_t* nc, void* y, const hstu_mx_io* io, void* ws,
-                              size_t ws_bytes, void* stream) {
+                              const int32_t* nc, void* y, const hstu_mx_io* io,
+                              const hstu_layer_saved* saved, void* ws, size_t ws_bytes,
+                              void* stream) {
   hstu_status s = check_mx_layer(L);
   if (s != HSTU_OK) return s;
+  // saved (training): every buffer, as hstu_layer_fwd's
+  if (saved && !(saved->Z && saved->Zh && saved->O && saved->G && saved->mu && saved->rstd &&
+                 aligned16(saved->Z) && aligned16(saved->Zh) && aligned16(saved->G)))
+    return HSTU_ERR_INVALID_ARG;
   const hstu_attn_desc* d = &L->attn;
   if (!w || !w->rab_pos || !w->rab_time || !offs || !ws || !wm || !wm->W1 || !wm->W1_scales ||
       !wm->W2 || !wm->W2_scales)
@@ -1119,6 +1126,15 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
   if (io && io->y_codes) {
     plan.y8 = static_cast<uint8_t*>(io->y_codes);
     plan.ys = static_cast<uint8_t*>(io->y_scales);
+  }
+  if (saved) {
+    float* So = static_cast<float*>(saved->O);
+    auto attention_s = [&](const void* q, const void* k, const void* v, int64_t ld) {
+      return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, So, W,
+                           /*out_f32=*/true, lw.attn, st);
+    };
+    return layer_fwd_steps(L, x, w, y, saved->Z, saved->Zh, So, saved->G, saved->mu,
+                           saved->rstd, attention_s, st, &plan);
   }
   return layer_fwd_steps(L, x, w, y, nullptr, lw.Zh, O, lw.G, nullptr, nullptr, attention, st,
                          &plan);
@@ -1213,11 +1229,45 @@ hstu_status hstu_layer_fwd_cached(const hstu_layer_desc* L, const void* x,
   return layer_fwd_steps(L, x, w, y, nullptr, lw.Zh, O, lw.G, nullptr, nullptr, attention, st);
 }
 
-hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
+// MXFP8 operands of the training backward's two activation-gradient
+// products: dY and W2 along d_model (dG = dY W2^T), dZ and W1 along F1
+// (dX = dZ W1^T); codes [rows][K], scales [rows][K/32]
+struct MxBwdWs {
+  uint8_t *dy8 = nullptr, *dys = nullptr, *dz8 = nullptr, *dzs = nullptr;
+  uint8_t *w28 = nullptr, *w2s = nullptr, *w18 = nullptr, *w1s = nullptr;
+};
+MxBwdWs carve_mx_bwd(Carver& c, const hstu_layer_desc* L) {
+  const hstu_attn_desc* d = &L->attn;
+  const int64_t T = std::max<int64_t>(d->T, 1), D = L->D, W = (int64_t)d->H * d->d_v;
+  const int64_t F1 = f1_width(L);
+  MxBwdWs m;
+  m.dy8 = c.take<uint8_t>(T * D);
+  m.dys = c.take<uint8_t>(T * D / 32);
+  m.dz8 = c.take<uint8_t>(T * F1);
+  m.dzs = c.take<uint8_t>(T * F1 / 32);
+  m.w28 = c.take<uint8_t>(W * D);
+  m.w2s = c.take<uint8_t>(W * D / 32);
+  m.w18 = c.take<uint8_t>(D * F1);
+  m.w1s = c.take<uint8_t>(D * F1 / 32);
+  return m;
+}
+
+hstu_status check_mx_train(const hstu_layer_desc* L) {
+  hstu_status s = check_layer(L);
+  if (s != HSTU_OK) return s;
+  const int64_t W = (int64_t)L->attn.H * L->attn.d_v;
+  if (L->attn.dtype != HSTU_BF16 || L->D % 128 != 0 || W % 128 != 0 || f1_width(L) % 128 != 0)
+    return HSTU_ERR_UNSUPPORTED;
+  return HSTU_OK;
+}
+
+// The layer backward; mx: dG and dX as MXFP8 products (hstu_layer_bwd_mx)
+hstu_status layer_bwd_impl(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
                            const int32_t* offs, const int64_t* ts, const int32_t* nc,
                            const hstu_layer_saved* saved, const void* dy, void* dx,
-                           const hstu_layer_grads* g, void* ws, size_t ws_bytes, void* stream) {
-  hstu_status s = check_layer(L);
+                           const hstu_layer_grads* g, void* ws, size_t ws_bytes, void* stream,
+                           bool mx) {
+  hstu_status s = mx ? check_mx_train(L) : check_layer(L);
   if (s != HSTU_OK) return s;
   const hstu_attn_desc* d = &L->attn;
   if (d->dtype != HSTU_BF16) return HSTU_ERR_UNSUPPORTED;
@@ -1234,12 +1284,15 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
       !aligned16(w->W2) || !aligned16(saved->Z) || !aligned16(saved->Zh) ||
       !aligned16(saved->O) || !aligned16(saved->G) || !aligned16(ws))
     return HSTU_ERR_INVALID_ARG;
-  if (ws_bytes < hstu_layer_bwd_workspace_size(L)) return HSTU_ERR_WORKSPACE;
+  if (ws_bytes < (mx ? hstu_layer_bwd_mx_workspace_size(L) : hstu_layer_bwd_workspace_size(L)))
+    return HSTU_ERR_WORKSPACE;
   plans_forget(ws, ws_bytes);
   hipStream_t st = entry_stream(stream);
 
   Carver c(ws);
   LayerBwdWs bw = carve_layer_bwd(c, L);
+  MxBwdWs mb;
+  if (mx) mb = carve_mx_bwd(c, L);
   const int64_t T = d->T, D = L->D, F1 = f1_width(L);
   const int64_t W = (int64_t)d->H * d->d_v, HQ = (int64_t)d->H * d->d_qk;
   const size_t es = esize(d->dtype);
@@ -1270,6 +1323,17 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a1.B = w->W2; a1.ldb = D; a1.b_kcont = true;
   a1.C = bw.dG; a1.ldc = W;
   a1.epi = EPI_STORE;
+  if (mx) {
+    {
+      HSTU_TIMED(TT_MX_QUANT, st);
+      HSTU_TRY(launch_mx_quant_rows(dy, D, T, D, mb.dy8, mb.dys, st));
+      HSTU_TRY(launch_mx_quant_rows(w->W2, D, W, D, mb.w28, mb.w2s, st));
+    }
+    a1.mx = true;
+    a1.A = mb.dy8; a1.lda = D / 2; a1.K = D / 2;
+    a1.B = mb.w28; a1.ldb = D / 2;
+    a1.scale_a = mb.dys; a1.scale_b = mb.w2s;
+  }
   { HSTU_TIMED(TT_GEMM_DG, st); HSTU_TRY(launch_gemm(a1, d->dtype, st)); }
   // 2. dW2 = G^T dY (split over T)
   GemmArgs a2;
@@ -1331,9 +1395,43 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_l
   a4.C = dx; a4.ldc = D;
   a4.epi = EPI_RESID;
   a4.R = L->residual ? dy : nullptr; a4.ldr = D;
+  if (mx) {
+    {
+      HSTU_TIMED(TT_MX_QUANT, st);
+      HSTU_TRY(launch_mx_quant_rows(dz, F1, T, F1, mb.dz8, mb.dzs, st));
+      HSTU_TRY(launch_mx_quant_rows(w->W1, F1, D, F1, mb.w18, mb.w1s, st));
+    }
+    a4.mx = true;
+    a4.A = mb.dz8; a4.lda = F1 / 2; a4.K = F1 / 2;
+    a4.B = mb.w18; a4.ldb = F1 / 2;
+    a4.scale_a = mb.dzs; a4.scale_b = mb.w1s;
+  }
   { HSTU_TIMED(TT_GEMM_DX, st); HSTU_TRY(launch_gemm(a4, d->dtype, st)); }
   HSTU_TRY(side.join());
   return HSTU_OK;
+}
+
+hstu_status hstu_layer_bwd(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
+                           const int32_t* offs, const int64_t* ts, const int32_t* nc,
+                           const hstu_layer_saved* saved, const void* dy, void* dx,
+                           const hstu_layer_grads* g, void* ws, size_t ws_bytes, void* stream) {
+  return layer_bwd_impl(L, x, w, offs, ts, nc, saved, dy, dx, g, ws, ws_bytes, stream, false);
+}
+
+size_t hstu_layer_bwd_mx_workspace_size(const hstu_layer_desc* L) {
+  if (check_mx_train(L) != HSTU_OK) return 0;
+  Carver c(nullptr);
+  carve_layer_bwd(c, L);
+  carve_mx_bwd(c, L);
+  return c.off + 256;
+}
+
+hstu_status hstu_layer_bwd_mx(const hstu_layer_desc* L, const void* x,
+                              const hstu_layer_weights* w, const int32_t* offs, const int64_t* ts,
+                              const int32_t* nc, const hstu_layer_saved* saved, const void* dy,
+                              void* dx, const hstu_layer_grads* g, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return layer_bwd_impl(L, x, w, offs, ts, nc, saved, dy, dx, g, ws, ws_bytes, stream, true);
 }
 
 size_t hstu_schedule_workspace_size(int32_t B, int64_t T, int32_t block_rows) {

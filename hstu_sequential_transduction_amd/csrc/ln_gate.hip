@@ -160,6 +160,8 @@ __global__ __launch_bounds__(256) void k_ln_gate_fwd(LnArgs a) {
             reinterpret_cast<u32x4*>(dst)[q] = u32x4{cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]};
         }
         if (lane % LPB == 0) a.g_scales[rr[k] * (W / 32) + c0 / 32] = (uint8_t)(sh + 127);
+        // training keeps the bf16 G as well (the backward's dW2 = G^T dY)
+        if (G) store_row<EPL, VEC>(G + rr[k] * a.ld_g, c0, W, gv);
       } else {
         store_row<EPL, VEC>(G + rr[k] * a.ld_g, c0, W, gv);
       }

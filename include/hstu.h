@@ -347,12 +347,15 @@ hstu_status hstu_mx_gemm(int64_t M, int64_t N, int64_t K, const void* a, const v
                          const void* b, const void* b_scales, float* c, int64_t ldc,
                          void* stream);
 /*
- * Inference forward of one layer with MXFP8 projection and output products
- * (X and the gated LayerNorm G are quantized on the fly; attention,
- * LayerNorm and gating in bf16 / fp32 as in hstu_layer_fwd).  `w` supplies
- * the biases, LayerNorm affine and bias tables (its W1, W2 are not read);
- * `wm` the MXFP8 weights; `io` (may be NULL) the optional MXFP8 inputs and
- * outputs below.  bf16 only, D and H*d_v multiples of 128.
+ * Forward of one layer with MXFP8 projection and output products
+ * ("Bending the Scaling Law Curve in Large-Scale Recommendation Systems",
+ * Mixed precision: the matrix products in FP8; X and the gated LayerNorm G
+ * are quantized on the fly; attention, LayerNorm and gating in bf16 / fp32
+ * as in hstu_layer_fwd).  `w` supplies the biases, LayerNorm affine and bias
+ * tables (its W1, W2 are not read); `wm` the MXFP8 weights; `io` (may be
+ * NULL) the optional MXFP8 inputs and outputs below; `saved` (may be NULL;
+ * all six buffers, as for hstu_layer_fwd) keeps the intermediates for
+ * hstu_layer_bwd_mx.  bf16 only, D and H*d_v multiples of 128.
  */
 typedef struct {
   /* x already in MXFP8 ([T][D] codes, [T][D/32] scales): skips its
@@ -371,6 +374,27 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* desc, const void* x,
                               const hstu_layer_weights* w, const hstu_mx_weights* wm,
                               const int32_t* seq_offsets, const int64_t* timestamps,
                               const int32_t* num_candidates, void* y, const hstu_mx_io* io,
+                              const hstu_layer_saved* saved,
+                              void* workspace, size_t workspace_bytes, void* stream);
+/*
+ * Training backward of hstu_layer_fwd_mx (same arguments as hstu_layer_bwd;
+ * `saved` from hstu_layer_fwd_mx).  The two products that carry the
+ * activation gradients back are MXFP8 products, each operand quantized
+ * along its own contraction as in the forward: dG = dY W2^T (dY and W2 in
+ * blocks of 32 along d_model) and dX = dZ W1^T (+ dY) (dZ and W1 in blocks
+ * along F1); the weight gradients dW1 = X^T dZ and dW2 = G^T dY, the
+ * attention and LayerNorm backward stay bf16 / fp32; the forward's
+ * quantizers count as the identity in the chain rule.  The weights' MXFP8
+ * copies are made inside the call from w->W1 and w->W2.  bf16 only; D,
+ * H*d_v and F1 multiples of 128, else HSTU_ERR_UNSUPPORTED.
+ */
+size_t hstu_layer_bwd_mx_workspace_size(const hstu_layer_desc* desc);
+hstu_status hstu_layer_bwd_mx(const hstu_layer_desc* desc, const void* x,
+                              const hstu_layer_weights* w,
+                              const int32_t* seq_offsets, const int64_t* timestamps,
+                              const int32_t* num_candidates,
+                              const hstu_layer_saved* saved, const void* dy, void* dx,
+                              const hstu_layer_grads* grads,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- ranking against a cached history --------------------------------- */

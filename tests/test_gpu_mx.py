@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 import synth
+from tests.test_oracle_mx import _mx_err_bound
 from oracle import hstu as orc
 from tests.gpu_util import check_close, dev, host, say, torch_dtype
 
@@ -213,3 +214,82 @@ def test_mx_layer_chain_hands_y_codes_to_the_next_layer(B):
     plain = B.hstu_layer_fwd_mx(y1, ws[1][2], ws[1][0], ws[1][1], offs, ts, lc,
                                 num_candidates=nc)
     np.testing.assert_array_equal(host(chained), host(plain))
+
+
+TRAIN_CASES = [
+    (4, [300, 1100, 129], 0, "unit", 0),
+    (4, [300, 1100, 129], 0, "unit", 1100),     # dQ from the kept dS
+    (4, [300, 1100, 129], 0, "literal", 0),
+    (5, [100, 300, 0, 64], 40, "unit", 0),
+]
+
+
+@pytest.mark.parametrize("ci,hist,c,variant,max_len", TRAIN_CASES)
+def test_mx_layer_train_step(B, ci, hist, c, variant, max_len):
+    """MXFP8 training step (hstu_layer_fwd_mx keeping its intermediates,
+    then hstu_layer_bwd_mx) against the oracle's MX forward and backward:
+    every gradient to the bf16 tolerance.  Only the quantization of dZ can
+    round differently on the two sides (the GPU's dZ carries bf16 rounding);
+    dY, X and the weights are inputs, quantized identically.  The distance of
+    dX from the exact backward is reported."""
+    import torch
+    cfg = synth.get_config(ci).shrunk(B=len(hist), lengths=("list", hist), num_candidates=c,
+                                      n_layers=1)
+    if variant == "unit":
+        cfg = cfg.unit_scale()
+    say(f"mx train cfg{ci} {variant} lengths={hist} c={c} max_len={max_len}")
+    inp = synth.make_inputs(cfg, seed=1800 + ci)
+    w = inp.layers[0]
+    td = torch.bfloat16
+    T = inp.T
+    dY = inp.dY
+    if dY is None:
+        dY = synth.bf16_round(np.random.default_rng(1900 + ci).standard_normal((T, cfg.D)))
+    X, W1, W2 = dev(inp.X, td), dev(w.W1, td), dev(w.W2, td)
+    rp, rt = dev(w.rab_pos), dev(w.rab_time)
+    offs, ts = dev(inp.seq_offsets.astype(np.int32)), dev(inp.timestamps)
+    nc = None if inp.num_candidates is None else dev(inp.num_candidates.astype(np.int32))
+    lc = _lcfg(B, cfg)
+    lc.attn.max_len = max_len
+    wm = B.MxLayerWeights.from_bf16(W1, W2)
+    saved = B.Saved(T, lc, td, "cuda")
+    y = B.hstu_layer_fwd_mx(X, wm, rp, rt, offs, ts, lc, num_candidates=nc, saved=saved)
+    dx, g = B.hstu_layer_bwd(X, W1, W2, rp, rt, offs, ts, lc, saved, dev(dY, td),
+                             num_candidates=nc, mx=True)
+    f = orc.LayerFlags(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len, eps=1e-6)
+    Yo, sv = orc.layer_fwd_mx(inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                              inp.timestamps, inp.num_candidates, f, return_saved=True)
+    want = orc.layer_bwd_mx(dY, inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                            inp.timestamps, inp.num_candidates, f, sv)
+    # the training forward: G codes may round differently from the oracle's
+    # (see test_mx_layer_fwd), so Y is compared in norm; its bf16 G exactly
+    # as the oracle's within the bf16 tolerance
+    ref = inp.X if variant == "unit" else 0.0
+    rel_y = np.linalg.norm((host(y) - ref) - (Yo - ref)) / np.linalg.norm(Yo - ref)
+    assert rel_y < 2e-2, rel_y
+    check_close(host(saved.G), sv["G"], "bf16", "G kept for the backward")
+    # dX = MX(dZ) MX(W1^T) (+ dY): the GPU's dZ carries bf16 rounding, so its
+    # codes, and a block's scale near a power of two, may round differently
+    # from the oracle's.  Element by element, dX must lie within the MXFP8
+    # rounding bound of the exact product of the oracle's dZ (the block
+    # scale allowed one binade higher) plus the bf16 tolerance; in norm, it
+    # must match the oracle's MX backward to the bf16 tolerance.
+    a, b = want["dZ"], np.asarray(w.W1, np.float64).T
+    ea, eb = 2.0 * _mx_err_bound(a, axis=1), _mx_err_bound(b, axis=0)
+    bound = ea @ np.abs(b) + np.abs(a) @ eb + ea @ eb
+    ex_dx = a @ b + dY
+    slack = 2e-2 * np.abs(ex_dx) + 2e-2 * np.abs(ex_dx).max()
+    err = np.abs(host(dx) - ex_dx)
+    assert np.all(err <= bound + slack), f"dX outside the MXFP8 bound: {(err - bound - slack).max()}"
+    rel_dx = np.linalg.norm(host(dx) - want["dX"]) / np.linalg.norm(want["dX"])
+    assert rel_dx < 2e-2, rel_dx
+    for k in ("dW1", "dW2", "drab_pos", "drab_time"):
+        check_close(host(getattr(g, k)), want[k], "bf16", k)
+    _, sx = orc.layer_fwd(inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                          inp.timestamps, inp.num_candidates, f)
+    ex = orc.layer_bwd(dY, inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                       inp.timestamps, inp.num_candidates, f, sx)
+    rel = {k: float(np.linalg.norm(host(v) - ex[k]) / np.linalg.norm(ex[k]))
+           for k, v in (("dX", dx), ("dW1", g.dW1), ("dW2", g.dW2))}
+    say(f"  relative L2 vs the exact backward: " +
+        ", ".join(f"{k} {v:.4f}" for k, v in rel.items()))
