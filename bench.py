@@ -525,13 +525,16 @@ def roofline(cfg, inp, kern, steps, traffic_dir):
     table = {}
     for name, (n, ms) in kern.items():
         per = ms / max(n, 1)
-        entry = {"launches_per_step": n / max(steps, 1), "ms_per_launch": round(per, 5)}
+        # a tag's work is per step (a product may run as several launches)
+        per_step = ms / max(steps, 1)
+        entry = {"launches_per_step": n / max(steps, 1), "ms_per_launch": round(per, 5),
+                 "ms_per_step": round(per_step, 5)}
         if name in work:
             kind, amt = work[name]
             if kind == "mfma":
-                entry["tflops"] = round(amt / (per * 1e-3) / 1e12, 2)
+                entry["tflops"] = round(amt / (per_step * 1e-3) / 1e12, 2)
             else:
-                entry["gbs"] = round(amt / (per * 1e-3) / 1e9, 1)
+                entry["gbs"] = round(amt / (per_step * 1e-3) / 1e9, 1)
         table[name] = entry
     ms, name, n = best
     kind, amt = work[name]
