@@ -86,6 +86,29 @@ HSTU_DEV void store_row(T* row, int c0, int W, const float* x) {
   }
 }
 
+// A lane's chunk of a row kept as loaded (16-byte words), for loads issued
+// ahead of their use: unpacking to fp32 would make the load complete first.
+template <int EPL, typename T>
+struct RawChunk {
+  static constexpr int NQ = EPL * (int)sizeof(T) / 16;
+  u32x4 w[NQ];
+};
+template <int EPL, typename T>
+HSTU_DEV void load_raw(const T* row, int c0, RawChunk<EPL, T>& r) {
+#pragma unroll
+  for (int q = 0; q < RawChunk<EPL, T>::NQ; ++q)
+    r.w[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(row + c0) + 16 * q);
+}
+template <int EPL, typename T>
+HSTU_DEV void unpack_raw(const RawChunk<EPL, T>& r, float* x) {
+  constexpr bool BF = sizeof(T) == 2;
+#pragma unroll
+  for (int q = 0; q < RawChunk<EPL, T>::NQ; ++q) {
+    const uint32_t w[4] = {r.w[q][0], r.w[q][1], r.w[q][2], r.w[q][3]};
+    unpack4(w, x + q * (BF ? 8 : 4), 4, BF);
+  }
+}
+
 template <int EPL, bool VEC, typename T, typename TO, bool MXO = false>
 __global__ __launch_bounds__(256) void k_ln_gate_fwd(LnArgs a) {
   const int lane = threadIdx.x & 63;
@@ -194,26 +217,15 @@ __global__ __launch_bounds__(256) void k_ln_gate_bwd(LnArgs a) {
     pg[e] = 0.0f;
     pb[e] = 0.0f;
   }
-  // two adjacent rows per wave and iteration (as in the forward)
+  // Two adjacent rows per wave and iteration (as in the forward).
   const int64_t step = (int64_t)gridDim.x * 4;
-  for (int64_t r0 = 2 * ((int64_t)blockIdx.x * 4 + wave); r0 < a.T; r0 += 2 * step) {
-    const int64_t rr[2] = {r0, r0 + 1};
-    float x[2][EPL], u[2][EPL], dg[2][EPL], z[2][EPL];
-    float mean[2] = {0.f, 0.f}, rstd[2] = {0.f, 0.f};
+  auto process = [&](const float (&x)[2][EPL], const float (&u)[2][EPL], const float (&dg)[2][EPL],
+                     const float (&z)[2][EPL], const float (&mean)[2], const float (&rstd)[2],
+                     int64_t r0) HSTU_INLINE_LAMBDA {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      if (rr[k] < a.T) {
-        load_row<EPL, VEC>(O + rr[k] * a.ld_o, c0, W, x[k]);
-        load_row<EPL, VEC>(U + rr[k] * a.ld_u, c0, W, u[k]);
-        load_row<EPL, VEC>(dG + rr[k] * a.ld_dg, c0, W, dg[k]);
-        if (zu) load_row<EPL, VEC>(zu + rr[k] * a.ld_zu, c0, W, z[k]);
-        mean[k] = a.mu[rr[k]];
-        rstd[k] = a.rstd[rr[k]];
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      if (rr[k] >= a.T) break;
+      const int64_t r = r0 + k;
+      if (r >= a.T) break;
       float xh[EPL], dxh[EPL], du[EPL];
       float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
@@ -236,8 +248,73 @@ __global__ __launch_bounds__(256) void k_ln_gate_bwd(LnArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) du[e] *= silu_grad_f(z[k][e]);
       }
-      store_row<EPL, VEC>(dU + rr[k] * a.ld_du, c0, W, du);
-      store_row<EPL, VEC>(dO + rr[k] * a.ld_do, c0, W, dx);
+      store_row<EPL, VEC>(dU + r * a.ld_du, c0, W, du);
+      store_row<EPL, VEC>(dO + r * a.ld_do, c0, W, dx);
+    }
+  };
+  int64_t r0 = 2 * ((int64_t)blockIdx.x * 4 + wave);
+  constexpr bool RAW = VEC && EPL <= 8 && (EPL * sizeof(T)) % 16 == 0 &&
+                       (EPL * sizeof(TO)) % 16 == 0;
+  if constexpr (RAW) {
+    // The next iteration's rows are loaded, as raw 16-byte words, before the
+    // current ones are computed (register sets A and B in turn), so a wave
+    // always has loads in flight while it computes and stores.
+    struct Raw {
+      RawChunk<EPL, TO> x[2];
+      RawChunk<EPL, T> u[2], dg[2], z[2];
+      float mean[2], rstd[2];
+    };
+    auto load = [&](Raw& R, int64_t rb) HSTU_INLINE_LAMBDA {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        // rows past the end repeat the last row (loaded, never used)
+        const int64_t r = rb + k < a.T ? rb + k : a.T - 1;
+        load_raw<EPL, TO>(O + r * a.ld_o, c0, R.x[k]);
+        load_raw<EPL, T>(U + r * a.ld_u, c0, R.u[k]);
+        load_raw<EPL, T>(dG + r * a.ld_dg, c0, R.dg[k]);
+        if (zu) load_raw<EPL, T>(zu + r * a.ld_zu, c0, R.z[k]);
+        R.mean[k] = a.mu[r];
+        R.rstd[k] = a.rstd[r];
+      }
+    };
+    auto run = [&](const Raw& R, int64_t rb) HSTU_INLINE_LAMBDA {
+      float x[2][EPL], u[2][EPL], dg[2][EPL], z[2][EPL];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        unpack_raw<EPL, TO>(R.x[k], x[k]);
+        unpack_raw<EPL, T>(R.u[k], u[k]);
+        unpack_raw<EPL, T>(R.dg[k], dg[k]);
+        if (zu) unpack_raw<EPL, T>(R.z[k], z[k]);
+      }
+      process(x, u, dg, z, R.mean, R.rstd, rb);
+    };
+    Raw A, B;
+    if (r0 < a.T) load(A, r0);
+    while (r0 < a.T) {
+      if (r0 + 2 * step < a.T) load(B, r0 + 2 * step);
+      run(A, r0);
+      r0 += 2 * step;
+      if (r0 >= a.T) break;
+      if (r0 + 2 * step < a.T) load(A, r0 + 2 * step);
+      run(B, r0);
+      r0 += 2 * step;
+    }
+  } else {
+    for (; r0 < a.T; r0 += 2 * step) {
+      float x[2][EPL], u[2][EPL], dg[2][EPL], z[2][EPL];
+      float mean[2] = {0.f, 0.f}, rstd[2] = {0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (r0 + k < a.T) {
+          load_row<EPL, VEC>(O + (r0 + k) * a.ld_o, c0, W, x[k]);
+          load_row<EPL, VEC>(U + (r0 + k) * a.ld_u, c0, W, u[k]);
+          load_row<EPL, VEC>(dG + (r0 + k) * a.ld_dg, c0, W, dg[k]);
+          if (zu) load_row<EPL, VEC>(zu + (r0 + k) * a.ld_zu, c0, W, z[k]);
+          mean[k] = a.mu[r0 + k];
+          rstd[k] = a.rstd[r0 + k];
+        }
+      }
+      process(x, u, dg, z, mean, rstd, r0);
     }
   }
   if (a.dgamma_part || a.dbeta_part) {
