@@ -598,15 +598,21 @@ def bench_fwd_configs(timer, configs=(2, 3, 5), reps=20):
         st = time_region(run, reps, 2)
         kern, _ = instrumented(run, timer, reps, 64 * cfg.n_layers)
         ms = st["ms_median"]
-        # the attention kernel with long blocks' keys split in up to 4 parts
-        # (not the default), for comparison
-        lc, lc_r = (dataclasses.replace(c, attn=dataclasses.replace(c.attn, key_splits=4))
-                    for c in (lc, lc_r))
-        ws1 = ws
-        ws = B.LayerWorkspace()
-        kern1, _ = instrumented(run, timer, reps, 64 * cfg.n_layers)
-        n_a1, ms_a1 = kern1.get("attn_fwd", (0, 0.0))
-        ws = ws1
+        # the attention kernel, for comparison, with long blocks' keys split
+        # in up to 4 workgroups, and with 128-row work items only (key_splits
+        # 1; the default takes 64-row items whose key tiles two waves share
+        # when the 128-row items would not fill the GPU)
+        lc0, lc_r0, ws0 = lc, lc_r, ws
+        alt = {}
+        for ks in (4, 1):
+            lc, lc_r = (dataclasses.replace(c, attn=dataclasses.replace(c.attn, key_splits=ks))
+                        for c in (lc0, lc_r0))
+            ws = B.LayerWorkspace()
+            kern1, _ = instrumented(run, timer, reps, 64 * cfg.n_layers)
+            alt[ks] = kern1.get("attn_fwd", (0, 0.0))
+        lc, lc_r, ws = lc0, lc_r0, ws0
+        n_a1, ms_a1 = alt[4]
+        n_a2, ms_a2 = alt[1]
         lf = flops.layer_flops(inp.lengths, inp.num_candidates, cfg.D, cfg.H, cfg.d_qk, cfg.d_v,
                                backward=False)
         tot = lf["total"] * cfg.n_layers
@@ -620,6 +626,7 @@ def bench_fwd_configs(timer, configs=(2, 3, 5), reps=20):
             "tokens_per_s": round(inp.T / (ms * 1e-3), 1),
             "attn_fwd_ms_per_layer": None if not n_a else round(ms_a / n_a, 5),
             "attn_fwd_ms_per_layer_key_splits_4": None if not n_a1 else round(ms_a1 / n_a1, 5),
+            "attn_fwd_ms_per_layer_128_row_items": None if not n_a2 else round(ms_a2 / n_a2, 5),
             "attn_fwd_tflops": None if a_tf is None else round(a_tf, 2),
             "attn_fwd_frac_bf16_peak": None if a_tf is None else round(a_tf / PEAK_BF16_TFLOPS, 4),
             "kernel_ms": {k: round(v[1] / reps, 4) for k, v in kern.items()},

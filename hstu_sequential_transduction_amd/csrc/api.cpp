@@ -162,9 +162,24 @@ int fwd_splits(const hstu_attn_desc* d) {
   return d->key_splits >= 2 ? d->key_splits : 1;
 }
 
+// Whether the forward runs 64-row work items with the key tiles shared by two
+// waves (bf16, no windows, key_splits 0): when even an upper bound on the
+// 128-row items (T/128 + B per head) leaves compute units without work, the
+// run is bound by the longest items' chains of key tiles, which this halves
+// (1-layer workload: 32 sequences of U[64,1024], 4 heads of 64: at most 660
+// items against 768 workgroup slots).  Decided from sizes alone, so a
+// planning call and a reuse_plan call agree.
+bool fwd_key_halves(const hstu_attn_desc* d) {
+  if (d->dtype != HSTU_BF16 || d->win_local > 0 || d->key_splits != 0) return false;
+  const int64_t items = (d->T + 127) / 128 + d->B;
+  const int64_t slots = 256 * (int64_t)attn_fwd_occupancy(d->d_qk, d->d_v);
+  return items * d->H <= slots;
+}
+
 struct FwdWs {
   TimeMeta tm;
   Sched sc;
+  bool kh = false;
   int splits = 1;
   float* part = nullptr;       // [cap * H][splits][block rows][d_v]
   int32_t* part_cnt = nullptr; // [cap * H] parts per work item (written by the kernel)
@@ -172,7 +187,8 @@ struct FwdWs {
 FwdWs carve_fwd(Carver& c, const hstu_attn_desc* d) {
   FwdWs w;
   w.tm = carve_time(c, d->T, d->B);
-  const int bm = attn_fwd_block_rows(d->dtype, d->d_qk, d->d_v);
+  w.kh = fwd_key_halves(d);
+  const int bm = attn_fwd_block_rows(d->dtype, d->d_qk, d->d_v, w.kh);
   w.sc = carve_sched(c, d->T, d->B, bm);
   w.splits = fwd_splits(d);
   if (w.splits > 1) {
@@ -184,8 +200,8 @@ FwdWs carve_fwd(Carver& c, const hstu_attn_desc* d) {
 
 // ---- plans left in workspaces (reuse_plan) ---------------------------------
 // A forward call that plans records what its plan depends on: the device, the
-// plan's bytes in the workspace, B, T, the row-block size (dtype and head
-// sizes) and the seq_offsets / timestamps buffers.  A later forward that sets
+// plan's bytes in the workspace, B, T, the row-block size (dtype, head
+// sizes and the key-half choice) and the seq_offsets / timestamps buffers.  A later forward that sets
 // reuse_plan must name the same workspace bytes and the same inputs, else it
 // is rejected before anything is launched.  Every other call that is handed
 // a workspace forgets the plans recorded in the bytes it may write.  The
@@ -196,7 +212,7 @@ FwdWs carve_fwd(Carver& c, const hstu_attn_desc* d) {
 struct PlanTag {
   int dev = -1;
   uintptr_t p0 = 0, p1 = 0;  // plan bytes [p0, p1)
-  int32_t B = 0, H = 0, d_qk = 0, d_v = 0, dtype = 0;
+  int32_t B = 0, H = 0, d_qk = 0, d_v = 0, dtype = 0, bm = 0;
   int64_t T = 0;
   const void* offs = nullptr;
   const void* ts = nullptr;
@@ -244,6 +260,7 @@ PlanTag plan_tag(const hstu_attn_desc* d, const void* ws, const int32_t* offs,
   t.d_qk = d->d_qk;
   t.d_v = d->d_v;
   t.dtype = d->dtype;
+  t.bm = attn_fwd_block_rows(d->dtype, d->d_qk, d->d_v, fwd_key_halves(d));
   t.T = d->T;
   t.offs = offs;
   t.ts = ts;
@@ -266,7 +283,7 @@ bool plan_recorded(const hstu_attn_desc* d, const void* ws, const int32_t* offs,
   for (const PlanTag& t : g_plan_tags)
     if (t.dev == q.dev && t.p0 == q.p0 && t.p1 == q.p1 && t.B == q.B && t.T == q.T &&
         t.H == q.H && t.d_qk == q.d_qk && t.d_v == q.d_v && t.dtype == q.dtype &&
-        t.offs == q.offs && t.ts == q.ts)
+        t.bm == q.bm && t.offs == q.offs && t.ts == q.ts)
       return true;
   return false;
 }
@@ -376,6 +393,7 @@ hstu_status attn_fwd_run(const hstu_attn_desc* d, const void* q, const void* k, 
   a.splits = w.splits;
   a.part = w.part;
   a.part_cnt = w.part_cnt;
+  a.key_halves = w.kh ? 1 : 0;
   { HSTU_TIMED(TT_ATTN_FWD, st); HSTU_TRY(launch_attn_fwd(a, d->dtype, d->d_qk, d->d_v, w.sc.cap, st)); }
   return HSTU_OK;
 }

@@ -82,10 +82,16 @@ using mconst = std::integral_constant<int, V>;
 // item's visited key tiles are cut into np <= S contiguous runs of at least
 // four tiles.  With np = 1 the one part writes O; otherwise each part writes
 // its scaled partial sum of O to a.part and k_attn_fwd_combine adds them.
-template <int DQK, int DV, bool WIN, bool SPLIT>
+// KH (key halves): 64-row work items; waves 2r and 2r+1 share the rows of
+// group r and each takes one 32-key half of every tile (half the work per
+// tile, so the longest item's chain of tiles takes about half as long),
+// adding their partial sums of O through LDS at the end.  For batches whose
+// 128-row items do not fill the GPU.
+template <int DQK, int DV, bool WIN, bool SPLIT, bool KH = false>
 __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16(AttnArgs a) {
+  static_assert(!(KH && (SPLIT || WIN)), "key halves: no split, no windows");
   constexpr int QG = FwdShape<DQK, DV>::QG;
-  constexpr int BM = FwdShape<DQK, DV>::BM;
+  constexpr int BM = KH ? 64 : FwdShape<DQK, DV>::BM;
   __shared__ __attribute__((aligned(1024))) FwdBuf<DQK, DV> fwb0;
   __shared__ __attribute__((aligned(1024))) FwdBuf<DQK, DV> fwb1;
   __shared__ FwdTables sm;
@@ -96,7 +102,7 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
   // S-th of the XCDs
   const int S = SPLIT ? a.splits : 1;
   const int nwi = SPLIT ? (int)(gridDim.x / (unsigned)S) : 0;
-  const int part = SPLIT ? (int)(blockIdx.x / (unsigned)nwi) : 0;
+  const int part = SPLIT ? (int)(blockIdx.x / (unsigned)max(nwi, 1)) : 0;
   const int wi = SPLIT ? (int)blockIdx.x - part * nwi : (int)blockIdx.x;
   const int n_items = a.counters[0];
   if (wi >= n_items * a.H) return;
@@ -149,7 +155,9 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
 
   const int rb0 = m * BM;
   const int rb1 = min(rb0 + BM, n);
-  const int r0 = rb0 + wave * 32 * QG;
+  const int rg = KH ? (wave >> 1) : wave;  // row group of this wave
+  const int khalf = KH ? (wave & 1) : 0;   // its key half of every tile (KH)
+  const int r0 = rb0 + rg * 32 * QG;
   const int rw1 = min(r0 + 32 * QG, n);
 
   const bf16* qbase = reinterpret_cast<const bf16*>(a.q) + (int64_t)o0 * a.ld_qk + h * DQK;
@@ -273,6 +281,7 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
 
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
+        if (KH && hf != khalf) continue;
         f32x16 sacc[QG];
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) sacc[qg] = f32x16{};
@@ -425,6 +434,26 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
         }
       return;
     }
+  }
+
+  if constexpr (KH) {
+    // the key-half-1 wave of each row group hands its partial sum of O to the
+    // key-half-0 wave (the tile buffers are free after the loop's last barrier)
+    static_assert((DV / 32) * 16 * 64 * 4 <= (int)sizeof(FwdBuf<DQK, DV>), "exchange fits a tile buffer");
+    float* xo = reinterpret_cast<float*>(rg == 0 ? reinterpret_cast<uint8_t*>(&fwb0)
+                                                 : reinterpret_cast<uint8_t*>(&fwb1));
+    if (khalf == 1) {
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(d * 16 + r) * 64 + lane] = oacc[0][d][r];
+    }
+    __syncthreads();
+    if (khalf == 1) return;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[0][d][r] += xo[(d * 16 + r) * 64 + lane];
   }
 
   // ---- write O * (-ln2 / N) ----
@@ -621,8 +650,11 @@ hipError_t launch_fwd_t(const AttnArgs& a, int dtype, int64_t max_items, hipStre
   if (grid <= 0) return hipSuccess;
   if (dtype == HSTU_BF16) {
     if (a.splits > 1 && (a.win_local > 0 || !a.part || !a.part_cnt)) return hipErrorInvalidValue;
+    if (a.key_halves && (a.win_local > 0 || a.splits > 1)) return hipErrorInvalidValue;
     if (a.win_local > 0)
       k_attn_fwd_bf16<DQK, DV, true, false><<<(unsigned)grid, 256, 0, st>>>(a);
+    else if (a.key_halves)
+      k_attn_fwd_bf16<DQK, DV, false, false, true><<<(unsigned)grid, 256, 0, st>>>(a);
     else if (a.splits > 1) {
       k_attn_fwd_bf16<DQK, DV, false, true><<<(unsigned)(grid * a.splits), 256, 0, st>>>(a);
       constexpr int BM = FwdShape<DQK, DV>::BM;
@@ -647,11 +679,15 @@ hipError_t launch_fwd_dv(const AttnArgs& a, int dtype, int d_v, int64_t mi, hipS
 
 }  // namespace
 
-int attn_fwd_block_rows(int dtype, int d_qk, int d_v) {
+int attn_fwd_block_rows(int dtype, int d_qk, int d_v, bool key_halves) {
   if (dtype != HSTU_BF16) return ATTN_FWD_BM_F32;
   (void)d_qk;
   (void)d_v;
-  return FwdShape<64, 64>::BM;  // the same for every head size
+  return key_halves ? 64 : FwdShape<64, 64>::BM;  // the same for every head size
+}
+
+int attn_fwd_occupancy(int d_qk, int d_v) {
+  return (d_qk <= 64 && d_v <= 64) ? FwdShape<64, 64>::OCC : FwdShape<128, 128>::OCC;
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, int d_qk, int d_v, int64_t max_items,

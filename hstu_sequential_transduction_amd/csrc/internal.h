@@ -130,6 +130,9 @@ struct AttnArgs {
   int splits = 1;
   float* part = nullptr;
   int32_t* part_cnt = nullptr;
+  // forward: 64-row work items whose key tiles two waves share (1), or
+  // 128-row items (0); the plan's block rows must match
+  int key_halves = 0;
   // backward with dS kept: 128 x 128 bf16 blocks (key-major) of the causal
   // part, per sequence and head; ds_base[b] = first block of sequence b;
   // *ds_flag != 0: the blocks did not fit, dQ is recomputed instead
@@ -159,7 +162,9 @@ constexpr int ATTN_BWD_BM = 128;   // queries per dQ work item
 
 // Query rows per forward work item for a head size (bf16 kernels use 32 or 64
 // rows per wave; fp32 uses 64 rows per workgroup).
-int attn_fwd_block_rows(int dtype, int d_qk, int d_v);
+int attn_fwd_block_rows(int dtype, int d_qk, int d_v, bool key_halves = false);
+// forward attention workgroups one compute unit holds (bf16)
+int attn_fwd_occupancy(int d_qk, int d_v);
 hipError_t launch_attn_fwd(const AttnArgs& a, int dtype, int d_qk, int d_v,
                            int64_t max_items, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv(const AttnArgs& a, int d_qk, int d_v, int64_t max_items,

@@ -128,14 +128,17 @@ typedef struct {
    * backward and cached-history calls, which always plan. */
   int32_t reuse_plan;
   /* Forward (bf16, no semi-local windows): split the keys of long query
-   * blocks over several workgroups whose partial sums add (no softmax, so
-   * the parts add exactly up to rounding order), meant for batches too small
-   * to fill the GPU.  0: library default (currently no split: it measured
-   * slower on every workload tried); 1: never; 2..8: split every query
-   * block into up to this many runs of at least 4 key tiles of 64; the
+   * blocks so that partial sums add (no softmax, so the parts add exactly up
+   * to rounding order), meant for batches too small to fill the GPU.
+   * 0: library default: when even an upper bound on the work items of
+   * 128 query rows (T/128 + B per head) fits the GPU's workgroup slots at
+   * once, 64-row items whose 64-key tiles two waves share, each adding half
+   * of every tile's keys (their partial sums meet in LDS); otherwise no
+   * split.  1: never split.  2..8: split every query block into up to this
+   * many runs of at least 4 key tiles of 64 over separate workgroups; the
    * parts write fp32 partial sums to the workspace and a second kernel adds
-   * them.  Other values: HSTU_ERR_INVALID_ARG.  The workspace size depends
-   * on it. */
+   * them (measured slower on every workload tried).  Other values:
+   * HSTU_ERR_INVALID_ARG.  The workspace size depends on it. */
   int32_t key_splits;
 } hstu_attn_desc;
 

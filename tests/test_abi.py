@@ -54,9 +54,22 @@ def test_workspace_sizes_grow_with_T(L):
     a = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=1)))
     b = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=100000, key_splits=1)))
     assert 0 < a < b
-    # split keys keep partial sums of [block rows x d_v] per part and work item;
-    # the default is not to split
-    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000))) == a
+    # the default (key_splits 0) plans 64-row work items (twice the list) when
+    # even T/128 + B items per head fit the GPU at once, 128-row ones otherwise
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000))) > a
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=100000))) == b
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, win_local=64))) == a
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, dtype=0))) == \
+        L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=1, dtype=0)))
+    # the workloads: 32 x U[64,1024] with 4 heads of 64 takes the 64-row items,
+    # the 8-layer Zipf batch (64 sequences, 8 heads) does not
+    c2 = dict(B=32, T=17016, H=4, d_qk=64, d_v=64)
+    c3 = dict(B=64, T=34485, H=8, d_qk=64, d_v=64)
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(**c2))) > \
+        L.hstu_attn_fwd_workspace_size(C.byref(_desc(key_splits=1, **c2)))
+    assert L.hstu_attn_fwd_workspace_size(C.byref(_desc(**c3))) == \
+        L.hstu_attn_fwd_workspace_size(C.byref(_desc(key_splits=1, **c3)))
+    # split keys keep partial sums of [block rows x d_v] per part and work item
     s4 = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=4)))
     s2 = L.hstu_attn_fwd_workspace_size(C.byref(_desc(T=1000, key_splits=2)))
     assert a < s2 < s4

@@ -56,28 +56,34 @@ SMALL = {
 }
 
 
+# key_splits 0: the library default, which for these small bf16 batches runs
+# 64-row work items whose key tiles two waves share; 1: 128-row items
+@pytest.mark.parametrize("ks", [0, 1])
 @pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
-def test_attn_fwd_small(B, ci):
+def test_attn_fwd_small(B, ci, ks):
     base = synth.get_config(ci)
     hist = SMALL[ci]
     cfg = base.shrunk(B=len(hist), lengths=("list", hist))
-    say(f"attn fwd small cfg{ci} lengths={hist} c={cfg.num_candidates}")
+    say(f"attn fwd small cfg{ci} key_splits={ks} lengths={hist} c={cfg.num_candidates}")
     a = synth.make_attn_inputs(cfg, seed=100 + ci)
     ac = _cfgobj(B, cfg)
+    ac.key_splits = ks
     got = _fwd(B, a, cfg, ac)
     want = orc.attn_fwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
                         a.num_candidates, 0, cfg.norm_len)
     check_close(got, want, cfg.dtype, f"O cfg{ci}")
 
 
+@pytest.mark.parametrize("ks", [0, 1])
 @pytest.mark.parametrize("ci", [2, 3, 4, 5])
-def test_attn_fwd_literal_scale(B, ci):
+def test_attn_fwd_literal_scale(B, ci, ks):
     """Small q, k and rab tables of std 0.02 as in the workloads' literal scales."""
     base = synth.get_config(ci)
     hist = SMALL[ci]
     cfg = base.shrunk(B=len(hist), lengths=("list", hist))
     a = synth.make_attn_inputs(cfg, seed=200 + ci, qk_std=0.15, rab_std=0.02)
     ac = _cfgobj(B, cfg)
+    ac.key_splits = ks
     got = _fwd(B, a, cfg, ac)
     want = orc.attn_fwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
                         a.num_candidates, 0, cfg.norm_len)
@@ -97,10 +103,12 @@ def test_attn_fwd_norm_mode_1_and_shared_tables(B):
     check_close(got, want, "bf16", "O norm_mode=1 shared")
 
 
-def test_attn_fwd_all_candidates_and_edge_sequences(B):
+@pytest.mark.parametrize("ks", [0, 1])
+def test_attn_fwd_all_candidates_and_edge_sequences(B, ks):
     cfg = synth.get_config(5).shrunk(B=4, lengths=("list", [0, 1, 127, 128]), num_candidates=3)
     a = synth.make_attn_inputs(cfg, seed=8)
     ac = _cfgobj(B, cfg)
+    ac.key_splits = ks
     got = _fwd(B, a, cfg, ac)
     want = orc.attn_fwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
                         a.num_candidates, 0, cfg.norm_len)
@@ -117,11 +125,13 @@ def test_attn_fwd_unsorted_and_wide_timestamps(B):
     ts[o[0]:o[1]] = ts[o[0]] + rng.integers(-5000, 5000, size=150)          # unsorted
     ts[o[1]:o[2]] = np.sort(rng.integers(0, 1 << 40, size=90))               # wide span
     a = dataclasses.replace(a, timestamps=ts)
-    ac = _cfgobj(B, cfg)
-    got = _fwd(B, a, cfg, ac)
-    want = orc.attn_fwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
-                        None, 0, cfg.norm_len)
-    check_close(got, want, "bf16", "O unsorted/wide")
+    for ks in (0, 1):
+        ac = _cfgobj(B, cfg)
+        ac.key_splits = ks
+        got = _fwd(B, a, cfg, ac)
+        want = orc.attn_fwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
+                            None, 0, cfg.norm_len)
+        check_close(got, want, "bf16", f"O unsorted/wide key_splits={ks}")
 
 
 SPLIT_CASES = {
