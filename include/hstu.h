@@ -114,7 +114,8 @@ typedef struct {
    * hstu_layer_fwd_mx): 1 asks to skip the plan (time pre-pass and work
    * list) because the workspace already holds the plan an earlier forward
    * call on the same batch wrote, e.g. the previous layer of a stack run
-   * with one workspace.  The plan depends on B, T, dtype, d_qk, d_v and the
+   * with one workspace.  The plan depends on B, T, H, dtype, d_qk, d_v,
+   * key_splits and win_local (which fix its work-item rows) and the
    * contents of seq_offsets and timestamps.  The library records, per device,
    * every plan a forward call writes (its bytes in the workspace, those
    * sizes and the offsets and timestamps pointers) and forgets the plans in
