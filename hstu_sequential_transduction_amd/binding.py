@@ -255,7 +255,7 @@ def hstu_layer_bwd(x, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, cfg: L
                    beta=None, dx=None, grads: Optional[Grads] = None,
                    workspace: Optional[LayerWorkspace] = None, stream=None, mx: bool = False):
     """(dx, Grads) of the layer for the output gradient dy.  mx: the backward
-    of hstu_layer_fwd_mx (hstu_layer_bwd_mx: dG and dX as MXFP8 products)."""
+    of hstu_layer_fwd_mx (hstu_layer_bwd_mx: dG, dX, dW2 and dW1 as MXFP8 products)."""
     T = x.shape[0]
     B = seq_offsets.shape[0] - 1
     dev = x.device

@@ -74,7 +74,7 @@ hipStream_t entry_stream(void* stream) {
 // created, that work stays on the caller's stream.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t ev[4] = {};
+  hipEvent_t ev[5] = {};
   int state = 0;  // 0 untried, 1 ready, -1 unavailable
 };
 SideStream* side_stream() {
@@ -87,7 +87,7 @@ SideStream* side_stream() {
   SideStream& sd = sides[dev];
   if (sd.state == 0) {
     bool ok = hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess;
-    for (int i = 0; ok && i < 4; ++i)
+    for (int i = 0; ok && i < 5; ++i)
       ok = hipEventCreateWithFlags(&sd.ev[i], hipEventDisableTiming) == hipSuccess;
     sd.state = ok ? 1 : -1;
     (void)hipGetLastError();
@@ -1250,9 +1250,16 @@ hstu_status hstu_layer_fwd_cached(const hstu_layer_desc* L, const void* x,
 // MXFP8 operands of the training backward's two activation-gradient
 // products: dY and W2 along d_model (dG = dY W2^T), dZ and W1 along F1
 // (dX = dZ W1^T); codes [rows][K], scales [rows][K/32]
+// MXFP8 operands of the training backward: dY, dZ and the weights along the
+// activation products' contractions (d_model, F1), and G^T, dY^T, X^T, dZ^T
+// along the tokens for the weight gradients (Tp = T rounded up to 128, the
+// extra tokens zero).
 struct MxBwdWs {
   uint8_t *dy8 = nullptr, *dys = nullptr, *dz8 = nullptr, *dzs = nullptr;
   uint8_t *w28 = nullptr, *w2s = nullptr, *w18 = nullptr, *w1s = nullptr;
+  uint8_t *gt8 = nullptr, *gts = nullptr, *dyt8 = nullptr, *dyts = nullptr;
+  uint8_t *xt8 = nullptr, *xts = nullptr, *dzt8 = nullptr, *dzts = nullptr;
+  int64_t Tp = 0;
 };
 MxBwdWs carve_mx_bwd(Carver& c, const hstu_layer_desc* L) {
   const hstu_attn_desc* d = &L->attn;
@@ -1267,6 +1274,15 @@ MxBwdWs carve_mx_bwd(Carver& c, const hstu_layer_desc* L) {
   m.w2s = c.take<uint8_t>(W * D / 32);
   m.w18 = c.take<uint8_t>(D * F1);
   m.w1s = c.take<uint8_t>(D * F1 / 32);
+  m.Tp = (T + 127) / 128 * 128;
+  m.gt8 = c.take<uint8_t>(W * m.Tp);
+  m.gts = c.take<uint8_t>(W * m.Tp / 32);
+  m.dyt8 = c.take<uint8_t>(D * m.Tp);
+  m.dyts = c.take<uint8_t>(D * m.Tp / 32);
+  m.xt8 = c.take<uint8_t>(D * m.Tp);
+  m.xts = c.take<uint8_t>(D * m.Tp / 32);
+  m.dzt8 = c.take<uint8_t>(F1 * m.Tp);
+  m.dzts = c.take<uint8_t>(F1 * m.Tp / 32);
   return m;
 }
 
@@ -1279,7 +1295,7 @@ hstu_status check_mx_train(const hstu_layer_desc* L) {
   return HSTU_OK;
 }
 
-// The layer backward; mx: dG and dX as MXFP8 products (hstu_layer_bwd_mx)
+// The layer backward; mx: dG, dX, dW2 and dW1 as MXFP8 products (hstu_layer_bwd_mx)
 hstu_status layer_bwd_impl(const hstu_layer_desc* L, const void* x, const hstu_layer_weights* w,
                            const int32_t* offs, const int64_t* ts, const int32_t* nc,
                            const hstu_layer_saved* saved, const void* dy, void* dx,
@@ -1343,10 +1359,12 @@ hstu_status layer_bwd_impl(const hstu_layer_desc* L, const void* x, const hstu_l
   a1.epi = EPI_STORE;
   if (mx) {
     {
+      // dY along d_model for dG and along the tokens for dW2, one read
       HSTU_TIMED(TT_MX_QUANT, st);
-      HSTU_TRY(launch_mx_quant_rows(dy, D, T, D, mb.dy8, mb.dys, st));
+      HSTU_TRY(launch_mx_quant_both(dy, D, T, D, mb.Tp, mb.dyt8, mb.dyts, mb.dy8, mb.dys, st));
       HSTU_TRY(launch_mx_quant_rows(w->W2, D, W, D, mb.w28, mb.w2s, st));
     }
+    if (sd) HSTU_TRY(hipEventRecord(sd->ev[4], st));
     a1.mx = true;
     a1.A = mb.dy8; a1.lda = D / 2; a1.K = D / 2;
     a1.B = mb.w28; a1.ldb = D / 2;
@@ -1359,6 +1377,21 @@ hstu_status layer_bwd_impl(const hstu_layer_desc* L, const void* x, const hstu_l
   a2.A = saved->G; a2.lda = W; a2.a_kcont = false;
   a2.B = dy; a2.ldb = D; a2.b_kcont = false;
   a2.epi = EPI_PARTIAL; a2.split_k = bw.s2; a2.partial = bw.part2;
+  if (mx) {
+    // G^T along the tokens (X^T too: it is ready now); dY^T comes from the
+    // caller's stream
+    {
+      HSTU_TIMED(TT_MX_QUANT, ss);
+      HSTU_TRY(launch_mx_quant_rows_t(saved->G, W, T, W, mb.Tp, mb.gt8, mb.gts, ss));
+      HSTU_TRY(launch_mx_quant_rows_t(x, D, T, D, mb.Tp, mb.xt8, mb.xts, ss));
+    }
+    if (sd) HSTU_TRY(hipStreamWaitEvent(ss, sd->ev[4], 0));
+    a2.mx = true;
+    a2.K = mb.Tp / 2;
+    a2.A = mb.gt8; a2.lda = mb.Tp / 2; a2.a_kcont = true;
+    a2.B = mb.dyt8; a2.ldb = mb.Tp / 2; a2.b_kcont = true;
+    a2.scale_a = mb.gts; a2.scale_b = mb.dyts; a2.scale_kstep_major = true;
+  }
   { HSTU_TIMED(TT_GEMM_DW2, ss); HSTU_TRY(launch_gemm(a2, d->dtype, ss)); }
   {
     HSTU_TIMED(TT_REDUCE, ss);
@@ -1398,7 +1431,20 @@ hstu_status layer_bwd_impl(const hstu_layer_desc* L, const void* x, const hstu_l
   a3.A = x; a3.lda = D; a3.a_kcont = false;
   a3.B = dz; a3.ldb = F1; a3.b_kcont = false;
   a3.epi = EPI_PARTIAL; a3.split_k = bw.s1; a3.partial = bw.part1;
+  if (mx) {
+    // dZ along F1 for dX and along the tokens for dW1, one read
+    HSTU_TIMED(TT_MX_QUANT, st);
+    HSTU_TRY(launch_mx_quant_both(dz, F1, T, F1, mb.Tp, mb.dzt8, mb.dzts, mb.dz8, mb.dzs, st));
+    HSTU_TRY(launch_mx_quant_rows(w->W1, F1, D, F1, mb.w18, mb.w1s, st));
+  }
   if (sd) HSTU_TRY(order_after(ss, st, sd->ev[2]));
+  if (mx) {
+    a3.mx = true;
+    a3.K = mb.Tp / 2;
+    a3.A = mb.xt8; a3.lda = mb.Tp / 2; a3.a_kcont = true;
+    a3.B = mb.dzt8; a3.ldb = mb.Tp / 2; a3.b_kcont = true;
+    a3.scale_a = mb.xts; a3.scale_b = mb.dzts; a3.scale_kstep_major = true;
+  }
   { HSTU_TIMED(TT_GEMM_DW1, ss); HSTU_TRY(launch_gemm(a3, d->dtype, ss)); }
   {
     HSTU_TIMED(TT_REDUCE, ss);
@@ -1414,11 +1460,6 @@ hstu_status layer_bwd_impl(const hstu_layer_desc* L, const void* x, const hstu_l
   a4.epi = EPI_RESID;
   a4.R = L->residual ? dy : nullptr; a4.ldr = D;
   if (mx) {
-    {
-      HSTU_TIMED(TT_MX_QUANT, st);
-      HSTU_TRY(launch_mx_quant_rows(dz, F1, T, F1, mb.dz8, mb.dzs, st));
-      HSTU_TRY(launch_mx_quant_rows(w->W1, F1, D, F1, mb.w18, mb.w1s, st));
-    }
     a4.mx = true;
     a4.A = mb.dz8; a4.lda = F1 / 2; a4.K = F1 / 2;
     a4.B = mb.w18; a4.ldb = F1 / 2;

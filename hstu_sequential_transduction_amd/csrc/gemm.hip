@@ -524,32 +524,40 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
 
   // MXFP8: per k-step (128 codes = four MX blocks) each lane needs the scales
   // of its rows' blocks g and 2 + g: one 32-bit word of four scale bytes per
-  // row, shifted so that bytes 0 and 2 are the two blocks (MFMA op_sel)
+  // row, kept as loaded and shifted at use so that bytes 0 and 2 are the two
+  // blocks (MFMA op_sel); the shift at use also lets the loads of the next
+  // k-step's words stay in flight under the current step's MFMAs.
   G2OffMX amx, bmx;
-  uint32_t sa[FM], sb[FN];
   const int64_t kblk = g.K / 16;  // MX blocks per row (K counts pairs of codes)
   if constexpr (MX) {
     amx.init(wm * 32 * FM, lane);
     bmx.init(wn * 32 * FN, lane);
   }
-  auto load_scales = [&](int64_t k0) HSTU_INLINE_LAMBDA {
-    const int64_t b0 = k0 / 16;
+  // word of row r at k-step k0: [rows][K/32] (four adjacent bytes of the
+  // row) or k-step-major [K/128][rows][4]
+  auto scale_word = [&](const uint8_t* sc, int64_t rows, int64_t r, int64_t k0) HSTU_INLINE_LAMBDA {
+    const int64_t off = g.scale_kstep_major ? ((k0 / G2_BK) * rows + r) * 4 : r * kblk + k0 / 16;
+    return *reinterpret_cast<const uint32_t*>(sc + off);
+  };
+  auto load_scales = [&](int64_t k0, uint32_t (&wa)[FM], uint32_t (&wb)[FN]) HSTU_INLINE_LAMBDA {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int64_t r = m0 + wm * 32 * FM + 32 * i + ql;
-      const uint32_t wd = r < g.M ? *reinterpret_cast<const uint32_t*>(g.scale_a + r * kblk + b0)
-                                  : 0x7F7F7F7Fu;
-      sa[i] = wd >> (8 * gq);
+      wa[i] = r < g.M ? scale_word(g.scale_a, g.M, r, k0) : 0x7F7F7F7Fu;
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t r = n0 + wn * 32 * FN + 32 * j + ql;
-      const uint32_t wd = r < g.N ? *reinterpret_cast<const uint32_t*>(g.scale_b + r * kblk + b0)
-                                  : 0x7F7F7F7Fu;
-      sb[j] = wd >> (8 * gq);
+      wb[j] = r < g.N ? scale_word(g.scale_b, g.N, r, k0) : 0x7F7F7F7Fu;
     }
   };
-  auto compute_mx = [&](const uint8_t* ta, const uint8_t* tb) HSTU_INLINE_LAMBDA {
+  auto compute_mx = [&](const uint8_t* ta, const uint8_t* tb, const uint32_t (&wa)[FM],
+                        const uint32_t (&wb)[FN]) HSTU_INLINE_LAMBDA {
+    int sa[FM], sb[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa[i] = (int)(wa[i] >> (8 * gq));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sb[j] = (int)(wb[j] >> (8 * gq));
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       i32x8 af[FM], bfr[FN];
@@ -563,10 +571,10 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
         for (int j = 0; j < FN; ++j) {
           if (kh == 0)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[i], bfr[j], acc[i][j], 0, 0, 0, (int)sa[i], 0, (int)sb[j]);
+                af[i], bfr[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
           else
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[i], bfr[j], acc[i][j], 0, 0, 2, (int)sa[i], 2, (int)sb[j]);
+                af[i], bfr[j], acc[i][j], 0, 0, 2, sa[i], 2, sb[j]);
         }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -577,29 +585,38 @@ __global__ __launch_bounds__(64 * G2_NW, (G2Shape<BM, BN, NST>::WPC)) void k_gem
   // make the register allocator shuffle the accumulators)
   // k-steps of this split (an empty last split has kend < kbeg)
   const int nks = kend > kbeg ? (int)((kend - kbeg + G2_BK - 1) / G2_BK) : 0;
+  uint32_t wa0[FM] = {}, wb0[FN] = {}, wa1[FM] = {}, wb1[FN] = {};
+  auto step = [&](const uint8_t* ta, const uint8_t* tb, const uint32_t (&wa)[FM],
+                  const uint32_t (&wb)[FN]) HSTU_INLINE_LAMBDA {
+    if constexpr (MX) compute_mx(ta, tb, wa, wb);
+    else compute(ta, tb);
+  };
+  auto issue_s = [&](uint8_t* ta, uint8_t* tb, int64_t k0, uint32_t (&wa)[FM],
+                     uint32_t (&wb)[FN]) HSTU_INLINE_LAMBDA {
+    issue(ta, tb, k0);
+    if constexpr (MX) load_scales(k0, wa, wb);
+  };
   if constexpr (NST == 2) {
-    if (nks > 0) issue(a0, b0, kbeg);
+    if (nks > 0) issue_s(a0, b0, kbeg, wa0, wb0);
     dma_wait();
     __syncthreads();
     for (int ks = 0; ks + 1 < nks; ks += 2) {
-      issue(a1, b1, kbeg + (int64_t)(ks + 1) * G2_BK);
-      compute(a0, b0);
+      issue_s(a1, b1, kbeg + (int64_t)(ks + 1) * G2_BK, wa1, wb1);
+      step(a0, b0, wa0, wb0);
       dma_wait();
       __syncthreads();
-      if (ks + 2 < nks) issue(a0, b0, kbeg + (int64_t)(ks + 2) * G2_BK);
-      compute(a1, b1);
+      if (ks + 2 < nks) issue_s(a0, b0, kbeg + (int64_t)(ks + 2) * G2_BK, wa0, wb0);
+      step(a1, b1, wa1, wb1);
       dma_wait();
       __syncthreads();
     }
-    if (nks & 1) compute(a0, b0);
+    if (nks & 1) step(a0, b0, wa0, wb0);
   } else {
     for (int ks = 0; ks < nks; ++ks) {
-      issue(a0, b0, kbeg + (int64_t)ks * G2_BK);
-      if constexpr (MX) load_scales(kbeg + (int64_t)ks * G2_BK);
+      issue_s(a0, b0, kbeg + (int64_t)ks * G2_BK, wa0, wb0);
       dma_wait();
       __syncthreads();
-      if constexpr (MX) compute_mx(a0, b0);
-      else compute(a0, b0);
+      step(a0, b0, wa0, wb0);
       __syncthreads();
     }
   }
@@ -864,7 +881,17 @@ hipError_t gemm2_mx(const GemmArgs& g, hipStream_t st) {
   const int mt = (int)((g.M + BM - 1) / BM), nt = (int)((g.N + BN - 1) / BN);
   const int slots = (mt * nt + 7) / 8;
   dim3 grid((unsigned)(8 * slots), 1);
+  if (g.epi == EPI_PARTIAL) {
+    // split-K (the weight gradients, contracted over the tokens): the same
+    // grid as the bf16 split-K products
+    if (g.split_k < 1) return hipErrorInvalidValue;
+    grid = g.split_k % 8 == 0 ? dim3((unsigned)(g.split_k * mt * nt), 1)
+                              : dim3((unsigned)(8 * slots), (unsigned)g.split_k);
+  }
   switch (g.epi) {
+    case EPI_PARTIAL:  // long k: two stages, as the bf16 split-K products
+      k_gemm2_bf16<BM, BN, true, true, EPI_PARTIAL, true, 2, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);
+      break;
     case EPI_STORE:
       if (g.c_f32)
         k_gemm2_bf16<BM, BN, true, true, EPI_STORE, true, 1, true><<<grid, NT, 0, st>>>(g, mt, nt, slots);

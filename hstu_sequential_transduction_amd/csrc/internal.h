@@ -210,6 +210,10 @@ struct GemmArgs {
   bool mx = false;
   const uint8_t* scale_a = nullptr;
   const uint8_t* scale_b = nullptr;
+  // scales laid out k-step-major instead: [K/128 codes][rows][4], the four
+  // blocks of one k-step of a row in one word and consecutive rows' words
+  // adjacent (long contractions, e.g. over the tokens)
+  bool scale_kstep_major = false;
   // MX kernels, EPI_RESID with bf16 C: also write C as MXFP8 along N
   // (codes [M][N], scales [M][N/32]; N a multiple of 32)
   uint8_t* c_codes = nullptr;
@@ -299,6 +303,16 @@ hipError_t launch_attn_cached(const CachedArgs& a, int dtype, int d_qk, int d_v,
 // MXFP8 quantization (blocks of 32 along the contraction, k-contiguous output)
 hipError_t launch_mx_quant_rows(const void* x, int64_t ld, int64_t rows, int64_t K,
                                 uint8_t* codes, uint8_t* scales, hipStream_t st);
+// MXFP8 of x^T: x [T][C] (row stride ld) -> codes [C][Tp] and k-step-major
+// scales [Tp/128][C][4], blocks of 32 rows, rows T..Tp-1 as zeros
+// (C % 64 == 0, Tp % 128 == 0)
+hipError_t launch_mx_quant_rows_t(const void* x, int64_t ld, int64_t T, int64_t C, int64_t Tp,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t st);
+// both at once from one read of x: the transposed codes and scales above and
+// the row-wise ones of launch_mx_quant_rows (rcodes [T][C], rscales [T][C/32])
+hipError_t launch_mx_quant_both(const void* x, int64_t ld, int64_t T, int64_t C, int64_t Tp,
+                                uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
+                                uint8_t* rscales, hipStream_t st);
 hipError_t launch_mx_quant_cols(const void* w, int64_t K, int64_t N, uint8_t* codes,
                                 uint8_t* scales, hipStream_t st);
 

@@ -66,6 +66,64 @@ __global__ __launch_bounds__(256) void k_mx_quant(const bf16* __restrict__ in, i
   }
 }
 
+// Transposed quantization for products contracted over the rows of a
+// row-major matrix (the weight gradients, contracted over the tokens):
+// in [T][C] (row stride ld) -> codes [C][Tp], blocks of 32 rows of one
+// column, rows T..Tp-1 read as zeros (Tp a multiple of 128), and the scales
+// k-step-major, [Tp/128][C][4]: the MX GEMM's k-step covers 128 codes, so a
+// row's four scales of one step are one word and a wave's rows read
+// adjacent words (with [C][Tp/32] every row's word would sit on its own
+// cache line).  A workgroup stages a 128-row x 64-column tile in LDS with
+// 16-byte row loads, then each thread encodes one column's block of 32 rows.
+// With rcodes (ROWS): the same tile also encoded along its rows, codes
+// [T][C] and scales [T][C/32] (the layout of k_mx_quant), so that a matrix
+// needed in both orientations is read once.
+template <bool ROWS>
+__global__ __launch_bounds__(256) void k_mx_quant_t(const bf16* __restrict__ in, int64_t ld,
+                                                    int64_t T, int64_t C, int64_t Tp,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales,
+                                                    uint8_t* __restrict__ rcodes,
+                                                    uint8_t* __restrict__ rscales) {
+  __shared__ bf16 tile[128][64 + 8];  // padded rows: column reads stay off one bank
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 128, c0 = (int64_t)blockIdx.y * 64;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = tid / 8 + 32 * k, ch = tid % 8;
+    bf16x8 v{};
+    if (t0 + r < T) v = *reinterpret_cast<const bf16x8*>(in + (t0 + r) * ld + c0 + 8 * ch);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[r][8 * ch + e] = v[e];
+  }
+  __syncthreads();
+  if constexpr (ROWS) {
+    // one block of 32 columns of one row per thread
+    const int r = tid / 2, hb = tid % 2;
+    if (t0 + r < T) {
+      float v[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) v[e] = bf2f(tile[r][32 * hb + e]);
+      uint32_t out[8];
+      const int sc = mx_block(v, out);
+      u32x4* dst = reinterpret_cast<u32x4*>(rcodes + (t0 + r) * C + c0 + 32 * hb);
+      dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+      dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+      rscales[(t0 + r) * (C / 32) + c0 / 32 + hb] = (uint8_t)sc;
+    }
+  }
+  const int c = tid % 64, b = tid / 64;  // a wave: the 64 columns of one block of rows
+  float v[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e] = bf2f(tile[32 * b + e][c]);
+  uint32_t out[8];
+  const int sc = mx_block(v, out);
+  u32x4* dst = reinterpret_cast<u32x4*>(codes + (c0 + c) * Tp + t0 + 32 * b);
+  dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+  dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+  scales[((t0 / 128) * C + c0 + c) * 4 + b] = (uint8_t)sc;
+}
+
 int quant_grid(int64_t blocks) {
   const int64_t g = (blocks + 255) / 256;
   return (int)std::min<int64_t>(std::max<int64_t>(g, 1), 8192);
@@ -78,6 +136,30 @@ hipError_t launch_mx_quant_rows(const void* x, int64_t ld, int64_t rows, int64_t
   if (rows <= 0 || K <= 0) return hipSuccess;
   k_mx_quant<true><<<quant_grid(rows * K / 32), 256, 0, st>>>(
       static_cast<const bf16*>(x), ld, 1, rows, K, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_rows_t(const void* x, int64_t ld, int64_t T, int64_t C, int64_t Tp,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  if (C <= 0 || Tp <= 0) return hipSuccess;
+  if (C % 64 || Tp % 128 || Tp < T || ld < C || (ld % 8) ||
+      (reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(codes) & 15))
+    return hipErrorInvalidValue;
+  k_mx_quant_t<false><<<dim3((unsigned)(Tp / 128), (unsigned)(C / 64)), 256, 0, st>>>(
+      static_cast<const bf16*>(x), ld, T, C, Tp, codes, scales, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_both(const void* x, int64_t ld, int64_t T, int64_t C, int64_t Tp,
+                                uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
+                                uint8_t* rscales, hipStream_t st) {
+  if (C <= 0 || Tp <= 0) return hipSuccess;
+  if (C % 64 || Tp % 128 || Tp < T || ld < C || (ld % 8) ||
+      (reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(codes) & 15) ||
+      (reinterpret_cast<uintptr_t>(rcodes) & 15))
+    return hipErrorInvalidValue;
+  k_mx_quant_t<true><<<dim3((unsigned)(Tp / 128), (unsigned)(C / 64)), 256, 0, st>>>(
+      static_cast<const bf16*>(x), ld, T, C, Tp, codes, scales, rcodes, rscales);
   return hipGetLastError();
 }
 

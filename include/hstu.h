@@ -382,15 +382,20 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* desc, const void* x,
                               void* workspace, size_t workspace_bytes, void* stream);
 /*
  * Training backward of hstu_layer_fwd_mx (same arguments as hstu_layer_bwd;
- * `saved` from hstu_layer_fwd_mx).  The two products that carry the
- * activation gradients back are MXFP8 products, each operand quantized
- * along its own contraction as in the forward: dG = dY W2^T (dY and W2 in
- * blocks of 32 along d_model) and dX = dZ W1^T (+ dY) (dZ and W1 in blocks
- * along F1); the weight gradients dW1 = X^T dZ and dW2 = G^T dY, the
+ * `saved` from hstu_layer_fwd_mx).  All four products of the backward are
+ * MXFP8 products ("Bending the Scaling Law Curve in Large-Scale
+ * Recommendation Systems", Mixed precision: the matrix products in FP8),
+ * each operand quantized along its own contraction as in the forward:
+ * dG = dY W2^T (dY and W2 in blocks of 32 along d_model), dX = dZ W1^T (+ dY)
+ * (dZ and W1 in blocks along F1), and the weight gradients dW2 = G^T dY and
+ * dW1 = X^T dZ (G, dY, X and dZ in blocks of 32 tokens, the last block of
+ * a token count that is not a multiple of 32 padded with zeros); the
  * attention and LayerNorm backward stay bf16 / fp32; the forward's
- * quantizers count as the identity in the chain rule.  The weights' MXFP8
- * copies are made inside the call from w->W1 and w->W2.  bf16 only; D,
- * H*d_v and F1 multiples of 128, else HSTU_ERR_UNSUPPORTED.
+ * quantizers count as the identity in the chain rule.  Every MXFP8 copy
+ * (the weights' too) is made inside the call.  bf16 only; D, H*d_v and F1
+ * multiples of 128, else HSTU_ERR_UNSUPPORTED.  The workspace holds the
+ * copies: (1 + 1/32)(3 D + 2 F1 + H*d_v) bytes per token (tokens rounded up
+ * to 128 for the transposed ones) and the weights' beyond hstu_layer_bwd's.
  */
 size_t hstu_layer_bwd_mx_workspace_size(const hstu_layer_desc* desc);
 hstu_status hstu_layer_bwd_mx(const hstu_layer_desc* desc, const void* x,

@@ -332,12 +332,15 @@ def layer_fwd(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candida
 
 def layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
               f: LayerFlags, saved: Dict, b1=None, b2=None, gamma=None, beta=None,
-              act_matmul=None):
+              act_matmul=None, wgt_matmul=None):
     """All gradients of one layer, by the chain rule written out (step 5).
     act_matmul (default: the exact product) computes the two products that
-    carry the activation gradients back, dG = dY W2^T and dX = dZ W1^T
-    (layer_bwd_mx passes the MXFP8 product)."""
+    carry the activation gradients back, dG = dY W2^T and dX = dZ W1^T;
+    wgt_matmul (default: exact) the two weight gradients dW2 = G^T dY and
+    dW1 = X^T dZ, contracted over the tokens (layer_bwd_mx passes the MXFP8
+    product for all four)."""
     mm = act_matmul if act_matmul is not None else (lambda a, b: a @ b)
+    wm = wgt_matmul if wgt_matmul is not None else (lambda a, b: a @ b)
     dY = np.asarray(dY, np.float64)
     X = np.asarray(X, np.float64)
     W1 = np.asarray(W1, np.float64); W2 = np.asarray(W2, np.float64)
@@ -345,7 +348,7 @@ def layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_can
     U, V, Q, K = split_uvqk(saved["Zh"], f)
     # Y = G W2 + b2 (+ X)
     dG = mm(dY, W2.T)
-    dW2 = saved["G"].T @ dY
+    dW2 = wm(saved["G"].T, dY)
     db2 = dY.sum(axis=0)
     # G = Yn * U
     dU = dG * saved["Yn"]
@@ -358,7 +361,7 @@ def layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_can
                                     win_local=f.win_local, win_global=f.win_global)
     dZh = np.concatenate([dU, dV.reshape(T, -1), dQ.reshape(T, -1), dK.reshape(T, -1)], axis=1)
     dZ = dZh * silu_grad(saved["Z"]) if f.proj_silu else dZh
-    dW1 = X.T @ dZ
+    dW1 = wm(X.T, dZ)
     db1 = dZ.sum(axis=0)
     dX = mm(dZ, W1.T)
     if f.residual:
@@ -616,7 +619,17 @@ def mx_dequantize(codes, scales, axis=-1):
 
 def mx_matmul(a, b):
     """a @ b with both operands rounded to MXFP8 along the contraction (a's
-    rows, b's columns), the products summed exactly."""
+    rows, b's columns), the products summed exactly.  A contraction whose
+    length is not a multiple of 32 ends in a short block, read as padded
+    with zeros (zeros change neither a block's largest magnitude nor the
+    product)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    k = a.shape[1]
+    kp = -(-k // MX_BLOCK) * MX_BLOCK
+    if kp != k:
+        a = np.pad(a, ((0, 0), (0, kp - k)))
+        b = np.pad(b, ((0, kp - k), (0, 0)))
     qa, sa = mx_quantize(a, axis=1)
     qb, sb = mx_quantize(b, axis=0)
     return mx_dequantize(qa, sa, axis=1) @ mx_dequantize(qb, sb, axis=0)
@@ -654,11 +667,13 @@ def layer_bwd_mx(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_
                  f: LayerFlags, saved: Dict, b1=None, b2=None, gamma=None, beta=None):
     """Gradients of layer_fwd_mx for training with FP8 matmuls ([ULTRA] "Mixed
     precision": the matrix products in FP8, the rest in BF16).  Reading:
-    the two products that carry the activation gradients back, dG = dY W2^T
-    and dX = dZ W1^T, are MXFP8 products, each operand rounded along its own
-    contraction (the forward's recipe); the weight gradients dW2 = G^T dY and
-    dW1 = X^T dZ stay exact here (bf16 on the device); the quantizers count
-    as the identity in the chain rule (the forward's rounding is not
+    all four products of the backward are MXFP8 products, each operand
+    rounded along its own contraction (the forward's recipe): dG = dY W2^T
+    and dX = dZ W1^T (blocks along D and along F1), and the weight gradients
+    dW2 = G^T dY and dW1 = X^T dZ (blocks of 32 tokens along the token
+    index, a short last block read as zero-padded); the quantizers count as
+    the identity in the chain rule (the forward's rounding is not
     differentiated).  `saved` from layer_fwd_mx(..., return_saved=True)."""
     return layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps,
-                     num_candidates, f, saved, b1, b2, gamma, beta, act_matmul=mx_matmul)
+                     num_candidates, f, saved, b1, b2, gamma, beta, act_matmul=mx_matmul,
+                     wgt_matmul=mx_matmul)

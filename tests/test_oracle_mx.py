@@ -188,16 +188,25 @@ def _mx_case(seed, representable=False):
     return X, W1, W2, dY, rp, rt, offs, ts, f
 
 
+def _pad_k(a, b):
+    """a [M, K], b [K, N] with K zero-padded to a multiple of 32."""
+    k = a.shape[1]
+    kp = -(-k // 32) * 32
+    return np.pad(a, ((0, 0), (0, kp - k))), np.pad(b, ((0, kp - k), (0, 0)))
+
+
 def test_mx_backward_products_within_the_rounding_bound():
-    """dG and dX of the MX backward differ from the exact products of the
-    same operands by at most the bound the per-element rounding allows:
+    """All four products of the MX backward differ from the exact products of
+    the same operands by at most the bound the per-element rounding allows:
     |MX(a) MX(b) - a b| <= sum_k e_a |b| + |a| e_b + e_a e_b, each operand
-    rounded along the contraction."""
+    rounded along the contraction (for the weight gradients the 22 tokens,
+    one short block)."""
     X, W1, W2, dY, rp, rt, offs, ts, f = _mx_case(21)
     _, sv = orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f, return_saved=True)
     g = orc.layer_bwd_mx(dY, X, W1, W2, rp, rt, offs, ts, None, f, sv)
 
     def check(a, b, got):
+        a, b = _pad_k(np.asarray(a, np.float64), np.asarray(b, np.float64))
         ea, eb = _mx_err_bound(a, axis=1), _mx_err_bound(b, axis=0)
         bound = ea @ np.abs(b) + np.abs(a) @ eb + ea @ eb
         assert np.all(np.abs(got - a @ b) <= bound * (1 + 1e-9) + 1e-300)
@@ -206,18 +215,46 @@ def test_mx_backward_products_within_the_rounding_bound():
 
     check(dY, W2.T, g["dG"])
     check(g["dZ"], W1.T, g["dX"] - dY)
+    check(sv["G"].T, dY, g["dW2"])
+    check(X.T, g["dZ"], g["dW1"])
+
+
+def test_mx_matmul_short_last_block():
+    """A contraction of 40: the second block holds 8 values.  It equals the
+    product of the operands zero-padded to 64 (the reading), is exact when
+    both operands lie on the MXFP8 grid of their padded blocks, and is not
+    the product with the short block dropped."""
+    rng = np.random.default_rng(31)
+    a = rng.standard_normal((5, 40))
+    b = rng.standard_normal((40, 6))
+    ap, bp = _pad_k(a, b)
+    qa, sa = orc.mx_quantize(ap, axis=1)
+    qb, sb = orc.mx_quantize(bp, axis=0)
+    want = orc.mx_dequantize(qa, sa, axis=1) @ orc.mx_dequantize(qb, sb, axis=0)
+    got = orc.mx_matmul(a, b)
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-300)
+    assert np.abs(got - orc.mx_matmul(a[:, :32], b[:32])).max() > 1e-3
+    ar = orc.mx_dequantize(qa, sa, axis=1)[:, :40]
+    br = orc.mx_dequantize(qb, sb, axis=0)[:40]
+    np.testing.assert_allclose(orc.mx_matmul(ar, br), ar @ br, rtol=1e-13, atol=1e-300)
 
 
 def test_mx_backward_exact_on_representable_operands():
     """With dY and W2 on the MXFP8 grid along D (the contraction of dG), dG is
-    the exact product; the weight gradients are the exact products of the
-    chain's operands."""
+    the exact product; with X and dY on the grid along the tokens as well,
+    the only rounding left in dW1 and dW2 is that of dZ and G."""
     X, W1, W2, dY, rp, rt, offs, ts, f = _mx_case(22, representable=True)
+    rng = np.random.default_rng(22)
     _, sv = orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f, return_saved=True)
     g = orc.layer_bwd_mx(dY, X, W1, W2, rp, rt, offs, ts, None, f, sv)
     np.testing.assert_allclose(g["dG"], dY @ W2.T, rtol=1e-13, atol=1e-300)
-    np.testing.assert_allclose(g["dW2"], sv["G"].T @ dY, rtol=1e-13, atol=1e-300)
-    np.testing.assert_allclose(g["dW1"], X.T @ g["dZ"], rtol=1e-13, atol=1e-300)
+    # tokens-axis grid: operands whose MXFP8 along the (padded) tokens is exact
+    Xt = _representable(rng, (32, X.shape[1]), axis=0)[:X.shape[0]]
+    dYt = _representable(rng, (32, dY.shape[1]), axis=0)[:dY.shape[0]]
+    Gq = orc.mx_quantize(np.pad(sv["G"], ((0, 32 - sv["G"].shape[0]), (0, 0))), axis=0)
+    Gr = orc.mx_dequantize(*Gq, axis=0)[:sv["G"].shape[0]]
+    np.testing.assert_allclose(orc.mx_matmul(Gr.T, dYt), Gr.T @ dYt, rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(orc.mx_matmul(Xt.T, dYt), Xt.T @ dYt, rtol=1e-13, atol=1e-300)
     # quantizing along the other axis would not be exact here
     q, s = orc.mx_quantize(W2.T, axis=1)
     assert np.abs(orc.mx_dequantize(q, s, axis=1) - W2.T).max() > 0
@@ -233,5 +270,9 @@ def test_mx_backward_close_to_the_exact_backward():
     for k in ("dX", "dW1", "dW2", "drab_pos", "drab_time"):
         rel = np.linalg.norm(g[k] - ex[k]) / np.linalg.norm(ex[k])
         assert rel < 0.1, (k, rel)
-    # the weight gradient of the output product uses the same operands
-    np.testing.assert_allclose(g["dW2"], ex["dW2"], rtol=1e-13)
+    # the output product's weight gradient: the same operands (G, dY) in both,
+    # so its difference is the MXFP8 rounding alone, within its bound
+    G, dYp = _pad_k(sv["G"].T, dY)
+    bound = _mx_err_bound(G, 1) @ np.abs(dYp) + np.abs(G) @ _mx_err_bound(dYp, 0) + \
+        _mx_err_bound(G, 1) @ _mx_err_bound(dYp, 0)
+    assert np.all(np.abs(g["dW2"] - ex["dW2"]) <= bound * (1 + 1e-9))
