@@ -77,10 +77,15 @@ def test_semilocal_bwd(B, ci, hist, c, wl, wg):
 
 
 def test_semilocal_wide_window_equals_full(B):
-    """A window covering every sequence gives the full causal result bit for bit."""
+    """A window covering every sequence gives the full causal result bit for
+    bit when both run 128-row work items (key_splits 1); the full pass's
+    default for this small batch, 64-row items whose two key halves are
+    added at the end, sums in another order and agrees to the tolerance."""
     cfg = synth.get_config(4).shrunk(B=2, lengths=("list", [500, 900]))
     a = synth.make_attn_inputs(cfg, seed=700)
-    ac = _cfgobj(B, cfg)
+    ac = dataclasses.replace(_cfgobj(B, cfg), key_splits=1)
     full = _fwd(B, a, cfg, ac)
     wide = _fwd(B, a, cfg, dataclasses.replace(ac, win_local=4096, win_global=7))
     assert np.array_equal(full, wide)
+    halves = _fwd(B, a, cfg, dataclasses.replace(ac, key_splits=0))
+    check_close(halves, full, "bf16", "key-half items vs 128-row items")
