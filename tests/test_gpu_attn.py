@@ -390,3 +390,29 @@ def test_attn_bwd_full_size_config4_sampled_sequence(B):
     torch.cuda.synchronize()
     check_close(got[3], tot_p, "bf16", "drab_pos additivity")
     check_close(got[4], tot_t, "bf16", "drab_time additivity")
+
+
+# Every (d_qk, d_v) the bf16 kernels instantiate, including mixed ones, with
+# candidates; forward with both item shapes (key_splits 0: 64-row key-half
+# items for this small batch; 1: 128-row items) and the backward.
+HEAD_SIZES = [(32, 32), (32, 128), (128, 32), (64, 128), (128, 64), (32, 64)]
+
+
+@pytest.mark.parametrize("dqk,dv", HEAD_SIZES)
+def test_attn_mixed_head_sizes(B, dqk, dv):
+    cfg = dataclasses.replace(synth.get_config(5), H=2, d_qk=dqk, d_v=dv)
+    hist = [70, 260, 1, 140]
+    cfg = cfg.shrunk(B=len(hist), lengths=("list", hist), num_candidates=9)
+    say(f"attn mixed head sizes d_qk={dqk} d_v={dv} lengths={hist} c=9")
+    a = synth.make_attn_inputs(cfg, seed=900 + dqk + dv)
+    want = orc.attn_fwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
+                        a.num_candidates, 0, cfg.norm_len)
+    for ks in (0, 1):
+        ac = _cfgobj(B, cfg)
+        ac.key_splits = ks
+        check_close(_fwd(B, a, cfg, ac), want, "bf16", f"O d=({dqk},{dv}) key_splits={ks}")
+    got = _bwd(B, a, cfg, _cfgobj(B, cfg))
+    want_b = orc.attn_bwd(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
+                          a.d_out, a.num_candidates, 0, cfg.norm_len)
+    for g, w, name in zip(got, want_b, ("dq", "dk", "dv", "drab_pos", "drab_time")):
+        check_close(g, w, "bf16", f"{name} d=({dqk},{dv})")
