@@ -64,7 +64,10 @@ What is computed (every array is float64; integer work is exact):
    values along the contraction share a power-of-two scale
    2^(floor(log2 amax) - 8) and are rounded to E4M3 (nearest, ties to even,
    saturating at 448); the product of two such operands is computed exactly
-   here.  Attention and everything else stay as above.
+   here.  Attention and everything else stay as above, except in
+   attn_fwd_mx, where the attention's score product q_i . k_j is an MXFP8
+   product too: q and k rounded along their contraction (the d_qk channels
+   of each head, in blocks of 32), the rest of step 2 unchanged.
 5. Backward: the chain rule of 1-4 written out by hand (no autograd).
 
 Readings where the pages are silent (each is a flag here):
@@ -677,3 +680,23 @@ def layer_bwd_mx(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_
     return layer_bwd(dY, X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps,
                      num_candidates, f, saved, b1, b2, gamma, beta, act_matmul=mx_matmul,
                      wgt_matmul=mx_matmul)
+
+
+def attn_fwd_mx(q, k, v, seq_offsets, timestamps, rab_pos, rab_time,
+                num_candidates=None, norm_mode=0, norm_len=1, return_rows=None):
+    """attn_fwd with the score product in MXFP8 ([ULTRA] "Mixed precision":
+    the matrix products in FP8).  q and k [T, H, d_qk] are rounded to MXFP8
+    along their contraction index, the d_qk channels of one head (d_qk a
+    multiple of 32: whole blocks per head), and their products summed
+    exactly; bias, SiLU, mask, normalisation and the product with v follow
+    attn_fwd unchanged.  Reading: of the attention's two products only the
+    score product q_i . k_j is taken in FP8 (v keeps the precision of the
+    rest of the layer)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    assert q.shape[2] % MX_BLOCK == 0
+    qc, qs = mx_quantize(q, axis=2)
+    kc, ks = mx_quantize(k, axis=2)
+    return attn_fwd(mx_dequantize(qc, qs, axis=2), mx_dequantize(kc, ks, axis=2), v,
+                    seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
+                    norm_mode, norm_len, return_rows=return_rows)

@@ -276,3 +276,104 @@ def test_mx_backward_close_to_the_exact_backward():
     bound = _mx_err_bound(G, 1) @ np.abs(dYp) + np.abs(G) @ _mx_err_bound(dYp, 0) + \
         _mx_err_bound(G, 1) @ _mx_err_bound(dYp, 0)
     assert np.all(np.abs(g["dW2"] - ex["dW2"]) <= bound * (1 + 1e-9))
+
+
+# ---- the attention's score product in MXFP8 (attn_fwd_mx) -------------------
+
+def _attn_mx_case(seed, representable=False, d=64):
+    rng = np.random.default_rng(seed)
+    H = 2
+    lengths, cands = [9, 1, 14, 6], [0, 0, 3, 6]
+    offs = np.concatenate([[0], np.cumsum(lengths)])
+    T = int(offs[-1])
+    ts = np.concatenate([1_600_000_000 + np.cumsum(rng.integers(0, 400, n)) for n in lengths])
+    if representable:
+        q = _representable(rng, (T, H, d), axis=2)
+        k = _representable(rng, (T, H, d), axis=2)
+    else:
+        # channels spread over binades so that blocks saturate and go subnormal
+        q = rng.standard_normal((T, H, d)) * np.exp2(rng.integers(-3, 3, (T, H, d))) / 4
+        k = rng.standard_normal((T, H, d)) * np.exp2(rng.integers(-3, 3, (T, H, d))) / 4
+    v = rng.standard_normal((T, H, d))
+    rp, rt = rng.standard_normal((H, 128)) * 0.1, rng.standard_normal((H, 128)) * 0.1
+    return q, k, v, offs, ts.astype(np.int64), rp, rt, np.array(cands, np.int32)
+
+
+def test_attn_mx_exact_on_representable_qk():
+    """Q and K already on the MXFP8 grid with their blocks along each head's
+    channels: the MX score product is the exact one, so attn_fwd_mx equals
+    attn_fwd (blocks taken along the tokens or across heads would round)."""
+    q, k, v, offs, ts, rp, rt, nc = _attn_mx_case(11, representable=True)
+    got = orc.attn_fwd_mx(q, k, v, offs, ts, rp, rt, nc, norm_len=16)
+    want = orc.attn_fwd(q, k, v, offs, ts, rp, rt, nc, norm_len=16)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_attn_mx_within_the_rounding_bound(d):
+    """|O_mx - O| per element stays within what the per-element MXFP8
+    rounding of q and k (blocks of 32 along each head's channels) allows,
+    written out pair by pair: |dS_ij| <= sum_c (eq|k| + |q|ek + eq ek), and
+    SiLU is Lipschitz with constant max|SiLU'| < 1.1, so
+    |dO_i| <= (1/N) sum_{j allowed} 1.1 |dS_ij| |v_j|.  The bound is not
+    vacuous: the rounding changes the output."""
+    q, k, v, offs, ts, rp, rt, nc = _attn_mx_case(12 + d, d=d)
+    N = 16
+    got = orc.attn_fwd_mx(q, k, v, offs, ts, rp, rt, nc, norm_len=N)
+    ex = orc.attn_fwd(q, k, v, offs, ts, rp, rt, nc, norm_len=N)
+    eq, ek = _mx_err_bound(q, axis=2), _mx_err_bound(k, axis=2)
+    T, H, _ = q.shape
+    bound = np.zeros_like(ex)
+    for b in range(len(offs) - 1):
+        o0, o1, c = int(offs[b]), int(offs[b + 1]), int(nc[b])
+        n, nh = o1 - o0, o1 - o0 - c
+        for i in range(n):
+            for j in range(n):
+                ok = j <= i if i < nh else (j < nh or j == i)
+                if not ok:
+                    continue
+                for h in range(H):
+                    qi, kj = q[o0 + i, h], k[o0 + j, h]
+                    ei, ej = eq[o0 + i, h], ek[o0 + j, h]
+                    ds = np.sum(ei * np.abs(kj) + np.abs(qi) * ej + ei * ej)
+                    bound[o0 + i, h] += 1.1 * ds * np.abs(v[o0 + j, h]) / N
+    assert np.all(np.abs(got - ex) <= bound * (1 + 1e-9) + 1e-300)
+    assert np.abs(got - ex).max() > 0.0
+
+
+def _round_block_by_search(vals):
+    """One 32-value block rounded to MXFP8 by a search over all 254 finite
+    E4M3 values (decoded from their fields): scale 2^(floor(log2 amax) - 8)
+    from math.frexp, each value clamped to +-448 scaled units and sent to the
+    nearest grid value, ties to the even code."""
+    import math
+    amax = max(abs(x) for x in vals)
+    if amax == 0.0:
+        return [0.0] * len(vals)
+    X = 2.0 ** (math.frexp(amax)[1] - 1 - 8)
+    grid = [(c, _decode_by_fields(c)) for c in range(256) if not math.isnan(_decode_by_fields(c))]
+    out = []
+    for x in vals:
+        y = min(max(x / X, -448.0), 448.0)
+        best = min(grid, key=lambda cv: (abs(cv[1] - y), cv[0] & 1))
+        out.append(best[1] * X)
+    return out
+
+
+def test_attn_mx_matches_brute_force_on_searched_roundings():
+    """attn_fwd_mx against the per-pair brute-force attention run on q and k
+    rounded block by block (32 channels of one head) by a grid search."""
+    from tests.brute import brute_attn_fwd
+    q, k, v, offs, ts, rp, rt, nc = _attn_mx_case(21, d=64)
+    T, H, d = q.shape
+    qr, kr = np.empty_like(q), np.empty_like(k)
+    for t in range(T):
+        for h in range(H):
+            for b0 in range(0, d, 32):
+                qr[t, h, b0:b0 + 32] = _round_block_by_search(list(q[t, h, b0:b0 + 32]))
+                kr[t, h, b0:b0 + 32] = _round_block_by_search(list(k[t, h, b0:b0 + 32]))
+    want = brute_attn_fwd(qr, kr, v, offs, ts, rp, rt, nc, 0, 16)
+    got = orc.attn_fwd_mx(q, k, v, offs, ts, rp, rt, nc, norm_len=16)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+    # the rounding is not a no-op here
+    assert np.abs(got - orc.attn_fwd(q, k, v, offs, ts, rp, rt, nc, norm_len=16)).max() > 1e-6
