@@ -522,6 +522,64 @@ def bench_mx(timer, reps=10):
     return out
 
 
+def bench_attn_mx(timer, configs=(3, 5, 4), reps=20):
+    """Attention forward with the score product in MXFP8 (q and k quantized
+    along each head's channels, the scaled FP8 MFMA for q.k, P V in bf16)
+    against the bf16 attention on the same q, k, v: whole-call medians
+    (quantization of q and k included on the MX side) and kernel times."""
+    import numpy as np
+    import torch
+
+    import synth
+    from hstu_sequential_transduction_amd import binding as B
+    from hstu_sequential_transduction_amd import flops
+    out = {}
+    for ci in configs:
+        cfg = synth.get_config(ci)
+        a = synth.make_attn_inputs(cfg)
+        T = a.q.shape[0]
+        td = torch.bfloat16
+        q = torch.from_numpy(a.q.reshape(T, -1)).to(td).cuda()
+        k = torch.from_numpy(a.k.reshape(T, -1)).to(td).cuda()
+        v = torch.from_numpy(a.v.reshape(T, -1)).to(td).cuda()
+        offs = torch.from_numpy(a.seq_offsets.astype(np.int32)).cuda()
+        ts = torch.from_numpy(a.timestamps.astype(np.int64)).cuda()
+        rp, rt = torch.from_numpy(a.rab_pos).cuda(), torch.from_numpy(a.rab_time).cuda()
+        nc = None if a.num_candidates is None else \
+            torch.from_numpy(a.num_candidates.astype(np.int32)).cuda()
+        ac = B.AttnConfig(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len)
+        ws = B.LayerWorkspace()
+        o = torch.empty((T, cfg.H * cfg.d_v), dtype=td, device="cuda")
+
+        def run_bf16():
+            B.hstu_attn_fwd(q, k, v, offs, ts, rp, rt, ac, num_candidates=nc, out=o, workspace=ws)
+
+        def run_mx():
+            qc, qs = B.hstu_mx_quantize_heads(q, cfg.H, cfg.d_qk)
+            kc, ks = B.hstu_mx_quantize_heads(k, cfg.H, cfg.d_qk)
+            B.hstu_attn_fwd_mx(qc, qs, kc, ks, v, offs, ts, rp, rt, ac, num_candidates=nc,
+                               out=o, workspace=ws)
+
+        sb = time_region(run_bf16, reps, 2)
+        sm = time_region(run_mx, reps, 2)
+        kb, _ = instrumented(run_bf16, timer, reps, 4)
+        km, _ = instrumented(run_mx, timer, reps, 8)
+        per = lambda kern, tag: kern[tag][1] / reps if tag in kern else None
+        fl = flops.attn_fwd_flops(a.lengths, a.num_candidates, cfg.H, cfg.d_qk, cfg.d_v)
+        tf = lambda ms: round(fl / (ms * 1e-3) / 1e12, 1) if ms else None
+        ab, am, qm = per(kb, "attn_fwd"), per(km, "attn_fwd"), per(km, "mx_quant")
+        out[cfg.name] = {
+            "d_qk": cfg.d_qk, "bf16_ms": round(sb["ms_median"], 4),
+            "mx_ms": round(sm["ms_median"], 4),
+            "speedup_whole_call": round(sb["ms_median"] / sm["ms_median"], 3),
+            "attn_kernel_ms_bf16": round(ab, 4), "attn_kernel_ms_mx": round(am, 4),
+            "quantize_q_and_k_ms": round(qm, 4) if qm else None,
+            "attn_kernel_tflops_bf16": tf(ab), "attn_kernel_tflops_mx": tf(am),
+            "attn_kernel_speedup": round(ab / am, 3)}
+        log(f"attention mx {cfg.name}: {out[cfg.name]}")
+    return out
+
+
 def roofline(cfg, inp, kern, steps, traffic_dir):
     work = kernel_work(cfg, inp.lengths, inp.T)
     best = max(((ms, name, n) for name, (n, ms) in kern.items() if name in work), default=None)
@@ -805,7 +863,7 @@ def cpu_baseline_configs():
 
 
 ALL_PARTS = ("train", "recompute", "trainmx", "fwd", "semilocal", "trunc", "cached", "mx",
-             "epilogue", "peaks", "cpu")
+             "attnmx", "epilogue", "peaks", "cpu")
 
 
 def main():
@@ -889,6 +947,8 @@ def main():
         line["cached_ranking"] = bench_cached(timer)
     if "mx" in parts:
         line["mxfp8"] = bench_mx(timer)
+    if "attnmx" in parts:
+        line["attention_mxfp8_scores"] = bench_attn_mx(timer)
     if "epilogue" in parts:
         line["ln_gate_epilogue"] = bench_epilogue(timer)
     if "peaks" in parts:

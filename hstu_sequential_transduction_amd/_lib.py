@@ -28,6 +28,7 @@ EXPORTED = [
     "hstu_truncate_offsets", "hstu_truncate_gather", "hstu_truncate_scatter",
     "hstu_attn_cached_workspace_size", "hstu_attn_cached_fwd",
     "hstu_mx_quantize", "hstu_mx_quantize_weight", "hstu_mx_gemm",
+    "hstu_mx_quantize_heads", "hstu_attn_fwd_mx",
     "hstu_layer_fwd_mx_workspace_size", "hstu_layer_fwd_mx",
     "hstu_layer_bwd_mx_workspace_size", "hstu_layer_bwd_mx",
     "hstu_layer_cached_workspace_size", "hstu_layer_fwd_cached",
@@ -76,6 +77,11 @@ class MxWeights(C.Structure):
 class MxIO(C.Structure):
     _fields_ = [("x_codes", C.c_void_p), ("x_scales", C.c_void_p), ("y_codes", C.c_void_p),
                 ("y_scales", C.c_void_p), ("g_codes", C.c_void_p), ("g_scales", C.c_void_p)]
+
+
+class AttnMxQK(C.Structure):
+    _fields_ = [("q_codes", C.c_void_p), ("k_codes", C.c_void_p), ("ld_codes", C.c_int64),
+                ("q_scales", C.c_void_p), ("k_scales", C.c_void_p)]
 
 
 class HistoryKV(C.Structure):
@@ -152,6 +158,11 @@ def lib() -> C.CDLL:
     L.hstu_validate_inputs.restype = C.c_int
     L.hstu_validate_inputs.argtypes = [i32, i64, vp, vp, vp, vp]
     L.hstu_mx_quantize.restype = C.c_int
+    L.hstu_mx_quantize_heads.restype = C.c_int
+    L.hstu_mx_quantize_heads.argtypes = [i64, i32, i32, vp, i64, vp, i64, vp, vp]
+    L.hstu_attn_fwd_mx.restype = C.c_int
+    L.hstu_attn_fwd_mx.argtypes = [P(AttnDesc), P(AttnMxQK), vp, i64, vp, vp, vp, vp, vp, vp,
+                                   i64, vp, sz, vp]
     L.hstu_mx_quantize.argtypes = [i64, i64, vp, i64, vp, vp, vp]
     L.hstu_mx_quantize_weight.restype = C.c_int
     L.hstu_mx_quantize_weight.argtypes = [i64, i64, vp, vp, vp, vp]

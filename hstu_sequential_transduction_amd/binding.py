@@ -358,6 +358,49 @@ def hstu_mx_quantize(x, stream=None):
     return codes, scales
 
 
+def hstu_mx_quantize_heads(x, H, d, stream=None):
+    """MXFP8 of an attention operand x [T, >= H*d] (bf16, e.g. q or k) along each
+    head's d channels: (codes uint8 [T, H*d], head-major scale words int32
+    [H, T], byte b of a word = the scale of channels 32b..32b+31)."""
+    T = x.shape[0]
+    codes = torch.empty((T, H * d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((H, T), dtype=torch.int32, device=x.device)
+    st = _lib.lib().hstu_mx_quantize_heads(T, H, d, _ptr(x), x.stride(0), _ptr(codes), H * d,
+                                           _ptr(scales), _stream(stream))
+    check("hstu_mx_quantize_heads", st)
+    return codes, scales
+
+
+def hstu_attn_fwd_mx(q_codes, q_scales, k_codes, k_scales, v, seq_offsets, timestamps, rab_pos,
+                     rab_time, cfg: AttnConfig, num_candidates=None, out=None, stream=None,
+                     workspace: Optional["LayerWorkspace"] = None):
+    """hstu_attn_fwd with the score product in MXFP8: q and k as written by
+    hstu_mx_quantize_heads (codes [T, ld] with one row stride, scale words [H, T])."""
+    for n_, t_ in (("q_codes", q_codes), ("k_codes", k_codes), ("q_scales", q_scales),
+                   ("k_scales", k_scales), ("v", v), ("seq_offsets", seq_offsets),
+                   ("timestamps", timestamps), ("rab_pos", rab_pos), ("rab_time", rab_time),
+                   ("num_candidates", num_candidates)):
+        _dev(t_, n_)
+    if q_codes.stride(0) != k_codes.stride(0):
+        raise ValueError("q_codes and k_codes need one row stride")
+    T = v.shape[0]
+    B = seq_offsets.shape[0] - 1
+    if out is None:
+        out = torch.empty((T, cfg.H * cfg.d_v), dtype=v.dtype, device=v.device)
+    d = attn_desc(cfg, B, T, v.dtype, _rab_stride(rab_pos, rab_time))
+    L = _lib.lib()
+    nb = L.hstu_attn_fwd_workspace_size(C.byref(d))
+    ws = _layer_ws(workspace, nb, v.device, cfg.reuse_plan)
+    qk = _lib.AttnMxQK(_ptr(q_codes), _ptr(k_codes), q_codes.stride(0), _ptr(q_scales),
+                       _ptr(k_scales))
+    st = L.hstu_attn_fwd_mx(C.byref(d), C.byref(qk), _ptr(v), v.stride(0), _ptr(seq_offsets),
+                            _ptr(timestamps), _ptr(rab_pos), _ptr(rab_time),
+                            _ptr(num_candidates), _ptr(out), out.stride(0), _ptr(ws), ws.numel(),
+                            _stream(stream))
+    check("hstu_attn_fwd_mx", st)
+    return out
+
+
 def hstu_mx_quantize_weight(w, stream=None):
     """(codes [N, K], scales [N, K/32]) of a bf16 [K, N] weight, blocks along K."""
     K, N = w.shape

@@ -381,10 +381,19 @@ hstu_status attn_fwd_plan(const hstu_attn_desc* d, const int32_t* offs, const in
 hstu_status attn_fwd_run(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
                          const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
                          const float* rp, const float* rt, const int32_t* nc, void* out,
-                         int64_t ld_out, bool out_f32, void* ws, hipStream_t st) {
+                         int64_t ld_out, bool out_f32, void* ws, hipStream_t st,
+                         const hstu_attn_mx_qk* mx = nullptr) {
   Carver c(ws);
   FwdWs w = carve_fwd(c, d);
   AttnArgs a = base_args(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, w.tm);
+  if (mx) {
+    a.q_mx = static_cast<const uint8_t*>(mx->q_codes);
+    a.k_mx = static_cast<const uint8_t*>(mx->k_codes);
+    a.ld_mx = mx->ld_codes;
+    a.q_mxs = mx->q_scales;
+    a.k_mxs = mx->k_scales;
+    a.T_rows = d->T;
+  }
   a.out = out;
   a.ld_out = ld_out;
   a.out_f32 = out_f32;
@@ -401,13 +410,15 @@ hstu_status attn_fwd_run(const hstu_attn_desc* d, const void* q, const void* k, 
 hstu_status attn_fwd_impl(const hstu_attn_desc* d, const void* q, const void* k, int64_t ld_qk,
                           const void* v, int64_t ld_v, const int32_t* offs, const int64_t* ts,
                           const float* rp, const float* rt, const int32_t* nc, void* out,
-                          int64_t ld_out, bool out_f32, void* ws, hipStream_t st) {
+                          int64_t ld_out, bool out_f32, void* ws, hipStream_t st,
+                          const hstu_attn_mx_qk* mx = nullptr) {
   if (!d->reuse_plan) {
     hstu_status s = attn_fwd_plan(d, offs, ts, ws, st);
     if (s != HSTU_OK) return s;
     plan_record(d, ws, offs, ts);
   }
-  return attn_fwd_run(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, out_f32, ws, st);
+  return attn_fwd_run(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, out_f32, ws, st,
+                      mx);
 }
 
 // Ranking against a cached history: key splits per (user, candidate block)
@@ -905,6 +916,50 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* d, const void* q, const void* k,
   if (d->reuse_plan && !plan_recorded(d, ws, offs, ts)) return HSTU_ERR_INVALID_ARG;
   return attn_fwd_impl(d, q, k, ld_qk, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, false, ws,
                        entry_stream(stream));
+}
+
+hstu_status hstu_attn_fwd_mx(const hstu_attn_desc* d, const hstu_attn_mx_qk* qk, const void* v,
+                             int64_t ld_v, const int32_t* offs, const int64_t* ts,
+                             const float* rp, const float* rt, const int32_t* nc, void* out,
+                             int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
+  hstu_status s = check_attn_desc(d);
+  if (s != HSTU_OK) return s;
+  if (!qk) return HSTU_ERR_INVALID_ARG;
+  if (d->dtype != HSTU_BF16 || d->d_qk != d->d_v || (d->d_qk != 64 && d->d_qk != 128) ||
+      d->win_local > 0 || d->key_splits > 1)
+    return HSTU_ERR_UNSUPPORTED;
+  const int64_t hq = (int64_t)d->H * d->d_qk, hv = (int64_t)d->H * d->d_v;
+  if (d->T > 0 && (!qk->q_codes || !qk->k_codes || !qk->q_scales || !qk->k_scales || !v ||
+                   !out || !ts))
+    return HSTU_ERR_INVALID_ARG;
+  if (!offs || !rp || !rt || !ws) return HSTU_ERR_INVALID_ARG;
+  if (d->T > 0 && (!aligned16(qk->q_codes) || !aligned16(qk->k_codes) || qk->ld_codes < hq ||
+                   qk->ld_codes % 16 != 0 ||
+                   (reinterpret_cast<uintptr_t>(qk->q_scales) & 3) ||
+                   (reinterpret_cast<uintptr_t>(qk->k_scales) & 3) ||
+                   !stride_ok(d->dtype, v, ld_v, hv) || ld_out < hv))
+    return HSTU_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return HSTU_ERR_INVALID_ARG;
+  if (ws_bytes < hstu_attn_fwd_workspace_size(d)) return HSTU_ERR_WORKSPACE;
+  if (d->reuse_plan && !plan_recorded(d, ws, offs, ts)) return HSTU_ERR_INVALID_ARG;
+  return attn_fwd_impl(d, nullptr, nullptr, 0, v, ld_v, offs, ts, rp, rt, nc, out, ld_out, false,
+                       ws, entry_stream(stream), qk);
+}
+
+hstu_status hstu_mx_quantize_heads(int64_t T, int32_t H, int32_t dh, const void* x, int64_t ld,
+                                   void* codes, int64_t ld_codes, uint32_t* scales,
+                                   void* stream) {
+  if (T < 0 || H <= 0 || dh <= 0 || dh % 32 != 0 || dh > 128) return HSTU_ERR_INVALID_ARG;
+  const int64_t w = (int64_t)H * dh;
+  if (ld < w || ld_codes < w || ld % 8 != 0 || ld_codes % 16 != 0) return HSTU_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !codes || !scales || !aligned16(x) || !aligned16(codes) ||
+                (reinterpret_cast<uintptr_t>(scales) & 3)))
+    return HSTU_ERR_INVALID_ARG;
+  hipStream_t st = entry_stream(stream);
+  HSTU_TIMED(TT_MX_QUANT, st);
+  HSTU_TRY(launch_mx_quant_heads(x, ld, T, H, dh, static_cast<uint8_t*>(codes), ld_codes,
+                                 scales, st));
+  return HSTU_OK;
 }
 
 hstu_status hstu_attn_fwd_noalloc(const hstu_attn_desc* d, const void* q, const void* k,

@@ -34,6 +34,7 @@ namespace {
 constexpr int FWD_BN = 64;  // keys per tile
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 // One 32-row query group per wave.  The kernel is bound by latency inside
 // each wave (LDS reads -> S MFMAs -> VALU -> P V MFMAs), so what pays is
@@ -49,13 +50,20 @@ struct FwdShape {
   static constexpr int OCC = (DQK <= 64 && DV <= 64) ? 3 : 2;  // workgroups per CU
 };
 
-// One staged key tile: row-major K and V and the key times.
-template <int DQK, int DV>
+// One staged key tile: row-major K and V and the key times.  MX: K as E4M3
+// codes (DQK bytes per row, staged like DQK/2 bf16) and the keys' scale words.
+template <int DQK, bool MX>
+constexpr int fwd_k_bytes() {
+  if constexpr (MX) return SwzTile<DQK / 2>::bytes(FWD_BN);
+  else return SwzTile<DQK>::bytes(FWD_BN);
+}
+template <int DQK, int DV, bool MX = false>
 struct FwdBuf {
-  uint8_t k[SwzTile<DQK>::bytes(FWD_BN)];
+  uint8_t k[fwd_k_bytes<DQK, MX>()];
   uint8_t v[SwzTile<DV>::bytes(FWD_BN)];
   int32_t t[FWD_BN];    // key times relative to the sequence minimum (narrow)
   int64_t t64[FWD_BN];  // key times (wide sequences)
+  uint32_t ks[MX ? FWD_BN : 1];  // MX: scale word of each key (byte b: channels 32b..)
 };
 
 // Bias tables, a separate LDS object from the tile buffers.
@@ -87,13 +95,19 @@ using mconst = std::integral_constant<int, V>;
 // tile, so the longest item's chain of tiles takes about half as long),
 // adding their partial sums of O through LDS at the end.  For batches whose
 // 128-row items do not fill the GPU.
-template <int DQK, int DV, bool WIN, bool SPLIT, bool KH = false>
+// MX: the score product in MXFP8 (E4M3 codes of q and k with E8M0 block
+// scales along d_qk, the scaled 32x32x64 FP8 MFMA; one per 64 channels);
+// P V stays bf16.
+template <int DQK, int DV, bool WIN, bool SPLIT, bool KH = false, bool MX = false>
 __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16(AttnArgs a) {
   static_assert(!(KH && (SPLIT || WIN)), "key halves: no split, no windows");
+  static_assert(!MX || (!SPLIT && !WIN && (DQK == 64 || DQK == 128)),
+                "MX scores: no split, no windows, d_qk 64 or 128");
   constexpr int QG = FwdShape<DQK, DV>::QG;
   constexpr int BM = KH ? 64 : FwdShape<DQK, DV>::BM;
-  __shared__ __attribute__((aligned(1024))) FwdBuf<DQK, DV> fwb0;
-  __shared__ __attribute__((aligned(1024))) FwdBuf<DQK, DV> fwb1;
+  using Buf = FwdBuf<DQK, DV, MX>;
+  __shared__ __attribute__((aligned(1024))) Buf fwb0;
+  __shared__ __attribute__((aligned(1024))) Buf fwb1;
   __shared__ FwdTables sm;
 
   // part-major numbering (parts 0 of every item first): consecutive workgroups
@@ -168,7 +182,12 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
   int iq[QG], pI[QG];
   int32_t ti1[QG];
   int64_t tq64[QG];
-  bf16x8 qr[QG][DQK / 16];
+  bf16x8 qr[QG][MX ? 1 : DQK / 16];
+  // MX: lane half g holds channels 64 c + 16 g + {0..15} and 64 c + 32 + 16 g
+  // + {0..15} of its row (c = 0 .. DQK/64 - 1) (the scaled MFMA's k order) and the row's scale word
+  // shifted so that bytes 0 and 2 are blocks g and 2 + g
+  i32x8 qm[QG][MX ? DQK / 64 : 1];
+  int qsc[QG];
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     iq[qg] = r0 + 32 * qg + ql;
@@ -176,11 +195,22 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
     pI[qg] = min(iq[qg], nh);
     ti1[qg] = (qv && !wide) ? a.rel_t[o0 + iq[qg]] + 1 : 0;
     tq64[qg] = (qv && wide) ? tsq[iq[qg]] : 0;
+    if constexpr (MX) {
+      const uint8_t* qp = a.q_mx + (int64_t)(o0 + iq[qg]) * a.ld_mx + h * DQK + 16 * g;
 #pragma unroll
-    for (int ch = 0; ch < DQK / 16; ++ch)
-      qr[qg][ch] = qv ? *reinterpret_cast<const bf16x8*>(qbase + (int64_t)iq[qg] * a.ld_qk +
-                                                         ch * 16 + 8 * g)
-                      : bf16x8{};
+      for (int c64 = 0; c64 < DQK / 64; ++c64) {
+        const i32x4 lo = qv ? *reinterpret_cast<const i32x4*>(qp + 64 * c64) : i32x4{};
+        const i32x4 hi = qv ? *reinterpret_cast<const i32x4*>(qp + 64 * c64 + 32) : i32x4{};
+        qm[qg][c64] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      qsc[qg] = qv ? (int)(a.q_mxs[h * a.T_rows + o0 + iq[qg]] >> (8 * g)) : 0;
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < DQK / 16; ++ch)
+        qr[qg][ch] = qv ? *reinterpret_cast<const bf16x8*>(qbase + (int64_t)iq[qg] * a.ld_qk +
+                                                           ch * 16 + 8 * g)
+                        : bf16x8{};
+    }
   }
 
   f32x16 oacc[QG][DV / 32];
@@ -211,9 +241,17 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
   };
 
   // DMA of key tile kt; keys >= n arrive as zeros
-  auto issue = [&](FwdBuf<DQK, DV>& Bf, int kt) HSTU_INLINE_LAMBDA {
+  // MX: rows of DQK code bytes staged as DQK/2 bf16; the keys' scale words
+  const bf16* kmx = MX ? reinterpret_cast<const bf16*>(a.k_mx + (int64_t)o0 * a.ld_mx + h * DQK)
+                       : nullptr;
+  auto issue = [&](Buf& Bf, int kt) HSTU_INLINE_LAMBDA {
     const int j0 = kt * FWD_BN;
-    dma_tile<DQK, FWD_BN, 4>(Bf.k, kh, a.ld_qk, j0, n, wave, lane);
+    if constexpr (MX) {
+      dma_tile<DQK / 2, FWD_BN, 4>(Bf.k, kmx, a.ld_mx / 2, j0, n, wave, lane);
+      if (wave == 1) dma_words64(Bf.ks, a.k_mxs + h * a.T_rows + o0, j0, n, lane);
+    } else {
+      dma_tile<DQK, FWD_BN, 4>(Bf.k, kh, a.ld_qk, j0, n, wave, lane);
+    }
     dma_tile<DV, FWD_BN, 4>(Bf.v, vh, a.ld_v, j0, n, wave, lane);
     if (wave == 0) {
       if (!wide) dma_words64(Bf.t, a.rel_t + o0, j0, n, lane);
@@ -221,7 +259,7 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
     }
   };
 
-  auto body = [&](const FwdBuf<DQK, DV>& B, int kt) HSTU_INLINE_LAMBDA {
+  auto body = [&](const Buf& B, int kt) HSTU_INLINE_LAMBDA {
     const int j0 = kt * FWD_BN;
     const int j1 = min(j0 + FWD_BN, n);
     const bool hist_rows = r0 < nh;
@@ -285,7 +323,28 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
         f32x16 sacc[QG];
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) sacc[qg] = f32x16{};
-        {
+        if constexpr (MX) {
+          // S^T = K Q^T with E8M0 block scales: key row hf*32 + ql of the
+          // tile, channels in the order of the Q registers above
+          const int ksc = (int)(B.ks[hf * 32 + ql] >> (8 * g));
+          i32x8 ka[DQK / 64];
+#pragma unroll
+          for (int c64 = 0; c64 < DQK / 64; ++c64) {
+            const i32x4 lo =
+                __builtin_bit_cast(i32x4, lds_row8<DQK / 2>(B.k, hf * 32 + ql, 2 * c64, g));
+            const i32x4 hi =
+                __builtin_bit_cast(i32x4, lds_row8<DQK / 2>(B.k, hf * 32 + ql, 2 * c64 + 1, g));
+            ka[c64] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) {
+            sacc[qg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                ka[0], qm[qg][0], sacc[qg], 0, 0, 0, ksc, 0, qsc[qg]);
+            if constexpr (DQK == 128)
+              sacc[qg] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  ka[1], qm[qg][1], sacc[qg], 0, 0, 2, ksc, 2, qsc[qg]);
+          }
+        } else {
           bf16x8 ka[DQK / 16];
 #pragma unroll
           for (int ch = 0; ch < DQK / 16; ++ch) ka[ch] = lds_row8<DQK>(B.k, hf * 32 + ql, ch, g);
@@ -439,7 +498,7 @@ __global__ __launch_bounds__(256, (FwdShape<DQK, DV>::OCC)) void k_attn_fwd_bf16
   if constexpr (KH) {
     // the key-half-1 wave of each row group hands its partial sum of O to the
     // key-half-0 wave (the tile buffers are free after the loop's last barrier)
-    static_assert((DV / 32) * 16 * 64 * 4 <= (int)sizeof(FwdBuf<DQK, DV>), "exchange fits a tile buffer");
+    static_assert((DV / 32) * 16 * 64 * 4 <= (int)sizeof(Buf), "exchange fits a tile buffer");
     float* xo = reinterpret_cast<float*>(rg == 0 ? reinterpret_cast<uint8_t*>(&fwb0)
                                                  : reinterpret_cast<uint8_t*>(&fwb1));
     if (khalf == 1) {
@@ -651,6 +710,20 @@ hipError_t launch_fwd_t(const AttnArgs& a, int dtype, int64_t max_items, hipStre
   if (dtype == HSTU_BF16) {
     if (a.splits > 1 && (a.win_local > 0 || !a.part || !a.part_cnt)) return hipErrorInvalidValue;
     if (a.key_halves && (a.win_local > 0 || a.splits > 1)) return hipErrorInvalidValue;
+    if (a.q_mx) {
+      // MX scores: d_qk = d_v in {64, 128}, no windows, no key split
+      if constexpr (DQK == DV && (DQK == 64 || DQK == 128)) {
+        if (a.win_local > 0 || a.splits > 1 || !a.k_mx || !a.q_mxs || !a.k_mxs)
+          return hipErrorInvalidValue;
+        if (a.key_halves)
+          k_attn_fwd_bf16<DQK, DV, false, false, true, true><<<(unsigned)grid, 256, 0, st>>>(a);
+        else
+          k_attn_fwd_bf16<DQK, DV, false, false, false, true><<<(unsigned)grid, 256, 0, st>>>(a);
+        return hipGetLastError();
+      } else {
+        return hipErrorInvalidValue;
+      }
+    }
     if (a.win_local > 0)
       k_attn_fwd_bf16<DQK, DV, true, false><<<(unsigned)grid, 256, 0, st>>>(a);
     else if (a.key_halves)

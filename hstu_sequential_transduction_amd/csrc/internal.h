@@ -133,6 +133,16 @@ struct AttnArgs {
   // forward: 64-row work items whose key tiles two waves share (1), or
   // 128-row items (0); the plan's block rows must match
   int key_halves = 0;
+  // forward with the score product in MXFP8: E4M3 codes of q and k (rows of
+  // ld_mx bytes, head h at byte h*d_qk) and head-major scale words
+  // (q_mxs[h*T_rows + row], byte b = E8M0 scale of channels 32b..32b+31);
+  // q_mx == nullptr: bf16 q and k
+  const uint8_t* q_mx = nullptr;
+  const uint8_t* k_mx = nullptr;
+  int64_t ld_mx = 0;
+  const uint32_t* q_mxs = nullptr;
+  const uint32_t* k_mxs = nullptr;
+  int64_t T_rows = 0;
   // backward with dS kept: 128 x 128 bf16 blocks (key-major) of the causal
   // part, per sequence and head; ds_base[b] = first block of sequence b;
   // *ds_flag != 0: the blocks did not fit, dQ is recomputed instead
@@ -313,6 +323,11 @@ hipError_t launch_mx_quant_rows_t(const void* x, int64_t ld, int64_t T, int64_t 
 hipError_t launch_mx_quant_both(const void* x, int64_t ld, int64_t T, int64_t C, int64_t Tp,
                                 uint8_t* codes, uint8_t* scales, uint8_t* rcodes,
                                 uint8_t* rscales, hipStream_t st);
+// MXFP8 of attention operands along each head's channels: codes [T][ld_codes]
+// (head h at byte h*d), head-major scale words scales[h*T + t] (byte b: block b)
+hipError_t launch_mx_quant_heads(const void* x, int64_t ld, int64_t T, int H, int d,
+                                 uint8_t* codes, int64_t ld_codes, uint32_t* scales,
+                                 hipStream_t st);
 hipError_t launch_mx_quant_cols(const void* w, int64_t K, int64_t N, uint8_t* codes,
                                 uint8_t* scales, hipStream_t st);
 

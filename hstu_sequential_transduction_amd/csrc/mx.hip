@@ -129,6 +129,41 @@ int quant_grid(int64_t blocks) {
   return (int)std::min<int64_t>(std::max<int64_t>(g, 1), 8192);
 }
 
+// Attention operands (q or k, [T][H*d] bf16, row stride ld): blocks of 32
+// along each head's d channels; codes [T][ld_codes] bytes (head h at byte
+// h*d) and one scale word per (head, row), head-major: scales[h*T + t],
+// byte b = the E8M0 scale of channels 32b..32b+31 (d <= 128; unused bytes
+// zero), so that a key tile's words are one contiguous run.  One lane per
+// (head, row), consecutive lanes on consecutive rows.
+__global__ __launch_bounds__(256) void k_mx_quant_heads(const bf16* __restrict__ in, int64_t ld,
+                                                        int64_t T, int H, int d,
+                                                        uint8_t* __restrict__ codes,
+                                                        int64_t ld_codes,
+                                                        uint32_t* __restrict__ scales) {
+  const int64_t total = T * H;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t h = i / T, t = i - h * T;
+    const bf16* p = in + t * ld + h * d;
+    u32x4* dst = reinterpret_cast<u32x4*>(codes + t * ld_codes + h * d);
+    uint32_t word = 0;
+    for (int kb = 0; kb < d / 32; ++kb) {
+      float v[32];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(p + 32 * kb + 8 * q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[8 * q + e] = bf2f(x[e]);
+      }
+      uint32_t out[8];
+      word |= (uint32_t)mx_block(v, out) << (8 * kb);
+      dst[2 * kb] = u32x4{out[0], out[1], out[2], out[3]};
+      dst[2 * kb + 1] = u32x4{out[4], out[5], out[6], out[7]};
+    }
+    scales[h * T + t] = word;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_mx_quant_rows(const void* x, int64_t ld, int64_t rows, int64_t K,
@@ -136,6 +171,19 @@ hipError_t launch_mx_quant_rows(const void* x, int64_t ld, int64_t rows, int64_t
   if (rows <= 0 || K <= 0) return hipSuccess;
   k_mx_quant<true><<<quant_grid(rows * K / 32), 256, 0, st>>>(
       static_cast<const bf16*>(x), ld, 1, rows, K, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_heads(const void* x, int64_t ld, int64_t T, int H, int d,
+                                 uint8_t* codes, int64_t ld_codes, uint32_t* scales,
+                                 hipStream_t st) {
+  if (T <= 0 || H <= 0) return hipSuccess;
+  if (d % 32 || d > 128 || ld < (int64_t)H * d || (ld % 8) || ld_codes < (int64_t)H * d ||
+      (ld_codes % 16) || (reinterpret_cast<uintptr_t>(x) & 15) ||
+      (reinterpret_cast<uintptr_t>(codes) & 15) || (reinterpret_cast<uintptr_t>(scales) & 3))
+    return hipErrorInvalidValue;
+  k_mx_quant_heads<<<quant_grid(T * H), 256, 0, st>>>(static_cast<const bf16*>(x), ld, T, H, d,
+                                                       codes, ld_codes, scales);
   return hipGetLastError();
 }
 

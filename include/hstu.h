@@ -351,6 +351,53 @@ hstu_status hstu_mx_gemm(int64_t M, int64_t N, int64_t K, const void* a, const v
                          const void* b, const void* b_scales, float* c, int64_t ldc,
                          void* stream);
 /*
+ * The attention's score product in MXFP8 ("Bending the Scaling Law Curve in
+ * Large-Scale Recommendation Systems", Mixed precision: the matrix products
+ * in FP8; the scores q_i . k_j are one of the attention's two products).
+ * q and k are rounded along their contraction, the d_qk channels of each
+ * head, in blocks of 32 (the MX encoding above); the scaled FP8 matrix
+ * cores multiply the codes, and the bias, SiLU, mask, normalisation and
+ * the product with v run as in hstu_attn_fwd (P and v in bf16).
+ *
+ * hstu_mx_quantize_heads: MXFP8 of x [T][H*d] bf16 (row stride ld
+ * elements, a multiple of 8; x 16-byte aligned) along each head's d
+ * channels (d a multiple of 32, at most 128): codes [T][ld_codes] bytes
+ * (head h at byte h*d; ld_codes >= H*d, a multiple of 16; codes 16-byte
+ * aligned) and one 32-bit scale word per head and row, head-major:
+ * scales[h*T + t], byte b = the E8M0 scale of channels 32b..32b+31 of head
+ * h (bytes past d/32 zero; scales 4-byte aligned).  A key tile's scale
+ * words are then one contiguous run.  Invalid sizes or alignment:
+ * HSTU_ERR_INVALID_ARG.
+ */
+hstu_status hstu_mx_quantize_heads(int64_t T, int32_t H, int32_t d, const void* x, int64_t ld,
+                                   void* codes, int64_t ld_codes, uint32_t* scales,
+                                   void* stream);
+
+/* q and k of hstu_attn_fwd_mx as written by hstu_mx_quantize_heads (device
+ * memory, caller-owned; both with the same ld_codes). */
+typedef struct {
+  const void* q_codes;
+  const void* k_codes;
+  int64_t ld_codes;
+  const uint32_t* q_scales; /* [H][T] words */
+  const uint32_t* k_scales; /* [H][T] words */
+} hstu_attn_mx_qk;
+
+/* hstu_attn_fwd with the score product in MXFP8: `qk` replaces q, k and
+ * ld_qk; v, out (bf16), the tables, offsets, timestamps, candidates,
+ * workspace (hstu_attn_fwd_workspace_size of the same descriptor) and
+ * reuse_plan as for hstu_attn_fwd.  Supported: bf16, d_qk = d_v in
+ * {64, 128}, no semi-local windows, key_splits 0 or 1; other descriptors
+ * return HSTU_ERR_UNSUPPORTED before anything is launched. */
+hstu_status hstu_attn_fwd_mx(const hstu_attn_desc* desc, const hstu_attn_mx_qk* qk,
+                             const void* v, int64_t ld_v,
+                             const int32_t* seq_offsets, const int64_t* timestamps,
+                             const float* rab_pos, const float* rab_time,
+                             const int32_t* num_candidates,
+                             void* out, int64_t ld_out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Forward of one layer with MXFP8 projection and output products
  * ("Bending the Scaling Law Curve in Large-Scale Recommendation Systems",
  * Mixed precision: the matrix products in FP8; X and the gated LayerNorm G

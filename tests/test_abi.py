@@ -147,7 +147,8 @@ def test_descriptor_layouts_match_the_header(tmp_path):
     structs = {"hstu_attn_desc": _lib.AttnDesc, "hstu_layer_desc": _lib.LayerDesc,
                "hstu_layer_weights": _lib.LayerWeights, "hstu_layer_saved": _lib.LayerSaved,
                "hstu_layer_grads": _lib.LayerGrads, "hstu_history_kv": _lib.HistoryKV,
-               "hstu_mx_weights": _lib.MxWeights, "hstu_mx_io": _lib.MxIO}
+               "hstu_mx_weights": _lib.MxWeights, "hstu_mx_io": _lib.MxIO,
+               "hstu_attn_mx_qk": _lib.AttnMxQK}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hstu.h"', "int main(void) {"]
     for cname, ct in structs.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -275,3 +276,37 @@ def test_check_mode_switch(L):
         out = subprocess.run([sys.executable, "-c", code], cwd=root, env=env,
                              capture_output=True, text=True, timeout=120)
         assert out.stdout.strip().splitlines()[-1] == want, out.stderr[-2000:]
+
+
+def test_mx_attention_argument_errors(L):
+    """Host-side checks of the MXFP8-score attention and its quantizer
+    (nothing is launched): unsupported descriptors, missing operands,
+    misaligned codes or strides."""
+    buf = C.create_string_buffer(1 << 20)
+    ws = C.c_void_p((C.addressof(buf) + 255) & ~255)
+    p = C.c_void_p(1 << 20)
+    odd = C.c_void_p((1 << 20) + 8)
+    qk = _lib.AttnMxQK(p, p, 256, p, p)
+
+    def call(d_, qk_=qk, nbytes=1 << 19):
+        return L.hstu_attn_fwd_mx(C.byref(d_), None if qk_ is None else C.byref(qk_), p, 256,
+                                  p, p, p, p, None, p, 256, ws, nbytes, None)
+    bf = dict(dtype=1, H=2, d_qk=64, d_v=64)
+    assert call(_desc(**bf), None) == -1                         # no q/k
+    assert call(_desc(**{**bf, "dtype": 0})) == -2                # fp32
+    assert call(_desc(**{**bf, "d_qk": 32, "d_v": 32})) == -2     # d_qk below one FP8 k-step
+    assert call(_desc(**{**bf, "d_v": 128})) == -2                # d_qk != d_v
+    assert call(_desc(**bf, win_local=8)) == -2                   # windows
+    assert call(_desc(**bf, key_splits=2)) == -2                  # key split
+    assert call(_desc(**bf), _lib.AttnMxQK(odd, p, 256, p, p)) == -1   # misaligned codes
+    assert call(_desc(**bf), _lib.AttnMxQK(p, p, 120, p, p)) == -1     # ld below H*d_qk
+    assert call(_desc(**bf), _lib.AttnMxQK(p, p, 136, p, p)) == -1     # ld not 16-byte
+    assert call(_desc(**bf), _lib.AttnMxQK(p, p, 256, None, p)) == -1  # no scales
+    assert call(_desc(**bf), nbytes=16) == -3                          # workspace
+    q = L.hstu_mx_quantize_heads
+    assert q(10, 2, 48, p, 128, p, 128, p, None) == -1       # d not a multiple of 32
+    assert q(10, 2, 160, p, 512, p, 512, p, None) == -1      # d above 128
+    assert q(10, 2, 64, p, 100, p, 128, p, None) == -1       # ld below H*d
+    assert q(10, 2, 64, p, 128, p, 136, p, None) == -1       # codes stride not 16-byte
+    assert q(10, 2, 64, odd, 128, p, 128, p, None) == -1     # misaligned input
+    assert q(10, 2, 64, p, 128, p, 128, C.c_void_p((1 << 20) + 2), None) == -1
