@@ -495,12 +495,22 @@ def bench_mx(timer, reps=10):
                                     y=bufs[li % 2], workspace=ws, x_mx=x_mx, y_mx=y_mx)
             x_mx = y_mx
 
+    def run_mx_scores():
+        x, x_mx = X, None
+        for li, (w, m) in enumerate(zip(lay, mxw)):
+            y_mx = mxb[li % 2] if li + 1 < len(lay) else None
+            x = B.hstu_layer_fwd_mx(x, m, w["rp"], w["rt"], offs, ts, lc, num_candidates=nc,
+                                    y=bufs[li % 2], workspace=ws, x_mx=x_mx, y_mx=y_mx,
+                                    mx_scores=True)
+            x_mx = y_mx
+
     def timed(fn):
         ms, kern = timed_pair(fn, timer, reps, 64 * cfg.n_layers)
         return ms, {k: round(v[1] / reps, 4) for k, v in kern.items()}
 
     ms_b, kb = timed(run_bf16)
     ms_m, km = timed(run_mx)
+    ms_s, ks = timed(run_mx_scores)
     proj = 2.0 * T * cfg.D * cfg.f1_width * cfg.n_layers
     outp = 2.0 * T * cfg.H * cfg.d_v * cfg.D * cfg.n_layers
     tf = lambda fl, ms: round(fl / (ms * 1e-3) / 1e12, 2) if ms else None
@@ -517,7 +527,13 @@ def bench_mx(timer, reps=10):
            "proj_gemm_tflops_mx": tf(proj, km.get("gemm_uvqk")),
            "out_gemm_tflops_bf16": tf(outp, kb.get("gemm_out")),
            "out_gemm_tflops_mx": tf(outp, km.get("gemm_out")),
-           "kernel_ms_bf16": kb, "kernel_ms_mx": km}
+           "kernel_ms_bf16": kb, "kernel_ms_mx": km,
+           "with_mx_scores": {
+               "format": "also the attention's q.k in MXFP8 (q and k quantized along each "
+                         "head's channels in one pass per layer); P V bf16",
+               "ms": round(ms_s, 4), "speedup_vs_bf16": round(ms_b / ms_s, 3),
+               "speedup_vs_mx_products": round(ms_m / ms_s, 3), "tflops": tf(lf, ms_s),
+               "kernel_ms": ks}}
     log(f"mxfp8: {out}")
     return out
 

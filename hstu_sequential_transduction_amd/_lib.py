@@ -76,7 +76,8 @@ class MxWeights(C.Structure):
 
 class MxIO(C.Structure):
     _fields_ = [("x_codes", C.c_void_p), ("x_scales", C.c_void_p), ("y_codes", C.c_void_p),
-                ("y_scales", C.c_void_p), ("g_codes", C.c_void_p), ("g_scales", C.c_void_p)]
+                ("y_scales", C.c_void_p), ("g_codes", C.c_void_p), ("g_scales", C.c_void_p),
+                ("mx_scores", C.c_int32)]
 
 
 class AttnMxQK(C.Structure):

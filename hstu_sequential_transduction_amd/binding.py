@@ -446,12 +446,14 @@ class MxLayerWeights:
 def hstu_layer_fwd_mx(x, wm: MxLayerWeights, rab_pos, rab_time, seq_offsets, timestamps,
                       cfg: LayerConfig, num_candidates=None, b1=None, b2=None, gamma=None,
                       beta=None, y=None, workspace: Optional[LayerWorkspace] = None, stream=None,
-                      g_out=None, x_mx=None, y_mx=None, saved: Optional["Saved"] = None):
+                      g_out=None, x_mx=None, y_mx=None, saved: Optional["Saved"] = None,
+                      mx_scores: bool = False):
     """Y of one layer with MXFP8 projection and output products.
     Optional (codes, scales) pairs: x_mx holds x already in MXFP8 (e.g. the
     previous layer's y_mx), y_mx receives y in MXFP8, g_out the quantized
     gated output the output product used.  saved (training): receives the
-    intermediates for hstu_layer_bwd(..., mx=True)."""
+    intermediates for hstu_layer_bwd(..., mx=True).  mx_scores (inference):
+    the attention's score product in MXFP8 too."""
     T = x.shape[0]
     B = seq_offsets.shape[0] - 1
     if y is None:
@@ -463,7 +465,7 @@ def hstu_layer_fwd_mx(x, wm: MxLayerWeights, rab_pos, rab_time, seq_offsets, tim
     w = _weights(None, None, rab_pos, rab_time, b1, b2, gamma, beta)
     m = wm.c()
     pair = lambda p: (None, None) if p is None else (_ptr(p[0]), _ptr(p[1]))
-    io = MxIO(*pair(x_mx), *pair(y_mx), *pair(g_out))
+    io = MxIO(*pair(x_mx), *pair(y_mx), *pair(g_out), 1 if mx_scores else 0)
     sv = saved.c() if saved is not None else None
     st = L.hstu_layer_fwd_mx(C.byref(d), _ptr(x), C.byref(w), C.byref(m), _ptr(seq_offsets),
                              _ptr(timestamps), _ptr(num_candidates), _ptr(y), C.byref(io),

@@ -949,7 +949,8 @@ hstu_status hstu_attn_fwd_mx(const hstu_attn_desc* d, const hstu_attn_mx_qk* qk,
 hstu_status hstu_mx_quantize_heads(int64_t T, int32_t H, int32_t dh, const void* x, int64_t ld,
                                    void* codes, int64_t ld_codes, uint32_t* scales,
                                    void* stream) {
-  if (T < 0 || H <= 0 || dh <= 0 || dh % 32 != 0 || dh > 128) return HSTU_ERR_INVALID_ARG;
+  if (T < 0 || H <= 0 || H > 64 || dh <= 0 || dh % 32 != 0 || dh > 128)
+    return HSTU_ERR_INVALID_ARG;
   const int64_t w = (int64_t)H * dh;
   if (ld < w || ld_codes < w || ld % 8 != 0 || ld_codes % 16 != 0) return HSTU_ERR_INVALID_ARG;
   if (T > 0 && (!x || !codes || !scales || !aligned16(x) || !aligned16(codes) ||
@@ -1101,9 +1102,18 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* L, const void* x, const hstu_l
                          full ? saved->mu : nullptr, full ? saved->rstd : nullptr, attention, st);
 }
 
-// MXFP8 layer: the inference workspace plus the quantized X and G
+// descriptors whose attention can take its score product in MXFP8
+bool mx_scores_ok(const hstu_attn_desc* d) {
+  return d->dtype == HSTU_BF16 && d->d_qk == d->d_v && (d->d_qk == 64 || d->d_qk == 128) &&
+         d->win_local == 0 && d->key_splits <= 1;
+}
+
+// MXFP8 layer: the inference workspace plus the quantized X and G, and (for
+// descriptors that allow MXFP8 scores) the codes of Q|K, [T][2 H d_qk], and
+// their head-major scale words, [2H][T]
 struct MxWs {
-  uint8_t *x8, *xs, *g8, *gs;
+  uint8_t *x8, *xs, *g8, *gs, *qk8 = nullptr;
+  uint32_t* qks = nullptr;
 };
 MxWs carve_mx(Carver& c, const hstu_layer_desc* L) {
   const hstu_attn_desc* d = &L->attn;
@@ -1113,6 +1123,10 @@ MxWs carve_mx(Carver& c, const hstu_layer_desc* L) {
   m.xs = c.take<uint8_t>(T * D / 32);
   m.g8 = c.take<uint8_t>(T * W);
   m.gs = c.take<uint8_t>(T * W / 32);
+  if (mx_scores_ok(d)) {
+    m.qk8 = c.take<uint8_t>(T * 2 * d->H * d->d_qk);
+    m.qks = c.take<uint32_t>(T * 2 * d->H);
+  }
   return m;
 }
 
@@ -1157,7 +1171,10 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
     if (!pair_ok(io->x_codes, io->x_scales) || !pair_ok(io->y_codes, io->y_scales) ||
         !pair_ok(io->g_codes, io->g_scales))
       return HSTU_ERR_INVALID_ARG;
+    if (io->mx_scores != 0 && io->mx_scores != 1) return HSTU_ERR_INVALID_ARG;
+    if (io->mx_scores && (saved || !mx_scores_ok(d))) return HSTU_ERR_UNSUPPORTED;
   }
+  const bool mx_scores = io && io->mx_scores;
   if (!aligned16(x) || !aligned16(y) || !aligned16(wm->W1) || !aligned16(wm->W2) ||
       (reinterpret_cast<uintptr_t>(wm->W1_scales) & 3) ||
       (reinterpret_cast<uintptr_t>(wm->W2_scales) & 3))
@@ -1178,8 +1195,26 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
   const int64_t W = (int64_t)d->H * d->d_v;
   float* O = static_cast<float*>(lw.O);
   auto attention = [&](const void* q, const void* k, const void* v, int64_t ld) {
-    return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, O, W,
-                         /*out_f32=*/true, lw.attn, st);
+    if (!mx_scores)
+      return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, O, W,
+                           /*out_f32=*/true, lw.attn, st);
+    // Q and K are adjacent column blocks of each U|V|Q|K row: one pass
+    // quantizes them as 2H heads
+    const int64_t hq = (int64_t)d->H * d->d_qk;
+    if (static_cast<const char*>(k) != static_cast<const char*>(q) + 2 * hq)
+      return HSTU_ERR_INVALID_ARG;
+    {
+      HSTU_TIMED(TT_MX_QUANT, st);
+      HSTU_TRY(launch_mx_quant_heads(q, ld, d->T, 2 * d->H, d->d_qk, m.qk8, 2 * hq, m.qks, st));
+    }
+    hstu_attn_mx_qk qk;
+    qk.q_codes = m.qk8;
+    qk.k_codes = m.qk8 + hq;
+    qk.ld_codes = 2 * hq;
+    qk.q_scales = m.qks;
+    qk.k_scales = m.qks + d->H * d->T;
+    return attn_fwd_impl(d, nullptr, nullptr, 0, v, ld, offs, ts, w->rab_pos, w->rab_time, nc,
+                         O, W, /*out_f32=*/true, lw.attn, st, &qk);
   };
   MxPlan plan;
   plan.wm = wm;

@@ -133,34 +133,50 @@ int quant_grid(int64_t blocks) {
 // along each head's d channels; codes [T][ld_codes] bytes (head h at byte
 // h*d) and one scale word per (head, row), head-major: scales[h*T + t],
 // byte b = the E8M0 scale of channels 32b..32b+31 (d <= 128; unused bytes
-// zero), so that a key tile's words are one contiguous run.  One lane per
-// (head, row), consecutive lanes on consecutive rows.
+// zero), so that a key tile's words are one contiguous run.  A workgroup
+// takes 16 rows: thread i encodes block i of them (blocks numbered along
+// each row, so consecutive threads read and write consecutive 64- and
+// 32-byte pieces), the scale bytes meet in LDS, and the 16 words of each
+// head go out as one contiguous 64-byte run.
+constexpr int MXH_ROWS = 16;
 __global__ __launch_bounds__(256) void k_mx_quant_heads(const bf16* __restrict__ in, int64_t ld,
                                                         int64_t T, int H, int d,
                                                         uint8_t* __restrict__ codes,
                                                         int64_t ld_codes,
                                                         uint32_t* __restrict__ scales) {
-  const int64_t total = T * H;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * 256) {
-    const int64_t h = i / T, t = i - h * T;
-    const bf16* p = in + t * ld + h * d;
-    u32x4* dst = reinterpret_cast<u32x4*>(codes + t * ld_codes + h * d);
-    uint32_t word = 0;
-    for (int kb = 0; kb < d / 32; ++kb) {
+  __shared__ uint32_t wsc[MXH_ROWS * 64];  // [row][head] words, H <= 64
+  const int nb = d / 32;
+  const int bpr = H * nb;  // blocks per row
+  const int64_t ngroups = (T + MXH_ROWS - 1) / MXH_ROWS;
+  for (int64_t grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+    const int64_t t0 = grp * MXH_ROWS;
+    const int rows = (int)min<int64_t>(MXH_ROWS, T - t0);
+    for (int i = threadIdx.x; i < MXH_ROWS * 64; i += 256) wsc[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < rows * bpr; i += 256) {
+      const int r = i / bpr, c = i - r * bpr;  // c = h * nb + kb
+      const bf16* p = in + (t0 + r) * ld + 32 * c;
       float v[32];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(p + 32 * kb + 8 * q);
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(p + 8 * q);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[8 * q + e] = bf2f(x[e]);
       }
       uint32_t out[8];
-      word |= (uint32_t)mx_block(v, out) << (8 * kb);
-      dst[2 * kb] = u32x4{out[0], out[1], out[2], out[3]};
-      dst[2 * kb + 1] = u32x4{out[4], out[5], out[6], out[7]};
+      const uint32_t sb = (uint32_t)mx_block(v, out);
+      u32x4* dst = reinterpret_cast<u32x4*>(codes + (t0 + r) * ld_codes + 32 * c);
+      dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+      dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+      const int h = c / nb, kb = c - h * nb;
+      atomicOr(&wsc[r * 64 + h], sb << (8 * kb));
     }
-    scales[h * T + t] = word;
+    __syncthreads();
+    for (int i = threadIdx.x; i < H * MXH_ROWS; i += 256) {
+      const int h = i / MXH_ROWS, r = i - h * MXH_ROWS;
+      if (r < rows) scales[h * T + t0 + r] = wsc[r * 64 + h];
+    }
+    __syncthreads();
   }
 }
 
@@ -178,12 +194,14 @@ hipError_t launch_mx_quant_heads(const void* x, int64_t ld, int64_t T, int H, in
                                  uint8_t* codes, int64_t ld_codes, uint32_t* scales,
                                  hipStream_t st) {
   if (T <= 0 || H <= 0) return hipSuccess;
-  if (d % 32 || d > 128 || ld < (int64_t)H * d || (ld % 8) || ld_codes < (int64_t)H * d ||
+  if (d % 32 || d > 128 || H > 64 || ld < (int64_t)H * d || (ld % 8) ||
+      ld_codes < (int64_t)H * d ||
       (ld_codes % 16) || (reinterpret_cast<uintptr_t>(x) & 15) ||
       (reinterpret_cast<uintptr_t>(codes) & 15) || (reinterpret_cast<uintptr_t>(scales) & 3))
     return hipErrorInvalidValue;
-  k_mx_quant_heads<<<quant_grid(T * H), 256, 0, st>>>(static_cast<const bf16*>(x), ld, T, H, d,
-                                                       codes, ld_codes, scales);
+  const int64_t groups = (T + MXH_ROWS - 1) / MXH_ROWS;
+  k_mx_quant_heads<<<(unsigned)std::min<int64_t>(groups, 8192), 256, 0, st>>>(
+      static_cast<const bf16*>(x), ld, T, H, d, codes, ld_codes, scales);
   return hipGetLastError();
 }
 

@@ -361,7 +361,9 @@ hstu_status hstu_mx_gemm(int64_t M, int64_t N, int64_t K, const void* a, const v
  *
  * hstu_mx_quantize_heads: MXFP8 of x [T][H*d] bf16 (row stride ld
  * elements, a multiple of 8; x 16-byte aligned) along each head's d
- * channels (d a multiple of 32, at most 128): codes [T][ld_codes] bytes
+ * channels (d a multiple of 32, at most 128; H at most 64; q and k side by
+ * side, as in the layer's U|V|Q|K rows, can be quantized in one call as 2H
+ * heads): codes [T][ld_codes] bytes
  * (head h at byte h*d; ld_codes >= H*d, a multiple of 16; codes 16-byte
  * aligned) and one 32-bit scale word per head and row, head-major:
  * scales[h*T + t], byte b = the E8M0 scale of channels 32b..32b+31 of head
@@ -419,6 +421,12 @@ typedef struct {
   /* receive the quantized gated output G ([T][H*d_v], [T][H*d_v/32]) */
   void* g_codes;
   void* g_scales;
+  /* 1: the attention's score product in MXFP8 too (as hstu_attn_fwd_mx: q
+   * and k quantized along each head's channels inside the call, into the
+   * workspace); inference only (saved must be NULL), d_qk = d_v in {64, 128},
+   * no semi-local windows, key_splits 0 or 1, else HSTU_ERR_UNSUPPORTED.
+   * 0: bf16 attention. */
+  int32_t mx_scores;
 } hstu_mx_io;  /* each pair NULL or both given; codes 16-, scales 4-byte aligned */
 size_t hstu_layer_fwd_mx_workspace_size(const hstu_layer_desc* desc);
 hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* desc, const void* x,

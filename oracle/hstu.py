@@ -95,6 +95,15 @@ INT31_MAX = (1 << 31) - 1
 # Elementwise pieces
 # ----------------------------------------------------------------------------
 
+def bf16_round(x) -> np.ndarray:
+    """x rounded to float32 and then to bfloat16 (8 significant bits), both
+    to nearest with ties to even, returned as float64: a finite value
+    m 2^e with m in [0.5, 1) becomes rint(256 m) 2^(e - 8)."""
+    f = np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+    m, e = np.frexp(f)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 def sigmoid(x: np.ndarray) -> np.ndarray:
     """Logistic function via the exact identity 1/(1+e^-x) = (1 + tanh(x/2)) / 2."""
     return 0.5 * (1.0 + np.tanh(0.5 * x))
@@ -640,19 +649,28 @@ def mx_matmul(a, b):
 
 def layer_fwd_mx(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_candidates,
                  f: LayerFlags, b1=None, b2=None, gamma=None, beta=None, return_g=False,
-                 return_saved=False):
+                 return_saved=False, mx_scores=False):
     """One layer with MXFP8 projection and output matmuls (steps 1 and 4);
     attention, LayerNorm and gating as in layer_fwd.  return_g: also the
     gated output G before its quantization; return_saved: also the
-    intermediates layer_bwd_mx needs (as layer_fwd's)."""
+    intermediates layer_bwd_mx needs (as layer_fwd's).  mx_scores: the
+    attention's score product in MXFP8 as well (attn_fwd_mx; no windows).
+    Reading: q and k are quantized from the layer's stored bf16 U|V|Q|K
+    (bf16_round of Zh), the precision in which the kernels decide those
+    codes."""
     X = np.asarray(X, np.float64)
     Z = mx_matmul(X, W1)
     if b1 is not None:
         Z = Z + np.asarray(b1, np.float64)
     Zh = silu(Z) if f.proj_silu else Z
     U, V, Q, K = split_uvqk(Zh, f)
-    O = attn_fwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
-                 f.norm_mode, f.norm_len, win_local=f.win_local, win_global=f.win_global)
+    if mx_scores:
+        assert f.win_local == 0
+        O = attn_fwd_mx(bf16_round(Q), bf16_round(K), V, seq_offsets, timestamps, rab_pos,
+                        rab_time, num_candidates, f.norm_mode, f.norm_len)
+    else:
+        O = attn_fwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
+                     f.norm_mode, f.norm_len, win_local=f.win_local, win_global=f.win_global)
     O2 = O.reshape(X.shape[0], f.H * f.d_v)
     Yn, mu, rstd, xhat = layernorm_fwd(O2, f.eps, gamma, beta)
     G = Yn * U

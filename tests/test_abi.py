@@ -306,7 +306,35 @@ def test_mx_attention_argument_errors(L):
     q = L.hstu_mx_quantize_heads
     assert q(10, 2, 48, p, 128, p, 128, p, None) == -1       # d not a multiple of 32
     assert q(10, 2, 160, p, 512, p, 512, p, None) == -1      # d above 128
+    assert q(10, 65, 32, p, 2080, p, 2080, p, None) == -1    # more than 64 heads
     assert q(10, 2, 64, p, 100, p, 128, p, None) == -1       # ld below H*d
     assert q(10, 2, 64, p, 128, p, 136, p, None) == -1       # codes stride not 16-byte
     assert q(10, 2, 64, odd, 128, p, 128, p, None) == -1     # misaligned input
     assert q(10, 2, 64, p, 128, p, 128, C.c_void_p((1 << 20) + 2), None) == -1
+
+
+def test_mx_layer_scores_argument_errors(L):
+    """hstu_layer_fwd_mx with mx_scores: descriptors the MX-score attention
+    does not take, training (saved) and flag values other than 0/1 are
+    refused before launch."""
+    buf = C.create_string_buffer(1 << 22)
+    ws = C.c_void_p((C.addressof(buf) + 255) & ~255)
+    p = C.c_void_p(1 << 20)
+    w = _lib.LayerWeights(p, p, None, None, None, None, p, p)
+    m = _lib.MxWeights(p, p, p, p)
+    sv = _lib.LayerSaved(p, p, p, p, p, p)
+
+    def call(ad, flag, saved=None):
+        ld = _lib.LayerDesc(ad, 128, 1, 1, 1e-6)
+        nb = L.hstu_layer_fwd_mx_workspace_size(C.byref(ld))
+        io = _lib.MxIO(None, None, None, None, None, None, flag)
+        return L.hstu_layer_fwd_mx(C.byref(ld), p, C.byref(w), C.byref(m), p, p, None,
+                                   C.c_void_p((1 << 20) + 4096), C.byref(io),
+                                   None if saved is None else C.byref(saved), ws,
+                                   max(nb, 1 << 21), None)
+    ok = dict(T=300, H=2, d_qk=64, d_v=64)
+    assert call(_desc(**ok), 2) == -1                                # flag not 0/1
+    assert call(_desc(**ok, win_local=16), 1) == -2                  # windows
+    assert call(_desc(T=300, H=4, d_qk=32, d_v=32), 1) == -2         # d_qk 32
+    assert call(_desc(**ok, key_splits=3), 1) == -2                  # key split
+    assert call(_desc(**ok), 1, saved=sv) == -2                      # training

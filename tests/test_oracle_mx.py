@@ -377,3 +377,42 @@ def test_attn_mx_matches_brute_force_on_searched_roundings():
     np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
     # the rounding is not a no-op here
     assert np.abs(got - orc.attn_fwd(q, k, v, offs, ts, rp, rt, nc, norm_len=16)).max() > 1e-6
+
+
+def test_bf16_round_against_torch_and_ties():
+    """The oracle's bf16 rounding equals torch's float32 -> bfloat16
+    conversion (round to nearest even) on spread values, and sends exact
+    midpoints to the even neighbour."""
+    import torch
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-30, 30, 20000))).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.bf16_round(x), want)
+    k = np.arange(128, 256, dtype=np.float64)
+    mid = (k + 0.5) / 128.0                       # halfway between bf16 neighbours in [1, 2)
+    even = np.where(k % 2 == 0, k, k + 1) / 128.0
+    np.testing.assert_array_equal(orc.bf16_round(mid), even)
+    assert orc.bf16_round(0.0) == 0.0 and orc.bf16_round(-3.0) == -3.0
+
+
+def test_mx_layer_scores_quantize_the_bf16_activations():
+    """layer_fwd_mx with mx_scores equals its composition written out: the
+    MX projection, SiLU, the attention with q and k rounded to bf16 and then
+    to MXFP8, and the plain LayerNorm-gate and MX output product."""
+    X, W1, W2, dY, rp, rt, offs, ts, f = _mx_case(41)
+    f = orc.LayerFlags(H=f.H, d_qk=32, d_v=32, norm_len=16, eps=1e-3)
+    Y = orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f, mx_scores=True)
+    Zh = orc.silu(orc.mx_matmul(X, W1))
+    T, H, d = X.shape[0], f.H, 32
+    U, V, Q, K = (Zh[:, i * H * d:(i + 1) * H * d].reshape(T, H, d) for i in range(4))
+    qc, qs = orc.mx_quantize(orc.bf16_round(Q), axis=2)
+    kc, ks = orc.mx_quantize(orc.bf16_round(K), axis=2)
+    O = orc.attn_fwd(orc.mx_dequantize(qc, qs, axis=2), orc.mx_dequantize(kc, ks, axis=2), V,
+                     offs, ts, rp, rt, None, 0, 16).reshape(T, H * d)
+    mu = O.mean(axis=1, keepdims=True)
+    var = ((O - mu) ** 2).mean(axis=1, keepdims=True)
+    G = (O - mu) / np.sqrt(var + 1e-3) * U.reshape(T, H * d)
+    want = orc.mx_matmul(G, W2) + X
+    np.testing.assert_allclose(Y, want, rtol=1e-10, atol=1e-12)
+    # and the score rounding changes the layer
+    assert np.abs(Y - orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f)).max() > 0
