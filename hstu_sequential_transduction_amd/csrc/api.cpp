@@ -705,6 +705,10 @@ struct MxPlan {
   uint8_t* gs = nullptr;
   uint8_t* y8 = nullptr;  // optional MXFP8 copy of Y (the next layer's X)
   uint8_t* ys = nullptr;
+  // optional MXFP8 copy of the attention's Q|K columns ([T][2 H d_qk] codes,
+  // [2H][T] scale words), written by the projection's epilogue
+  uint8_t* qk8 = nullptr;
+  uint32_t* qks = nullptr;
 };
 
 template <typename Attn>
@@ -754,6 +758,13 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
     g1.b_kcont = true;
     g1.scale_a = mx->xs;
     g1.scale_b = static_cast<const uint8_t*>(mx->wm->W1_scales);
+    if (mx->qk8) {
+      g1.qk_codes = mx->qk8;
+      g1.qk_scales = reinterpret_cast<uint8_t*>(mx->qks);
+      g1.qk_col0 = 2 * (int64_t)d->H * d->d_v;
+      g1.qk_cols = 2 * (int64_t)d->H * d->d_qk;
+      g1.qk_d = d->d_qk;
+    }
   }
   { HSTU_TIMED(TT_GEMM_UVQK, st); HSTU_TRY(launch_gemm(g1, d->dtype, st)); }
   if (!L->proj_silu && Zsave) {
@@ -1198,12 +1209,13 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
     if (!mx_scores)
       return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, O, W,
                            /*out_f32=*/true, lw.attn, st);
-    // Q and K are adjacent column blocks of each U|V|Q|K row: one pass
-    // quantizes them as 2H heads
+    // Q|K as MXFP8 (codes [T][2 H d_qk], scale words of the 2H heads Q then
+    // K): written by the projection's SiLU epilogue, or, without the SiLU,
+    // by one pass over the adjacent Q and K column blocks
     const int64_t hq = (int64_t)d->H * d->d_qk;
-    if (static_cast<const char*>(k) != static_cast<const char*>(q) + 2 * hq)
-      return HSTU_ERR_INVALID_ARG;
-    {
+    if (!L->proj_silu) {
+      if (static_cast<const char*>(k) != static_cast<const char*>(q) + 2 * hq)
+        return HSTU_ERR_INVALID_ARG;
       HSTU_TIMED(TT_MX_QUANT, st);
       HSTU_TRY(launch_mx_quant_heads(q, ld, d->T, 2 * d->H, d->d_qk, m.qk8, 2 * hq, m.qks, st));
     }
@@ -1234,6 +1246,10 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
   if (io && io->y_codes) {
     plan.y8 = static_cast<uint8_t*>(io->y_codes);
     plan.ys = static_cast<uint8_t*>(io->y_scales);
+  }
+  if (mx_scores && L->proj_silu) {
+    plan.qk8 = m.qk8;
+    plan.qks = m.qks;
   }
   if (saved) {
     float* So = static_cast<float*>(saved->O);

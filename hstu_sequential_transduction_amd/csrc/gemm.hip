@@ -414,6 +414,29 @@ HSTU_DEV void g2_epilogue(const GemmArgs& g, f32x16 (&acc)[FM][FN], float* stg, 
 #pragma unroll
         for (int e = 0; e < 4; ++e) sv[e] = silu_f(v[e]);
         put(g.C, sv, false);
+        if constexpr (MX) {
+          // the attention's q|k columns also as MXFP8 along each head's
+          // channels (the 32-column blocks and the range are aligned, so the
+          // eight lanes of a block take this branch together)
+          const int64_t cq = ncol - g.qk_col0;
+          if (g.qk_codes && cq >= 0 && cq < g.qk_cols) {
+            float q[4], am = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              q[e] = (float)(bf16)sv[e];
+              am = fmaxf(am, fabsf(q[e]));
+            }
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+            const int sh = mx_shared_exp(am);
+            *reinterpret_cast<uint32_t*>(g.qk_codes + m * g.qk_cols + cq) =
+                mx_cvt4(q[0], q[1], q[2], q[3], sh);
+            if ((lc & 7) == 0) {
+              const int64_t hq = cq / g.qk_d, kb = (cq - hq * g.qk_d) / 32;
+              g.qk_scales[(hq * g.M + m) * 4 + kb] = (uint8_t)(sh + 127);
+            }
+          }
+        }
       } else {
         put(g.C, v, OUTF32);
       }
@@ -876,6 +899,12 @@ hipError_t gemm2_mx(const GemmArgs& g, hipStream_t st) {
     return hipErrorInvalidValue;
   if (g.c_codes && (g.epi != EPI_RESID || g.c_f32 || (g.N % 32) || !g.c_scales ||
                     (reinterpret_cast<uintptr_t>(g.c_codes) & 3)))
+    return hipErrorInvalidValue;
+  if (g.qk_codes && (g.epi != EPI_SILU || !g.qk_scales || g.qk_d <= 0 || g.qk_d % 32 ||
+                     g.qk_d > 128 || g.qk_col0 % 32 || g.qk_cols % g.qk_d ||
+                     g.qk_col0 < 0 || g.qk_col0 + g.qk_cols > g.N ||
+                     (reinterpret_cast<uintptr_t>(g.qk_codes) & 3) ||
+                     (reinterpret_cast<uintptr_t>(g.qk_scales) & 3)))
     return hipErrorInvalidValue;
   constexpr int BM = 128, BN = 128, NT = 64 * G2_NW;
   const int mt = (int)((g.M + BM - 1) / BM), nt = (int)((g.N + BN - 1) / BN);

@@ -228,6 +228,15 @@ struct GemmArgs {
   // (codes [M][N], scales [M][N/32]; N a multiple of 32)
   uint8_t* c_codes = nullptr;
   uint8_t* c_scales = nullptr;
+  // MX kernels, EPI_SILU: also write the (bf16-rounded) SiLU outputs of
+  // columns [qk_col0, qk_col0 + qk_cols) as MXFP8 along each head's qk_d
+  // channels, the attention's q|k operands: codes [M][qk_cols], head-major
+  // scale words (qk_scales bytes, word h*M + m, byte = 32-channel block of the
+  // head; bytes past qk_d/32 are not written)
+  uint8_t* qk_codes = nullptr;
+  uint8_t* qk_scales = nullptr;
+  int64_t qk_col0 = 0, qk_cols = 0;
+  int qk_d = 0;
 };
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st);
 // Split-K reduction: out[m*ldo + n] = sum_z partial[z][m][n]  (fp32)

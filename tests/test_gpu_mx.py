@@ -206,6 +206,33 @@ def test_mx_layer_fwd(B, ci, hist, c, variant, mx_scores):
     assert rel < 0.15
 
 
+def test_mx_layer_scores_without_the_projection_silu(B):
+    """mx_scores on a layer without the projection's SiLU: Q|K are then
+    quantized by a separate pass instead of the projection's epilogue; Y - X
+    against the oracle's MX-score layer to the bf16 tolerance in norm."""
+    import dataclasses
+    import torch
+    cfg = synth.get_config(5).shrunk(B=3, lengths=("list", [100, 300, 64]), num_candidates=40,
+                                     n_layers=1).unit_scale()
+    inp = synth.make_inputs(cfg, seed=1777)
+    w = inp.layers[0]
+    td = torch.bfloat16
+    wm = B.MxLayerWeights.from_bf16(dev(w.W1, td), dev(w.W2, td))
+    lc = dataclasses.replace(_lcfg(B, cfg), proj_silu=False)
+    y = B.hstu_layer_fwd_mx(dev(inp.X, td), wm, dev(w.rab_pos), dev(w.rab_time),
+                            dev(inp.seq_offsets.astype(np.int32)), dev(inp.timestamps), lc,
+                            num_candidates=dev(inp.num_candidates.astype(np.int32)),
+                            mx_scores=True)
+    f = orc.LayerFlags(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len, eps=1e-6,
+                       proj_silu=False)
+    want = orc.layer_fwd_mx(inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                            inp.timestamps, inp.num_candidates, f, mx_scores=True)
+    got = host(y)
+    rel = np.linalg.norm((got - inp.X) - (want - inp.X)) / np.linalg.norm(want - inp.X)
+    say(f"  mx scores, no projection SiLU: relative L2 of Y - X {rel:.4f}")
+    assert rel < 2e-2
+
+
 def test_mx_layer_chain_hands_y_codes_to_the_next_layer(B):
     """The output product's epilogue writes Y in MXFP8 for the next layer:
     those codes equal the quantizer's on the stored bf16 Y, and a two-layer
