@@ -894,7 +894,7 @@ def main():
                     help="timed runs of each forward-only workload")
     ap.add_argument("--only", default="",
                     help="comma list of parts to run (" + ",".join(ALL_PARTS) + "); "
-                         "fwd may name workloads, e.g. fwd3 or fwd2+fwd5")
+                         "fwd and attnmx may name workloads, e.g. fwd3 or fwd2+fwd5")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the data-parallel "
@@ -909,11 +909,15 @@ def main():
 
     parts = set(ALL_PARTS)
     fwd_cfgs = (2, 3, 5)
+    attnmx_cfgs = []
     if args.only:
         parts, picked = set(), []
         for tok in args.only.replace("+", ",").split(","):
             tok = tok.strip()
-            if tok.startswith("fwd") and tok != "fwd":
+            if tok.startswith("attnmx") and tok != "attnmx":
+                attnmx_cfgs.append(int(tok[6:]))
+                parts.add("attnmx")
+            elif tok.startswith("fwd") and tok != "fwd":
                 picked.append(int(tok[3:]))
                 parts.add("fwd")
             elif tok:
@@ -964,7 +968,8 @@ def main():
     if "mx" in parts:
         line["mxfp8"] = bench_mx(timer)
     if "attnmx" in parts:
-        line["attention_mxfp8_scores"] = bench_attn_mx(timer)
+        line["attention_mxfp8_scores"] = bench_attn_mx(
+            timer, tuple(attnmx_cfgs) if attnmx_cfgs else (3, 5, 4), reps=args.reps)
     if "epilogue" in parts:
         line["ln_gate_epilogue"] = bench_epilogue(timer)
     if "peaks" in parts:
