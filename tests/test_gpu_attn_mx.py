@@ -110,6 +110,52 @@ def test_attn_fwd_mx_edge_sequences(B, ks):
     check_close(got, want, "bf16", "O mx edge")
 
 
+@pytest.mark.parametrize("ks", [0, 1])
+def test_attn_fwd_mx_unsorted_and_wide_timestamps(B, ks):
+    """The MX kernels share the bias paths: negative time distances (bucket 0)
+    and a span beyond 2^31 s (the 64-bit path)."""
+    import dataclasses
+    cfg = synth.get_config(2).shrunk(B=3, lengths=("list", [150, 90, 200]))
+    a = synth.make_attn_inputs(cfg, seed=19)
+    rng = np.random.default_rng(19)
+    ts = a.timestamps.copy()
+    o = a.seq_offsets
+    ts[o[0]:o[1]] = ts[o[0]] + rng.integers(-5000, 5000, size=150)          # unsorted
+    ts[o[1]:o[2]] = np.sort(rng.integers(0, 1 << 40, size=90))               # wide span
+    a = dataclasses.replace(a, timestamps=ts)
+    got = _run(B, a, cfg, ks)
+    want = orc.attn_fwd_mx(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
+                           None, 0, cfg.norm_len)
+    check_close(got, want, "bf16", f"O mx unsorted/wide key_splits={ks}")
+
+
+def test_attn_fwd_mx_reused_plan_across_calls(B):
+    """reuse_plan with the MX entry point: a second call on the same batch and
+    workspace skips the plan and gives the same output bit for bit."""
+    import dataclasses
+    import torch
+    cfg = synth.get_config(5).shrunk(B=3, lengths=("list", [300, 100, 64]), num_candidates=20)
+    a = synth.make_attn_inputs(cfg, seed=23)
+    T = a.q.shape[0]
+    qc, qs = _quantize_checked(B, a.q, cfg.H, cfg.d_qk)
+    kc, ksw = _quantize_checked(B, a.k, cfg.H, cfg.d_qk)
+    v = dev(a.v.reshape(T, -1), torch.bfloat16)
+    offs, ts = dev(a.seq_offsets.astype(np.int32)), dev(a.timestamps.astype(np.int64))
+    rp, rt = dev(a.rab_pos), dev(a.rab_time)
+    nc = dev(a.num_candidates.astype(np.int32))
+    ws = B.LayerWorkspace()
+    ac = _ac(B, cfg)
+    first = B.hstu_attn_fwd_mx(qc, qs, kc, ksw, v, offs, ts, rp, rt, ac, num_candidates=nc,
+                               workspace=ws)
+    again = B.hstu_attn_fwd_mx(qc, qs, kc, ksw, v, offs, ts, rp, rt,
+                               dataclasses.replace(ac, reuse_plan=1), num_candidates=nc,
+                               workspace=ws)
+    assert torch.equal(first, again)
+    want = orc.attn_fwd_mx(a.q, a.k, a.v, a.seq_offsets, a.timestamps, a.rab_pos, a.rab_time,
+                           a.num_candidates, 0, cfg.norm_len)
+    check_close(host(again).reshape(a.v.shape), want, "bf16", "O mx reused plan")
+
+
 @pytest.mark.parametrize("ci", [4, 5])
 def test_attn_fwd_mx_full_size_sampled_rows(B, ci):
     """The training (d 128) and ranking (d 64) batches at full size, checked
