@@ -53,7 +53,8 @@ def _run(binding, a, cfg, ks=0):
     qc, qs = _quantize_checked(binding, a.q, cfg.H, cfg.d_qk)
     kc, ksw = _quantize_checked(binding, a.k, cfg.H, cfg.d_qk)
     nc = None if a.num_candidates is None else dev(a.num_candidates.astype(np.int32))
-    out = binding.hstu_attn_fwd_mx(qc, qs, kc, ksw, dev(a.v.reshape(T, -1), torch.bfloat16),
+    out = binding.hstu_attn_fwd_mx(qc, qs, kc, ksw,
+                                   dev(a.v.reshape(T, cfg.H * cfg.d_v), torch.bfloat16),
                                    dev(a.seq_offsets.astype(np.int32)),
                                    dev(a.timestamps.astype(np.int64)), dev(a.rab_pos),
                                    dev(a.rab_time), _ac(binding, cfg, ks), num_candidates=nc)
@@ -177,6 +178,15 @@ def test_attn_fwd_mx_full_size_sampled_rows(B, ci):
     sel = np.concatenate([a.seq_offsets[b] + np.asarray(rows[b], dtype=np.int64)
                           for b in range(cfg.B)])
     check_close(got[sel], want[sel], "bf16", f"O mx full cfg{ci} sampled", scale_ref=want[sel])
+
+
+def test_attn_fwd_mx_empty_batch(B):
+    """A batch of empty sequences: nothing to quantize or attend, no error."""
+    cfg = synth.get_config(5).shrunk(B=2, lengths=("list", [0, 0]), num_candidates=0)
+    a = synth.make_attn_inputs(cfg, seed=5)
+    assert a.q.shape[0] == 0
+    got = _run(B, a, cfg)
+    assert got.shape == a.v.shape
 
 
 def test_attn_fwd_mx_unsupported(B):
