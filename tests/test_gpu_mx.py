@@ -233,10 +233,12 @@ def test_mx_layer_scores_without_the_projection_silu(B):
     assert rel < 2e-2
 
 
-def test_mx_layer_chain_hands_y_codes_to_the_next_layer(B):
+@pytest.mark.parametrize("mx_scores", [False, True])
+def test_mx_layer_chain_hands_y_codes_to_the_next_layer(B, mx_scores):
     """The output product's epilogue writes Y in MXFP8 for the next layer:
     those codes equal the quantizer's on the stored bf16 Y, and a two-layer
-    chain that passes them on is bit-identical to one quantizing X itself."""
+    chain that passes them on is bit-identical to one quantizing X itself
+    (also with the attention scores in MXFP8)."""
     import torch
     cfg = synth.get_config(5).shrunk(B=4, lengths=("list", [100, 300, 0, 64]), num_candidates=40,
                                      n_layers=2).unit_scale()
@@ -253,15 +255,30 @@ def test_mx_layer_chain_hands_y_codes_to_the_next_layer(B):
     yc = torch.empty((T, D), dtype=torch.uint8, device="cuda")
     ys = torch.empty((T, D // 32), dtype=torch.uint8, device="cuda")
     y1 = B.hstu_layer_fwd_mx(x0, ws[0][2], ws[0][0], ws[0][1], offs, ts, lc, num_candidates=nc,
-                             y_mx=(yc, ys))
+                             y_mx=(yc, ys), mx_scores=mx_scores)
     qc, qs = B.hstu_mx_quantize(y1)
     np.testing.assert_array_equal(host(ys), host(qs))
     np.testing.assert_array_equal(host(yc), host(qc))
     chained = B.hstu_layer_fwd_mx(y1, ws[1][2], ws[1][0], ws[1][1], offs, ts, lc,
-                                  num_candidates=nc, x_mx=(yc, ys))
+                                  num_candidates=nc, x_mx=(yc, ys), mx_scores=mx_scores)
     plain = B.hstu_layer_fwd_mx(y1, ws[1][2], ws[1][0], ws[1][1], offs, ts, lc,
-                                num_candidates=nc)
+                                num_candidates=nc, mx_scores=mx_scores)
     np.testing.assert_array_equal(host(chained), host(plain))
+    if mx_scores:
+        # and the two-layer MX-score chain against the oracle's, in norm: the
+        # per-layer parity with its derived code bands is test_mx_layer_fwd;
+        # chained, the second layer quantizes inputs that already differ by
+        # those roundings (about 1.7 % per layer at this unit scale), so this
+        # reports the distance and only bounds it loosely
+        f = orc.LayerFlags(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len, eps=1e-6)
+        x = inp.X
+        for w in inp.layers:
+            x = orc.layer_fwd_mx(x, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
+                                 inp.timestamps, inp.num_candidates, f, mx_scores=True)
+        got = host(chained)
+        rel = np.linalg.norm((got - inp.X) - (x - inp.X)) / np.linalg.norm(x - inp.X)
+        say(f"  two MX-score layers: relative L2 of Y - X {rel:.4f} vs the oracle")
+        assert rel < 0.1
 
 
 TRAIN_CASES = [
