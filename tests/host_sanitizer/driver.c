@@ -92,6 +92,49 @@ int main(void) {
   EXPECT(hstu_truncate_gather(4, 100, 10, 7, HSTU_BF16, p, p, p, NULL, p, NULL, NULL) !=
          HSTU_OK);
   EXPECT(hstu_mx_quantize(4, 33, p, 64, p, p, NULL) == HSTU_ERR_INVALID_ARG);
+  /* MXFP8 attention operands and scores: extreme sizes are refused on the host */
+  EXPECT(hstu_mx_quantize_heads(-1, 2, 64, p, 128, p, 128, (uint32_t*)p, NULL) ==
+         HSTU_ERR_INVALID_ARG);
+  EXPECT(hstu_mx_quantize_heads(100, 2147483647, 64, p, 128, p, 128, (uint32_t*)p, NULL) ==
+         HSTU_ERR_INVALID_ARG);
+  EXPECT(hstu_mx_quantize_heads(100, 2, 2147483616, p, 128, p, 128, (uint32_t*)p, NULL) ==
+         HSTU_ERR_INVALID_ARG);
+  {
+    hstu_attn_desc dm = desc();
+    dm.d_qk = 64;
+    dm.d_v = 64;
+    hstu_attn_mx_qk qk;
+    qk.q_codes = p;
+    qk.k_codes = p;
+    qk.ld_codes = 128;
+    qk.q_scales = (const uint32_t*)p;
+    qk.k_scales = (const uint32_t*)p;
+    EXPECT(hstu_attn_fwd_mx(&dm, NULL, p, 128, p, p, p, p, NULL, p, 128, ws, 4096, NULL) ==
+           HSTU_ERR_INVALID_ARG);
+    qk.ld_codes = -16;
+    EXPECT(hstu_attn_fwd_mx(&dm, &qk, p, 128, p, p, p, p, NULL, p, 128, ws, 4096, NULL) ==
+           HSTU_ERR_INVALID_ARG);
+    qk.ld_codes = 128;
+    EXPECT(hstu_attn_fwd_mx(&dm, &qk, p, 128, p, p, p, p, NULL, p, 128, ws, 16, NULL) ==
+           HSTU_ERR_WORKSPACE);
+    dm.d_qk = 32;
+    dm.d_v = 32;
+    EXPECT(hstu_attn_fwd_mx(&dm, &qk, p, 128, p, p, p, p, NULL, p, 128, ws, 4096, NULL) ==
+           HSTU_ERR_UNSUPPORTED);
+    /* the MX layer's workspace with room for MXFP8 scores at a huge T */
+    hstu_layer_desc Lm;
+    memset(&Lm, 0, sizeof Lm);
+    Lm.attn = desc();
+    Lm.attn.d_qk = 128;
+    Lm.attn.d_v = 128;
+    Lm.attn.H = 4;
+    Lm.attn.T = (int64_t)1 << 34;
+    Lm.D = 512;
+    Lm.proj_silu = 1;
+    Lm.residual = 1;
+    Lm.ln_eps = 1e-6f;
+    (void)hstu_layer_fwd_mx_workspace_size(&Lm);
+  }
   EXPECT(hstu_set_check_mode(7) == HSTU_ERR_INVALID_ARG);
   EXPECT(hstu_check_mode() == 0);
 
