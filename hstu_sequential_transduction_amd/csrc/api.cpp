@@ -709,6 +709,7 @@ struct MxPlan {
   // [2H][T] scale words), written by the projection's epilogue
   uint8_t* qk8 = nullptr;
   uint32_t* qks = nullptr;
+  bool qk_dequant = false;  // store Q|K as their MXFP8 values too (training)
 };
 
 template <typename Attn>
@@ -764,6 +765,7 @@ hstu_status layer_fwd_steps(const hstu_layer_desc* L, const void* x, const hstu_
       g1.qk_col0 = 2 * (int64_t)d->H * d->d_v;
       g1.qk_cols = 2 * (int64_t)d->H * d->d_qk;
       g1.qk_d = d->d_qk;
+      g1.qk_dequant = mx->qk_dequant;
     }
   }
   { HSTU_TIMED(TT_GEMM_UVQK, st); HSTU_TRY(launch_gemm(g1, d->dtype, st)); }
@@ -1183,7 +1185,10 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
         !pair_ok(io->g_codes, io->g_scales))
       return HSTU_ERR_INVALID_ARG;
     if (io->mx_scores != 0 && io->mx_scores != 1) return HSTU_ERR_INVALID_ARG;
-    if (io->mx_scores && (saved || !mx_scores_ok(d))) return HSTU_ERR_UNSUPPORTED;
+    // training (saved) needs the projection's SiLU epilogue, which stores q
+    // and k as their MXFP8 values for the backward
+    if (io->mx_scores && (!mx_scores_ok(d) || (saved && !L->proj_silu)))
+      return HSTU_ERR_UNSUPPORTED;
   }
   const bool mx_scores = io && io->mx_scores;
   if (!aligned16(x) || !aligned16(y) || !aligned16(wm->W1) || !aligned16(wm->W2) ||
@@ -1204,7 +1209,8 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
     plans_forget(ws, ws_bytes);
   }
   const int64_t W = (int64_t)d->H * d->d_v;
-  float* O = static_cast<float*>(lw.O);
+  // O: the workspace's (inference) or saved->O (training)
+  float* O = saved ? static_cast<float*>(saved->O) : static_cast<float*>(lw.O);
   auto attention = [&](const void* q, const void* k, const void* v, int64_t ld) {
     if (!mx_scores)
       return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, O, W,
@@ -1250,16 +1256,11 @@ hstu_status hstu_layer_fwd_mx(const hstu_layer_desc* L, const void* x, const hst
   if (mx_scores && L->proj_silu) {
     plan.qk8 = m.qk8;
     plan.qks = m.qks;
+    plan.qk_dequant = saved != nullptr;
   }
-  if (saved) {
-    float* So = static_cast<float*>(saved->O);
-    auto attention_s = [&](const void* q, const void* k, const void* v, int64_t ld) {
-      return attn_fwd_impl(d, q, k, ld, v, ld, offs, ts, w->rab_pos, w->rab_time, nc, So, W,
-                           /*out_f32=*/true, lw.attn, st);
-    };
-    return layer_fwd_steps(L, x, w, y, saved->Z, saved->Zh, So, saved->G, saved->mu,
-                           saved->rstd, attention_s, st, &plan);
-  }
+  if (saved)
+    return layer_fwd_steps(L, x, w, y, saved->Z, saved->Zh, O, saved->G, saved->mu,
+                           saved->rstd, attention, st, &plan);
   return layer_fwd_steps(L, x, w, y, nullptr, lw.Zh, O, lw.G, nullptr, nullptr, attention, st,
                          &plan);
 }

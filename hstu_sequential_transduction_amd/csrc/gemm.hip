@@ -429,8 +429,18 @@ HSTU_DEV void g2_epilogue(const GemmArgs& g, f32x16 (&acc)[FM][FN], float* stg, 
 #pragma unroll
             for (int o = 1; o < 8; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
             const int sh = mx_shared_exp(am);
-            *reinterpret_cast<uint32_t*>(g.qk_codes + m * g.qk_cols + cq) =
-                mx_cvt4(q[0], q[1], q[2], q[3], sh);
+            const uint32_t w4 = mx_cvt4(q[0], q[1], q[2], q[3], sh);
+            *reinterpret_cast<uint32_t*>(g.qk_codes + m * g.qk_cols + cq) = w4;
+            if (g.qk_dequant) {
+              // the stored q|k become their MXFP8 values (exact in bf16),
+              // over the bf16 values the same lane stored above
+              float dq[4];
+              dq[0] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w4, 0), sh);
+              dq[1] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w4, 1), sh);
+              dq[2] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w4, 2), sh);
+              dq[3] = ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)w4, 3), sh);
+              put(g.C, dq, false);
+            }
             if ((lc & 7) == 0) {
               const int64_t hq = cq / g.qk_d, kb = (cq - hq * g.qk_d) / 32;
               g.qk_scales[(hq * g.M + m) * 4 + kb] = (uint8_t)(sh + 127);

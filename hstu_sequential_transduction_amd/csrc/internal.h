@@ -237,6 +237,9 @@ struct GemmArgs {
   uint8_t* qk_scales = nullptr;
   int64_t qk_col0 = 0, qk_cols = 0;
   int qk_d = 0;
+  // also store those columns of C as their MXFP8 values (training: the
+  // backward then differentiates the scores the forward computed)
+  bool qk_dequant = false;
 };
 hipError_t launch_gemm(const GemmArgs& g, int dtype, hipStream_t st);
 // Split-K reduction: out[m*ldo + n] = sum_z partial[z][m][n]  (fp32)

@@ -423,8 +423,11 @@ typedef struct {
   void* g_scales;
   /* 1: the attention's score product in MXFP8 too (as hstu_attn_fwd_mx: q
    * and k quantized along each head's channels inside the call, into the
-   * workspace); inference only (saved must be NULL), d_qk = d_v in {64, 128},
-   * no semi-local windows, key_splits 0 or 1, else HSTU_ERR_UNSUPPORTED.
+   * workspace); d_qk = d_v in {64, 128}, no semi-local windows, key_splits
+   * 0 or 1, else HSTU_ERR_UNSUPPORTED.  With `saved` (training; the layer
+   * must have its projection SiLU) the stored U|V|Q|K holds q and k as their
+   * MXFP8 values, so that hstu_layer_bwd_mx differentiates the scores the
+   * forward computed (the quantizer taken as the identity).
    * 0: bf16 attention. */
   int32_t mx_scores;
 } hstu_mx_io;  /* each pair NULL or both given; codes 16-, scales 4-byte aligned */

@@ -657,7 +657,9 @@ def layer_fwd_mx(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_cand
     attention's score product in MXFP8 as well (attn_fwd_mx; no windows).
     Reading: q and k are quantized from the layer's stored bf16 U|V|Q|K
     (bf16_round of Zh), the precision in which the kernels decide those
-    codes."""
+    codes; in training (return_saved) the saved Zh holds q and k as those
+    MXFP8 values, so layer_bwd_mx differentiates the scores the forward
+    computed, the quantizer counting as the identity (as O31's)."""
     X = np.asarray(X, np.float64)
     Z = mx_matmul(X, W1)
     if b1 is not None:
@@ -666,8 +668,14 @@ def layer_fwd_mx(X, W1, W2, rab_pos, rab_time, seq_offsets, timestamps, num_cand
     U, V, Q, K = split_uvqk(Zh, f)
     if mx_scores:
         assert f.win_local == 0
-        O = attn_fwd_mx(bf16_round(Q), bf16_round(K), V, seq_offsets, timestamps, rab_pos,
-                        rab_time, num_candidates, f.norm_mode, f.norm_len)
+        qc, qs = mx_quantize(bf16_round(Q), axis=2)
+        kc, ks = mx_quantize(bf16_round(K), axis=2)
+        Qm, Km = mx_dequantize(qc, qs, axis=2), mx_dequantize(kc, ks, axis=2)
+        O = attn_fwd(Qm, Km, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
+                     f.norm_mode, f.norm_len)
+        T = X.shape[0]
+        Zh = np.concatenate([U.reshape(T, -1), V.reshape(T, -1), Qm.reshape(T, -1),
+                             Km.reshape(T, -1)], axis=1)
     else:
         O = attn_fwd(Q, K, V, seq_offsets, timestamps, rab_pos, rab_time, num_candidates,
                      f.norm_mode, f.norm_len, win_local=f.win_local, win_global=f.win_global)

@@ -315,8 +315,8 @@ def test_mx_attention_argument_errors(L):
 
 def test_mx_layer_scores_argument_errors(L):
     """hstu_layer_fwd_mx with mx_scores: descriptors the MX-score attention
-    does not take, training (saved) and flag values other than 0/1 are
-    refused before launch."""
+    does not take, training (saved) without the projection SiLU and flag
+    values other than 0/1 are refused before launch."""
     buf = C.create_string_buffer(1 << 22)
     ws = C.c_void_p((C.addressof(buf) + 255) & ~255)
     p = C.c_void_p(1 << 20)
@@ -324,8 +324,8 @@ def test_mx_layer_scores_argument_errors(L):
     m = _lib.MxWeights(p, p, p, p)
     sv = _lib.LayerSaved(p, p, p, p, p, p)
 
-    def call(ad, flag, saved=None):
-        ld = _lib.LayerDesc(ad, 128, 1, 1, 1e-6)
+    def call(ad, flag, saved=None, proj_silu=1):
+        ld = _lib.LayerDesc(ad, 128, proj_silu, 1, 1e-6)
         nb = L.hstu_layer_fwd_mx_workspace_size(C.byref(ld))
         io = _lib.MxIO(None, None, None, None, None, None, flag)
         return L.hstu_layer_fwd_mx(C.byref(ld), p, C.byref(w), C.byref(m), p, p, None,
@@ -337,4 +337,4 @@ def test_mx_layer_scores_argument_errors(L):
     assert call(_desc(**ok, win_local=16), 1) == -2                  # windows
     assert call(_desc(T=300, H=4, d_qk=32, d_v=32), 1) == -2         # d_qk 32
     assert call(_desc(**ok, key_splits=3), 1) == -2                  # key split
-    assert call(_desc(**ok), 1, saved=sv) == -2                      # training
+    assert call(_desc(**ok), 1, saved=sv, proj_silu=0) == -2         # training without SiLU

@@ -282,15 +282,18 @@ def test_mx_layer_chain_hands_y_codes_to_the_next_layer(B, mx_scores):
 
 
 TRAIN_CASES = [
-    (4, [300, 1100, 129], 0, "unit", 0),
-    (4, [300, 1100, 129], 0, "unit", 1100),     # dQ from the kept dS
-    (4, [300, 1100, 129], 0, "literal", 0),
-    (5, [100, 300, 0, 64], 40, "unit", 0),
+    (4, [300, 1100, 129], 0, "unit", 0, False),
+    (4, [300, 1100, 129], 0, "unit", 1100, False),     # dQ from the kept dS
+    (4, [300, 1100, 129], 0, "literal", 0, False),
+    (5, [100, 300, 0, 64], 40, "unit", 0, False),
+    # the attention's scores in MXFP8 too (q, k saved as their MXFP8 values)
+    (4, [300, 1100, 129], 0, "unit", 1100, True),
+    (5, [100, 300, 0, 64], 40, "unit", 0, True),
 ]
 
 
-@pytest.mark.parametrize("ci,hist,c,variant,max_len", TRAIN_CASES)
-def test_mx_layer_train_step(B, ci, hist, c, variant, max_len):
+@pytest.mark.parametrize("ci,hist,c,variant,max_len,mx_scores", TRAIN_CASES)
+def test_mx_layer_train_step(B, ci, hist, c, variant, max_len, mx_scores):
     """MXFP8 training step (hstu_layer_fwd_mx keeping its intermediates,
     then hstu_layer_bwd_mx) against the oracle's MX forward and backward.
     Only the quantization of dZ and G can round differently on the two sides
@@ -302,7 +305,8 @@ def test_mx_layer_train_step(B, ci, hist, c, variant, max_len):
                                       n_layers=1)
     if variant == "unit":
         cfg = cfg.unit_scale()
-    say(f"mx train cfg{ci} {variant} lengths={hist} c={c} max_len={max_len}")
+    say(f"mx train cfg{ci} {variant} lengths={hist} c={c} max_len={max_len} "
+        f"mx_scores={mx_scores}")
     inp = synth.make_inputs(cfg, seed=1800 + ci)
     w = inp.layers[0]
     td = torch.bfloat16
@@ -318,12 +322,14 @@ def test_mx_layer_train_step(B, ci, hist, c, variant, max_len):
     lc.attn.max_len = max_len
     wm = B.MxLayerWeights.from_bf16(W1, W2)
     saved = B.Saved(T, lc, td, "cuda")
-    y = B.hstu_layer_fwd_mx(X, wm, rp, rt, offs, ts, lc, num_candidates=nc, saved=saved)
+    y = B.hstu_layer_fwd_mx(X, wm, rp, rt, offs, ts, lc, num_candidates=nc, saved=saved,
+                            mx_scores=mx_scores)
     dx, g = B.hstu_layer_bwd(X, W1, W2, rp, rt, offs, ts, lc, saved, dev(dY, td),
                              num_candidates=nc, mx=True)
     f = orc.LayerFlags(H=cfg.H, d_qk=cfg.d_qk, d_v=cfg.d_v, norm_len=cfg.norm_len, eps=1e-6)
     Yo, sv = orc.layer_fwd_mx(inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
-                              inp.timestamps, inp.num_candidates, f, return_saved=True)
+                              inp.timestamps, inp.num_candidates, f, return_saved=True,
+                              mx_scores=mx_scores)
     want = orc.layer_bwd_mx(dY, inp.X, w.W1, w.W2, w.rab_pos, w.rab_time, inp.seq_offsets,
                             inp.timestamps, inp.num_candidates, f, sv)
     # the training forward: G codes may round differently from the oracle's

@@ -416,3 +416,37 @@ def test_mx_layer_scores_quantize_the_bf16_activations():
     np.testing.assert_allclose(Y, want, rtol=1e-10, atol=1e-12)
     # and the score rounding changes the layer
     assert np.abs(Y - orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f)).max() > 0
+
+
+def test_mx_layer_scores_training_saves_the_mx_values():
+    """With mx_scores and return_saved, the saved U|V|Q|K holds q and k as
+    their MXFP8 values (U and V unchanged), the forward output is the one
+    without return_saved, and the backward on those values equals the MX
+    backward of the plain MX layer when q and k are replaced by them: the
+    gradients reach Z through the quantizer as through the identity."""
+    X, W1, W2, dY, rp, rt, offs, ts, f = _mx_case(43)
+    f = orc.LayerFlags(H=f.H, d_qk=32, d_v=32, norm_len=16, eps=1e-3)
+    Y, sv = orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f, mx_scores=True,
+                             return_saved=True)
+    np.testing.assert_array_equal(Y, orc.layer_fwd_mx(X, W1, W2, rp, rt, offs, ts, None, f,
+                                                      mx_scores=True))
+    Zh = orc.silu(orc.mx_matmul(X, W1))
+    T, H, d = X.shape[0], f.H, 32
+    U, V, Q, K = (Zh[:, i * H * d:(i + 1) * H * d].reshape(T, H, d) for i in range(4))
+    qc, qs = orc.mx_quantize(orc.bf16_round(Q), axis=2)
+    kc, ks = orc.mx_quantize(orc.bf16_round(K), axis=2)
+    Qm = orc.mx_dequantize(qc, qs, axis=2).reshape(T, -1)
+    Km = orc.mx_dequantize(kc, ks, axis=2).reshape(T, -1)
+    np.testing.assert_array_equal(sv["Zh"][:, :2 * H * d], Zh[:, :2 * H * d])
+    np.testing.assert_array_equal(sv["Zh"][:, 2 * H * d:3 * H * d], Qm)
+    np.testing.assert_array_equal(sv["Zh"][:, 3 * H * d:], Km)
+    # the backward: dQ and dK of the attention on (Qm, Km), straight through
+    g = orc.layer_bwd_mx(dY, X, W1, W2, rp, rt, offs, ts, None, f, sv)
+    dO = g["dO"].reshape(T, H, d)
+    dQ, dK, dV, _, _ = orc.attn_bwd(Qm.reshape(T, H, d), Km.reshape(T, H, d), V, offs, ts, rp,
+                                    rt, dO, None, 0, 16)
+    sg = orc.silu_grad(sv["Z"])
+    np.testing.assert_allclose(g["dZ"][:, 2 * H * d:3 * H * d], dQ.reshape(T, -1) *
+                               sg[:, 2 * H * d:3 * H * d], rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(g["dZ"][:, 3 * H * d:], dK.reshape(T, -1) * sg[:, 3 * H * d:],
+                               rtol=1e-10, atol=1e-13)
